@@ -1,0 +1,279 @@
+"""Benchmark of the MISA routed indexer on one MI355X.
+
+Workload (DeepSeek-V3.2-like long-context decode): 4 queries, each over its
+own prefix of L = 131072 bf16 index keys (d = 128), H_I = 64 indexer heads,
+h = 8 routed heads, B = 128 (M = 1024 pooled blocks), top-k = 2048, with 32
+planted needle keys per query.
+
+One step = the whole indexer hot path for the batch: block pooling of the
+keys, head routing, routed scoring + exact top-k.  Inputs are resident in HBM
+before timing; the timed steps rotate over 4 replicas of the keys (512 MiB in
+all, twice the 256 MB last-level Infinity Cache), so every step starts from
+keys that are not cache resident.  Timed beside it with the same protocol:
+the same path with the pooled table cached (route + score), the dense 64-head
+DSA indexer, and MISA-dagger (coarse top-8192 + all-head rerank) on bf16 and
+fp8 keys.
+
+Prints ONE JSON line.  `value` = prefix tokens indexed per second (sum of
+the visible prefix lengths per step / time per step).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefix tokens indexed/sec (L=128K, h=8 of 64) + % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+REPLICAS = 4
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--h", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    return ap.parse_args()
+
+
+class Replicas:
+    """Device copies of one problem's keys plus preallocated outputs."""
+
+    def __init__(self, p, torch, binding, h, k_prime):
+        from long_context_mean_amd.binding import DeviceProblem
+        self.p = p
+        self.dp = DeviceProblem(p)
+        self.k = [self.dp.k] + [self.dp.k.clone() for _ in range(REPLICAS - 1)]
+        self.ks = [self.dp.k_scale] * REPLICAS if self.dp.k_scale is None else \
+            [self.dp.k_scale] + [self.dp.k_scale.clone() for _ in range(REPLICAS - 1)]
+        dev = self.dp.q.device
+        N, H_I, d, L, B = p.N, p.H_I, p.d, p.L, p.B
+        M = -(-L // B)
+        self.h = h
+        self.kbar = [torch.empty((p.S, M, d), dtype=torch.float32, device=dev)
+                     for _ in range(REPLICAS)]
+        self.heads = torch.empty((N, h), dtype=torch.int32, device=dev)
+        self.r = torch.empty((N, H_I), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((N, p.topk), dtype=torch.int32, device=dev)
+        self.sc = torch.empty((N, p.topk), dtype=torch.float32, device=dev)
+        self.k_prime = k_prime
+        self.cand = torch.empty((N, max(k_prime, 1)), dtype=torch.int32, device=dev)
+        self.ws_route = binding.workspace(binding.MISA_OP_ROUTE, N, L, d, H_I, B, device=dev)
+        self.ws_score = binding.workspace(binding.MISA_OP_SCORE_TOPK, N, L, d, H_I,
+                                          topk=max(p.topk, k_prime), device=dev)
+        self.ws_rerank = binding.workspace(binding.MISA_OP_RERANK, N, L, d, H_I, topk=p.topk,
+                                           k_prime=max(k_prime, p.topk), device=dev)
+        self.b = binding
+
+    def pool(self, i):
+        self.b.misa_pool_keys(self.k[i], self.p.B, self.ks[i], kbar=self.kbar[i])
+
+    def route(self, i):
+        d = self.dp
+        self.b.misa_route_heads(d.q, d.w, self.kbar[i], self.k[i], d.q_seq, d.q_pos, self.p.B,
+                                self.h, k_scale=self.ks[i], heads=self.heads, head_score=self.r,
+                                ws=self.ws_route)
+
+    def score(self, i, topk=None, out=None):
+        d = self.dp
+        self.b.misa_score_topk(d.q, d.w, self.k[i], d.q_seq, d.q_pos, self.heads,
+                               self.p.topk if topk is None else topk, k_scale=self.ks[i],
+                               idx=self.idx if out is None else out, score=None,
+                               ws=self.ws_score, want_score=False)
+
+    def dense(self, i):
+        d = self.dp
+        self.b.dsa_score_topk(d.q, d.w, self.k[i], d.q_seq, d.q_pos, self.p.topk,
+                              k_scale=self.ks[i], idx=self.idx, score=self.sc, ws=self.ws_score)
+
+    def rerank(self, i):
+        d = self.dp
+        self.b.misa_rerank(d.q, d.w, self.k[i], d.q_seq, d.q_pos, self.cand, self.p.topk,
+                           k_scale=self.ks[i], idx=self.idx, score=self.sc, ws=self.ws_rerank)
+
+    # step variants -------------------------------------------------------
+    def step_misa(self, i):
+        self.pool(i)
+        self.route(i)
+        self.score(i)
+
+    def step_misa_cached_pool(self, i):
+        self.route(i)
+        self.score(i)
+
+    def step_dense(self, i):
+        self.dense(i)
+
+    def step_dagger(self, i):
+        self.pool(i)
+        self.route(i)
+        self.score(i, topk=self.k_prime, out=self.cand)
+        self.rerank(i)
+
+
+def timed(torch, fn, steps, warmup):
+    for s in range(warmup):
+        fn(s % REPLICAS)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        fn(s % REPLICAS)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def kernel_times(torch, binding, fn, steps, warmup, per_step):
+    """Per-kernel HIP-event durations (ms) over `steps` steps of fn."""
+    for s in range(warmup):
+        fn(s % REPLICAS)
+    torch.cuda.synchronize()
+    binding.misa_profile_begin(steps * per_step + 16)
+    t0 = time.perf_counter()
+    for s in range(steps):
+        fn(s % REPLICAS)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    recs = binding.misa_profile_end(steps * per_step + 16)
+    by = {}
+    for name, ms in recs:
+        by.setdefault(name, []).append(ms)
+    return ms_step, {k: sum(v) / len(v) for k, v in by.items()}, \
+        {k: len(v) / steps for k, v in by.items()}
+
+
+def cpu_baseline(p, h):
+    import oracle
+    t0 = time.perf_counter()
+    oracle.misa(p, h=h)
+    dt = time.perf_counter() - t0
+    return {"value": p.tokens_indexed() / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"the full workload ({p.N} queries x {p.L} keys, pooling+routing+scoring+"
+                      f"top-k in double precision), one pass, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the indexer's queries shard across GPUs without any exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from long_context_mean_amd import binding, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    binding.lib()
+    h = args.h
+    log("[bench] generating c4 workload")
+    p = synth.make("c4", h=h)
+    rep = Replicas(p, torch, binding, h, k_prime=8192)
+    tokens = p.tokens_indexed()
+    key_bytes = p.N * p.L * p.d * 2
+
+    log("[bench] timing MISA step (pool + route + score/top-k)")
+    ms = timed(torch, rep.step_misa, args.steps, args.warmup)
+    value = tokens / (ms * 1e-3)
+    log(f"[bench] misa {ms:.4f} ms/step -> {value:.4e} tokens/s")
+
+    log("[bench] per-kernel HIP events over the timed steps")
+    ms_ev, kt, per = kernel_times(torch, binding, rep.step_misa, args.steps, 2, 16)
+    dominant = max(kt, key=lambda k: kt[k] * per[k])
+    bytes_per_launch = {"pool_kernel": key_bytes, "score_mfma_kernel": key_bytes}
+    alg = bytes_per_launch.get(dominant, key_bytes)
+    achieved = alg / (kt[dominant] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": dominant, "kernel_ms": round(kt[dominant], 5),
+                "algorithmic_bytes_per_launch": alg}
+
+    extra = {"kernel_ms": {k: round(v, 5) for k, v in kt.items()},
+             "step_ms_with_kernel_events": round(ms_ev, 4)}
+    sc_ms = kt.get("score_mfma_kernel")
+    if sc_ms:
+        extra["score_kernel_hbm_gbs"] = round(key_bytes / (sc_ms * 1e-3) / 1e9, 1)
+    pl_ms = kt.get("pool_kernel")
+    if pl_ms:
+        extra["pool_kernel_hbm_gbs"] = round(key_bytes / (pl_ms * 1e-3) / 1e9, 1)
+
+    if not args.no_extras:
+        ms_c = timed(torch, rep.step_misa_cached_pool, args.steps, args.warmup)
+        ms_d = timed(torch, rep.step_dense, args.steps, args.warmup)
+        ms_g = timed(torch, rep.step_dagger, args.steps, args.warmup)
+        extra.update({
+            "misa_cached_pool_ms": round(ms_c, 4),
+            "misa_cached_pool_tokens_per_s": tokens / (ms_c * 1e-3),
+            "dense_dsa_ms": round(ms_d, 4),
+            "speedup_vs_dense_full_step": round(ms_d / ms, 3),
+            "speedup_vs_dense_cached_pool": round(ms_d / ms_c, 3),
+            "misa_dagger_ms": round(ms_g, 4),
+        })
+        # recall of the dense top-k set (outside timing)
+        rep.step_misa(0)
+        torch.cuda.synchronize()
+        misa_idx = rep.idx.cpu().numpy()
+        rep.step_dense(0)
+        torch.cuda.synchronize()
+        dense_idx = rep.idx.cpu().numpy()
+        rep.step_dagger(0)
+        torch.cuda.synchronize()
+        dag_idx = rep.idx.cpu().numpy()
+
+        def rec(a, b):
+            return float(np.mean([len(set(x[x >= 0]) & set(y[y >= 0])) / max(1, (y >= 0).sum())
+                                  for x, y in zip(a, b)]))
+        extra["recall_vs_dense"] = round(rec(misa_idx, dense_idx), 4)
+        extra["misa_dagger_recall_vs_dense"] = round(rec(dag_idx, dense_idx), 4)
+        extra["needle_recall"] = round(float(np.mean(
+            [np.isin(p.needles[n, :, 0], misa_idx[n]).mean() for n in range(p.N)])), 4)
+        extra["needle_recall_dense"] = round(float(np.mean(
+            [np.isin(p.needles[n, :, 0], dense_idx[n]).mean() for n in range(p.N)])), 4)
+        del rep
+        torch.cuda.empty_cache()
+        log("[bench] fp8-key MISA-dagger (c5 shape)")
+        p5 = synth.make("c5")
+        r5 = Replicas(p5, torch, binding, p5.h, k_prime=p5.k_prime)
+        ms5 = timed(torch, r5.step_dagger, args.steps, args.warmup)
+        ms5d = timed(torch, r5.step_dense, args.steps, args.warmup)
+        extra["fp8_misa_dagger_ms"] = round(ms5, 4)
+        extra["fp8_misa_dagger_tokens_per_s"] = p5.tokens_indexed() / (ms5 * 1e-3)
+        extra["fp8_dense_dsa_ms"] = round(ms5d, 4)
+        del r5
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_baseline(p, h)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded 64-cluster Gaussian-mixture keys + planted needles)",
+        "config": {"workload": "long-context decode indexer: 4 queries x L=131072 bf16 keys, "
+                               "H_I=64, d=128, h=8, B=128, top-k=2048",
+                   "N": p.N, "L": p.L, "H_I": p.H_I, "h": h, "d": p.d, "B": p.B,
+                   "topk": p.topk, "step": "pool + route + routed score/top-k",
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+/*
+ * misa.h -- C ABI of the MISA routed indexer for AMD MI355X (gfx950).
+ *
+ * MISA (Mixture of Indexer Sparse Attention) is a drop-in replacement for the
+ * token indexer of DeepSeek Sparse Attention (DSA).  DSA's indexer scores every
+ * prefix token with all H_I indexer heads and keeps one shared top-k token set
+ * for the main attention (MISA abstract, HF Daily Papers digest).  MISA keeps
+ * only h of the H_I heads per query, chosen by a light router over
+ * block-pooled keys, so the per-query cost drops from O(H_I L) to
+ * O(h L + H_I M) with M = ceil(L/B) (MISA technical summary, gist.science,
+ * "Methodology" items 1-2).  MISA-dagger re-scores a wider routed candidate
+ * set of k' tokens with all H_I heads to recover the final top-k
+ * ("Hierarchical variant (MISA-dagger)").
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - All array pointers are DEVICE pointers to C-contiguous row-major memory
+ *    owned by the caller.  The library allocates and frees no device memory;
+ *    scratch space is the caller's workspace `ws` of `ws_bytes` bytes
+ *    (size it with misa_workspace_bytes; it needs no initialisation and is
+ *    overwritten).  The library keeps no pointer after a call returns.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously; outputs are valid once the stream has synchronised.
+ *  - Layouts:
+ *      q       [N, H_I, d]  dtype q_dt (MISA_F32 or MISA_BF16)
+ *      w       [N, H_I]     float32 head weights
+ *      k       [S, L, d]    dtype k_dt (MISA_F32, MISA_BF16 or MISA_FP8_E4M3)
+ *      k_scale [S, L]       float32 per-token scale, required iff k_dt is fp8
+ *                           (key value = scale * e4m3 value; scale > 0)
+ *      q_seq   [N]  int32   key sequence of query row n, 0 <= q_seq[n] < S
+ *      q_pos   [N]  int32   position of query row n, 0 <= q_pos[n] < L;
+ *                           row n sees keys 0..q_pos[n] (L_n = q_pos[n] + 1)
+ *    Supported (q_dt, k_dt): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3);
+ *    d in {64, 128}; 1 <= h <= H_I <= 64; 1 <= B <= 1024;
+ *    1 <= topk <= 16384; N >= 1; S >= 1; 1 <= L < 2^31 / d.
+ *  - Index-score: I(s) = sum over heads j of w[n,j] * ReLU(q[n,j,:] . key_s),
+ *    accumulated in fp32 from exact bf16 (or fp8-dequantised) products.
+ *  - Top-k outputs idx [N, topk] int32 and score [N, topk] float32 hold the
+ *    min(topk, L_n) tokens first under (score desc, token index asc), listed
+ *    in ASCENDING TOKEN INDEX order, followed by -1 / -inf padding.
+ *  - Errors: host-checkable arguments are validated before anything is
+ *    enqueued; a failed check returns its status and launches nothing.  A HIP
+ *    launch failure returns MISA_ERR_HIP (see misa_last_hip_error).
+ *    Device-resident values (q_seq, q_pos, heads, cand) are NOT read on the
+ *    host: out-of-range values there are undefined behaviour.
+ */
+#ifndef MISA_H
+#define MISA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MISA_F32 = 0, MISA_BF16 = 1, MISA_FP8_E4M3 = 2 } misa_dtype;
+
+typedef enum {
+  MISA_OK = 0,
+  MISA_ERR_NULL = 1,        /* a required pointer is NULL */
+  MISA_ERR_SHAPE = 2,       /* a size or size relation is out of range */
+  MISA_ERR_UNSUPPORTED = 3, /* dtype combination or d not supported */
+  MISA_ERR_WORKSPACE = 4,   /* ws_bytes smaller than misa_workspace_bytes */
+  MISA_ERR_HIP = 5          /* the HIP runtime reported an error */
+} misa_status;
+
+typedef enum {
+  MISA_OP_ROUTE = 0,        /* misa_route_heads */
+  MISA_OP_SCORE_TOPK = 1,   /* misa_score_topk (also dsa_score_topk) */
+  MISA_OP_RERANK = 2        /* misa_rerank */
+} misa_op;
+
+/*
+ * Block pooling (MISA technical summary, "Methodology" item 1: the prefix is
+ * split into M = ceil(L/B) blocks summarised by mean-pooled index keys).
+ *   kbar[s, b, :] = mean of key rows b*B .. min((b+1)*B, L) - 1 of sequence s
+ * Output kbar [S, ceil(L/B), d] float32 (fp32 accumulation).  The last block
+ * may be partial.  The table is causal only for rows that see all L keys;
+ * misa_route_heads handles each row's own partial block.
+ */
+int32_t misa_pool_keys(const void* k, const float* k_scale, int32_t k_dt, int32_t S, int32_t L,
+                       int32_t d, int32_t B, float* kbar, void* stream);
+
+/*
+ * Head router (same page, "Methodology" item 1: per-head affinities against
+ * the pooled keys, aggregated into a head importance, top-h heads kept; the
+ * router costs O(H_I M)).  The pages do not print the affinity formula; this
+ * library takes the indexer's own term at block granularity:
+ *   r[n, j] = |w[n,j]| * sum_{b < M_n} ReLU(q[n,j,:] . kbar_n[b])
+ * with M_n = ceil(L_n / B); blocks fully visible to row n come from the
+ * pooled table kbar [S, ceil(L/B), d] (from misa_pool_keys); a partial last
+ * block is the mean of row n's visible keys of that block only, read from k.
+ * heads [N, h] receives the first h heads under (r desc, head index asc),
+ * sorted ascending; head_score [N, H_I] receives r (may be NULL).
+ * Workspace: misa_workspace_bytes(MISA_OP_ROUTE, ...).
+ */
+int32_t misa_route_heads(const void* q, int32_t q_dt, const float* w, const float* kbar,
+                         const void* k, const float* k_scale, int32_t k_dt,
+                         const int32_t* q_seq, const int32_t* q_pos, int32_t N, int32_t S,
+                         int32_t L, int32_t d, int32_t B, int32_t H_I, int32_t h,
+                         int32_t* heads, float* head_score, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
+ * Routed token scoring + top-k (same page, "Methodology" item 2: only the h
+ * routed heads score every prefix token; the top-k tokens are taken from
+ * these reduced scores).  heads [N, h] are head indices in [0, H_I) (any
+ * order, distinct), normally the output of misa_route_heads.
+ *   I_n(s) = sum_{j in heads[n]} w[n,j] * ReLU(q[n,j,:] . key_{q_seq[n]}(s)),
+ *   s = 0 .. q_pos[n]
+ * Outputs idx/score as described in the conventions (score may be NULL).
+ * Workspace: misa_workspace_bytes(MISA_OP_SCORE_TOPK, ...).
+ */
+int32_t misa_score_topk(const void* q, int32_t q_dt, const float* w, const void* k,
+                        const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+                        const int32_t* q_pos, const int32_t* heads, int32_t N, int32_t S,
+                        int32_t L, int32_t d, int32_t H_I, int32_t h, int32_t topk,
+                        int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dense DSA indexer (the baseline MISA replaces: every one of the H_I heads
+ * scores every prefix token, MISA abstract and "Problem statement"):
+ * misa_score_topk with all H_I heads.
+ */
+int32_t dsa_score_topk(const void* q, int32_t q_dt, const float* w, const void* k,
+                       const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+                       const int32_t* q_pos, int32_t N, int32_t S, int32_t L, int32_t d,
+                       int32_t H_I, int32_t topk, int32_t* idx, float* score, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * MISA-dagger fine stage (same page, "Hierarchical variant (MISA-dagger)":
+ * the routed pass keeps a wider candidate set of k' tokens, e.g. 8192, and the
+ * original DSA indexer with all H_I heads re-scores only those candidates to
+ * recover the final top-k).
+ * cand [N, k_prime] int32: candidate token indices of row n, each < L_n, the
+ * valid ones strictly ascending, -1 marking empty slots (the idx output of
+ * misa_score_topk with topk = k_prime has exactly this form).
+ * Outputs idx/score [N, topk] as in the conventions, over the valid
+ * candidates, ranked by the all-head score.  Requires topk <= k_prime.
+ * Workspace: misa_workspace_bytes(MISA_OP_RERANK, ...).
+ */
+int32_t misa_rerank(const void* q, int32_t q_dt, const float* w, const void* k,
+                    const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+                    const int32_t* q_pos, const int32_t* cand, int32_t N, int32_t S, int32_t L,
+                    int32_t d, int32_t H_I, int32_t k_prime, int32_t topk, int32_t* idx,
+                    float* score, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Workspace bytes for `op` at these sizes (0 for invalid sizes).  Arguments
+ * an op does not use are ignored (k_prime only matters for MISA_OP_RERANK, B
+ * only for MISA_OP_ROUTE).
+ */
+size_t misa_workspace_bytes(int32_t op, int32_t N, int32_t L, int32_t d, int32_t H_I,
+                            int32_t B, int32_t topk, int32_t k_prime);
+
+/* Static description of a status code. */
+const char* misa_status_string(int32_t status);
+
+/* hipError_t of the last MISA_ERR_HIP on the calling thread (0 if none). */
+int32_t misa_last_hip_error(void);
+
+/*
+ * Kernel timing for benchmarks.  misa_profile_begin(capacity) creates
+ * `capacity` pairs of HIP events (host-side allocation happens here, not in
+ * the timed calls) and from then on brackets every kernel the library
+ * launches with an event pair recorded on that kernel's stream, until
+ * capacity is used up or misa_profile_end is called.  misa_profile_end
+ * synchronises the recorded events and writes up to `max` records:
+ * kernel_id[i] (see misa_kernel_name) and ms[i], the elapsed time between the
+ * pair.  It returns the number of records written (negative on error) and
+ * frees the events.  Profiling is process-global and not thread-safe.
+ */
+int32_t misa_profile_begin(int32_t capacity);
+int32_t misa_profile_end(int32_t* kernel_id, float* ms, int32_t max);
+const char* misa_kernel_name(int32_t kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MISA_H */

@@ -1,0 +1,254 @@
+"""Python binding of libmisa.so (include/misa.h): argument marshalling only.
+
+Each function has the name of the C entry point it calls.  Arguments are
+torch tensors on the GPU; sizes are read from their shapes, outputs are
+allocated with torch when not given, and the call is enqueued on torch's
+current HIP stream of the tensors' device.  Every step of the computation
+runs in the library's HIP kernels.  A missing library raises
+MisaLibraryMissing: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import synth
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmisa.so")
+
+MISA_F32, MISA_BF16, MISA_FP8_E4M3 = 0, 1, 2
+MISA_OP_ROUTE, MISA_OP_SCORE_TOPK, MISA_OP_RERANK = 0, 1, 2
+MISA_OK = 0
+
+EXPORTED = ("misa_pool_keys", "misa_route_heads", "misa_score_topk", "dsa_score_topk",
+            "misa_rerank", "misa_workspace_bytes", "misa_status_string",
+            "misa_last_hip_error", "misa_profile_begin", "misa_profile_end", "misa_kernel_name")
+
+
+class MisaLibraryMissing(ImportError):
+    pass
+
+
+class MisaError(RuntimeError):
+    def __init__(self, fn, status):
+        msg = lib().misa_status_string(status).decode()
+        if status == 5:
+            msg += f" (hipError {lib().misa_last_hip_error()})"
+        super().__init__(f"{fn}: {msg} [status {status}]")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmisa.so (raises MisaLibraryMissing if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise MisaLibraryMissing(
+            f"{LIB_PATH} is not built; run `python -m long_context_mean_amd.build_lib`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.misa_pool_keys.argtypes = [P, P, I32, I32, I32, I32, I32, P, P]
+    L.misa_route_heads.argtypes = [P, I32, P, P, P, P, I32, P, P] + [I32] * 7 + [P, P, P, SZ, P]
+    L.misa_score_topk.argtypes = [P, I32, P, P, P, I32, P, P, P] + [I32] * 7 + [P, P, P, SZ, P]
+    L.dsa_score_topk.argtypes = [P, I32, P, P, P, I32, P, P] + [I32] * 6 + [P, P, P, SZ, P]
+    L.misa_rerank.argtypes = [P, I32, P, P, P, I32, P, P, P] + [I32] * 7 + [P, P, P, SZ, P]
+    L.misa_workspace_bytes.argtypes = [I32] * 8
+    L.misa_workspace_bytes.restype = ctypes.c_size_t
+    L.misa_status_string.argtypes = [I32]
+    L.misa_status_string.restype = ctypes.c_char_p
+    L.misa_last_hip_error.argtypes = []
+    L.misa_profile_begin.argtypes = [I32]
+    L.misa_profile_end.argtypes = [P, P, I32]
+    L.misa_kernel_name.argtypes = [I32]
+    L.misa_kernel_name.restype = ctypes.c_char_p
+    for f in ("misa_pool_keys", "misa_route_heads", "misa_score_topk", "dsa_score_topk",
+              "misa_rerank", "misa_last_hip_error", "misa_profile_begin", "misa_profile_end"):
+        getattr(L, f).restype = ctypes.c_int32
+    _lib = L
+    return L
+
+
+# ---------------------------------------------------------------- marshalling helpers
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    assert t.is_contiguous(), "tensors must be contiguous"
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MISA_F32
+    if t.dtype in (torch.bfloat16, torch.int16):
+        return MISA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return MISA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(fn, status):
+    if status != MISA_OK:
+        raise MisaError(fn, status)
+
+
+def workspace(op: int, N: int, L: int, d: int, H_I: int, B: int = 1, topk: int = 1,
+              k_prime: int = 0, device="cuda") -> torch.Tensor:
+    n = misa_workspace_bytes(op, N, L, d, H_I, B, topk, k_prime)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- the C entry points
+def misa_workspace_bytes(op, N, L, d, H_I, B=1, topk=1, k_prime=0) -> int:
+    return int(lib().misa_workspace_bytes(op, N, L, d, H_I, B, topk, k_prime))
+
+
+def misa_pool_keys(k: torch.Tensor, B: int, k_scale: Optional[torch.Tensor] = None,
+                   kbar: Optional[torch.Tensor] = None) -> torch.Tensor:
+    S, L, d = k.shape
+    M = -(-L // B)
+    if kbar is None:
+        kbar = torch.empty((S, M, d), dtype=torch.float32, device=k.device)
+    _check("misa_pool_keys", lib().misa_pool_keys(_ptr(k), _ptr(k_scale), _dtype_code(k), S, L, d,
+                                                  B, _ptr(kbar), _stream(k)))
+    return kbar
+
+
+def misa_route_heads(q, w, kbar, k, q_seq, q_pos, B: int, h: int, k_scale=None, heads=None,
+                     head_score=None, ws=None, want_scores=True):
+    N, H_I, d = q.shape
+    S, L, _ = k.shape
+    if heads is None:
+        heads = torch.empty((N, h), dtype=torch.int32, device=q.device)
+    if head_score is None and want_scores:
+        head_score = torch.empty((N, H_I), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(MISA_OP_ROUTE, N, L, d, H_I, B, device=q.device)
+    _check("misa_route_heads", lib().misa_route_heads(
+        _ptr(q), _dtype_code(q), _ptr(w), _ptr(kbar), _ptr(k), _ptr(k_scale), _dtype_code(k),
+        _ptr(q_seq), _ptr(q_pos), N, S, L, d, B, H_I, h, _ptr(heads), _ptr(head_score),
+        _ptr(ws), ws.numel(), _stream(q)))
+    return heads, head_score
+
+
+def misa_score_topk(q, w, k, q_seq, q_pos, heads, topk: int, k_scale=None, idx=None, score=None,
+                    ws=None, want_score=True):
+    N, H_I, d = q.shape
+    S, L, _ = k.shape
+    h = heads.shape[1]
+    if idx is None:
+        idx = torch.empty((N, topk), dtype=torch.int32, device=q.device)
+    if score is None and want_score:
+        score = torch.empty((N, topk), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(MISA_OP_SCORE_TOPK, N, L, d, H_I, topk=topk, device=q.device)
+    _check("misa_score_topk", lib().misa_score_topk(
+        _ptr(q), _dtype_code(q), _ptr(w), _ptr(k), _ptr(k_scale), _dtype_code(k), _ptr(q_seq),
+        _ptr(q_pos), _ptr(heads), N, S, L, d, H_I, h, topk, _ptr(idx), _ptr(score), _ptr(ws),
+        ws.numel(), _stream(q)))
+    return idx, score
+
+
+def dsa_score_topk(q, w, k, q_seq, q_pos, topk: int, k_scale=None, idx=None, score=None,
+                   ws=None, want_score=True):
+    N, H_I, d = q.shape
+    S, L, _ = k.shape
+    if idx is None:
+        idx = torch.empty((N, topk), dtype=torch.int32, device=q.device)
+    if score is None and want_score:
+        score = torch.empty((N, topk), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(MISA_OP_SCORE_TOPK, N, L, d, H_I, topk=topk, device=q.device)
+    _check("dsa_score_topk", lib().dsa_score_topk(
+        _ptr(q), _dtype_code(q), _ptr(w), _ptr(k), _ptr(k_scale), _dtype_code(k), _ptr(q_seq),
+        _ptr(q_pos), N, S, L, d, H_I, topk, _ptr(idx), _ptr(score), _ptr(ws), ws.numel(),
+        _stream(q)))
+    return idx, score
+
+
+def misa_rerank(q, w, k, q_seq, q_pos, cand, topk: int, k_scale=None, idx=None, score=None,
+                ws=None, want_score=True):
+    N, H_I, d = q.shape
+    S, L, _ = k.shape
+    k_prime = cand.shape[1]
+    if idx is None:
+        idx = torch.empty((N, topk), dtype=torch.int32, device=q.device)
+    if score is None and want_score:
+        score = torch.empty((N, topk), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(MISA_OP_RERANK, N, L, d, H_I, topk=topk, k_prime=k_prime, device=q.device)
+    _check("misa_rerank", lib().misa_rerank(
+        _ptr(q), _dtype_code(q), _ptr(w), _ptr(k), _ptr(k_scale), _dtype_code(k), _ptr(q_seq),
+        _ptr(q_pos), _ptr(cand), N, S, L, d, H_I, k_prime, topk, _ptr(idx), _ptr(score),
+        _ptr(ws), ws.numel(), _stream(q)))
+    return idx, score
+
+
+def misa_profile_begin(capacity: int):
+    _check("misa_profile_begin", lib().misa_profile_begin(capacity))
+
+
+def misa_profile_end(max_records: int):
+    """Returns a list of (kernel_name, ms) records."""
+    ids = (ctypes.c_int32 * max_records)()
+    ms = (ctypes.c_float * max_records)()
+    n = lib().misa_profile_end(ids, ms, max_records)
+    if n < 0:
+        raise MisaError("misa_profile_end", -n)
+    return [(lib().misa_kernel_name(ids[i]).decode(), float(ms[i])) for i in range(n)]
+
+
+# ---------------------------------------------------------------- problems on the device
+class DeviceProblem:
+    """A synth.Problem's arrays as device tensors (q/k bf16 as torch.bfloat16,
+    e4m3 codes as torch.uint8)."""
+
+    def __init__(self, p: synth.Problem, device="cuda"):
+        self.p = p
+
+        def up(a, dtype=None):
+            t = torch.from_numpy(a)
+            if dtype is not None:
+                t = t.view(dtype)
+            return t.to(device)
+
+        self.q = up(p.q.view(np.int16), torch.bfloat16) if p.q_dt == synth.BF16 else up(p.q)
+        if p.k_dt == synth.BF16:
+            self.k = up(p.k.view(np.int16), torch.bfloat16)
+        else:
+            self.k = up(p.k)
+        self.w = up(p.w)
+        self.k_scale = up(p.k_scale) if p.k_scale is not None else None
+        self.q_seq = up(p.q_seq)
+        self.q_pos = up(p.q_pos)
+
+    def pool(self, B=None):
+        return misa_pool_keys(self.k, self.p.B if B is None else B, self.k_scale)
+
+    def route(self, kbar, h=None, **kw):
+        return misa_route_heads(self.q, self.w, kbar, self.k, self.q_seq, self.q_pos, self.p.B,
+                                self.p.h if h is None else h, k_scale=self.k_scale, **kw)
+
+    def score_topk(self, heads, topk=None, **kw):
+        return misa_score_topk(self.q, self.w, self.k, self.q_seq, self.q_pos, heads,
+                               self.p.topk if topk is None else topk, k_scale=self.k_scale, **kw)
+
+    def dsa(self, topk=None, **kw):
+        return dsa_score_topk(self.q, self.w, self.k, self.q_seq, self.q_pos,
+                              self.p.topk if topk is None else topk, k_scale=self.k_scale, **kw)
+
+    def rerank(self, cand, topk=None, **kw):
+        return misa_rerank(self.q, self.w, self.k, self.q_seq, self.q_pos, cand,
+                           self.p.topk if topk is None else topk, k_scale=self.k_scale, **kw)

@@ -1,0 +1,302 @@
+// C ABI of the MISA indexer library: argument validation, workspace layout,
+// dispatch to the gfx950 kernels, kernel timing.  See include/misa.h for the
+// contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <vector>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "misa.h"
+
+namespace {
+
+thread_local int32_t g_last_hip = 0;
+
+constexpr int kMaxN = 65535;          // grid y limit
+constexpr int kMaxL = 1 << 27;
+constexpr int kMaxTopk = 65536;
+constexpr int kOneRowMinN = 128;      // rows at which one workgroup per row fills the chip
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return MISA_OK;
+  g_last_hip = static_cast<int32_t>(e);
+  return MISA_ERR_HIP;
+}
+
+int32_t check_dtypes(int32_t q_dt, int32_t k_dt, const float* k_scale) {
+  const bool ok = (q_dt == MISA_F32 && k_dt == MISA_F32) ||
+                  (q_dt == MISA_BF16 && k_dt == MISA_BF16) ||
+                  (q_dt == MISA_BF16 && k_dt == MISA_FP8_E4M3);
+  if (!ok) return MISA_ERR_UNSUPPORTED;
+  if (k_dt == MISA_FP8_E4M3 && !k_scale) return MISA_ERR_NULL;
+  return MISA_OK;
+}
+
+int32_t check_sizes(int32_t N, int32_t S, int32_t L, int32_t d, int32_t H_I) {
+  if (d != 64 && d != 128) return MISA_ERR_UNSUPPORTED;
+  if (N < 1 || N > kMaxN || S < 1 || S > kMaxN || L < 1 || L > kMaxL) return MISA_ERR_SHAPE;
+  if (H_I < 1 || H_I > 64) return MISA_ERR_SHAPE;
+  return MISA_OK;
+}
+
+// ---------------------------------------------------------------- workspace layouts
+struct TopkLayout {
+  bool one_row = false;
+  int u_stride = 0;
+  size_t off_hist = 0, off_cnt = 0, bytes = 0;
+};
+
+TopkLayout topk_layout(int N, int len_max) {
+  TopkLayout t;
+  const int chunk = misa::topk_chunk();
+  t.u_stride = static_cast<int>(align_up(static_cast<size_t>(len_max), chunk));
+  t.one_row = N >= kOneRowMinN || t.u_stride <= chunk;
+  size_t off = align_up(static_cast<size_t>(N) * t.u_stride * 4, 256);
+  if (!t.one_row) {
+    t.off_hist = off;
+    off = align_up(off + static_cast<size_t>(N) * misa::kHistWords * 4, 256);
+    t.off_cnt = off;
+    off = align_up(off + static_cast<size_t>(N) * (t.u_stride / chunk) * 2 * 4, 256);
+  }
+  t.bytes = off;
+  return t;
+}
+
+int route_chunks(int L, int B) {
+  const int mf = L / B;
+  const int per = misa::route_blocks_per_chunk();
+  const int c = (mf + per - 1) / per;
+  return c > 0 ? c : 1;
+}
+
+size_t route_bytes(int N, int L, int B, int H_I) {
+  return align_up(static_cast<size_t>(N) * route_chunks(L, B) * H_I * 4, 256);
+}
+
+// ---------------------------------------------------------------- kernel timing
+struct Profiler {
+  bool on = false;
+  int cap = 0, used = 0, pending = -1;
+  std::vector<hipEvent_t> ev0, ev1;
+  std::vector<int> ids;
+};
+Profiler g_prof;
+
+int32_t score_topk_impl(const void* q, int32_t q_dt, const float* w, const void* k,
+                        const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+                        const int32_t* q_pos, const int32_t* heads, int32_t N, int32_t S,
+                        int32_t L, int32_t d, int32_t H_I, int32_t h, int32_t topk,
+                        int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !w || !k || !q_seq || !q_pos || !idx) return MISA_ERR_NULL;
+  int32_t rc = check_dtypes(q_dt, k_dt, k_scale);
+  if (rc) return rc;
+  if ((rc = check_sizes(N, S, L, d, H_I))) return rc;
+  if (h < 1 || h > H_I || topk < 1 || topk > kMaxTopk) return MISA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k)) return MISA_ERR_SHAPE;
+  const TopkLayout lay = topk_layout(N, L);
+  if (!ws) return MISA_ERR_NULL;
+  if (ws_bytes < lay.bytes) return MISA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint32_t* u = reinterpret_cast<uint32_t*>(base);
+  uint32_t* hist = lay.one_row ? nullptr : reinterpret_cast<uint32_t*>(base + lay.off_hist);
+  uint32_t* cnt = lay.one_row ? nullptr : reinterpret_cast<uint32_t*>(base + lay.off_cnt);
+  hipError_t e = hipSuccess;
+  if (hist) e = misa::launch_clear(hist, static_cast<size_t>(N) * misa::kHistWords, st);
+  if (e != hipSuccess) return hip_status(e);
+  misa::ScoreArgs sa{q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, heads, nullptr,
+                     N, S, L, d, H_I, h, 0, u, lay.u_stride, hist};
+  e = misa::launch_score(sa, st);
+  if (e != hipSuccess) return hip_status(e);
+  misa::TopkArgs ta{u, lay.u_stride, q_pos, 0, N, topk, lay.one_row, hist, cnt,
+                    nullptr, 0, idx, score};
+  return hip_status(misa::launch_topk(ta, st));
+}
+
+}  // namespace
+
+namespace misa {
+
+void prof_start(hipStream_t st, int kernel_id) {
+  if (!g_prof.on || g_prof.used >= g_prof.cap) return;
+  g_prof.pending = kernel_id;
+  (void)hipEventRecord(g_prof.ev0[g_prof.used], st);
+}
+
+void prof_stop(hipStream_t st) {
+  if (!g_prof.on || g_prof.pending < 0 || g_prof.used >= g_prof.cap) return;
+  (void)hipEventRecord(g_prof.ev1[g_prof.used], st);
+  g_prof.ids[g_prof.used] = g_prof.pending;
+  g_prof.pending = -1;
+  ++g_prof.used;
+}
+
+}  // namespace misa
+
+extern "C" {
+
+const char* misa_status_string(int32_t status) {
+  switch (status) {
+    case MISA_OK: return "ok";
+    case MISA_ERR_NULL: return "a required pointer is NULL";
+    case MISA_ERR_SHAPE: return "size or alignment out of range";
+    case MISA_ERR_UNSUPPORTED: return "unsupported dtype combination or head dimension";
+    case MISA_ERR_WORKSPACE: return "workspace too small";
+    case MISA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t misa_last_hip_error(void) { return g_last_hip; }
+
+size_t misa_workspace_bytes(int32_t op, int32_t N, int32_t L, int32_t d, int32_t H_I, int32_t B,
+                            int32_t topk, int32_t k_prime) {
+  (void)d;
+  (void)topk;
+  if (N < 1 || N > kMaxN || L < 1 || L > kMaxL || H_I < 1 || H_I > 64) return 0;
+  switch (op) {
+    case MISA_OP_ROUTE:
+      if (B < 1 || B > 1024) return 0;
+      return route_bytes(N, L, B, H_I);
+    case MISA_OP_SCORE_TOPK:
+      return topk_layout(N, L).bytes;
+    case MISA_OP_RERANK: {
+      if (k_prime < 1 || k_prime > kMaxTopk) return 0;
+      TopkLayout t = topk_layout(kOneRowMinN, k_prime);   // always one row per workgroup
+      return align_up(static_cast<size_t>(N) * t.u_stride * 4, 256);
+    }
+    default:
+      return 0;
+  }
+}
+
+int32_t misa_pool_keys(const void* k, const float* k_scale, int32_t k_dt, int32_t S, int32_t L,
+                       int32_t d, int32_t B, float* kbar, void* stream) {
+  if (!k || !kbar) return MISA_ERR_NULL;
+  if (k_dt != MISA_F32 && k_dt != MISA_BF16 && k_dt != MISA_FP8_E4M3) return MISA_ERR_UNSUPPORTED;
+  if (k_dt == MISA_FP8_E4M3 && !k_scale) return MISA_ERR_NULL;
+  if (d != 64 && d != 128) return MISA_ERR_UNSUPPORTED;
+  if (S < 1 || S > kMaxN || L < 1 || L > kMaxL || B < 1 || B > 1024) return MISA_ERR_SHAPE;
+  if (!aligned16(k)) return MISA_ERR_SHAPE;
+  misa::PoolArgs a{k, k_scale, k_dt, S, L, d, B, kbar};
+  return hip_status(misa::launch_pool(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t misa_route_heads(const void* q, int32_t q_dt, const float* w, const float* kbar,
+                         const void* k, const float* k_scale, int32_t k_dt,
+                         const int32_t* q_seq, const int32_t* q_pos, int32_t N, int32_t S,
+                         int32_t L, int32_t d, int32_t B, int32_t H_I, int32_t h,
+                         int32_t* heads, float* head_score, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (!q || !w || !kbar || !k || !q_seq || !q_pos || !heads) return MISA_ERR_NULL;
+  int32_t rc = check_dtypes(q_dt, k_dt, k_scale);
+  if (rc) return rc;
+  if ((rc = check_sizes(N, S, L, d, H_I))) return rc;
+  if (B < 1 || B > 1024 || h < 1 || h > H_I) return MISA_ERR_SHAPE;
+  if (!ws) return MISA_ERR_NULL;
+  if (ws_bytes < route_bytes(N, L, B, H_I)) return MISA_ERR_WORKSPACE;
+  misa::RouteArgs a{q, q_dt, w, kbar, k, k_scale, k_dt, q_seq, q_pos, N, S, L, d, B, H_I, h,
+                    heads, head_score, static_cast<float*>(ws), route_chunks(L, B)};
+  return hip_status(misa::launch_route(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t misa_score_topk(const void* q, int32_t q_dt, const float* w, const void* k,
+                        const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+                        const int32_t* q_pos, const int32_t* heads, int32_t N, int32_t S,
+                        int32_t L, int32_t d, int32_t H_I, int32_t h, int32_t topk,
+                        int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream) {
+  if (!heads) return MISA_ERR_NULL;
+  return score_topk_impl(q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, heads, N, S, L, d, H_I, h,
+                         topk, idx, score, ws, ws_bytes, stream);
+}
+
+int32_t dsa_score_topk(const void* q, int32_t q_dt, const float* w, const void* k,
+                       const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+                       const int32_t* q_pos, int32_t N, int32_t S, int32_t L, int32_t d,
+                       int32_t H_I, int32_t topk, int32_t* idx, float* score, void* ws,
+                       size_t ws_bytes, void* stream) {
+  return score_topk_impl(q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, nullptr, N, S, L, d, H_I,
+                         H_I, topk, idx, score, ws, ws_bytes, stream);
+}
+
+int32_t misa_rerank(const void* q, int32_t q_dt, const float* w, const void* k,
+                    const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+                    const int32_t* q_pos, const int32_t* cand, int32_t N, int32_t S, int32_t L,
+                    int32_t d, int32_t H_I, int32_t k_prime, int32_t topk, int32_t* idx,
+                    float* score, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !w || !k || !q_seq || !q_pos || !cand || !idx) return MISA_ERR_NULL;
+  int32_t rc = check_dtypes(q_dt, k_dt, k_scale);
+  if (rc) return rc;
+  if ((rc = check_sizes(N, S, L, d, H_I))) return rc;
+  if (topk < 1 || k_prime < topk || k_prime > kMaxTopk) return MISA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k)) return MISA_ERR_SHAPE;
+  const size_t need = misa_workspace_bytes(MISA_OP_RERANK, N, L, d, H_I, 1, topk, k_prime);
+  if (!ws) return MISA_ERR_NULL;
+  if (ws_bytes < need) return MISA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int u_stride = topk_layout(kOneRowMinN, k_prime).u_stride;
+  uint32_t* u = static_cast<uint32_t*>(ws);
+  misa::ScoreArgs sa{q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, nullptr, cand,
+                     N, S, L, d, H_I, H_I, k_prime, u, u_stride, nullptr};
+  hipError_t e = misa::launch_score(sa, st);
+  if (e != hipSuccess) return hip_status(e);
+  misa::TopkArgs ta{u, u_stride, nullptr, k_prime, N, topk, true, nullptr, nullptr,
+                    cand, k_prime, idx, score};
+  return hip_status(misa::launch_topk(ta, st));
+}
+
+int32_t misa_profile_begin(int32_t capacity) {
+  if (capacity < 1) return MISA_ERR_SHAPE;
+  if (g_prof.on) (void)misa_profile_end(nullptr, nullptr, 0);
+  g_prof.ev0.assign(capacity, nullptr);
+  g_prof.ev1.assign(capacity, nullptr);
+  g_prof.ids.assign(capacity, -1);
+  for (int i = 0; i < capacity; ++i) {
+    hipError_t e = hipEventCreate(&g_prof.ev0[i]);
+    if (e == hipSuccess) e = hipEventCreate(&g_prof.ev1[i]);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  g_prof.cap = capacity;
+  g_prof.used = 0;
+  g_prof.pending = -1;
+  g_prof.on = true;
+  return MISA_OK;
+}
+
+int32_t misa_profile_end(int32_t* kernel_id, float* ms, int32_t max) {
+  int32_t written = 0;
+  for (int i = 0; i < g_prof.used; ++i) {
+    if (i < max && kernel_id && ms) {
+      float t = 0.f;
+      (void)hipEventSynchronize(g_prof.ev1[i]);
+      if (hipEventElapsedTime(&t, g_prof.ev0[i], g_prof.ev1[i]) != hipSuccess) t = -1.f;
+      kernel_id[i] = g_prof.ids[i];
+      ms[i] = t;
+      ++written;
+    }
+  }
+  for (size_t i = 0; i < g_prof.ev0.size(); ++i) {
+    if (g_prof.ev0[i]) (void)hipEventDestroy(g_prof.ev0[i]);
+    if (g_prof.ev1[i]) (void)hipEventDestroy(g_prof.ev1[i]);
+  }
+  g_prof = Profiler();
+  return written;
+}
+
+const char* misa_kernel_name(int32_t kernel_id) {
+  static const char* names[misa::K_COUNT_IDS] = {
+      "pool_kernel",       "route_partial_kernel", "route_select_kernel", "topk_clear_kernel",
+      "score_mfma_kernel", "score_f32_kernel",     "score_prefill_kernel",
+      "topk_hist_kernel1", "topk_hist_kernel2",    "topk_count_kernel",   "topk_write_kernel",
+      "topk_row_kernel"};
+  if (kernel_id < 0 || kernel_id >= misa::K_COUNT_IDS) return "unknown";
+  return names[kernel_id];
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// Host-side launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace misa {
+
+enum KernelId : int {
+  K_POOL = 0,
+  K_ROUTE_PARTIAL,
+  K_ROUTE_SELECT,
+  K_CLEAR,
+  K_SCORE_MFMA,
+  K_SCORE_F32,
+  K_SCORE_PREFILL,
+  K_TOPK_HIST1,
+  K_TOPK_HIST2,
+  K_TOPK_COUNT,
+  K_TOPK_WRITE,
+  K_TOPK_ROW,
+  K_COUNT_IDS
+};
+
+// Kernel timing hooks (no-ops unless misa_profile_begin is active).
+void prof_start(hipStream_t st, int kernel_id);
+void prof_stop(hipStream_t st);
+
+#define MISA_LAUNCH(kid, kernel, grid, block, lds, st, ...)              \
+  do {                                                                   \
+    ::misa::prof_start((st), (kid));                                     \
+    hipLaunchKernelGGL((kernel), (grid), (block), (lds), (st), __VA_ARGS__); \
+    ::misa::prof_stop((st));                                             \
+  } while (0)
+
+// ---------------------------------------------------------------- pooling
+struct PoolArgs {
+  const void* k;
+  const float* k_scale;
+  int k_dt, S, L, d, B;
+  float* kbar;
+};
+hipError_t launch_pool(const PoolArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- router
+struct RouteArgs {
+  const void* q;
+  int q_dt;
+  const float* w;
+  const float* kbar;
+  const void* k;
+  const float* k_scale;
+  int k_dt;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  int N, S, L, d, B, H_I, h;
+  int32_t* heads;
+  float* head_score;
+  float* partial;        // workspace [N, nchunks, H_I]
+  int nchunks;           // chunks of full blocks per row
+};
+int route_blocks_per_chunk();
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- scoring
+struct ScoreArgs {
+  const void* q;
+  int q_dt;
+  const float* w;
+  const void* k;
+  const float* k_scale;
+  int k_dt;
+  const int32_t* q_seq;
+  const int32_t* q_pos;     // row length L_n = q_pos[n] + 1 (NULL with cand)
+  const int32_t* heads;     // [N, h] or NULL = all H_I heads
+  const int32_t* cand;      // [N, ncols] token per element, -1 = empty; NULL = identity
+  int N, S, L, d, H_I, h;
+  int ncols;                // elements per row with cand
+  uint32_t* u;              // [N, u_stride] order keys
+  int u_stride;
+  uint32_t* hist0;          // [N, kHistWords] level-0 histogram (NULL = skip)
+};
+hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- top-k
+struct TopkArgs {
+  const uint32_t* u;
+  int u_stride;
+  const int32_t* q_pos;     // row length = q_pos[n] + 1, or fixed_len if NULL
+  int fixed_len;
+  int N, topk;
+  bool one_row_per_block;
+  uint32_t* hist;           // [N, kHistWords]   (few-rows layout)
+  uint32_t* cnt;            // [N, nchunks, 2]   (few-rows layout)
+  const int32_t* cand;      // output index map (NULL = element index)
+  int cand_stride;
+  int32_t* idx;
+  float* score;
+};
+int topk_chunk();
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+hipError_t launch_clear(uint32_t* p, size_t n_words, hipStream_t st);
+
+}  // namespace misa

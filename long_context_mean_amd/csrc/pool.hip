@@ -1,0 +1,131 @@
+// Block mean-pooling of index keys, gfx950.
+//
+// MISA's router summarises the prefix by M = ceil(L/B) blocks of mean-pooled
+// index keys (MISA technical summary, gist.science, "Methodology" item 1).
+// One workgroup pools one block of one sequence: its 256 threads stream the
+// block's key rows with 16-byte loads (consecutive threads read consecutive
+// 16-byte pieces of a row, so a wavefront reads whole rows), accumulate in
+// fp32 registers, and reduce the row groups through LDS.  The pass is one
+// HBM read of the keys: bandwidth bound.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace misa {
+namespace {
+
+template <int KT>
+struct KeyTraits;
+template <>
+struct KeyTraits<DT_F32> { static constexpr int bytes = 4; };
+template <>
+struct KeyTraits<DT_BF16> { static constexpr int bytes = 2; };
+template <>
+struct KeyTraits<DT_E4M3> { static constexpr int bytes = 1; };
+
+// Unpacks one 16-byte piece into fp32 values (count 16 / bytes).
+template <int KT>
+__device__ __forceinline__ void unpack16(uint4 x, float* out) {
+  const uint32_t wds[4] = {x.x, x.y, x.z, x.w};
+  if constexpr (KT == DT_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(wds[i]);
+  } else if constexpr (KT == DT_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = bf16_lo(wds[i]);
+      out[2 * i + 1] = bf16_hi(wds[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t lo, hi;
+      e4m3x4_to_bf16x4(wds[i], lo, hi);
+      out[4 * i + 0] = bf16_lo(lo);
+      out[4 * i + 1] = bf16_hi(lo);
+      out[4 * i + 2] = bf16_lo(hi);
+      out[4 * i + 3] = bf16_hi(hi);
+    }
+  }
+}
+
+template <int KT, int D>
+__global__ __launch_bounds__(256) void pool_kernel(const uint8_t* __restrict__ k,
+                                                   const float* __restrict__ k_scale, int L,
+                                                   int B, float* __restrict__ kbar) {
+  constexpr int EB = KeyTraits<KT>::bytes;
+  constexpr int ROW_BYTES = D * EB;
+  constexpr int CPR = ROW_BYTES / 16;          // 16-byte pieces per row
+  constexpr int EPC = 16 / EB;                 // elements per piece
+  constexpr int RG = 256 / CPR;                // row groups
+  __shared__ float part[RG][D + 1];
+
+  const int b = blockIdx.x, s = blockIdx.y, M = gridDim.x;
+  const int t0 = b * B;
+  const int t1 = (t0 + B < L) ? t0 + B : L;
+  const int c = threadIdx.x % CPR, g = threadIdx.x / CPR;
+  const size_t seq_row0 = static_cast<size_t>(s) * L;
+
+  float acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+
+  constexpr int U = 4;
+  for (int t = t0 + g; t < t1; t += U * RG) {
+    uint4 x[U];
+    float sc[U];
+#pragma unroll
+    for (int r = 0; r < U; ++r) {
+      const int tt = t + r * RG;
+      const int tc = tt < t1 ? tt : t;           // stay in bounds; masked below
+      x[r] = *reinterpret_cast<const uint4*>(k + (seq_row0 + tc) * ROW_BYTES + c * 16);
+      sc[r] = 1.f;
+      if constexpr (KT == DT_E4M3) sc[r] = k_scale[seq_row0 + tc];
+    }
+#pragma unroll
+    for (int r = 0; r < U; ++r) {
+      if (t + r * RG < t1) {
+        float v[EPC];
+        unpack16<KT>(x[r], v);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          if constexpr (KT == DT_E4M3)
+            acc[e] += v[e] * sc[r];
+          else
+            acc[e] += v[e];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) part[g][c * EPC + e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float sum = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < RG; ++r) sum += part[r][threadIdx.x];
+    kbar[(static_cast<size_t>(s) * M + b) * D + threadIdx.x] = sum / static_cast<float>(t1 - t0);
+  }
+}
+
+template <int KT, int D>
+hipError_t launch_pool_t(const PoolArgs& a, hipStream_t st) {
+  const int M = (a.L + a.B - 1) / a.B;
+  MISA_LAUNCH(K_POOL, (pool_kernel<KT, D>), dim3(M, a.S), dim3(256), 0, st,
+              static_cast<const uint8_t*>(a.k), a.k_scale, a.L, a.B, a.kbar);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pool(const PoolArgs& a, hipStream_t st) {
+  if (a.d == 64) {
+    if (a.k_dt == DT_F32) return launch_pool_t<DT_F32, 64>(a, st);
+    if (a.k_dt == DT_BF16) return launch_pool_t<DT_BF16, 64>(a, st);
+    return launch_pool_t<DT_E4M3, 64>(a, st);
+  }
+  if (a.k_dt == DT_F32) return launch_pool_t<DT_F32, 128>(a, st);
+  if (a.k_dt == DT_BF16) return launch_pool_t<DT_BF16, 128>(a, st);
+  return launch_pool_t<DT_E4M3, 128>(a, st);
+}
+
+}  // namespace misa

@@ -1,0 +1,115 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point
+declared in include/misa.h, and rejects invalid arguments before touching the
+GPU (every call here returns at validation, so no device is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_mean_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "misa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("misa_pool_keys", "misa_route_heads", "misa_score_topk", "misa_rerank",
+              "dsa_score_topk", "misa_workspace_bytes", "misa_status_string"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = b.lib()
+    for f in declared_functions():
+        assert hasattr(lib, f), f"{f} not exported"
+    assert set(b.EXPORTED) <= set(declared_functions())
+
+
+def test_status_strings():
+    lib = b.lib()
+    for s in range(6):
+        assert lib.misa_status_string(s)
+    assert lib.misa_status_string(99) == b"unknown status"
+
+
+def test_workspace_sizes():
+    lib = b.lib()
+    ws = lambda *a: lib.misa_workspace_bytes(*a)
+    # decode shape: order keys + 3 histogram levels + per-chunk counts
+    n = ws(b.MISA_OP_SCORE_TOPK, 4, 131072, 128, 64, 128, 2048, 0)
+    assert n >= 4 * 131072 * 4
+    assert ws(b.MISA_OP_SCORE_TOPK, 4096, 65536, 128, 64, 128, 2048, 0) >= 4096 * 65536 * 4
+    assert ws(b.MISA_OP_RERANK, 4, 131072, 128, 64, 128, 2048, 8192) >= 4 * 8192 * 4
+    assert ws(b.MISA_OP_ROUTE, 4, 131072, 128, 64, 128, 2048, 0) >= 4 * 32 * 64 * 4
+    assert ws(b.MISA_OP_SCORE_TOPK, 0, 100, 128, 64, 128, 10, 0) == 0
+    assert ws(b.MISA_OP_ROUTE, 1, 100, 128, 64, 0, 10, 0) == 0
+    assert ws(7, 1, 100, 128, 64, 1, 10, 0) == 0
+
+
+FAKE = ctypes.c_void_p(0x100000)        # aligned, never dereferenced: validation fails first
+
+
+def _score(**over):
+    a = dict(q=FAKE, q_dt=1, w=FAKE, k=FAKE, ks=None, k_dt=1, qs=FAKE, qp=FAKE, heads=FAKE,
+             N=4, S=4, L=1000, d=128, H_I=64, h=8, topk=100, idx=FAKE, score=None, ws=FAKE,
+             ws_bytes=1 << 30)
+    a.update(over)
+    return b.lib().misa_score_topk(a["q"], a["q_dt"], a["w"], a["k"], a["ks"], a["k_dt"],
+                                   a["qs"], a["qp"], a["heads"], a["N"], a["S"], a["L"], a["d"],
+                                   a["H_I"], a["h"], a["topk"], a["idx"], a["score"], a["ws"],
+                                   a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1), (dict(heads=None), 1), (dict(idx=None), 1), (dict(ws=None), 1),
+    (dict(k_dt=2), 1),                                   # fp8 keys without scale
+    (dict(q_dt=0), 3), (dict(d=96), 3), (dict(q_dt=2, k_dt=2, ks=FAKE), 3),
+    (dict(h=0), 2), (dict(h=65), 2), (dict(H_I=65, h=8), 2), (dict(topk=0), 2),
+    (dict(N=0), 2), (dict(L=0), 2), (dict(S=0), 2), (dict(N=70000), 2),
+    (dict(q=ctypes.c_void_p(0x100004)), 2),              # misaligned
+    (dict(ws_bytes=16), 4),
+])
+def test_score_topk_rejects(over, status):
+    assert _score(**over) == status
+
+
+def test_rerank_and_route_and_pool_reject():
+    lib = b.lib()
+    # k_prime < topk
+    assert lib.misa_rerank(FAKE, 1, FAKE, FAKE, None, 1, FAKE, FAKE, FAKE, 4, 4, 1000, 128, 64,
+                           100, 200, FAKE, None, FAKE, 1 << 30, None) == 2
+    # B out of range
+    assert lib.misa_route_heads(FAKE, 1, FAKE, FAKE, FAKE, None, 1, FAKE, FAKE, 4, 4, 1000, 128,
+                                2048, 64, 8, FAKE, None, FAKE, 1 << 30, None) == 2
+    # workspace too small
+    assert lib.misa_route_heads(FAKE, 1, FAKE, FAKE, FAKE, None, 1, FAKE, FAKE, 4, 4, 100000, 128,
+                                128, 64, 8, FAKE, None, FAKE, 8, None) == 4
+    assert lib.misa_pool_keys(None, None, 1, 1, 100, 128, 16, FAKE, None) == 1
+    assert lib.misa_pool_keys(FAKE, None, 2, 1, 100, 128, 16, FAKE, None) == 1
+    assert lib.misa_pool_keys(FAKE, None, 5, 1, 100, 128, 16, FAKE, None) == 3
+    assert lib.misa_pool_keys(FAKE, None, 1, 1, 100, 128, 0, FAKE, None) == 2
+
+
+def _param_counts():
+    text = open(os.path.join(ROOT, "include", "misa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = {}
+    for m in re.finditer(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(([^)]*)\)\s*;", text, flags=re.M):
+        args = [a for a in m.group(2).split(",") if a.strip() and a.strip() != "void"]
+        out[m.group(1)] = len(args)
+    return out
+
+
+def test_binding_argument_counts_match_header():
+    lib = b.lib()
+    counts = _param_counts()
+    for name, n in counts.items():
+        fn = getattr(lib, name)
+        assert fn.argtypes is not None and len(fn.argtypes) == n, name

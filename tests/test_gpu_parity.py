@@ -1,0 +1,260 @@
+"""GPU parity: the HIP library through its C ABI against the CPU oracle.
+
+Inputs are the seeded synthetic workloads; comparisons follow tests/parity.py
+(scores within 1e-3 relative / 1e-4 absolute of the double-precision oracle;
+head and token selections identical except for swaps at near-ties; integer
+inputs bit-exact, ties included).  When the GPU routes a different head at a
+near-tie, the oracle replays the GPU's heads for the scoring check.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_mean_amd import synth
+from long_context_mean_amd.binding import DeviceProblem
+
+from parity import check_heads, check_topk, recall, tol
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def np_(t):
+    torch.cuda.synchronize()
+    return None if t is None else t.cpu().numpy()
+
+
+def misa_gpu(dp, h=None, topk=None):
+    kbar = dp.pool()
+    heads, r = dp.route(kbar, h)
+    idx, sc = dp.score_topk(heads, topk)
+    return np_(kbar), np_(heads), np_(r), np_(idx), np_(sc)
+
+
+def sub_problem(p, rows):
+    """The same keys with a subset of query rows (oracle sampling)."""
+    rows = np.asarray(rows)
+    return synth.Problem(p.name + "_rows", p.q[rows].copy(), p.q_dt, p.w[rows].copy(), p.k,
+                         p.k_dt, p.k_scale, p.q_seq[rows].copy(), p.q_pos[rows].copy(), p.B, p.h,
+                         p.topk, p.k_prime)
+
+
+def check_misa(p, h=None, topk=None, rows=None):
+    """Full MISA on GPU (pool -> route -> score+top-k) vs the oracle."""
+    h = p.h if h is None else h
+    topk = p.topk if topk is None else topk
+    log(f"[misa] {p.name} N={p.N} L={p.L} d={p.d} H_I={p.H_I} h={h} k={topk} "
+        f"k_dt={synth.DTYPE_NAMES[p.k_dt]}")
+    dp = DeviceProblem(p)
+    kbar, heads, r, idx, sc = misa_gpu(dp, h, topk)
+    ref_kbar = oracle.pool_keys(p)
+    assert np.all(np.abs(kbar - ref_kbar) <= tol(ref_kbar)), "pooled keys"
+    rows = np.arange(p.N) if rows is None else np.asarray(rows)
+    ps = sub_problem(p, rows)
+    _, ref_r = oracle.route_heads(ps, h)
+    assert np.all(np.abs(r[rows] - ref_r) <= tol(ref_r)), "router scores"
+    differing = check_heads(heads[rows], ref_r, h)
+    ref_sc = oracle.scores(ps, heads[rows])            # replay the GPU's heads
+    swapped = check_topk(idx[rows], sc[rows], ref_sc, topk, ps.visible())
+    log(f"[misa] {p.name}: head rows differing at near-ties {differing}, token swaps {swapped}")
+    return dp, heads, idx
+
+
+# ---------------------------------------------------------------- pooling
+@pytest.mark.parametrize("k_dt,L,B,d", [(synth.F32, 4096, 64, 64), (synth.BF16, 5000, 128, 128),
+                                        (synth.FP8, 3001, 100, 128), (synth.BF16, 777, 1, 64),
+                                        (synth.FP8, 1000, 1024, 64)])
+def test_pool_parity(k_dt, L, B, d):
+    q_dt = synth.F32 if k_dt == synth.F32 else synth.BF16
+    p = synth.small("pool", 7, N=1, S=3, L=L, d=d, H_I=4, h=1, B=B, q_dt=q_dt, k_dt=k_dt)
+    log(f"[pool] k_dt={k_dt} L={L} B={B} d={d}")
+    kbar = np_(DeviceProblem(p).pool())
+    ref = oracle.pool_keys(p)
+    assert kbar.shape == ref.shape
+    assert np.all(np.abs(kbar - ref) <= tol(ref) * 0.01)
+
+
+def test_fp8_decode_all_codes_exact():
+    """B = 1 pooling returns each key exactly: every finite e4m3 code decodes
+    to its OCP value (times a power-of-two scale) on the GPU."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    L, d = len(codes), 128
+    t, i = np.meshgrid(np.arange(L), np.arange(d), indexing="ij")
+    k = codes[(t + i) % L][None].copy()                      # every code at every lane slot
+    scale = np.where(np.arange(L) % 2 == 0, 0.5, 4.0).astype(np.float32)[None]
+    p = synth.Problem("codes", np.zeros((1, 1, d), np.uint16), synth.BF16,
+                      np.ones((1, 1), np.float32), k, synth.FP8, scale, np.zeros(1, np.int32),
+                      np.array([L - 1], np.int32), 1, 1, 1)
+    kbar = np_(DeviceProblem(p).pool())
+    assert np.array_equal(kbar.astype(np.float64), oracle.pool_keys(p))
+
+
+# ---------------------------------------------------------------- full MISA, small shapes
+@pytest.mark.parametrize("case", [
+    dict(N=3, S=2, L=3000, d=128, H_I=64, h=8, B=128, topk=300),
+    dict(N=2, S=2, L=5000, d=64, H_I=32, h=8, B=64, topk=1000),          # GLM-5-like H_I
+    dict(N=4, S=1, L=2500, d=128, H_I=16, h=16, B=32, topk=2600),        # k > L_n
+    dict(N=2, S=2, L=4097, d=128, H_I=64, h=1, B=128, topk=50),
+    dict(N=5, S=1, L=9000, d=128, H_I=64, h=12, B=128, topk=2048,
+         q_pos=np.array([0, 1, 127, 128, 8999], np.int32)),               # ragged causal rows
+])
+@pytest.mark.parametrize("k_dt", [synth.BF16, synth.FP8])
+def test_misa_small(case, k_dt):
+    case = dict(case)
+    p = synth.small("small", 17, k_dt=k_dt, **case)
+    check_misa(p)
+
+
+def test_misa_c1_fp32():
+    check_misa(synth.make("c1"))
+
+
+def test_misa_many_rows_prefill_layout():
+    """300 causal rows over one prefix (one workgroup per row in the top-k)."""
+    L = 20000
+    pos = np.sort(np.random.default_rng(3).choice(L, 300, replace=False)).astype(np.int32)
+    p = synth.small("rows", 19, N=300, S=1, L=L, d=128, H_I=64, h=8, B=128, topk=512,
+                    q_pos=pos, q_seq=np.zeros(300, np.int32))
+    check_misa(p, rows=np.r_[0:8, 150:154, 292:300])
+
+
+# ---------------------------------------------------------------- exactness
+@pytest.mark.parametrize("k_dt,q_dt", [(synth.BF16, synth.BF16), (synth.FP8, synth.BF16),
+                                       (synth.F32, synth.F32)])
+def test_integer_inputs_bit_exact(k_dt, q_dt):
+    """Small-integer q, k, w: all dot products and head sums are exact in
+    fp32, so the GPU must match the oracle bit for bit, ties included (with
+    B = 1 the router sums are exact integers too)."""
+    p = synth.integer_problem("int", 5, N=3, S=2, L=3000, d=128 if k_dt != synth.F32 else 64,
+                              H_I=16, h=5, B=1, topk=700, q_dt=q_dt, k_dt=k_dt,
+                              q_pos=np.array([2999, 1500, 4], np.int32))
+    dp = DeviceProblem(p)
+    kbar, heads, r, idx, sc = misa_gpu(dp)
+    ref_heads, ref_r = oracle.route_heads(p)
+    assert np.array_equal(r.astype(np.float64), ref_r)
+    assert np.array_equal(heads, ref_heads)
+    ref_sc = oracle.scores(p, ref_heads)
+    check_topk(idx, sc, ref_sc, p.topk, p.visible(), exact=True)
+    didx, dsc = dp.dsa()
+    check_topk(np_(didx), np_(dsc), oracle.scores(p, None), p.topk, p.visible(), exact=True)
+
+
+def test_all_heads_routed_equals_dense_on_gpu():
+    """h = H_I routes every head; the GPU routed path and the GPU dense path
+    must return identical bytes."""
+    p = synth.small("hall", 23, N=3, S=3, L=6000, H_I=32, h=32, topk=500)
+    dp = DeviceProblem(p)
+    kbar = dp.pool()
+    heads, _ = dp.route(kbar)
+    assert np.array_equal(np_(heads), np.tile(np.arange(32), (3, 1)))
+    a_idx, a_sc = dp.score_topk(heads)
+    b_idx, b_sc = dp.dsa()
+    assert np.array_equal(np_(a_idx), np_(b_idx)) and np.array_equal(np_(a_sc), np_(b_sc))
+
+
+def test_determinism():
+    p = synth.small("det", 29, N=4, S=4, L=40000, H_I=64, h=8, topk=2048)
+    dp = DeviceProblem(p)
+    outs = [tuple(x.tobytes() for x in misa_gpu(dp)) for _ in range(2)]
+    assert outs[0] == outs[1]
+
+
+# ---------------------------------------------------------------- dense DSA and MISA-dagger
+@pytest.mark.parametrize("k_dt", [synth.BF16, synth.FP8])
+def test_dsa_parity(k_dt):
+    p = synth.small("dsa", 31, N=3, S=3, L=7000, H_I=64, h=8, topk=777, k_dt=k_dt,
+                    q_pos=np.array([6999, 3000, 100], np.int32))
+    idx, sc = DeviceProblem(p).dsa()
+    check_topk(np_(idx), np_(sc), oracle.scores(p, None), p.topk, p.visible())
+
+
+@pytest.mark.parametrize("k_dt", [synth.BF16, synth.FP8])
+def test_misa_dagger_parity(k_dt):
+    p = synth.small("dag", 37, N=3, S=3, L=20000, H_I=64, h=8, topk=300, k_prime=1200,
+                    k_dt=k_dt, q_pos=np.array([19999, 5000, 700], np.int32))
+    dp = DeviceProblem(p)
+    kbar = dp.pool()
+    heads, _ = dp.route(kbar)
+    cand, _ = dp.score_topk(heads, p.k_prime)
+    idx, sc = dp.rerank(cand)
+    cand_np = np_(cand)
+    ref_full = oracle.scores(p, None)
+    masked = np.full_like(ref_full, -np.inf)
+    for n in range(p.N):
+        c = cand_np[n][cand_np[n] >= 0]
+        masked[n, c] = ref_full[n, c]
+    check_topk(np_(idx), np_(sc), masked, p.topk, (cand_np >= 0).sum(1), cand=cand_np)
+
+
+def test_misa_dagger_wide_candidates_equal_dense():
+    """k' >= L_n: every token is a candidate, so MISA-dagger returns the dense
+    set; on the GPU both use the same all-head arithmetic, so bytes match."""
+    p = synth.small("dagw", 41, N=2, S=2, L=3000, H_I=64, h=4, topk=200, k_prime=3000)
+    dp = DeviceProblem(p)
+    heads, _ = dp.route(dp.pool())
+    cand, _ = dp.score_topk(heads, 3000)
+    idx, sc = dp.rerank(cand)
+    didx, dsc = dp.dsa()
+    assert np.array_equal(np_(idx), np_(didx)) and np.array_equal(np_(sc), np_(dsc))
+
+
+# ---------------------------------------------------------------- the named workloads at full size
+def test_c2_decode_batch():
+    p = synth.make("c2")
+    dp, heads, idx = check_misa(p)
+    didx, dsc = dp.dsa()
+    check_topk(np_(didx), np_(dsc), oracle.scores(p, None), p.topk, p.visible())
+    log(f"[c2] recall of dense top-k by MISA h=8: {recall(idx, np_(didx)):.4f}")
+
+
+@pytest.mark.parametrize("h", [4, 8, 16])
+def test_c4_long_decode_needles(h):
+    p = synth.make("c4")
+    dp, heads, idx = check_misa(p, h=h)
+    if h == 8:
+        didx, dsc = dp.dsa()
+        didx = np_(didx)
+        check_topk(didx, np_(dsc), oracle.scores(p, None), p.topk, p.visible())
+        needles = [np.mean(np.isin(p.needles[n, :, 0], a[a >= 0])) for n, a in enumerate(idx)]
+        dneedles = [np.mean(np.isin(p.needles[n, :, 0], a[a >= 0])) for n, a in enumerate(didx)]
+        log(f"[c4] recall vs dense {recall(idx, didx):.4f}; needle recall MISA "
+            f"{np.mean(needles):.3f} dense {np.mean(dneedles):.3f}")
+
+
+def test_c5_misa_dagger_fp8():
+    p = synth.make("c5")
+    dp = DeviceProblem(p)
+    kbar = dp.pool()
+    heads, r = dp.route(kbar)
+    _, ref_r = oracle.route_heads(p)
+    check_heads(np_(heads), ref_r, p.h)
+    cand, _ = dp.score_topk(heads, p.k_prime)
+    cand_np = np_(cand)
+    ref_coarse = oracle.scores(p, np_(heads))
+    check_topk(cand_np, None, ref_coarse, p.k_prime, p.visible())
+    idx, sc = dp.rerank(cand)
+    ref_full = oracle.scores(p, None)
+    masked = np.full_like(ref_full, -np.inf)
+    for n in range(p.N):
+        masked[n, cand_np[n]] = ref_full[n, cand_np[n]]
+    check_topk(np_(idx), np_(sc), masked, p.topk, np.full(p.N, p.k_prime), cand=cand_np)
+    didx, dsc = dp.dsa()
+    check_topk(np_(didx), np_(dsc), ref_full, p.topk, p.visible())
+    log(f"[c5] MISA-dagger recall of dense top-k {recall(np_(idx), np_(didx)):.4f}")
+
+
+def test_c3_prefill_chunk_sampled_rows():
+    p = synth.make("c3")
+    rows = np.r_[0:3, 127:130, 2047:2049, 4093:4096]
+    check_misa(p, rows=rows)

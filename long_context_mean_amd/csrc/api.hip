@@ -49,7 +49,7 @@ int32_t check_sizes(int32_t N, int32_t S, int32_t L, int32_t d, int32_t H_I) {
 struct TopkLayout {
   bool one_row = false;
   int u_stride = 0;
-  size_t off_hist = 0, off_cnt = 0, bytes = 0;
+  size_t off_hist = 0, bytes = 0;
 };
 
 TopkLayout topk_layout(int N, int len_max) {
@@ -60,9 +60,7 @@ TopkLayout topk_layout(int N, int len_max) {
   size_t off = align_up(static_cast<size_t>(N) * t.u_stride * 4, 256);
   if (!t.one_row) {
     t.off_hist = off;
-    off = align_up(off + static_cast<size_t>(N) * misa::kHistWords * 4, 256);
-    t.off_cnt = off;
-    off = align_up(off + static_cast<size_t>(N) * (t.u_stride / chunk) * 2 * 4, 256);
+    off = align_up(off + misa::topk_few_rows_bytes(N, t.u_stride), 256);
   }
   t.bytes = off;
   return t;
@@ -106,7 +104,6 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* w, const void*
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint32_t* u = reinterpret_cast<uint32_t*>(base);
   uint32_t* hist = lay.one_row ? nullptr : reinterpret_cast<uint32_t*>(base + lay.off_hist);
-  uint32_t* cnt = lay.one_row ? nullptr : reinterpret_cast<uint32_t*>(base + lay.off_cnt);
   hipError_t e = hipSuccess;
   if (hist) e = misa::launch_clear(hist, static_cast<size_t>(N) * misa::kHistWords, st);
   if (e != hipSuccess) return hip_status(e);
@@ -114,7 +111,7 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* w, const void*
                      N, S, L, d, H_I, h, 0, u, lay.u_stride, hist};
   e = misa::launch_score(sa, st);
   if (e != hipSuccess) return hip_status(e);
-  misa::TopkArgs ta{u, lay.u_stride, q_pos, 0, N, topk, lay.one_row, hist, cnt,
+  misa::TopkArgs ta{u, lay.u_stride, q_pos, 0, N, topk, lay.one_row, hist,
                     nullptr, 0, idx, score};
   return hip_status(misa::launch_topk(ta, st));
 }
@@ -246,7 +243,7 @@ int32_t misa_rerank(const void* q, int32_t q_dt, const float* w, const void* k,
                      N, S, L, d, H_I, H_I, k_prime, u, u_stride, nullptr};
   hipError_t e = misa::launch_score(sa, st);
   if (e != hipSuccess) return hip_status(e);
-  misa::TopkArgs ta{u, u_stride, nullptr, k_prime, N, topk, true, nullptr, nullptr,
+  misa::TopkArgs ta{u, u_stride, nullptr, k_prime, N, topk, true, nullptr,
                     cand, k_prime, idx, score};
   return hip_status(misa::launch_topk(ta, st));
 }
@@ -293,8 +290,7 @@ const char* misa_kernel_name(int32_t kernel_id) {
   static const char* names[misa::K_COUNT_IDS] = {
       "pool_kernel",       "route_partial_kernel", "route_select_kernel", "topk_clear_kernel",
       "score_mfma_kernel", "score_f32_kernel",     "score_prefill_kernel",
-      "topk_hist_kernel1", "topk_hist_kernel2",    "topk_count_kernel",   "topk_write_kernel",
-      "topk_row_kernel"};
+      "topk_collect_kernel", "topk_final_kernel",   "topk_row_kernel"};
   if (kernel_id < 0 || kernel_id >= misa::K_COUNT_IDS) return "unknown";
   return names[kernel_id];
 }

@@ -13,7 +13,10 @@ constexpr int kDigit0Bits = 12, kDigit1Bits = 12, kDigit2Bits = 8;
 constexpr int kBins0 = 1 << kDigit0Bits, kBins1 = 1 << kDigit1Bits, kBins2 = 1 << kDigit2Bits;
 constexpr int kShift0 = 32 - kDigit0Bits;                 // 20
 constexpr int kShift1 = kShift0 - kDigit1Bits;            // 8
-constexpr int kHistWords = kBins0 + kBins1 + kBins2;      // per row, in the workspace
+// Per-row words of the level-0 histogram region in the workspace: 4096 bins,
+// then the candidate count, padded to keep rows 256-byte aligned.
+constexpr int kHistWords = kBins0 + 64;
+constexpr int kCandCountOffset = kBins0;
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
@@ -32,6 +35,41 @@ __device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t codes, uint32_t& lo, u
   bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true);
   lo = __builtin_bit_cast(uint32_t, a);
   hi = __builtin_bit_cast(uint32_t, b);
+}
+
+template <int KT>
+struct KeyBytes;
+template <>
+struct KeyBytes<DT_F32> { static constexpr int value = 4; };
+template <>
+struct KeyBytes<DT_BF16> { static constexpr int value = 2; };
+template <>
+struct KeyBytes<DT_E4M3> { static constexpr int value = 1; };
+
+// Unpacks one 16-byte piece of key storage into 16 / bytes fp32 values.
+template <int KT>
+__device__ __forceinline__ void unpack16(uint4 x, float* out) {
+  const uint32_t wds[4] = {x.x, x.y, x.z, x.w};
+  if constexpr (KT == DT_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(wds[i]);
+  } else if constexpr (KT == DT_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = bf16_lo(wds[i]);
+      out[2 * i + 1] = bf16_hi(wds[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t lo, hi;
+      e4m3x4_to_bf16x4(wds[i], lo, hi);
+      out[4 * i + 0] = bf16_lo(lo);
+      out[4 * i + 1] = bf16_hi(lo);
+      out[4 * i + 2] = bf16_lo(hi);
+      out[4 * i + 3] = bf16_hi(hi);
+    }
+  }
 }
 
 // Total order on fp32 scores as unsigned keys: larger score <-> larger key,

@@ -15,10 +15,8 @@ enum KernelId : int {
   K_SCORE_MFMA,
   K_SCORE_F32,
   K_SCORE_PREFILL,
-  K_TOPK_HIST1,
-  K_TOPK_HIST2,
-  K_TOPK_COUNT,
-  K_TOPK_WRITE,
+  K_TOPK_COLLECT,
+  K_TOPK_FINAL,
   K_TOPK_ROW,
   K_COUNT_IDS
 };
@@ -91,14 +89,14 @@ struct TopkArgs {
   int fixed_len;
   int N, topk;
   bool one_row_per_block;
-  uint32_t* hist;           // [N, kHistWords]   (few-rows layout)
-  uint32_t* cnt;            // [N, nchunks, 2]   (few-rows layout)
+  uint32_t* hist;           // few-rows layout: [N, kHistWords] | bitmap | candidates
   const int32_t* cand;      // output index map (NULL = element index)
   int cand_stride;
   int32_t* idx;
   float* score;
 };
 int topk_chunk();
+size_t topk_few_rows_bytes(int N, int u_stride);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 hipError_t launch_clear(uint32_t* p, size_t n_words, hipStream_t st);
 

@@ -13,46 +13,11 @@
 namespace misa {
 namespace {
 
-template <int KT>
-struct KeyTraits;
-template <>
-struct KeyTraits<DT_F32> { static constexpr int bytes = 4; };
-template <>
-struct KeyTraits<DT_BF16> { static constexpr int bytes = 2; };
-template <>
-struct KeyTraits<DT_E4M3> { static constexpr int bytes = 1; };
-
-// Unpacks one 16-byte piece into fp32 values (count 16 / bytes).
-template <int KT>
-__device__ __forceinline__ void unpack16(uint4 x, float* out) {
-  const uint32_t wds[4] = {x.x, x.y, x.z, x.w};
-  if constexpr (KT == DT_F32) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(wds[i]);
-  } else if constexpr (KT == DT_BF16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      out[2 * i] = bf16_lo(wds[i]);
-      out[2 * i + 1] = bf16_hi(wds[i]);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t lo, hi;
-      e4m3x4_to_bf16x4(wds[i], lo, hi);
-      out[4 * i + 0] = bf16_lo(lo);
-      out[4 * i + 1] = bf16_hi(lo);
-      out[4 * i + 2] = bf16_lo(hi);
-      out[4 * i + 3] = bf16_hi(hi);
-    }
-  }
-}
-
 template <int KT, int D>
 __global__ __launch_bounds__(256) void pool_kernel(const uint8_t* __restrict__ k,
                                                    const float* __restrict__ k_scale, int L,
                                                    int B, float* __restrict__ kbar) {
-  constexpr int EB = KeyTraits<KT>::bytes;
+  constexpr int EB = KeyBytes<KT>::value;
   constexpr int ROW_BYTES = D * EB;
   constexpr int CPR = ROW_BYTES / 16;          // 16-byte pieces per row
   constexpr int EPC = 16 / EB;                 // elements per piece
@@ -69,7 +34,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint8_t* __restrict__ k
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
 
-  constexpr int U = 4;
+  constexpr int U = 8;
   for (int t = t0 + g; t < t1; t += U * RG) {
     uint4 x[U];
     float sc[U];

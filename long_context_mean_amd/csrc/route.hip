@@ -8,16 +8,15 @@
 // the row are read from the pooled table; the row's partial last block (when
 // L_n is not a multiple of B) is the mean of its visible keys only.
 //
-// Two kernels:
-//  route_partial: grid (chunk of 32 full blocks, row).  The row's query heads
-//    (fp32, padded rows) and the chunk's pooled keys sit in LDS; each lane
-//    owns one head and walks four blocks at a time, so a q element read from
-//    LDS feeds four FMAs.  Partial sums go to the workspace (no float
-//    atomics: the final sum is taken in a fixed order and is deterministic).
+//  route_partial: grid (chunk of 32 full blocks, row).  Lane j of every
+//    wavefront holds head j's query row in registers (fp32); the chunk's
+//    pooled keys sit in LDS and are read as broadcasts, each wavefront taking
+//    every fourth block.  Per-chunk sums go to the workspace (no float
+//    atomics: the final sum runs in a fixed order and is deterministic).
 //  route_select: one workgroup per row.  Sums the chunk partials, adds the
-//    partial-block term, applies |w|, and picks the top-h heads with
-//    wavefront reductions (ties -> lower head index); heads are written
-//    ascending.
+//    partial-block term, applies |w|, and routes every head that fewer than
+//    h heads beat under (r desc, head index asc); heads are written in
+//    ascending order.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -26,27 +25,23 @@ namespace {
 
 constexpr int kRouteBlocks = 32;     // pooled blocks per route_partial workgroup
 
-template <int QT>
-__device__ __forceinline__ float load_q(const void* q, size_t i) {
-  if constexpr (QT == DT_F32)
-    return static_cast<const float*>(q)[i];
-  else
-    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(q)[i]) << 16);
-}
-
-template <int KT>
-__device__ __forceinline__ float load_key(const void* k, const float* k_scale, size_t row, int D,
-                                          int i) {
-  if constexpr (KT == DT_F32) {
-    return static_cast<const float*>(k)[row * D + i];
-  } else if constexpr (KT == DT_BF16) {
-    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(k)[row * D + i])
-                           << 16);
+// Head row (D values) of q into registers as fp32.
+template <int QT, int D>
+__device__ __forceinline__ void load_q_row(const void* q, size_t row, float (&out)[D]) {
+  if constexpr (QT == DT_F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q) + row * D);
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) {
+      const float4 x = p[i];
+      out[4 * i] = x.x;
+      out[4 * i + 1] = x.y;
+      out[4 * i + 2] = x.z;
+      out[4 * i + 3] = x.w;
+    }
   } else {
-    const uint32_t code = static_cast<const uint8_t*>(k)[row * D + i];
-    uint32_t lo, hi;
-    e4m3x4_to_bf16x4(code, lo, hi);
-    return bf16_lo(lo) * k_scale[row];
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + row * D);
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) unpack16<DT_BF16>(p[i], &out[8 * i]);
   }
 }
 
@@ -55,9 +50,8 @@ __global__ __launch_bounds__(256) void route_partial_kernel(
     const void* __restrict__ q, const float* __restrict__ kbar, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int L, int B, int H_I, int nchunks,
     float* __restrict__ partial) {
-  __shared__ float q_lds[64][D + 1];
-  __shared__ float kb_lds[kRouteBlocks][D + 4];
-  __shared__ float red[4 * 64];
+  __shared__ __align__(16) float kb_lds[kRouteBlocks][D];
+  __shared__ float red[4][64];
 
   const int n = blockIdx.y, chunk = blockIdx.x;
   const int Ln = q_pos[n] + 1;
@@ -71,46 +65,45 @@ __global__ __launch_bounds__(256) void route_partial_kernel(
     return;
   }
   const int s = q_seq[n];
-  for (int e = threadIdx.x; e < H_I * D; e += 256)
-    q_lds[e / D][e % D] = load_q<QT>(q, static_cast<size_t>(n) * H_I * D + e);
   const int nb = b1 - b0;
-  for (int e = threadIdx.x; e < nb * D; e += 256)
-    kb_lds[e / D][e % D] = kbar[(static_cast<size_t>(s) * M + b0) * D + e];
+  // all loads in flight at once: pooled keys of the chunk, then the head row
+  constexpr int NF = kRouteBlocks * D / 4 / 256;      // float4 per thread
+  const float4* src = reinterpret_cast<const float4*>(kbar + (static_cast<size_t>(s) * M + b0) * D);
+  float4 tmp[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int e = threadIdx.x + f * 256;
+    tmp[f] = e < nb * D / 4 ? src[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float qr[D];
+  if (lane < H_I) load_q_row<QT, D>(q, static_cast<size_t>(n) * H_I + lane, qr);
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+    reinterpret_cast<float4*>(&kb_lds[0][0])[threadIdx.x + f * 256] = tmp[f];
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int G = 64 / H_I;                      // lane groups per wave
-  const int j = lane % H_I, sub = lane / H_I;
-  const bool active = sub < G;
-  const int slot = wave * G + sub;             // 0 .. 4G-1
-  const int nslots = 4 * G;
   float acc = 0.f;
-  if (active) {
-    for (int bb = slot * 4; bb < nb; bb += nslots * 4) {
-      float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
-      const int r1 = bb + 1 < nb ? bb + 1 : bb, r2 = bb + 2 < nb ? bb + 2 : bb,
-                r3 = bb + 3 < nb ? bb + 3 : bb;
-#pragma unroll 8
-      for (int i = 0; i < D; ++i) {
-        const float qv = q_lds[j][i];
-        d0 += qv * kb_lds[bb][i];
-        d1 += qv * kb_lds[r1][i];
-        d2 += qv * kb_lds[r2][i];
-        d3 += qv * kb_lds[r3][i];
+  if (lane < H_I) {
+    for (int b = wave; b < nb; b += 8) {
+      const int b2 = b + 4 < nb ? b + 4 : b;
+      float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < D; i += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(&kb_lds[b][i]);
+        const float4 y = *reinterpret_cast<const float4*>(&kb_lds[b2][i]);
+        d0 += qr[i] * x.x + qr[i + 1] * x.y + qr[i + 2] * x.z + qr[i + 3] * x.w;
+        d1 += qr[i] * y.x + qr[i + 1] * y.y + qr[i + 2] * y.z + qr[i + 3] * y.w;
       }
       acc += fmaxf(d0, 0.f);
-      if (bb + 1 < nb) acc += fmaxf(d1, 0.f);
-      if (bb + 2 < nb) acc += fmaxf(d2, 0.f);
-      if (bb + 3 < nb) acc += fmaxf(d3, 0.f);
+      if (b + 4 < nb) acc += fmaxf(d1, 0.f);
     }
   }
-  if (active) red[slot * H_I + j] = acc;          // nslots * H_I <= 256
+  red[wave][lane] = acc;
   __syncthreads();
-  for (int jj = threadIdx.x; jj < H_I; jj += 256) {
-    float sum = 0.f;
-    for (int sl = 0; sl < nslots; ++sl) sum += red[sl * H_I + jj];
-    out[jj] = sum;
-  }
+  if (threadIdx.x < H_I)
+    out[threadIdx.x] = (red[0][threadIdx.x] + red[1][threadIdx.x]) +
+                       (red[2][threadIdx.x] + red[3][threadIdx.x]);
 }
 
 template <int QT, int KT, int D>
@@ -120,8 +113,14 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     const int32_t* __restrict__ q_pos, int L, int B, int H_I, int h, int nchunks,
     const float* __restrict__ partial, int32_t* __restrict__ heads,
     float* __restrict__ head_score) {
-  __shared__ float psum[256];
+  constexpr int EB = KeyBytes<KT>::value;
+  constexpr int PIECES = D * EB / 16;          // 16-byte pieces per key row
+  constexpr int EPP = 16 / EB;                 // elements per piece
+  constexpr int RG = 256 / PIECES;             // key rows per pass
+  __shared__ float psum[RG][D + 1];
   __shared__ float mean[D];
+  __shared__ float red[4][64];
+  __shared__ float rs[64];
 
   const int n = blockIdx.x;
   const int Ln = q_pos[n] + 1;
@@ -129,60 +128,82 @@ __global__ __launch_bounds__(256) void route_select_kernel(
   const int cp = Ln - Mf * B;                 // visible keys of the partial block
   const int s = q_seq[n];
 
+  // chunk partial sums: 4 groups of 64 threads, 8 loads in flight per pass,
+  // fixed summation order
+  {
+    const int j = threadIdx.x & 63, g = threadIdx.x >> 6;
+    float a = 0.f;
+    if (j < H_I) {
+      const float* pp = partial + static_cast<size_t>(n) * nchunks * H_I + j;
+      for (int c0 = g; c0 < nchunks; c0 += 32) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int c = c0 + 4 * u;
+          v[u] = c < nchunks ? pp[static_cast<size_t>(c) * H_I] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a += v[u];
+      }
+    }
+    red[g][j] = a;
+  }
   // partial-block mean over the row's visible keys of that block
   if (cp > 0) {
-    constexpr int SUBS = 256 / D;
-    const int i = threadIdx.x % D, sub = threadIdx.x / D;
-    float acc = 0.f;
-    for (int t = Mf * B + sub; t < Ln; t += SUBS)
-      acc += load_key<KT>(k, k_scale, static_cast<size_t>(s) * L + t, D, i);
-    psum[threadIdx.x] = acc;
-    __syncthreads();
-    if (threadIdx.x < D) {
-      float m = 0.f;
+    const int piece = threadIdx.x % PIECES, rg = threadIdx.x / PIECES;
+    float acc[EPP];
 #pragma unroll
-      for (int sb = 0; sb < SUBS; ++sb) m += psum[sb * D + threadIdx.x];
-      mean[threadIdx.x] = m / static_cast<float>(cp);
+    for (int e = 0; e < EPP; ++e) acc[e] = 0.f;
+    const uint8_t* kb = static_cast<const uint8_t*>(k);
+    for (int t = Mf * B + rg; t < Ln; t += RG) {
+      const size_t row = static_cast<size_t>(s) * L + t;
+      const uint4 x = *reinterpret_cast<const uint4*>(kb + row * (D * EB) + piece * 16);
+      float v[EPP];
+      unpack16<KT>(x, v);
+      const float sc = (KT == DT_E4M3) ? k_scale[row] : 1.f;
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) acc[e] += (KT == DT_E4M3) ? v[e] * sc : v[e];
     }
-    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPP; ++e) psum[rg][piece * EPP + e] = acc[e];
   }
+  __syncthreads();
+  if (cp > 0 && threadIdx.x < D) {
+    float m = 0.f;
+    for (int r = 0; r < RG; ++r) m += psum[r][threadIdx.x];
+    mean[threadIdx.x] = m / static_cast<float>(cp);
+  }
+  __syncthreads();
 
   if (threadIdx.x < 64) {
     const int j = threadIdx.x;
     float r = -1.f;
     if (j < H_I) {
-      float a = 0.f;
-      const float* pp = partial + static_cast<size_t>(n) * nchunks * H_I + j;
-      for (int c = 0; c < nchunks; ++c) a += pp[static_cast<size_t>(c) * H_I];
+      float a = (red[0][j] + red[1][j]) + (red[2][j] + red[3][j]);
       if (cp > 0) {
+        float qr[D];
+        load_q_row<QT, D>(q, static_cast<size_t>(n) * H_I + j, qr);
         float dt = 0.f;
-        const size_t qb = (static_cast<size_t>(n) * H_I + j) * D;
-        for (int i = 0; i < D; ++i) dt += load_q<QT>(q, qb + i) * mean[i];
+#pragma unroll
+        for (int i = 0; i < D; ++i) dt += qr[i] * mean[i];
         a += fmaxf(dt, 0.f);
       }
       r = fabsf(w[static_cast<size_t>(n) * H_I + j]) * a;
       if (head_score) head_score[static_cast<size_t>(n) * H_I + j] = r;
     }
-    // top-h: h rounds of a wavefront arg-max (ties -> lower head index)
-    float v = r;
-    bool chosen = false;
-    for (int it = 0; it < h; ++it) {
-      float bv = v;
-      int bj = j;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oj = __shfl_xor(bj, o, 64);
-        if (ov > bv || (ov == bv && oj < bj)) {
-          bv = ov;
-          bj = oj;
-        }
-      }
-      if (bj == j) {
-        chosen = true;
-        v = -2.f;
+    // top-h: a head is routed when fewer than h heads beat it under
+    // (r desc, head index asc); the 64 scores sit in LDS for the ranking
+    rs[j] = r;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    int rank = 0;
+    if (j < H_I) {
+      for (int o = 0; o < H_I; ++o) {
+        const float ro = rs[o];
+        rank += (ro > r || (ro == r && o < j)) ? 1 : 0;
       }
     }
+    const bool chosen = j < H_I && rank < h;
     const uint64_t mask = __ballot(chosen);
     if (chosen) {
       const int pos = __popcll(mask & ((1ull << j) - 1ull));

@@ -8,9 +8,11 @@
 // keys.  The row's heads form the A operand of v_mfma_f32_16x16x32_bf16
 // (16 head rows per tile, zero-padded), 16 keys form the B operand, so one
 // MFMA per 32 elements of d yields 16 heads x 16 keys of dot products in fp32
-// from exact bf16 products.  Keys go straight from global memory into the B
-// registers: each lane reads d/4 contiguous elements of one key row (a
-// wavefront reads 16 whole rows per tile), four tiles in flight per wave.
+// from exact bf16 products.  Keys are read with flat 16-byte loads (a load
+// instruction covers whole key rows) into two register buffers that
+// ping-pong, so the next group of tiles is in flight while the current one is
+// scored; each tile passes through a small padded wavefront-private LDS tile
+// that turns rows into the MFMA operand layout without bank conflicts.
 // fp8 keys are widened to bf16 in registers (exact) and their per-token
 // scale is applied to the fp32 dot before the ReLU.  The epilogue applies
 // ReLU, multiplies by the head weight and sums the heads (4 rows per lane, 2
@@ -20,6 +22,8 @@
 //
 // score_f32_kernel (fp32 keys): one thread per key, plain FMAs (fp32 inputs
 // have no exact low-precision MFMA form).
+#include <cstdlib>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -48,13 +52,24 @@ template <int KT, int D>
 struct KeyLayout {
   static constexpr int EB = KT == DT_E4M3 ? 1 : 2;     // bytes per element
   static constexpr int ROW = D * EB;                   // bytes per key row
-  static constexpr int LANE_BYTES = ROW / 4;           // bytes per lane (d/4 elements)
-  static constexpr int NLOAD = LANE_BYTES / 16;        // 16-byte loads per lane per tile
+  static constexpr int NLOAD = ROW / 64;               // 16-byte pieces per lane per tile
   static constexpr int KK = D / 32;                    // MFMAs per head tile
+  static constexpr int LANES_PER_ROW = ROW / 16;       // flat load: lanes covering one row
+  static constexpr int ROWS_PER_LOAD = 64 / LANES_PER_ROW;
+  static constexpr int LDS_STRIDE = ROW + 16;          // padded row stride of the LDS tile
+  static constexpr int TILE_LDS = 16 * LDS_STRIDE;
 };
 
-// B fragments for one tile: lane (g = lane/16, c = lane%16) holds elements
-// [g*d/4, (g+1)*d/4) of key row c, split in KK pieces of 8.
+// d-elements that lane group g (= lane / 16) feeds to MFMA kk, as the first
+// of 8 consecutive elements.  Load p of a lane reads bytes [64p + 16g, +16)
+// of its key row, so one load instruction covers 64 contiguous bytes of each
+// of 16 rows; the query fragments use the same assignment (the contraction
+// order over d is free).
+template <int KT>
+__device__ __forceinline__ constexpr int elem_off(int g, int kk) {
+  return KT == DT_E4M3 ? 64 * (kk >> 1) + 16 * g + 8 * (kk & 1) : 32 * kk + 8 * g;
+}
+
 template <int KT, int D>
 __device__ __forceinline__ void to_fragments(const u32x4_t (&raw)[KeyLayout<KT, D>::NLOAD],
                                              bf16x8_t (&b)[KeyLayout<KT, D>::KK]) {
@@ -63,10 +78,10 @@ __device__ __forceinline__ void to_fragments(const u32x4_t (&raw)[KeyLayout<KT, 
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) b[kk] = __builtin_bit_cast(bf16x8_t, raw[kk]);
   } else {
-    // 8 codes (2 words) per piece -> 4 packed bf16 words
+    // load p holds 16 codes: the first 8 feed MFMA 2p, the last 8 MFMA 2p+1
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const u32x4_t& r = raw[kk / 2];
+      const u32x4_t& r = raw[kk >> 1];
       const uint32_t w0 = (kk & 1) ? r.z : r.x;
       const uint32_t w1 = (kk & 1) ? r.w : r.y;
       u32x4_t o;
@@ -82,26 +97,134 @@ __device__ __forceinline__ void to_fragments(const u32x4_t (&raw)[KeyLayout<KT, 
   }
 }
 
-template <int KT, int NT, int D>
+// Issues the key loads of U tiles (16 elements each) starting at element e0;
+// bit t of the returned mask is set when tile t's element is a valid token.
+template <int KT, int D, int U>
+using RawGroup = u32x4_t[U][KeyLayout<KT, D>::NLOAD];
+
+// Issues the key loads of U tiles (16 elements each) starting at element e0.
+// Without a candidate list the key address depends only on the element
+// index, so no load waits on another load; bit t of the result is set when
+// tile t's element is a valid token.
+template <int KT, int D, int U, bool CAND>
+__device__ __forceinline__ uint32_t issue_group(RawGroup<KT, D, U>& raw, float* sc, int tile0,
+                                                int tstride, int lane, int c, int len,
+                                                const int32_t* crow, const uint8_t* kseq,
+                                                const float* sseq) {
+  using LY = KeyLayout<KT, D>;
+  const int rsub = lane / LY::LANES_PER_ROW, q = lane % LY::LANES_PER_ROW;
+  uint32_t valid = 0;
+#pragma unroll
+  for (int t = 0; t < U; ++t) {
+    const int te = (tile0 + t * tstride) * 16;
+    // flat: load i of lane l reads 16 bytes of row i*ROWS_PER_LOAD + l/LANES_PER_ROW
+#pragma unroll
+    for (int i = 0; i < LY::NLOAD; ++i) {
+      const int e = te + i * LY::ROWS_PER_LOAD + rsub;
+      int tok = -1;
+      if (e < len) tok = CAND ? crow[e] : e;
+      const int tt = tok >= 0 ? tok : 0;
+      raw[t][i] = *reinterpret_cast<const u32x4_t*>(kseq + static_cast<size_t>(tt) * LY::ROW +
+                                                     16 * q);
+    }
+    const int e = te + c;
+    int tok = -1;
+    if (e < len) tok = CAND ? crow[e] : e;
+    valid |= tok >= 0 ? (1u << t) : 0u;
+    sc[t] = (KT == DT_E4M3) ? sseq[tok >= 0 ? tok : 0] : 1.f;
+  }
+  return valid;
+}
+
+template <int KT, int NT, int D, int U>
+__device__ __forceinline__ void score_group(const RawGroup<KT, D, U>& raw, const float* sc,
+                                            uint32_t valid, int tile0, int tstride, uint8_t* tile,
+                                            int lane,
+                                            const bf16x8_t (&a)[NT][KeyLayout<KT, D>::KK],
+                                            const float (&wv)[NT][4], int g, int c, int len,
+                                            uint32_t* urow, uint32_t* lh, bool do_hist) {
+  using LY = KeyLayout<KT, D>;
+  constexpr int KK = LY::KK;
+  const int rsub = lane / LY::LANES_PER_ROW, q = lane % LY::LANES_PER_ROW;
+#pragma unroll
+  for (int t = 0; t < U; ++t) {
+    // rows in through the wavefront's padded LDS tile, operand pieces out
+    // (LDS operations of one wavefront execute in order)
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < LY::NLOAD; ++i)
+      *reinterpret_cast<u32x4_t*>(tile + (i * LY::ROWS_PER_LOAD + rsub) * LY::LDS_STRIDE +
+                                  16 * q) = raw[t][i];
+    __builtin_amdgcn_wave_barrier();
+    u32x4_t pieces[LY::NLOAD];
+#pragma unroll
+    for (int p = 0; p < LY::NLOAD; ++p)
+      pieces[p] = *reinterpret_cast<const u32x4_t*>(tile + c * LY::LDS_STRIDE + 64 * p + 16 * g);
+    bf16x8_t b[KK];
+    to_fragments<KT, D>(pieces, b);
+    float part = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[nt][kk], b[kk], acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = acc[i];
+        if (KT == DT_E4M3) v *= sc[t];
+        part += wv[nt][i] * fmaxf(v, 0.f);
+      }
+    }
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    const int e = (tile0 + t * tstride) * 16 + c;
+    if (g == 0 && e < len) {
+      const bool ok = (valid >> t) & 1u;
+      const uint32_t key = ok ? order_key(part) : 0u;
+      urow[e] = key;
+      if (do_hist && ok) atomicAdd(&lh[key >> kShift0], 1u);
+    }
+  }
+}
+
+template <int KT, int NT, int D, int U, bool CAND>
 __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
   using LY = KeyLayout<KT, D>;
   constexpr int KK = LY::KK;
-  constexpr int NLOAD = LY::NLOAD;
-  constexpr int U = 4;                                 // tiles in flight per wave
   __shared__ uint32_t lh[kBins0];
+  __shared__ __align__(16) uint8_t tiles[4][LY::TILE_LDS];
 
   const int n = blockIdx.y;
-  const int len = p.cand ? p.ncols : p.q_pos[n] + 1;
-  const int tiles_per_wg = 4 * p.tiles_per_wave;
-  const int chunk0 = blockIdx.x * tiles_per_wg * 16;
-  if (chunk0 >= len) return;
+  const int len = CAND ? p.ncols : p.q_pos[n] + 1;
+  // tiles of 16 elements are dealt round-robin to the row's wavefronts, so at
+  // any moment the whole grid streams one compact stretch of the keys
+  const int ntiles = (len + 15) / 16;
+  const int tstride = gridDim.x * 4;                 // wavefronts per row
+  if (static_cast<int>(blockIdx.x) * 4 >= ntiles) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
   const bool do_hist = p.hist0 != nullptr;
+
+  const int s = p.q_seq[n];
+  const uint8_t* kseq = p.k + static_cast<size_t>(s) * p.L * LY::ROW;
+  uint8_t* tile = tiles[wave];
+  const float* sseq = (KT == DT_E4M3) ? p.k_scale + static_cast<size_t>(s) * p.L : nullptr;
+  const int32_t* crow = CAND ? p.cand + static_cast<size_t>(n) * p.ncols : nullptr;
+  uint32_t* urow = p.u + static_cast<size_t>(n) * p.u_stride;
+  const int wtile = blockIdx.x * 4 + wave;            // this wavefront's first tile
+  const int wtiles = wtile < ntiles ? (ntiles - wtile + tstride - 1) / tstride : 0;
+
+  // first key group in flight before anything else
+  u32x4_t ra[U][LY::NLOAD], rb[U][LY::NLOAD];
+  float sa[U], sb[U];
+  uint32_t va = 0, vb = 0;
+  if (wtiles > 0)
+    va = issue_group<KT, D, U, CAND>(ra, sa, wtile, tstride, lane, c, len, crow, kseq, sseq);
+
   if (do_hist) {
     for (int b = threadIdx.x; b < kBins0; b += 256) lh[b] = 0u;
   }
-
   // A operand: head rows of this query row; W: weights of this lane's D rows.
   bf16x8_t a[NT][KK];
   float wv[NT][4];
@@ -111,11 +234,10 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
     int j = 0;
     const bool rv = r < p.nrows;
     if (rv) j = p.heads ? p.heads[static_cast<size_t>(n) * p.nrows + r] : r;
-    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(
-        p.q + (static_cast<size_t>(n) * p.H_I + j) * D + g * (D / 4));
+    const uint16_t* qrow = p.q + (static_cast<size_t>(n) * p.H_I + j) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      u32x4_t x = qp[kk];
+      u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + elem_off<KT>(g, kk));
       if (!rv) x = u32x4_t{0u, 0u, 0u, 0u};
       a[nt][kk] = __builtin_bit_cast(bf16x8_t, x);
     }
@@ -130,59 +252,38 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
       wv[nt][i] = wf;
     }
   }
-  const int s = p.q_seq[n];
-  const uint8_t* kseq = p.k + static_cast<size_t>(s) * p.L * LY::ROW + g * LY::LANE_BYTES;
-  const float* sseq = (KT == DT_E4M3) ? p.k_scale + static_cast<size_t>(s) * p.L : nullptr;
-  const int32_t* crow = p.cand ? p.cand + static_cast<size_t>(n) * p.ncols : nullptr;
-  uint32_t* urow = p.u + static_cast<size_t>(n) * p.u_stride;
   if (do_hist) __syncthreads();
 
-  const int wave_e0 = chunk0 + wave * p.tiles_per_wave * 16;
-  for (int tb = 0; tb < p.tiles_per_wave; tb += U) {
-    if (wave_e0 + tb * 16 >= len) break;
-    u32x4_t raw[U][NLOAD];
-    float sc[U];
-    int ev[U];
-    bool valid[U];
-#pragma unroll
-    for (int t = 0; t < U; ++t) {
-      const int e = wave_e0 + (tb + t) * 16 + c;
-      int tok = -1;
-      if (e < len) tok = crow ? crow[e] : e;
-      ev[t] = e;
-      valid[t] = tok >= 0;
-      const int tt = tok >= 0 ? tok : 0;
-      const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(kseq + static_cast<size_t>(tt) * LY::ROW);
-#pragma unroll
-      for (int i = 0; i < NLOAD; ++i) raw[t][i] = kp[i];
-      sc[t] = (KT == DT_E4M3) ? sseq[tt] : 1.f;
+  // ping-pong over two register buffers: the next group's loads are in
+  // flight while the current group is scored.  Loads in the steady-state
+  // loop are unconditional (elements past the row end read token 0 and are
+  // masked), so the compiler's wait counts never drain the prefetch.
+  if (wtiles > 0) {
+    int t0 = wtile;                                    // first tile of the current group
+    const int gstep = U * tstride;                     // tiles between consecutive groups
+    int left = (wtiles + U - 1) / U;                   // groups left, current included
+    while (left >= 3) {
+      vb = issue_group<KT, D, U, CAND>(rb, sb, t0 + gstep, tstride, lane, c, len, crow, kseq,
+                                       sseq);
+      score_group<KT, NT, D, U>(ra, sa, va, t0, tstride, tile, lane, a, wv, g, c, len, urow,
+                                lh, do_hist);
+      va = issue_group<KT, D, U, CAND>(ra, sa, t0 + 2 * gstep, tstride, lane, c, len, crow,
+                                       kseq, sseq);
+      score_group<KT, NT, D, U>(rb, sb, vb, t0 + gstep, tstride, tile, lane, a, wv, g, c, len,
+                                urow, lh, do_hist);
+      t0 += 2 * gstep;
+      left -= 2;
     }
-#pragma unroll
-    for (int t = 0; t < U; ++t) {
-      bf16x8_t b[KK];
-      to_fragments<KT, D>(raw[t], b);
-      float part = 0.f;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[nt][kk], b[kk], acc, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = acc[i];
-          if (KT == DT_E4M3) v *= sc[t];
-          part += wv[nt][i] * fmaxf(v, 0.f);
-        }
-      }
-      part += __shfl_xor(part, 16, 64);
-      part += __shfl_xor(part, 32, 64);
-      const int e = ev[t];
-      if (g == 0 && e < len) {
-        const uint32_t key = valid[t] ? order_key(part) : 0u;
-        urow[e] = key;
-        if (do_hist && valid[t]) atomicAdd(&lh[key >> kShift0], 1u);
-      }
+    if (left == 2) {
+      vb = issue_group<KT, D, U, CAND>(rb, sb, t0 + gstep, tstride, lane, c, len, crow, kseq,
+                                       sseq);
+      score_group<KT, NT, D, U>(ra, sa, va, t0, tstride, tile, lane, a, wv, g, c, len, urow,
+                                lh, do_hist);
+      score_group<KT, NT, D, U>(rb, sb, vb, t0 + gstep, tstride, tile, lane, a, wv, g, c, len,
+                                urow, lh, do_hist);
+    } else {
+      score_group<KT, NT, D, U>(ra, sa, va, t0, tstride, tile, lane, a, wv, g, c, len, urow,
+                                lh, do_hist);
     }
   }
   if (do_hist) {
@@ -260,6 +361,7 @@ __global__ __launch_bounds__(256) void score_f32_kernel(
 
 template <int KT, int NT, int D>
 hipError_t launch_mfma(const ScoreArgs& a, hipStream_t st, int tiles_per_wave) {
+  constexpr int U = 2;                                 // tiles per group (two groups in flight)
   ScoreParams p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.w = a.w;
@@ -280,8 +382,12 @@ hipError_t launch_mfma(const ScoreArgs& a, hipStream_t st, int tiles_per_wave) {
   const int maxlen = a.cand ? a.ncols : a.L;
   const int per_wg = 4 * tiles_per_wave * 16;
   const int nchunks = (maxlen + per_wg - 1) / per_wg;
-  MISA_LAUNCH(K_SCORE_MFMA, (score_mfma_kernel<KT, NT, D>), dim3(nchunks, a.N), dim3(256), 0,
-              st, p);
+  if (a.cand)
+    MISA_LAUNCH(K_SCORE_MFMA, (score_mfma_kernel<KT, NT, D, U, true>), dim3(nchunks, a.N),
+                dim3(256), 0, st, p);
+  else
+    MISA_LAUNCH(K_SCORE_MFMA, (score_mfma_kernel<KT, NT, D, U, false>), dim3(nchunks, a.N),
+                dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -292,6 +398,11 @@ hipError_t launch_mfma_rows(const ScoreArgs& a, hipStream_t st, int tpw) {
   if (nrows <= 32) return launch_mfma<KT, 2, D>(a, st, tpw);
   if (nrows <= 48) return launch_mfma<KT, 3, D>(a, st, tpw);
   return launch_mfma<KT, 4, D>(a, st, tpw);
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : dflt;
 }
 
 }  // namespace
@@ -313,8 +424,11 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
                   a.hist0);
     return hipGetLastError();
   }
-  // short candidate lists: smaller chunks so more workgroups share the gather
-  const int tpw = a.cand ? 4 : 16;
+  // tiles (of 16 keys) per wavefront; short candidate lists use smaller
+  // chunks so more workgroups share the gather.  MISA_SCORE_TPW overrides
+  // (launch-shape tuning only).
+  static const int tpw_env = env_int("MISA_SCORE_TPW", 0);
+  const int tpw = tpw_env > 0 ? tpw_env : (a.cand ? 4 : 16);
   if (a.k_dt == DT_BF16)
     return a.d == 64 ? launch_mfma_rows<DT_BF16, 64>(a, st, tpw)
                      : launch_mfma_rows<DT_BF16, 128>(a, st, tpw);

@@ -1,48 +1,76 @@
 // Exact top-k selection over fp32 index scores, gfx950.
 //
 // Scores arrive as 32-bit order keys (order_key: larger score <-> larger key,
-// -0 == +0, key 0 = empty slot).  The k-th largest key T is found by a
-// three-level radix select (12 + 12 + 8 bit digits) over per-row histograms;
-// the selected set is {key > T} plus the first K2 tokens (lowest index) with
-// key == T, which realises the order (score desc, token index asc) exactly.
-// Results are written in ascending index order by an ordered compaction
-// (per-thread runs + workgroup scans), so outputs are deterministic.
+// -0 == +0, key 0 = empty slot).  The wanted set is the min(k, valid) keys
+// first under (key desc, index asc).  With T the k-th largest key and K2 the
+// number of key == T elements that make the cut, the set is {key > T} plus
+// the K2 lowest-index elements with key == T.  T is found by radix select on
+// 12 + 12 + 8 bit digits; outputs are written in ascending index order, so
+// results are deterministic.
 //
-// Two layouts share the device code:
-//  - few long rows (decode): a grid of 4096-element chunks per row; the
-//    level-0 histogram comes from the scoring kernel, levels 1-2 and the
-//    per-chunk counts go through global memory;
-//  - many rows, or short rows (prefill, rerank): one 1024-thread workgroup
-//    per row keeps every histogram in LDS.
+// Few long rows (decode): the scoring kernel has already built each row's
+// level-0 histogram (top 12 key bits).
+//  topk_collect (grid: 4096-element chunks x rows) finds the bin d0 holding
+//    the k-th key; elements above it are certain winners and are recorded in
+//    a bitmap (each chunk writes its own words, no atomics); elements in bin
+//    d0 are appended to a short candidate list.
+//  topk_final (one 1024-thread workgroup per row) loads the bitmap and the
+//    candidates into LDS, resolves the exact threshold among the candidates
+//    with two more radix levels, marks the candidate winners in the bitmap
+//    and emits every marked element in index order.  When the candidates do
+//    not fit in LDS (heavily tied scores) or the row is very long, the same
+//    workgroup falls back to a full radix select over the row.
+// Many rows or short rows (prefill, rerank): topk_row, one 1024-thread
+//    workgroup per row with every histogram in LDS.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace misa {
 namespace {
 
-constexpr int kChunk = 4096;          // elements per workgroup (few-rows layout)
+constexpr int kChunk = 4096;          // elements per collect workgroup
 constexpr int kPerThread = 16;        // contiguous elements per thread per tile
+constexpr int kCandCap = 8192;        // candidates resolved in LDS
+constexpr int kBitmapWords = 8192;    // rows up to 262144 elements use the LDS bitmap
 
-struct Digit {
-  uint32_t digit, rank;   // rank (1-based) of the wanted key inside the digit's bin
-};
-
-// Scans histogram `hist` (nbins bins, highest bin first) and finds the bin that
-// holds the K-th largest element.  With clamp_total, K = min(K, total count)
-// first.  Must be called by all NT threads; results in LDS `res` ([0] digit,
-// [1] rank, [2] K, [3] total).  K == 0 leaves digit/rank at 0.
-template <int NT>
-__device__ void find_digit(const uint32_t* hist, int nbins, uint32_t K, bool clamp_total,
-                           uint32_t* sm, uint32_t* res) {
-  const int per = (nbins + NT - 1) / NT;
-  const int hi = nbins - static_cast<int>(threadIdx.x) * per;
-  const int lo = hi - per > 0 ? hi - per : 0;
+// Finds the bin of a histogram (NBINS bins, bin NBINS-1 = largest keys) that
+// holds the K-th largest element.  With clamp_total, K = min(K, total) first.
+// All NT threads call it; results in `res`: [0] digit, [1] rank inside the
+// digit's bin (1-based), [2] K, [3] total.  K == 0 leaves digit/rank 0.
+template <int NT, int NBINS>
+__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t K, bool clamp_total, uint32_t* sm,
+                           uint32_t* res) {
+  constexpr int PER = NBINS >= NT ? NBINS / NT : 1;
+  const int t = static_cast<int>(threadIdx.x);
+  const bool owner = NBINS >= NT || t < NBINS;
+  const int lo = NBINS - (t + 1) * PER;                 // this thread's lowest bin
+  uint32_t v[PER];
+  if (owner) {
+    if constexpr (PER % 4 == 0) {
+      const uint4* p4 = reinterpret_cast<const uint4*>(hist + lo);
+#pragma unroll
+      for (int q = 0; q < PER / 4; ++q) {
+        const uint4 x = p4[q];
+        v[4 * q] = x.x;
+        v[4 * q + 1] = x.y;
+        v[4 * q + 2] = x.z;
+        v[4 * q + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < PER; ++q) v[q] = hist[lo + q];
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) v[q] = 0u;
+  }
   uint32_t c = 0;
-  for (int b = hi - 1; b >= lo; --b) c += hist[b];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) c += v[q];
   uint32_t total;
   const uint32_t above = block_excl_scan<NT>(c, sm, total);
   if (clamp_total && K > total) K = total;
-  if (threadIdx.x == 0) {
+  if (t == 0) {
     res[0] = 0;
     res[1] = 0;
     res[2] = K;
@@ -51,14 +79,13 @@ __device__ void find_digit(const uint32_t* hist, int nbins, uint32_t K, bool cla
   __syncthreads();
   if (K > 0 && above < K && K <= above + c) {
     uint32_t acc = above;
-    for (int b = hi - 1; b >= lo; --b) {
-      const uint32_t hb = hist[b];
-      if (acc + hb >= K) {
-        res[0] = static_cast<uint32_t>(b);
+#pragma unroll
+    for (int q = PER - 1; q >= 0; --q) {
+      if (acc < K && acc + v[q] >= K) {
+        res[0] = static_cast<uint32_t>(lo + q);
         res[1] = K - acc;
-        break;
       }
-      acc += hb;
+      acc += v[q];
     }
   }
   __syncthreads();
@@ -70,38 +97,12 @@ struct Threshold {
   uint32_t K;     // number selected = min(topk, valid elements)
 };
 
-// Derives the threshold from the three histogram levels (all NT threads).
-template <int NT>
-__device__ Threshold derive_threshold(const uint32_t* h0, const uint32_t* h1, const uint32_t* h2,
-                                      uint32_t topk, uint32_t* sm, uint32_t* res) {
-  Threshold th;
-  find_digit<NT>(h0, kBins0, topk, true, sm, res);
-  th.K = res[2];
-  const uint32_t d0 = res[0], r0 = res[1];
-  __syncthreads();
-  if (th.K == 0) {
-    th.T = 0xFFFFFFFFu;
-    th.K2 = 0;
-    return th;
-  }
-  find_digit<NT>(h1, kBins1, r0, false, sm, res);
-  const uint32_t d1 = res[0], r1 = res[1];
-  __syncthreads();
-  find_digit<NT>(h2, kBins2, r1, false, sm, res);
-  const uint32_t d2 = res[0], r2 = res[1];
-  __syncthreads();
-  th.T = (d0 << kShift0) | (d1 << kShift1) | d2;
-  th.K2 = r2;
-  return th;
-}
-
 __device__ __forceinline__ int row_len(const int32_t* q_pos, int fixed_len, int n) {
   return q_pos ? q_pos[n] + 1 : fixed_len;
 }
 
-// Loads 16 consecutive keys starting at element i0 (row stride is a multiple
-// of the chunk size, so the loads stay inside the buffer); keys at or past
-// `len` read as 0 (empty).
+// 16 consecutive keys from element i0 (buffers are padded to whole chunks, so
+// the loads stay in bounds); keys at or past `len` read as 0 (empty).
 __device__ __forceinline__ void load16(const uint32_t* row, int i0, int len, uint32_t (&v)[16]) {
   const uint4* p = reinterpret_cast<const uint4*>(row + i0);
 #pragma unroll
@@ -117,13 +118,12 @@ __device__ __forceinline__ void load16(const uint32_t* row, int i0, int len, uin
     if (i0 + j >= len) v[j] = 0u;
 }
 
-// Histogram of digit `level` over elements [i_begin, i_end) of a row that
-// match the higher digits in `prefix`, accumulated into LDS `lh` (NT threads).
+// LDS histogram of digit LEVEL over the row's elements [0, span) whose higher
+// digits equal `prefix` (NT threads).
 template <int NT, int LEVEL>
-__device__ void hist_range(const uint32_t* row, int i_begin, int i_end, int len, uint32_t prefix,
+__device__ __forceinline__ void hist_range(const uint32_t* row, int span, int len, uint32_t prefix,
                            uint32_t* lh) {
-  for (int i0 = i_begin + static_cast<int>(threadIdx.x) * kPerThread; i0 < i_end;
-       i0 += NT * kPerThread) {
+  for (int i0 = static_cast<int>(threadIdx.x) * kPerThread; i0 < span; i0 += NT * kPerThread) {
     uint32_t v[16];
     load16(row, i0, len, v);
 #pragma unroll
@@ -141,17 +141,17 @@ __device__ void hist_range(const uint32_t* row, int i_begin, int i_end, int len,
   }
 }
 
-// Ordered compaction of elements [i_begin, i_end): writes the selected
-// elements to out positions starting at `offset`, in index order.  eq_before
-// is the number of key == T elements before i_begin in the row.
+// Ordered compaction of the row's elements [0, span) against threshold th:
+// writes the selected elements, in index order, to idx_row/score_row.
 template <int NT>
-__device__ void compact_range(const uint32_t* row, int i_begin, int i_end, int len, Threshold th,
-                              uint32_t offset, uint32_t eq_before, const int32_t* cand_row,
-                              int32_t* idx_row, float* score_row, uint32_t* sm) {
-  for (int t0 = i_begin; t0 < i_end; t0 += NT * kPerThread) {
+__device__ __forceinline__ void compact_row(const uint32_t* row, int span, int len, Threshold th,
+                            const int32_t* cand_row, int32_t* idx_row, float* score_row,
+                            uint32_t* sm) {
+  uint32_t offset = 0, eq_before = 0;
+  for (int t0 = 0; t0 < span; t0 += NT * kPerThread) {
     const int i0 = t0 + static_cast<int>(threadIdx.x) * kPerThread;
     uint32_t v[16];
-    if (i0 < i_end) {
+    if (i0 < span) {
       load16(row, i0, len, v);
     } else {
 #pragma unroll
@@ -161,13 +161,13 @@ __device__ void compact_range(const uint32_t* row, int i_begin, int i_end, int l
 #pragma unroll
     for (int j = 0; j < 16; ++j) n_eq += (v[j] == th.T) ? 1u : 0u;
     uint32_t eq_tot;
-    uint32_t eq_rank = eq_before + block_excl_scan<NT>(n_eq, sm, eq_tot);
+    const uint32_t eq_rank = eq_before + block_excl_scan<NT>(n_eq, sm, eq_tot);
     uint32_t sel_mask = 0, n_sel = 0;
     {
       uint32_t r = eq_rank;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const bool gt = v[j] > th.T && v[j] != 0u;
+        const bool gt = v[j] > th.T;
         const bool eq = v[j] == th.T;
         const bool sel = gt || (eq && r < th.K2);
         r += eq ? 1u : 0u;
@@ -191,120 +191,215 @@ __device__ void compact_range(const uint32_t* row, int i_begin, int i_end, int l
   }
 }
 
-// ---------------------------------------------------------------- few rows
-__global__ __launch_bounds__(256) void topk_hist_kernel(const uint32_t* __restrict__ u,
-                                                        int u_stride, const int32_t* q_pos,
-                                                        int fixed_len, uint32_t* hist,
-                                                        int topk, int level) {
-  __shared__ uint32_t lh[kBins1];
+// Full single-workgroup selection over one row (three LDS histogram levels
+// and an ordered compaction).  h0 may already hold the level-0 histogram
+// (have_h0); h0/h1 hold 4096 words, h2 256 words, all in LDS.
+template <int NT>
+__device__ __forceinline__ void row_select(const uint32_t* row, int len, int topk, const int32_t* cand_row,
+                           int32_t* idx_row, float* score_row, uint32_t* h0, uint32_t* h1,
+                           uint32_t* h2, bool have_h0, uint32_t* sm, uint32_t* res) {
+  const int span = (len + kPerThread - 1) / kPerThread * kPerThread;
+  for (int b = threadIdx.x; b < kBins0; b += NT) {
+    if (!have_h0) h0[b] = 0u;
+    h1[b] = 0u;
+  }
+  for (int b = threadIdx.x; b < kBins2; b += NT) h2[b] = 0u;
+  __syncthreads();
+  if (!have_h0) {
+    hist_range<NT, 0>(row, span, len, 0u, h0);
+    __syncthreads();
+  }
+  find_digit<NT, kBins0>(h0, static_cast<uint32_t>(topk), true, sm, res);
+  const uint32_t K = res[2], d0 = res[0], r0 = res[1];
+  __syncthreads();
+  for (int i = static_cast<int>(K) + threadIdx.x; i < topk; i += NT) {
+    idx_row[i] = -1;
+    if (score_row) score_row[i] = -__builtin_inff();
+  }
+  if (K == 0) return;
+  hist_range<NT, 1>(row, span, len, d0, h1);
+  __syncthreads();
+  find_digit<NT, kBins1>(h1, r0, false, sm, res);
+  const uint32_t d1 = res[0], r1 = res[1];
+  __syncthreads();
+  hist_range<NT, 2>(row, span, len, (d0 << kDigit1Bits) | d1, h2);
+  __syncthreads();
+  find_digit<NT, kBins2>(h2, r1, false, sm, res);
+  Threshold th;
+  th.K = K;
+  th.T = (d0 << kShift0) | (d1 << kShift1) | res[0];
+  th.K2 = res[1];
+  __syncthreads();
+  compact_row<NT>(row, span, len, th, cand_row, idx_row, score_row, sm);
+}
+
+// ---------------------------------------------------------------- few long rows
+__global__ __launch_bounds__(256) void topk_collect_kernel(
+    const uint32_t* __restrict__ u, int u_stride, const int32_t* __restrict__ q_pos,
+    int fixed_len, uint32_t* hist, uint32_t* __restrict__ bitmap, uint2* __restrict__ clist,
+    int topk) {
   __shared__ uint32_t sm[4];
   __shared__ uint32_t res[4];
+  __shared__ uint32_t base_slot;
   const int n = blockIdx.y;
   const int len = row_len(q_pos, fixed_len, n);
   const int base = blockIdx.x * kChunk;
   if (base >= len) return;
   uint32_t* h0 = hist + static_cast<size_t>(n) * kHistWords;
-  uint32_t* h1 = h0 + kBins0;
-  uint32_t* h2 = h1 + kBins1;
-  find_digit<256>(h0, kBins0, static_cast<uint32_t>(topk), true, sm, res);
-  const uint32_t K = res[2], d0 = res[0], r0 = res[1];
-  __syncthreads();
+  find_digit<256, kBins0>(h0, static_cast<uint32_t>(topk), true, sm, res);
+  const uint32_t K = res[2], d0 = res[0];
   if (K == 0) return;
-  uint32_t prefix = d0;
-  const int nb = level == 1 ? kBins1 : kBins2;
-  if (level == 2) {
-    find_digit<256>(h1, kBins1, r0, false, sm, res);
-    prefix = (d0 << kDigit1Bits) | res[0];
-  }
-  for (int b = threadIdx.x; b < nb; b += 256) lh[b] = 0u;
-  __syncthreads();
   const uint32_t* row = u + static_cast<size_t>(n) * u_stride;
-  const int end = base + kChunk;
-  if (level == 1)
-    hist_range<256, 1>(row, base, end, len, prefix, lh);
-  else
-    hist_range<256, 2>(row, base, end, len, prefix, lh);
-  __syncthreads();
-  uint32_t* dst = level == 1 ? h1 : h2;
-  for (int b = threadIdx.x; b < nb; b += 256) {
-    const uint32_t c = lh[b];
-    if (c) atomicAdd(&dst[b], c);
-  }
-}
-
-__global__ __launch_bounds__(256) void topk_count_kernel(const uint32_t* __restrict__ u,
-                                                         int u_stride, const int32_t* q_pos,
-                                                         int fixed_len, const uint32_t* hist,
-                                                         uint32_t* cnt, int nchunks, int topk) {
-  __shared__ uint32_t sm[4];
-  __shared__ uint32_t res[4];
-  const int n = blockIdx.y;
-  const int len = row_len(q_pos, fixed_len, n);
-  const int base = blockIdx.x * kChunk;
-  uint32_t* my = cnt + (static_cast<size_t>(n) * nchunks + blockIdx.x) * 2;
-  if (base >= len) {
-    if (threadIdx.x == 0) my[0] = my[1] = 0u;
-    return;
-  }
-  const uint32_t* h0 = hist + static_cast<size_t>(n) * kHistWords;
-  const Threshold th = derive_threshold<256>(h0, h0 + kBins0, h0 + kBins0 + kBins1,
-                                             static_cast<uint32_t>(topk), sm, res);
-  const uint32_t* row = u + static_cast<size_t>(n) * u_stride;
-  uint32_t gt = 0, eq = 0;
   const int i0 = base + threadIdx.x * kPerThread;
-  if (th.K > 0) {
-    uint32_t v[16];
-    load16(row, i0, len, v);
+  uint32_t v[16];
+  load16(row, i0, len, v);
+  uint32_t sure = 0, n_cand = 0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      gt += (v[j] > th.T && v[j] != 0u) ? 1u : 0u;
-      eq += (v[j] == th.T) ? 1u : 0u;
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t dg = v[j] >> kShift0;
+    sure |= (v[j] != 0u && dg > d0) ? (1u << j) : 0u;
+    n_cand += (v[j] != 0u && dg == d0) ? 1u : 0u;
+  }
+  // bitmap word = 32 elements = this thread's 16 bits and its odd neighbour's
+  const uint32_t other = __shfl_xor(sure, 1, 64);
+  if ((threadIdx.x & 1) == 0)
+    bitmap[static_cast<size_t>(n) * (u_stride / 32) + (i0 >> 5)] = sure | (other << 16);
+  uint32_t tot;
+  uint32_t off = block_excl_scan<256>(n_cand, sm, tot);
+  if (threadIdx.x == 0) base_slot = tot ? atomicAdd(&h0[kCandCountOffset], tot) : 0u;
+  __syncthreads();
+  off += base_slot;
+  uint2* cl = clist + static_cast<size_t>(n) * kCandCap;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (v[j] != 0u && (v[j] >> kShift0) == d0) {
+      if (off < kCandCap) cl[off] = make_uint2(v[j], static_cast<uint32_t>(i0 + j));
+      ++off;
     }
   }
-  gt = block_sum<256>(gt, sm);
-  eq = block_sum<256>(eq, sm);
-  if (threadIdx.x == 0) {
-    my[0] = gt;
-    my[1] = eq;
-  }
 }
 
-__global__ __launch_bounds__(256) void topk_write_kernel(
-    const uint32_t* __restrict__ u, int u_stride, const int32_t* q_pos, int fixed_len,
-    const uint32_t* hist, const uint32_t* cnt, int nchunks, int topk,
-    const int32_t* __restrict__ cand, int cand_stride, int32_t* __restrict__ idx,
+__global__ __launch_bounds__(1024) void topk_final_kernel(
+    const uint32_t* __restrict__ u, int u_stride, const int32_t* __restrict__ q_pos,
+    int fixed_len, const uint32_t* hist, const uint32_t* __restrict__ bitmap,
+    const uint2* __restrict__ clist, int topk, int32_t* __restrict__ idx,
     float* __restrict__ score) {
-  __shared__ uint32_t sm[4];
+  __shared__ __align__(16) uint32_t bm[kBitmapWords];   // winners, one bit per element
+  __shared__ __align__(16) uint32_t cu[kCandCap];       // candidate order key
+  __shared__ __align__(16) uint32_t ci[kCandCap];       // candidate element index
+  __shared__ __align__(16) uint32_t hA[kBins0];
+  __shared__ __align__(16) uint32_t hB[kBins2];
+  __shared__ uint32_t sm[16];
   __shared__ uint32_t res[4];
-  const int n = blockIdx.y;
-  const int c = blockIdx.x;
+  const int n = blockIdx.x;
   const int len = row_len(q_pos, fixed_len, n);
-  const int base = c * kChunk;
-  const uint32_t* h0 = hist + static_cast<size_t>(n) * kHistWords;
-  const Threshold th = derive_threshold<256>(h0, h0 + kBins0, h0 + kBins0 + kBins1,
-                                             static_cast<uint32_t>(topk), sm, res);
+  const uint32_t* row = u + static_cast<size_t>(n) * u_stride;
+  const uint32_t* h0g = hist + static_cast<size_t>(n) * kHistWords;
   int32_t* idx_row = idx + static_cast<size_t>(n) * topk;
   float* score_row = score ? score + static_cast<size_t>(n) * topk : nullptr;
-  if (c == 0) {
-    for (int i = static_cast<int>(th.K) + threadIdx.x; i < topk; i += 256) {
-      idx_row[i] = -1;
-      if (score_row) score_row[i] = -__builtin_inff();
+  const int nwords = (len + 31) / 32;
+
+  find_digit<1024, kBins0>(h0g, static_cast<uint32_t>(topk), true, sm, res);
+  const uint32_t K = res[2], d0 = res[0], r0 = res[1];
+  const uint32_t c = h0g[kCandCountOffset];
+  __syncthreads();
+  bool fallback = c > static_cast<uint32_t>(kCandCap) || nwords > kBitmapWords;
+  uint32_t T = 0, K2 = 0, n_eq = 0;
+  if (!fallback && K > 0) {
+    // certain winners (bitmap) and the candidates of bin d0 into LDS
+    const uint32_t* bmg = bitmap + static_cast<size_t>(n) * (u_stride / 32);
+    for (int w = 4 * threadIdx.x; w < nwords; w += 4 * 1024) {
+      if (w + 3 < nwords) {
+        *reinterpret_cast<uint4*>(&bm[w]) = *reinterpret_cast<const uint4*>(bmg + w);
+      } else {
+        for (int q = 0; q < 4 && w + q < nwords; ++q) bm[w + q] = bmg[w + q];
+      }
     }
+    const uint2* cl = clist + static_cast<size_t>(n) * kCandCap;
+    for (int i = threadIdx.x; i < static_cast<int>(c); i += 1024) {
+      const uint2 e = cl[i];
+      cu[i] = e.x;
+      ci[i] = e.y;
+    }
+    for (int b = threadIdx.x; b < kBins1; b += 1024) hA[b] = 0u;
+    if (threadIdx.x < kBins2) hB[threadIdx.x] = 0u;
+    __syncthreads();
+    // exact threshold among the candidates: digits 1 and 2 (rank r0)
+    for (int i = threadIdx.x; i < static_cast<int>(c); i += 1024)
+      atomicAdd(&hA[(cu[i] >> kShift1) & (kBins1 - 1)], 1u);
+    __syncthreads();
+    find_digit<1024, kBins1>(hA, r0, false, sm, res);
+    const uint32_t d1 = res[0], r1 = res[1];
+    __syncthreads();
+    const uint32_t pre = (d0 << kDigit1Bits) | d1;
+    for (int i = threadIdx.x; i < static_cast<int>(c); i += 1024)
+      if ((cu[i] >> kShift1) == pre) atomicAdd(&hB[cu[i] & (kBins2 - 1)], 1u);
+    __syncthreads();
+    find_digit<1024, kBins2>(hB, r1, false, sm, res);
+    T = (d0 << kShift0) | (d1 << kShift1) | res[0];
+    K2 = res[1];
+    n_eq = hB[res[0]];                    // candidates whose key equals T
+    __syncthreads();
+    // ties beyond what the quadratic rank below handles: use the full path
+    fallback = n_eq != K2 && n_eq > 2048u;
   }
-  if (base >= len || th.K == 0) return;
-  uint32_t gt_b = 0, eq_b = 0;
-  const uint32_t* my = cnt + static_cast<size_t>(n) * nchunks * 2;
-  for (int j = threadIdx.x; j < c; j += 256) {
-    gt_b += my[2 * j];
-    eq_b += my[2 * j + 1];
+  if (fallback) {
+    for (int b = threadIdx.x; b < kBins0; b += 1024) hA[b] = h0g[b];
+    __syncthreads();
+    row_select<1024>(row, len, topk, nullptr, idx_row, score_row, hA, cu, hB, true, sm, res);
+    return;
   }
-  gt_b = block_sum<256>(gt_b, sm);
-  eq_b = block_sum<256>(eq_b, sm);
-  const uint32_t offset = gt_b + (eq_b < th.K2 ? eq_b : th.K2);
-  const uint32_t* row = u + static_cast<size_t>(n) * u_stride;
-  const int32_t* cand_row = cand ? cand + static_cast<size_t>(n) * cand_stride : nullptr;
-  compact_range<256>(row, base, base + kChunk, len, th, offset, eq_b, cand_row, idx_row,
-                     score_row, sm);
+  for (int i = static_cast<int>(K) + threadIdx.x; i < topk; i += 1024) {
+    idx_row[i] = -1;
+    if (score_row) score_row[i] = -__builtin_inff();
+  }
+  if (K == 0) return;
+
+  // mark the candidate winners: key > T, or key == T among the K2 lowest
+  // indices (all ties win when n_eq == K2, the usual case)
+  for (int i = threadIdx.x; i < static_cast<int>(c); i += 1024) {
+    const uint32_t kv = cu[i], e = ci[i];
+    bool win = kv > T;
+    if (kv == T) {
+      if (n_eq == K2) {
+        win = true;
+      } else {
+        uint32_t rank = 0;
+        for (int j2 = 0; j2 < static_cast<int>(c); ++j2)
+          rank += (cu[j2] == T && ci[j2] < e) ? 1u : 0u;
+        win = rank < K2;
+      }
+    }
+    if (win) atomicOr(&bm[e >> 5], 1u << (e & 31));
+  }
+  __syncthreads();
+
+  // ordered emit of every marked element
+  uint32_t base_pos = 0;
+  for (int w0 = 0; w0 < nwords; w0 += 4 * 1024) {
+    const int w = w0 + 4 * threadIdx.x;
+    uint32_t wd[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wd[q] = (w + q < nwords) ? bm[w + q] : 0u;
+    const uint32_t cnt = __popc(wd[0]) + __popc(wd[1]) + __popc(wd[2]) + __popc(wd[3]);
+    uint32_t tot;
+    uint32_t pos = base_pos + block_excl_scan<1024>(cnt, sm, tot);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t bits = wd[q];
+      while (bits) {
+        const int b = __ffs(bits) - 1;
+        bits &= bits - 1u;
+        const uint32_t e = static_cast<uint32_t>(32 * (w + q) + b);
+        if (pos < K) {
+          idx_row[pos] = static_cast<int32_t>(e);
+          if (score_row) score_row[pos] = key_score(row[e]);
+        }
+        ++pos;
+      }
+    }
+    base_pos += tot;
+  }
 }
 
 __global__ void topk_clear_kernel(uint32_t* __restrict__ p, size_t n_words) {
@@ -318,55 +413,28 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(
     const uint32_t* __restrict__ u, int u_stride, const int32_t* q_pos, int fixed_len, int topk,
     const int32_t* __restrict__ cand, int cand_stride, int32_t* __restrict__ idx,
     float* __restrict__ score) {
-  __shared__ uint32_t h0[kBins0];
-  __shared__ uint32_t h1[kBins1];
-  __shared__ uint32_t h2[kBins2];
+  __shared__ __align__(16) uint32_t h0[kBins0];
+  __shared__ __align__(16) uint32_t h1[kBins1];
+  __shared__ __align__(16) uint32_t h2[kBins2];
   __shared__ uint32_t sm[16];
   __shared__ uint32_t res[4];
   const int n = blockIdx.x;
   const int len = row_len(q_pos, fixed_len, n);
-  const int span = (len + kPerThread - 1) / kPerThread * kPerThread;
   const uint32_t* row = u + static_cast<size_t>(n) * u_stride;
-  for (int b = threadIdx.x; b < kBins0; b += 1024) {
-    h0[b] = 0u;
-    h1[b] = 0u;
-  }
-  if (threadIdx.x < kBins2) h2[threadIdx.x] = 0u;
-  __syncthreads();
-  hist_range<1024, 0>(row, 0, span, len, 0u, h0);
-  __syncthreads();
-  find_digit<1024>(h0, kBins0, static_cast<uint32_t>(topk), true, sm, res);
-  const uint32_t K = res[2], d0 = res[0], r0 = res[1];
-  __syncthreads();
-  Threshold th;
-  th.K = K;
-  th.T = 0xFFFFFFFFu;
-  th.K2 = 0;
-  if (K > 0) {
-    hist_range<1024, 1>(row, 0, span, len, d0, h1);
-    __syncthreads();
-    find_digit<1024>(h1, kBins1, r0, false, sm, res);
-    const uint32_t d1 = res[0], r1 = res[1];
-    __syncthreads();
-    hist_range<1024, 2>(row, 0, span, len, (d0 << kDigit1Bits) | d1, h2);
-    __syncthreads();
-    find_digit<1024>(h2, kBins2, r1, false, sm, res);
-    th.T = (d0 << kShift0) | (d1 << kShift1) | res[0];
-    th.K2 = res[1];
-    __syncthreads();
-  }
-  int32_t* idx_row = idx + static_cast<size_t>(n) * topk;
-  float* score_row = score ? score + static_cast<size_t>(n) * topk : nullptr;
-  for (int i = static_cast<int>(K) + threadIdx.x; i < topk; i += 1024) {
-    idx_row[i] = -1;
-    if (score_row) score_row[i] = -__builtin_inff();
-  }
-  if (K == 0) return;
   const int32_t* cand_row = cand ? cand + static_cast<size_t>(n) * cand_stride : nullptr;
-  compact_range<1024>(row, 0, span, len, th, 0u, 0u, cand_row, idx_row, score_row, sm);
+  row_select<1024>(row, len, topk, cand_row, idx + static_cast<size_t>(n) * topk,
+                   score ? score + static_cast<size_t>(n) * topk : nullptr, h0, h1, h2, false,
+                   sm, res);
 }
 
 }  // namespace
+
+size_t topk_few_rows_bytes(int N, int u_stride) {
+  // hist | bitmap | candidate list, each 256-byte aligned
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  return al(static_cast<size_t>(N) * kHistWords * 4) + al(static_cast<size_t>(N) * u_stride / 8) +
+         al(static_cast<size_t>(N) * kCandCap * 8);
+}
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.one_row_per_block) {
@@ -374,17 +442,16 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
                 a.q_pos, a.fixed_len, a.topk, a.cand, a.cand_stride, a.idx, a.score);
     return hipGetLastError();
   }
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  uint8_t* base = reinterpret_cast<uint8_t*>(a.hist);
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + al(static_cast<size_t>(a.N) * kHistWords * 4));
+  uint2* clist = reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(bitmap) +
+                                          al(static_cast<size_t>(a.N) * a.u_stride / 8));
   const int nchunks = a.u_stride / kChunk;
-  const dim3 grid(nchunks, a.N);
-  MISA_LAUNCH(K_TOPK_HIST1, topk_hist_kernel, grid, dim3(256), 0, st, a.u, a.u_stride, a.q_pos,
-              a.fixed_len, a.hist, a.topk, 1);
-  MISA_LAUNCH(K_TOPK_HIST2, topk_hist_kernel, grid, dim3(256), 0, st, a.u, a.u_stride, a.q_pos,
-              a.fixed_len, a.hist, a.topk, 2);
-  MISA_LAUNCH(K_TOPK_COUNT, topk_count_kernel, grid, dim3(256), 0, st, a.u, a.u_stride, a.q_pos,
-              a.fixed_len, a.hist, a.cnt, nchunks, a.topk);
-  MISA_LAUNCH(K_TOPK_WRITE, topk_write_kernel, grid, dim3(256), 0, st, a.u, a.u_stride, a.q_pos,
-              a.fixed_len, a.hist, a.cnt, nchunks, a.topk, a.cand, a.cand_stride, a.idx,
-              a.score);
+  MISA_LAUNCH(K_TOPK_COLLECT, topk_collect_kernel, dim3(nchunks, a.N), dim3(256), 0, st, a.u,
+              a.u_stride, a.q_pos, a.fixed_len, a.hist, bitmap, clist, a.topk);
+  MISA_LAUNCH(K_TOPK_FINAL, topk_final_kernel, dim3(a.N), dim3(1024), 0, st, a.u, a.u_stride,
+              a.q_pos, a.fixed_len, a.hist, bitmap, clist, a.topk, a.idx, a.score);
   return hipGetLastError();
 }
 

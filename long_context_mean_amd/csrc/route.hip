@@ -8,7 +8,7 @@
 // the row are read from the pooled table; the row's partial last block (when
 // L_n is not a multiple of B) is the mean of its visible keys only.
 //
-//  route_partial: grid (chunk of 32 full blocks, row).  Lane j of every
+//  route_partial: grid (chunk of 16 full blocks, row).  Lane j of every
 //    wavefront holds head j's query row in registers (fp32); the chunk's
 //    pooled keys sit in LDS and are read as broadcasts, each wavefront taking
 //    every fourth block.  Per-chunk sums go to the workspace (no float
@@ -23,7 +23,7 @@
 namespace misa {
 namespace {
 
-constexpr int kRouteBlocks = 32;     // pooled blocks per route_partial workgroup
+constexpr int kRouteBlocks = 16;     // pooled blocks per route_partial workgroup
 
 // Head row (D values) of q into registers as fp32.
 template <int QT, int D>

@@ -299,22 +299,31 @@ __global__ __launch_bounds__(1024) void topk_final_kernel(
   float* score_row = score ? score + static_cast<size_t>(n) * topk : nullptr;
   const int nwords = (len + 31) / 32;
 
+  // the bitmap words (certain winners) and the candidate count are read in
+  // the same round trip as the level-0 histogram
+  const uint32_t* bmg = bitmap + static_cast<size_t>(n) * (u_stride / 32);
+  uint4 bw[kBitmapWords / 4096];
+#pragma unroll
+  for (int q = 0; q < kBitmapWords / 4096; ++q) {
+    const int w = 4 * (threadIdx.x + q * 1024);
+    bw[q] = w + 3 < nwords ? *reinterpret_cast<const uint4*>(bmg + w) : make_uint4(0u, 0u, 0u, 0u);
+    if (w < nwords && w + 3 >= nwords) {          // ragged last words
+      bw[q].x = bmg[w];
+      if (w + 1 < nwords) bw[q].y = bmg[w + 1];
+      if (w + 2 < nwords) bw[q].z = bmg[w + 2];
+    }
+  }
+  const uint32_t c = h0g[kCandCountOffset];
   find_digit<1024, kBins0>(h0g, static_cast<uint32_t>(topk), true, sm, res);
   const uint32_t K = res[2], d0 = res[0], r0 = res[1];
-  const uint32_t c = h0g[kCandCountOffset];
   __syncthreads();
   bool fallback = c > static_cast<uint32_t>(kCandCap) || nwords > kBitmapWords;
   uint32_t T = 0, K2 = 0, n_eq = 0;
   if (!fallback && K > 0) {
     // certain winners (bitmap) and the candidates of bin d0 into LDS
-    const uint32_t* bmg = bitmap + static_cast<size_t>(n) * (u_stride / 32);
-    for (int w = 4 * threadIdx.x; w < nwords; w += 4 * 1024) {
-      if (w + 3 < nwords) {
-        *reinterpret_cast<uint4*>(&bm[w]) = *reinterpret_cast<const uint4*>(bmg + w);
-      } else {
-        for (int q = 0; q < 4 && w + q < nwords; ++q) bm[w + q] = bmg[w + q];
-      }
-    }
+#pragma unroll
+    for (int q = 0; q < kBitmapWords / 4096; ++q)
+      *reinterpret_cast<uint4*>(&bm[4 * (threadIdx.x + q * 1024)]) = bw[q];
     const uint2* cl = clist + static_cast<size_t>(n) * kCandCap;
     for (int i = threadIdx.x; i < static_cast<int>(c); i += 1024) {
       const uint2 e = cl[i];

@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--h", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--workload", default="c4", choices=["c4", "c3", "c3x"],
+                    help="c4: the long-context decode indexer (the headline line); "
+                         "c3 / c3x: the prefill chunk at L=64K / 128K")
     return ap.parse_args()
 
 
@@ -162,8 +165,74 @@ def cpu_baseline(p, h):
                       f"top-k in double precision), one pass, {dt:.2f} s"}
 
 
+def prefill_main(args):
+    """Prefill chunk: 4096 consecutive query rows over one causal prefix."""
+    import torch
+
+    from long_context_mean_amd import binding, synth
+    from long_context_mean_amd.binding import DeviceProblem
+    p = synth.make(args.workload, h=args.h)
+    dp = DeviceProblem(p)
+    N, L, d, H_I, B = p.N, p.L, p.d, p.H_I, p.B
+    M = -(-L // B)
+    dev = dp.q.device
+    kbar = torch.empty((1, M, d), dtype=torch.float32, device=dev)
+    heads = torch.empty((N, args.h), dtype=torch.int32, device=dev)
+    r = torch.empty((N, H_I), dtype=torch.float32, device=dev)
+    idx = torch.empty((N, p.topk), dtype=torch.int32, device=dev)
+    ws_r = binding.workspace(binding.MISA_OP_ROUTE, N, L, d, H_I, B, device=dev)
+    ws_s = binding.workspace(binding.MISA_OP_SCORE_TOPK, N, L, d, H_I, topk=p.topk, device=dev)
+
+    def step(_):
+        binding.misa_pool_keys(dp.k, B, kbar=kbar)
+        binding.misa_route_heads(dp.q, dp.w, kbar, dp.k, dp.q_seq, dp.q_pos, B, args.h,
+                                 heads=heads, head_score=r, ws=ws_r)
+        binding.misa_score_topk(dp.q, dp.w, dp.k, dp.q_seq, dp.q_pos, heads, p.topk, idx=idx,
+                                ws=ws_s, want_score=False)
+
+    def dense(_):
+        binding.dsa_score_topk(dp.q, dp.w, dp.k, dp.q_seq, dp.q_pos, p.topk, idx=idx, ws=ws_s,
+                               want_score=False)
+
+    ms = timed(torch, step, args.steps, args.warmup)
+    ms_e, kt, per = kernel_times(torch, binding, step, max(3, args.steps // 4), 1, 16)
+    ms_d = timed(torch, dense, max(3, args.steps // 4), 1)
+    _, ktd, _ = kernel_times(torch, binding, dense, 3, 1, 8)
+    pairs = p.tokens_indexed()
+    flops = 2.0 * args.h * d * pairs
+    sc_ms = kt.get("score_prefill_kernel")
+    tflops = flops / (sc_ms * 1e-3) / 1e12 if sc_ms else None
+    dflops = 2.0 * H_I * d * pairs
+    dsc = ktd.get("score_prefill_kernel")
+    line = {
+        "metric": "prefix tokens indexed/sec (prefill chunk)", "value": pairs / (ms * 1e-3),
+        "unit": "(query, prefix token) pairs/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"prefill chunk: {N} rows at positions {int(p.q_pos[0])}.."
+                               f"{int(p.q_pos[-1])} over L={L}, H_I={H_I}, d={d}, h={args.h}, "
+                               f"B={B}, top-k={p.topk}"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1) if tflops else None,
+                     "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 4) if tflops else None,
+                     "kernel": "score_prefill_kernel", "kernel_ms": sc_ms,
+                     "algorithmic_flop_per_launch": flops},
+        "extra": {"kernel_ms": {k: round(v, 4) for k, v in kt.items()},
+                  "dense_ms": round(ms_d, 4), "speedup_vs_dense": round(ms_d / ms, 3),
+                  "dense_kernel_ms": {k: round(v, 4) for k, v in ktd.items()},
+                  "dense_score_tflops": round(dflops / (dsc * 1e-3) / 1e12, 1) if dsc else None,
+                  "routed_score_vs_dense_score": round(dsc / sc_ms, 3) if dsc and sc_ms else None},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
+    if args.workload != "c4":
+        if args.gpus != 1:
+            sys.exit(2)
+        prefill_main(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the indexer's queries shard across GPUs without any exchange; see DESIGN.md)",

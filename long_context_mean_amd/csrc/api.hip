@@ -107,9 +107,15 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* w, const void*
   hipError_t e = hipSuccess;
   if (hist) e = misa::launch_clear(hist, static_cast<size_t>(N) * misa::kHistWords, st);
   if (e != hipSuccess) return hip_status(e);
-  misa::ScoreArgs sa{q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, heads, nullptr,
-                     N, S, L, d, H_I, h, 0, u, lay.u_stride, hist};
-  e = misa::launch_score(sa, st);
+  if (S == 1 && lay.one_row && N >= kOneRowMinN && q_dt == MISA_BF16 && k_dt == MISA_BF16) {
+    // many rows over one sequence: GEMM over the gathered head rows
+    misa::PrefillArgs pa{q, w, k, q_pos, heads, N, L, d, H_I, h, u, lay.u_stride};
+    e = misa::launch_prefill(pa, st);
+  } else {
+    misa::ScoreArgs sa{q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, heads, nullptr,
+                       N, S, L, d, H_I, h, 0, u, lay.u_stride, hist};
+    e = misa::launch_score(sa, st);
+  }
   if (e != hipSuccess) return hip_status(e);
   misa::TopkArgs ta{u, lay.u_stride, q_pos, 0, N, topk, lay.one_row, hist,
                     nullptr, 0, idx, score};

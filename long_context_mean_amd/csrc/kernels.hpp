@@ -59,6 +59,7 @@ struct RouteArgs {
   int nchunks;           // chunks of full blocks per row
 };
 int route_blocks_per_chunk();
+bool route_uses_mfma(const RouteArgs& a);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------- scoring
@@ -80,6 +81,21 @@ struct ScoreArgs {
   uint32_t* hist0;          // [N, kHistWords] level-0 histogram (NULL = skip)
 };
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- prefill scoring
+// Rows that all read one key sequence (bf16 q and keys): MFMA GEMM over the
+// gathered routed head rows; writes order keys u[t, s] for s <= q_pos[t].
+struct PrefillArgs {
+  const void* q;
+  const float* w;
+  const void* k;            // the key sequence [L, d] bf16
+  const int32_t* q_pos;
+  const int32_t* heads;     // [N, h] or NULL = all H_I heads
+  int N, L, d, H_I, h;
+  uint32_t* u;
+  int u_stride;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------- top-k
 struct TopkArgs {

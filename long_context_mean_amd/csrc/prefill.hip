@@ -1,0 +1,253 @@
+// Prefill scoring for the MISA indexer: many query rows over one causal key
+// sequence, gfx950.
+//
+//   I_t(s) = sum over row t's heads j of w[t,j] * ReLU(q[t,j,:] . k_s),  s <= pos_t
+// (DSA token-wise indexer score; MISA scores only the h routed heads of each
+// row, MISA technical summary, gist.science, "Methodology" item 2.)
+//
+// In prefill the rows share the keys, so the work is a GEMM: the gathered
+// routed head rows of a block of query rows, [rows x HP, d] with HP = the
+// head count rounded up to a power of two (padding rows have zero weight),
+// times the key matrix [d, L].  One workgroup (4 wavefronts) owns 256 such
+// head rows (256 / HP query rows) and one slice of the key range; each
+// wavefront keeps its 4 row tiles of v_mfma_f32_16x16x32_bf16 A operands in
+// registers for the whole slice.  Key tiles of 64 keys are read with flat
+// 16-byte loads into a double-buffered padded LDS tile (one barrier per tile)
+// and each B fragment read from LDS feeds 4 MFMAs.  The epilogue applies
+// ReLU, multiplies by the head weight, sums the HP rows of each query row
+// (in-lane, then across lane groups) and writes the order key of every
+// causally visible (row, key) pair.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace misa {
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kRowsPerWG = 256;       // gathered head rows per workgroup
+constexpr int kKeyTile = 64;          // keys per LDS tile
+
+struct PrefillParams {
+  const uint16_t* q;
+  const float* w;
+  const uint8_t* k;          // one key sequence [L, D] bf16
+  const int32_t* q_pos;
+  const int32_t* heads;      // [N, h] or NULL (all heads)
+  int N, L, H_I, h;
+  int keys_per_split;        // multiple of kKeyTile
+  uint32_t* u;
+  int u_stride;
+};
+
+template <int D>
+struct PLayout {
+  static constexpr int ROW = D * 2;                    // bytes per key row (bf16)
+  static constexpr int STRIDE = ROW + 16;              // padded LDS row
+  static constexpr int TILE = kKeyTile * STRIDE;       // bytes per LDS key tile
+  static constexpr int KK = D / 32;                    // MFMAs per 16x16 output tile
+  static constexpr int PIECES = kKeyTile * ROW / 16;   // 16-byte pieces per key tile
+  static constexpr int PER_THREAD = PIECES / 256;
+  static constexpr int PIECES_PER_ROW = ROW / 16;
+};
+
+template <int D>
+__device__ __forceinline__ void load_key_tile(const uint8_t* k, int key0, int L, int tid,
+                                              u32x4_t (&r)[PLayout<D>::PER_THREAD]) {
+  using LY = PLayout<D>;
+#pragma unroll
+  for (int i = 0; i < LY::PER_THREAD; ++i) {
+    const int f = tid + 256 * i;
+    int key = key0 + f / LY::PIECES_PER_ROW;
+    key = key < L ? key : L - 1;                      // past the end: any valid row, masked later
+    r[i] = *reinterpret_cast<const u32x4_t*>(k + static_cast<size_t>(key) * LY::ROW +
+                                             16 * (f % LY::PIECES_PER_ROW));
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_key_tile(uint8_t* tile, int tid,
+                                               const u32x4_t (&r)[PLayout<D>::PER_THREAD]) {
+  using LY = PLayout<D>;
+#pragma unroll
+  for (int i = 0; i < LY::PER_THREAD; ++i) {
+    const int f = tid + 256 * i;
+    *reinterpret_cast<u32x4_t*>(tile + (f / LY::PIECES_PER_ROW) * LY::STRIDE +
+                                16 * (f % LY::PIECES_PER_ROW)) = r[i];
+  }
+}
+
+template <int HP, int D>
+__global__ __launch_bounds__(256) void score_prefill_kernel(PrefillParams p) {
+  using LY = PLayout<D>;
+  constexpr int KK = LY::KK;
+  constexpr int QB = kRowsPerWG / HP;                  // query rows per workgroup
+  constexpr int QPT = HP >= 16 ? 1 : 16 / HP;          // query rows per 16-row tile
+  constexpr int TPQ = HP >= 16 ? HP / 16 : 1;          // row tiles per query row
+  __shared__ __align__(16) uint8_t tiles[2][LY::TILE];
+  __shared__ int pos_lds[QB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int qrow0 = blockIdx.y * QB;
+  for (int i = tid; i < QB; i += 256) {
+    const int t = qrow0 + i;
+    pos_lds[i] = t < p.N ? p.q_pos[t] : -1;
+  }
+  __syncthreads();
+  int kmax = 0;                                         // keys [0, kmax) are visible to some row
+  for (int i = 0; i < QB; ++i) kmax = max(kmax, pos_lds[i] + 1);
+  const int ks0 = blockIdx.x * p.keys_per_split;
+  const int ks1 = min(ks0 + p.keys_per_split, kmax);
+  if (ks0 >= ks1) return;
+
+  // A operand (4 row tiles of this wavefront) and the weights of the lane's rows
+  bf16x8_t a[4][KK];
+  float wv[4][4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int r = wave * 64 + rt * 16 + c;              // gathered row of this lane's A data
+    const int t = qrow0 + r / HP, hs = r % HP;
+    const bool rv = t < p.N && hs < p.h;
+    int j = 0;
+    if (rv) j = p.heads ? p.heads[static_cast<size_t>(t) * p.h + hs] : hs;
+    const uint16_t* qr = p.q + (static_cast<size_t>(rv ? t : 0) * p.H_I + j) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4_t x = *reinterpret_cast<const u32x4_t*>(qr + 32 * kk + 8 * g);
+      if (!rv) x = u32x4_t{0u, 0u, 0u, 0u};
+      a[rt][kk] = __builtin_bit_cast(bf16x8_t, x);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = wave * 64 + rt * 16 + 4 * g + i;   // output row of this lane's results
+      const int tt = qrow0 + rr / HP, hh = rr % HP;
+      float wf = 0.f;
+      if (tt < p.N && hh < p.h) {
+        const int jj = p.heads ? p.heads[static_cast<size_t>(tt) * p.h + hh] : hh;
+        wf = p.w[static_cast<size_t>(tt) * p.H_I + jj];
+      }
+      wv[rt][i] = wf;
+    }
+  }
+  // query rows whose results this lane writes, per row tile (HP < 16: several
+  // query rows share a tile; the writer lanes are the first lane group of each)
+  int wq[4];
+  bool writer[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int rbase = wave * 64 + rt * 16;
+    int qi;
+    bool wr;
+    if constexpr (HP >= 16) {
+      qi = rbase / HP;
+      wr = g == 0 && (rt % TPQ) == TPQ - 1;            // last tile of the query row holds the sum
+    } else if constexpr (HP == 8) {
+      qi = (rbase + 4 * g) / 8;
+      wr = (g & 1) == 0;
+    } else {
+      qi = (rbase + 4 * g) / HP;
+      wr = true;
+    }
+    wq[rt] = qi;
+    writer[rt] = wr;
+  }
+
+  u32x4_t pre[LY::PER_THREAD];
+  load_key_tile<D>(p.k, ks0, p.L, tid, pre);
+  store_key_tile<D>(tiles[0], tid, pre);
+  __syncthreads();
+  int buf = 0;
+  for (int key0 = ks0; key0 < ks1; key0 += kKeyTile) {
+    const bool more = key0 + kKeyTile < ks1;
+    if (more) load_key_tile<D>(p.k, key0 + kKeyTile, p.L, tid, pre);
+    const uint8_t* tile = tiles[buf];
+#pragma unroll
+    for (int ct = 0; ct < kKeyTile / 16; ++ct) {
+      bf16x8_t b[KK];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        b[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                                 tile + (ct * 16 + c) * LY::STRIDE + 64 * kk +
+                                                 16 * g));
+      float part[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][kk], b[kk], acc, 0, 0, 0);
+        float s4 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s4 += wv[rt][i] * fmaxf(acc[i], 0.f);
+        part[rt] = s4;
+      }
+      const int key = key0 + ct * 16 + c;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        float v = part[rt];
+        if constexpr (HP >= 32) {
+          // sum the TPQ tiles of the query row into its last tile
+          if ((rt % TPQ) != TPQ - 1) continue;
+#pragma unroll
+          for (int o = 1; o < TPQ; ++o) v += part[rt - o];
+        }
+        if constexpr (HP >= 8) v += __shfl_xor(v, 16, 64);
+        if constexpr (HP >= 16) v += __shfl_xor(v, 32, 64);
+        if (writer[rt]) {
+          const int t = qrow0 + wq[rt];
+          if (t < p.N && key <= pos_lds[wq[rt]])
+            p.u[static_cast<size_t>(t) * p.u_stride + key] = order_key(v);
+        }
+      }
+    }
+    if (more) {
+      store_key_tile<D>(tiles[buf ^ 1], tid, pre);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+}
+
+template <int HP, int D>
+hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
+  PrefillParams p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.w = a.w;
+  p.k = static_cast<const uint8_t*>(a.k);
+  p.q_pos = a.q_pos;
+  p.heads = a.heads;
+  p.N = a.N;
+  p.L = a.L;
+  p.H_I = a.H_I;
+  p.h = a.heads ? a.h : a.H_I;
+  p.u = a.u;
+  p.u_stride = a.u_stride;
+  constexpr int QB = kRowsPerWG / HP;
+  const int qblocks = (a.N + QB - 1) / QB;
+  // split the key range so the grid has at least ~4 workgroups per CU
+  int splits = 1;
+  while (qblocks * splits < 1024 && a.L / (splits * 2) >= 4 * kKeyTile) splits *= 2;
+  p.keys_per_split = ((a.L + splits - 1) / splits + kKeyTile - 1) / kKeyTile * kKeyTile;
+  MISA_LAUNCH(K_SCORE_PREFILL, (score_prefill_kernel<HP, D>), dim3(splits, qblocks), dim3(256),
+              0, st, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const PrefillArgs& a, hipStream_t st) {
+  const int h = a.heads ? a.h : a.H_I;
+  if (h <= 4) return launch_t<4, D>(a, st);
+  if (h <= 8) return launch_t<8, D>(a, st);
+  if (h <= 16) return launch_t<16, D>(a, st);
+  if (h <= 32) return launch_t<32, D>(a, st);
+  return launch_t<64, D>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
+  return a.d == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
+}
+
+}  // namespace misa

@@ -106,6 +106,126 @@ __global__ __launch_bounds__(256) void route_partial_kernel(
                        (red[2][threadIdx.x] + red[3][threadIdx.x]);
 }
 
+// Many query rows over one key sequence (prefill): the router dots are a
+// GEMM, [rows x H_I, d] x [d, M], run on v_mfma_f32_16x16x32_bf16.  q is
+// exact in bf16; each pooled key is split as kbar = hi + lo with hi, lo
+// bf16 (round to nearest), so q.kbar = q.hi + q.lo with both products exact
+// and fp32 accumulation (relative error ~2^-17 of |q||kbar|).  One
+// workgroup owns 256 / HPI query rows (HPI = H_I padded to 16, 32 or 64
+// rows, 64 head rows per wavefront) and streams the pooled blocks visible to
+// them in tiles of 64 through LDS; each lane sums ReLU(dot) over the blocks
+// of its output column, masked per row to the row's fully visible blocks,
+// and the 16 columns are reduced across lanes at the end.  The partial
+// visible block is added by route_select.
+constexpr int kRouteTile = 64;       // pooled blocks per LDS tile
+
+template <int HPI>
+__global__ __launch_bounds__(256) void route_mfma_kernel(const uint16_t* __restrict__ q,
+                                                         const float* __restrict__ kbar,
+                                                         const int32_t* __restrict__ q_pos,
+                                                         int N, int L, int B, int H_I,
+                                                         float* __restrict__ partial) {
+  constexpr int D = 128;
+  constexpr int KK = D / 32;
+  constexpr int STRIDE = D * 2 + 16;                   // padded bf16 row in LDS (bytes)
+  constexpr int QB = 256 / HPI;                        // query rows per workgroup
+  __shared__ __align__(16) uint8_t hi_t[kRouteTile * STRIDE];
+  __shared__ __align__(16) uint8_t lo_t[kRouteTile * STRIDE];
+  __shared__ int mf_lds[QB];
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int q0 = blockIdx.x * QB;
+  const int M = (L + B - 1) / B;
+  for (int i = tid; i < QB; i += 256) mf_lds[i] = q0 + i < N ? (q_pos[q0 + i] + 1) / B : 0;
+  __syncthreads();
+  int mmax = 0;
+  for (int i = 0; i < QB; ++i) mmax = max(mmax, mf_lds[i]);
+
+  // A operand: 4 row tiles of head rows; row r of the workgroup is head r % HPI
+  // of query row r / HPI
+  bf16x8_t a[4][KK];
+  int mf_row[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int r = wave * 64 + rt * 16 + c;
+    const int t = q0 + r / HPI, j = r % HPI;
+    const bool rv = t < N && j < H_I;
+    const uint16_t* qr = q + (static_cast<size_t>(rv ? t : 0) * H_I + (rv ? j : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4_t x = *reinterpret_cast<const u32x4_t*>(qr + 32 * kk + 8 * g);
+      if (!rv) x = u32x4_t{0u, 0u, 0u, 0u};
+      a[rt][kk] = __builtin_bit_cast(bf16x8_t, x);
+    }
+    // rows 4g..4g+3 of the tile all belong to one query row (HPI >= 16)
+    mf_row[rt] = mf_lds[(wave * 64 + rt * 16) / HPI];
+  }
+  float acc_rows[4][4] = {};
+
+  for (int b0 = 0; b0 < mmax; b0 += kRouteTile) {
+    __syncthreads();
+    // split the tile's pooled keys into hi / lo bf16 rows in LDS
+    for (int f = tid; f < kRouteTile * D / 4; f += 256) {
+      const int blk = f / (D / 4), col = (f % (D / 4)) * 4;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (b0 + blk < M) x = *reinterpret_cast<const float4*>(kbar + static_cast<size_t>(b0 + blk) * D + col);
+      const float xs[4] = {x.x, x.y, x.z, x.w};
+      uint32_t hb[4], lb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t u = __float_as_uint(xs[e]);
+        hb[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+        const float lo = xs[e] - __uint_as_float(hb[e] << 16);
+        const uint32_t ul = __float_as_uint(lo);
+        lb[e] = (ul + 0x7FFFu + ((ul >> 16) & 1u)) >> 16;
+      }
+      uint2 hp = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+      uint2 lp = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+      *reinterpret_cast<uint2*>(hi_t + blk * STRIDE + col * 2) = hp;
+      *reinterpret_cast<uint2*>(lo_t + blk * STRIDE + col * 2) = lp;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ct = 0; ct < kRouteTile / 16; ++ct) {
+      const int blk = b0 + ct * 16 + c;                // this lane's output column
+      bf16x8_t bh[KK], bl[KK];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int off = (ct * 16 + c) * STRIDE + 64 * kk + 16 * g;
+        bh[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(hi_t + off));
+        bl[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(lo_t + off));
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][kk], bh[kk], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][kk], bl[kk], acc, 0, 0, 0);
+        }
+        const bool vis = blk < mf_row[rt];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc_rows[rt][i] += vis ? fmaxf(acc[i], 0.f) : 0.f;
+      }
+    }
+  }
+  // sum the 16 output columns held by lanes c = 0..15 of each lane group
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = acc_rows[rt][i];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+      const int r = wave * 64 + rt * 16 + 4 * g + i;
+      const int t = q0 + r / HPI, j = r % HPI;
+      if (c == 0 && t < N && j < H_I) partial[static_cast<size_t>(t) * H_I + j] = v;
+    }
+  }
+}
+
 template <int QT, int KT, int D>
 __global__ __launch_bounds__(256) void route_select_kernel(
     const void* __restrict__ q, const float* __restrict__ w, const void* __restrict__ k,
@@ -214,10 +334,27 @@ __global__ __launch_bounds__(256) void route_select_kernel(
 
 template <int QT, int KT, int D>
 hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
-  MISA_LAUNCH(K_ROUTE_PARTIAL, (route_partial_kernel<QT, D>), dim3(a.nchunks, a.N), dim3(256),
-              0, st, a.q, a.kbar, a.q_seq, a.q_pos, a.L, a.B, a.H_I, a.nchunks, a.partial);
+  int nchunks = a.nchunks;
+  if (route_uses_mfma(a)) {
+    nchunks = 1;
+    const int hpi = a.H_I <= 16 ? 16 : (a.H_I <= 32 ? 32 : 64);
+    const dim3 grid((a.N + 256 / hpi - 1) / (256 / hpi));
+    const uint16_t* q = static_cast<const uint16_t*>(a.q);
+    if (hpi == 16)
+      MISA_LAUNCH(K_ROUTE_PARTIAL, route_mfma_kernel<16>, grid, dim3(256), 0, st, q, a.kbar,
+                  a.q_pos, a.N, a.L, a.B, a.H_I, a.partial);
+    else if (hpi == 32)
+      MISA_LAUNCH(K_ROUTE_PARTIAL, route_mfma_kernel<32>, grid, dim3(256), 0, st, q, a.kbar,
+                  a.q_pos, a.N, a.L, a.B, a.H_I, a.partial);
+    else
+      MISA_LAUNCH(K_ROUTE_PARTIAL, route_mfma_kernel<64>, grid, dim3(256), 0, st, q, a.kbar,
+                  a.q_pos, a.N, a.L, a.B, a.H_I, a.partial);
+  } else {
+    MISA_LAUNCH(K_ROUTE_PARTIAL, (route_partial_kernel<QT, D>), dim3(a.nchunks, a.N), dim3(256),
+                0, st, a.q, a.kbar, a.q_seq, a.q_pos, a.L, a.B, a.H_I, a.nchunks, a.partial);
+  }
   MISA_LAUNCH(K_ROUTE_SELECT, (route_select_kernel<QT, KT, D>), dim3(a.N), dim3(256), 0, st,
-              a.q, a.w, a.k, a.k_scale, a.q_seq, a.q_pos, a.L, a.B, a.H_I, a.h, a.nchunks,
+              a.q, a.w, a.k, a.k_scale, a.q_seq, a.q_pos, a.L, a.B, a.H_I, a.h, nchunks,
               a.partial, a.heads, a.head_score);
   return hipGetLastError();
 }
@@ -232,6 +369,10 @@ hipError_t launch_route_d(const RouteArgs& a, hipStream_t st) {
 }  // namespace
 
 int route_blocks_per_chunk() { return kRouteBlocks; }
+
+bool route_uses_mfma(const RouteArgs& a) {
+  return a.S == 1 && a.N >= 128 && a.q_dt == DT_BF16 && a.d == 128;
+}
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
   return a.d == 64 ? launch_route_d<64>(a, st) : launch_route_d<128>(a, st);

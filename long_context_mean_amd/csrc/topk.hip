@@ -418,22 +418,146 @@ __global__ void topk_clear_kernel(uint32_t* __restrict__ p, size_t n_words) {
 }
 
 // ---------------------------------------------------------------- one row per workgroup
+// Two sweeps over the row: (1) level-0 histogram; (2) certain winners into an
+// LDS bitmap, candidates of the threshold bin into an LDS list.  The
+// candidates are resolved and the winners emitted exactly as in topk_final.
+// Rows longer than the LDS bitmap, or with more threshold-bin candidates than
+// fit in LDS, take the full radix path (row_select).
 __global__ __launch_bounds__(1024) void topk_row_kernel(
     const uint32_t* __restrict__ u, int u_stride, const int32_t* q_pos, int fixed_len, int topk,
     const int32_t* __restrict__ cand, int cand_stride, int32_t* __restrict__ idx,
     float* __restrict__ score) {
-  __shared__ __align__(16) uint32_t h0[kBins0];
-  __shared__ __align__(16) uint32_t h1[kBins1];
-  __shared__ __align__(16) uint32_t h2[kBins2];
+  __shared__ __align__(16) uint32_t bm[kBitmapWords];
+  __shared__ __align__(16) uint32_t cu[kCandCap];
+  __shared__ __align__(16) uint32_t ci[kCandCap];
+  __shared__ __align__(16) uint32_t hA[kBins0];
+  __shared__ __align__(16) uint32_t hB[kBins2];
   __shared__ uint32_t sm[16];
   __shared__ uint32_t res[4];
+  __shared__ uint32_t n_cand;
   const int n = blockIdx.x;
   const int len = row_len(q_pos, fixed_len, n);
   const uint32_t* row = u + static_cast<size_t>(n) * u_stride;
   const int32_t* cand_row = cand ? cand + static_cast<size_t>(n) * cand_stride : nullptr;
-  row_select<1024>(row, len, topk, cand_row, idx + static_cast<size_t>(n) * topk,
-                   score ? score + static_cast<size_t>(n) * topk : nullptr, h0, h1, h2, false,
-                   sm, res);
+  int32_t* idx_row = idx + static_cast<size_t>(n) * topk;
+  float* score_row = score ? score + static_cast<size_t>(n) * topk : nullptr;
+  const int span = (len + kPerThread - 1) / kPerThread * kPerThread;
+  const int nwords = (len + 31) / 32;
+  if (nwords > kBitmapWords) {
+    row_select<1024>(row, len, topk, cand_row, idx_row, score_row, hA, cu, hB, false, sm, res);
+    return;
+  }
+  for (int b = threadIdx.x; b < kBins0; b += 1024) hA[b] = 0u;
+  if (threadIdx.x < kBins2) hB[threadIdx.x] = 0u;
+  if (threadIdx.x == 0) n_cand = 0u;
+  __syncthreads();
+  hist_range<1024, 0>(row, span, len, 0u, hA);
+  __syncthreads();
+  find_digit<1024, kBins0>(hA, static_cast<uint32_t>(topk), true, sm, res);
+  const uint32_t K = res[2], d0 = res[0], r0 = res[1];
+  __syncthreads();
+  for (int i = static_cast<int>(K) + threadIdx.x; i < topk; i += 1024) {
+    idx_row[i] = -1;
+    if (score_row) score_row[i] = -__builtin_inff();
+  }
+  if (K == 0) return;
+  // sweep 2: bitmap of certain winners, candidate list of bin d0
+  for (int i0 = static_cast<int>(threadIdx.x) * kPerThread; i0 < ((span + 31) / 32) * 32;
+       i0 += 1024 * kPerThread) {
+    uint32_t v[16];
+    if (i0 < span) {
+      load16(row, i0, len, v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = 0u;
+    }
+    uint32_t sure = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t dg = v[j] >> kShift0;
+      sure |= (v[j] != 0u && dg > d0) ? (1u << j) : 0u;
+      if (v[j] != 0u && dg == d0) {
+        const uint32_t slot = atomicAdd(&n_cand, 1u);
+        if (slot < static_cast<uint32_t>(kCandCap)) {
+          cu[slot] = v[j];
+          ci[slot] = static_cast<uint32_t>(i0 + j);
+        }
+      }
+    }
+    const uint32_t other = __shfl_xor(sure, 1, 64);
+    if ((threadIdx.x & 1) == 0 && (i0 >> 5) < nwords) bm[i0 >> 5] = sure | (other << 16);
+  }
+  for (int b = threadIdx.x; b < kBins1; b += 1024) hA[b] = 0u;
+  __syncthreads();
+  const uint32_t c = n_cand;
+  if (c > static_cast<uint32_t>(kCandCap)) {
+    __syncthreads();
+    row_select<1024>(row, len, topk, cand_row, idx_row, score_row, hA, cu, hB, false, sm, res);
+    return;
+  }
+  // exact threshold among the candidates: digits 1 and 2 (rank r0)
+  for (int i = threadIdx.x; i < static_cast<int>(c); i += 1024)
+    atomicAdd(&hA[(cu[i] >> kShift1) & (kBins1 - 1)], 1u);
+  __syncthreads();
+  find_digit<1024, kBins1>(hA, r0, false, sm, res);
+  const uint32_t d1 = res[0], r1 = res[1];
+  __syncthreads();
+  const uint32_t pre = (d0 << kDigit1Bits) | d1;
+  for (int i = threadIdx.x; i < static_cast<int>(c); i += 1024)
+    if ((cu[i] >> kShift1) == pre) atomicAdd(&hB[cu[i] & (kBins2 - 1)], 1u);
+  __syncthreads();
+  find_digit<1024, kBins2>(hB, r1, false, sm, res);
+  const uint32_t T = (d0 << kShift0) | (d1 << kShift1) | res[0];
+  const uint32_t K2 = res[1];
+  const uint32_t n_eq = hB[res[0]];
+  __syncthreads();
+  if (n_eq != K2 && n_eq > 2048u) {
+    row_select<1024>(row, len, topk, cand_row, idx_row, score_row, hA, cu, hB, false, sm, res);
+    return;
+  }
+  // mark candidate winners (ties: the K2 lowest element indices)
+  for (int i = threadIdx.x; i < static_cast<int>(c); i += 1024) {
+    const uint32_t kv = cu[i], e = ci[i];
+    bool win = kv > T;
+    if (kv == T) {
+      if (n_eq == K2) {
+        win = true;
+      } else {
+        uint32_t rank = 0;
+        for (int j2 = 0; j2 < static_cast<int>(c); ++j2)
+          rank += (cu[j2] == T && ci[j2] < e) ? 1u : 0u;
+        win = rank < K2;
+      }
+    }
+    if (win) atomicOr(&bm[e >> 5], 1u << (e & 31));
+  }
+  __syncthreads();
+  // ordered emit of every marked element
+  uint32_t base_pos = 0;
+  for (int w0 = 0; w0 < nwords; w0 += 4 * 1024) {
+    const int w = w0 + 4 * threadIdx.x;
+    uint32_t wd[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wd[q] = (w + q < nwords) ? bm[w + q] : 0u;
+    const uint32_t cnt = __popc(wd[0]) + __popc(wd[1]) + __popc(wd[2]) + __popc(wd[3]);
+    uint32_t tot;
+    uint32_t pos = base_pos + block_excl_scan<1024>(cnt, sm, tot);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t bits = wd[q];
+      while (bits) {
+        const int b = __ffs(bits) - 1;
+        bits &= bits - 1u;
+        const uint32_t e = static_cast<uint32_t>(32 * (w + q) + b);
+        if (pos < K) {
+          idx_row[pos] = cand_row ? cand_row[e] : static_cast<int32_t>(e);
+          if (score_row) score_row[pos] = key_score(row[e]);
+        }
+        ++pos;
+      }
+    }
+    base_pos += tot;
+  }
 }
 
 }  // namespace

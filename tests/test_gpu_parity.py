@@ -258,3 +258,45 @@ def test_c3_prefill_chunk_sampled_rows():
     p = synth.make("c3")
     rows = np.r_[0:3, 127:130, 2047:2049, 4093:4096]
     check_misa(p, rows=rows)
+
+
+# ---------------------------------------------------------------- prefill (rows sharing one prefix)
+@pytest.mark.parametrize("h,d,H_I", [(8, 128, 64), (4, 128, 16), (3, 128, 16), (16, 64, 32),
+                                     (32, 128, 64), (12, 128, 64)])
+def test_prefill_gemm_parity(h, d, H_I):
+    """Rows sharing one key sequence (the prefill GEMM path), at unsorted causal
+    positions including block boundaries and position 0."""
+    L, N = 6000, 320
+    rng = np.random.default_rng(h * 100 + d)
+    pos = rng.choice(L, N, replace=False).astype(np.int32)
+    pos[:4] = [0, 127, 128, L - 1]
+    p = synth.small("pre", 43 + h, N=N, S=1, L=L, d=d, H_I=H_I, h=h, B=128, topk=700,
+                    q_pos=pos, q_seq=np.zeros(N, np.int32))
+    check_misa(p, rows=np.r_[0:8, 100:104, N - 6:N])
+
+
+def test_prefill_dense_parity():
+    L, N = 5000, 256
+    pos = np.random.default_rng(5).choice(L, N, replace=False).astype(np.int32)
+    p = synth.small("pred", 47, N=N, S=1, L=L, d=128, H_I=64, h=8, topk=512,
+                    q_pos=pos, q_seq=np.zeros(N, np.int32))
+    idx, sc = DeviceProblem(p).dsa()
+    rows = np.r_[0:6, 250:256]
+    ps = sub_problem(p, rows)
+    check_topk(np_(idx)[rows], np_(sc)[rows], oracle.scores(ps, None), p.topk, ps.visible())
+
+
+def test_prefill_integer_bit_exact():
+    """Integer inputs on the prefill GEMM path: bit-exact, ties included."""
+    N, L = 200, 2000
+    pos = np.random.default_rng(9).choice(L, N, replace=False).astype(np.int32)
+    p = synth.integer_problem("preint", 6, N=N, S=1, L=L, d=128, H_I=16, h=5, B=1, topk=300,
+                              q_pos=pos, q_seq=np.zeros(N, np.int32))
+    dp = DeviceProblem(p)
+    kbar, heads, r, idx, sc = misa_gpu(dp)
+    rows = np.r_[0:10, 190:200]
+    ps = sub_problem(p, rows)
+    ref_heads, ref_r = oracle.route_heads(ps)
+    assert np.array_equal(heads[rows], ref_heads)
+    check_topk(idx[rows], sc[rows], oracle.scores(ps, ref_heads), p.topk, ps.visible(),
+               exact=True)

@@ -73,12 +73,17 @@ __device__ __forceinline__ void unpack16(uint4 x, float* out) {
 }
 
 // Total order on fp32 scores as unsigned keys: larger score <-> larger key,
-// -0.0 and +0.0 map to the same key.  Key 0 (a negative NaN pattern) is never
-// produced for a finite score and marks an empty slot.
+// -0.0 and +0.0 map to the same key (adding +0.0 turns -0.0 into +0.0).  Key
+// 0 (a negative NaN pattern) is never produced for a finite score and marks
+// an empty slot.
 __device__ __forceinline__ uint32_t order_key(float v) {
-  uint32_t b = __float_as_uint(v);
-  if ((b << 1) == 0u) b = 0u;
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  const uint32_t b = __float_as_uint(v + 0.0f);
+  return b ^ (static_cast<uint32_t>(static_cast<int32_t>(b) >> 31) | 0x80000000u);
+}
+
+// ReLU in one instruction (median of x, 0 and the largest finite float).
+__device__ __forceinline__ float relu(float x) {
+  return __builtin_amdgcn_fmed3f(x, 0.0f, 3.4028234663852886e38f);
 }
 
 __device__ __forceinline__ float key_score(uint32_t u) {

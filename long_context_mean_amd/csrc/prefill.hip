@@ -16,7 +16,8 @@
 // and each B fragment read from LDS feeds 4 MFMAs.  The epilogue applies
 // ReLU, multiplies by the head weight, sums the HP rows of each query row
 // (in-lane, then across lane groups) and writes the order key of every
-// causally visible (row, key) pair.
+// causally visible (row, key) pair; tiles away from the causal diagonal store
+// without masks.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -77,13 +78,62 @@ __device__ __forceinline__ void store_key_tile(uint8_t* tile, int tid,
   }
 }
 
+// One LDS key tile (64 keys) against the wavefront's 4 row tiles; writes the
+// order keys.  MASK: some (row, key) of the tile may be outside the causal
+// prefix or the row block.
+template <int HP, int D, bool MASK>
+__device__ __forceinline__ void score_tile(const uint8_t* tile, int key0,
+                                           const bf16x8_t (&a)[4][PLayout<D>::KK],
+                                           const float (&wv)[4][4], const int (&wq)[4],
+                                           uint32_t* const (&urow)[4], const int* pos_lds,
+                                           int qrow0, int N, int g, int c) {
+  using LY = PLayout<D>;
+  constexpr int KK = LY::KK;
+  constexpr int TPQ = HP >= 16 ? HP / 16 : 1;          // row tiles per query row
+#pragma unroll
+  for (int ct = 0; ct < kKeyTile / 16; ++ct) {
+    bf16x8_t b[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      b[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                               tile + (ct * 16 + c) * LY::STRIDE + 64 * kk +
+                                               16 * g));
+    float part[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][kk], b[kk], acc, 0, 0, 0);
+      float s4 = wv[rt][0] * relu(acc[0]);
+#pragma unroll
+      for (int i = 1; i < 4; ++i) s4 += wv[rt][i] * relu(acc[i]);
+      part[rt] = s4;
+    }
+    const int key = key0 + ct * 16 + c;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      float v = part[rt];
+      if constexpr (HP >= 32) {
+        // sum the TPQ tiles of the query row into its last tile
+        if ((rt % TPQ) != TPQ - 1) continue;
+#pragma unroll
+        for (int o = 1; o < TPQ; ++o) v += part[rt - o];
+      }
+      if constexpr (HP >= 8) v += __shfl_xor(v, 16, 64);
+      if constexpr (HP >= 16) v += __shfl_xor(v, 32, 64);
+      // lanes holding the same row sum write the same value (benign duplicates)
+      const uint32_t kv = order_key(v);
+      if (!MASK || (qrow0 + wq[rt] < N && key <= pos_lds[wq[rt]])) urow[rt][key] = kv;
+    }
+  }
+}
+
 template <int HP, int D>
 __global__ __launch_bounds__(256) void score_prefill_kernel(PrefillParams p) {
   using LY = PLayout<D>;
   constexpr int KK = LY::KK;
   constexpr int QB = kRowsPerWG / HP;                  // query rows per workgroup
-  constexpr int QPT = HP >= 16 ? 1 : 16 / HP;          // query rows per 16-row tile
-  constexpr int TPQ = HP >= 16 ? HP / 16 : 1;          // row tiles per query row
   __shared__ __align__(16) uint8_t tiles[2][LY::TILE];
   __shared__ int pos_lds[QB];
 
@@ -130,27 +180,21 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(PrefillParams p) {
       wv[rt][i] = wf;
     }
   }
-  // query rows whose results this lane writes, per row tile (HP < 16: several
-  // query rows share a tile; the writer lanes are the first lane group of each)
+  // query row (index in the block) whose sums this lane holds, per row tile
   int wq[4];
-  bool writer[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     const int rbase = wave * 64 + rt * 16;
-    int qi;
-    bool wr;
-    if constexpr (HP >= 16) {
-      qi = rbase / HP;
-      wr = g == 0 && (rt % TPQ) == TPQ - 1;            // last tile of the query row holds the sum
-    } else if constexpr (HP == 8) {
-      qi = (rbase + 4 * g) / 8;
-      wr = (g & 1) == 0;
-    } else {
-      qi = (rbase + 4 * g) / HP;
-      wr = true;
-    }
-    wq[rt] = qi;
-    writer[rt] = wr;
+    wq[rt] = HP >= 16 ? rbase / HP : (rbase + 4 * g) / HP;
+  }
+  int minpos = 0x7FFFFFFF;                              // keys <= minpos are visible to every row
+  for (int i = 0; i < QB; ++i) minpos = min(minpos, pos_lds[i] < 0 ? 0x7FFFFFFF : pos_lds[i]);
+  const bool full_block = qrow0 + QB <= p.N;
+  uint32_t* urow[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int t = qrow0 + wq[rt];
+    urow[rt] = p.u + static_cast<size_t>(t < p.N ? t : 0) * p.u_stride;
   }
 
   u32x4_t pre[LY::PER_THREAD];
@@ -161,46 +205,12 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(PrefillParams p) {
   for (int key0 = ks0; key0 < ks1; key0 += kKeyTile) {
     const bool more = key0 + kKeyTile < ks1;
     if (more) load_key_tile<D>(p.k, key0 + kKeyTile, p.L, tid, pre);
-    const uint8_t* tile = tiles[buf];
-#pragma unroll
-    for (int ct = 0; ct < kKeyTile / 16; ++ct) {
-      bf16x8_t b[KK];
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        b[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
-                                                 tile + (ct * 16 + c) * LY::STRIDE + 64 * kk +
-                                                 16 * g));
-      float part[4];
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][kk], b[kk], acc, 0, 0, 0);
-        float s4 = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s4 += wv[rt][i] * fmaxf(acc[i], 0.f);
-        part[rt] = s4;
-      }
-      const int key = key0 + ct * 16 + c;
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        float v = part[rt];
-        if constexpr (HP >= 32) {
-          // sum the TPQ tiles of the query row into its last tile
-          if ((rt % TPQ) != TPQ - 1) continue;
-#pragma unroll
-          for (int o = 1; o < TPQ; ++o) v += part[rt - o];
-        }
-        if constexpr (HP >= 8) v += __shfl_xor(v, 16, 64);
-        if constexpr (HP >= 16) v += __shfl_xor(v, 32, 64);
-        if (writer[rt]) {
-          const int t = qrow0 + wq[rt];
-          if (t < p.N && key <= pos_lds[wq[rt]])
-            p.u[static_cast<size_t>(t) * p.u_stride + key] = order_key(v);
-        }
-      }
-    }
+    // every (row, key) of the tile is visible: stores need no mask
+    const bool unmasked = full_block && key0 + kKeyTile - 1 <= minpos;
+    if (unmasked)
+      score_tile<HP, D, false>(tiles[buf], key0, a, wv, wq, urow, pos_lds, qrow0, p.N, g, c);
+    else
+      score_tile<HP, D, true>(tiles[buf], key0, a, wv, wq, urow, pos_lds, qrow0, p.N, g, c);
     if (more) {
       store_key_tile<D>(tiles[buf ^ 1], tid, pre);
       __syncthreads();

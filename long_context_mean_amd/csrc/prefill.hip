@@ -78,18 +78,48 @@ __device__ __forceinline__ void store_key_tile(uint8_t* tile, int tid,
   }
 }
 
+// Row mapping of the gathered A operand.  Each wavefront holds 4 row tiles of
+// 16 MFMA rows; output lane (g, c) of v_mfma_f32_16x16x32_bf16 holds rows
+// 4g..4g+3 of column c.
+//  HP <= 16: a query row owns rows 4g..4g+3 of TQ = HP/4 consecutive row
+//    tiles, so a lane sums whole query rows in registers; lane group g holds
+//    query rows p*4 + g (p < NG).
+//  HP >= 32: a query row owns TQ = HP/16 whole row tiles; each lane sums its
+//    part and the 4 lane groups are combined with two cross-lane adds.
+template <int HP>
+struct RowMap {
+  static constexpr bool IN_LANE = HP <= 16;
+  static constexpr int TQ = IN_LANE ? HP / 4 : HP / 16;  // row tiles per query-row group
+  static constexpr int NG = 4 / TQ;                      // query-row groups per wavefront
+  static constexpr int QW = IN_LANE ? 4 * NG : NG;       // query rows per wavefront
+  // query row (in the workgroup) and head slot of MFMA row m of row tile rt
+  __device__ static void row(int wave, int rt, int m, int& qr, int& hs) {
+    if constexpr (IN_LANE) {
+      qr = wave * QW + (rt / TQ) * 4 + (m >> 2);
+      hs = (rt % TQ) * 4 + (m & 3);
+    } else {
+      qr = wave * QW + rt / TQ;
+      hs = (rt % TQ) * 16 + m;
+    }
+  }
+  // query row whose sums lane group g holds for group p
+  __device__ static int out_row(int wave, int p, int g) {
+    return IN_LANE ? wave * QW + p * 4 + g : wave * QW + p;
+  }
+};
+
 // One LDS key tile (64 keys) against the wavefront's 4 row tiles; writes the
 // order keys.  MASK: some (row, key) of the tile may be outside the causal
 // prefix or the row block.
 template <int HP, int D, bool MASK>
 __device__ __forceinline__ void score_tile(const uint8_t* tile, int key0,
                                            const bf16x8_t (&a)[4][PLayout<D>::KK],
-                                           const float (&wv)[4][4], const int (&wq)[4],
-                                           uint32_t* const (&urow)[4], const int* pos_lds,
-                                           int qrow0, int N, int g, int c) {
+                                           const float (&wv)[4][4],
+                                           uint32_t* const (&urow)[RowMap<HP>::NG],
+                                           const int (&opos)[RowMap<HP>::NG], int g, int c) {
   using LY = PLayout<D>;
+  using RM = RowMap<HP>;
   constexpr int KK = LY::KK;
-  constexpr int TPQ = HP >= 16 ? HP / 16 : 1;          // row tiles per query row
 #pragma unroll
   for (int ct = 0; ct < kKeyTile / 16; ++ct) {
     bf16x8_t b[KK];
@@ -98,40 +128,37 @@ __device__ __forceinline__ void score_tile(const uint8_t* tile, int key0,
       b[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
                                                tile + (ct * 16 + c) * LY::STRIDE + 64 * kk +
                                                16 * g));
-    float part[4];
+    float v[RM::NG];
+#pragma unroll
+    for (int p = 0; p < RM::NG; ++p) v[p] = 0.f;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][kk], b[kk], acc, 0, 0, 0);
-      float s4 = wv[rt][0] * relu(acc[0]);
 #pragma unroll
-      for (int i = 1; i < 4; ++i) s4 += wv[rt][i] * relu(acc[i]);
-      part[rt] = s4;
+      for (int i = 0; i < 4; ++i) v[rt / RM::TQ] = fmaf(wv[rt][i], relu(acc[i]), v[rt / RM::TQ]);
     }
     const int key = key0 + ct * 16 + c;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      float v = part[rt];
-      if constexpr (HP >= 32) {
-        // sum the TPQ tiles of the query row into its last tile
-        if ((rt % TPQ) != TPQ - 1) continue;
-#pragma unroll
-        for (int o = 1; o < TPQ; ++o) v += part[rt - o];
+    for (int p = 0; p < RM::NG; ++p) {
+      float x = v[p];
+      if constexpr (!RM::IN_LANE) {
+        x += __shfl_xor(x, 16, 64);
+        x += __shfl_xor(x, 32, 64);
       }
-      if constexpr (HP >= 8) v += __shfl_xor(v, 16, 64);
-      if constexpr (HP >= 16) v += __shfl_xor(v, 32, 64);
-      // lanes holding the same row sum write the same value (benign duplicates)
-      const uint32_t kv = order_key(v);
-      if (!MASK || (qrow0 + wq[rt] < N && key <= pos_lds[wq[rt]])) urow[rt][key] = kv;
+      const uint32_t kv = order_key(x);
+      const bool owner = RM::IN_LANE || g == 0;
+      if (owner && (!MASK || key <= opos[p])) urow[p][key] = kv;
     }
   }
 }
 
 template <int HP, int D>
-__global__ __launch_bounds__(256) void score_prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(PrefillParams p) {
   using LY = PLayout<D>;
+  using RM = RowMap<HP>;
   constexpr int KK = LY::KK;
   constexpr int QB = kRowsPerWG / HP;                  // query rows per workgroup
   __shared__ __align__(16) uint8_t tiles[2][LY::TILE];
@@ -156,46 +183,45 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(PrefillParams p) {
   float wv[4][4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    const int r = wave * 64 + rt * 16 + c;              // gathered row of this lane's A data
-    const int t = qrow0 + r / HP, hs = r % HP;
+    int qr, hs;
+    RM::row(wave, rt, c, qr, hs);                       // row c of the tile: this lane's A data
+    const int t = qrow0 + qr;
     const bool rv = t < p.N && hs < p.h;
     int j = 0;
     if (rv) j = p.heads ? p.heads[static_cast<size_t>(t) * p.h + hs] : hs;
-    const uint16_t* qr = p.q + (static_cast<size_t>(rv ? t : 0) * p.H_I + j) * D;
+    const uint16_t* qrp = p.q + (static_cast<size_t>(rv ? t : 0) * p.H_I + j) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      u32x4_t x = *reinterpret_cast<const u32x4_t*>(qr + 32 * kk + 8 * g);
+      u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrp + 32 * kk + 8 * g);
       if (!rv) x = u32x4_t{0u, 0u, 0u, 0u};
       a[rt][kk] = __builtin_bit_cast(bf16x8_t, x);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rr = wave * 64 + rt * 16 + 4 * g + i;   // output row of this lane's results
-      const int tt = qrow0 + rr / HP, hh = rr % HP;
+      int qo, ho;
+      RM::row(wave, rt, 4 * g + i, qo, ho);             // output rows of this lane's results
+      const int tt = qrow0 + qo;
       float wf = 0.f;
-      if (tt < p.N && hh < p.h) {
-        const int jj = p.heads ? p.heads[static_cast<size_t>(tt) * p.h + hh] : hh;
+      if (tt < p.N && ho < p.h) {
+        const int jj = p.heads ? p.heads[static_cast<size_t>(tt) * p.h + ho] : ho;
         wf = p.w[static_cast<size_t>(tt) * p.H_I + jj];
       }
       wv[rt][i] = wf;
     }
   }
-  // query row (index in the block) whose sums this lane holds, per row tile
-  int wq[4];
+  // per query-row group: position (-1 = no row) and output row pointer
+  int opos[RM::NG];
+  uint32_t* urow[RM::NG];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int rbase = wave * 64 + rt * 16;
-    wq[rt] = HP >= 16 ? rbase / HP : (rbase + 4 * g) / HP;
+  for (int q = 0; q < RM::NG; ++q) {
+    const int qr = RM::out_row(wave, q, g);
+    opos[q] = pos_lds[qr];
+    const int t = qrow0 + qr;
+    urow[q] = p.u + static_cast<size_t>(t < p.N ? t : 0) * p.u_stride;
   }
   int minpos = 0x7FFFFFFF;                              // keys <= minpos are visible to every row
   for (int i = 0; i < QB; ++i) minpos = min(minpos, pos_lds[i] < 0 ? 0x7FFFFFFF : pos_lds[i]);
   const bool full_block = qrow0 + QB <= p.N;
-  uint32_t* urow[4];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int t = qrow0 + wq[rt];
-    urow[rt] = p.u + static_cast<size_t>(t < p.N ? t : 0) * p.u_stride;
-  }
 
   u32x4_t pre[LY::PER_THREAD];
   load_key_tile<D>(p.k, ks0, p.L, tid, pre);
@@ -208,9 +234,9 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(PrefillParams p) {
     // every (row, key) of the tile is visible: stores need no mask
     const bool unmasked = full_block && key0 + kKeyTile - 1 <= minpos;
     if (unmasked)
-      score_tile<HP, D, false>(tiles[buf], key0, a, wv, wq, urow, pos_lds, qrow0, p.N, g, c);
+      score_tile<HP, D, false>(tiles[buf], key0, a, wv, urow, opos, g, c);
     else
-      score_tile<HP, D, true>(tiles[buf], key0, a, wv, wq, urow, pos_lds, qrow0, p.N, g, c);
+      score_tile<HP, D, true>(tiles[buf], key0, a, wv, urow, opos, g, c);
     if (more) {
       store_key_tile<D>(tiles[buf ^ 1], tid, pre);
       __syncthreads();

@@ -32,7 +32,7 @@
  *                           row n sees keys 0..q_pos[n] (L_n = q_pos[n] + 1)
  *    Supported (q_dt, k_dt): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3);
  *    d in {64, 128}; 1 <= h <= H_I <= 64; 1 <= B <= 1024;
- *    1 <= topk <= 16384; N >= 1; S >= 1; 1 <= L < 2^31 / d.
+ *    1 <= topk <= 65536; 1 <= N <= 65535; 1 <= S <= 65535; 1 <= L <= 2^27.
  *  - Index-score: I(s) = sum over heads j of w[n,j] * ReLU(q[n,j,:] . key_s),
  *    accumulated in fp32 from exact bf16 (or fp8-dequantised) products.
  *  - Top-k outputs idx [N, topk] int32 and score [N, topk] float32 hold the
@@ -150,7 +150,11 @@ int32_t misa_rerank(const void* q, int32_t q_dt, const float* w, const void* k,
 /*
  * Workspace bytes for `op` at these sizes (0 for invalid sizes).  Arguments
  * an op does not use are ignored (k_prime only matters for MISA_OP_RERANK, B
- * only for MISA_OP_ROUTE).
+ * only for MISA_OP_ROUTE).  For MISA_OP_SCORE_TOPK with many rows over one
+ * long sequence (N >= 128, L >= 32768, topk <= 2048) the size includes the
+ * region of the sampled-threshold candidate path; a workspace that only
+ * covers the full path (the size for topk > 2048) is accepted too, and then
+ * that path runs.
  */
 size_t misa_workspace_bytes(int32_t op, int32_t N, int32_t L, int32_t d, int32_t H_I,
                             int32_t B, int32_t topk, int32_t k_prime);

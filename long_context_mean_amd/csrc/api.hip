@@ -18,6 +18,12 @@ constexpr int kMaxN = 65535;          // grid y limit
 constexpr int kMaxL = 1 << 27;
 constexpr int kMaxTopk = 65536;
 constexpr int kOneRowMinN = 128;      // rows at which one workgroup per row fills the chip
+// prefill candidate path: sampled threshold from every 32nd key
+constexpr int kSampleShift = 5;
+constexpr int kCandMinL = 32768;      // shorter sequences keep the full path
+constexpr int kCandMaxTopk = 2048;    // about 2 topk candidates must fit the LDS select
+constexpr int kCandRegion = 16384;    // candidate slots per row, shared evenly by the splits
+constexpr int kMaxSplits = 256;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -66,6 +72,44 @@ TopkLayout topk_layout(int N, int len_max) {
   return t;
 }
 
+// Candidate path region, placed after the full-path layout.
+struct CandLayout {
+  int us_stride = 0;
+  size_t off_us = 0, off_tau = 0, off_cnt = 0, off_cand = 0, off_rflag = 0, off_bflag = 0;
+  size_t bytes = 0;   // end offset
+};
+
+bool cand_eligible(int N, int L, int topk) {
+  return N >= kOneRowMinN && L >= kCandMinL && topk <= kCandMaxTopk;
+}
+
+CandLayout cand_layout(size_t start, int N, int L) {
+  CandLayout c;
+  c.us_stride = static_cast<int>(align_up(static_cast<size_t>((L + (1 << kSampleShift) - 1) >>
+                                                              kSampleShift), 64));
+  size_t off = align_up(start, 256);
+  c.off_us = off;
+  off = align_up(off + static_cast<size_t>(N) * c.us_stride * 4, 256);
+  c.off_tau = off;
+  off = align_up(off + static_cast<size_t>(N) * 4, 256);
+  c.off_cnt = off;
+  off = align_up(off + static_cast<size_t>(N) * kMaxSplits * 4, 256);
+  c.off_cand = off;
+  off = align_up(off + static_cast<size_t>(N) * kCandRegion * 8, 256);
+  c.off_rflag = off;
+  off = align_up(off + static_cast<size_t>(N) * 4, 256);
+  c.off_bflag = off;
+  off = align_up(off + static_cast<size_t>(N) * 4, 256);
+  c.bytes = off;
+  return c;
+}
+
+size_t score_topk_bytes(int N, int L, int topk) {
+  const TopkLayout t = topk_layout(N, L);
+  if (!cand_eligible(N, L, topk)) return t.bytes;
+  return cand_layout(t.bytes, N, L).bytes;
+}
+
 int route_chunks(int L, int B) {
   const int mf = L / B;
   const int per = misa::route_blocks_per_chunk();
@@ -107,7 +151,47 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* w, const void*
   hipError_t e = hipSuccess;
   if (hist) e = misa::launch_clear(hist, static_cast<size_t>(N) * misa::kHistWords, st);
   if (e != hipSuccess) return hip_status(e);
-  if (S == 1 && lay.one_row && N >= kOneRowMinN && q_dt == MISA_BF16 && k_dt == MISA_BF16) {
+  const bool gemm = S == 1 && lay.one_row && N >= kOneRowMinN && q_dt == MISA_BF16 &&
+                    k_dt == MISA_BF16;
+  if (gemm && cand_eligible(N, L, topk) && ws_bytes >= cand_layout(lay.bytes, N, L).bytes) {
+    // many rows over one sequence, candidate path: sampled thresholds, GEMM
+    // keeping only the keys above them, exact select; unproven rows redo the
+    // full path
+    const CandLayout cl = cand_layout(lay.bytes, N, L);
+    const int h_eff = heads ? h : H_I;
+    const int qb = misa::prefill_rows_per_block(h_eff);
+    const int splits = misa::prefill_splits(N, L, h_eff);
+    const int cap = kCandRegion / splits;
+    uint32_t* us = reinterpret_cast<uint32_t*>(base + cl.off_us);
+    uint32_t* tau = reinterpret_cast<uint32_t*>(base + cl.off_tau);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(base + cl.off_cnt);
+    uint2* cand = reinterpret_cast<uint2*>(base + cl.off_cand);
+    uint32_t* rflag = reinterpret_cast<uint32_t*>(base + cl.off_rflag);
+    uint32_t* bflag = reinterpret_cast<uint32_t*>(base + cl.off_bflag);
+    misa::PrefillArgs sp{q, w, k, q_pos, heads, N, L, d, H_I, h, us, cl.us_stride};
+    sp.key_step = 1 << kSampleShift;
+    sp.pos_shift = kSampleShift;
+    sp.kernel_id = misa::K_PREFILL_SAMPLE;
+    if ((e = misa::launch_prefill(sp, st)) != hipSuccess) return hip_status(e);
+    misa::TauArgs ta{us, cl.us_stride, q_pos, N, topk, kSampleShift, qb, tau, bflag};
+    if ((e = misa::launch_tau(ta, st)) != hipSuccess) return hip_status(e);
+    misa::PrefillArgs mp{q, w, k, q_pos, heads, N, L, d, H_I, h, nullptr, 0};
+    mp.tau = tau;
+    mp.cnt_out = cnt;
+    mp.cand_out = cand;
+    mp.cap = cap;
+    if ((e = misa::launch_prefill(mp, st)) != hipSuccess) return hip_status(e);
+    misa::CandTopkArgs ca{cnt, cand, splits, cap, q_pos, N, topk, qb, rflag, bflag, idx, score};
+    if ((e = misa::launch_cand_topk(ca, st)) != hipSuccess) return hip_status(e);
+    misa::PrefillArgs fp{q, w, k, q_pos, heads, N, L, d, H_I, h, u, lay.u_stride};
+    fp.block_flag = bflag;
+    fp.kernel_id = misa::K_PREFILL_FULL;
+    if ((e = misa::launch_prefill(fp, st)) != hipSuccess) return hip_status(e);
+    misa::TopkArgs ft{u, lay.u_stride, q_pos, 0, N, topk, true, nullptr, nullptr, 0, idx, score};
+    ft.row_flag = rflag;
+    return hip_status(misa::launch_topk(ft, st));
+  }
+  if (gemm) {
     // many rows over one sequence: GEMM over the gathered head rows
     misa::PrefillArgs pa{q, w, k, q_pos, heads, N, L, d, H_I, h, u, lay.u_stride};
     e = misa::launch_prefill(pa, st);
@@ -161,14 +245,14 @@ int32_t misa_last_hip_error(void) { return g_last_hip; }
 size_t misa_workspace_bytes(int32_t op, int32_t N, int32_t L, int32_t d, int32_t H_I, int32_t B,
                             int32_t topk, int32_t k_prime) {
   (void)d;
-  (void)topk;
   if (N < 1 || N > kMaxN || L < 1 || L > kMaxL || H_I < 1 || H_I > 64) return 0;
   switch (op) {
     case MISA_OP_ROUTE:
       if (B < 1 || B > 1024) return 0;
       return route_bytes(N, L, B, H_I);
     case MISA_OP_SCORE_TOPK:
-      return topk_layout(N, L).bytes;
+      if (topk < 1 || topk > kMaxTopk) return 0;
+      return score_topk_bytes(N, L, topk);
     case MISA_OP_RERANK: {
       if (k_prime < 1 || k_prime > kMaxTopk) return 0;
       TopkLayout t = topk_layout(kOneRowMinN, k_prime);   // always one row per workgroup
@@ -296,7 +380,8 @@ const char* misa_kernel_name(int32_t kernel_id) {
   static const char* names[misa::K_COUNT_IDS] = {
       "pool_kernel",       "route_partial_kernel", "route_select_kernel", "topk_clear_kernel",
       "score_mfma_kernel", "score_f32_kernel",     "score_prefill_kernel",
-      "topk_collect_kernel", "topk_final_kernel",   "topk_row_kernel"};
+      "topk_collect_kernel", "topk_final_kernel",   "topk_row_kernel",
+      "score_prefill_sample", "score_prefill_full", "topk_tau_kernel", "topk_cand_kernel"};
   if (kernel_id < 0 || kernel_id >= misa::K_COUNT_IDS) return "unknown";
   return names[kernel_id];
 }

@@ -18,6 +18,10 @@ enum KernelId : int {
   K_TOPK_COLLECT,
   K_TOPK_FINAL,
   K_TOPK_ROW,
+  K_PREFILL_SAMPLE,
+  K_PREFILL_FULL,
+  K_TOPK_TAU,
+  K_TOPK_CAND,
   K_COUNT_IDS
 };
 
@@ -84,7 +88,15 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------- prefill scoring
 // Rows that all read one key sequence (bf16 q and keys): MFMA GEMM over the
-// gathered routed head rows; writes order keys u[t, s] for s <= q_pos[t].
+// gathered routed head rows.
+//  plain mode (cand_out NULL): writes order keys u[t, s] for s <= q_pos[t];
+//    with key_step > 1 it scores only keys key_step*s' (s' <= q_pos[t] >>
+//    pos_shift) and writes them to u[t, s'].  With block_flag, row blocks
+//    whose flag is 0 are skipped.
+//  candidate mode: writes no u; every visible (t, s) with order key >= tau[t]
+//    is appended as (key, s) to cand_out[(t * splits + split) * cap + slot]
+//    (slots past cap are dropped) and cnt_out[t * splits + split] receives
+//    the number of such keys (which may exceed cap).
 struct PrefillArgs {
   const void* q;
   const float* w;
@@ -94,7 +106,17 @@ struct PrefillArgs {
   int N, L, d, H_I, h;
   uint32_t* u;
   int u_stride;
+  int key_step = 1;
+  int pos_shift = 0;
+  const uint32_t* block_flag = nullptr;
+  const uint32_t* tau = nullptr;
+  uint32_t* cnt_out = nullptr;
+  uint2* cand_out = nullptr;
+  int cap = 0;
+  int kernel_id = K_SCORE_PREFILL;
 };
+int prefill_rows_per_block(int h_eff);
+int prefill_splits(int N, int L, int h_eff);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------- top-k
@@ -110,10 +132,44 @@ struct TopkArgs {
   int cand_stride;
   int32_t* idx;
   float* score;
+  const uint32_t* row_flag = nullptr;   // one-row mode: rows whose flag is 0 are skipped
 };
 int topk_chunk();
 size_t topk_few_rows_bytes(int N, int u_stride);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 hipError_t launch_clear(uint32_t* p, size_t n_words, hipStream_t st);
+
+// Sampled threshold per row (prefill candidate path): from the sample order
+// keys us[n, 0 .. (q_pos[n] >> sample_shift)], a key tau[n] such that about
+// 2 * min(topk, L_n) of the row's keys are expected at or above it.  Also
+// clears block_flag[n / rows_per_block].
+struct TauArgs {
+  const uint32_t* us;
+  int us_stride;
+  const int32_t* q_pos;
+  int N, topk, sample_shift, rows_per_block;
+  uint32_t* tau;
+  uint32_t* block_flag;
+};
+hipError_t launch_tau(const TauArgs& a, hipStream_t st);
+
+// Exact top-k of each row from its candidate list (the keys >= tau[n]).  A row
+// whose candidates cannot prove the result (a split list overflowed, fewer
+// than min(topk, L_n) candidates, too many candidates or ties for the LDS
+// path) is flagged in row_flag[n] and block_flag[n / rows_per_block] and left
+// to the full path; other rows get idx/score written and row_flag[n] = 0.
+struct CandTopkArgs {
+  const uint32_t* cnt;
+  const uint2* cand;
+  int splits, cap;
+  const int32_t* q_pos;
+  int N, topk, rows_per_block;
+  uint32_t* row_flag;
+  uint32_t* block_flag;
+  int32_t* idx;
+  float* score;
+};
+int cand_topk_capacity();
+hipError_t launch_cand_topk(const CandTopkArgs& a, hipStream_t st);
 
 }  // namespace misa

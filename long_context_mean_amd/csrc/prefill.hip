@@ -39,6 +39,12 @@ struct PrefillParams {
   int keys_per_split;        // multiple of kKeyTile
   uint32_t* u;
   int u_stride;
+  int key_step, pos_shift;   // scored keys are key_step * s (sample pass: s <= pos >> pos_shift)
+  const uint32_t* block_flag;
+  const uint32_t* tau;       // candidate mode
+  uint32_t* cnt_out;
+  uint2* cand_out;
+  int cap, splits;
 };
 
 template <int D>
@@ -52,17 +58,19 @@ struct PLayout {
   static constexpr int PIECES_PER_ROW = ROW / 16;
 };
 
+// Key rows key_step * s for s in [key0, key0 + 64); s >= L (in the same units)
+// reads row 0 instead (masked later).
 template <int D>
-__device__ __forceinline__ void load_key_tile(const uint8_t* k, int key0, int L, int tid,
-                                              u32x4_t (&r)[PLayout<D>::PER_THREAD]) {
+__device__ __forceinline__ void load_key_tile(const uint8_t* k, int key0, int L, int key_step,
+                                              int tid, u32x4_t (&r)[PLayout<D>::PER_THREAD]) {
   using LY = PLayout<D>;
 #pragma unroll
   for (int i = 0; i < LY::PER_THREAD; ++i) {
     const int f = tid + 256 * i;
     int key = key0 + f / LY::PIECES_PER_ROW;
-    key = key < L ? key : L - 1;                      // past the end: any valid row, masked later
-    r[i] = *reinterpret_cast<const u32x4_t*>(k + static_cast<size_t>(key) * LY::ROW +
-                                             16 * (f % LY::PIECES_PER_ROW));
+    key = key < L ? key : 0;
+    r[i] = *reinterpret_cast<const u32x4_t*>(
+        k + static_cast<size_t>(key) * key_step * LY::ROW + 16 * (f % LY::PIECES_PER_ROW));
   }
 }
 
@@ -108,15 +116,25 @@ struct RowMap {
   }
 };
 
-// One LDS key tile (64 keys) against the wavefront's 4 row tiles; writes the
-// order keys.  MASK: some (row, key) of the tile may be outside the causal
-// prefix or the row block.
-template <int HP, int D, bool MASK>
+// Per-lane output state of the epilogue, one entry per query-row group.
+template <int HP, bool CAND>
+struct OutState {
+  static constexpr int NG = RowMap<HP>::NG;
+  int pos[NG];             // key s is visible iff s <= pos (-1: no row)
+  uint32_t* urow;          // plain mode: order-key row of group 0 (group q: + q * step)
+  uint2* crow;             // candidate mode: (key, token) list of group 0's row and split
+  size_t step;             // elements from one group's row to the next
+  uint32_t tau[NG];        // candidate mode: threshold key
+  uint32_t cnt[NG];        // candidate mode: keys >= tau so far (uniform over the lane group)
+};
+
+// One LDS key tile (64 keys) against the wavefront's 4 row tiles.  MASK: some
+// (row, key) of the tile may be outside the causal prefix or the row block.
+template <int HP, int D, bool MASK, bool CAND>
 __device__ __forceinline__ void score_tile(const uint8_t* tile, int key0,
                                            const bf16x8_t (&a)[4][PLayout<D>::KK],
-                                           const float (&wv)[4][4],
-                                           uint32_t* const (&urow)[RowMap<HP>::NG],
-                                           const int (&opos)[RowMap<HP>::NG], int g, int c) {
+                                           const float (&wv)[4][4], OutState<HP, CAND>& o,
+                                           int cap, int g, int c) {
   using LY = PLayout<D>;
   using RM = RowMap<HP>;
   constexpr int KK = LY::KK;
@@ -130,7 +148,7 @@ __device__ __forceinline__ void score_tile(const uint8_t* tile, int key0,
                                                16 * g));
     float v[RM::NG];
 #pragma unroll
-    for (int p = 0; p < RM::NG; ++p) v[p] = 0.f;
+    for (int q = 0; q < RM::NG; ++q) v[q] = 0.f;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -142,20 +160,34 @@ __device__ __forceinline__ void score_tile(const uint8_t* tile, int key0,
     }
     const int key = key0 + ct * 16 + c;
 #pragma unroll
-    for (int p = 0; p < RM::NG; ++p) {
-      float x = v[p];
+    for (int q = 0; q < RM::NG; ++q) {
+      float x = v[q];
       if constexpr (!RM::IN_LANE) {
         x += __shfl_xor(x, 16, 64);
         x += __shfl_xor(x, 32, 64);
       }
       const uint32_t kv = order_key(x);
       const bool owner = RM::IN_LANE || g == 0;
-      if (owner && (!MASK || key <= opos[p])) urow[p][key] = kv;
+      const bool vis = owner && (!MASK || key <= o.pos[q]);
+      if constexpr (!CAND) {
+        if (vis) o.urow[q * o.step + key] = kv;
+      } else {
+        const bool pass = vis && kv >= o.tau[q];
+        const uint64_t m = __ballot(pass);
+        if (m != 0u) {
+          // slots in key order within the lane group (16 keys of one query row)
+          const uint32_t grp = static_cast<uint32_t>(m >> (16 * g)) & 0xFFFFu;
+          const uint32_t slot = o.cnt[q] + __popc(grp & ((1u << c) - 1u));
+          if (pass && slot < static_cast<uint32_t>(cap))
+            o.crow[q * o.step + slot] = make_uint2(kv, key);
+          o.cnt[q] += __popc(grp);
+        }
+      }
     }
   }
 }
 
-template <int HP, int D>
+template <int HP, int D, bool CAND>
 __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(PrefillParams p) {
   using LY = PLayout<D>;
   using RM = RowMap<HP>;
@@ -164,19 +196,27 @@ __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(Pre
   __shared__ __align__(16) uint8_t tiles[2][LY::TILE];
   __shared__ int pos_lds[QB];
 
+  if (p.block_flag && p.block_flag[blockIdx.y] == 0u) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int qrow0 = blockIdx.y * QB;
   for (int i = tid; i < QB; i += 256) {
     const int t = qrow0 + i;
-    pos_lds[i] = t < p.N ? p.q_pos[t] : -1;
+    pos_lds[i] = t < p.N ? (p.q_pos[t] >> p.pos_shift) : -1;
   }
   __syncthreads();
   int kmax = 0;                                         // keys [0, kmax) are visible to some row
   for (int i = 0; i < QB; ++i) kmax = max(kmax, pos_lds[i] + 1);
   const int ks0 = blockIdx.x * p.keys_per_split;
   const int ks1 = min(ks0 + p.keys_per_split, kmax);
-  if (ks0 >= ks1) return;
+  if (ks0 >= ks1) {
+    if constexpr (CAND) {
+      for (int i = tid; i < QB; i += 256)
+        if (qrow0 + i < p.N)
+          p.cnt_out[static_cast<size_t>(qrow0 + i) * p.splits + blockIdx.x] = 0u;
+    }
+    return;
+  }
 
   // A operand (4 row tiles of this wavefront) and the weights of the lane's rows
   bf16x8_t a[4][KK];
@@ -209,40 +249,63 @@ __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(Pre
       wv[rt][i] = wf;
     }
   }
-  // per query-row group: position (-1 = no row) and output row pointer
-  int opos[RM::NG];
-  uint32_t* urow[RM::NG];
+  OutState<HP, CAND> o;
+  // group q's row is group 0's row + q * rstep (rows past N are never written)
+  constexpr int rstep = RM::IN_LANE ? 4 : 1;
+  const size_t t0 = static_cast<size_t>(qrow0 + RM::out_row(wave, 0, g));
+  if constexpr (CAND) {
+    o.crow = p.cand_out + (t0 * p.splits + blockIdx.x) * p.cap;
+    o.step = static_cast<size_t>(rstep) * p.splits * p.cap;
+  } else {
+    o.urow = p.u + t0 * p.u_stride;
+    o.step = static_cast<size_t>(rstep) * p.u_stride;
+  }
 #pragma unroll
   for (int q = 0; q < RM::NG; ++q) {
     const int qr = RM::out_row(wave, q, g);
-    opos[q] = pos_lds[qr];
+    o.pos[q] = pos_lds[qr];
     const int t = qrow0 + qr;
-    urow[q] = p.u + static_cast<size_t>(t < p.N ? t : 0) * p.u_stride;
+    if constexpr (CAND) {
+      o.tau[q] = t < p.N ? p.tau[t] : 0xFFFFFFFFu;
+      o.cnt[q] = 0u;
+    }
   }
   int minpos = 0x7FFFFFFF;                              // keys <= minpos are visible to every row
   for (int i = 0; i < QB; ++i) minpos = min(minpos, pos_lds[i] < 0 ? 0x7FFFFFFF : pos_lds[i]);
   const bool full_block = qrow0 + QB <= p.N;
 
   u32x4_t pre[LY::PER_THREAD];
-  load_key_tile<D>(p.k, ks0, p.L, tid, pre);
+  load_key_tile<D>(p.k, ks0, p.L, p.key_step, tid, pre);
   store_key_tile<D>(tiles[0], tid, pre);
   __syncthreads();
   int buf = 0;
   for (int key0 = ks0; key0 < ks1; key0 += kKeyTile) {
     const bool more = key0 + kKeyTile < ks1;
-    if (more) load_key_tile<D>(p.k, key0 + kKeyTile, p.L, tid, pre);
-    // every (row, key) of the tile is visible: stores need no mask
+    if (more) load_key_tile<D>(p.k, key0 + kKeyTile, p.L, p.key_step, tid, pre);
+    // every (row, key) of the tile is visible: no masks
     const bool unmasked = full_block && key0 + kKeyTile - 1 <= minpos;
     if (unmasked)
-      score_tile<HP, D, false>(tiles[buf], key0, a, wv, urow, opos, g, c);
+      score_tile<HP, D, false, CAND>(tiles[buf], key0, a, wv, o, p.cap, g, c);
     else
-      score_tile<HP, D, true>(tiles[buf], key0, a, wv, urow, opos, g, c);
+      score_tile<HP, D, true, CAND>(tiles[buf], key0, a, wv, o, p.cap, g, c);
     if (more) {
       store_key_tile<D>(tiles[buf ^ 1], tid, pre);
       __syncthreads();
       buf ^= 1;
     }
   }
+  if constexpr (CAND) {
+#pragma unroll
+    for (int q = 0; q < RM::NG; ++q) {
+      const int t = qrow0 + RM::out_row(wave, q, g);
+      if (c == 0 && (RM::IN_LANE || g == 0) && t < p.N)
+        p.cnt_out[static_cast<size_t>(t) * p.splits + blockIdx.x] = o.cnt[q];
+    }
+  }
+}
+
+int hp_of(int h) {
+  return h <= 4 ? 4 : h <= 8 ? 8 : h <= 16 ? 16 : h <= 32 ? 32 : 64;
 }
 
 template <int HP, int D>
@@ -254,33 +317,56 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   p.q_pos = a.q_pos;
   p.heads = a.heads;
   p.N = a.N;
-  p.L = a.L;
   p.H_I = a.H_I;
   p.h = a.heads ? a.h : a.H_I;
   p.u = a.u;
   p.u_stride = a.u_stride;
+  p.key_step = a.key_step;
+  p.pos_shift = a.pos_shift;
+  p.L = (a.L + a.key_step - 1) / a.key_step;           // keys in scored units
+  p.block_flag = a.block_flag;
+  p.tau = a.tau;
+  p.cnt_out = a.cnt_out;
+  p.cand_out = a.cand_out;
+  p.cap = a.cap;
   constexpr int QB = kRowsPerWG / HP;
   const int qblocks = (a.N + QB - 1) / QB;
-  // split the key range so the grid has at least ~4 workgroups per CU
-  int splits = 1;
-  while (qblocks * splits < 1024 && a.L / (splits * 2) >= 4 * kKeyTile) splits *= 2;
-  p.keys_per_split = ((a.L + splits - 1) / splits + kKeyTile - 1) / kKeyTile * kKeyTile;
-  MISA_LAUNCH(K_SCORE_PREFILL, (score_prefill_kernel<HP, D>), dim3(splits, qblocks), dim3(256),
-              0, st, p);
+  const int splits = prefill_splits(a.N, p.L, HP);
+  p.splits = splits;
+  p.keys_per_split = ((p.L + splits - 1) / splits + kKeyTile - 1) / kKeyTile * kKeyTile;
+  if (a.cand_out)
+    MISA_LAUNCH(a.kernel_id, (score_prefill_kernel<HP, D, true>), dim3(splits, qblocks),
+                dim3(256), 0, st, p);
+  else
+    MISA_LAUNCH(a.kernel_id, (score_prefill_kernel<HP, D, false>), dim3(splits, qblocks),
+                dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const PrefillArgs& a, hipStream_t st) {
-  const int h = a.heads ? a.h : a.H_I;
-  if (h <= 4) return launch_t<4, D>(a, st);
-  if (h <= 8) return launch_t<8, D>(a, st);
-  if (h <= 16) return launch_t<16, D>(a, st);
-  if (h <= 32) return launch_t<32, D>(a, st);
-  return launch_t<64, D>(a, st);
+  switch (hp_of(a.heads ? a.h : a.H_I)) {
+    case 4: return launch_t<4, D>(a, st);
+    case 8: return launch_t<8, D>(a, st);
+    case 16: return launch_t<16, D>(a, st);
+    case 32: return launch_t<32, D>(a, st);
+    default: return launch_t<64, D>(a, st);
+  }
 }
 
 }  // namespace
+
+int prefill_rows_per_block(int h_eff) { return kRowsPerWG / hp_of(h_eff); }
+
+// Key-range splits of the GEMM grid: enough workgroups to fill the chip
+// (about 4 per CU), each split at least 4 key tiles long; at most 256.
+int prefill_splits(int N, int L, int h_eff) {
+  const int qb = prefill_rows_per_block(h_eff);
+  const int qblocks = (N + qb - 1) / qb;
+  int splits = 1;
+  while (splits < 256 && qblocks * splits < 1024 && L / (splits * 2) >= 4 * kKeyTile) splits *= 2;
+  return splits;
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   return a.d == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);

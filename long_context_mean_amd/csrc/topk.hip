@@ -91,6 +91,32 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t K, boo
   __syncthreads();
 }
 
+// Ties at the threshold: among the n_eq candidates whose key equals T, the K2
+// lowest token indices win (K2 <= n_eq).  Returns the largest winning index.
+// Radix select on the indices (< 2^18: bits 6..17, then 0..5) in hA (4096
+// words) and hB (64 words); every thread calls it.
+template <int NT>
+__device__ __forceinline__ uint32_t tie_cut(const uint32_t* cu, const uint32_t* ci, int total,
+                                            uint32_t T, uint32_t K2, uint32_t n_eq, uint32_t* hA,
+                                            uint32_t* hB, uint32_t* sm, uint32_t* res) {
+  for (int b = threadIdx.x; b < 4096; b += NT) hA[b] = 0u;
+  if (threadIdx.x < 64) hB[threadIdx.x] = 0u;
+  __syncthreads();
+  for (int i = threadIdx.x; i < total; i += NT)
+    if (cu[i] == T) atomicAdd(&hA[ci[i] >> 6], 1u);
+  __syncthreads();
+  // the K2-th smallest index is the (n_eq - K2 + 1)-th largest
+  find_digit<NT, 4096>(hA, n_eq - K2 + 1u, false, sm, res);
+  const uint32_t dA = res[0], rA = res[1];
+  for (int i = threadIdx.x; i < total; i += NT)
+    if (cu[i] == T && (ci[i] >> 6) == dA) atomicAdd(&hB[ci[i] & 63u], 1u);
+  __syncthreads();
+  find_digit<NT, 64>(hB, rA, false, sm, res);
+  const uint32_t cut = (dA << 6) | res[0];
+  __syncthreads();
+  return cut;
+}
+
 struct Threshold {
   uint32_t T;     // exact k-th largest key
   uint32_t K2;    // number of key == T elements to take (lowest indices)
@@ -349,8 +375,6 @@ __global__ __launch_bounds__(1024) void topk_final_kernel(
     K2 = res[1];
     n_eq = hB[res[0]];                    // candidates whose key equals T
     __syncthreads();
-    // ties beyond what the quadratic rank below handles: use the full path
-    fallback = n_eq != K2 && n_eq > 2048u;
   }
   if (fallback) {
     for (int b = threadIdx.x; b < kBins0; b += 1024) hA[b] = h0g[b];
@@ -366,20 +390,12 @@ __global__ __launch_bounds__(1024) void topk_final_kernel(
 
   // mark the candidate winners: key > T, or key == T among the K2 lowest
   // indices (all ties win when n_eq == K2, the usual case)
+  const uint32_t cut = n_eq == K2 ? 0xFFFFFFFFu
+                                  : tie_cut<1024>(cu, ci, static_cast<int>(c), T, K2, n_eq, hA,
+                                                  hB, sm, res);
   for (int i = threadIdx.x; i < static_cast<int>(c); i += 1024) {
     const uint32_t kv = cu[i], e = ci[i];
-    bool win = kv > T;
-    if (kv == T) {
-      if (n_eq == K2) {
-        win = true;
-      } else {
-        uint32_t rank = 0;
-        for (int j2 = 0; j2 < static_cast<int>(c); ++j2)
-          rank += (cu[j2] == T && ci[j2] < e) ? 1u : 0u;
-        win = rank < K2;
-      }
-    }
-    if (win) atomicOr(&bm[e >> 5], 1u << (e & 31));
+    if (kv > T || (kv == T && e <= cut)) atomicOr(&bm[e >> 5], 1u << (e & 31));
   }
   __syncthreads();
 
@@ -426,7 +442,7 @@ __global__ void topk_clear_kernel(uint32_t* __restrict__ p, size_t n_words) {
 __global__ __launch_bounds__(1024) void topk_row_kernel(
     const uint32_t* __restrict__ u, int u_stride, const int32_t* q_pos, int fixed_len, int topk,
     const int32_t* __restrict__ cand, int cand_stride, int32_t* __restrict__ idx,
-    float* __restrict__ score) {
+    float* __restrict__ score, const uint32_t* __restrict__ row_flag) {
   __shared__ __align__(16) uint32_t bm[kBitmapWords];
   __shared__ __align__(16) uint32_t cu[kCandCap];
   __shared__ __align__(16) uint32_t ci[kCandCap];
@@ -436,6 +452,7 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(
   __shared__ uint32_t res[4];
   __shared__ uint32_t n_cand;
   const int n = blockIdx.x;
+  if (row_flag && row_flag[n] == 0u) return;
   const int len = row_len(q_pos, fixed_len, n);
   const uint32_t* row = u + static_cast<size_t>(n) * u_stride;
   const int32_t* cand_row = cand ? cand + static_cast<size_t>(n) * cand_stride : nullptr;
@@ -511,25 +528,14 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(
   const uint32_t K2 = res[1];
   const uint32_t n_eq = hB[res[0]];
   __syncthreads();
-  if (n_eq != K2 && n_eq > 2048u) {
-    row_select<1024>(row, len, topk, cand_row, idx_row, score_row, hA, cu, hB, false, sm, res);
-    return;
-  }
-  // mark candidate winners (ties: the K2 lowest element indices)
+  // mark the candidate winners: key > T, or key == T among the K2 lowest
+  // indices (all ties win when n_eq == K2, the usual case)
+  const uint32_t cut = n_eq == K2 ? 0xFFFFFFFFu
+                                  : tie_cut<1024>(cu, ci, static_cast<int>(c), T, K2, n_eq, hA,
+                                                  hB, sm, res);
   for (int i = threadIdx.x; i < static_cast<int>(c); i += 1024) {
     const uint32_t kv = cu[i], e = ci[i];
-    bool win = kv > T;
-    if (kv == T) {
-      if (n_eq == K2) {
-        win = true;
-      } else {
-        uint32_t rank = 0;
-        for (int j2 = 0; j2 < static_cast<int>(c); ++j2)
-          rank += (cu[j2] == T && ci[j2] < e) ? 1u : 0u;
-        win = rank < K2;
-      }
-    }
-    if (win) atomicOr(&bm[e >> 5], 1u << (e & 31));
+    if (kv > T || (kv == T && e <= cut)) atomicOr(&bm[e >> 5], 1u << (e & 31));
   }
   __syncthreads();
   // ordered emit of every marked element
@@ -560,6 +566,177 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(
   }
 }
 
+
+// ---------------------------------------------------------------- prefill candidate path
+// A row's exact top-k only needs the keys at or above any threshold that at
+// least min(k, L_n) keys reach.  topk_tau picks such a threshold per row from
+// a strided sample of the row's scores (aiming at about twice the wanted
+// count), the scoring GEMM keeps only the keys at or above it, and
+// topk_cand selects exactly among them.  Whether the threshold was low enough
+// is checked exactly (the candidate count), so a poor sample only costs time:
+// such rows are flagged and take the full path.
+
+constexpr int kCandRow = 8192;        // candidates per row resolved in LDS
+
+__global__ __launch_bounds__(256) void topk_tau_kernel(const uint32_t* __restrict__ us,
+                                                       int us_stride,
+                                                       const int32_t* __restrict__ q_pos,
+                                                       int topk, int shift, int rows_per_block,
+                                                       uint32_t* __restrict__ tau,
+                                                       uint32_t* __restrict__ block_flag) {
+  __shared__ __align__(16) uint32_t hA[kBins0];
+  __shared__ uint32_t sm[4];
+  __shared__ uint32_t res[4];
+  const int n = blockIdx.x;
+  if (threadIdx.x == 0 && n % rows_per_block == 0) block_flag[n / rows_per_block] = 0u;
+  const int pos = q_pos[n];
+  const int len = pos + 1;
+  const int m = (pos >> shift) + 1;                    // visible samples
+  const int K = min(topk, len);
+  // sample rank whose key about 2K of the row's keys reach; at least
+  // min(K, 32), since the sampled keys are row keys themselves
+  long long r = (2LL * K * m + len - 1) / len;
+  r = max(r, static_cast<long long>(min(K, 32)));
+  r = min(r, static_cast<long long>(m));
+  const uint32_t* row = us + static_cast<size_t>(n) * us_stride;
+  for (int b = threadIdx.x; b < kBins0; b += 256) hA[b] = 0u;
+  __syncthreads();
+  for (int i = threadIdx.x; i < m; i += 256) atomicAdd(&hA[row[i] >> kShift0], 1u);
+  __syncthreads();
+  find_digit<256, kBins0>(hA, static_cast<uint32_t>(r), true, sm, res);
+  const uint32_t d0 = res[0], r0 = res[1];
+  for (int b = threadIdx.x; b < kBins1; b += 256) hA[b] = 0u;
+  __syncthreads();
+  for (int i = threadIdx.x; i < m; i += 256) {
+    const uint32_t v = row[i];
+    if ((v >> kShift0) == d0) atomicAdd(&hA[(v >> kShift1) & (kBins1 - 1)], 1u);
+  }
+  __syncthreads();
+  find_digit<256, kBins1>(hA, r0, false, sm, res);
+  if (threadIdx.x == 0) {
+    const uint32_t t = (d0 << kShift0) | (res[0] << kShift1);
+    tau[n] = t > 0u ? t : 1u;                          // key 0 marks empty slots
+  }
+}
+
+// One 1024-thread workgroup per row.
+__global__ __launch_bounds__(1024) void topk_cand_kernel(
+    const uint32_t* __restrict__ cnt, const uint2* __restrict__ cand, int splits, int cap,
+    const int32_t* __restrict__ q_pos, int topk, int rows_per_block,
+    uint32_t* __restrict__ row_flag, uint32_t* __restrict__ block_flag,
+    int32_t* __restrict__ idx, float* __restrict__ score) {
+  __shared__ __align__(16) uint32_t cu[kCandRow];
+  __shared__ __align__(16) uint32_t ci[kCandRow];
+  __shared__ __align__(16) uint32_t bm[kBitmapWords];
+  __shared__ __align__(16) uint32_t hA[kBins0];
+  __shared__ __align__(16) uint32_t hB[kBins2];
+  __shared__ uint32_t tpre[1024];
+  __shared__ uint32_t spre[257];
+  __shared__ uint32_t sm[16];
+  __shared__ uint32_t res[4];
+  __shared__ uint32_t bad;
+  const int n = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int len = q_pos[n] + 1;
+  const uint32_t K = static_cast<uint32_t>(min(topk, len));
+  const int nwords = (len + 31) / 32;
+  // split counts -> offsets; overflow check
+  uint32_t cs = 0;
+  if (tid < splits) cs = cnt[static_cast<size_t>(n) * splits + tid];
+  if (tid == 0) bad = 0u;
+  __syncthreads();
+  if (cs > static_cast<uint32_t>(cap)) bad = 1u;
+  uint32_t total;
+  const uint32_t before = block_excl_scan<1024>(cs, sm, total);
+  if (tid < splits) spre[tid] = before;
+  if (tid == 0) spre[splits] = total;
+  __syncthreads();
+  const bool flag = bad != 0u || total < K || total > static_cast<uint32_t>(kCandRow) ||
+                    nwords > kBitmapWords;
+  if (flag) {
+    if (tid == 0) {
+      row_flag[n] = 1u;
+      atomicOr(&block_flag[n / rows_per_block], 1u);
+    }
+    return;
+  }
+  // gather the candidates: element j lives in split s with spre[s] <= j < spre[s+1]
+  for (int j = tid; j < static_cast<int>(total); j += 1024) {
+    int lo = 0, hi = splits - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (spre[mid] <= static_cast<uint32_t>(j)) lo = mid; else hi = mid - 1;
+    }
+    const uint2 e = cand[(static_cast<size_t>(n) * splits + lo) * cap + (j - spre[lo])];
+    cu[j] = e.x;
+    ci[j] = e.y;
+  }
+  for (int b = tid; b < kBins0; b += 1024) hA[b] = 0u;
+  if (tid < kBins2) hB[tid] = 0u;
+  __syncthreads();
+  // exact threshold: three radix levels over the candidates
+  for (int i = tid; i < static_cast<int>(total); i += 1024) atomicAdd(&hA[cu[i] >> kShift0], 1u);
+  __syncthreads();
+  find_digit<1024, kBins0>(hA, K, false, sm, res);
+  const uint32_t d0 = res[0], r0 = res[1];
+  for (int b = tid; b < kBins1; b += 1024) hA[b] = 0u;
+  __syncthreads();
+  for (int i = tid; i < static_cast<int>(total); i += 1024)
+    if ((cu[i] >> kShift0) == d0) atomicAdd(&hA[(cu[i] >> kShift1) & (kBins1 - 1)], 1u);
+  __syncthreads();
+  find_digit<1024, kBins1>(hA, r0, false, sm, res);
+  const uint32_t d1 = res[0], r1 = res[1];
+  const uint32_t pre = (d0 << kDigit1Bits) | d1;
+  for (int i = tid; i < static_cast<int>(total); i += 1024)
+    if ((cu[i] >> kShift1) == pre) atomicAdd(&hB[cu[i] & (kBins2 - 1)], 1u);
+  __syncthreads();
+  find_digit<1024, kBins2>(hB, r1, false, sm, res);
+  const uint32_t T = (d0 << kShift0) | (d1 << kShift1) | res[0];
+  const uint32_t K2 = res[1];
+  const uint32_t n_eq = hB[res[0]];
+  __syncthreads();
+  if (tid == 0) row_flag[n] = 0u;
+  for (int w = tid; w < nwords; w += 1024) bm[w] = 0u;
+  // mark the winners (ties: the K2 lowest token indices)
+  const uint32_t cut = n_eq == K2 ? 0xFFFFFFFFu
+                                  : tie_cut<1024>(cu, ci, static_cast<int>(total), T, K2, n_eq,
+                                                  hA, hB, sm, res);
+  __syncthreads();
+  for (int i = tid; i < static_cast<int>(total); i += 1024) {
+    const uint32_t kv = cu[i], e = ci[i];
+    if (kv > T || (kv == T && e <= cut)) atomicOr(&bm[e >> 5], 1u << (e & 31));
+  }
+  __syncthreads();
+  // output position of a winner = marked bits before it: per-thread prefix
+  // over WPT consecutive words, then popcounts inside the thread's range
+  const int wpt = (nwords + 1023) / 1024;
+  uint32_t mine = 0;
+  for (int q = 0; q < wpt; ++q) {
+    const int w = tid * wpt + q;
+    if (w < nwords) mine += __popc(bm[w]);
+  }
+  uint32_t tot;
+  tpre[tid] = block_excl_scan<1024>(mine, sm, tot);
+  __syncthreads();
+  int32_t* idx_row = idx + static_cast<size_t>(n) * topk;
+  float* score_row = score ? score + static_cast<size_t>(n) * topk : nullptr;
+  for (int i = tid; i < static_cast<int>(total); i += 1024) {
+    const uint32_t e = ci[i];
+    const int w = static_cast<int>(e >> 5);
+    const uint32_t word = bm[w];
+    if (!((word >> (e & 31)) & 1u)) continue;
+    const int owner = w / wpt;
+    uint32_t pos = tpre[owner] + __popc(word & ((1u << (e & 31)) - 1u));
+    for (int w2 = owner * wpt; w2 < w; ++w2) pos += __popc(bm[w2]);
+    idx_row[pos] = static_cast<int32_t>(e);
+    if (score_row) score_row[pos] = key_score(cu[i]);
+  }
+  for (int i = static_cast<int>(K) + tid; i < topk; i += 1024) {
+    idx_row[i] = -1;
+    if (score_row) score_row[i] = -__builtin_inff();
+  }
+}
+
 }  // namespace
 
 size_t topk_few_rows_bytes(int N, int u_stride) {
@@ -572,7 +749,7 @@ size_t topk_few_rows_bytes(int N, int u_stride) {
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.one_row_per_block) {
     MISA_LAUNCH(K_TOPK_ROW, topk_row_kernel, dim3(a.N), dim3(1024), 0, st, a.u, a.u_stride,
-                a.q_pos, a.fixed_len, a.topk, a.cand, a.cand_stride, a.idx, a.score);
+                a.q_pos, a.fixed_len, a.topk, a.cand, a.cand_stride, a.idx, a.score, a.row_flag);
     return hipGetLastError();
   }
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -598,5 +775,21 @@ hipError_t launch_clear(uint32_t* p, size_t n_words, hipStream_t st) {
 }
 
 int topk_chunk() { return kChunk; }
+
+int cand_topk_capacity() { return kCandRow; }
+
+hipError_t launch_tau(const TauArgs& a, hipStream_t st) {
+  MISA_LAUNCH(K_TOPK_TAU, topk_tau_kernel, dim3(a.N), dim3(256), 0, st, a.us, a.us_stride,
+              a.q_pos, a.topk, a.sample_shift, a.rows_per_block, a.tau, a.block_flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_cand_topk(const CandTopkArgs& a, hipStream_t st) {
+  if (a.splits < 1 || a.splits > 256) return hipErrorInvalidValue;
+  MISA_LAUNCH(K_TOPK_CAND, topk_cand_kernel, dim3(a.N), dim3(1024), 0, st, a.cnt, a.cand,
+              a.splits, a.cap, a.q_pos, a.topk, a.rows_per_block, a.row_flag, a.block_flag,
+              a.idx, a.score);
+  return hipGetLastError();
+}
 
 }  // namespace misa

@@ -256,7 +256,7 @@ def test_c5_misa_dagger_fp8():
 
 def test_c3_prefill_chunk_sampled_rows():
     p = synth.make("c3")
-    rows = np.r_[0:3, 127:130, 2047:2049, 4093:4096]
+    rows = np.r_[0:3, 127:130, 2047:2049, 3976, 4093:4096]   # row 3976: 852 zero-score ties at the k-th score
     check_misa(p, rows=rows)
 
 
@@ -295,6 +295,79 @@ def test_prefill_integer_bit_exact():
     dp = DeviceProblem(p)
     kbar, heads, r, idx, sc = misa_gpu(dp)
     rows = np.r_[0:10, 190:200]
+    ps = sub_problem(p, rows)
+    ref_heads, ref_r = oracle.route_heads(ps)
+    assert np.array_equal(heads[rows], ref_heads)
+    check_topk(idx[rows], sc[rows], oracle.scores(ps, ref_heads), p.topk, ps.visible(),
+               exact=True)
+
+
+# ---------------------------------------------------------------- prefill candidate path
+# Long shared prefixes (L >= 32768, top-k <= 2048, >= 128 rows) take the
+# sampled-threshold path: the GEMM keeps only keys at or above a per-row
+# threshold and the select runs on those; rows whose candidates cannot prove
+# the result redo the full path.  Short rows in these tests overflow their
+# split lists and exercise that fallback inside the same call.
+@pytest.mark.parametrize("h,d,H_I", [(8, 128, 64), (4, 128, 16), (16, 64, 32), (12, 128, 64)])
+def test_prefill_candidate_parity(h, d, H_I):
+    L, N = 40000, 256
+    rng = np.random.default_rng(7 * h + d)
+    pos = rng.choice(np.arange(20000, L), N, replace=False).astype(np.int32)
+    pos[:5] = [0, 100, 5000, 32767, L - 1]
+    p = synth.small("cand", 71 + h, N=N, S=1, L=L, d=d, H_I=H_I, h=h, B=128, topk=2048,
+                    q_pos=pos, q_seq=np.zeros(N, np.int32), n_clusters=64)
+    check_misa(p, rows=np.r_[0:8, 128:131, N - 3:N])
+
+
+def test_prefill_candidate_dense_parity():
+    L, N = 32768, 128
+    pos = np.random.default_rng(3).choice(np.arange(16000, L), N, replace=False).astype(np.int32)
+    pos[:2] = [7, L - 1]
+    p = synth.small("candd", 53, N=N, S=1, L=L, d=128, H_I=64, h=8, topk=2048,
+                    q_pos=pos, q_seq=np.zeros(N, np.int32), n_clusters=64)
+    idx, sc = DeviceProblem(p).dsa()
+    rows = np.r_[0:4, 60:62, 124:128]
+    ps = sub_problem(p, rows)
+    check_topk(np_(idx)[rows], np_(sc)[rows], oracle.scores(ps, None), p.topk, ps.visible())
+
+
+def test_prefill_candidate_integer_ties_bit_exact():
+    """Integer inputs: many exact ties at the k-th score, resolved by the lower
+    token index on the candidate path; bit-exact."""
+    N, L = 128, 32768
+    pos = np.random.default_rng(11).choice(np.arange(8000, L), N, replace=False).astype(np.int32)
+    pos[0] = L - 1
+    p = synth.integer_problem("candint", 12, N=N, S=1, L=L, d=128, H_I=16, h=4, B=64,
+                              topk=2048, q_pos=pos, q_seq=np.zeros(N, np.int32))
+    dp = DeviceProblem(p)
+    kbar, heads, r, idx, sc = misa_gpu(dp)
+    rows = np.r_[0:6, 120:128]
+    ps = sub_problem(p, rows)
+    ref_heads, ref_r = oracle.route_heads(ps)
+    assert np.array_equal(heads[rows], ref_heads)
+    check_topk(idx[rows], sc[rows], oracle.scores(ps, ref_heads), p.topk, ps.visible(),
+               exact=True)
+
+
+def test_prefill_candidate_fallback_bit_exact():
+    """Thresholds that cannot prove the result: only every 32nd key is non-zero
+    (the sampled keys), so the threshold is reached by too few keys or, where
+    it admits the zero scores, by too many; rows with q = 0 score every key 0.
+    Every row takes the full path; results bit-exact, zero-score ties by index."""
+    N, L = 128, 32768
+    pos = np.random.default_rng(13).choice(np.arange(4000, L), N, replace=False).astype(np.int32)
+    p = synth.integer_problem("candfb", 14, N=N, S=1, L=L, d=128, H_I=16, h=4, B=64,
+                              topk=2048, q_pos=pos, q_seq=np.zeros(N, np.int32))
+    keep = (np.arange(L) % 32) == 0
+    k = p.k.copy()
+    k[:, ~keep] = 0
+    q = p.q.copy()
+    q[::5] = 0
+    p = synth.Problem(p.name, q, p.q_dt, p.w, k, p.k_dt, p.k_scale, p.q_seq, p.q_pos, p.B, p.h,
+                      p.topk, p.k_prime)
+    dp = DeviceProblem(p)
+    kbar, heads, r, idx, sc = misa_gpu(dp)
+    rows = np.r_[0:6, 120:128]
     ps = sub_problem(p, rows)
     ref_heads, ref_r = oracle.route_heads(ps)
     assert np.array_equal(heads[rows], ref_heads)

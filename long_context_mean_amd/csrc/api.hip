@@ -181,7 +181,8 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* w, const void*
     mp.cand_out = cand;
     mp.cap = cap;
     if ((e = misa::launch_prefill(mp, st)) != hipSuccess) return hip_status(e);
-    misa::CandTopkArgs ca{cnt, cand, splits, cap, q_pos, N, topk, qb, rflag, bflag, idx, score};
+    misa::CandTopkArgs ca{cnt, cand, splits, cap, q_pos, N, L, topk, qb, rflag, bflag, idx,
+                          score};
     if ((e = misa::launch_cand_topk(ca, st)) != hipSuccess) return hip_status(e);
     misa::PrefillArgs fp{q, w, k, q_pos, heads, N, L, d, H_I, h, u, lay.u_stride};
     fp.block_flag = bflag;

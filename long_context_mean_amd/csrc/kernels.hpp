@@ -163,7 +163,7 @@ struct CandTopkArgs {
   const uint2* cand;
   int splits, cap;
   const int32_t* q_pos;
-  int N, topk, rows_per_block;
+  int N, L, topk, rows_per_block;     // L: longest row length
   uint32_t* row_flag;
   uint32_t* block_flag;
   int32_t* idx;

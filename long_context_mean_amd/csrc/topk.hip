@@ -619,22 +619,28 @@ __global__ __launch_bounds__(256) void topk_tau_kernel(const uint32_t* __restric
   }
 }
 
-// One 1024-thread workgroup per row.
-__global__ __launch_bounds__(1024) void topk_cand_kernel(
+// One 256-thread workgroup per row; each thread keeps up to kCandPer
+// candidates in registers.  Dynamic LDS: the row's winner bitmap (nwords_max
+// words) and a 16-bit per-word prefix of marked bits.
+constexpr int kCandThreads = 256;
+constexpr int kCandPer = kCandRow / kCandThreads;
+
+__global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
     const uint32_t* __restrict__ cnt, const uint2* __restrict__ cand, int splits, int cap,
-    const int32_t* __restrict__ q_pos, int topk, int rows_per_block,
+    const int32_t* __restrict__ q_pos, int topk, int rows_per_block, int nwords_max,
     uint32_t* __restrict__ row_flag, uint32_t* __restrict__ block_flag,
     int32_t* __restrict__ idx, float* __restrict__ score) {
-  __shared__ __align__(16) uint32_t cu[kCandRow];
-  __shared__ __align__(16) uint32_t ci[kCandRow];
-  __shared__ __align__(16) uint32_t bm[kBitmapWords];
+  extern __shared__ __align__(16) uint32_t dyn[];
   __shared__ __align__(16) uint32_t hA[kBins0];
   __shared__ __align__(16) uint32_t hB[kBins2];
-  __shared__ uint32_t tpre[1024];
   __shared__ uint32_t spre[257];
-  __shared__ uint32_t sm[16];
+  __shared__ uint32_t tpre[kCandThreads];
+  __shared__ uint32_t sm[4];
   __shared__ uint32_t res[4];
   __shared__ uint32_t bad;
+  constexpr int NT = kCandThreads;
+  uint32_t* bm = dyn;
+  uint16_t* wpre = reinterpret_cast<uint16_t*>(dyn + nwords_max);
   const int n = blockIdx.x;
   const int tid = threadIdx.x;
   const int len = q_pos[n] + 1;
@@ -647,12 +653,12 @@ __global__ __launch_bounds__(1024) void topk_cand_kernel(
   __syncthreads();
   if (cs > static_cast<uint32_t>(cap)) bad = 1u;
   uint32_t total;
-  const uint32_t before = block_excl_scan<1024>(cs, sm, total);
+  const uint32_t before = block_excl_scan<NT>(cs, sm, total);
   if (tid < splits) spre[tid] = before;
   if (tid == 0) spre[splits] = total;
   __syncthreads();
   const bool flag = bad != 0u || total < K || total > static_cast<uint32_t>(kCandRow) ||
-                    nwords > kBitmapWords;
+                    nwords > nwords_max;
   if (flag) {
     if (tid == 0) {
       row_flag[n] = 1u;
@@ -660,78 +666,109 @@ __global__ __launch_bounds__(1024) void topk_cand_kernel(
     }
     return;
   }
-  // gather the candidates: element j lives in split s with spre[s] <= j < spre[s+1]
-  for (int j = tid; j < static_cast<int>(total); j += 1024) {
-    int lo = 0, hi = splits - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (spre[mid] <= static_cast<uint32_t>(j)) lo = mid; else hi = mid - 1;
+  // candidates into registers: element j = tid + NT * i lives in split s with
+  // spre[s] <= j < spre[s + 1]; key 0 marks an empty register slot
+  uint32_t ck[kCandPer], cx[kCandPer];
+#pragma unroll
+  for (int i = 0; i < kCandPer; ++i) {
+    const int j = tid + NT * i;
+    ck[i] = 0u;
+    cx[i] = 0u;
+    if (j < static_cast<int>(total)) {
+      int lo = 0, hi = splits - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (spre[mid] <= static_cast<uint32_t>(j)) lo = mid; else hi = mid - 1;
+      }
+      const uint2 e = cand[(static_cast<size_t>(n) * splits + lo) * cap + (j - spre[lo])];
+      ck[i] = e.x;
+      cx[i] = e.y;
     }
-    const uint2 e = cand[(static_cast<size_t>(n) * splits + lo) * cap + (j - spre[lo])];
-    cu[j] = e.x;
-    ci[j] = e.y;
   }
-  for (int b = tid; b < kBins0; b += 1024) hA[b] = 0u;
-  if (tid < kBins2) hB[tid] = 0u;
+  for (int b = tid; b < kBins0; b += NT) hA[b] = 0u;
+  hB[tid] = 0u;
   __syncthreads();
   // exact threshold: three radix levels over the candidates
-  for (int i = tid; i < static_cast<int>(total); i += 1024) atomicAdd(&hA[cu[i] >> kShift0], 1u);
+#pragma unroll
+  for (int i = 0; i < kCandPer; ++i)
+    if (ck[i] != 0u) atomicAdd(&hA[ck[i] >> kShift0], 1u);
   __syncthreads();
-  find_digit<1024, kBins0>(hA, K, false, sm, res);
+  find_digit<NT, kBins0>(hA, K, false, sm, res);
   const uint32_t d0 = res[0], r0 = res[1];
-  for (int b = tid; b < kBins1; b += 1024) hA[b] = 0u;
+  for (int b = tid; b < kBins1; b += NT) hA[b] = 0u;
   __syncthreads();
-  for (int i = tid; i < static_cast<int>(total); i += 1024)
-    if ((cu[i] >> kShift0) == d0) atomicAdd(&hA[(cu[i] >> kShift1) & (kBins1 - 1)], 1u);
+#pragma unroll
+  for (int i = 0; i < kCandPer; ++i)
+    if (ck[i] != 0u && (ck[i] >> kShift0) == d0) atomicAdd(&hA[(ck[i] >> kShift1) & (kBins1 - 1)], 1u);
   __syncthreads();
-  find_digit<1024, kBins1>(hA, r0, false, sm, res);
+  find_digit<NT, kBins1>(hA, r0, false, sm, res);
   const uint32_t d1 = res[0], r1 = res[1];
   const uint32_t pre = (d0 << kDigit1Bits) | d1;
-  for (int i = tid; i < static_cast<int>(total); i += 1024)
-    if ((cu[i] >> kShift1) == pre) atomicAdd(&hB[cu[i] & (kBins2 - 1)], 1u);
+#pragma unroll
+  for (int i = 0; i < kCandPer; ++i)
+    if (ck[i] != 0u && (ck[i] >> kShift1) == pre) atomicAdd(&hB[ck[i] & (kBins2 - 1)], 1u);
   __syncthreads();
-  find_digit<1024, kBins2>(hB, r1, false, sm, res);
+  find_digit<NT, kBins2>(hB, r1, false, sm, res);
   const uint32_t T = (d0 << kShift0) | (d1 << kShift1) | res[0];
   const uint32_t K2 = res[1];
   const uint32_t n_eq = hB[res[0]];
   __syncthreads();
-  if (tid == 0) row_flag[n] = 0u;
-  for (int w = tid; w < nwords; w += 1024) bm[w] = 0u;
-  // mark the winners (ties: the K2 lowest token indices)
-  const uint32_t cut = n_eq == K2 ? 0xFFFFFFFFu
-                                  : tie_cut<1024>(cu, ci, static_cast<int>(total), T, K2, n_eq,
-                                                  hA, hB, sm, res);
-  __syncthreads();
-  for (int i = tid; i < static_cast<int>(total); i += 1024) {
-    const uint32_t kv = cu[i], e = ci[i];
-    if (kv > T || (kv == T && e <= cut)) atomicOr(&bm[e >> 5], 1u << (e & 31));
+  // ties at T: the K2 lowest token indices win (radix select on the indices,
+  // which are < 2^18 here: bits 6..17, then 0..5)
+  uint32_t cut = 0xFFFFFFFFu;
+  if (n_eq != K2) {
+    for (int b = tid; b < kBins0; b += NT) hA[b] = 0u;
+    if (tid < 64) hB[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kCandPer; ++i)
+      if (ck[i] == T) atomicAdd(&hA[cx[i] >> 6], 1u);
+    __syncthreads();
+    find_digit<NT, kBins0>(hA, n_eq - K2 + 1u, false, sm, res);
+    const uint32_t dA = res[0], rA = res[1];
+#pragma unroll
+    for (int i = 0; i < kCandPer; ++i)
+      if (ck[i] == T && (cx[i] >> 6) == dA) atomicAdd(&hB[cx[i] & 63u], 1u);
+    __syncthreads();
+    find_digit<NT, 64>(hB, rA, false, sm, res);
+    cut = (dA << 6) | res[0];
   }
+  if (tid == 0) row_flag[n] = 0u;
+  for (int w = tid; w < nwords; w += NT) bm[w] = 0u;
   __syncthreads();
-  // output position of a winner = marked bits before it: per-thread prefix
-  // over WPT consecutive words, then popcounts inside the thread's range
-  const int wpt = (nwords + 1023) / 1024;
+#pragma unroll
+  for (int i = 0; i < kCandPer; ++i)
+    if (ck[i] > T || (ck[i] == T && ck[i] != 0u && cx[i] <= cut))
+      atomicOr(&bm[cx[i] >> 5], 1u << (cx[i] & 31));
+  __syncthreads();
+  // output position of a winner = marked bits before it: thread prefix over
+  // wpt consecutive words, plus a 16-bit prefix inside the thread's words
+  const int wpt = (nwords + NT - 1) / NT;
   uint32_t mine = 0;
   for (int q = 0; q < wpt; ++q) {
     const int w = tid * wpt + q;
-    if (w < nwords) mine += __popc(bm[w]);
+    if (w < nwords) {
+      wpre[w] = static_cast<uint16_t>(mine);
+      mine += __popc(bm[w]);
+    }
   }
   uint32_t tot;
-  tpre[tid] = block_excl_scan<1024>(mine, sm, tot);
+  tpre[tid] = block_excl_scan<NT>(mine, sm, tot);
   __syncthreads();
   int32_t* idx_row = idx + static_cast<size_t>(n) * topk;
   float* score_row = score ? score + static_cast<size_t>(n) * topk : nullptr;
-  for (int i = tid; i < static_cast<int>(total); i += 1024) {
-    const uint32_t e = ci[i];
+#pragma unroll
+  for (int i = 0; i < kCandPer; ++i) {
+    const uint32_t e = cx[i];
+    if (ck[i] == 0u) continue;
     const int w = static_cast<int>(e >> 5);
     const uint32_t word = bm[w];
     if (!((word >> (e & 31)) & 1u)) continue;
-    const int owner = w / wpt;
-    uint32_t pos = tpre[owner] + __popc(word & ((1u << (e & 31)) - 1u));
-    for (int w2 = owner * wpt; w2 < w; ++w2) pos += __popc(bm[w2]);
+    const uint32_t pos = tpre[w / wpt] + wpre[w] + __popc(word & ((1u << (e & 31)) - 1u));
     idx_row[pos] = static_cast<int32_t>(e);
-    if (score_row) score_row[pos] = key_score(cu[i]);
+    if (score_row) score_row[pos] = key_score(ck[i]);
   }
-  for (int i = static_cast<int>(K) + tid; i < topk; i += 1024) {
+  for (int i = static_cast<int>(K) + tid; i < topk; i += NT) {
     idx_row[i] = -1;
     if (score_row) score_row[i] = -__builtin_inff();
   }
@@ -786,9 +823,12 @@ hipError_t launch_tau(const TauArgs& a, hipStream_t st) {
 
 hipError_t launch_cand_topk(const CandTopkArgs& a, hipStream_t st) {
   if (a.splits < 1 || a.splits > 256) return hipErrorInvalidValue;
-  MISA_LAUNCH(K_TOPK_CAND, topk_cand_kernel, dim3(a.N), dim3(1024), 0, st, a.cnt, a.cand,
-              a.splits, a.cap, a.q_pos, a.topk, a.rows_per_block, a.row_flag, a.block_flag,
-              a.idx, a.score);
+  // bitmap + 16-bit word prefix for the longest row (longer rows are flagged)
+  const int nwords_max = min((a.L + 31) / 32, kBitmapWords);
+  const size_t lds = static_cast<size_t>(nwords_max) * 4 + (static_cast<size_t>(nwords_max) * 2 + 15) / 16 * 16;
+  MISA_LAUNCH(K_TOPK_CAND, topk_cand_kernel, dim3(a.N), dim3(kCandThreads), lds, st, a.cnt,
+              a.cand, a.splits, a.cap, a.q_pos, a.topk, a.rows_per_block, nwords_max, a.row_flag,
+              a.block_flag, a.idx, a.score);
   return hipGetLastError();
 }
 

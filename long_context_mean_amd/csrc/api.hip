@@ -160,7 +160,7 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* w, const void*
     const CandLayout cl = cand_layout(lay.bytes, N, L);
     const int h_eff = heads ? h : H_I;
     const int qb = misa::prefill_rows_per_block(h_eff);
-    const int splits = misa::prefill_splits(N, L, h_eff);
+    const int splits = misa::prefill_cand_splits(N, L, h_eff, d);
     const int cap = kCandRegion / splits;
     uint32_t* us = reinterpret_cast<uint32_t*>(base + cl.off_us);
     uint32_t* tau = reinterpret_cast<uint32_t*>(base + cl.off_tau);

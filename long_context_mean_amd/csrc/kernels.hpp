@@ -116,7 +116,8 @@ struct PrefillArgs {
   int kernel_id = K_SCORE_PREFILL;
 };
 int prefill_rows_per_block(int h_eff);
-int prefill_splits(int N, int L, int h_eff);
+// key-range splits of the candidate-mode GEMM (the layout of cnt_out / cand_out)
+int prefill_cand_splits(int N, int L, int h_eff, int d);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------- top-k

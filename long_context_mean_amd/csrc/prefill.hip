@@ -308,6 +308,48 @@ int hp_of(int h) {
   return h <= 4 ? 4 : h <= 8 ? 8 : h <= 16 ? 16 : h <= 32 ? 32 : 64;
 }
 
+// Workgroups of one kernel instantiation resident on the whole chip at once.
+template <int HP, int D, bool CAND>
+int chip_slots() {
+  static const int slots = [] {
+    int dev = 0, cus = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, score_prefill_kernel<HP, D, CAND>, 256,
+                                                      0) != hipSuccess ||
+        cus < 1 || per < 1)
+      return 1024;
+    return cus * per;
+  }();
+  return slots;
+}
+
+int gcd(int a, int b) {
+  while (b) {
+    const int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+// Key-range splits: about 4 rounds of chip-resident workgroups (the last
+// round partly idle costs at most a quarter), rounded to whole rounds when
+// the row-block count allows; at least 4 key tiles per split, at most 256.
+int choose_splits(int qblocks, int L, int slots) {
+  const int max_s = max(1, min(256, L / (4 * kKeyTile)));
+  int s = (4 * slots + qblocks - 1) / qblocks;
+  const int m = slots / gcd(slots, qblocks);            // splits per whole round
+  if (m <= max_s) s = (s + m - 1) / m * m;
+  return max(1, min(s, max_s));
+}
+
+template <int HP, int D, bool CAND>
+int splits_t(int N, int L) {
+  constexpr int QB = kRowsPerWG / HP;
+  return choose_splits((N + QB - 1) / QB, L, chip_slots<HP, D, CAND>());
+}
+
 template <int HP, int D>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   PrefillParams p;
@@ -331,7 +373,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   p.cap = a.cap;
   constexpr int QB = kRowsPerWG / HP;
   const int qblocks = (a.N + QB - 1) / QB;
-  const int splits = prefill_splits(a.N, p.L, HP);
+  const int splits = a.cand_out ? splits_t<HP, D, true>(a.N, p.L) : splits_t<HP, D, false>(a.N, p.L);
   p.splits = splits;
   p.keys_per_split = ((p.L + splits - 1) / splits + kKeyTile - 1) / kKeyTile * kKeyTile;
   if (a.cand_out)
@@ -341,6 +383,17 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
     MISA_LAUNCH(a.kernel_id, (score_prefill_kernel<HP, D, false>), dim3(splits, qblocks),
                 dim3(256), 0, st, p);
   return hipGetLastError();
+}
+
+template <int D>
+int cand_splits_d(int N, int L, int hp) {
+  switch (hp) {
+    case 4: return splits_t<4, D, true>(N, L);
+    case 8: return splits_t<8, D, true>(N, L);
+    case 16: return splits_t<16, D, true>(N, L);
+    case 32: return splits_t<32, D, true>(N, L);
+    default: return splits_t<64, D, true>(N, L);
+  }
 }
 
 template <int D>
@@ -358,14 +411,8 @@ hipError_t launch_d(const PrefillArgs& a, hipStream_t st) {
 
 int prefill_rows_per_block(int h_eff) { return kRowsPerWG / hp_of(h_eff); }
 
-// Key-range splits of the GEMM grid: enough workgroups to fill the chip
-// (about 4 per CU), each split at least 4 key tiles long; at most 256.
-int prefill_splits(int N, int L, int h_eff) {
-  const int qb = prefill_rows_per_block(h_eff);
-  const int qblocks = (N + qb - 1) / qb;
-  int splits = 1;
-  while (splits < 256 && qblocks * splits < 1024 && L / (splits * 2) >= 4 * kKeyTile) splits *= 2;
-  return splits;
+int prefill_cand_splits(int N, int L, int h_eff, int d) {
+  return d == 64 ? cand_splits_d<64>(N, L, hp_of(h_eff)) : cand_splits_d<128>(N, L, hp_of(h_eff));
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {

@@ -50,40 +50,48 @@ struct PrefillParams {
 template <int D>
 struct PLayout {
   static constexpr int ROW = D * 2;                    // bytes per key row (bf16)
-  static constexpr int STRIDE = ROW + 16;              // padded LDS row
-  static constexpr int TILE = kKeyTile * STRIDE;       // bytes per LDS key tile
+  static constexpr int CH = ROW / 16;                  // 16-byte chunks per row
+  static constexpr int TILE = kKeyTile * ROW;          // bytes per LDS key tile
   static constexpr int KK = D / 32;                    // MFMAs per 16x16 output tile
-  static constexpr int PIECES = kKeyTile * ROW / 16;   // 16-byte pieces per key tile
-  static constexpr int PER_THREAD = PIECES / 256;
-  static constexpr int PIECES_PER_ROW = ROW / 16;
+  static constexpr int PER_THREAD = kKeyTile * CH / 256;  // 16-byte loads per thread per tile
+  // Chunk q of row r sits at chunk position q ^ swz(r): the 16 rows read by
+  // one MFMA B fragment then hit 16 different bank groups.
+  __device__ static int swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 };
 
-// Key rows key_step * s for s in [key0, key0 + 64); s >= L (in the same units)
-// reads row 0 instead (masked later).
+constexpr int kStages = 3;                             // LDS key tiles in flight
+
+// Key rows key_step * s for s in [key0, key0 + 64) straight into an LDS tile
+// (global_load_lds_dwordx4: each wavefront instruction fills 1 KB of the
+// tile, lane l the l-th 16 bytes).  s >= L (in the same units) reads row 0
+// instead (masked later).  Completion is tracked by vmcnt.
 template <int D>
-__device__ __forceinline__ void load_key_tile(const uint8_t* k, int key0, int L, int key_step,
-                                              int tid, u32x4_t (&r)[PLayout<D>::PER_THREAD]) {
+__device__ __forceinline__ void dma_key_tile(const uint8_t* k, int key0, int L, int key_step,
+                                             uint8_t* tile, int wave, int lane) {
   using LY = PLayout<D>;
 #pragma unroll
-  for (int i = 0; i < LY::PER_THREAD; ++i) {
-    const int f = tid + 256 * i;
-    int key = key0 + f / LY::PIECES_PER_ROW;
+  for (int j = 0; j < LY::PER_THREAD; ++j) {
+    const int blk = j * 4 + wave;                       // 1 KB block of the tile
+    const int f = blk * 64 + lane;                      // 16-byte chunk slot in the tile
+    const int r = f / LY::CH;
+    int key = key0 + r;
     key = key < L ? key : 0;
-    r[i] = *reinterpret_cast<const u32x4_t*>(
-        k + static_cast<size_t>(key) * key_step * LY::ROW + 16 * (f % LY::PIECES_PER_ROW));
+    const uint8_t* src = k + static_cast<size_t>(key) * key_step * LY::ROW +
+                         16 * ((f % LY::CH) ^ LY::swz(r));
+    __builtin_amdgcn_global_load_lds(src, tile + blk * 1024, 16, 0, 0);
   }
 }
 
-template <int D>
-__device__ __forceinline__ void store_key_tile(uint8_t* tile, int tid,
-                                               const u32x4_t (&r)[PLayout<D>::PER_THREAD]) {
-  using LY = PLayout<D>;
-#pragma unroll
-  for (int i = 0; i < LY::PER_THREAD; ++i) {
-    const int f = tid + 256 * i;
-    *reinterpret_cast<u32x4_t*>(tile + (f / LY::PIECES_PER_ROW) * LY::STRIDE +
-                                16 * (f % LY::PIECES_PER_ROW)) = r[i];
-  }
+// Wait until at most N vector memory operations of this wavefront are
+// outstanding (loads complete in order), then a workgroup barrier.  No
+// memory fence: the key tiles in flight stay in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);              // expcnt, lgkmcnt: no wait
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Row mapping of the gathered A operand.  Each wavefront holds 4 row tiles of
@@ -144,8 +152,8 @@ __device__ __forceinline__ void score_tile(const uint8_t* tile, int key0,
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       b[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
-                                               tile + (ct * 16 + c) * LY::STRIDE + 64 * kk +
-                                               16 * g));
+                                               tile + (ct * 16 + c) * LY::ROW +
+                                               16 * ((4 * kk + g) ^ LY::swz(ct * 16 + c))));
     float v[RM::NG];
 #pragma unroll
     for (int q = 0; q < RM::NG; ++q) v[q] = 0.f;
@@ -193,7 +201,7 @@ __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(Pre
   using RM = RowMap<HP>;
   constexpr int KK = LY::KK;
   constexpr int QB = kRowsPerWG / HP;                  // query rows per workgroup
-  __shared__ __align__(16) uint8_t tiles[2][LY::TILE];
+  __shared__ __align__(16) uint8_t tiles[kStages][LY::TILE];
   __shared__ int pos_lds[QB];
 
   if (p.block_flag && p.block_flag[blockIdx.y] == 0u) return;
@@ -274,25 +282,32 @@ __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(Pre
   for (int i = 0; i < QB; ++i) minpos = min(minpos, pos_lds[i] < 0 ? 0x7FFFFFFF : pos_lds[i]);
   const bool full_block = qrow0 + QB <= p.N;
 
-  u32x4_t pre[LY::PER_THREAD];
-  load_key_tile<D>(p.k, ks0, p.L, p.key_step, tid, pre);
-  store_key_tile<D>(tiles[0], tid, pre);
-  __syncthreads();
+  // three-stage pipeline: tile i+2 streams into LDS while tile i is scored
+  const int ntiles = (ks1 - ks0 + kKeyTile - 1) / kKeyTile;
+  dma_key_tile<D>(p.k, ks0, p.L, p.key_step, tiles[0], wave, lane);
+  if (ntiles > 1) {
+    dma_key_tile<D>(p.k, ks0 + kKeyTile, p.L, p.key_step, tiles[1], wave, lane);
+    wait_vm_barrier<LY::PER_THREAD>();
+  } else {
+    wait_vm_barrier<0>();
+  }
   int buf = 0;
-  for (int key0 = ks0; key0 < ks1; key0 += kKeyTile) {
-    const bool more = key0 + kKeyTile < ks1;
-    if (more) load_key_tile<D>(p.k, key0 + kKeyTile, p.L, p.key_step, tid, pre);
+  for (int i = 0; i < ntiles; ++i) {
+    const int key0 = ks0 + i * kKeyTile;
     // every (row, key) of the tile is visible: no masks
     const bool unmasked = full_block && key0 + kKeyTile - 1 <= minpos;
     if (unmasked)
       score_tile<HP, D, false, CAND>(tiles[buf], key0, a, wv, o, p.cap, g, c);
     else
       score_tile<HP, D, true, CAND>(tiles[buf], key0, a, wv, o, p.cap, g, c);
-    if (more) {
-      store_key_tile<D>(tiles[buf ^ 1], tid, pre);
-      __syncthreads();
-      buf ^= 1;
+    const int nb = buf == 0 ? kStages - 1 : buf - 1;    // (buf + 2) % 3, read two tiles ago
+    if (i + 2 < ntiles) {
+      dma_key_tile<D>(p.k, key0 + 2 * kKeyTile, p.L, p.key_step, tiles[nb], wave, lane);
+      wait_vm_barrier<LY::PER_THREAD>();                 // tile i+1 has landed
+    } else {
+      wait_vm_barrier<0>();
     }
+    buf = buf == kStages - 1 ? 0 : buf + 1;
   }
   if constexpr (CAND) {
 #pragma unroll

@@ -46,7 +46,111 @@ def parse():
     ap.add_argument("--workload", default="c4", choices=["c4", "c3", "c3x"],
                     help="c4: the long-context decode indexer (the headline line); "
                          "c3 / c3x: the prefill chunk at L=64K / 128K")
+    # profiling helpers (no benchmark line)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run plain 256 MiB device copies (scale reference for HBM counters)")
+    ap.add_argument("--summarize", metavar="DB",
+                    help="print a markdown kernel table of a rocprofv3 --kernel-trace database")
+    ap.add_argument("--traffic", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB",
+                                                   "COPY_WRITE_DB"),
+                    help="print the per-launch HBM traffic record of --kernel from rocprofv3 "
+                         "--pmc FETCH_SIZE / WRITE_SIZE databases, scaled by the copy probe's")
+    ap.add_argument("--kernel", default="score_mfma_kernel")
+    ap.add_argument("--match", default=None,
+                    help="kernel-name substring selecting the dispatches (default: --kernel)")
+    ap.add_argument("--title", default="")
+    ap.add_argument("--cmd", default="")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20
+
+
+def copy_probe():
+    import torch
+    x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 5}), flush=True)
+
+
+def summarize(db, title, cmd):
+    import sqlite3
+    c = sqlite3.connect(db)
+    rows = list(c.execute("select name, count(*), avg(end-start), min(end-start), max(end-start), "
+                          "sum(end-start) from kernels group by name order by sum(end-start) desc"))
+    tot = sum(r[5] for r in rows)
+    out = [f"# {title}", "", "Command (from the repository root, on one MI355X):", "", "```", cmd,
+           "```", "", "| kernel | calls | avg us | min us | max us | share |",
+           "|---|---|---|---|---|---|"]
+    for name, n, avg, mn, mx, sm in rows:
+        short = name.replace("misa::(anonymous namespace)::", "").split("(")[0]
+        out.append(f"| `{short}` | {n} | {avg / 1000:.2f} | {mn / 1000:.2f} | {mx / 1000:.2f} "
+                   f"| {100 * sm / tot:.1f}% |")
+    print("\n".join(out))
+
+
+def _counter_per_dispatch(db, counter, name_part):
+    """Mean value of `counter` per dispatch of kernels whose name contains name_part."""
+    import sqlite3
+    c = sqlite3.connect(db)
+    rows = c.execute("select dispatch_id, kernel_name, value from counters_collection "
+                     "where counter_name = ?", (counter,)).fetchall()
+    per = {}
+    for did, kn, v in rows:
+        if name_part in kn:
+            per[did] = per.get(did, 0.0) + v
+    return sum(per.values()) / len(per) if per else None
+
+
+# source files whose text defines each measured kernel
+KERNEL_SOURCES = {
+    "score_mfma_kernel": ["score.hip"],
+    "pool_kernel": ["pool.hip"],
+    "score_prefill_kernel": ["prefill.hip"],
+}
+
+
+def kernel_source_sha(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "long_context_mean_amd", "csrc")
+    for f in KERNEL_SOURCES.get(kernel, []) + ["common.hpp", "kernels.hpp"]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_record(fetch_db, write_db, copy_fetch_db, copy_write_db, kernel, match, cmd):
+    copy_name = "copyBuffer"
+    kf = _counter_per_dispatch(fetch_db, "FETCH_SIZE", match)
+    kw = _counter_per_dispatch(write_db, "WRITE_SIZE", match)
+    cf = _counter_per_dispatch(copy_fetch_db, "FETCH_SIZE", copy_name)
+    cw = _counter_per_dispatch(copy_write_db, "WRITE_SIZE", copy_name)
+    # counters read KiB; the copy moves COPY_BYTES each way
+    sf = COPY_BYTES / (cf * 1024.0)
+    sw = COPY_BYTES / (cw * 1024.0)
+    return {"kernel": kernel, "dispatches": match, "source_sha256": kernel_source_sha(kernel),
+            "fetch_kib_per_launch": kf, "write_kib_per_launch": kw,
+            "copy_fetch_kib": cf, "copy_write_kib": cw, "scale_fetch": sf, "scale_write": sw,
+            "fetch_bytes_per_launch": kf * 1024.0 * sf, "write_bytes_per_launch": kw * 1024.0 * sw,
+            "traffic_bytes_per_launch": (kf * 1024.0 * sf + kw * 1024.0 * sw), "command": cmd}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter record, if the kernel's
+    source is unchanged since the counters were taken (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_sha(kernel):
+        return None
+    return round(rec["traffic_bytes_per_launch"])
 
 
 class Replicas:
@@ -215,6 +319,7 @@ def prefill_main(args):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1) if tflops else None,
                      "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(tflops / 2500.0, 4) if tflops else None,
+                     "traffic": measured_traffic("score_prefill_kernel", args.workload),
                      "kernel": "score_prefill_kernel", "kernel_ms": sc_ms,
                      "algorithmic_flop_per_launch": flops},
         "extra": {"kernel_ms": {k: round(v, 4) for k, v in kt.items()},
@@ -228,16 +333,24 @@ def prefill_main(args):
 
 def main():
     args = parse()
-    if args.workload != "c4":
-        if args.gpus != 1:
-            sys.exit(2)
-        prefill_main(args)
+    if args.summarize:
+        summarize(args.summarize, args.title, args.cmd)
+        return
+    if args.traffic:
+        print(json.dumps(traffic_record(*args.traffic, args.kernel, args.match or args.kernel,
+                                        args.cmd), indent=1))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the indexer's queries shard across GPUs without any exchange; see DESIGN.md)",
+              "(the indexer's queries shard across GPUs without any exchange)",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+    if args.workload != "c4":
+        prefill_main(args)
+        return
     import numpy as np
     import torch
 
@@ -265,7 +378,8 @@ def main():
     alg = bytes_per_launch.get(dominant, key_bytes)
     achieved = alg / (kt[dominant] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dominant, "c4"),
                 "kernel": dominant, "kernel_ms": round(kt[dominant], 5),
                 "algorithmic_bytes_per_launch": alg}
 

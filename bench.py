@@ -117,7 +117,7 @@ def kernel_source_sha(kernel):
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "long_context_mean_amd", "csrc")
-    for f in KERNEL_SOURCES.get(kernel, []) + ["common.hpp", "kernels.hpp"]:
+    for f in KERNEL_SOURCES.get(kernel, []) + ["common.hpp"]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

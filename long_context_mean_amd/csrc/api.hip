@@ -163,7 +163,7 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* w, const void*
     const int splits = misa::prefill_cand_splits(N, L, h_eff, d);
     const int cap = kCandRegion / splits;
     uint32_t* us = reinterpret_cast<uint32_t*>(base + cl.off_us);
-    uint32_t* tau = reinterpret_cast<uint32_t*>(base + cl.off_tau);
+    float* tau = reinterpret_cast<float*>(base + cl.off_tau);
     uint32_t* cnt = reinterpret_cast<uint32_t*>(base + cl.off_cnt);
     uint2* cand = reinterpret_cast<uint2*>(base + cl.off_cand);
     uint32_t* rflag = reinterpret_cast<uint32_t*>(base + cl.off_rflag);

@@ -93,8 +93,8 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
 //    with key_step > 1 it scores only keys key_step*s' (s' <= q_pos[t] >>
 //    pos_shift) and writes them to u[t, s'].  With block_flag, row blocks
 //    whose flag is 0 are skipped.
-//  candidate mode: writes no u; every visible (t, s) with order key >= tau[t]
-//    is appended as (key, s) to cand_out[(t * splits + split) * cap + slot]
+//  candidate mode: writes no u; every visible (t, s) with score >= tau[t]
+//    is appended as (score bits, s) to cand_out[(t * splits + split) * cap + slot]
 //    (slots past cap are dropped) and cnt_out[t * splits + split] receives
 //    the number of such keys (which may exceed cap).
 struct PrefillArgs {
@@ -109,7 +109,7 @@ struct PrefillArgs {
   int key_step = 1;
   int pos_shift = 0;
   const uint32_t* block_flag = nullptr;
-  const uint32_t* tau = nullptr;
+  const float* tau = nullptr;
   uint32_t* cnt_out = nullptr;
   uint2* cand_out = nullptr;
   int cap = 0;
@@ -141,20 +141,20 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 hipError_t launch_clear(uint32_t* p, size_t n_words, hipStream_t st);
 
 // Sampled threshold per row (prefill candidate path): from the sample order
-// keys us[n, 0 .. (q_pos[n] >> sample_shift)], a key tau[n] such that about
-// 2 * min(topk, L_n) of the row's keys are expected at or above it.  Also
+// keys us[n, 0 .. (q_pos[n] >> sample_shift)], a score tau[n] such that about
+// 2 * min(topk, L_n) of the row's scores are expected at or above it.  Also
 // clears block_flag[n / rows_per_block].
 struct TauArgs {
   const uint32_t* us;
   int us_stride;
   const int32_t* q_pos;
   int N, topk, sample_shift, rows_per_block;
-  uint32_t* tau;
+  float* tau;
   uint32_t* block_flag;
 };
 hipError_t launch_tau(const TauArgs& a, hipStream_t st);
 
-// Exact top-k of each row from its candidate list (the keys >= tau[n]).  A row
+// Exact top-k of each row from its candidate list (the scores >= tau[n]).  A row
 // whose candidates cannot prove the result (a split list overflowed, fewer
 // than min(topk, L_n) candidates, too many candidates or ties for the LDS
 // path) is flagged in row_flag[n] and block_flag[n / rows_per_block] and left

@@ -41,7 +41,7 @@ struct PrefillParams {
   int u_stride;
   int key_step, pos_shift;   // scored keys are key_step * s (sample pass: s <= pos >> pos_shift)
   const uint32_t* block_flag;
-  const uint32_t* tau;       // candidate mode
+  const float* tau;          // candidate mode: threshold score per row
   uint32_t* cnt_out;
   uint2* cand_out;
   int cap, splits;
@@ -132,8 +132,8 @@ struct OutState {
   uint32_t* urow;          // plain mode: order-key row of group 0 (group q: + q * step)
   uint2* crow;             // candidate mode: (key, token) list of group 0's row and split
   size_t step;             // elements from one group's row to the next
-  uint32_t tau[NG];        // candidate mode: threshold key
-  uint32_t cnt[NG];        // candidate mode: keys >= tau so far (uniform over the lane group)
+  float tau[NG];           // candidate mode: threshold score
+  uint32_t cnt[NG];        // candidate mode: scores >= tau so far (uniform over the lane group)
 };
 
 // One LDS key tile (64 keys) against the wavefront's 4 row tiles.  MASK: some
@@ -174,22 +174,21 @@ __device__ __forceinline__ void score_tile(const uint8_t* tile, int key0,
         x += __shfl_xor(x, 16, 64);
         x += __shfl_xor(x, 32, 64);
       }
-      const uint32_t kv = order_key(x);
       const bool owner = RM::IN_LANE || g == 0;
       const bool vis = owner && (!MASK || key <= o.pos[q]);
       if constexpr (!CAND) {
-        if (vis) o.urow[q * o.step + key] = kv;
+        if (vis) o.urow[q * o.step + key] = order_key(x);
       } else {
-        const bool pass = vis && kv >= o.tau[q];
+        // score compare (same order as the keys: -0 == +0, no NaN scores);
+        // the list keeps the score bits, the select turns them into keys
+        const bool pass = vis && x >= o.tau[q];
         const uint64_t m = __ballot(pass);
-        if (m != 0u) {
-          // slots in key order within the lane group (16 keys of one query row)
-          const uint32_t grp = static_cast<uint32_t>(m >> (16 * g)) & 0xFFFFu;
-          const uint32_t slot = o.cnt[q] + __popc(grp & ((1u << c) - 1u));
-          if (pass && slot < static_cast<uint32_t>(cap))
-            o.crow[q * o.step + slot] = make_uint2(kv, key);
-          o.cnt[q] += __popc(grp);
-        }
+        // slots in key order within the lane group (16 keys of one query row)
+        const uint32_t grp = static_cast<uint32_t>(m >> (16 * g)) & 0xFFFFu;
+        const uint32_t slot = o.cnt[q] + __popc(grp & ((1u << c) - 1u));
+        if (pass && slot < static_cast<uint32_t>(cap))
+          o.crow[q * o.step + slot] = make_uint2(__float_as_uint(x), static_cast<uint32_t>(key));
+        o.cnt[q] += __popc(grp);
       }
     }
   }
@@ -274,7 +273,7 @@ __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(Pre
     o.pos[q] = pos_lds[qr];
     const int t = qrow0 + qr;
     if constexpr (CAND) {
-      o.tau[q] = t < p.N ? p.tau[t] : 0xFFFFFFFFu;
+      o.tau[q] = t < p.N ? p.tau[t] : __builtin_inff();
       o.cnt[q] = 0u;
     }
   }

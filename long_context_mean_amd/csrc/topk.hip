@@ -582,7 +582,7 @@ __global__ __launch_bounds__(256) void topk_tau_kernel(const uint32_t* __restric
                                                        int us_stride,
                                                        const int32_t* __restrict__ q_pos,
                                                        int topk, int shift, int rows_per_block,
-                                                       uint32_t* __restrict__ tau,
+                                                       float* __restrict__ tau,
                                                        uint32_t* __restrict__ block_flag) {
   __shared__ __align__(16) uint32_t hA[kBins0];
   __shared__ uint32_t sm[4];
@@ -614,8 +614,10 @@ __global__ __launch_bounds__(256) void topk_tau_kernel(const uint32_t* __restric
   __syncthreads();
   find_digit<256, kBins1>(hA, r0, false, sm, res);
   if (threadIdx.x == 0) {
+    // lower end of the sample's 24-bit key bin, at least the key of -FLT_MAX
+    // (every finite score's key is), as a score
     const uint32_t t = (d0 << kShift0) | (res[0] << kShift1);
-    tau[n] = t > 0u ? t : 1u;                          // key 0 marks empty slots
+    tau[n] = key_score(t > 0x00800000u ? t : 0x00800000u);
   }
 }
 
@@ -681,7 +683,7 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
         if (spre[mid] <= static_cast<uint32_t>(j)) lo = mid; else hi = mid - 1;
       }
       const uint2 e = cand[(static_cast<size_t>(n) * splits + lo) * cap + (j - spre[lo])];
-      ck[i] = e.x;
+      ck[i] = order_key(__uint_as_float(e.x));
       cx[i] = e.y;
     }
   }

@@ -117,8 +117,14 @@ int route_chunks(int L, int B) {
   return c > 0 ? c : 1;
 }
 
-size_t route_bytes(int N, int L, int B, int H_I) {
+size_t route_partial_bytes(int N, int L, int B, int H_I) {
   return align_up(static_cast<size_t>(N) * route_chunks(L, B) * H_I * 4, 256);
+}
+
+// partial sums, then the pooled table split into bf16 hi / lo halves (d <= 128)
+size_t route_bytes(int N, int L, int B, int H_I) {
+  const size_t M = (static_cast<size_t>(L) + B - 1) / B;
+  return route_partial_bytes(N, L, B, H_I) + align_up(M * 128 * 2 * 2, 256);
 }
 
 // ---------------------------------------------------------------- kernel timing
@@ -289,8 +295,10 @@ int32_t misa_route_heads(const void* q, int32_t q_dt, const float* w, const floa
   if (B < 1 || B > 1024 || h < 1 || h > H_I) return MISA_ERR_SHAPE;
   if (!ws) return MISA_ERR_NULL;
   if (ws_bytes < route_bytes(N, L, B, H_I)) return MISA_ERR_WORKSPACE;
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
   misa::RouteArgs a{q, q_dt, w, kbar, k, k_scale, k_dt, q_seq, q_pos, N, S, L, d, B, H_I, h,
-                    heads, head_score, static_cast<float*>(ws), route_chunks(L, B)};
+                    heads, head_score, reinterpret_cast<float*>(wsb), route_chunks(L, B),
+                    reinterpret_cast<uint16_t*>(wsb + route_partial_bytes(N, L, B, H_I))};
   return hip_status(misa::launch_route(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -382,7 +390,8 @@ const char* misa_kernel_name(int32_t kernel_id) {
       "pool_kernel",       "route_partial_kernel", "route_select_kernel", "topk_clear_kernel",
       "score_mfma_kernel", "score_f32_kernel",     "score_prefill_kernel",
       "topk_collect_kernel", "topk_final_kernel",   "topk_row_kernel",
-      "score_prefill_sample", "score_prefill_full", "topk_tau_kernel", "topk_cand_kernel"};
+      "score_prefill_sample", "score_prefill_full", "topk_tau_kernel", "topk_cand_kernel",
+      "route_split_kernel"};
   if (kernel_id < 0 || kernel_id >= misa::K_COUNT_IDS) return "unknown";
   return names[kernel_id];
 }

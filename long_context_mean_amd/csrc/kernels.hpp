@@ -22,6 +22,7 @@ enum KernelId : int {
   K_PREFILL_FULL,
   K_TOPK_TAU,
   K_TOPK_CAND,
+  K_ROUTE_SPLIT,
   K_COUNT_IDS
 };
 
@@ -61,6 +62,7 @@ struct RouteArgs {
   float* head_score;
   float* partial;        // workspace [N, nchunks, H_I]
   int nchunks;           // chunks of full blocks per row
+  uint16_t* kb_split;    // workspace [2, M, d] bf16: pooled keys as hi + lo (one-sequence GEMM)
 };
 int route_blocks_per_chunk();
 bool route_uses_mfma(const RouteArgs& a);

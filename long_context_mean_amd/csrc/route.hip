@@ -8,11 +8,12 @@
 // the row are read from the pooled table; the row's partial last block (when
 // L_n is not a multiple of B) is the mean of its visible keys only.
 //
-//  route_partial: grid (chunk of 16 full blocks, row).  Lane j of every
-//    wavefront holds head j's query row in registers (fp32); the chunk's
-//    pooled keys sit in LDS and are read as broadcasts, each wavefront taking
-//    every fourth block.  Per-chunk sums go to the workspace (no float
-//    atomics: the final sum runs in a fixed order and is deterministic).
+//  route_partial: grid (chunk of 16 full blocks, row); per-chunk sums go to
+//    the workspace (no float atomics: the final sum runs in a fixed order and
+//    is deterministic).  bf16 q: an MFMA product of the heads against the
+//    chunk's pooled keys split into two bf16 parts.  fp32 q: lane j holds
+//    head j's query row in registers and reads the pooled keys from LDS as
+//    broadcasts.
 //  route_select: one workgroup per row.  Sums the chunk partials, adds the
 //    partial-block term, applies |w|, and routes every head that fewer than
 //    h heads beat under (r desc, head index asc); heads are written in
@@ -106,6 +107,91 @@ __global__ __launch_bounds__(256) void route_partial_kernel(
                        (red[2][threadIdx.x] + red[3][threadIdx.x]);
 }
 
+// route_partial on the matrix cores (bf16 q): grid (chunk of 16 full
+// blocks, row).  Wavefront w takes heads 16w..16w+15 as the A operand of
+// v_mfma_f32_16x16x32_bf16 (straight from q); the chunk's 16 pooled keys are
+// split as kbar = hi + lo (both bf16, round to nearest, so each product is
+// exact and the dot carries ~2^-17 relative error) and laid out in LDS as
+// the B operand, one column per block.  Lane (g, c) gets heads 4g..4g+3
+// against block c; ReLU, the visibility mask and the sum over the 16 blocks
+// (across lanes) give the chunk's partial for every head.
+template <int D>
+__global__ __launch_bounds__(256) void route_partial_mfma_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ kbar,
+    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int L, int B, int H_I,
+    int nchunks, float* __restrict__ partial) {
+  constexpr int KK = D / 32;
+  constexpr int STRIDE = D * 2 + 16;                   // padded bf16 row (bytes)
+  __shared__ __align__(16) uint8_t hi_t[kRouteBlocks * STRIDE];
+  __shared__ __align__(16) uint8_t lo_t[kRouteBlocks * STRIDE];
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+  const int n = blockIdx.y, chunk = blockIdx.x;
+  const int Mf = (q_pos[n] + 1) / B;                   // blocks fully visible to row n
+  const int M = (L + B - 1) / B;
+  const int b0 = chunk * kRouteBlocks;
+  const int nb = min(kRouteBlocks, Mf - b0);
+  float* out = partial + (static_cast<size_t>(n) * nchunks + chunk) * H_I;
+  if (nb <= 0) {
+    for (int j = threadIdx.x; j < H_I; j += 256) out[j] = 0.f;
+    return;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  // A operand: head 16 * wave + c, elements 32 kk + 8 g .. + 8
+  const int j = wave * 16 + c;
+  bf16x8_t a[KK];
+  {
+    const uint16_t* qr = q + (static_cast<size_t>(n) * H_I + (j < H_I ? j : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4_t x = *reinterpret_cast<const u32x4_t*>(qr + 32 * kk + 8 * g);
+      if (j >= H_I) x = u32x4_t{0u, 0u, 0u, 0u};
+      a[kk] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
+  // the chunk's pooled keys, split into hi / lo bf16 rows
+  const float* src = kbar + (static_cast<size_t>(q_seq[n]) * M + b0) * D;
+  for (int f = tid; f < kRouteBlocks * D / 4; f += 256) {
+    const int blk = f / (D / 4), col = (f % (D / 4)) * 4;
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (blk < nb) x = *reinterpret_cast<const float4*>(src + static_cast<size_t>(blk) * D + col);
+    const float xs[4] = {x.x, x.y, x.z, x.w};
+    uint32_t hb[4], lb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t u = __float_as_uint(xs[e]);
+      hb[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+      const uint32_t ul = __float_as_uint(xs[e] - __uint_as_float(hb[e] << 16));
+      lb[e] = (ul + 0x7FFFu + ((ul >> 16) & 1u)) >> 16;
+    }
+    *reinterpret_cast<uint2*>(hi_t + blk * STRIDE + col * 2) =
+        make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+    *reinterpret_cast<uint2*>(lo_t + blk * STRIDE + col * 2) =
+        make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+  }
+  __syncthreads();
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const int off = c * STRIDE + 64 * kk + 16 * g;
+    const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(hi_t + off));
+    const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(lo_t + off));
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk], bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk], bl, acc, 0, 0, 0);
+  }
+  // ReLU over the visible blocks, then the sum over the 16 block columns
+  const bool vis = c < nb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v = vis ? relu(acc[i]) : 0.f;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+    const int jj = wave * 16 + 4 * g + i;
+    if (c == 0 && jj < H_I) out[jj] = v;
+  }
+}
+
 // Many query rows over one key sequence (prefill): the router dots are a
 // GEMM, [rows x H_I, d] x [d, M], run on v_mfma_f32_16x16x32_bf16.  q is
 // exact in bf16; each pooled key is split as kbar = hi + lo with hi, lo
@@ -119,9 +205,32 @@ __global__ __launch_bounds__(256) void route_partial_kernel(
 // visible block is added by route_select.
 constexpr int kRouteTile = 64;       // pooled blocks per LDS tile
 
+// The pooled table of one sequence as bf16 hi / lo halves: kbar = hi + lo,
+// hi = RNE(kbar), lo = RNE(kbar - hi).
+__global__ __launch_bounds__(256) void route_split_kernel(const float* __restrict__ kbar,
+                                                          size_t n4, uint16_t* __restrict__ hi,
+                                                          uint16_t* __restrict__ lo) {
+  for (size_t f = blockIdx.x * static_cast<size_t>(256) + threadIdx.x; f < n4;
+       f += static_cast<size_t>(gridDim.x) * 256) {
+    const float4 x = reinterpret_cast<const float4*>(kbar)[f];
+    const float xs[4] = {x.x, x.y, x.z, x.w};
+    uint32_t hb[4], lb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t u = __float_as_uint(xs[e]);
+      hb[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+      const uint32_t ul = __float_as_uint(xs[e] - __uint_as_float(hb[e] << 16));
+      lb[e] = (ul + 0x7FFFu + ((ul >> 16) & 1u)) >> 16;
+    }
+    reinterpret_cast<uint2*>(hi)[f] = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+    reinterpret_cast<uint2*>(lo)[f] = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+  }
+}
+
 template <int HPI>
 __global__ __launch_bounds__(256) void route_mfma_kernel(const uint16_t* __restrict__ q,
-                                                         const float* __restrict__ kbar,
+                                                         const uint16_t* __restrict__ kb_hi,
+                                                         const uint16_t* __restrict__ kb_lo,
                                                          const int32_t* __restrict__ q_pos,
                                                          int N, int L, int B, int H_I,
                                                          float* __restrict__ partial) {
@@ -166,27 +275,19 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const uint16_t* __restr
 
   for (int b0 = 0; b0 < mmax; b0 += kRouteTile) {
     __syncthreads();
-    // split the tile's pooled keys into hi / lo bf16 rows in LDS
-    for (int f = tid; f < kRouteTile * D / 4; f += 256) {
-      const int blk = f / (D / 4), col = (f % (D / 4)) * 4;
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (b0 + blk < M) x = *reinterpret_cast<const float4*>(kbar + static_cast<size_t>(b0 + blk) * D + col);
-      const float xs[4] = {x.x, x.y, x.z, x.w};
-      uint32_t hb[4], lb[4];
+    // the tile's pooled keys (bf16 hi / lo rows) into LDS
+    constexpr int PIECES = kRouteTile * D * 2 / 16;     // 16-byte pieces per half
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t u = __float_as_uint(xs[e]);
-        hb[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-        const float lo = xs[e] - __uint_as_float(hb[e] << 16);
-        const uint32_t ul = __float_as_uint(lo);
-        lb[e] = (ul + 0x7FFFu + ((ul >> 16) & 1u)) >> 16;
-      }
-      uint2 hp = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
-      uint2 lp = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
-      *reinterpret_cast<uint2*>(hi_t + blk * STRIDE + col * 2) = hp;
-      *reinterpret_cast<uint2*>(lo_t + blk * STRIDE + col * 2) = lp;
+    for (int i = 0; i < PIECES / 256; ++i) {
+      const int f = tid + 256 * i;
+      const int blk = f / (D / 8), col = (f % (D / 8)) * 8;
+      const size_t src = static_cast<size_t>(b0 + blk < M ? b0 + blk : 0) * D + col;
+      const u32x4_t h = *reinterpret_cast<const u32x4_t*>(kb_hi + src);
+      const u32x4_t l = *reinterpret_cast<const u32x4_t*>(kb_lo + src);
+      *reinterpret_cast<u32x4_t*>(hi_t + blk * STRIDE + col * 2) = h;
+      *reinterpret_cast<u32x4_t*>(lo_t + blk * STRIDE + col * 2) = l;
     }
-    __syncthreads();
+  __syncthreads();
 #pragma unroll
     for (int ct = 0; ct < kRouteTile / 16; ++ct) {
       const int blk = b0 + ct * 16 + c;                // this lane's output column
@@ -207,7 +308,7 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const uint16_t* __restr
         }
         const bool vis = blk < mf_row[rt];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc_rows[rt][i] += vis ? fmaxf(acc[i], 0.f) : 0.f;
+        for (int i = 0; i < 4; ++i) acc_rows[rt][i] += vis ? relu(acc[i]) : 0.f;
       }
     }
   }
@@ -337,21 +438,35 @@ hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
   int nchunks = a.nchunks;
   if (route_uses_mfma(a)) {
     nchunks = 1;
+    const int M = (a.L + a.B - 1) / a.B;
+    const size_t n4 = static_cast<size_t>(M) * 128 / 4;
+    uint16_t* hi = a.kb_split;
+    uint16_t* lo = a.kb_split + static_cast<size_t>(M) * 128;
+    const size_t nblk = (n4 + 255) / 256;
+    const unsigned sb = static_cast<unsigned>(nblk < 1024 ? nblk : 1024);
+    MISA_LAUNCH(K_ROUTE_SPLIT, route_split_kernel, dim3(sb), dim3(256), 0, st, a.kbar, n4, hi,
+                lo);
     const int hpi = a.H_I <= 16 ? 16 : (a.H_I <= 32 ? 32 : 64);
     const dim3 grid((a.N + 256 / hpi - 1) / (256 / hpi));
     const uint16_t* q = static_cast<const uint16_t*>(a.q);
     if (hpi == 16)
-      MISA_LAUNCH(K_ROUTE_PARTIAL, route_mfma_kernel<16>, grid, dim3(256), 0, st, q, a.kbar,
+      MISA_LAUNCH(K_ROUTE_PARTIAL, route_mfma_kernel<16>, grid, dim3(256), 0, st, q, hi, lo,
                   a.q_pos, a.N, a.L, a.B, a.H_I, a.partial);
     else if (hpi == 32)
-      MISA_LAUNCH(K_ROUTE_PARTIAL, route_mfma_kernel<32>, grid, dim3(256), 0, st, q, a.kbar,
+      MISA_LAUNCH(K_ROUTE_PARTIAL, route_mfma_kernel<32>, grid, dim3(256), 0, st, q, hi, lo,
                   a.q_pos, a.N, a.L, a.B, a.H_I, a.partial);
     else
-      MISA_LAUNCH(K_ROUTE_PARTIAL, route_mfma_kernel<64>, grid, dim3(256), 0, st, q, a.kbar,
+      MISA_LAUNCH(K_ROUTE_PARTIAL, route_mfma_kernel<64>, grid, dim3(256), 0, st, q, hi, lo,
                   a.q_pos, a.N, a.L, a.B, a.H_I, a.partial);
   } else {
-    MISA_LAUNCH(K_ROUTE_PARTIAL, (route_partial_kernel<QT, D>), dim3(a.nchunks, a.N), dim3(256),
-                0, st, a.q, a.kbar, a.q_seq, a.q_pos, a.L, a.B, a.H_I, a.nchunks, a.partial);
+    if constexpr (QT == DT_BF16)
+      MISA_LAUNCH(K_ROUTE_PARTIAL, route_partial_mfma_kernel<D>, dim3(a.nchunks, a.N), dim3(256),
+                  0, st, static_cast<const uint16_t*>(a.q), a.kbar, a.q_seq, a.q_pos, a.L, a.B,
+                  a.H_I, a.nchunks, a.partial);
+    else
+      MISA_LAUNCH(K_ROUTE_PARTIAL, (route_partial_kernel<QT, D>), dim3(a.nchunks, a.N),
+                  dim3(256), 0, st, a.q, a.kbar, a.q_seq, a.q_pos, a.L, a.B, a.H_I, a.nchunks,
+                  a.partial);
   }
   MISA_LAUNCH(K_ROUTE_SELECT, (route_select_kernel<QT, KT, D>), dim3(a.N), dim3(256), 0, st,
               a.q, a.w, a.k, a.k_scale, a.q_seq, a.q_pos, a.L, a.B, a.H_I, a.h, nchunks,

@@ -621,10 +621,10 @@ __global__ __launch_bounds__(256) void topk_tau_kernel(const uint32_t* __restric
   }
 }
 
-// One 256-thread workgroup per row; each thread keeps up to kCandPer
+// One 512-thread workgroup per row; each thread keeps up to kCandPer
 // candidates in registers.  Dynamic LDS: the row's winner bitmap (nwords_max
 // words) and a 16-bit per-word prefix of marked bits.
-constexpr int kCandThreads = 256;
+constexpr int kCandThreads = 512;
 constexpr int kCandPer = kCandRow / kCandThreads;
 
 __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
@@ -637,7 +637,7 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
   __shared__ __align__(16) uint32_t hB[kBins2];
   __shared__ uint32_t spre[257];
   __shared__ uint32_t tpre[kCandThreads];
-  __shared__ uint32_t sm[4];
+  __shared__ uint32_t sm[kCandThreads / 64];
   __shared__ uint32_t res[4];
   __shared__ uint32_t bad;
   constexpr int NT = kCandThreads;
@@ -688,7 +688,7 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
     }
   }
   for (int b = tid; b < kBins0; b += NT) hA[b] = 0u;
-  hB[tid] = 0u;
+  if (tid < kBins2) hB[tid] = 0u;
   __syncthreads();
   // exact threshold: three radix levels over the candidates
 #pragma unroll

@@ -349,19 +349,22 @@ int gcd(int a, int b) {
 
 // Key-range splits: about 4 rounds of chip-resident workgroups (the last
 // round partly idle costs at most a quarter), rounded to whole rounds when
-// the row-block count allows; at least 4 key tiles per split, at most 256.
-int choose_splits(int qblocks, int L, int slots) {
-  const int max_s = max(1, min(256, L / (4 * kKeyTile)));
+// the row-block count allows; at least min_tiles key tiles per split, at most
+// 256 splits.
+int choose_splits(int qblocks, int L, int slots, int min_tiles) {
+  const int max_s = max(1, min(256, L / (min_tiles * kKeyTile)));
   int s = (4 * slots + qblocks - 1) / qblocks;
   const int m = slots / gcd(slots, qblocks);            // splits per whole round
   if (m <= max_s) s = (s + m - 1) / m * m;
   return max(1, min(s, max_s));
 }
 
+// min_tiles: key tiles per split at least (the sampled pass, with few keys
+// per row, keeps longer splits so each workgroup's operand loads pay off)
 template <int HP, int D, bool CAND>
-int splits_t(int N, int L) {
+int splits_t(int N, int L, int min_tiles = 4) {
   constexpr int QB = kRowsPerWG / HP;
-  return choose_splits((N + QB - 1) / QB, L, chip_slots<HP, D, CAND>());
+  return choose_splits((N + QB - 1) / QB, L, chip_slots<HP, D, CAND>(), min_tiles);
 }
 
 template <int HP, int D>
@@ -387,7 +390,8 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   p.cap = a.cap;
   constexpr int QB = kRowsPerWG / HP;
   const int qblocks = (a.N + QB - 1) / QB;
-  const int splits = a.cand_out ? splits_t<HP, D, true>(a.N, p.L) : splits_t<HP, D, false>(a.N, p.L);
+  const int splits = a.cand_out ? splits_t<HP, D, true>(a.N, p.L)
+                                : splits_t<HP, D, false>(a.N, p.L, a.key_step > 1 ? 16 : 4);
   p.splits = splits;
   p.keys_per_split = ((p.L + splits - 1) / splits + kKeyTile - 1) / kKeyTile * kKeyTile;
   if (a.cand_out)

@@ -168,9 +168,10 @@ int32_t misa_last_hip_error(void);
 /*
  * Kernel timing for benchmarks.  misa_profile_begin(capacity) creates
  * `capacity` pairs of HIP events (host-side allocation happens here, not in
- * the timed calls) and from then on brackets every kernel the library
- * launches with an event pair recorded on that kernel's stream, until
- * capacity is used up or misa_profile_end is called.  misa_profile_end
+ * the timed calls) and from then on launches every kernel of the library
+ * with an event pair (hipExtLaunchKernelGGL) that the runtime stamps with the
+ * kernel's own start and end on its stream, until capacity is used up or
+ * misa_profile_end is called.  misa_profile_end
  * synchronises the recorded events and writes up to `max` records:
  * kernel_id[i] (see misa_kernel_name) and ms[i], the elapsed time between the
  * pair.  It returns the number of records written (negative on error) and

@@ -130,7 +130,7 @@ size_t route_bytes(int N, int L, int B, int H_I) {
 // ---------------------------------------------------------------- kernel timing
 struct Profiler {
   bool on = false;
-  int cap = 0, used = 0, pending = -1;
+  int cap = 0, used = 0;
   std::vector<hipEvent_t> ev0, ev1;
   std::vector<int> ids;
 };
@@ -217,18 +217,13 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* w, const void*
 
 namespace misa {
 
-void prof_start(hipStream_t st, int kernel_id) {
-  if (!g_prof.on || g_prof.used >= g_prof.cap) return;
-  g_prof.pending = kernel_id;
-  (void)hipEventRecord(g_prof.ev0[g_prof.used], st);
-}
-
-void prof_stop(hipStream_t st) {
-  if (!g_prof.on || g_prof.pending < 0 || g_prof.used >= g_prof.cap) return;
-  (void)hipEventRecord(g_prof.ev1[g_prof.used], st);
-  g_prof.ids[g_prof.used] = g_prof.pending;
-  g_prof.pending = -1;
+bool prof_events(int kernel_id, hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_prof.on || g_prof.used >= g_prof.cap) return false;
+  *start = g_prof.ev0[g_prof.used];
+  *stop = g_prof.ev1[g_prof.used];
+  g_prof.ids[g_prof.used] = kernel_id;
   ++g_prof.used;
+  return true;
 }
 
 }  // namespace misa
@@ -360,7 +355,6 @@ int32_t misa_profile_begin(int32_t capacity) {
   }
   g_prof.cap = capacity;
   g_prof.used = 0;
-  g_prof.pending = -1;
   g_prof.on = true;
   return MISA_OK;
 }

@@ -1,6 +1,7 @@
 // Host-side launch interface between the C ABI layer and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -26,15 +27,19 @@ enum KernelId : int {
   K_COUNT_IDS
 };
 
-// Kernel timing hooks (no-ops unless misa_profile_begin is active).
-void prof_start(hipStream_t st, int kernel_id);
-void prof_stop(hipStream_t st);
+// Kernel timing (only while misa_profile_begin is active): the launch goes
+// through hipExtLaunchKernelGGL with a start/stop event pair, which the
+// runtime stamps with the kernel's own start and end.
+bool prof_events(int kernel_id, hipEvent_t* start, hipEvent_t* stop);
 
-#define MISA_LAUNCH(kid, kernel, grid, block, lds, st, ...)              \
-  do {                                                                   \
-    ::misa::prof_start((st), (kid));                                     \
-    hipLaunchKernelGGL((kernel), (grid), (block), (lds), (st), __VA_ARGS__); \
-    ::misa::prof_stop((st));                                             \
+#define MISA_LAUNCH(kid, kernel, grid, block, lds, st, ...)                                  \
+  do {                                                                                     \
+    hipEvent_t misa_ev0_, misa_ev1_;                                                       \
+    if (::misa::prof_events((kid), &misa_ev0_, &misa_ev1_))                                \
+      hipExtLaunchKernelGGL((kernel), (grid), (block), (lds), (st), misa_ev0_, misa_ev1_, 0, \
+                            __VA_ARGS__);                                                  \
+    else                                                                                   \
+      hipLaunchKernelGGL((kernel), (grid), (block), (lds), (st), __VA_ARGS__);             \
   } while (0)
 
 // ---------------------------------------------------------------- pooling

@@ -373,3 +373,61 @@ def test_prefill_candidate_fallback_bit_exact():
     assert np.array_equal(heads[rows], ref_heads)
     check_topk(idx[rows], sc[rows], oracle.scores(ps, ref_heads), p.topk, ps.visible(),
                exact=True)
+
+
+# ---------------------------------------------------------------- edge cases and fallback paths
+def _exact_misa(p, rows=None):
+    """Full MISA on the GPU vs the oracle, bit for bit (integer inputs)."""
+    dp = DeviceProblem(p)
+    kbar, heads, r, idx, sc = misa_gpu(dp)
+    rows = np.arange(p.N) if rows is None else np.asarray(rows)
+    ps = sub_problem(p, rows)
+    ref_heads, _ = oracle.route_heads(ps)
+    assert np.array_equal(heads[rows], ref_heads)
+    check_topk(idx[rows], sc[rows], oracle.scores(ps, ref_heads), p.topk, ps.visible(),
+               exact=True)
+    return dp
+
+
+def test_rows_longer_than_lds_bitmap():
+    """Rows past 2^18 tokens: the few-rows select and the one-row select both
+    fall back to the full radix path (and the prefill candidate path flags
+    every row)."""
+    L = 300000
+    p = synth.integer_problem("long2", 61, N=2, S=2, L=L, d=64, H_I=8, h=2, B=512, topk=3000,
+                              q_pos=np.array([L - 1, 270000], np.int32))
+    _exact_misa(p)
+    pos = np.random.default_rng(62).choice(np.arange(263000, L), 128, replace=False)
+    p = synth.integer_problem("long128", 63, N=128, S=1, L=L, d=64, H_I=8, h=2, B=512,
+                              topk=100, q_pos=pos.astype(np.int32),
+                              q_seq=np.zeros(128, np.int32))
+    _exact_misa(p, rows=np.r_[0:3, 125:128])
+
+
+@pytest.mark.parametrize("N", [3, 130])
+def test_all_scores_tied(N):
+    """Zero keys: every score is 0, the threshold bin holds every token (more
+    than the LDS candidate list), and the lowest indices must win."""
+    L = 20000
+    p = synth.integer_problem("tied", 64, N=N, S=1, L=L, d=128, H_I=16, h=4, B=128,
+                              topk=1500, q_pos=(L - 1 - np.arange(N)).astype(np.int32),
+                              q_seq=np.zeros(N, np.int32))
+    p = synth.Problem(p.name, p.q, p.q_dt, p.w, np.zeros_like(p.k), p.k_dt, p.k_scale, p.q_seq,
+                      p.q_pos, p.B, p.h, p.topk, p.k_prime)
+    dp = _exact_misa(p, rows=np.r_[0:3])
+    heads, _ = dp.route(dp.pool())
+    idx, _ = dp.score_topk(heads)
+    assert np.array_equal(np_(idx)[0], np.arange(p.topk))
+
+
+def test_single_key_and_one_head():
+    """L = 1, B > L, H_I = h = 1, k > L: one token, one head."""
+    p = synth.integer_problem("one", 65, N=3, S=3, L=1, d=128, H_I=1, h=1, B=128, topk=5,
+                              q_pos=np.zeros(3, np.int32))
+    _exact_misa(p)
+
+
+def test_topk_at_the_limit():
+    """k = 65536 (the largest the ABI takes) over 70000-token rows."""
+    p = synth.small("kmax", 66, N=2, S=2, L=70000, d=64, H_I=16, h=4, B=256, topk=65536)
+    check_misa(p)

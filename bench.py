@@ -258,15 +258,21 @@ def kernel_times(torch, binding, fn, steps, warmup, per_step):
         {k: len(v) / steps for k, v in by.items()}
 
 
-def cpu_baseline(p, h):
+def cpu_baseline(p, h, min_seconds=10.0, max_passes=200):
+    """The oracle on the host cores over the whole workload, repeated until
+    about min_seconds of CPU work have run (one pass is well under a second)."""
     import oracle
-    t0 = time.perf_counter()
-    oracle.misa(p, h=h)
-    dt = time.perf_counter() - t0
-    return {"value": p.tokens_indexed() / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.misa(p, h=h)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or passes >= max_passes:
+            break
+    return {"value": passes * p.tokens_indexed() / dt, "unit": "tokens/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
             "sample": f"the full workload ({p.N} queries x {p.L} keys, pooling+routing+scoring+"
-                      f"top-k in double precision), one pass, {dt:.2f} s"}
+                      f"top-k in double precision), {passes} passes in {dt:.1f} s"}
 
 
 def prefill_main(args):

@@ -281,15 +281,19 @@ __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(Pre
   for (int i = 0; i < QB; ++i) minpos = min(minpos, pos_lds[i] < 0 ? 0x7FFFFFFF : pos_lds[i]);
   const bool full_block = qrow0 + QB <= p.N;
 
-  // three-stage pipeline: tile i+2 streams into LDS while tile i is scored
+  // kStages-stage ring: tiles i+1 .. i+kStages-1 stream into LDS while tile i
+  // is scored; before each barrier a wavefront waits only for the tile the
+  // next iteration reads (its DMA loads complete in order)
+  constexpr int S = kStages;
+  constexpr int AHEAD = (S - 2) * LY::PER_THREAD;      // loads still in flight after a wait
   const int ntiles = (ks1 - ks0 + kKeyTile - 1) / kKeyTile;
-  dma_key_tile<D>(p.k, ks0, p.L, p.key_step, tiles[0], wave, lane);
-  if (ntiles > 1) {
-    dma_key_tile<D>(p.k, ks0 + kKeyTile, p.L, p.key_step, tiles[1], wave, lane);
-    wait_vm_barrier<LY::PER_THREAD>();
-  } else {
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j)
+    if (j < ntiles) dma_key_tile<D>(p.k, ks0 + j * kKeyTile, p.L, p.key_step, tiles[j], wave, lane);
+  if (ntiles >= S - 1)
+    wait_vm_barrier<AHEAD>();
+  else
     wait_vm_barrier<0>();
-  }
   int buf = 0;
   for (int i = 0; i < ntiles; ++i) {
     const int key0 = ks0 + i * kKeyTile;
@@ -299,14 +303,14 @@ __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(Pre
       score_tile<HP, D, false, CAND>(tiles[buf], key0, a, wv, o, p.cap, g, c);
     else
       score_tile<HP, D, true, CAND>(tiles[buf], key0, a, wv, o, p.cap, g, c);
-    const int nb = buf == 0 ? kStages - 1 : buf - 1;    // (buf + 2) % 3, read two tiles ago
-    if (i + 2 < ntiles) {
-      dma_key_tile<D>(p.k, key0 + 2 * kKeyTile, p.L, p.key_step, tiles[nb], wave, lane);
-      wait_vm_barrier<LY::PER_THREAD>();                 // tile i+1 has landed
+    const int nb = buf == 0 ? S - 1 : buf - 1;          // the buffer tile i-1 was read from
+    if (i + S - 1 < ntiles) {
+      dma_key_tile<D>(p.k, key0 + (S - 1) * kKeyTile, p.L, p.key_step, tiles[nb], wave, lane);
+      wait_vm_barrier<AHEAD>();                         // tile i+1 has landed
     } else {
       wait_vm_barrier<0>();
     }
-    buf = buf == kStages - 1 ? 0 : buf + 1;
+    buf = buf == S - 1 ? 0 : buf + 1;
   }
   if constexpr (CAND) {
 #pragma unroll

@@ -78,11 +78,25 @@ def lib():
 
 
 # ---------------------------------------------------------------- marshalling helpers
-def _ptr(t: Optional[torch.Tensor]):
+def _ptr(t: Optional[torch.Tensor], name: str = "tensor", dtypes=None, shape=None):
+    """Device pointer of a contiguous GPU tensor (None passes through).  The
+    library reads and writes raw memory, so layout mistakes are caught here."""
     if t is None:
         return None
-    assert t.is_contiguous(), "tensors must be contiguous"
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     return ctypes.c_void_p(t.data_ptr())
+
+
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+_KEYS = (torch.float32, torch.bfloat16, torch.int16, torch.uint8, torch.float8_e4m3fn)
 
 
 def _stream(t: torch.Tensor):
@@ -121,8 +135,9 @@ def misa_pool_keys(k: torch.Tensor, B: int, k_scale: Optional[torch.Tensor] = No
     M = -(-L // B)
     if kbar is None:
         kbar = torch.empty((S, M, d), dtype=torch.float32, device=k.device)
-    _check("misa_pool_keys", lib().misa_pool_keys(_ptr(k), _ptr(k_scale), _dtype_code(k), S, L, d,
-                                                  B, _ptr(kbar), _stream(k)))
+    _check("misa_pool_keys", lib().misa_pool_keys(
+        _ptr(k, "k", _KEYS), _ptr(k_scale, "k_scale", _F32, (S, L)), _dtype_code(k), S, L, d, B,
+        _ptr(kbar, "kbar", _F32, (S, M, d)), _stream(k)))
     return kbar
 
 
@@ -130,6 +145,8 @@ def misa_route_heads(q, w, kbar, k, q_seq, q_pos, B: int, h: int, k_scale=None, 
                      head_score=None, ws=None, want_scores=True):
     N, H_I, d = q.shape
     S, L, _ = k.shape
+    if k.shape[2] != d:
+        raise ValueError(f"q has d={d} but k has d={k.shape[2]}")
     if heads is None:
         heads = torch.empty((N, h), dtype=torch.int32, device=q.device)
     if head_score is None and want_scores:
@@ -137,9 +154,12 @@ def misa_route_heads(q, w, kbar, k, q_seq, q_pos, B: int, h: int, k_scale=None, 
     if ws is None:
         ws = workspace(MISA_OP_ROUTE, N, L, d, H_I, B, device=q.device)
     _check("misa_route_heads", lib().misa_route_heads(
-        _ptr(q), _dtype_code(q), _ptr(w), _ptr(kbar), _ptr(k), _ptr(k_scale), _dtype_code(k),
-        _ptr(q_seq), _ptr(q_pos), N, S, L, d, B, H_I, h, _ptr(heads), _ptr(head_score),
-        _ptr(ws), ws.numel(), _stream(q)))
+        _ptr(q, "q", _KEYS), _dtype_code(q), _ptr(w, "w", _F32, (N, H_I)),
+        _ptr(kbar, "kbar", _F32, (S, -(-L // B), d)), _ptr(k, "k", _KEYS),
+        _ptr(k_scale, "k_scale", _F32, (S, L)), _dtype_code(k), _ptr(q_seq, "q_seq", _I32, (N,)),
+        _ptr(q_pos, "q_pos", _I32, (N,)), N, S, L, d, B, H_I, h,
+        _ptr(heads, "heads", _I32, (N, h)), _ptr(head_score, "head_score", _F32, (N, H_I)),
+        _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(q)))
     return heads, head_score
 
 
@@ -147,6 +167,8 @@ def misa_score_topk(q, w, k, q_seq, q_pos, heads, topk: int, k_scale=None, idx=N
                     ws=None, want_score=True):
     N, H_I, d = q.shape
     S, L, _ = k.shape
+    if k.shape[2] != d:
+        raise ValueError(f"q has d={d} but k has d={k.shape[2]}")
     h = heads.shape[1]
     if idx is None:
         idx = torch.empty((N, topk), dtype=torch.int32, device=q.device)
@@ -155,9 +177,11 @@ def misa_score_topk(q, w, k, q_seq, q_pos, heads, topk: int, k_scale=None, idx=N
     if ws is None:
         ws = workspace(MISA_OP_SCORE_TOPK, N, L, d, H_I, topk=topk, device=q.device)
     _check("misa_score_topk", lib().misa_score_topk(
-        _ptr(q), _dtype_code(q), _ptr(w), _ptr(k), _ptr(k_scale), _dtype_code(k), _ptr(q_seq),
-        _ptr(q_pos), _ptr(heads), N, S, L, d, H_I, h, topk, _ptr(idx), _ptr(score), _ptr(ws),
-        ws.numel(), _stream(q)))
+        _ptr(q, "q", _KEYS), _dtype_code(q), _ptr(w, "w", _F32, (N, H_I)), _ptr(k, "k", _KEYS),
+        _ptr(k_scale, "k_scale", _F32, (S, L)), _dtype_code(k), _ptr(q_seq, "q_seq", _I32, (N,)),
+        _ptr(q_pos, "q_pos", _I32, (N,)), _ptr(heads, "heads", _I32, (N, h)), N, S, L, d, H_I, h,
+        topk, _ptr(idx, "idx", _I32, (N, topk)), _ptr(score, "score", _F32, (N, topk)),
+        _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(q)))
     return idx, score
 
 
@@ -165,6 +189,8 @@ def dsa_score_topk(q, w, k, q_seq, q_pos, topk: int, k_scale=None, idx=None, sco
                    ws=None, want_score=True):
     N, H_I, d = q.shape
     S, L, _ = k.shape
+    if k.shape[2] != d:
+        raise ValueError(f"q has d={d} but k has d={k.shape[2]}")
     if idx is None:
         idx = torch.empty((N, topk), dtype=torch.int32, device=q.device)
     if score is None and want_score:
@@ -172,8 +198,11 @@ def dsa_score_topk(q, w, k, q_seq, q_pos, topk: int, k_scale=None, idx=None, sco
     if ws is None:
         ws = workspace(MISA_OP_SCORE_TOPK, N, L, d, H_I, topk=topk, device=q.device)
     _check("dsa_score_topk", lib().dsa_score_topk(
-        _ptr(q), _dtype_code(q), _ptr(w), _ptr(k), _ptr(k_scale), _dtype_code(k), _ptr(q_seq),
-        _ptr(q_pos), N, S, L, d, H_I, topk, _ptr(idx), _ptr(score), _ptr(ws), ws.numel(),
+        _ptr(q, "q", _KEYS), _dtype_code(q), _ptr(w, "w", _F32, (N, H_I)), _ptr(k, "k", _KEYS),
+        _ptr(k_scale, "k_scale", _F32, (S, L)), _dtype_code(k), _ptr(q_seq, "q_seq", _I32, (N,)),
+        _ptr(q_pos, "q_pos", _I32, (N,)), N, S, L, d, H_I, topk,
+        _ptr(idx, "idx", _I32, (N, topk)), _ptr(score, "score", _F32, (N, topk)), _ptr(ws, "ws"),
+        ws.numel() * ws.element_size(),
         _stream(q)))
     return idx, score
 
@@ -182,6 +211,8 @@ def misa_rerank(q, w, k, q_seq, q_pos, cand, topk: int, k_scale=None, idx=None, 
                 ws=None, want_score=True):
     N, H_I, d = q.shape
     S, L, _ = k.shape
+    if k.shape[2] != d:
+        raise ValueError(f"q has d={d} but k has d={k.shape[2]}")
     k_prime = cand.shape[1]
     if idx is None:
         idx = torch.empty((N, topk), dtype=torch.int32, device=q.device)
@@ -190,9 +221,12 @@ def misa_rerank(q, w, k, q_seq, q_pos, cand, topk: int, k_scale=None, idx=None, 
     if ws is None:
         ws = workspace(MISA_OP_RERANK, N, L, d, H_I, topk=topk, k_prime=k_prime, device=q.device)
     _check("misa_rerank", lib().misa_rerank(
-        _ptr(q), _dtype_code(q), _ptr(w), _ptr(k), _ptr(k_scale), _dtype_code(k), _ptr(q_seq),
-        _ptr(q_pos), _ptr(cand), N, S, L, d, H_I, k_prime, topk, _ptr(idx), _ptr(score),
-        _ptr(ws), ws.numel(), _stream(q)))
+        _ptr(q, "q", _KEYS), _dtype_code(q), _ptr(w, "w", _F32, (N, H_I)), _ptr(k, "k", _KEYS),
+        _ptr(k_scale, "k_scale", _F32, (S, L)), _dtype_code(k), _ptr(q_seq, "q_seq", _I32, (N,)),
+        _ptr(q_pos, "q_pos", _I32, (N,)), _ptr(cand, "cand", _I32, (N, k_prime)), N, S, L, d,
+        H_I, k_prime, topk, _ptr(idx, "idx", _I32, (N, topk)),
+        _ptr(score, "score", _F32, (N, topk)), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+        _stream(q)))
     return idx, score
 
 

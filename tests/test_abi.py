@@ -113,3 +113,30 @@ def test_binding_argument_counts_match_header():
     for name, n in counts.items():
         fn = getattr(lib, name)
         assert fn.argtypes is not None and len(fn.argtypes) == n, name
+
+
+def test_binding_rejects_host_and_strided_tensors():
+    """The binding hands raw pointers to the library: host tensors, strided
+    views and wrong dtypes are refused before any call."""
+    import torch
+    k = torch.zeros((1, 256, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        b.misa_pool_keys(k, 128)
+    q = torch.zeros((2, 4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        b.misa_score_topk(q, torch.zeros((2, 4)), k, torch.zeros(2, dtype=torch.int32),
+                          torch.zeros(2, dtype=torch.int32), torch.zeros((2, 1), dtype=torch.int32),
+                          8, ws=torch.zeros(256, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="d="):
+        b.misa_score_topk(q, torch.zeros((2, 4)), torch.zeros((1, 256, 64), dtype=torch.bfloat16),
+                          torch.zeros(2, dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
+                          torch.zeros((2, 1), dtype=torch.int32), 8)
+
+
+def test_binding_pointer_checks():
+    import torch
+    with pytest.raises(ValueError, match="GPU tensor"):
+        b._ptr(torch.zeros((4, 4)), "t")
+    with pytest.raises(ValueError, match="GPU tensor"):
+        b._ptr(object(), "t")
+    assert b._ptr(None, "t") is None

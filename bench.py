@@ -258,6 +258,62 @@ def kernel_times(torch, binding, fn, steps, warmup, per_step):
         {k: len(v) / steps for k, v in by.items()}
 
 
+def step_percentiles(torch, fn, reps=100, warmup=5):
+    """Per-step latency (us) from a torch event pair around each step: p10/p50/p90."""
+    import numpy as np
+    for s in range(warmup):
+        fn(s % REPLICAS)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for s, (a, b) in enumerate(ev):
+        a.record()
+        fn(s % REPLICAS)
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return {"p10": round(float(np.percentile(t, 10)), 2), "p50": round(float(np.median(t)), 2),
+            "p90": round(float(np.percentile(t, 90)), 2)}
+
+
+def measured_read_gbs(torch):
+    """In-run streaming-read reference: row sums of a [4096, 32768] fp32 tensor
+    (512 MiB read, 16 KiB written) with torch, not the library: what a plain
+    HBM-bound kernel reaches on this GPU."""
+    x = torch.ones((4096, 32768), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        x.sum(dim=1)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(10):
+        x.sum(dim=1)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 10 * x.numel() * 4 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del x
+    return round(gbs, 1)
+
+
+def measured_mfma_tflops(torch):
+    """In-run bf16 matrix-core reference: an 8192^3 torch.matmul (hipBLASLt)."""
+    n = 8192
+    x = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
+    y = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        torch.matmul(x, y)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(10):
+        torch.matmul(x, y)
+    b.record()
+    torch.cuda.synchronize()
+    tf = 10 * 2.0 * n ** 3 / (a.elapsed_time(b) * 1e-3) / 1e12
+    del x, y
+    return round(tf, 1)
+
+
 def cpu_baseline(p, h, min_seconds=10.0, max_passes=200):
     """The oracle on the host cores over the whole workload, repeated until
     about min_seconds of CPU work have run (one pass is well under a second)."""
@@ -305,6 +361,7 @@ def prefill_main(args):
                                want_score=False)
 
     ms = timed(torch, step, args.steps, args.warmup)
+    pct = step_percentiles(torch, step, reps=max(20, args.steps), warmup=2)
     ms_e, kt, per = kernel_times(torch, binding, step, max(3, args.steps // 4), 1, 16)
     ms_d = timed(torch, dense, max(3, args.steps // 4), 1)
     _, ktd, _ = kernel_times(torch, binding, dense, 3, 1, 8)
@@ -329,11 +386,15 @@ def prefill_main(args):
                      "kernel": "score_prefill_kernel", "kernel_ms": sc_ms,
                      "algorithmic_flop_per_launch": flops},
         "extra": {"kernel_ms": {k: round(v, 4) for k, v in kt.items()},
+                  "step_us_percentiles": pct,
                   "dense_ms": round(ms_d, 4), "speedup_vs_dense": round(ms_d / ms, 3),
                   "dense_kernel_ms": {k: round(v, 4) for k, v in ktd.items()},
                   "dense_score_tflops": round(dflops / (dsc * 1e-3) / 1e12, 1) if dsc else None,
                   "routed_score_vs_dense_score": round(dsc / sc_ms, 3) if dsc and sc_ms else None},
     }
+    mtf = measured_mfma_tflops(torch)
+    line["roofline"]["measured_peak"] = mtf
+    line["roofline"]["frac_vs_measured_peak"] = round(tflops / mtf, 4) if tflops else None
     print(json.dumps(line), flush=True)
 
 
@@ -375,6 +436,7 @@ def main():
     log("[bench] timing MISA step (pool + route + score/top-k)")
     ms = timed(torch, rep.step_misa, args.steps, args.warmup)
     value = tokens / (ms * 1e-3)
+    pct = step_percentiles(torch, rep.step_misa, reps=max(100, args.steps), warmup=5)
     log(f"[bench] misa {ms:.4f} ms/step -> {value:.4e} tokens/s")
 
     log("[bench] per-kernel HIP events over the timed steps")
@@ -390,7 +452,10 @@ def main():
                 "algorithmic_bytes_per_launch": alg}
 
     extra = {"kernel_ms": {k: round(v, 5) for k, v in kt.items()},
-             "step_ms_with_kernel_events": round(ms_ev, 4)}
+             "step_ms_with_kernel_events": round(ms_ev, 4), "step_us_percentiles": pct}
+    mgbs = measured_read_gbs(torch)
+    roofline["measured_peak"] = mgbs
+    roofline["frac_vs_measured_peak"] = round(achieved / mgbs, 4)
     sc_ms = kt.get("score_mfma_kernel")
     if sc_ms:
         extra["score_kernel_hbm_gbs"] = round(key_bytes / (sc_ms * 1e-3) / 1e9, 1)

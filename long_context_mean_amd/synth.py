@@ -11,7 +11,8 @@ Shapes follow the DSA indexer of DeepSeek-V3.2 as described on the MISA pages
 from a Gaussian-cluster mixture; queries are N(0, 1/d); head weights N(0, 1).
 
 Storage conventions (all C-contiguous numpy arrays):
-  q       [N, H_I, d]  float32, or uint16 holding bf16 bit patterns
+  q       [N, H_I, d]  float32, uint16 holding bf16 bit patterns, or uint8 (e4m3 codes)
+  q_scale [N, H_I]     float32 (fp8 queries only, else None: one scale per head vector)
   w       [N, H_I]     float32
   k       [S, L, d]    float32, uint16 (bf16 bits), or uint8 (e4m3 codes)
   k_scale [S, L]       float32 (fp8 keys only, else None)
@@ -76,13 +77,22 @@ def f64_to_e4m3_codes(x: np.ndarray) -> np.ndarray:
     return code | sign
 
 
-def quantize_keys_e4m3(k32: np.ndarray):
-    """Per-token fp8 storage: scale = absmax/448 (fp32), codes = e4m3(k/scale).
-    A token whose keys are all zero gets scale 1 and zero codes."""
-    absmax = np.abs(k32).max(axis=-1).astype(np.float32)
+def quantize_e4m3(x32: np.ndarray):
+    """fp8 storage of vectors along the last axis (a key token, or one query
+    head): scale = absmax/448 (fp32), codes = e4m3(x/scale).  An all-zero
+    vector gets scale 1 and zero codes."""
+    absmax = np.abs(x32).max(axis=-1).astype(np.float32)
     scale = np.where(absmax > 0, absmax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    codes = f64_to_e4m3_codes(k32.astype(np.float64) / scale[..., None].astype(np.float64))
+    codes = f64_to_e4m3_codes(x32.astype(np.float64) / scale[..., None].astype(np.float64))
     return codes, scale
+
+
+def e4m3_codes_to_f32(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Stored value of fp8 vectors: scale * code value (fp32 product)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    mag = _E4M3_POS[np.minimum(c & 0x7F, 126)]
+    v = np.where(c & 0x80, -mag, mag).astype(np.float32)
+    return (v * np.asarray(scale, np.float32)[..., None]).astype(np.float32)
 
 
 # --------------------------------------------------------------------------
@@ -104,6 +114,7 @@ class Problem:
     topk: int
     k_prime: int = 0
     needles: Optional[np.ndarray] = None      # [N, n_needle, 2] (position, head)
+    q_scale: Optional[np.ndarray] = None      # [N, H_I] float32 (fp8 queries only)
 
     @property
     def N(self): return self.q.shape[0]
@@ -149,7 +160,11 @@ def mixture_problem(name, *, seed, N, S, L, d, H_I, h, B, topk, q_dt, k_dt,
         keys32[s] = _mixture_keys(rng, L, d, n_clusters, sigma)
     q32 = (rng.standard_normal((N, H_I, d)) / np.sqrt(d)).astype(np.float32)
     w = rng.standard_normal((N, H_I)).astype(np.float32)
-    q = _store(q32, q_dt)
+    q_scale = None
+    if q_dt == FP8:
+        q, q_scale = quantize_e4m3(q32)
+    else:
+        q = _store(q32, q_dt)
     if q_seq is None:
         q_seq = np.arange(N, dtype=np.int32) % S
     if q_pos is None:
@@ -159,7 +174,8 @@ def mixture_problem(name, *, seed, N, S, L, d, H_I, h, B, topk, q_dt, k_dt,
 
     needles = None
     if n_needles:
-        qv = bf16_bits_to_f32(q) if q_dt == BF16 else q
+        qv = (bf16_bits_to_f32(q) if q_dt == BF16 else
+              e4m3_codes_to_f32(q, q_scale) if q_dt == FP8 else q)
         needles = np.empty((N, n_needles, 2), dtype=np.int64)
         for n in range(N):
             pos = rng.choice(int(q_pos[n]) + 1, size=n_needles, replace=False)
@@ -170,17 +186,18 @@ def mixture_problem(name, *, seed, N, S, L, d, H_I, h, B, topk, q_dt, k_dt,
 
     k_scale = None
     if k_dt == FP8:
-        k, k_scale = quantize_keys_e4m3(keys32)
+        k, k_scale = quantize_e4m3(keys32)
     else:
         k = _store(keys32, k_dt)
     return Problem(name, q, q_dt, w, k, k_dt, k_scale, q_seq, q_pos, B, h, topk,
-                   k_prime, needles)
+                   k_prime, needles, q_scale)
 
 
 # --------------------------------------------------------------------------
 # the named workloads
 # --------------------------------------------------------------------------
-CONFIG_SEEDS = {"c1": 1001, "c2": 1002, "c3": 1003, "c3x": 1013, "c4": 1004, "c5": 1005}
+CONFIG_SEEDS = {"c1": 1001, "c2": 1002, "c3": 1003, "c3x": 1013, "c3f8": 1003, "c4": 1004,
+                "c5": 1005}
 
 
 def make(name: str, seed: Optional[int] = None, **over) -> Problem:
@@ -190,6 +207,8 @@ def make(name: str, seed: Optional[int] = None, **over) -> Problem:
           64 clusters (sigma 0.5)
       c3  bf16 prefill chunk: 4096 rows at positions 61440..65535 over one causal L=65536 prefix
       c3x the same prefill chunk at L=131072 (positions 126976..131071)
+      c3f8 the c3 chunk (same seed, same fp32 draws) stored in fp8: q per head and k per token
+          as e4m3 codes with an absmax/448 scale
       c4  bf16 long decode: 4 queries each over its own L=131072 with 32 planted needles (alpha=3)
       c5  fp8-key long decode for MISA-dagger: as c4 without needles, k'=8192 -> k=2048
     """
@@ -200,10 +219,11 @@ def make(name: str, seed: Optional[int] = None, **over) -> Problem:
     elif name == "c2":
         kw = dict(N=8, S=8, L=32768, d=128, H_I=64, h=8, B=128, topk=2048, q_dt=BF16, k_dt=BF16,
                   n_clusters=64, sigma=0.5)
-    elif name in ("c3", "c3x"):
-        L = 65536 if name == "c3" else 131072
+    elif name in ("c3", "c3x", "c3f8"):
+        L = 131072 if name == "c3x" else 65536
         T = 4096
-        kw = dict(N=T, S=1, L=L, d=128, H_I=64, h=8, B=128, topk=2048, q_dt=BF16, k_dt=BF16,
+        dt = FP8 if name == "c3f8" else BF16
+        kw = dict(N=T, S=1, L=L, d=128, H_I=64, h=8, B=128, topk=2048, q_dt=dt, k_dt=dt,
                   n_clusters=64, sigma=0.5, q_seq=np.zeros(T, np.int32),
                   q_pos=np.arange(L - T, L, dtype=np.int32))
     elif name == "c4":
@@ -232,11 +252,17 @@ def integer_problem(name: str, seed: int, *, N=2, S=2, L=300, d=64, H_I=8, h=3, 
                     wmax=4) -> Problem:
     """Small-integer q, k, w (exact in bf16, fp32 and e4m3): every dot product
     and every weighted head sum is an exact small integer in any precision,
-    so exact ties occur and every implementation must agree bit for bit."""
+    so exact ties occur and every implementation must agree bit for bit.
+    fp8 queries get power-of-two head scales, so their sums stay exact
+    (multiples of 1/4)."""
     rng = np.random.default_rng(seed)
     k32 = rng.integers(-kmax, kmax + 1, size=(S, L, d)).astype(np.float32)
     q32 = rng.integers(-qmax, qmax + 1, size=(N, H_I, d)).astype(np.float32)
     w = rng.integers(-wmax, wmax + 1, size=(N, H_I)).astype(np.float32)
+    q_scale = None
+    if q_dt == FP8:
+        # power-of-two head scales 1/4 .. 4: scaled products and sums stay exact
+        q_scale = np.ldexp(np.float32(1.0), rng.integers(-2, 3, size=(N, H_I))).astype(np.float32)
     if q_seq is None:
         q_seq = np.arange(N, dtype=np.int32) % S
     if q_pos is None:
@@ -247,6 +273,7 @@ def integer_problem(name: str, seed: int, *, N=2, S=2, L=300, d=64, H_I=8, h=3, 
         k_scale = np.ones((S, L), dtype=np.float32)
     else:
         k = _store(k32, k_dt)
-    return Problem(name, _store(q32, q_dt), q_dt, w, k, k_dt, k_scale,
+    q = f64_to_e4m3_codes(q32.astype(np.float64)) if q_dt == FP8 else _store(q32, q_dt)
+    return Problem(name, q, q_dt, w, k, k_dt, k_scale,
                    np.ascontiguousarray(q_seq, np.int32), np.ascontiguousarray(q_pos, np.int32),
-                   B, h, topk, k_prime)
+                   B, h, topk, k_prime, q_scale=q_scale)

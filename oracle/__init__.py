@@ -38,7 +38,7 @@ def _load():
     P = ctypes.c_void_p
     I = ctypes.c_int
     I64 = ctypes.c_int64
-    common = [P, I, P, P, P, I, P, P]            # q q_dt w k k_scale k_dt q_seq q_pos
+    common = [P, I, P, P, P, P, I, P, P]   # q q_dt q_scale w k k_scale k_dt q_seq q_pos
     lib.misa_ref_decode.argtypes = [P, P, I, I64, I, P]
     lib.misa_ref_pool_keys.argtypes = [P, P, I, I, I, I, I, P, P]
     lib.misa_ref_route_heads.argtypes = common + [I] * 7 + [P, P, P]
@@ -82,10 +82,11 @@ def _check(rc, what):
 
 
 def _args(p):
+    """(q, q_scale, w, k, k_scale, q_seq, q_pos) as contiguous arrays (scales may be None)."""
     q = np.ascontiguousarray(p.q)
     k = np.ascontiguousarray(p.k)
-    return (q, _c(p.w, np.float32), k, _c(p.k_scale, np.float32),
-            _c(p.q_seq, np.int32), _c(p.q_pos, np.int32))
+    return (q, _c(getattr(p, "q_scale", None), np.float32), _c(p.w, np.float32), k,
+            _c(p.k_scale, np.float32), _c(p.q_seq, np.int32), _c(p.q_pos, np.int32))
 
 
 def max_threads() -> int:
@@ -114,11 +115,11 @@ def pool_keys(p, mac=None):
 
 def route_heads(p, h=None, mac=None):
     h = p.h if h is None else h
-    q, w, k, ks, qs, qp = _args(p)
+    q, qsc, w, k, ks, sq, qp = _args(p)
     N, H_I, d = q.shape
     heads = np.empty((N, h), dtype=np.int32)
     r = np.empty((N, H_I), dtype=np.float64)
-    _check(lib().misa_ref_route_heads(_p(q), p.q_dt, _p(w), _p(k), _p(ks), p.k_dt, _p(qs), _p(qp),
+    _check(lib().misa_ref_route_heads(_p(q), p.q_dt, _p(qsc), _p(w), _p(k), _p(ks), p.k_dt, _p(sq), _p(qp),
                                       N, p.k.shape[0], p.k.shape[1], d, p.B, H_I, h,
                                       _p(heads), _p(r), _p(mac)), "route_heads")
     return heads, r
@@ -126,12 +127,12 @@ def route_heads(p, h=None, mac=None):
 
 def scores(p, heads=None, mac=None):
     """Full score rows [N, L] (-inf past each row's visible prefix); heads None = all heads."""
-    q, w, k, ks, qs, qp = _args(p)
+    q, qsc, w, k, ks, sq, qp = _args(p)
     N, H_I, d = q.shape
     hd = _c(heads, np.int32)
     h = H_I if hd is None else hd.shape[1]
     out = np.empty((N, p.k.shape[1]), dtype=np.float64)
-    _check(lib().misa_ref_scores(_p(q), p.q_dt, _p(w), _p(k), _p(ks), p.k_dt, _p(qs), _p(qp),
+    _check(lib().misa_ref_scores(_p(q), p.q_dt, _p(qsc), _p(w), _p(k), _p(ks), p.k_dt, _p(sq), _p(qp),
                                  _p(hd), N, p.k.shape[0], p.k.shape[1], d, H_I, h, _p(out),
                                  _p(mac)), "scores")
     return out
@@ -139,13 +140,13 @@ def scores(p, heads=None, mac=None):
 
 def score_topk(p, heads, topk=None, mac=None):
     topk = p.topk if topk is None else topk
-    q, w, k, ks, qs, qp = _args(p)
+    q, qsc, w, k, ks, sq, qp = _args(p)
     N, H_I, d = q.shape
     hd = _c(heads, np.int32)
     idx = np.empty((N, topk), dtype=np.int32)
     sc = np.empty((N, topk), dtype=np.float64)
     kth = np.empty(N, dtype=np.float64)
-    _check(lib().misa_ref_score_topk(_p(q), p.q_dt, _p(w), _p(k), _p(ks), p.k_dt, _p(qs), _p(qp),
+    _check(lib().misa_ref_score_topk(_p(q), p.q_dt, _p(qsc), _p(w), _p(k), _p(ks), p.k_dt, _p(sq), _p(qp),
                                      _p(hd), N, p.k.shape[0], p.k.shape[1], d, H_I, hd.shape[1],
                                      topk, _p(idx), _p(sc), _p(kth), _p(mac)), "score_topk")
     return idx, sc, kth
@@ -153,12 +154,12 @@ def score_topk(p, heads, topk=None, mac=None):
 
 def dsa_score_topk(p, topk=None, mac=None):
     topk = p.topk if topk is None else topk
-    q, w, k, ks, qs, qp = _args(p)
+    q, qsc, w, k, ks, sq, qp = _args(p)
     N, H_I, d = q.shape
     idx = np.empty((N, topk), dtype=np.int32)
     sc = np.empty((N, topk), dtype=np.float64)
     kth = np.empty(N, dtype=np.float64)
-    _check(lib().dsa_ref_score_topk(_p(q), p.q_dt, _p(w), _p(k), _p(ks), p.k_dt, _p(qs), _p(qp),
+    _check(lib().dsa_ref_score_topk(_p(q), p.q_dt, _p(qsc), _p(w), _p(k), _p(ks), p.k_dt, _p(sq), _p(qp),
                                     N, p.k.shape[0], p.k.shape[1], d, H_I, topk,
                                     _p(idx), _p(sc), _p(kth), _p(mac)), "dsa_score_topk")
     return idx, sc, kth
@@ -166,13 +167,13 @@ def dsa_score_topk(p, topk=None, mac=None):
 
 def rerank(p, cand, topk=None, mac=None):
     topk = p.topk if topk is None else topk
-    q, w, k, ks, qs, qp = _args(p)
+    q, qsc, w, k, ks, sq, qp = _args(p)
     N, H_I, d = q.shape
     cd = _c(cand, np.int32)
     idx = np.empty((N, topk), dtype=np.int32)
     sc = np.empty((N, topk), dtype=np.float64)
     kth = np.empty(N, dtype=np.float64)
-    _check(lib().misa_ref_rerank(_p(q), p.q_dt, _p(w), _p(k), _p(ks), p.k_dt, _p(qs), _p(qp),
+    _check(lib().misa_ref_rerank(_p(q), p.q_dt, _p(qsc), _p(w), _p(k), _p(ks), p.k_dt, _p(sq), _p(qp),
                                  _p(cd), N, p.k.shape[0], p.k.shape[1], d, H_I, cd.shape[1], topk,
                                  _p(idx), _p(sc), _p(kth), _p(mac)), "rerank")
     return idx, sc, kth

@@ -55,12 +55,20 @@ void key_row(const void* k, const float* k_scale, int k_dt, int L, int d, int s,
   for (int i = 0; i < d; ++i) out[i] = stored_value(k, k_dt, row * d + i) * sc;
 }
 
-// Decoded query heads of row n: [H_I][d].
-std::vector<double> query_heads(const void* q, int q_dt, int n, int H_I, int d) {
+// Decoded query heads of row n: [H_I][d] (e4m3: head j's codes times
+// q_scale[n, j]).
+std::vector<double> query_heads(const void* q, int q_dt, const float* q_scale, int n, int H_I,
+                                int d) {
   std::vector<double> out(static_cast<size_t>(H_I) * d);
   const int64_t base = static_cast<int64_t>(n) * H_I * d;
-  for (int64_t i = 0; i < static_cast<int64_t>(H_I) * d; ++i)
-    out[i] = stored_value(q, q_dt, base + i);
+  for (int j = 0; j < H_I; ++j) {
+    const double sc =
+        (q_dt == DT_E4M3) ? static_cast<double>(q_scale[static_cast<int64_t>(n) * H_I + j]) : 1.0;
+    for (int i = 0; i < d; ++i) {
+      const int64_t e = static_cast<int64_t>(j) * d + i;
+      out[e] = stored_value(q, q_dt, base + e) * sc;
+    }
+  }
   return out;
 }
 
@@ -72,12 +80,13 @@ double dot(const double* a, const double* b, int d) {
 
 double relu(double x) { return x > 0.0 ? x : 0.0; }
 
-int check_common(const void* q, int q_dt, const float* w, const void* k, const float* k_scale,
-                 int k_dt, const int32_t* q_seq, const int32_t* q_pos, int N, int S, int L,
-                 int d, int H_I) {
+int check_common(const void* q, int q_dt, const float* q_scale, const float* w, const void* k,
+                 const float* k_scale, int k_dt, const int32_t* q_seq, const int32_t* q_pos,
+                 int N, int S, int L, int d, int H_I) {
   if (!q || !w || !k || !q_seq || !q_pos) return 1;
   if (k_dt == DT_E4M3 && !k_scale) return 1;
-  if (q_dt != DT_F32 && q_dt != DT_BF16) return 3;
+  if (q_dt == DT_E4M3 && !q_scale) return 1;
+  if (q_dt != DT_F32 && q_dt != DT_BF16 && q_dt != DT_E4M3) return 3;
   if (k_dt != DT_F32 && k_dt != DT_BF16 && k_dt != DT_E4M3) return 3;
   if (N < 0 || S < 1 || L < 1 || d < 1 || H_I < 1) return 2;
   for (int n = 0; n < N; ++n) {
@@ -110,10 +119,10 @@ void select_topk(const std::vector<double>& sc, const std::vector<int32_t>& tok,
 }
 
 // Routed or dense scores of query n over its visible prefix.
-std::vector<double> query_scores(const void* q, int q_dt, const float* w, const void* k,
-                                 const float* k_scale, int k_dt, int n, int s, int Ln, int L,
-                                 int d, int H_I, const std::vector<int>& heads) {
-  const std::vector<double> qh = query_heads(q, q_dt, n, H_I, d);
+std::vector<double> query_scores(const void* q, int q_dt, const float* q_scale, const float* w,
+                                 const void* k, const float* k_scale, int k_dt, int n, int s,
+                                 int Ln, int L, int d, int H_I, const std::vector<int>& heads) {
+  const std::vector<double> qh = query_heads(q, q_dt, q_scale, n, H_I, d);
   std::vector<double> out(Ln);
 #pragma omp parallel
   {
@@ -184,11 +193,11 @@ int misa_ref_pool_keys(const void* k, const float* k_scale, int k_dt, int S, int
   return 0;
 }
 
-int misa_ref_route_heads(const void* q, int q_dt, const float* w, const void* k,
+int misa_ref_route_heads(const void* q, int q_dt, const float* q_scale, const float* w, const void* k,
                          const float* k_scale, int k_dt, const int32_t* q_seq,
                          const int32_t* q_pos, int N, int S, int L, int d, int B, int H_I,
                          int h, int32_t* heads, double* head_score, uint64_t* mac) {
-  int rc = check_common(q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, N, S, L, d, H_I);
+  int rc = check_common(q, q_dt, q_scale, w, k, k_scale, k_dt, q_seq, q_pos, N, S, L, d, H_I);
   if (rc) return rc;
   if (!heads) return 1;
   if (B < 1 || h < 1 || h > H_I) return 2;
@@ -197,7 +206,7 @@ int misa_ref_route_heads(const void* q, int q_dt, const float* w, const void* k,
   for (int n = 0; n < N; ++n) {
     const int s = q_seq[n], Ln = q_pos[n] + 1;
     const int Mn = (Ln + B - 1) / B;
-    const std::vector<double> qh = query_heads(q, q_dt, n, H_I, d);
+    const std::vector<double> qh = query_heads(q, q_dt, q_scale, n, H_I, d);
     std::vector<double> affinity(H_I, 0.0), kr(d), mean(d);
     for (int b = 0; b < Mn; ++b) {
       const int t0 = b * B, t1 = std::min(t0 + B, Ln);       // visible part of block b
@@ -233,11 +242,11 @@ int misa_ref_route_heads(const void* q, int q_dt, const float* w, const void* k,
   return 0;
 }
 
-int misa_ref_scores(const void* q, int q_dt, const float* w, const void* k,
+int misa_ref_scores(const void* q, int q_dt, const float* q_scale, const float* w, const void* k,
                     const float* k_scale, int k_dt, const int32_t* q_seq, const int32_t* q_pos,
                     const int32_t* heads, int N, int S, int L, int d, int H_I, int h,
                     double* scores, uint64_t* mac) {
-  int rc = check_common(q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, N, S, L, d, H_I);
+  int rc = check_common(q, q_dt, q_scale, w, k, k_scale, k_dt, q_seq, q_pos, N, S, L, d, H_I);
   if (rc) return rc;
   if (!scores) return 1;
   if (heads && (h < 1 || h > H_I)) return 2;
@@ -248,7 +257,7 @@ int misa_ref_scores(const void* q, int q_dt, const float* w, const void* k,
       if (j < 0 || j >= H_I) return 2;
     const int Ln = q_pos[n] + 1;
     const std::vector<double> sc =
-        query_scores(q, q_dt, w, k, k_scale, k_dt, n, q_seq[n], Ln, L, d, H_I, hs);
+        query_scores(q, q_dt, q_scale, w, k, k_scale, k_dt, n, q_seq[n], Ln, L, d, H_I, hs);
     double* row = scores + static_cast<int64_t>(n) * L;
     for (int t = 0; t < L; ++t) row[t] = t < Ln ? sc[t] : NEG_INF;
     score_macs += static_cast<uint64_t>(hs.size()) * Ln * d;
@@ -257,12 +266,12 @@ int misa_ref_scores(const void* q, int q_dt, const float* w, const void* k,
   return 0;
 }
 
-int misa_ref_score_topk(const void* q, int q_dt, const float* w, const void* k,
+int misa_ref_score_topk(const void* q, int q_dt, const float* q_scale, const float* w, const void* k,
                         const float* k_scale, int k_dt, const int32_t* q_seq,
                         const int32_t* q_pos, const int32_t* heads, int N, int S, int L, int d,
                         int H_I, int h, int topk, int32_t* idx, double* score, double* kth,
                         uint64_t* mac) {
-  int rc = check_common(q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, N, S, L, d, H_I);
+  int rc = check_common(q, q_dt, q_scale, w, k, k_scale, k_dt, q_seq, q_pos, N, S, L, d, H_I);
   if (rc) return rc;
   if (!idx) return 1;
   if (topk < 1 || (heads && (h < 1 || h > H_I))) return 2;
@@ -273,7 +282,7 @@ int misa_ref_score_topk(const void* q, int q_dt, const float* w, const void* k,
       if (j < 0 || j >= H_I) return 2;
     const int Ln = q_pos[n] + 1;
     const std::vector<double> sc =
-        query_scores(q, q_dt, w, k, k_scale, k_dt, n, q_seq[n], Ln, L, d, H_I, hs);
+        query_scores(q, q_dt, q_scale, w, k, k_scale, k_dt, n, q_seq[n], Ln, L, d, H_I, hs);
     std::vector<int32_t> tok(Ln);
     std::iota(tok.begin(), tok.end(), 0);
     select_topk(sc, tok, topk, idx + static_cast<int64_t>(n) * topk,
@@ -284,19 +293,19 @@ int misa_ref_score_topk(const void* q, int q_dt, const float* w, const void* k,
   return 0;
 }
 
-int dsa_ref_score_topk(const void* q, int q_dt, const float* w, const void* k,
+int dsa_ref_score_topk(const void* q, int q_dt, const float* q_scale, const float* w, const void* k,
                        const float* k_scale, int k_dt, const int32_t* q_seq,
                        const int32_t* q_pos, int N, int S, int L, int d, int H_I, int topk,
                        int32_t* idx, double* score, double* kth, uint64_t* mac) {
-  return misa_ref_score_topk(q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, nullptr, N, S, L, d,
+  return misa_ref_score_topk(q, q_dt, q_scale, w, k, k_scale, k_dt, q_seq, q_pos, nullptr, N, S, L, d,
                              H_I, H_I, topk, idx, score, kth, mac);
 }
 
-int misa_ref_rerank(const void* q, int q_dt, const float* w, const void* k,
+int misa_ref_rerank(const void* q, int q_dt, const float* q_scale, const float* w, const void* k,
                     const float* k_scale, int k_dt, const int32_t* q_seq, const int32_t* q_pos,
                     const int32_t* cand, int N, int S, int L, int d, int H_I, int k_prime,
                     int topk, int32_t* idx, double* score, double* kth, uint64_t* mac) {
-  int rc = check_common(q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, N, S, L, d, H_I);
+  int rc = check_common(q, q_dt, q_scale, w, k, k_scale, k_dt, q_seq, q_pos, N, S, L, d, H_I);
   if (rc) return rc;
   if (!cand || !idx) return 1;
   if (topk < 1 || k_prime < topk) return 2;
@@ -313,7 +322,7 @@ int misa_ref_rerank(const void* q, int q_dt, const float* w, const void* k,
     std::vector<int32_t> sorted_tok(tok);
     std::sort(sorted_tok.begin(), sorted_tok.end());
     if (std::adjacent_find(sorted_tok.begin(), sorted_tok.end()) != sorted_tok.end()) return 2;
-    const std::vector<double> qh = query_heads(q, q_dt, n, H_I, d);
+    const std::vector<double> qh = query_heads(q, q_dt, q_scale, n, H_I, d);
     std::vector<double> sc(tok.size());
 #pragma omp parallel
     {

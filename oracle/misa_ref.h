@@ -35,7 +35,9 @@
  * subnormals, 0x7F/0xFF NaN) and are multiplied by their token's fp32 scale.
  *
  * All pointers are host pointers to C-contiguous arrays:
- *   q [N,H_I,d] (dt 0 = f32, 1 = bf16 bits), w [N,H_I] f32,
+ *   q [N,H_I,d] (dt 0 = f32, 1 = bf16 bits, 2 = e4m3 codes), q_scale [N,H_I]
+ *   f32 (e4m3 only, else NULL: head j of row n is q_scale[n,j] times its
+ *   codes), w [N,H_I] f32,
  *   k [S,L,d] (dt 0 = f32, 1 = bf16 bits, 2 = e4m3 codes), k_scale [S,L] f32
  *   (e4m3 only, else NULL), q_seq [N], q_pos [N] int32.
  * Every function returns 0 on success, 1 for a NULL pointer, 2 for a shape or
@@ -61,14 +63,14 @@ int misa_ref_pool_keys(const void* k, const float* k_scale, int k_dt, int S, int
                        int B, double* kbar, uint64_t* mac);
 
 /* heads [N,h] ascending; head_score [N,H_I] = r_j (may be NULL). */
-int misa_ref_route_heads(const void* q, int q_dt, const float* w, const void* k,
+int misa_ref_route_heads(const void* q, int q_dt, const float* q_scale, const float* w, const void* k,
                          const float* k_scale, int k_dt, const int32_t* q_seq,
                          const int32_t* q_pos, int N, int S, int L, int d, int B, int H_I,
                          int h, int32_t* heads, double* head_score, uint64_t* mac);
 
 /* scores [N,L]: I(s) for s < L_n with the given heads [N,h] (heads == NULL means
  * all H_I heads, h ignored); -inf for s >= L_n. */
-int misa_ref_scores(const void* q, int q_dt, const float* w, const void* k,
+int misa_ref_scores(const void* q, int q_dt, const float* q_scale, const float* w, const void* k,
                     const float* k_scale, int k_dt, const int32_t* q_seq, const int32_t* q_pos,
                     const int32_t* heads, int N, int S, int L, int d, int H_I, int h,
                     double* scores, uint64_t* mac);
@@ -76,14 +78,14 @@ int misa_ref_scores(const void* q, int q_dt, const float* w, const void* k,
 /* Top-k of the routed score: idx [N,topk] in (score desc, index asc) order,
  * score [N,topk]; slots past min(topk, L_n) hold -1 / -inf.  kth [N] is the
  * score of the last selected token (may be NULL). */
-int misa_ref_score_topk(const void* q, int q_dt, const float* w, const void* k,
+int misa_ref_score_topk(const void* q, int q_dt, const float* q_scale, const float* w, const void* k,
                         const float* k_scale, int k_dt, const int32_t* q_seq,
                         const int32_t* q_pos, const int32_t* heads, int N, int S, int L, int d,
                         int H_I, int h, int topk, int32_t* idx, double* score, double* kth,
                         uint64_t* mac);
 
 /* Dense DSA indexer: misa_ref_score_topk with every head. */
-int dsa_ref_score_topk(const void* q, int q_dt, const float* w, const void* k,
+int dsa_ref_score_topk(const void* q, int q_dt, const float* q_scale, const float* w, const void* k,
                        const float* k_scale, int k_dt, const int32_t* q_seq,
                        const int32_t* q_pos, int N, int S, int L, int d, int H_I, int topk,
                        int32_t* idx, double* score, double* kth, uint64_t* mac);
@@ -91,7 +93,7 @@ int dsa_ref_score_topk(const void* q, int q_dt, const float* w, const void* k,
 /* MISA-dagger fine stage: cand [N,k_prime] token indices (-1 = empty slot;
  * valid entries distinct and < L_n) re-scored with all H_I heads; top-k as
  * above. */
-int misa_ref_rerank(const void* q, int q_dt, const float* w, const void* k,
+int misa_ref_rerank(const void* q, int q_dt, const float* q_scale, const float* w, const void* k,
                     const float* k_scale, int k_dt, const int32_t* q_seq, const int32_t* q_pos,
                     const int32_t* cand, int N, int S, int L, int d, int H_I, int k_prime,
                     int topk, int32_t* idx, double* score, double* kth, uint64_t* mac);

@@ -21,7 +21,13 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
 
 
 def _problem_from_golden(ex, topk, h):
-    q = np.array(ex["q"], dtype=np.float32)
+    if ex.get("q_dt") == "e4m3":
+        q = np.array(ex["q_codes"], dtype=np.uint8)
+        qsc = np.array(ex["q_scale"], dtype=np.float32)
+        qdt = synth.FP8
+    else:
+        q = np.array(ex["q"], dtype=np.float32)
+        qsc, qdt = None, synth.F32
     w = np.array(ex["w"], dtype=np.float32)
     if ex["k_dt"] == "e4m3":
         k = np.array(ex["k_codes"], dtype=np.uint8)
@@ -31,8 +37,8 @@ def _problem_from_golden(ex, topk, h):
         k = np.array(ex["k"], dtype=np.float32)
         ks, kdt = None, synth.F32
     N = q.shape[0]
-    return synth.Problem(ex["name"], q, synth.F32, w, k, kdt, ks, np.zeros(N, np.int32),
-                         np.array(ex["q_pos"], np.int32), ex["B"], h, topk)
+    return synth.Problem(ex["name"], q, qdt, w, k, kdt, ks, np.zeros(N, np.int32),
+                         np.array(ex["q_pos"], np.int32), ex["B"], h, topk, q_scale=qsc)
 
 
 def _golden():
@@ -49,8 +55,9 @@ def _nan_to_neg_inf(rows):
 def test_hand_worked_examples(ex):
     """Hand-derived values: catches wrong block boundaries, a partial block
     averaged over B or over future keys, a missing |w| in the router, a
-    missing ReLU, a wrong tie-break, wrong e4m3 decoding or scaling, and a
-    wrong MAC count."""
+    missing ReLU, a wrong tie-break, wrong e4m3 decoding or scaling (of keys,
+    and of query heads: a dropped or misplaced head scale), and a wrong MAC
+    count."""
     e = ex["expect"]
     p = _problem_from_golden(ex, e["topk"], e["h"])
     mac = np.zeros(4, dtype=np.uint64)
@@ -122,19 +129,32 @@ def test_pool_block_size_one_is_identity():
 
 
 # ---------------------------------------------------------------- router
+def _torch_decode(x, dt, scale):
+    """Stored values via torch's own casts (bf16 / float8_e4m3fn -> float64)."""
+    if dt == synth.F32:
+        return x.astype(np.float64)
+    if dt == synth.BF16:
+        return torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    v = torch.from_numpy(x.copy()).view(torch.float8_e4m3fn).double().numpy()
+    return v * scale.astype(np.float64)[..., None]
+
+
 def _numpy_dense_dots(p):
     """q_j . k_s for every row/head/token via float64 BLAS matmul."""
-    q = oracle.decode(p.q, p.q_dt) if p.q_dt != synth.F32 else p.q.astype(np.float64)
-    k = oracle.decode(p.k, p.k_dt, p.k_scale) if p.k_dt != synth.F32 else p.k.astype(np.float64)
+    q = _torch_decode(p.q, p.q_dt, p.q_scale)
+    k = _torch_decode(p.k, p.k_dt, p.k_scale)
     return np.stack([q[n] @ k[p.q_seq[n]].T for n in range(p.N)])   # [N, H_I, L]
 
 
-@pytest.mark.parametrize("k_dt", [synth.F32, synth.BF16, synth.FP8])
-def test_router_block_size_one_closed_form(k_dt):
+DT_PAIRS = [(synth.F32, synth.F32), (synth.BF16, synth.BF16), (synth.BF16, synth.FP8),
+            (synth.FP8, synth.FP8)]
+
+
+@pytest.mark.parametrize("q_dt,k_dt", DT_PAIRS)
+def test_router_block_size_one_closed_form(q_dt, k_dt):
     """B = 1: every block is one key, so r_j = |w_j| * sum_{s<L_n} ReLU(q_j.k_s),
     from a BLAS matmul; heads = first h by numpy lexsort.  Catches a missing
     |w|, ReLU applied after aggregation, and causal leakage."""
-    q_dt = synth.F32 if k_dt == synth.F32 else synth.BF16
     p = synth.small("r1", 11, N=3, S=2, L=300, d=64, H_I=12, h=5, B=1, q_dt=q_dt, k_dt=k_dt,
                     q_pos=np.array([299, 150, 17], np.int32))
     heads, r = oracle.route_heads(p)
@@ -185,12 +205,12 @@ def test_router_head_permutation():
 
 
 # ---------------------------------------------------------------- scoring
-@pytest.mark.parametrize("k_dt", [synth.F32, synth.BF16, synth.FP8])
-def test_scores_match_blas(k_dt):
+@pytest.mark.parametrize("q_dt,k_dt", DT_PAIRS)
+def test_scores_match_blas(q_dt, k_dt):
     """Routed and dense scores == w^T ReLU(Q K^T) from a float64 BLAS matmul
-    (P5); -inf past the causal boundary.  Catches a dropped ReLU, a wrong sign
-    of w, a transposed operand and a wrong head subset."""
-    q_dt = synth.F32 if k_dt == synth.F32 else synth.BF16
+    over torch-decoded inputs (P5); -inf past the causal boundary.  Catches a
+    dropped ReLU, a wrong sign of w, a transposed operand, a wrong head subset
+    and a query or key scale applied to the wrong vector."""
     p = synth.small("sc", 12, N=3, S=2, L=400, d=64, H_I=10, h=3, q_dt=q_dt, k_dt=k_dt,
                     q_pos=np.array([399, 200, 0], np.int32))
     dots = _numpy_dense_dots(p)
@@ -261,6 +281,52 @@ def test_integer_inputs_are_exact():
         order = np.lexsort((np.arange(p.L), -ref))[:p.topk]
         assert np.array_equal(idx[n], order)
         assert len(np.unique(ref)) < p.L                      # ties really occur
+
+
+def test_integer_inputs_are_exact_with_e4m3_queries():
+    """fp8 queries with power-of-two head scales (1/4 .. 4) and fp8 keys: the
+    scores are exact multiples of 1/4; times 4 they are the int64 matmul
+    result, ties included."""
+    p = synth.integer_problem("int8", 6, N=3, L=300, d=64, H_I=8, h=3, B=32, topk=40,
+                              q_dt=synth.FP8, k_dt=synth.FP8)
+    assert len(np.unique(p.q_scale)) > 1
+    heads, _ = oracle.route_heads(p)
+    q = torch.from_numpy(p.q.copy()).view(torch.float8_e4m3fn).double().numpy().astype(np.int64)
+    k = torch.from_numpy(p.k.copy()).view(torch.float8_e4m3fn).double().numpy().astype(np.int64)
+    qs4 = (p.q_scale.astype(np.float64) * 4).astype(np.int64)          # 1 .. 16
+    w = p.w.astype(np.int64)
+    sc = oracle.scores(p, heads)
+    idx, _, _ = oracle.score_topk(p, heads)
+    for n in range(p.N):
+        dots = q[n, heads[n]] @ k[p.q_seq[n]].T
+        ref4 = ((w[n, heads[n]] * qs4[n, heads[n]])[:, None] * np.maximum(dots, 0)).sum(0)
+        assert np.array_equal(sc[n] * 4, ref4.astype(np.float64))
+        order = np.lexsort((np.arange(p.L), -ref4))[:p.topk]
+        assert np.array_equal(idx[n], order)
+
+
+def test_e4m3_queries_equal_their_f32_values():
+    """Head scales that are powers of two make scale * code exact in fp32, so
+    the fp8-query problem and the fp32-query problem holding those products
+    must give identical heads, scores and top-k.  Catches a scale indexed
+    [j, n] instead of [n, j], applied to the wrong row, or divided."""
+    p = synth.small("e8", 41, N=3, S=2, L=500, d=64, H_I=12, h=4, B=32, topk=50,
+                    q_dt=synth.BF16, k_dt=synth.FP8, q_pos=np.array([499, 260, 33], np.int32))
+    rng = np.random.default_rng(41)
+    codes = synth.f64_to_e4m3_codes(rng.standard_normal((p.N, p.H_I, p.d)) * 8)
+    qsc = np.ldexp(np.float32(1.0), rng.integers(-6, 4, size=(p.N, p.H_I))).astype(np.float32)
+    p8 = synth.Problem("e8q", codes, synth.FP8, p.w, p.k, p.k_dt, p.k_scale, p.q_seq, p.q_pos,
+                       p.B, p.h, p.topk, q_scale=qsc)
+    qf = (torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().numpy()
+          * qsc[..., None]).astype(np.float32)
+    pf = synth.Problem("e8f", qf, synth.F32, p.w, p.k, p.k_dt, p.k_scale, p.q_seq, p.q_pos,
+                       p.B, p.h, p.topk)
+    h8, r8 = oracle.route_heads(p8)
+    hf, rf = oracle.route_heads(pf)
+    assert np.array_equal(h8, hf) and np.array_equal(r8, rf)
+    assert np.array_equal(oracle.scores(p8, None), oracle.scores(pf, None))
+    for a, b in zip(oracle.score_topk(p8, h8), oracle.score_topk(pf, hf)):
+        assert np.array_equal(a, b)
 
 
 # ---------------------------------------------------------------- invariants

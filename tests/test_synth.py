@@ -32,7 +32,7 @@ def test_e4m3_quantization_scale():
     rng = np.random.default_rng(2)
     k = rng.standard_normal((3, 50, 128)).astype(np.float32)
     k[1, 7] = 0.0
-    codes, scale = synth.quantize_keys_e4m3(k)
+    codes, scale = synth.quantize_e4m3(k)
     assert codes.dtype == np.uint8 and scale.dtype == np.float32
     assert scale[1, 7] == 1.0 and np.all(codes[1, 7] == 0)
     dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy() * scale[..., None]
@@ -67,3 +67,20 @@ def test_prefill_positions():
                    q_seq=np.zeros(256, np.int32), N=256)
     assert p.N == 256 and p.q_pos[0] == 8192 - 256 and p.q_pos[-1] == 8191
     assert p.tokens_indexed() == int(np.arange(8192 - 255, 8193).sum())
+
+
+def test_fp8_prefill_workload_quantizes_the_bf16_draws():
+    """The fp8 prefill chunk stores the same fp32 draws as the bf16 one: q per
+    head and k per token as e4m3 codes with an absmax/448 scale."""
+    over = dict(L=4096, N=64, q_seq=np.zeros(64, np.int32),
+                q_pos=np.arange(4096 - 64, 4096, dtype=np.int32))
+    p8 = synth.make("c3f8", **over)
+    pb = synth.make("c3", **over)
+    assert p8.q.dtype == np.uint8 and p8.k.dtype == np.uint8
+    assert p8.q_scale.shape == (64, 64) and p8.k_scale.shape == (1, 4096)
+    q8 = torch.from_numpy(p8.q.copy()).view(torch.float8_e4m3fn).float().numpy()
+    assert np.all(np.abs(q8).max(-1) == 448.0)
+    qd = q8 * p8.q_scale[..., None]
+    qb = synth.bf16_bits_to_f32(pb.q)
+    assert np.max(np.abs(qd - qb)) <= np.abs(qb).max() / 8
+    assert np.array_equal(synth.e4m3_codes_to_f32(p8.q, p8.q_scale), qd)

@@ -43,9 +43,10 @@ def parse():
     ap.add_argument("--h", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--workload", default="c4", choices=["c4", "c3", "c3x"],
+    ap.add_argument("--workload", default="c4", choices=["c4", "c3", "c3x", "c3f8"],
                     help="c4: the long-context decode indexer (the headline line); "
-                         "c3 / c3x: the prefill chunk at L=64K / 128K")
+                         "c3 / c3x: the prefill chunk at L=64K / 128K; c3f8: the L=64K "
+                         "chunk with e4m3 queries and keys")
     # profiling helpers (no benchmark line)
     ap.add_argument("--copy-probe", action="store_true",
                     help="run plain 256 MiB device copies (scale reference for HBM counters)")
@@ -175,11 +176,12 @@ class Replicas:
         self.sc = torch.empty((N, p.topk), dtype=torch.float32, device=dev)
         self.k_prime = k_prime
         self.cand = torch.empty((N, max(k_prime, 1)), dtype=torch.int32, device=dev)
-        self.ws_route = binding.workspace(binding.MISA_OP_ROUTE, N, L, d, H_I, B, device=dev)
+        self.ws_route = binding.workspace(binding.MISA_OP_ROUTE, N, L, d, H_I, B, q_dt=p.q_dt,
+                                          device=dev)
         self.ws_score = binding.workspace(binding.MISA_OP_SCORE_TOPK, N, L, d, H_I,
-                                          topk=max(p.topk, k_prime), device=dev)
+                                          topk=max(p.topk, k_prime), q_dt=p.q_dt, device=dev)
         self.ws_rerank = binding.workspace(binding.MISA_OP_RERANK, N, L, d, H_I, topk=p.topk,
-                                           k_prime=max(k_prime, p.topk), device=dev)
+                                           k_prime=max(k_prime, p.topk), q_dt=p.q_dt, device=dev)
         self.b = binding
 
     def pool(self, i):
@@ -188,25 +190,27 @@ class Replicas:
     def route(self, i):
         d = self.dp
         self.b.misa_route_heads(d.q, d.w, self.kbar[i], self.k[i], d.q_seq, d.q_pos, self.p.B,
-                                self.h, k_scale=self.ks[i], heads=self.heads, head_score=self.r,
-                                ws=self.ws_route)
+                                self.h, k_scale=self.ks[i], q_scale=d.q_scale, heads=self.heads,
+                                head_score=self.r, ws=self.ws_route)
 
     def score(self, i, topk=None, out=None):
         d = self.dp
         self.b.misa_score_topk(d.q, d.w, self.k[i], d.q_seq, d.q_pos, self.heads,
                                self.p.topk if topk is None else topk, k_scale=self.ks[i],
-                               idx=self.idx if out is None else out, score=None,
+                               q_scale=d.q_scale, idx=self.idx if out is None else out, score=None,
                                ws=self.ws_score, want_score=False)
 
     def dense(self, i):
         d = self.dp
         self.b.dsa_score_topk(d.q, d.w, self.k[i], d.q_seq, d.q_pos, self.p.topk,
-                              k_scale=self.ks[i], idx=self.idx, score=self.sc, ws=self.ws_score)
+                              k_scale=self.ks[i], q_scale=d.q_scale, idx=self.idx, score=self.sc,
+                              ws=self.ws_score)
 
     def rerank(self, i):
         d = self.dp
         self.b.misa_rerank(d.q, d.w, self.k[i], d.q_seq, d.q_pos, self.cand, self.p.topk,
-                           k_scale=self.ks[i], idx=self.idx, score=self.sc, ws=self.ws_rerank)
+                           k_scale=self.ks[i], q_scale=d.q_scale, idx=self.idx, score=self.sc,
+                           ws=self.ws_rerank)
 
     # step variants -------------------------------------------------------
     def step_misa(self, i):
@@ -295,18 +299,33 @@ def measured_read_gbs(torch):
     return round(gbs, 1)
 
 
-def measured_mfma_tflops(torch):
-    """In-run bf16 matrix-core reference: an 8192^3 torch.matmul (hipBLASLt)."""
+def measured_mfma_tflops(torch, fp8=False):
+    """In-run matrix-core reference: an 8192^3 bf16 torch.matmul, or for fp8
+    an e4m3 x e4m3 torch._scaled_mm (both hipBLASLt); None if unavailable."""
     n = 8192
     x = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
     y = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
-    for _ in range(3):
-        torch.matmul(x, y)
-    torch.cuda.synchronize()
+    if fp8:
+        x = x.to(torch.float8_e4m3fn)
+        y = y.to(torch.float8_e4m3fn).t().contiguous().t()      # column-major right operand
+        one = torch.ones((), dtype=torch.float32, device="cuda")
+
+        def mm():
+            return torch._scaled_mm(x, y, scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+    else:
+        def mm():
+            return torch.matmul(x, y)
+    try:
+        for _ in range(3):
+            mm()
+        torch.cuda.synchronize()
+    except RuntimeError as e:
+        log(f"[bench] matrix-core reference unavailable: {e}")
+        return None
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(10):
-        torch.matmul(x, y)
+        mm()
     b.record()
     torch.cuda.synchronize()
     tf = 10 * 2.0 * n ** 3 / (a.elapsed_time(b) * 1e-3) / 1e12
@@ -340,25 +359,28 @@ def prefill_main(args):
     p = synth.make(args.workload, h=args.h)
     dp = DeviceProblem(p)
     N, L, d, H_I, B = p.N, p.L, p.d, p.H_I, p.B
+    fp8 = p.q_dt == synth.FP8
     M = -(-L // B)
     dev = dp.q.device
     kbar = torch.empty((1, M, d), dtype=torch.float32, device=dev)
     heads = torch.empty((N, args.h), dtype=torch.int32, device=dev)
     r = torch.empty((N, H_I), dtype=torch.float32, device=dev)
     idx = torch.empty((N, p.topk), dtype=torch.int32, device=dev)
-    ws_r = binding.workspace(binding.MISA_OP_ROUTE, N, L, d, H_I, B, device=dev)
-    ws_s = binding.workspace(binding.MISA_OP_SCORE_TOPK, N, L, d, H_I, topk=p.topk, device=dev)
+    ws_r = binding.workspace(binding.MISA_OP_ROUTE, N, L, d, H_I, B, q_dt=p.q_dt, device=dev)
+    ws_s = binding.workspace(binding.MISA_OP_SCORE_TOPK, N, L, d, H_I, topk=p.topk, q_dt=p.q_dt,
+                             device=dev)
+    ks, qs = dp.k_scale, dp.q_scale
 
     def step(_):
-        binding.misa_pool_keys(dp.k, B, kbar=kbar)
+        binding.misa_pool_keys(dp.k, B, ks, kbar=kbar)
         binding.misa_route_heads(dp.q, dp.w, kbar, dp.k, dp.q_seq, dp.q_pos, B, args.h,
-                                 heads=heads, head_score=r, ws=ws_r)
-        binding.misa_score_topk(dp.q, dp.w, dp.k, dp.q_seq, dp.q_pos, heads, p.topk, idx=idx,
-                                ws=ws_s, want_score=False)
+                                 k_scale=ks, q_scale=qs, heads=heads, head_score=r, ws=ws_r)
+        binding.misa_score_topk(dp.q, dp.w, dp.k, dp.q_seq, dp.q_pos, heads, p.topk, k_scale=ks,
+                                q_scale=qs, idx=idx, ws=ws_s, want_score=False)
 
     def dense(_):
-        binding.dsa_score_topk(dp.q, dp.w, dp.k, dp.q_seq, dp.q_pos, p.topk, idx=idx, ws=ws_s,
-                               want_score=False)
+        binding.dsa_score_topk(dp.q, dp.w, dp.k, dp.q_seq, dp.q_pos, p.topk, k_scale=ks,
+                               q_scale=qs, idx=idx, ws=ws_s, want_score=False)
 
     ms = timed(torch, step, args.steps, args.warmup)
     pct = step_percentiles(torch, step, reps=max(20, args.steps), warmup=2)
@@ -371,17 +393,20 @@ def prefill_main(args):
     tflops = flops / (sc_ms * 1e-3) / 1e12 if sc_ms else None
     dflops = 2.0 * H_I * d * pairs
     dsc = ktd.get("score_prefill_kernel")
+    peak = 5000.0 if fp8 else 2500.0              # dense MFMA: e4m3 5.0, bf16 2.5 PFLOP/s
     line = {
         "metric": "prefix tokens indexed/sec (prefill chunk)", "value": pairs / (ms * 1e-3),
         "unit": "(query, prefix token) pairs/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": "e4m3" if fp8 else "bf16", "data": "synthetic",
         "config": {"workload": f"prefill chunk: {N} rows at positions {int(p.q_pos[0])}.."
                                f"{int(p.q_pos[-1])} over L={L}, H_I={H_I}, d={d}, h={args.h}, "
-                               f"B={B}, top-k={p.topk}"},
+                               f"B={B}, top-k={p.topk}" +
+                               (", e4m3 q (per-head scale) and k (per-token scale)" if fp8
+                                else "")},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1) if tflops else None,
-                     "peak": 2500.0, "unit": "TFLOP/s",
-                     "frac": round(tflops / 2500.0, 4) if tflops else None,
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4) if tflops else None,
                      "traffic": measured_traffic("score_prefill_kernel", args.workload),
                      "kernel": "score_prefill_kernel", "kernel_ms": sc_ms,
                      "algorithmic_flop_per_launch": flops},
@@ -392,9 +417,9 @@ def prefill_main(args):
                   "dense_score_tflops": round(dflops / (dsc * 1e-3) / 1e12, 1) if dsc else None,
                   "routed_score_vs_dense_score": round(dsc / sc_ms, 3) if dsc and sc_ms else None},
     }
-    mtf = measured_mfma_tflops(torch)
+    mtf = measured_mfma_tflops(torch, fp8)
     line["roofline"]["measured_peak"] = mtf
-    line["roofline"]["frac_vs_measured_peak"] = round(tflops / mtf, 4) if tflops else None
+    line["roofline"]["frac_vs_measured_peak"] = round(tflops / mtf, 4) if tflops and mtf else None
     print(json.dumps(line), flush=True)
 
 

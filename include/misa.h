@@ -22,7 +22,10 @@
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *    asynchronously; outputs are valid once the stream has synchronised.
  *  - Layouts:
- *      q       [N, H_I, d]  dtype q_dt (MISA_F32 or MISA_BF16)
+ *      q       [N, H_I, d]  dtype q_dt (MISA_F32, MISA_BF16 or MISA_FP8_E4M3)
+ *      q_scale [N, H_I]     float32 per-head scale, required iff q_dt is fp8
+ *                           (head j of row n = q_scale[n,j] * its e4m3
+ *                           values; scale > 0), else ignored (may be NULL)
  *      w       [N, H_I]     float32 head weights
  *      k       [S, L, d]    dtype k_dt (MISA_F32, MISA_BF16 or MISA_FP8_E4M3)
  *      k_scale [S, L]       float32 per-token scale, required iff k_dt is fp8
@@ -30,8 +33,9 @@
  *      q_seq   [N]  int32   key sequence of query row n, 0 <= q_seq[n] < S
  *      q_pos   [N]  int32   position of query row n, 0 <= q_pos[n] < L;
  *                           row n sees keys 0..q_pos[n] (L_n = q_pos[n] + 1)
- *    Supported (q_dt, k_dt): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3);
- *    d in {64, 128}; 1 <= h <= H_I <= 64; 1 <= B <= 1024;
+ *    Supported (q_dt, k_dt): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3),
+ *    (FP8_E4M3, FP8_E4M3) (e4m3 as in the OCP 8-bit floating point format:
+ *    bias 7, max 448, no infinities); d in {64, 128}; 1 <= h <= H_I <= 64; 1 <= B <= 1024;
  *    1 <= topk <= 65536; 1 <= N <= 65535; 1 <= S <= 65535; 1 <= L <= 2^27.
  *  - Index-score: I(s) = sum over heads j of w[n,j] * ReLU(q[n,j,:] . key_s),
  *    accumulated in fp32 from exact bf16 (or fp8-dequantised) products.
@@ -95,8 +99,8 @@ int32_t misa_pool_keys(const void* k, const float* k_scale, int32_t k_dt, int32_
  * sorted ascending; head_score [N, H_I] receives r (may be NULL).
  * Workspace: misa_workspace_bytes(MISA_OP_ROUTE, ...).
  */
-int32_t misa_route_heads(const void* q, int32_t q_dt, const float* w, const float* kbar,
-                         const void* k, const float* k_scale, int32_t k_dt,
+int32_t misa_route_heads(const void* q, int32_t q_dt, const float* q_scale, const float* w,
+                         const float* kbar, const void* k, const float* k_scale, int32_t k_dt,
                          const int32_t* q_seq, const int32_t* q_pos, int32_t N, int32_t S,
                          int32_t L, int32_t d, int32_t B, int32_t H_I, int32_t h,
                          int32_t* heads, float* head_score, void* ws, size_t ws_bytes,
@@ -112,8 +116,8 @@ int32_t misa_route_heads(const void* q, int32_t q_dt, const float* w, const floa
  * Outputs idx/score as described in the conventions (score may be NULL).
  * Workspace: misa_workspace_bytes(MISA_OP_SCORE_TOPK, ...).
  */
-int32_t misa_score_topk(const void* q, int32_t q_dt, const float* w, const void* k,
-                        const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+int32_t misa_score_topk(const void* q, int32_t q_dt, const float* q_scale, const float* w,
+                        const void* k, const float* k_scale, int32_t k_dt, const int32_t* q_seq,
                         const int32_t* q_pos, const int32_t* heads, int32_t N, int32_t S,
                         int32_t L, int32_t d, int32_t H_I, int32_t h, int32_t topk,
                         int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream);
@@ -123,8 +127,8 @@ int32_t misa_score_topk(const void* q, int32_t q_dt, const float* w, const void*
  * scores every prefix token, MISA abstract and "Problem statement"):
  * misa_score_topk with all H_I heads.
  */
-int32_t dsa_score_topk(const void* q, int32_t q_dt, const float* w, const void* k,
-                       const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+int32_t dsa_score_topk(const void* q, int32_t q_dt, const float* q_scale, const float* w,
+                       const void* k, const float* k_scale, int32_t k_dt, const int32_t* q_seq,
                        const int32_t* q_pos, int32_t N, int32_t S, int32_t L, int32_t d,
                        int32_t H_I, int32_t topk, int32_t* idx, float* score, void* ws,
                        size_t ws_bytes, void* stream);
@@ -141,23 +145,25 @@ int32_t dsa_score_topk(const void* q, int32_t q_dt, const float* w, const void* 
  * candidates, ranked by the all-head score.  Requires topk <= k_prime.
  * Workspace: misa_workspace_bytes(MISA_OP_RERANK, ...).
  */
-int32_t misa_rerank(const void* q, int32_t q_dt, const float* w, const void* k,
-                    const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+int32_t misa_rerank(const void* q, int32_t q_dt, const float* q_scale, const float* w,
+                    const void* k, const float* k_scale, int32_t k_dt, const int32_t* q_seq,
                     const int32_t* q_pos, const int32_t* cand, int32_t N, int32_t S, int32_t L,
                     int32_t d, int32_t H_I, int32_t k_prime, int32_t topk, int32_t* idx,
                     float* score, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Workspace bytes for `op` at these sizes (0 for invalid sizes).  Arguments
- * an op does not use are ignored (k_prime only matters for MISA_OP_RERANK, B
- * only for MISA_OP_ROUTE).  For MISA_OP_SCORE_TOPK with many rows over one
- * long sequence (N >= 128, L >= 32768, topk <= 2048) the size includes the
- * region of the sampled-threshold candidate path; a workspace that only
+ * Workspace bytes for `op` at these sizes with queries of dtype q_dt (0 for
+ * invalid sizes or dtype).  Arguments an op does not use are ignored
+ * (k_prime only matters for MISA_OP_RERANK, B only for MISA_OP_ROUTE).  For
+ * MISA_OP_SCORE_TOPK with many rows over one long sequence (N >= 128,
+ * L >= 32768, topk <= 2048) the size includes the region of the
+ * sampled-threshold candidate path; for bf16 queries a workspace that only
  * covers the full path (the size for topk > 2048) is accepted too, and then
- * that path runs.
+ * that path runs.  fp8 queries add N * H_I * (2d + 4) bytes (rounded up) for
+ * their bf16 copies and folded weights on the paths that read bf16 queries.
  */
-size_t misa_workspace_bytes(int32_t op, int32_t N, int32_t L, int32_t d, int32_t H_I,
-                            int32_t B, int32_t topk, int32_t k_prime);
+size_t misa_workspace_bytes(int32_t op, int32_t q_dt, int32_t N, int32_t L, int32_t d,
+                            int32_t H_I, int32_t B, int32_t topk, int32_t k_prime);
 
 /* Static description of a status code. */
 const char* misa_status_string(int32_t status);

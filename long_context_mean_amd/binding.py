@@ -57,11 +57,12 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     L.misa_pool_keys.argtypes = [P, P, I32, I32, I32, I32, I32, P, P]
-    L.misa_route_heads.argtypes = [P, I32, P, P, P, P, I32, P, P] + [I32] * 7 + [P, P, P, SZ, P]
-    L.misa_score_topk.argtypes = [P, I32, P, P, P, I32, P, P, P] + [I32] * 7 + [P, P, P, SZ, P]
-    L.dsa_score_topk.argtypes = [P, I32, P, P, P, I32, P, P] + [I32] * 6 + [P, P, P, SZ, P]
-    L.misa_rerank.argtypes = [P, I32, P, P, P, I32, P, P, P] + [I32] * 7 + [P, P, P, SZ, P]
-    L.misa_workspace_bytes.argtypes = [I32] * 8
+    # q q_dt q_scale w [kbar] k k_scale k_dt q_seq q_pos [heads | cand] sizes... outputs ws ws_bytes stream
+    L.misa_route_heads.argtypes = [P, I32, P, P, P, P, P, I32, P, P] + [I32] * 7 + [P, P, P, SZ, P]
+    L.misa_score_topk.argtypes = [P, I32, P, P, P, P, I32, P, P, P] + [I32] * 7 + [P, P, P, SZ, P]
+    L.dsa_score_topk.argtypes = [P, I32, P, P, P, P, I32, P, P] + [I32] * 6 + [P, P, P, SZ, P]
+    L.misa_rerank.argtypes = [P, I32, P, P, P, P, I32, P, P, P] + [I32] * 7 + [P, P, P, SZ, P]
+    L.misa_workspace_bytes.argtypes = [I32] * 9
     L.misa_workspace_bytes.restype = ctypes.c_size_t
     L.misa_status_string.argtypes = [I32]
     L.misa_status_string.restype = ctypes.c_char_p
@@ -119,14 +120,17 @@ def _check(fn, status):
 
 
 def workspace(op: int, N: int, L: int, d: int, H_I: int, B: int = 1, topk: int = 1,
-              k_prime: int = 0, device="cuda") -> torch.Tensor:
-    n = misa_workspace_bytes(op, N, L, d, H_I, B, topk, k_prime)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+              k_prime: int = 0, q_dt: int = MISA_BF16, device="cuda") -> torch.Tensor:
+    n = misa_workspace_bytes(op, q_dt, N, L, d, H_I, B, topk, k_prime)
+    if n == 0:
+        raise ValueError(f"no workspace size for op {op} at N={N} L={L} d={d} H_I={H_I} "
+                         f"B={B} topk={topk} k_prime={k_prime} q_dt={q_dt}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 # ---------------------------------------------------------------- the C entry points
-def misa_workspace_bytes(op, N, L, d, H_I, B=1, topk=1, k_prime=0) -> int:
-    return int(lib().misa_workspace_bytes(op, N, L, d, H_I, B, topk, k_prime))
+def misa_workspace_bytes(op, q_dt, N, L, d, H_I, B=1, topk=1, k_prime=0) -> int:
+    return int(lib().misa_workspace_bytes(op, q_dt, N, L, d, H_I, B, topk, k_prime))
 
 
 def misa_pool_keys(k: torch.Tensor, B: int, k_scale: Optional[torch.Tensor] = None,
@@ -142,7 +146,7 @@ def misa_pool_keys(k: torch.Tensor, B: int, k_scale: Optional[torch.Tensor] = No
 
 
 def misa_route_heads(q, w, kbar, k, q_seq, q_pos, B: int, h: int, k_scale=None, heads=None,
-                     head_score=None, ws=None, want_scores=True):
+                     head_score=None, ws=None, want_scores=True, q_scale=None):
     N, H_I, d = q.shape
     S, L, _ = k.shape
     if k.shape[2] != d:
@@ -152,9 +156,10 @@ def misa_route_heads(q, w, kbar, k, q_seq, q_pos, B: int, h: int, k_scale=None, 
     if head_score is None and want_scores:
         head_score = torch.empty((N, H_I), dtype=torch.float32, device=q.device)
     if ws is None:
-        ws = workspace(MISA_OP_ROUTE, N, L, d, H_I, B, device=q.device)
+        ws = workspace(MISA_OP_ROUTE, N, L, d, H_I, B, q_dt=_dtype_code(q), device=q.device)
     _check("misa_route_heads", lib().misa_route_heads(
-        _ptr(q, "q", _KEYS), _dtype_code(q), _ptr(w, "w", _F32, (N, H_I)),
+        _ptr(q, "q", _KEYS), _dtype_code(q), _ptr(q_scale, "q_scale", _F32, (N, H_I)),
+        _ptr(w, "w", _F32, (N, H_I)),
         _ptr(kbar, "kbar", _F32, (S, -(-L // B), d)), _ptr(k, "k", _KEYS),
         _ptr(k_scale, "k_scale", _F32, (S, L)), _dtype_code(k), _ptr(q_seq, "q_seq", _I32, (N,)),
         _ptr(q_pos, "q_pos", _I32, (N,)), N, S, L, d, B, H_I, h,
@@ -164,7 +169,7 @@ def misa_route_heads(q, w, kbar, k, q_seq, q_pos, B: int, h: int, k_scale=None, 
 
 
 def misa_score_topk(q, w, k, q_seq, q_pos, heads, topk: int, k_scale=None, idx=None, score=None,
-                    ws=None, want_score=True):
+                    ws=None, want_score=True, q_scale=None):
     N, H_I, d = q.shape
     S, L, _ = k.shape
     if k.shape[2] != d:
@@ -175,9 +180,11 @@ def misa_score_topk(q, w, k, q_seq, q_pos, heads, topk: int, k_scale=None, idx=N
     if score is None and want_score:
         score = torch.empty((N, topk), dtype=torch.float32, device=q.device)
     if ws is None:
-        ws = workspace(MISA_OP_SCORE_TOPK, N, L, d, H_I, topk=topk, device=q.device)
+        ws = workspace(MISA_OP_SCORE_TOPK, N, L, d, H_I, topk=topk, q_dt=_dtype_code(q),
+                       device=q.device)
     _check("misa_score_topk", lib().misa_score_topk(
-        _ptr(q, "q", _KEYS), _dtype_code(q), _ptr(w, "w", _F32, (N, H_I)), _ptr(k, "k", _KEYS),
+        _ptr(q, "q", _KEYS), _dtype_code(q), _ptr(q_scale, "q_scale", _F32, (N, H_I)),
+        _ptr(w, "w", _F32, (N, H_I)), _ptr(k, "k", _KEYS),
         _ptr(k_scale, "k_scale", _F32, (S, L)), _dtype_code(k), _ptr(q_seq, "q_seq", _I32, (N,)),
         _ptr(q_pos, "q_pos", _I32, (N,)), _ptr(heads, "heads", _I32, (N, h)), N, S, L, d, H_I, h,
         topk, _ptr(idx, "idx", _I32, (N, topk)), _ptr(score, "score", _F32, (N, topk)),
@@ -186,7 +193,7 @@ def misa_score_topk(q, w, k, q_seq, q_pos, heads, topk: int, k_scale=None, idx=N
 
 
 def dsa_score_topk(q, w, k, q_seq, q_pos, topk: int, k_scale=None, idx=None, score=None,
-                   ws=None, want_score=True):
+                   ws=None, want_score=True, q_scale=None):
     N, H_I, d = q.shape
     S, L, _ = k.shape
     if k.shape[2] != d:
@@ -196,9 +203,11 @@ def dsa_score_topk(q, w, k, q_seq, q_pos, topk: int, k_scale=None, idx=None, sco
     if score is None and want_score:
         score = torch.empty((N, topk), dtype=torch.float32, device=q.device)
     if ws is None:
-        ws = workspace(MISA_OP_SCORE_TOPK, N, L, d, H_I, topk=topk, device=q.device)
+        ws = workspace(MISA_OP_SCORE_TOPK, N, L, d, H_I, topk=topk, q_dt=_dtype_code(q),
+                       device=q.device)
     _check("dsa_score_topk", lib().dsa_score_topk(
-        _ptr(q, "q", _KEYS), _dtype_code(q), _ptr(w, "w", _F32, (N, H_I)), _ptr(k, "k", _KEYS),
+        _ptr(q, "q", _KEYS), _dtype_code(q), _ptr(q_scale, "q_scale", _F32, (N, H_I)),
+        _ptr(w, "w", _F32, (N, H_I)), _ptr(k, "k", _KEYS),
         _ptr(k_scale, "k_scale", _F32, (S, L)), _dtype_code(k), _ptr(q_seq, "q_seq", _I32, (N,)),
         _ptr(q_pos, "q_pos", _I32, (N,)), N, S, L, d, H_I, topk,
         _ptr(idx, "idx", _I32, (N, topk)), _ptr(score, "score", _F32, (N, topk)), _ptr(ws, "ws"),
@@ -208,7 +217,7 @@ def dsa_score_topk(q, w, k, q_seq, q_pos, topk: int, k_scale=None, idx=None, sco
 
 
 def misa_rerank(q, w, k, q_seq, q_pos, cand, topk: int, k_scale=None, idx=None, score=None,
-                ws=None, want_score=True):
+                ws=None, want_score=True, q_scale=None):
     N, H_I, d = q.shape
     S, L, _ = k.shape
     if k.shape[2] != d:
@@ -219,9 +228,11 @@ def misa_rerank(q, w, k, q_seq, q_pos, cand, topk: int, k_scale=None, idx=None, 
     if score is None and want_score:
         score = torch.empty((N, topk), dtype=torch.float32, device=q.device)
     if ws is None:
-        ws = workspace(MISA_OP_RERANK, N, L, d, H_I, topk=topk, k_prime=k_prime, device=q.device)
+        ws = workspace(MISA_OP_RERANK, N, L, d, H_I, topk=topk, k_prime=k_prime,
+                       q_dt=_dtype_code(q), device=q.device)
     _check("misa_rerank", lib().misa_rerank(
-        _ptr(q, "q", _KEYS), _dtype_code(q), _ptr(w, "w", _F32, (N, H_I)), _ptr(k, "k", _KEYS),
+        _ptr(q, "q", _KEYS), _dtype_code(q), _ptr(q_scale, "q_scale", _F32, (N, H_I)),
+        _ptr(w, "w", _F32, (N, H_I)), _ptr(k, "k", _KEYS),
         _ptr(k_scale, "k_scale", _F32, (S, L)), _dtype_code(k), _ptr(q_seq, "q_seq", _I32, (N,)),
         _ptr(q_pos, "q_pos", _I32, (N,)), _ptr(cand, "cand", _I32, (N, k_prime)), N, S, L, d,
         H_I, k_prime, topk, _ptr(idx, "idx", _I32, (N, topk)),
@@ -265,6 +276,7 @@ class DeviceProblem:
             self.k = up(p.k)
         self.w = up(p.w)
         self.k_scale = up(p.k_scale) if p.k_scale is not None else None
+        self.q_scale = up(p.q_scale) if p.q_scale is not None else None
         self.q_seq = up(p.q_seq)
         self.q_pos = up(p.q_pos)
 
@@ -273,16 +285,20 @@ class DeviceProblem:
 
     def route(self, kbar, h=None, **kw):
         return misa_route_heads(self.q, self.w, kbar, self.k, self.q_seq, self.q_pos, self.p.B,
-                                self.p.h if h is None else h, k_scale=self.k_scale, **kw)
+                                self.p.h if h is None else h, k_scale=self.k_scale,
+                                q_scale=self.q_scale, **kw)
 
     def score_topk(self, heads, topk=None, **kw):
         return misa_score_topk(self.q, self.w, self.k, self.q_seq, self.q_pos, heads,
-                               self.p.topk if topk is None else topk, k_scale=self.k_scale, **kw)
+                               self.p.topk if topk is None else topk, k_scale=self.k_scale,
+                               q_scale=self.q_scale, **kw)
 
     def dsa(self, topk=None, **kw):
         return dsa_score_topk(self.q, self.w, self.k, self.q_seq, self.q_pos,
-                              self.p.topk if topk is None else topk, k_scale=self.k_scale, **kw)
+                              self.p.topk if topk is None else topk, k_scale=self.k_scale,
+                              q_scale=self.q_scale, **kw)
 
     def rerank(self, cand, topk=None, **kw):
         return misa_rerank(self.q, self.w, self.k, self.q_seq, self.q_pos, cand,
-                           self.p.topk if topk is None else topk, k_scale=self.k_scale, **kw)
+                           self.p.topk if topk is None else topk, k_scale=self.k_scale,
+                           q_scale=self.q_scale, **kw)

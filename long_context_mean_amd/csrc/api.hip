@@ -35,12 +35,14 @@ int32_t hip_status(hipError_t e) {
   return MISA_ERR_HIP;
 }
 
-int32_t check_dtypes(int32_t q_dt, int32_t k_dt, const float* k_scale) {
+int32_t check_dtypes(int32_t q_dt, int32_t k_dt, const float* q_scale, const float* k_scale) {
   const bool ok = (q_dt == MISA_F32 && k_dt == MISA_F32) ||
                   (q_dt == MISA_BF16 && k_dt == MISA_BF16) ||
-                  (q_dt == MISA_BF16 && k_dt == MISA_FP8_E4M3);
+                  (q_dt == MISA_BF16 && k_dt == MISA_FP8_E4M3) ||
+                  (q_dt == MISA_FP8_E4M3 && k_dt == MISA_FP8_E4M3);
   if (!ok) return MISA_ERR_UNSUPPORTED;
   if (k_dt == MISA_FP8_E4M3 && !k_scale) return MISA_ERR_NULL;
+  if (q_dt == MISA_FP8_E4M3 && !q_scale) return MISA_ERR_NULL;
   return MISA_OK;
 }
 
@@ -110,6 +112,11 @@ size_t score_topk_bytes(int N, int L, int topk) {
   return cand_layout(t.bytes, N, L).bytes;
 }
 
+size_t rerank_bytes(int N, int k_prime) {
+  const TopkLayout t = topk_layout(kOneRowMinN, k_prime);   // always one row per workgroup
+  return align_up(static_cast<size_t>(N) * t.u_stride * 4, 256);
+}
+
 int route_chunks(int L, int B) {
   const int mf = L / B;
   const int per = misa::route_blocks_per_chunk();
@@ -127,6 +134,29 @@ size_t route_bytes(int N, int L, int B, int H_I) {
   return route_partial_bytes(N, L, B, H_I) + align_up(M * 128 * 2 * 2, 256);
 }
 
+// fp8 queries: bf16 copies of the codes [N, H_I, d] and the folded weights
+// w * q_scale [N, H_I], placed after an op's own workspace.
+size_t q8_bytes(int N, int H_I, int d) {
+  const size_t rows = static_cast<size_t>(N) * H_I;
+  return align_up(rows * d * 2, 256) + align_up(rows * 4, 256);
+}
+
+// Converts fp8 queries into `region` and points (q, q_dt, w) at the bf16
+// problem with the same scores (see launch_q8_prep).
+hipError_t prep_fp8_queries(const void*& q, int32_t& q_dt, const float*& w, const float* q_scale,
+                            int N, int H_I, int d, uint8_t* region, hipStream_t st) {
+  const size_t rows = static_cast<size_t>(N) * H_I;
+  uint16_t* qb = reinterpret_cast<uint16_t*>(region);
+  float* wq = reinterpret_cast<float*>(region + align_up(rows * d * 2, 256));
+  misa::Q8PrepArgs a{static_cast<const uint8_t*>(q), q_scale, w, static_cast<int64_t>(rows), d,
+                     qb, wq};
+  const hipError_t e = misa::launch_q8_prep(a, st);
+  q = qb;
+  q_dt = MISA_BF16;
+  w = wq;
+  return e;
+}
+
 // ---------------------------------------------------------------- kernel timing
 struct Profiler {
   bool on = false;
@@ -136,20 +166,22 @@ struct Profiler {
 };
 Profiler g_prof;
 
-int32_t score_topk_impl(const void* q, int32_t q_dt, const float* w, const void* k,
-                        const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+int32_t score_topk_impl(const void* q, int32_t q_dt, const float* q_scale, const float* w,
+                        const void* k, const float* k_scale, int32_t k_dt, const int32_t* q_seq,
                         const int32_t* q_pos, const int32_t* heads, int32_t N, int32_t S,
                         int32_t L, int32_t d, int32_t H_I, int32_t h, int32_t topk,
                         int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream) {
   if (!q || !w || !k || !q_seq || !q_pos || !idx) return MISA_ERR_NULL;
-  int32_t rc = check_dtypes(q_dt, k_dt, k_scale);
+  int32_t rc = check_dtypes(q_dt, k_dt, q_scale, k_scale);
   if (rc) return rc;
   if ((rc = check_sizes(N, S, L, d, H_I))) return rc;
   if (h < 1 || h > H_I || topk < 1 || topk > kMaxTopk) return MISA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k)) return MISA_ERR_SHAPE;
+  const bool f8 = q_dt == MISA_FP8_E4M3;
   const TopkLayout lay = topk_layout(N, L);
+  const size_t q8_off = score_topk_bytes(N, L, topk);
   if (!ws) return MISA_ERR_NULL;
-  if (ws_bytes < lay.bytes) return MISA_ERR_WORKSPACE;
+  if (ws_bytes < (f8 ? q8_off + q8_bytes(N, H_I, d) : lay.bytes)) return MISA_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint32_t* u = reinterpret_cast<uint32_t*>(base);
@@ -157,8 +189,21 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* w, const void*
   hipError_t e = hipSuccess;
   if (hist) e = misa::launch_clear(hist, static_cast<size_t>(N) * misa::kHistWords, st);
   if (e != hipSuccess) return hip_status(e);
-  const bool gemm = S == 1 && lay.one_row && N >= kOneRowMinN && q_dt == MISA_BF16 &&
-                    k_dt == MISA_BF16;
+  // many rows over one sequence: GEMM over the gathered head rows (bf16, or
+  // e4m3 straight from the codes)
+  const bool gemm = S == 1 && lay.one_row && N >= kOneRowMinN &&
+                    ((q_dt == MISA_BF16 && k_dt == MISA_BF16) || (f8 && d == 128));
+  if (f8 && !gemm) {
+    e = prep_fp8_queries(q, q_dt, w, q_scale, N, H_I, d, base + q8_off, st);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  auto prefill_args = [&](uint32_t* uu, int u_stride) {
+    misa::PrefillArgs a{q, w, k, q_pos, heads, N, L, d, H_I, h, uu, u_stride};
+    a.fp8 = f8;
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
+    return a;
+  };
   if (gemm && cand_eligible(N, L, topk) && ws_bytes >= cand_layout(lay.bytes, N, L).bytes) {
     // many rows over one sequence, candidate path: sampled thresholds, GEMM
     // keeping only the keys above them, exact select; unproven rows redo the
@@ -166,7 +211,7 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* w, const void*
     const CandLayout cl = cand_layout(lay.bytes, N, L);
     const int h_eff = heads ? h : H_I;
     const int qb = misa::prefill_rows_per_block(h_eff);
-    const int splits = misa::prefill_cand_splits(N, L, h_eff, d);
+    const int splits = misa::prefill_cand_splits(N, L, h_eff, d, f8);
     const int cap = kCandRegion / splits;
     uint32_t* us = reinterpret_cast<uint32_t*>(base + cl.off_us);
     float* tau = reinterpret_cast<float*>(base + cl.off_tau);
@@ -174,14 +219,14 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* w, const void*
     uint2* cand = reinterpret_cast<uint2*>(base + cl.off_cand);
     uint32_t* rflag = reinterpret_cast<uint32_t*>(base + cl.off_rflag);
     uint32_t* bflag = reinterpret_cast<uint32_t*>(base + cl.off_bflag);
-    misa::PrefillArgs sp{q, w, k, q_pos, heads, N, L, d, H_I, h, us, cl.us_stride};
+    misa::PrefillArgs sp = prefill_args(us, cl.us_stride);
     sp.key_step = 1 << kSampleShift;
     sp.pos_shift = kSampleShift;
     sp.kernel_id = misa::K_PREFILL_SAMPLE;
     if ((e = misa::launch_prefill(sp, st)) != hipSuccess) return hip_status(e);
     misa::TauArgs ta{us, cl.us_stride, q_pos, N, topk, kSampleShift, qb, tau, bflag};
     if ((e = misa::launch_tau(ta, st)) != hipSuccess) return hip_status(e);
-    misa::PrefillArgs mp{q, w, k, q_pos, heads, N, L, d, H_I, h, nullptr, 0};
+    misa::PrefillArgs mp = prefill_args(nullptr, 0);
     mp.tau = tau;
     mp.cnt_out = cnt;
     mp.cand_out = cand;
@@ -190,7 +235,7 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* w, const void*
     misa::CandTopkArgs ca{cnt, cand, splits, cap, q_pos, N, L, topk, qb, rflag, bflag, idx,
                           score};
     if ((e = misa::launch_cand_topk(ca, st)) != hipSuccess) return hip_status(e);
-    misa::PrefillArgs fp{q, w, k, q_pos, heads, N, L, d, H_I, h, u, lay.u_stride};
+    misa::PrefillArgs fp = prefill_args(u, lay.u_stride);
     fp.block_flag = bflag;
     fp.kernel_id = misa::K_PREFILL_FULL;
     if ((e = misa::launch_prefill(fp, st)) != hipSuccess) return hip_status(e);
@@ -199,9 +244,7 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* w, const void*
     return hip_status(misa::launch_topk(ft, st));
   }
   if (gemm) {
-    // many rows over one sequence: GEMM over the gathered head rows
-    misa::PrefillArgs pa{q, w, k, q_pos, heads, N, L, d, H_I, h, u, lay.u_stride};
-    e = misa::launch_prefill(pa, st);
+    e = misa::launch_prefill(prefill_args(u, lay.u_stride), st);
   } else {
     misa::ScoreArgs sa{q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, heads, nullptr,
                        N, S, L, d, H_I, h, 0, u, lay.u_stride, hist};
@@ -244,22 +287,22 @@ const char* misa_status_string(int32_t status) {
 
 int32_t misa_last_hip_error(void) { return g_last_hip; }
 
-size_t misa_workspace_bytes(int32_t op, int32_t N, int32_t L, int32_t d, int32_t H_I, int32_t B,
-                            int32_t topk, int32_t k_prime) {
-  (void)d;
+size_t misa_workspace_bytes(int32_t op, int32_t q_dt, int32_t N, int32_t L, int32_t d,
+                            int32_t H_I, int32_t B, int32_t topk, int32_t k_prime) {
   if (N < 1 || N > kMaxN || L < 1 || L > kMaxL || H_I < 1 || H_I > 64) return 0;
+  if (d != 64 && d != 128) return 0;
+  if (q_dt != MISA_F32 && q_dt != MISA_BF16 && q_dt != MISA_FP8_E4M3) return 0;
+  const size_t extra = q_dt == MISA_FP8_E4M3 ? q8_bytes(N, H_I, d) : 0;
   switch (op) {
     case MISA_OP_ROUTE:
       if (B < 1 || B > 1024) return 0;
-      return route_bytes(N, L, B, H_I);
+      return route_bytes(N, L, B, H_I) + extra;
     case MISA_OP_SCORE_TOPK:
       if (topk < 1 || topk > kMaxTopk) return 0;
-      return score_topk_bytes(N, L, topk);
-    case MISA_OP_RERANK: {
+      return score_topk_bytes(N, L, topk) + extra;
+    case MISA_OP_RERANK:
       if (k_prime < 1 || k_prime > kMaxTopk) return 0;
-      TopkLayout t = topk_layout(kOneRowMinN, k_prime);   // always one row per workgroup
-      return align_up(static_cast<size_t>(N) * t.u_stride * 4, 256);
-    }
+      return rerank_bytes(N, k_prime) + extra;
     default:
       return 0;
   }
@@ -277,60 +320,74 @@ int32_t misa_pool_keys(const void* k, const float* k_scale, int32_t k_dt, int32_
   return hip_status(misa::launch_pool(a, static_cast<hipStream_t>(stream)));
 }
 
-int32_t misa_route_heads(const void* q, int32_t q_dt, const float* w, const float* kbar,
-                         const void* k, const float* k_scale, int32_t k_dt,
+int32_t misa_route_heads(const void* q, int32_t q_dt, const float* q_scale, const float* w,
+                         const float* kbar, const void* k, const float* k_scale, int32_t k_dt,
                          const int32_t* q_seq, const int32_t* q_pos, int32_t N, int32_t S,
                          int32_t L, int32_t d, int32_t B, int32_t H_I, int32_t h,
                          int32_t* heads, float* head_score, void* ws, size_t ws_bytes,
                          void* stream) {
   if (!q || !w || !kbar || !k || !q_seq || !q_pos || !heads) return MISA_ERR_NULL;
-  int32_t rc = check_dtypes(q_dt, k_dt, k_scale);
+  int32_t rc = check_dtypes(q_dt, k_dt, q_scale, k_scale);
   if (rc) return rc;
   if ((rc = check_sizes(N, S, L, d, H_I))) return rc;
   if (B < 1 || B > 1024 || h < 1 || h > H_I) return MISA_ERR_SHAPE;
+  const bool f8 = q_dt == MISA_FP8_E4M3;
+  if (f8 && !aligned16(q)) return MISA_ERR_SHAPE;
+  const size_t own = route_bytes(N, L, B, H_I);
   if (!ws) return MISA_ERR_NULL;
-  if (ws_bytes < route_bytes(N, L, B, H_I)) return MISA_ERR_WORKSPACE;
+  if (ws_bytes < own + (f8 ? q8_bytes(N, H_I, d) : 0)) return MISA_ERR_WORKSPACE;
   uint8_t* wsb = static_cast<uint8_t*>(ws);
+  if (f8) {
+    const hipError_t e = prep_fp8_queries(q, q_dt, w, q_scale, N, H_I, d, wsb + own,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_status(e);
+  }
   misa::RouteArgs a{q, q_dt, w, kbar, k, k_scale, k_dt, q_seq, q_pos, N, S, L, d, B, H_I, h,
                     heads, head_score, reinterpret_cast<float*>(wsb), route_chunks(L, B),
                     reinterpret_cast<uint16_t*>(wsb + route_partial_bytes(N, L, B, H_I))};
   return hip_status(misa::launch_route(a, static_cast<hipStream_t>(stream)));
 }
 
-int32_t misa_score_topk(const void* q, int32_t q_dt, const float* w, const void* k,
-                        const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+int32_t misa_score_topk(const void* q, int32_t q_dt, const float* q_scale, const float* w,
+                        const void* k, const float* k_scale, int32_t k_dt, const int32_t* q_seq,
                         const int32_t* q_pos, const int32_t* heads, int32_t N, int32_t S,
                         int32_t L, int32_t d, int32_t H_I, int32_t h, int32_t topk,
                         int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream) {
   if (!heads) return MISA_ERR_NULL;
-  return score_topk_impl(q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, heads, N, S, L, d, H_I, h,
-                         topk, idx, score, ws, ws_bytes, stream);
+  return score_topk_impl(q, q_dt, q_scale, w, k, k_scale, k_dt, q_seq, q_pos, heads, N, S, L, d,
+                         H_I, h, topk, idx, score, ws, ws_bytes, stream);
 }
 
-int32_t dsa_score_topk(const void* q, int32_t q_dt, const float* w, const void* k,
-                       const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+int32_t dsa_score_topk(const void* q, int32_t q_dt, const float* q_scale, const float* w,
+                       const void* k, const float* k_scale, int32_t k_dt, const int32_t* q_seq,
                        const int32_t* q_pos, int32_t N, int32_t S, int32_t L, int32_t d,
                        int32_t H_I, int32_t topk, int32_t* idx, float* score, void* ws,
                        size_t ws_bytes, void* stream) {
-  return score_topk_impl(q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, nullptr, N, S, L, d, H_I,
-                         H_I, topk, idx, score, ws, ws_bytes, stream);
+  return score_topk_impl(q, q_dt, q_scale, w, k, k_scale, k_dt, q_seq, q_pos, nullptr, N, S, L,
+                         d, H_I, H_I, topk, idx, score, ws, ws_bytes, stream);
 }
 
-int32_t misa_rerank(const void* q, int32_t q_dt, const float* w, const void* k,
-                    const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+int32_t misa_rerank(const void* q, int32_t q_dt, const float* q_scale, const float* w,
+                    const void* k, const float* k_scale, int32_t k_dt, const int32_t* q_seq,
                     const int32_t* q_pos, const int32_t* cand, int32_t N, int32_t S, int32_t L,
                     int32_t d, int32_t H_I, int32_t k_prime, int32_t topk, int32_t* idx,
                     float* score, void* ws, size_t ws_bytes, void* stream) {
   if (!q || !w || !k || !q_seq || !q_pos || !cand || !idx) return MISA_ERR_NULL;
-  int32_t rc = check_dtypes(q_dt, k_dt, k_scale);
+  int32_t rc = check_dtypes(q_dt, k_dt, q_scale, k_scale);
   if (rc) return rc;
   if ((rc = check_sizes(N, S, L, d, H_I))) return rc;
   if (topk < 1 || k_prime < topk || k_prime > kMaxTopk) return MISA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k)) return MISA_ERR_SHAPE;
-  const size_t need = misa_workspace_bytes(MISA_OP_RERANK, N, L, d, H_I, 1, topk, k_prime);
+  const bool f8 = q_dt == MISA_FP8_E4M3;
+  const size_t own = rerank_bytes(N, k_prime);
   if (!ws) return MISA_ERR_NULL;
-  if (ws_bytes < need) return MISA_ERR_WORKSPACE;
+  if (ws_bytes < own + (f8 ? q8_bytes(N, H_I, d) : 0)) return MISA_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (f8) {
+    const hipError_t e =
+        prep_fp8_queries(q, q_dt, w, q_scale, N, H_I, d, static_cast<uint8_t*>(ws) + own, st);
+    if (e != hipSuccess) return hip_status(e);
+  }
   const int u_stride = topk_layout(kOneRowMinN, k_prime).u_stride;
   uint32_t* u = static_cast<uint32_t*>(ws);
   misa::ScoreArgs sa{q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, nullptr, cand,
@@ -385,7 +442,7 @@ const char* misa_kernel_name(int32_t kernel_id) {
       "score_mfma_kernel", "score_f32_kernel",     "score_prefill_kernel",
       "topk_collect_kernel", "topk_final_kernel",   "topk_row_kernel",
       "score_prefill_sample", "score_prefill_full", "topk_tau_kernel", "topk_cand_kernel",
-      "route_split_kernel"};
+      "route_split_kernel", "q8_prep_kernel"};
   if (kernel_id < 0 || kernel_id >= misa::K_COUNT_IDS) return "unknown";
   return names[kernel_id];
 }

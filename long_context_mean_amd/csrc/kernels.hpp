@@ -24,6 +24,7 @@ enum KernelId : int {
   K_TOPK_TAU,
   K_TOPK_CAND,
   K_ROUTE_SPLIT,
+  K_Q8_PREP,
   K_COUNT_IDS
 };
 
@@ -93,9 +94,26 @@ struct ScoreArgs {
 };
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
 
+// ---------------------------------------------------------------- fp8 queries
+// e4m3 query heads -> exact bf16 copies qb [rows, d], and wq = w * q_scale
+// [rows] (rows = N * H_I).  A positive head scale s gives
+// w * ReLU(s * x) = (w * s) * ReLU(x) and |w| * s = |w * s|, so the kernels
+// that read bf16 queries compute the fp8 problem from (qb, wq).
+struct Q8PrepArgs {
+  const uint8_t* q;
+  const float* q_scale;
+  const float* w;
+  int64_t rows;
+  int d;
+  uint16_t* qb;
+  float* wq;
+};
+hipError_t launch_q8_prep(const Q8PrepArgs& a, hipStream_t st);
+
 // ---------------------------------------------------------------- prefill scoring
-// Rows that all read one key sequence (bf16 q and keys): MFMA GEMM over the
-// gathered routed head rows.
+// Rows that all read one key sequence (bf16 q and keys, or e4m3 q and keys
+// with their scales and d = 128): MFMA GEMM over the gathered routed head
+// rows.
 //  plain mode (cand_out NULL): writes order keys u[t, s] for s <= q_pos[t];
 //    with key_step > 1 it scores only keys key_step*s' (s' <= q_pos[t] >>
 //    pos_shift) and writes them to u[t, s'].  With block_flag, row blocks
@@ -121,10 +139,13 @@ struct PrefillArgs {
   uint2* cand_out = nullptr;
   int cap = 0;
   int kernel_id = K_SCORE_PREFILL;
+  bool fp8 = false;                 // e4m3 q [N, H_I, d] and k [L, d] (d = 128)
+  const float* q_scale = nullptr;   // fp8: [N, H_I]
+  const float* k_scale = nullptr;   // fp8: [L]
 };
 int prefill_rows_per_block(int h_eff);
 // key-range splits of the candidate-mode GEMM (the layout of cnt_out / cand_out)
-int prefill_cand_splits(int N, int L, int h_eff, int d);
+int prefill_cand_splits(int N, int L, int h_eff, int d, bool fp8);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------- top-k

@@ -18,6 +18,16 @@
 // (in-lane, then across lane groups) and writes the order key of every
 // causally visible (row, key) pair; tiles away from the causal diagonal store
 // without masks.
+//
+// fp8 variant (e4m3 queries and keys, d = 128): each 128-byte key row is one
+// K = 128 step of v_mfma_f32_16x16x128_f8f6f4, so a row tile needs a single
+// MFMA per 16 keys.  Scales are positive, so w * ReLU(sq * sk * x) =
+// sk * (w * sq) * ReLU(x): the query head scale sq is folded into the head
+// weight when the weights are loaded, and the key scale sk multiplies each
+// key's head sum.  The key scales of a tile travel with it: every wavefront
+// DMAs the tile's 64 scales into its own LDS slot.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -25,14 +35,17 @@ namespace misa {
 namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kRowsPerWG = 256;       // gathered head rows per workgroup
 constexpr int kKeyTile = 64;          // keys per LDS tile
 
 struct PrefillParams {
-  const uint16_t* q;
+  const uint8_t* q;          // [N, H_I, D] bf16 or e4m3
   const float* w;
-  const uint8_t* k;          // one key sequence [L, D] bf16
+  const float* q_scale;      // e4m3 only: [N, H_I]
+  const uint8_t* k;          // one key sequence [L, D] bf16 or e4m3
+  const float* k_scale;      // e4m3 only: [L]
   const int32_t* q_pos;
   const int32_t* heads;      // [N, h] or NULL (all heads)
   int N, L, H_I, h;
@@ -47,16 +60,19 @@ struct PrefillParams {
   int cap, splits;
 };
 
-template <int D>
+template <int D, bool F8>
 struct PLayout {
-  static constexpr int ROW = D * 2;                    // bytes per key row (bf16)
+  static constexpr int ROW = F8 ? D : D * 2;           // bytes per key row
   static constexpr int CH = ROW / 16;                  // 16-byte chunks per row
   static constexpr int TILE = kKeyTile * ROW;          // bytes per LDS key tile
-  static constexpr int KK = D / 32;                    // MFMAs per 16x16 output tile
-  static constexpr int PER_THREAD = kKeyTile * CH / 256;  // 16-byte loads per thread per tile
+  static constexpr int KK = F8 ? D / 128 : D / 32;     // MFMAs per 16x16 output tile
+  static constexpr int ROW_LOADS = kKeyTile * CH / 256;  // 16-byte key loads per thread per tile
+  static constexpr int PER_THREAD = ROW_LOADS + (F8 ? 1 : 0);  // + the key-scale load
   // Chunk q of row r sits at chunk position q ^ swz(r): the 16 rows read by
   // one MFMA B fragment then hit 16 different bank groups.
-  __device__ static int swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static int swz(int r) { return CH == 16 ? (r & 15) : ((r >> 1) & 7); }
+  // A / B fragment: 8 bf16 (16 bytes) or 32 e4m3 codes (32 bytes) per lane
+  using Frag = std::conditional_t<F8, i32x8_t, bf16x8_t>;
 };
 
 constexpr int kStages = 3;                             // LDS key tiles in flight
@@ -65,12 +81,19 @@ constexpr int kStages = 3;                             // LDS key tiles in fligh
 // (global_load_lds_dwordx4: each wavefront instruction fills 1 KB of the
 // tile, lane l the l-th 16 bytes).  s >= L (in the same units) reads row 0
 // instead (masked later).  Completion is tracked by vmcnt.
-template <int D>
-__device__ __forceinline__ void dma_key_tile(const uint8_t* k, int key0, int L, int key_step,
-                                             uint8_t* tile, int wave, int lane) {
-  using LY = PLayout<D>;
+template <int D, bool F8>
+__device__ __forceinline__ void dma_key_tile(const uint8_t* k, const float* k_scale, int key0,
+                                             int L, int key_step, uint8_t* tile, float* scales,
+                                             int wave, int lane) {
+  using LY = PLayout<D, F8>;
+  if constexpr (F8) {
+    // this wavefront's copy of the tile's 64 key scales (lane l -> key key0 + l)
+    const int key = key0 + lane < L ? key0 + lane : 0;
+    __builtin_amdgcn_global_load_lds(k_scale + static_cast<size_t>(key) * key_step, scales, 4, 0,
+                                     0);
+  }
 #pragma unroll
-  for (int j = 0; j < LY::PER_THREAD; ++j) {
+  for (int j = 0; j < LY::ROW_LOADS; ++j) {
     const int blk = j * 4 + wave;                       // 1 KB block of the tile
     const int f = blk * 64 + lane;                      // 16-byte chunk slot in the tile
     const int r = f / LY::CH;
@@ -138,22 +161,46 @@ struct OutState {
 
 // One LDS key tile (64 keys) against the wavefront's 4 row tiles.  MASK: some
 // (row, key) of the tile may be outside the causal prefix or the row block.
-template <int HP, int D, bool MASK, bool CAND>
-__device__ __forceinline__ void score_tile(const uint8_t* tile, int key0,
-                                           const bf16x8_t (&a)[4][PLayout<D>::KK],
+// B fragment kk of key row r (lane group g): bf16 K-chunk 4kk+g, or e4m3
+// bytes 32g .. 32g+31 (chunks 2g, 2g+1).  A fragments use the same K order.
+template <int D, bool F8>
+__device__ __forceinline__ typename PLayout<D, F8>::Frag load_b(const uint8_t* tile, int r, int kk,
+                                                                int g) {
+  using LY = PLayout<D, F8>;
+  const uint8_t* row = tile + r * LY::ROW;
+  if constexpr (F8) {
+    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(row + 16 * ((2 * g) ^ LY::swz(r)));
+    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(row + 16 * ((2 * g + 1) ^ LY::swz(r)));
+    return i32x8_t{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z),
+                   static_cast<int>(lo.w), static_cast<int>(hi.x), static_cast<int>(hi.y),
+                   static_cast<int>(hi.z), static_cast<int>(hi.w)};
+  } else {
+    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                            row + 16 * ((4 * kk + g) ^ LY::swz(r))));
+  }
+}
+
+template <bool F8, typename Frag>
+__device__ __forceinline__ f32x4_t mfma_step(const Frag& a, const Frag& b, f32x4_t acc) {
+  if constexpr (F8)   // e4m3 x e4m3 (format codes 0, 0), no block scales
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+
+template <int HP, int D, bool F8, bool MASK, bool CAND>
+__device__ __forceinline__ void score_tile(const uint8_t* tile, const float* scales, int key0,
+                                           const typename PLayout<D, F8>::Frag (&a)[4][PLayout<D, F8>::KK],
                                            const float (&wv)[4][4], OutState<HP, CAND>& o,
                                            int cap, int g, int c) {
-  using LY = PLayout<D>;
+  using LY = PLayout<D, F8>;
   using RM = RowMap<HP>;
   constexpr int KK = LY::KK;
 #pragma unroll
   for (int ct = 0; ct < kKeyTile / 16; ++ct) {
-    bf16x8_t b[KK];
+    typename LY::Frag b[KK];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      b[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
-                                               tile + (ct * 16 + c) * LY::ROW +
-                                               16 * ((4 * kk + g) ^ LY::swz(ct * 16 + c))));
+    for (int kk = 0; kk < KK; ++kk) b[kk] = load_b<D, F8>(tile, ct * 16 + c, kk, g);
     float v[RM::NG];
 #pragma unroll
     for (int q = 0; q < RM::NG; ++q) v[q] = 0.f;
@@ -161,12 +208,13 @@ __device__ __forceinline__ void score_tile(const uint8_t* tile, int key0,
     for (int rt = 0; rt < 4; ++rt) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][kk], b[kk], acc, 0, 0, 0);
+      for (int kk = 0; kk < KK; ++kk) acc = mfma_step<F8>(a[rt][kk], b[kk], acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[rt / RM::TQ] = fmaf(wv[rt][i], relu(acc[i]), v[rt / RM::TQ]);
     }
     const int key = key0 + ct * 16 + c;
+    float ks = 1.f;
+    if constexpr (F8) ks = scales[ct * 16 + c];
 #pragma unroll
     for (int q = 0; q < RM::NG; ++q) {
       float x = v[q];
@@ -174,6 +222,7 @@ __device__ __forceinline__ void score_tile(const uint8_t* tile, int key0,
         x += __shfl_xor(x, 16, 64);
         x += __shfl_xor(x, 32, 64);
       }
+      if constexpr (F8) x *= ks;
       const bool owner = RM::IN_LANE || g == 0;
       const bool vis = owner && (!MASK || key <= o.pos[q]);
       if constexpr (!CAND) {
@@ -194,13 +243,14 @@ __device__ __forceinline__ void score_tile(const uint8_t* tile, int key0,
   }
 }
 
-template <int HP, int D, bool CAND>
+template <int HP, int D, bool F8, bool CAND>
 __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(PrefillParams p) {
-  using LY = PLayout<D>;
+  using LY = PLayout<D, F8>;
   using RM = RowMap<HP>;
   constexpr int KK = LY::KK;
   constexpr int QB = kRowsPerWG / HP;                  // query rows per workgroup
   __shared__ __align__(16) uint8_t tiles[kStages][LY::TILE];
+  __shared__ float kscales[kStages][F8 ? 4 : 1][F8 ? kKeyTile : 1];   // per wavefront copies
   __shared__ int pos_lds[QB];
 
   if (p.block_flag && p.block_flag[blockIdx.y] == 0u) return;
@@ -226,7 +276,7 @@ __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(Pre
   }
 
   // A operand (4 row tiles of this wavefront) and the weights of the lane's rows
-  bf16x8_t a[4][KK];
+  typename LY::Frag a[4][KK];
   float wv[4][4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
@@ -236,12 +286,18 @@ __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(Pre
     const bool rv = t < p.N && hs < p.h;
     int j = 0;
     if (rv) j = p.heads ? p.heads[static_cast<size_t>(t) * p.h + hs] : hs;
-    const uint16_t* qrp = p.q + (static_cast<size_t>(rv ? t : 0) * p.H_I + j) * D;
+    const uint8_t* qrp = p.q + (static_cast<size_t>(rv ? t : 0) * p.H_I + j) * LY::ROW;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrp + 32 * kk + 8 * g);
-      if (!rv) x = u32x4_t{0u, 0u, 0u, 0u};
-      a[rt][kk] = __builtin_bit_cast(bf16x8_t, x);
+      if constexpr (F8) {
+        i32x8_t x = *reinterpret_cast<const i32x8_t*>(qrp + 32 * g);
+        if (!rv) x = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        a[rt][kk] = x;
+      } else {
+        u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrp + 64 * kk + 16 * g);
+        if (!rv) x = u32x4_t{0u, 0u, 0u, 0u};
+        a[rt][kk] = __builtin_bit_cast(bf16x8_t, x);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -252,6 +308,7 @@ __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(Pre
       if (tt < p.N && ho < p.h) {
         const int jj = p.heads ? p.heads[static_cast<size_t>(tt) * p.h + ho] : ho;
         wf = p.w[static_cast<size_t>(tt) * p.H_I + jj];
+        if constexpr (F8) wf *= p.q_scale[static_cast<size_t>(tt) * p.H_I + jj];
       }
       wv[rt][i] = wf;
     }
@@ -289,7 +346,9 @@ __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(Pre
   const int ntiles = (ks1 - ks0 + kKeyTile - 1) / kKeyTile;
 #pragma unroll
   for (int j = 0; j < S - 1; ++j)
-    if (j < ntiles) dma_key_tile<D>(p.k, ks0 + j * kKeyTile, p.L, p.key_step, tiles[j], wave, lane);
+    if (j < ntiles)
+      dma_key_tile<D, F8>(p.k, p.k_scale, ks0 + j * kKeyTile, p.L, p.key_step, tiles[j],
+                          kscales[j][F8 ? wave : 0], wave, lane);
   if (ntiles >= S - 1)
     wait_vm_barrier<AHEAD>();
   else
@@ -299,13 +358,15 @@ __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(Pre
     const int key0 = ks0 + i * kKeyTile;
     // every (row, key) of the tile is visible: no masks
     const bool unmasked = full_block && key0 + kKeyTile - 1 <= minpos;
+    const float* sc = kscales[buf][F8 ? wave : 0];
     if (unmasked)
-      score_tile<HP, D, false, CAND>(tiles[buf], key0, a, wv, o, p.cap, g, c);
+      score_tile<HP, D, F8, false, CAND>(tiles[buf], sc, key0, a, wv, o, p.cap, g, c);
     else
-      score_tile<HP, D, true, CAND>(tiles[buf], key0, a, wv, o, p.cap, g, c);
+      score_tile<HP, D, F8, true, CAND>(tiles[buf], sc, key0, a, wv, o, p.cap, g, c);
     const int nb = buf == 0 ? S - 1 : buf - 1;          // the buffer tile i-1 was read from
     if (i + S - 1 < ntiles) {
-      dma_key_tile<D>(p.k, key0 + (S - 1) * kKeyTile, p.L, p.key_step, tiles[nb], wave, lane);
+      dma_key_tile<D, F8>(p.k, p.k_scale, key0 + (S - 1) * kKeyTile, p.L, p.key_step, tiles[nb],
+                          kscales[nb][F8 ? wave : 0], wave, lane);
       wait_vm_barrier<AHEAD>();                         // tile i+1 has landed
     } else {
       wait_vm_barrier<0>();
@@ -327,13 +388,13 @@ int hp_of(int h) {
 }
 
 // Workgroups of one kernel instantiation resident on the whole chip at once.
-template <int HP, int D, bool CAND>
+template <int HP, int D, bool F8, bool CAND>
 int chip_slots() {
   static const int slots = [] {
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, score_prefill_kernel<HP, D, CAND>, 256,
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, score_prefill_kernel<HP, D, F8, CAND>, 256,
                                                       0) != hipSuccess ||
         cus < 1 || per < 1)
       return 1024;
@@ -365,18 +426,20 @@ int choose_splits(int qblocks, int L, int slots, int min_tiles) {
 
 // min_tiles: key tiles per split at least (the sampled pass, with few keys
 // per row, keeps longer splits so each workgroup's operand loads pay off)
-template <int HP, int D, bool CAND>
+template <int HP, int D, bool F8, bool CAND>
 int splits_t(int N, int L, int min_tiles = 4) {
   constexpr int QB = kRowsPerWG / HP;
-  return choose_splits((N + QB - 1) / QB, L, chip_slots<HP, D, CAND>(), min_tiles);
+  return choose_splits((N + QB - 1) / QB, L, chip_slots<HP, D, F8, CAND>(), min_tiles);
 }
 
-template <int HP, int D>
+template <int HP, int D, bool F8>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   PrefillParams p;
-  p.q = static_cast<const uint16_t*>(a.q);
+  p.q = static_cast<const uint8_t*>(a.q);
   p.w = a.w;
+  p.q_scale = a.q_scale;
   p.k = static_cast<const uint8_t*>(a.k);
+  p.k_scale = a.k_scale;
   p.q_pos = a.q_pos;
   p.heads = a.heads;
   p.N = a.N;
@@ -394,38 +457,38 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   p.cap = a.cap;
   constexpr int QB = kRowsPerWG / HP;
   const int qblocks = (a.N + QB - 1) / QB;
-  const int splits = a.cand_out ? splits_t<HP, D, true>(a.N, p.L)
-                                : splits_t<HP, D, false>(a.N, p.L, a.key_step > 1 ? 16 : 4);
+  const int splits = a.cand_out ? splits_t<HP, D, F8, true>(a.N, p.L)
+                                : splits_t<HP, D, F8, false>(a.N, p.L, a.key_step > 1 ? 16 : 4);
   p.splits = splits;
   p.keys_per_split = ((p.L + splits - 1) / splits + kKeyTile - 1) / kKeyTile * kKeyTile;
   if (a.cand_out)
-    MISA_LAUNCH(a.kernel_id, (score_prefill_kernel<HP, D, true>), dim3(splits, qblocks),
+    MISA_LAUNCH(a.kernel_id, (score_prefill_kernel<HP, D, F8, true>), dim3(splits, qblocks),
                 dim3(256), 0, st, p);
   else
-    MISA_LAUNCH(a.kernel_id, (score_prefill_kernel<HP, D, false>), dim3(splits, qblocks),
+    MISA_LAUNCH(a.kernel_id, (score_prefill_kernel<HP, D, F8, false>), dim3(splits, qblocks),
                 dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool F8>
 int cand_splits_d(int N, int L, int hp) {
   switch (hp) {
-    case 4: return splits_t<4, D, true>(N, L);
-    case 8: return splits_t<8, D, true>(N, L);
-    case 16: return splits_t<16, D, true>(N, L);
-    case 32: return splits_t<32, D, true>(N, L);
-    default: return splits_t<64, D, true>(N, L);
+    case 4: return splits_t<4, D, F8, true>(N, L);
+    case 8: return splits_t<8, D, F8, true>(N, L);
+    case 16: return splits_t<16, D, F8, true>(N, L);
+    case 32: return splits_t<32, D, F8, true>(N, L);
+    default: return splits_t<64, D, F8, true>(N, L);
   }
 }
 
-template <int D>
+template <int D, bool F8>
 hipError_t launch_d(const PrefillArgs& a, hipStream_t st) {
   switch (hp_of(a.heads ? a.h : a.H_I)) {
-    case 4: return launch_t<4, D>(a, st);
-    case 8: return launch_t<8, D>(a, st);
-    case 16: return launch_t<16, D>(a, st);
-    case 32: return launch_t<32, D>(a, st);
-    default: return launch_t<64, D>(a, st);
+    case 4: return launch_t<4, D, F8>(a, st);
+    case 8: return launch_t<8, D, F8>(a, st);
+    case 16: return launch_t<16, D, F8>(a, st);
+    case 32: return launch_t<32, D, F8>(a, st);
+    default: return launch_t<64, D, F8>(a, st);
   }
 }
 
@@ -433,12 +496,15 @@ hipError_t launch_d(const PrefillArgs& a, hipStream_t st) {
 
 int prefill_rows_per_block(int h_eff) { return kRowsPerWG / hp_of(h_eff); }
 
-int prefill_cand_splits(int N, int L, int h_eff, int d) {
-  return d == 64 ? cand_splits_d<64>(N, L, hp_of(h_eff)) : cand_splits_d<128>(N, L, hp_of(h_eff));
+int prefill_cand_splits(int N, int L, int h_eff, int d, bool fp8) {
+  const int hp = hp_of(h_eff);
+  if (fp8) return cand_splits_d<128, true>(N, L, hp);
+  return d == 64 ? cand_splits_d<64, false>(N, L, hp) : cand_splits_d<128, false>(N, L, hp);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
-  return a.d == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
+  if (a.fp8) return a.d == 128 ? launch_d<128, true>(a, st) : hipErrorInvalidValue;
+  return a.d == 64 ? launch_d<64, false>(a, st) : launch_d<128, false>(a, st);
 }
 
 }  // namespace misa

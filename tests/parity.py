@@ -7,6 +7,15 @@ be swapped only if its oracle value lies within that tolerance of the
 boundary value (the h-th router score, the k-th token score): there the two
 precisions can legitimately order near-equal values differently.  Exact
 ties are not exempt: integer inputs must match bit for bit.
+
+One path is not fp32-accumulated: the e4m3 x e4m3 matrix-core GEMM
+(v_mfma_f32_16x16x128_f8f6f4) that scores fp8 queries against fp8 keys when
+many rows share one key sequence.  Measured on gfx950, that instruction sums
+its 128 products in groups of 8 consecutive K indices; in each group it
+truncates every product toward zero to a multiple of 2^(E - 13), E being the
+group's largest exponent sum e(a) + e(b), and adds the group sums exactly
+enough for fp32.  Scores from that path get the extra per-(row, token)
+tolerance fp8_mfma_error_bound on top of the one above.
 """
 import numpy as np
 
@@ -15,6 +24,43 @@ RTOL, ATOL = 1e-3, 1e-4
 
 def tol(x):
     return ATOL + RTOL * np.abs(x)
+
+
+def _e4m3_fields(codes):
+    """(exponent used for alignment, value) of e4m3 codes; subnormals and zero
+    count with exponent -6 (the most the alignment can see for them)."""
+    c = np.asarray(codes).astype(np.int32)
+    e, m = (c >> 3) & 15, c & 7
+    ebar = np.where(e > 0, e - 7, -6)
+    mag = np.where(e > 0, (8 + m) * np.exp2(e - 10.0), m * 2.0 ** -9)
+    return ebar, np.where(c & 0x80, -mag, mag)
+
+
+def fp8_mfma_error_bound(p, heads=None):
+    """Bound on |score from the e4m3 matrix cores - exact score| for every row
+    of p (heads [N, h], None = all heads) and token s < L_n; 0 past L_n.
+
+    A product of codes with exponent sum t has its lowest bit at 2^(t - 6),
+    so it is exact on the group grid 2^(E - 13) when t >= E - 7; otherwise it
+    loses less than min(|product|, grid).  The dot-product error carries
+    through ReLU (1-Lipschitz) times |w_j| * q_scale[n, j] * k_scale[s]."""
+    out = np.zeros((p.N, p.L))
+    for n in range(p.N):
+        s, Ln = int(p.q_seq[n]), int(p.q_pos[n]) + 1
+        hs = np.arange(p.H_I) if heads is None else np.asarray(heads[n])
+        eq, vq = _e4m3_fields(p.q[n, hs])                      # [h, d]
+        ek, vk = _e4m3_fields(p.k[s, :Ln])                     # [Ln, d]
+        groups = p.d // 8
+        tot = np.zeros(Ln)
+        for i, j in enumerate(hs):
+            t = (eq[i][None, :] + ek).reshape(Ln, groups, 8)
+            E = t.max(axis=2, keepdims=True)
+            grid = np.exp2(E - 13.0)
+            prod = np.abs(vq[i][None, :] * vk).reshape(Ln, groups, 8)
+            lost = np.where(t >= E - 7, 0.0, np.minimum(prod, grid))
+            tot += abs(float(p.w[n, j])) * float(p.q_scale[n, j]) * lost.sum(axis=(1, 2))
+        out[n, :Ln] = tot * p.k_scale[s, :Ln].astype(np.float64)
+    return out
 
 
 def check_heads(gpu_heads, ref_r, h):
@@ -37,12 +83,16 @@ def check_heads(gpu_heads, ref_r, h):
     return differing
 
 
-def check_topk(gpu_idx, gpu_score, ref_scores, topk, lengths, exact=False, cand=None):
+def check_topk(gpu_idx, gpu_score, ref_scores, topk, lengths, exact=False, cand=None,
+               extra=None):
     """GPU top-k (ascending index order, -1 padding) vs oracle score rows.
 
     ref_scores [N, L] holds the oracle score of every token (-inf where not a
     candidate).  `lengths[n]` = number of eligible tokens.  With exact=True
-    the set must be identical and scores bit-equal to the oracle value."""
+    the set must be identical and scores bit-equal to the oracle value.
+    extra [N, L]: additional per-token tolerance (fp8 matrix-core bound); a
+    swap of tokens a and b is then allowed when their oracle scores are
+    within tol + extra[a] + extra[b] of the k-th score."""
     N = gpu_idx.shape[0]
     swapped = 0
     for n in range(N):
@@ -65,9 +115,13 @@ def check_topk(gpu_idx, gpu_score, ref_scores, topk, lengths, exact=False, cand=
             assert np.array_equal(np.sort(ref), sel), f"row {n}: set differs"
         else:
             diff = set(sel.tolist()) ^ set(ref.tolist())
+            xk = 0.0
+            if extra is not None and diff:
+                xk = max(float(extra[n, t]) for t in diff | {int(ref[-1])})
             for t in diff:
-                assert abs(sc[t] - kth) <= tol(kth), (
-                    f"row {n}: token {t} score {sc[t]} vs k-th {kth}")
+                x = 0.0 if extra is None else float(extra[n, t]) + xk
+                assert abs(sc[t] - kth) <= tol(kth) + x, (
+                    f"row {n}: token {t} score {sc[t]} vs k-th {kth} (extra {x})")
             swapped += len(diff) // 2
         if gpu_score is not None:
             gs = np.asarray(gpu_score[n][:K], dtype=np.float64)
@@ -75,7 +129,7 @@ def check_topk(gpu_idx, gpu_score, ref_scores, topk, lengths, exact=False, cand=
                 assert np.array_equal(gs, sc[sel]), f"row {n}: scores differ"
             else:
                 err = np.abs(gs - sc[sel])
-                bad = err > tol(sc[sel])
+                bad = err > tol(sc[sel]) + (0.0 if extra is None else extra[n, sel])
                 assert not bad.any(), (
                     f"row {n}: score {gs[bad][:4]} vs {sc[sel][bad][:4]}")
     return swapped

@@ -42,26 +42,35 @@ def test_status_strings():
 def test_workspace_sizes():
     lib = b.lib()
     ws = lambda *a: lib.misa_workspace_bytes(*a)
+    BF, F8 = b.MISA_BF16, b.MISA_FP8_E4M3
     # decode shape: order keys + 3 histogram levels + per-chunk counts
-    n = ws(b.MISA_OP_SCORE_TOPK, 4, 131072, 128, 64, 128, 2048, 0)
+    n = ws(b.MISA_OP_SCORE_TOPK, BF, 4, 131072, 128, 64, 128, 2048, 0)
     assert n >= 4 * 131072 * 4
-    assert ws(b.MISA_OP_SCORE_TOPK, 4096, 65536, 128, 64, 128, 2048, 0) >= 4096 * 65536 * 4
-    assert ws(b.MISA_OP_RERANK, 4, 131072, 128, 64, 128, 2048, 8192) >= 4 * 8192 * 4
-    assert ws(b.MISA_OP_ROUTE, 4, 131072, 128, 64, 128, 2048, 0) >= 4 * 32 * 64 * 4
-    assert ws(b.MISA_OP_SCORE_TOPK, 0, 100, 128, 64, 128, 10, 0) == 0
-    assert ws(b.MISA_OP_ROUTE, 1, 100, 128, 64, 0, 10, 0) == 0
-    assert ws(7, 1, 100, 128, 64, 1, 10, 0) == 0
+    assert ws(b.MISA_OP_SCORE_TOPK, BF, 4096, 65536, 128, 64, 128, 2048, 0) >= 4096 * 65536 * 4
+    assert ws(b.MISA_OP_RERANK, BF, 4, 131072, 128, 64, 128, 2048, 8192) >= 4 * 8192 * 4
+    assert ws(b.MISA_OP_ROUTE, BF, 4, 131072, 128, 64, 128, 2048, 0) >= 4 * 32 * 64 * 4
+    assert ws(b.MISA_OP_SCORE_TOPK, BF, 0, 100, 128, 64, 128, 10, 0) == 0
+    assert ws(b.MISA_OP_ROUTE, BF, 1, 100, 128, 64, 0, 10, 0) == 0
+    assert ws(7, BF, 1, 100, 128, 64, 1, 10, 0) == 0
+    assert ws(b.MISA_OP_SCORE_TOPK, 3, 4, 100, 128, 64, 1, 10, 0) == 0       # unknown q dtype
+    assert ws(b.MISA_OP_SCORE_TOPK, BF, 4, 100, 96, 64, 1, 10, 0) == 0       # d
+    # fp8 queries: + bf16 copies (2d bytes) and folded weights (4 bytes) per head row
+    for op in (b.MISA_OP_ROUTE, b.MISA_OP_SCORE_TOPK, b.MISA_OP_RERANK):
+        for N, L in ((4, 131072), (4096, 65536)):
+            extra = ws(op, F8, N, L, 128, 64, 128, 2048, 8192) - ws(op, BF, N, L, 128, 64, 128,
+                                                                    2048, 8192)
+            assert N * 64 * (2 * 128 + 4) <= extra < N * 64 * (2 * 128 + 4) + 512
 
 
 FAKE = ctypes.c_void_p(0x100000)        # aligned, never dereferenced: validation fails first
 
 
 def _score(**over):
-    a = dict(q=FAKE, q_dt=1, w=FAKE, k=FAKE, ks=None, k_dt=1, qs=FAKE, qp=FAKE, heads=FAKE,
-             N=4, S=4, L=1000, d=128, H_I=64, h=8, topk=100, idx=FAKE, score=None, ws=FAKE,
-             ws_bytes=1 << 30)
+    a = dict(q=FAKE, q_dt=1, qsc=None, w=FAKE, k=FAKE, ks=None, k_dt=1, qs=FAKE, qp=FAKE,
+             heads=FAKE, N=4, S=4, L=1000, d=128, H_I=64, h=8, topk=100, idx=FAKE, score=None,
+             ws=FAKE, ws_bytes=1 << 30)
     a.update(over)
-    return b.lib().misa_score_topk(a["q"], a["q_dt"], a["w"], a["k"], a["ks"], a["k_dt"],
+    return b.lib().misa_score_topk(a["q"], a["q_dt"], a["qsc"], a["w"], a["k"], a["ks"], a["k_dt"],
                                    a["qs"], a["qp"], a["heads"], a["N"], a["S"], a["L"], a["d"],
                                    a["H_I"], a["h"], a["topk"], a["idx"], a["score"], a["ws"],
                                    a["ws_bytes"], None)
@@ -70,7 +79,10 @@ def _score(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(q=None), 1), (dict(heads=None), 1), (dict(idx=None), 1), (dict(ws=None), 1),
     (dict(k_dt=2), 1),                                   # fp8 keys without scale
-    (dict(q_dt=0), 3), (dict(d=96), 3), (dict(q_dt=2, k_dt=2, ks=FAKE), 3),
+    (dict(q_dt=0), 3), (dict(d=96), 3),
+    (dict(q_dt=2, k_dt=1), 3),                           # fp8 queries need fp8 keys
+    (dict(q_dt=2, k_dt=2, ks=FAKE), 1),                  # fp8 queries without scale
+    (dict(q_dt=2, k_dt=2, ks=FAKE, qsc=FAKE, ws_bytes=4 * 1000 * 4 + 4096), 4),
     (dict(h=0), 2), (dict(h=65), 2), (dict(H_I=65, h=8), 2), (dict(topk=0), 2),
     (dict(N=0), 2), (dict(L=0), 2), (dict(S=0), 2), (dict(N=70000), 2),
     (dict(q=ctypes.c_void_p(0x100004)), 2),              # misaligned
@@ -83,14 +95,24 @@ def test_score_topk_rejects(over, status):
 def test_rerank_and_route_and_pool_reject():
     lib = b.lib()
     # k_prime < topk
-    assert lib.misa_rerank(FAKE, 1, FAKE, FAKE, None, 1, FAKE, FAKE, FAKE, 4, 4, 1000, 128, 64,
-                           100, 200, FAKE, None, FAKE, 1 << 30, None) == 2
+    assert lib.misa_rerank(FAKE, 1, None, FAKE, FAKE, None, 1, FAKE, FAKE, FAKE, 4, 4, 1000, 128,
+                           64, 100, 200, FAKE, None, FAKE, 1 << 30, None) == 2
+    # fp8 queries without their scale
+    assert lib.misa_rerank(FAKE, 2, None, FAKE, FAKE, FAKE, 2, FAKE, FAKE, FAKE, 4, 4, 1000, 128,
+                           64, 200, 100, FAKE, None, FAKE, 1 << 30, None) == 1
+    # fp8 queries: the bf16 copies need room past the rerank's own workspace
+    own = lib.misa_workspace_bytes(b.MISA_OP_RERANK, 1, 4, 1000, 128, 64, 1, 100, 200)
+    assert lib.misa_rerank(FAKE, 2, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, FAKE, 4, 4, 1000, 128,
+                           64, 200, 100, FAKE, None, FAKE, own, None) == 4
     # B out of range
-    assert lib.misa_route_heads(FAKE, 1, FAKE, FAKE, FAKE, None, 1, FAKE, FAKE, 4, 4, 1000, 128,
-                                2048, 64, 8, FAKE, None, FAKE, 1 << 30, None) == 2
+    assert lib.misa_route_heads(FAKE, 1, None, FAKE, FAKE, FAKE, None, 1, FAKE, FAKE, 4, 4, 1000,
+                                128, 2048, 64, 8, FAKE, None, FAKE, 1 << 30, None) == 2
     # workspace too small
-    assert lib.misa_route_heads(FAKE, 1, FAKE, FAKE, FAKE, None, 1, FAKE, FAKE, 4, 4, 100000, 128,
-                                128, 64, 8, FAKE, None, FAKE, 8, None) == 4
+    assert lib.misa_route_heads(FAKE, 1, None, FAKE, FAKE, FAKE, None, 1, FAKE, FAKE, 4, 4,
+                                100000, 128, 128, 64, 8, FAKE, None, FAKE, 8, None) == 4
+    own = lib.misa_workspace_bytes(b.MISA_OP_ROUTE, 1, 4, 100000, 128, 64, 128, 1, 0)
+    assert lib.misa_route_heads(FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, 4, 4,
+                                100000, 128, 128, 64, 8, FAKE, None, FAKE, own, None) == 4
     assert lib.misa_pool_keys(None, None, 1, 1, 100, 128, 16, FAKE, None) == 1
     assert lib.misa_pool_keys(FAKE, None, 2, 1, 100, 128, 16, FAKE, None) == 1
     assert lib.misa_pool_keys(FAKE, None, 5, 1, 100, 128, 16, FAKE, None) == 3

@@ -4,7 +4,9 @@ Inputs are the seeded synthetic workloads; comparisons follow tests/parity.py
 (scores within 1e-3 relative / 1e-4 absolute of the double-precision oracle;
 head and token selections identical except for swaps at near-ties; integer
 inputs bit-exact, ties included).  When the GPU routes a different head at a
-near-tie, the oracle replays the GPU's heads for the scoring check.
+near-tie, the oracle replays the GPU's heads for the scoring check.  Scores
+from the e4m3 matrix-core GEMM also get that instruction's rounding bound
+(parity.fp8_mfma_error_bound).
 """
 import numpy as np
 import pytest
@@ -14,7 +16,7 @@ import oracle
 from long_context_mean_amd import synth
 from long_context_mean_amd.binding import DeviceProblem
 
-from parity import check_heads, check_topk, recall, tol
+from parity import check_heads, check_topk, fp8_mfma_error_bound, recall, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -45,9 +47,16 @@ def misa_gpu(dp, h=None, topk=None):
 def sub_problem(p, rows):
     """The same keys with a subset of query rows (oracle sampling)."""
     rows = np.asarray(rows)
+    qsc = None if p.q_scale is None else p.q_scale[rows].copy()
     return synth.Problem(p.name + "_rows", p.q[rows].copy(), p.q_dt, p.w[rows].copy(), p.k,
                          p.k_dt, p.k_scale, p.q_seq[rows].copy(), p.q_pos[rows].copy(), p.B, p.h,
-                         p.topk, p.k_prime)
+                         p.topk, p.k_prime, q_scale=qsc)
+
+
+def fp8_gemm(p):
+    """Does p take the e4m3 matrix-core GEMM?  (fp8 queries, rows sharing one
+    key sequence, at least 128 rows, d = 128.)"""
+    return p.q_dt == synth.FP8 and p.S == 1 and p.N >= 128 and p.d == 128
 
 
 def check_misa(p, h=None, topk=None, rows=None):
@@ -55,7 +64,7 @@ def check_misa(p, h=None, topk=None, rows=None):
     h = p.h if h is None else h
     topk = p.topk if topk is None else topk
     log(f"[misa] {p.name} N={p.N} L={p.L} d={p.d} H_I={p.H_I} h={h} k={topk} "
-        f"k_dt={synth.DTYPE_NAMES[p.k_dt]}")
+        f"q_dt={synth.DTYPE_NAMES[p.q_dt]} k_dt={synth.DTYPE_NAMES[p.k_dt]}")
     dp = DeviceProblem(p)
     kbar, heads, r, idx, sc = misa_gpu(dp, h, topk)
     ref_kbar = oracle.pool_keys(p)
@@ -66,7 +75,8 @@ def check_misa(p, h=None, topk=None, rows=None):
     assert np.all(np.abs(r[rows] - ref_r) <= tol(ref_r)), "router scores"
     differing = check_heads(heads[rows], ref_r, h)
     ref_sc = oracle.scores(ps, heads[rows])            # replay the GPU's heads
-    swapped = check_topk(idx[rows], sc[rows], ref_sc, topk, ps.visible())
+    extra = fp8_mfma_error_bound(ps, heads[rows]) if fp8_gemm(p) else None
+    swapped = check_topk(idx[rows], sc[rows], ref_sc, topk, ps.visible(), extra=extra)
     log(f"[misa] {p.name}: head rows differing at near-ties {differing}, token swaps {swapped}")
     return dp, heads, idx
 
@@ -364,7 +374,7 @@ def test_prefill_candidate_fallback_bit_exact():
     q = p.q.copy()
     q[::5] = 0
     p = synth.Problem(p.name, q, p.q_dt, p.w, k, p.k_dt, p.k_scale, p.q_seq, p.q_pos, p.B, p.h,
-                      p.topk, p.k_prime)
+                      p.topk, p.k_prime, q_scale=p.q_scale)
     dp = DeviceProblem(p)
     kbar, heads, r, idx, sc = misa_gpu(dp)
     rows = np.r_[0:6, 120:128]
@@ -373,6 +383,145 @@ def test_prefill_candidate_fallback_bit_exact():
     assert np.array_equal(heads[rows], ref_heads)
     check_topk(idx[rows], sc[rows], oracle.scores(ps, ref_heads), p.topk, ps.visible(),
                exact=True)
+
+
+# ---------------------------------------------------------------- fp8 queries and keys
+# e4m3 queries with per-head scales over e4m3 keys with per-token scales.
+# Rows sharing one key sequence with d = 128 run the fp8 MFMA GEMM straight
+# from the codes; every other path scores exact bf16 copies of the query
+# codes with the head scale folded into the weight.
+F8 = synth.FP8
+
+
+def _pow2_key_scales(p, seed):
+    """Power-of-two key scales (1/4 .. 4): scaled integer keys stay exact."""
+    rng = np.random.default_rng(seed)
+    ks = np.ldexp(np.float32(1.0), rng.integers(-2, 3, size=p.k_scale.shape)).astype(np.float32)
+    return synth.Problem(p.name, p.q, p.q_dt, p.w, p.k, p.k_dt, ks, p.q_seq, p.q_pos, p.B, p.h,
+                         p.topk, p.k_prime, q_scale=p.q_scale)
+
+
+@pytest.mark.parametrize("case", [
+    dict(N=3, S=2, L=3000, d=128, H_I=64, h=8, B=128, topk=300),
+    dict(N=2, S=2, L=5000, d=64, H_I=32, h=8, B=64, topk=1000),
+    dict(N=5, S=1, L=9000, d=128, H_I=64, h=12, B=128, topk=2048,
+         q_pos=np.array([0, 1, 127, 128, 8999], np.int32)),
+])
+def test_fp8_queries_decode_parity(case):
+    p = synth.small("q8dec", 81, q_dt=F8, k_dt=F8, **case)
+    check_misa(p)
+
+
+def test_fp8_queries_integer_bit_exact():
+    """Integer codes, power-of-two query and key scales: exact in fp32, so
+    heads, router scores and top-k match the oracle bit for bit (decode
+    path, routed and dense)."""
+    p = synth.integer_problem("q8int", 82, N=3, S=2, L=3000, d=128, H_I=16, h=5, B=1, topk=700,
+                              q_dt=F8, k_dt=F8, q_pos=np.array([2999, 1500, 4], np.int32))
+    p = _pow2_key_scales(p, 82)
+    dp = DeviceProblem(p)
+    kbar, heads, r, idx, sc = misa_gpu(dp)
+    ref_heads, ref_r = oracle.route_heads(p)
+    assert np.array_equal(r.astype(np.float64), ref_r)
+    assert np.array_equal(heads, ref_heads)
+    check_topk(idx, sc, oracle.scores(p, ref_heads), p.topk, p.visible(), exact=True)
+    didx, dsc = dp.dsa()
+    check_topk(np_(didx), np_(dsc), oracle.scores(p, None), p.topk, p.visible(), exact=True)
+
+
+@pytest.mark.parametrize("h,d,H_I", [(8, 128, 64), (4, 128, 16), (3, 128, 16), (32, 128, 64),
+                                     (16, 64, 32)])
+def test_fp8_prefill_gemm_parity(h, d, H_I):
+    """Rows sharing one key sequence: the fp8 GEMM (d = 128) or, for d = 64,
+    the bf16-copy path; unsorted causal positions incl. block edges and 0."""
+    L, N = 6000, 320
+    rng = np.random.default_rng(h * 10 + d + 1)
+    pos = rng.choice(L, N, replace=False).astype(np.int32)
+    pos[:4] = [0, 127, 128, L - 1]
+    p = synth.small("q8pre", 83 + h, N=N, S=1, L=L, d=d, H_I=H_I, h=h, B=128, topk=700,
+                    q_dt=F8, k_dt=F8, q_pos=pos, q_seq=np.zeros(N, np.int32))
+    check_misa(p, rows=np.r_[0:8, 100:104, N - 6:N])
+
+
+def test_fp8_prefill_integer_bit_exact():
+    """Integer codes with power-of-two scales on the fp8 GEMM path: bit-exact."""
+    N, L = 200, 2000
+    pos = np.random.default_rng(19).choice(L, N, replace=False).astype(np.int32)
+    p = synth.integer_problem("q8preint", 84, N=N, S=1, L=L, d=128, H_I=16, h=5, B=1, topk=300,
+                              q_dt=F8, k_dt=F8, q_pos=pos, q_seq=np.zeros(N, np.int32))
+    p = _pow2_key_scales(p, 84)
+    dp = DeviceProblem(p)
+    kbar, heads, r, idx, sc = misa_gpu(dp)
+    rows = np.r_[0:10, 190:200]
+    ps = sub_problem(p, rows)
+    ref_heads, ref_r = oracle.route_heads(ps)
+    assert np.array_equal(heads[rows], ref_heads)
+    check_topk(idx[rows], sc[rows], oracle.scores(ps, ref_heads), p.topk, ps.visible(),
+               exact=True)
+    didx, dsc = dp.dsa()
+    check_topk(np_(didx)[rows], np_(dsc)[rows], oracle.scores(ps, None), p.topk, ps.visible(),
+               exact=True)
+    assert not fp8_mfma_error_bound(ps, None).any()     # integer codes: every product exact
+
+
+@pytest.mark.parametrize("h,H_I", [(8, 64), (16, 64)])
+def test_fp8_prefill_candidate_parity(h, H_I):
+    L, N = 40000, 256
+    rng = np.random.default_rng(5 * h + 3)
+    pos = rng.choice(np.arange(20000, L), N, replace=False).astype(np.int32)
+    pos[:5] = [0, 100, 5000, 32767, L - 1]
+    p = synth.small("q8cand", 85 + h, N=N, S=1, L=L, d=128, H_I=H_I, h=h, B=128, topk=2048,
+                    q_dt=F8, k_dt=F8, q_pos=pos, q_seq=np.zeros(N, np.int32), n_clusters=64)
+    check_misa(p, rows=np.r_[0:8, 128:131, N - 3:N])
+
+
+def test_fp8_prefill_candidate_integer_ties_bit_exact():
+    N, L = 128, 32768
+    pos = np.random.default_rng(21).choice(np.arange(8000, L), N, replace=False).astype(np.int32)
+    pos[0] = L - 1
+    p = synth.integer_problem("q8candint", 86, N=N, S=1, L=L, d=128, H_I=16, h=4, B=64,
+                              topk=2048, q_dt=F8, k_dt=F8, q_pos=pos, q_seq=np.zeros(N, np.int32))
+    p = _pow2_key_scales(p, 86)
+    dp = DeviceProblem(p)
+    kbar, heads, r, idx, sc = misa_gpu(dp)
+    rows = np.r_[0:6, 120:128]
+    ps = sub_problem(p, rows)
+    ref_heads, ref_r = oracle.route_heads(ps)
+    assert np.array_equal(heads[rows], ref_heads)
+    check_topk(idx[rows], sc[rows], oracle.scores(ps, ref_heads), p.topk, ps.visible(),
+               exact=True)
+
+
+def test_fp8_prefill_dense_and_dagger_parity():
+    """All 64 heads on the fp8 GEMM (dense DSA), then MISA-dagger's rerank of a
+    routed candidate set with fp8 queries."""
+    L, N = 5000, 256
+    pos = np.random.default_rng(23).choice(L, N, replace=False).astype(np.int32)
+    p = synth.small("q8dd", 87, N=N, S=1, L=L, d=128, H_I=64, h=8, topk=300, k_prime=1200,
+                    q_dt=F8, k_dt=F8, q_pos=pos, q_seq=np.zeros(N, np.int32))
+    dp = DeviceProblem(p)
+    idx, sc = dp.dsa()
+    rows = np.r_[0:6, 250:256]
+    ps = sub_problem(p, rows)
+    check_topk(np_(idx)[rows], np_(sc)[rows], oracle.scores(ps, None), p.topk, ps.visible(),
+               extra=fp8_mfma_error_bound(ps, None))
+    kbar = dp.pool()
+    heads, _ = dp.route(kbar)
+    cand, _ = dp.score_topk(heads, p.k_prime)
+    gidx, gsc = dp.rerank(cand)
+    cand_np = np_(cand)
+    full = oracle.scores(ps, None)
+    ref = np.full_like(full, -np.inf)
+    for i, n in enumerate(rows):
+        c = cand_np[n][cand_np[n] >= 0]
+        ref[i, c] = full[i, c]
+    check_topk(np_(gidx)[rows], np_(gsc)[rows], ref, p.topk,
+               (cand_np[rows] >= 0).sum(1), cand=cand_np[rows])
+
+
+def test_c3f8_prefill_chunk_sampled_rows():
+    p = synth.make("c3f8")
+    check_misa(p, rows=np.r_[0:3, 127:130, 2047:2049, 4093:4096])
 
 
 # ---------------------------------------------------------------- edge cases and fallback paths

@@ -39,6 +39,13 @@
  *    1 <= topk <= 65536; 1 <= N <= 65535; 1 <= S <= 65535; 1 <= L <= 2^27.
  *  - Index-score: I(s) = sum over heads j of w[n,j] * ReLU(q[n,j,:] . key_s),
  *    accumulated in fp32 from exact bf16 (or fp8-dequantised) products.
+ *    Exception: fp8 queries on the many-rows path (S = 1, N >= 128,
+ *    d = 128) are scored by the e4m3 matrix cores
+ *    (v_mfma_f32_16x16x128_f8f6f4), which sum each group of 8 consecutive
+ *    products after truncating every product toward zero to a multiple of
+ *    2^(E - 13), E the group's largest exponent sum e(q) + e(k) of the codes
+ *    (measured on gfx950).  Those scores carry that rounding on top of fp32;
+ *    fp8 queries on every other path are scored exactly like bf16 ones.
  *  - Top-k outputs idx [N, topk] int32 and score [N, topk] float32 hold the
  *    min(topk, L_n) tokens first under (score desc, token index asc), listed
  *    in ASCENDING TOKEN INDEX order, followed by -1 / -inf padding.

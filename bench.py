@@ -232,6 +232,35 @@ class Replicas:
         self.rerank(i)
 
 
+class PagedServing:
+    """A decode serving step on a paged key cache (pages of 64 tokens): the
+    newest token of every sequence completes its last block, so the step pools
+    that one block into the cached table (misa_pool_update), then routes and
+    scores.  REPLICAS paged copies of the keys rotate like Replicas."""
+
+    def __init__(self, p, torch, binding, h, page_size=64):
+        from long_context_mean_amd.binding import DeviceProblem
+        self.p, self.b, self.h = p, binding, h
+        self.dps = [DeviceProblem(p, page_size=page_size, page_seed=i) for i in range(REPLICAS)]
+        self.kbar = [dp.pool() for dp in self.dps]
+        dev = self.dps[0].q.device
+        self.len_old = torch.full((p.S,), p.L - 1, dtype=torch.int32, device=dev)
+        self.len_new = torch.full((p.S,), p.L, dtype=torch.int32, device=dev)
+        self.heads = torch.empty((p.N, h), dtype=torch.int32, device=dev)
+        self.r = torch.empty((p.N, p.H_I), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((p.N, p.topk), dtype=torch.int32, device=dev)
+        self.ws_route = binding.workspace(binding.MISA_OP_ROUTE, p.N, p.L, p.d, p.H_I, p.B,
+                                          device=dev)
+        self.ws_score = binding.workspace(binding.MISA_OP_SCORE_TOPK, p.N, p.L, p.d, p.H_I,
+                                          topk=p.topk, device=dev)
+
+    def step(self, i):
+        dp = self.dps[i]
+        dp.pool_update(self.len_old, self.len_new, 1, self.kbar[i])
+        dp.route(self.kbar[i], self.h, heads=self.heads, head_score=self.r, ws=self.ws_route)
+        dp.score_topk(self.heads, idx=self.idx, score=None, ws=self.ws_score, want_score=False)
+
+
 def timed(torch, fn, steps, warmup):
     for s in range(warmup):
         fn(s % REPLICAS)
@@ -521,6 +550,18 @@ def main():
         extra["needle_recall_dense"] = round(float(np.mean(
             [np.isin(p.needles[n, :, 0], dense_idx[n]).mean() for n in range(p.N)])), 4)
         del rep
+        torch.cuda.empty_cache()
+        log("[bench] paged decode serving step (incremental pool + route + score)")
+        srv = PagedServing(p, torch, binding, h)
+        ms_s = timed(torch, srv.step, args.steps, args.warmup)
+        _, kts, _ = kernel_times(torch, binding, srv.step, max(3, args.steps // 2), 1, 16)
+        srv.step(0)
+        torch.cuda.synchronize()
+        extra["paged_serving_step_ms"] = round(ms_s, 4)
+        extra["paged_serving_tokens_per_s"] = tokens / (ms_s * 1e-3)
+        extra["paged_serving_kernel_ms"] = {k: round(v, 5) for k, v in kts.items()}
+        extra["paged_serving_recall_vs_dense"] = round(rec(srv.idx.cpu().numpy(), dense_idx), 4)
+        del srv
         torch.cuda.empty_cache()
         log("[bench] fp8-key MISA-dagger (c5 shape)")
         p5 = synth.make("c5")

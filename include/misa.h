@@ -30,6 +30,19 @@
  *      k       [S, L, d]    dtype k_dt (MISA_F32, MISA_BF16 or MISA_FP8_E4M3)
  *      k_scale [S, L]       float32 per-token scale, required iff k_dt is fp8
  *                           (key value = scale * e4m3 value; scale > 0)
+ *    Paged keys (every entry point that reads k takes block_table, page_size
+ *    right after k_dt): page_size 0 means the contiguous layout above and
+ *    block_table must be NULL.  Otherwise keys live in a page pool
+ *      k       [P, page_size, d], k_scale [P, page_size] (fp8)
+ *      block_table [S, ceil(L / page_size)] int32: physical page of each
+ *                  logical page of each sequence; token t of sequence s is
+ *                  row t % page_size of page block_table[s][t / page_size]
+ *    with page_size a power of two in [16, 65536] and L the per-sequence
+ *    capacity in tokens.  Entries are read only for pages that hold tokens a
+ *    call can see (t <= q_pos[n], or the tokens being pooled); they must be
+ *    valid page numbers of the pool (device-resident: not checked).  Many
+ *    rows over one paged sequence take the per-row scoring kernels (the
+ *    prefill GEMM reads contiguous keys only).
  *      q_seq   [N]  int32   key sequence of query row n, 0 <= q_seq[n] < S
  *      q_pos   [N]  int32   position of query row n, 0 <= q_pos[n] < L;
  *                           row n sees keys 0..q_pos[n] (L_n = q_pos[n] + 1)
@@ -90,8 +103,27 @@ typedef enum {
  * may be partial.  The table is causal only for rows that see all L keys;
  * misa_route_heads handles each row's own partial block.
  */
-int32_t misa_pool_keys(const void* k, const float* k_scale, int32_t k_dt, int32_t S, int32_t L,
+int32_t misa_pool_keys(const void* k, const float* k_scale, int32_t k_dt,
+                       const int32_t* block_table, int32_t page_size, int32_t S, int32_t L,
                        int32_t d, int32_t B, float* kbar, void* stream);
+
+/*
+ * Incremental block pooling for a decode loop that appends tokens to its key
+ * cache (same page, "Methodology" item 1: the router works on block means, at
+ * O(H_I M) per query).  The router reads only the blocks a row sees
+ * completely and computes the row's partial last block from k itself, so a
+ * cached table needs only complete blocks.  For every sequence s this writes
+ * kbar[s, b] (as misa_pool_keys would) for exactly the blocks b completed by
+ * the tokens len_old[s] .. len_new[s]-1, i.e. those with
+ * len_old[s] < (b+1)*B <= len_new[s]; other rows of kbar are not touched.
+ * len_old, len_new: [S] int32 device arrays with 0 <= len_old <= len_new <= L;
+ * max_new >= len_new[s] - len_old[s] for every s (host bound that sizes the
+ * launch; 0 = nothing to do).  Cost: O(B d) per completed block.
+ */
+int32_t misa_pool_update(const void* k, const float* k_scale, int32_t k_dt,
+                         const int32_t* block_table, int32_t page_size, int32_t S, int32_t L,
+                         int32_t d, int32_t B, const int32_t* len_old, const int32_t* len_new,
+                         int32_t max_new, float* kbar, void* stream);
 
 /*
  * Head router (same page, "Methodology" item 1: per-head affinities against
@@ -108,10 +140,10 @@ int32_t misa_pool_keys(const void* k, const float* k_scale, int32_t k_dt, int32_
  */
 int32_t misa_route_heads(const void* q, int32_t q_dt, const float* q_scale, const float* w,
                          const float* kbar, const void* k, const float* k_scale, int32_t k_dt,
-                         const int32_t* q_seq, const int32_t* q_pos, int32_t N, int32_t S,
-                         int32_t L, int32_t d, int32_t B, int32_t H_I, int32_t h,
-                         int32_t* heads, float* head_score, void* ws, size_t ws_bytes,
-                         void* stream);
+                         const int32_t* block_table, int32_t page_size, const int32_t* q_seq,
+                         const int32_t* q_pos, int32_t N, int32_t S, int32_t L, int32_t d,
+                         int32_t B, int32_t H_I, int32_t h, int32_t* heads, float* head_score,
+                         void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Routed token scoring + top-k (same page, "Methodology" item 2: only the h
@@ -124,7 +156,8 @@ int32_t misa_route_heads(const void* q, int32_t q_dt, const float* q_scale, cons
  * Workspace: misa_workspace_bytes(MISA_OP_SCORE_TOPK, ...).
  */
 int32_t misa_score_topk(const void* q, int32_t q_dt, const float* q_scale, const float* w,
-                        const void* k, const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+                        const void* k, const float* k_scale, int32_t k_dt,
+                        const int32_t* block_table, int32_t page_size, const int32_t* q_seq,
                         const int32_t* q_pos, const int32_t* heads, int32_t N, int32_t S,
                         int32_t L, int32_t d, int32_t H_I, int32_t h, int32_t topk,
                         int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream);
@@ -135,7 +168,8 @@ int32_t misa_score_topk(const void* q, int32_t q_dt, const float* q_scale, const
  * misa_score_topk with all H_I heads.
  */
 int32_t dsa_score_topk(const void* q, int32_t q_dt, const float* q_scale, const float* w,
-                       const void* k, const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+                       const void* k, const float* k_scale, int32_t k_dt,
+                       const int32_t* block_table, int32_t page_size, const int32_t* q_seq,
                        const int32_t* q_pos, int32_t N, int32_t S, int32_t L, int32_t d,
                        int32_t H_I, int32_t topk, int32_t* idx, float* score, void* ws,
                        size_t ws_bytes, void* stream);
@@ -153,10 +187,11 @@ int32_t dsa_score_topk(const void* q, int32_t q_dt, const float* q_scale, const 
  * Workspace: misa_workspace_bytes(MISA_OP_RERANK, ...).
  */
 int32_t misa_rerank(const void* q, int32_t q_dt, const float* q_scale, const float* w,
-                    const void* k, const float* k_scale, int32_t k_dt, const int32_t* q_seq,
-                    const int32_t* q_pos, const int32_t* cand, int32_t N, int32_t S, int32_t L,
-                    int32_t d, int32_t H_I, int32_t k_prime, int32_t topk, int32_t* idx,
-                    float* score, void* ws, size_t ws_bytes, void* stream);
+                    const void* k, const float* k_scale, int32_t k_dt, const int32_t* block_table,
+                    int32_t page_size, const int32_t* q_seq, const int32_t* q_pos,
+                    const int32_t* cand, int32_t N, int32_t S, int32_t L, int32_t d, int32_t H_I,
+                    int32_t k_prime, int32_t topk, int32_t* idx, float* score, void* ws,
+                    size_t ws_bytes, void* stream);
 
 /*
  * Workspace bytes for `op` at these sizes with queries of dtype q_dt (0 for

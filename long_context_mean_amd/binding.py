@@ -25,7 +25,7 @@ MISA_F32, MISA_BF16, MISA_FP8_E4M3 = 0, 1, 2
 MISA_OP_ROUTE, MISA_OP_SCORE_TOPK, MISA_OP_RERANK = 0, 1, 2
 MISA_OK = 0
 
-EXPORTED = ("misa_pool_keys", "misa_route_heads", "misa_score_topk", "dsa_score_topk",
+EXPORTED = ("misa_pool_keys", "misa_pool_update", "misa_route_heads", "misa_score_topk", "dsa_score_topk",
             "misa_rerank", "misa_workspace_bytes", "misa_status_string",
             "misa_last_hip_error", "misa_profile_begin", "misa_profile_end", "misa_kernel_name")
 
@@ -56,12 +56,15 @@ def lib():
             f"{LIB_PATH} is not built; run `python -m long_context_mean_amd.build_lib`")
     L = ctypes.CDLL(LIB_PATH)
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
-    L.misa_pool_keys.argtypes = [P, P, I32, I32, I32, I32, I32, P, P]
-    # q q_dt q_scale w [kbar] k k_scale k_dt q_seq q_pos [heads | cand] sizes... outputs ws ws_bytes stream
-    L.misa_route_heads.argtypes = [P, I32, P, P, P, P, P, I32, P, P] + [I32] * 7 + [P, P, P, SZ, P]
-    L.misa_score_topk.argtypes = [P, I32, P, P, P, P, I32, P, P, P] + [I32] * 7 + [P, P, P, SZ, P]
-    L.dsa_score_topk.argtypes = [P, I32, P, P, P, P, I32, P, P] + [I32] * 6 + [P, P, P, SZ, P]
-    L.misa_rerank.argtypes = [P, I32, P, P, P, P, I32, P, P, P] + [I32] * 7 + [P, P, P, SZ, P]
+    # k k_scale k_dt block_table page_size
+    KEYS = [P, P, I32, P, I32]
+    L.misa_pool_keys.argtypes = KEYS + [I32] * 4 + [P, P]
+    L.misa_pool_update.argtypes = KEYS + [I32] * 4 + [P, P, I32, P, P]
+    # q q_dt q_scale w [kbar] <keys> q_seq q_pos [heads | cand] sizes... outputs ws ws_bytes stream
+    L.misa_route_heads.argtypes = [P, I32, P, P, P] + KEYS + [P, P] + [I32] * 7 + [P, P, P, SZ, P]
+    L.misa_score_topk.argtypes = [P, I32, P, P] + KEYS + [P, P, P] + [I32] * 7 + [P, P, P, SZ, P]
+    L.dsa_score_topk.argtypes = [P, I32, P, P] + KEYS + [P, P] + [I32] * 6 + [P, P, P, SZ, P]
+    L.misa_rerank.argtypes = [P, I32, P, P] + KEYS + [P, P, P] + [I32] * 7 + [P, P, P, SZ, P]
     L.misa_workspace_bytes.argtypes = [I32] * 9
     L.misa_workspace_bytes.restype = ctypes.c_size_t
     L.misa_status_string.argtypes = [I32]
@@ -71,7 +74,7 @@ def lib():
     L.misa_profile_end.argtypes = [P, P, I32]
     L.misa_kernel_name.argtypes = [I32]
     L.misa_kernel_name.restype = ctypes.c_char_p
-    for f in ("misa_pool_keys", "misa_route_heads", "misa_score_topk", "dsa_score_topk",
+    for f in ("misa_pool_keys", "misa_pool_update", "misa_route_heads", "misa_score_topk", "dsa_score_topk",
               "misa_rerank", "misa_last_hip_error", "misa_profile_begin", "misa_profile_end"):
         getattr(L, f).restype = ctypes.c_int32
     _lib = L
@@ -119,6 +122,30 @@ def _check(fn, status):
         raise MisaError(fn, status)
 
 
+def _keys(k, k_scale, block_table, page_size, L=None, d_q=None):
+    """(S, L, d) of the key storage and its pointer arguments (k, k_scale,
+    k_dt, block_table, page_size).  Contiguous keys are [S, L, d]; paged keys
+    are a page pool [P, page_size, d] with block_table [S, pages per sequence]
+    (L defaults to pages per sequence * page_size)."""
+    if d_q is not None and k.shape[-1] != d_q:
+        raise ValueError(f"q has d={d_q} but k has d={k.shape[-1]}")
+    if block_table is None:
+        if page_size:
+            raise ValueError("page_size given without a block table")
+        S, L, d = k.shape
+        return S, L, d, [_ptr(k, "k", _KEYS), _ptr(k_scale, "k_scale", _F32, (S, L)),
+                         _dtype_code(k), None, 0]
+    P, ps, d = k.shape
+    if ps != page_size:
+        raise ValueError(f"k pages hold {ps} tokens, page_size is {page_size}")
+    S, mp = block_table.shape
+    L = mp * page_size if L is None else L
+    if -(-L // page_size) != mp:
+        raise ValueError(f"block table has {mp} pages per sequence, L={L} needs {-(-L // page_size)}")
+    return S, L, d, [_ptr(k, "k", _KEYS), _ptr(k_scale, "k_scale", _F32, (P, page_size)),
+                     _dtype_code(k), _ptr(block_table, "block_table", _I32, (S, mp)), page_size]
+
+
 def workspace(op: int, N: int, L: int, d: int, H_I: int, B: int = 1, topk: int = 1,
               k_prime: int = 0, q_dt: int = MISA_BF16, device="cuda") -> torch.Tensor:
     n = misa_workspace_bytes(op, q_dt, N, L, d, H_I, B, topk, k_prime)
@@ -134,23 +161,34 @@ def misa_workspace_bytes(op, q_dt, N, L, d, H_I, B=1, topk=1, k_prime=0) -> int:
 
 
 def misa_pool_keys(k: torch.Tensor, B: int, k_scale: Optional[torch.Tensor] = None,
-                   kbar: Optional[torch.Tensor] = None) -> torch.Tensor:
-    S, L, d = k.shape
+                   kbar: Optional[torch.Tensor] = None, block_table=None, page_size=0,
+                   L=None) -> torch.Tensor:
+    S, L, d, kargs = _keys(k, k_scale, block_table, page_size, L)
     M = -(-L // B)
     if kbar is None:
         kbar = torch.empty((S, M, d), dtype=torch.float32, device=k.device)
     _check("misa_pool_keys", lib().misa_pool_keys(
-        _ptr(k, "k", _KEYS), _ptr(k_scale, "k_scale", _F32, (S, L)), _dtype_code(k), S, L, d, B,
-        _ptr(kbar, "kbar", _F32, (S, M, d)), _stream(k)))
+        *kargs, S, L, d, B, _ptr(kbar, "kbar", _F32, (S, M, d)), _stream(k)))
+    return kbar
+
+
+def misa_pool_update(k: torch.Tensor, B: int, len_old: torch.Tensor, len_new: torch.Tensor,
+                     max_new: int, kbar: torch.Tensor, k_scale=None, block_table=None,
+                     page_size=0, L=None) -> torch.Tensor:
+    S, L, d, kargs = _keys(k, k_scale, block_table, page_size, L)
+    M = -(-L // B)
+    _check("misa_pool_update", lib().misa_pool_update(
+        *kargs, S, L, d, B, _ptr(len_old, "len_old", _I32, (S,)),
+        _ptr(len_new, "len_new", _I32, (S,)), max_new, _ptr(kbar, "kbar", _F32, (S, M, d)),
+        _stream(k)))
     return kbar
 
 
 def misa_route_heads(q, w, kbar, k, q_seq, q_pos, B: int, h: int, k_scale=None, heads=None,
-                     head_score=None, ws=None, want_scores=True, q_scale=None):
+                     head_score=None, ws=None, want_scores=True, q_scale=None, block_table=None,
+                     page_size=0, L=None):
     N, H_I, d = q.shape
-    S, L, _ = k.shape
-    if k.shape[2] != d:
-        raise ValueError(f"q has d={d} but k has d={k.shape[2]}")
+    S, L, _, kargs = _keys(k, k_scale, block_table, page_size, L, d_q=d)
     if heads is None:
         heads = torch.empty((N, h), dtype=torch.int32, device=q.device)
     if head_score is None and want_scores:
@@ -159,21 +197,18 @@ def misa_route_heads(q, w, kbar, k, q_seq, q_pos, B: int, h: int, k_scale=None, 
         ws = workspace(MISA_OP_ROUTE, N, L, d, H_I, B, q_dt=_dtype_code(q), device=q.device)
     _check("misa_route_heads", lib().misa_route_heads(
         _ptr(q, "q", _KEYS), _dtype_code(q), _ptr(q_scale, "q_scale", _F32, (N, H_I)),
-        _ptr(w, "w", _F32, (N, H_I)),
-        _ptr(kbar, "kbar", _F32, (S, -(-L // B), d)), _ptr(k, "k", _KEYS),
-        _ptr(k_scale, "k_scale", _F32, (S, L)), _dtype_code(k), _ptr(q_seq, "q_seq", _I32, (N,)),
-        _ptr(q_pos, "q_pos", _I32, (N,)), N, S, L, d, B, H_I, h,
+        _ptr(w, "w", _F32, (N, H_I)), _ptr(kbar, "kbar", _F32, (S, -(-L // B), d)), *kargs,
+        _ptr(q_seq, "q_seq", _I32, (N,)), _ptr(q_pos, "q_pos", _I32, (N,)), N, S, L, d, B, H_I, h,
         _ptr(heads, "heads", _I32, (N, h)), _ptr(head_score, "head_score", _F32, (N, H_I)),
         _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(q)))
     return heads, head_score
 
 
 def misa_score_topk(q, w, k, q_seq, q_pos, heads, topk: int, k_scale=None, idx=None, score=None,
-                    ws=None, want_score=True, q_scale=None):
+                    ws=None, want_score=True, q_scale=None, block_table=None, page_size=0,
+                    L=None):
     N, H_I, d = q.shape
-    S, L, _ = k.shape
-    if k.shape[2] != d:
-        raise ValueError(f"q has d={d} but k has d={k.shape[2]}")
+    S, L, _, kargs = _keys(k, k_scale, block_table, page_size, L, d_q=d)
     h = heads.shape[1]
     if idx is None:
         idx = torch.empty((N, topk), dtype=torch.int32, device=q.device)
@@ -184,8 +219,7 @@ def misa_score_topk(q, w, k, q_seq, q_pos, heads, topk: int, k_scale=None, idx=N
                        device=q.device)
     _check("misa_score_topk", lib().misa_score_topk(
         _ptr(q, "q", _KEYS), _dtype_code(q), _ptr(q_scale, "q_scale", _F32, (N, H_I)),
-        _ptr(w, "w", _F32, (N, H_I)), _ptr(k, "k", _KEYS),
-        _ptr(k_scale, "k_scale", _F32, (S, L)), _dtype_code(k), _ptr(q_seq, "q_seq", _I32, (N,)),
+        _ptr(w, "w", _F32, (N, H_I)), *kargs, _ptr(q_seq, "q_seq", _I32, (N,)),
         _ptr(q_pos, "q_pos", _I32, (N,)), _ptr(heads, "heads", _I32, (N, h)), N, S, L, d, H_I, h,
         topk, _ptr(idx, "idx", _I32, (N, topk)), _ptr(score, "score", _F32, (N, topk)),
         _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(q)))
@@ -193,11 +227,10 @@ def misa_score_topk(q, w, k, q_seq, q_pos, heads, topk: int, k_scale=None, idx=N
 
 
 def dsa_score_topk(q, w, k, q_seq, q_pos, topk: int, k_scale=None, idx=None, score=None,
-                   ws=None, want_score=True, q_scale=None):
+                   ws=None, want_score=True, q_scale=None, block_table=None, page_size=0,
+                   L=None):
     N, H_I, d = q.shape
-    S, L, _ = k.shape
-    if k.shape[2] != d:
-        raise ValueError(f"q has d={d} but k has d={k.shape[2]}")
+    S, L, _, kargs = _keys(k, k_scale, block_table, page_size, L, d_q=d)
     if idx is None:
         idx = torch.empty((N, topk), dtype=torch.int32, device=q.device)
     if score is None and want_score:
@@ -207,8 +240,7 @@ def dsa_score_topk(q, w, k, q_seq, q_pos, topk: int, k_scale=None, idx=None, sco
                        device=q.device)
     _check("dsa_score_topk", lib().dsa_score_topk(
         _ptr(q, "q", _KEYS), _dtype_code(q), _ptr(q_scale, "q_scale", _F32, (N, H_I)),
-        _ptr(w, "w", _F32, (N, H_I)), _ptr(k, "k", _KEYS),
-        _ptr(k_scale, "k_scale", _F32, (S, L)), _dtype_code(k), _ptr(q_seq, "q_seq", _I32, (N,)),
+        _ptr(w, "w", _F32, (N, H_I)), *kargs, _ptr(q_seq, "q_seq", _I32, (N,)),
         _ptr(q_pos, "q_pos", _I32, (N,)), N, S, L, d, H_I, topk,
         _ptr(idx, "idx", _I32, (N, topk)), _ptr(score, "score", _F32, (N, topk)), _ptr(ws, "ws"),
         ws.numel() * ws.element_size(),
@@ -217,11 +249,9 @@ def dsa_score_topk(q, w, k, q_seq, q_pos, topk: int, k_scale=None, idx=None, sco
 
 
 def misa_rerank(q, w, k, q_seq, q_pos, cand, topk: int, k_scale=None, idx=None, score=None,
-                ws=None, want_score=True, q_scale=None):
+                ws=None, want_score=True, q_scale=None, block_table=None, page_size=0, L=None):
     N, H_I, d = q.shape
-    S, L, _ = k.shape
-    if k.shape[2] != d:
-        raise ValueError(f"q has d={d} but k has d={k.shape[2]}")
+    S, L, _, kargs = _keys(k, k_scale, block_table, page_size, L, d_q=d)
     k_prime = cand.shape[1]
     if idx is None:
         idx = torch.empty((N, topk), dtype=torch.int32, device=q.device)
@@ -232,8 +262,7 @@ def misa_rerank(q, w, k, q_seq, q_pos, cand, topk: int, k_scale=None, idx=None, 
                        q_dt=_dtype_code(q), device=q.device)
     _check("misa_rerank", lib().misa_rerank(
         _ptr(q, "q", _KEYS), _dtype_code(q), _ptr(q_scale, "q_scale", _F32, (N, H_I)),
-        _ptr(w, "w", _F32, (N, H_I)), _ptr(k, "k", _KEYS),
-        _ptr(k_scale, "k_scale", _F32, (S, L)), _dtype_code(k), _ptr(q_seq, "q_seq", _I32, (N,)),
+        _ptr(w, "w", _F32, (N, H_I)), *kargs, _ptr(q_seq, "q_seq", _I32, (N,)),
         _ptr(q_pos, "q_pos", _I32, (N,)), _ptr(cand, "cand", _I32, (N, k_prime)), N, S, L, d,
         H_I, k_prime, topk, _ptr(idx, "idx", _I32, (N, topk)),
         _ptr(score, "score", _F32, (N, topk)), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
@@ -258,47 +287,62 @@ def misa_profile_end(max_records: int):
 # ---------------------------------------------------------------- problems on the device
 class DeviceProblem:
     """A synth.Problem's arrays as device tensors (q/k bf16 as torch.bfloat16,
-    e4m3 codes as torch.uint8)."""
+    e4m3 codes as torch.uint8).  With page_size > 0 the keys are stored as a
+    paged cache (synth.to_pages: seeded page order, spare pages) and every
+    call passes the block table."""
 
-    def __init__(self, p: synth.Problem, device="cuda"):
+    def __init__(self, p: synth.Problem, device="cuda", page_size: int = 0, page_seed: int = 0):
         self.p = p
 
         def up(a, dtype=None):
-            t = torch.from_numpy(a)
+            t = torch.from_numpy(np.ascontiguousarray(a))
             if dtype is not None:
                 t = t.view(dtype)
             return t.to(device)
 
+        def keys(a):
+            return up(a.view(np.int16), torch.bfloat16) if p.k_dt == synth.BF16 else up(a)
+
         self.q = up(p.q.view(np.int16), torch.bfloat16) if p.q_dt == synth.BF16 else up(p.q)
-        if p.k_dt == synth.BF16:
-            self.k = up(p.k.view(np.int16), torch.bfloat16)
+        self.block_table, self.page_size = None, 0
+        if page_size:
+            pages, spages, table = synth.to_pages(p.k, p.k_scale, page_size, page_seed)
+            self.k = keys(pages)
+            self.k_scale = up(spages) if spages is not None else None
+            self.block_table, self.page_size = up(table), page_size
         else:
-            self.k = up(p.k)
+            self.k = keys(p.k)
+            self.k_scale = up(p.k_scale) if p.k_scale is not None else None
+        self.kv = dict(k_scale=self.k_scale, block_table=self.block_table,
+                       page_size=self.page_size, L=p.L if page_size else None)
         self.w = up(p.w)
-        self.k_scale = up(p.k_scale) if p.k_scale is not None else None
         self.q_scale = up(p.q_scale) if p.q_scale is not None else None
         self.q_seq = up(p.q_seq)
         self.q_pos = up(p.q_pos)
 
     def pool(self, B=None):
-        return misa_pool_keys(self.k, self.p.B if B is None else B, self.k_scale)
+        return misa_pool_keys(self.k, self.p.B if B is None else B, **self.kv)
+
+    def pool_update(self, len_old, len_new, max_new, kbar, B=None):
+        return misa_pool_update(self.k, self.p.B if B is None else B, len_old, len_new, max_new,
+                                kbar, **self.kv)
 
     def route(self, kbar, h=None, **kw):
         return misa_route_heads(self.q, self.w, kbar, self.k, self.q_seq, self.q_pos, self.p.B,
-                                self.p.h if h is None else h, k_scale=self.k_scale,
-                                q_scale=self.q_scale, **kw)
+                                self.p.h if h is None else h, q_scale=self.q_scale,
+                                **self.kv, **kw)
 
     def score_topk(self, heads, topk=None, **kw):
         return misa_score_topk(self.q, self.w, self.k, self.q_seq, self.q_pos, heads,
-                               self.p.topk if topk is None else topk, k_scale=self.k_scale,
-                               q_scale=self.q_scale, **kw)
+                               self.p.topk if topk is None else topk, q_scale=self.q_scale,
+                               **self.kv, **kw)
 
     def dsa(self, topk=None, **kw):
         return dsa_score_topk(self.q, self.w, self.k, self.q_seq, self.q_pos,
-                              self.p.topk if topk is None else topk, k_scale=self.k_scale,
-                              q_scale=self.q_scale, **kw)
+                              self.p.topk if topk is None else topk, q_scale=self.q_scale,
+                              **self.kv, **kw)
 
     def rerank(self, cand, topk=None, **kw):
         return misa_rerank(self.q, self.w, self.k, self.q_seq, self.q_pos, cand,
-                           self.p.topk if topk is None else topk, k_scale=self.k_scale,
-                           q_scale=self.q_scale, **kw)
+                           self.p.topk if topk is None else topk, q_scale=self.q_scale,
+                           **self.kv, **kw)

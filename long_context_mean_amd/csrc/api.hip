@@ -53,6 +53,31 @@ int32_t check_sizes(int32_t N, int32_t S, int32_t L, int32_t d, int32_t H_I) {
   return MISA_OK;
 }
 
+// Key storage: page_size 0 = contiguous [S, L, d] (block_table must be NULL);
+// otherwise pages of page_size tokens (a power of two, 16 .. 65536) listed
+// per sequence by block_table [S, ceil(L / page_size)].
+int32_t key_index(const int32_t* block_table, int32_t page_size, int32_t L, misa::KeyIndex& ki) {
+  ki = misa::KeyIndex{nullptr, L, 0, 0};
+  if (page_size == 0) return block_table ? MISA_ERR_SHAPE : MISA_OK;
+  if (!block_table) return MISA_ERR_NULL;
+  if (page_size < 16 || page_size > 65536 || (page_size & (page_size - 1))) return MISA_ERR_SHAPE;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  ki = misa::KeyIndex{block_table, L, shift, (L + page_size - 1) >> shift};
+  return MISA_OK;
+}
+
+int32_t check_pool(const void* k, const float* k_scale, int32_t k_dt, int32_t S, int32_t L,
+                   int32_t d, int32_t B, const float* kbar) {
+  if (!k || !kbar) return MISA_ERR_NULL;
+  if (k_dt != MISA_F32 && k_dt != MISA_BF16 && k_dt != MISA_FP8_E4M3) return MISA_ERR_UNSUPPORTED;
+  if (k_dt == MISA_FP8_E4M3 && !k_scale) return MISA_ERR_NULL;
+  if (d != 64 && d != 128) return MISA_ERR_UNSUPPORTED;
+  if (S < 1 || S > kMaxN || L < 1 || L > kMaxL || B < 1 || B > 1024) return MISA_ERR_SHAPE;
+  if (!aligned16(k)) return MISA_ERR_SHAPE;
+  return MISA_OK;
+}
+
 // ---------------------------------------------------------------- workspace layouts
 struct TopkLayout {
   bool one_row = false;
@@ -167,7 +192,8 @@ struct Profiler {
 Profiler g_prof;
 
 int32_t score_topk_impl(const void* q, int32_t q_dt, const float* q_scale, const float* w,
-                        const void* k, const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+                        const void* k, const float* k_scale, int32_t k_dt,
+                        const int32_t* block_table, int32_t page_size, const int32_t* q_seq,
                         const int32_t* q_pos, const int32_t* heads, int32_t N, int32_t S,
                         int32_t L, int32_t d, int32_t H_I, int32_t h, int32_t topk,
                         int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream) {
@@ -175,6 +201,8 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* q_scale, const
   int32_t rc = check_dtypes(q_dt, k_dt, q_scale, k_scale);
   if (rc) return rc;
   if ((rc = check_sizes(N, S, L, d, H_I))) return rc;
+  misa::KeyIndex ki;
+  if ((rc = key_index(block_table, page_size, L, ki))) return rc;
   if (h < 1 || h > H_I || topk < 1 || topk > kMaxTopk) return MISA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k)) return MISA_ERR_SHAPE;
   const bool f8 = q_dt == MISA_FP8_E4M3;
@@ -189,9 +217,9 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* q_scale, const
   hipError_t e = hipSuccess;
   if (hist) e = misa::launch_clear(hist, static_cast<size_t>(N) * misa::kHistWords, st);
   if (e != hipSuccess) return hip_status(e);
-  // many rows over one sequence: GEMM over the gathered head rows (bf16, or
-  // e4m3 straight from the codes)
-  const bool gemm = S == 1 && lay.one_row && N >= kOneRowMinN &&
+  // many rows over one contiguous sequence: GEMM over the gathered head rows
+  // (bf16, or e4m3 straight from the codes)
+  const bool gemm = S == 1 && !block_table && lay.one_row && N >= kOneRowMinN &&
                     ((q_dt == MISA_BF16 && k_dt == MISA_BF16) || (f8 && d == 128));
   if (f8 && !gemm) {
     e = prep_fp8_queries(q, q_dt, w, q_scale, N, H_I, d, base + q8_off, st);
@@ -247,7 +275,7 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* q_scale, const
     e = misa::launch_prefill(prefill_args(u, lay.u_stride), st);
   } else {
     misa::ScoreArgs sa{q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, heads, nullptr,
-                       N, S, L, d, H_I, h, 0, u, lay.u_stride, hist};
+                       N, S, L, d, H_I, h, 0, u, lay.u_stride, hist, ki};
     e = misa::launch_score(sa, st);
   }
   if (e != hipSuccess) return hip_status(e);
@@ -308,28 +336,44 @@ size_t misa_workspace_bytes(int32_t op, int32_t q_dt, int32_t N, int32_t L, int3
   }
 }
 
-int32_t misa_pool_keys(const void* k, const float* k_scale, int32_t k_dt, int32_t S, int32_t L,
+int32_t misa_pool_keys(const void* k, const float* k_scale, int32_t k_dt,
+                       const int32_t* block_table, int32_t page_size, int32_t S, int32_t L,
                        int32_t d, int32_t B, float* kbar, void* stream) {
-  if (!k || !kbar) return MISA_ERR_NULL;
-  if (k_dt != MISA_F32 && k_dt != MISA_BF16 && k_dt != MISA_FP8_E4M3) return MISA_ERR_UNSUPPORTED;
-  if (k_dt == MISA_FP8_E4M3 && !k_scale) return MISA_ERR_NULL;
-  if (d != 64 && d != 128) return MISA_ERR_UNSUPPORTED;
-  if (S < 1 || S > kMaxN || L < 1 || L > kMaxL || B < 1 || B > 1024) return MISA_ERR_SHAPE;
-  if (!aligned16(k)) return MISA_ERR_SHAPE;
-  misa::PoolArgs a{k, k_scale, k_dt, S, L, d, B, kbar};
+  int32_t rc = check_pool(k, k_scale, k_dt, S, L, d, B, kbar);
+  if (rc) return rc;
+  misa::KeyIndex ki;
+  if ((rc = key_index(block_table, page_size, L, ki))) return rc;
+  misa::PoolArgs a{k, k_scale, k_dt, S, L, d, B, kbar, ki};
+  return hip_status(misa::launch_pool(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t misa_pool_update(const void* k, const float* k_scale, int32_t k_dt,
+                         const int32_t* block_table, int32_t page_size, int32_t S, int32_t L,
+                         int32_t d, int32_t B, const int32_t* len_old, const int32_t* len_new,
+                         int32_t max_new, float* kbar, void* stream) {
+  int32_t rc = check_pool(k, k_scale, k_dt, S, L, d, B, kbar);
+  if (rc) return rc;
+  if (!len_old || !len_new) return MISA_ERR_NULL;
+  if (max_new < 0 || max_new > L) return MISA_ERR_SHAPE;
+  misa::KeyIndex ki;
+  if ((rc = key_index(block_table, page_size, L, ki))) return rc;
+  if (max_new == 0) return MISA_OK;
+  misa::PoolArgs a{k, k_scale, k_dt, S, L, d, B, kbar, ki, len_old, len_new, max_new};
   return hip_status(misa::launch_pool(a, static_cast<hipStream_t>(stream)));
 }
 
 int32_t misa_route_heads(const void* q, int32_t q_dt, const float* q_scale, const float* w,
                          const float* kbar, const void* k, const float* k_scale, int32_t k_dt,
-                         const int32_t* q_seq, const int32_t* q_pos, int32_t N, int32_t S,
-                         int32_t L, int32_t d, int32_t B, int32_t H_I, int32_t h,
-                         int32_t* heads, float* head_score, void* ws, size_t ws_bytes,
-                         void* stream) {
+                         const int32_t* block_table, int32_t page_size, const int32_t* q_seq,
+                         const int32_t* q_pos, int32_t N, int32_t S, int32_t L, int32_t d,
+                         int32_t B, int32_t H_I, int32_t h, int32_t* heads, float* head_score,
+                         void* ws, size_t ws_bytes, void* stream) {
   if (!q || !w || !kbar || !k || !q_seq || !q_pos || !heads) return MISA_ERR_NULL;
   int32_t rc = check_dtypes(q_dt, k_dt, q_scale, k_scale);
   if (rc) return rc;
   if ((rc = check_sizes(N, S, L, d, H_I))) return rc;
+  misa::KeyIndex ki;
+  if ((rc = key_index(block_table, page_size, L, ki))) return rc;
   if (B < 1 || B > 1024 || h < 1 || h > H_I) return MISA_ERR_SHAPE;
   const bool f8 = q_dt == MISA_FP8_E4M3;
   if (f8 && !aligned16(q)) return MISA_ERR_SHAPE;
@@ -344,38 +388,45 @@ int32_t misa_route_heads(const void* q, int32_t q_dt, const float* q_scale, cons
   }
   misa::RouteArgs a{q, q_dt, w, kbar, k, k_scale, k_dt, q_seq, q_pos, N, S, L, d, B, H_I, h,
                     heads, head_score, reinterpret_cast<float*>(wsb), route_chunks(L, B),
-                    reinterpret_cast<uint16_t*>(wsb + route_partial_bytes(N, L, B, H_I))};
+                    reinterpret_cast<uint16_t*>(wsb + route_partial_bytes(N, L, B, H_I)), ki};
   return hip_status(misa::launch_route(a, static_cast<hipStream_t>(stream)));
 }
 
 int32_t misa_score_topk(const void* q, int32_t q_dt, const float* q_scale, const float* w,
-                        const void* k, const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+                        const void* k, const float* k_scale, int32_t k_dt,
+                        const int32_t* block_table, int32_t page_size, const int32_t* q_seq,
                         const int32_t* q_pos, const int32_t* heads, int32_t N, int32_t S,
                         int32_t L, int32_t d, int32_t H_I, int32_t h, int32_t topk,
                         int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream) {
   if (!heads) return MISA_ERR_NULL;
-  return score_topk_impl(q, q_dt, q_scale, w, k, k_scale, k_dt, q_seq, q_pos, heads, N, S, L, d,
-                         H_I, h, topk, idx, score, ws, ws_bytes, stream);
+  return score_topk_impl(q, q_dt, q_scale, w, k, k_scale, k_dt, block_table, page_size, q_seq,
+                         q_pos, heads, N, S, L, d, H_I, h, topk, idx, score, ws, ws_bytes,
+                         stream);
 }
 
 int32_t dsa_score_topk(const void* q, int32_t q_dt, const float* q_scale, const float* w,
-                       const void* k, const float* k_scale, int32_t k_dt, const int32_t* q_seq,
+                       const void* k, const float* k_scale, int32_t k_dt,
+                       const int32_t* block_table, int32_t page_size, const int32_t* q_seq,
                        const int32_t* q_pos, int32_t N, int32_t S, int32_t L, int32_t d,
                        int32_t H_I, int32_t topk, int32_t* idx, float* score, void* ws,
                        size_t ws_bytes, void* stream) {
-  return score_topk_impl(q, q_dt, q_scale, w, k, k_scale, k_dt, q_seq, q_pos, nullptr, N, S, L,
-                         d, H_I, H_I, topk, idx, score, ws, ws_bytes, stream);
+  return score_topk_impl(q, q_dt, q_scale, w, k, k_scale, k_dt, block_table, page_size, q_seq,
+                         q_pos, nullptr, N, S, L, d, H_I, H_I, topk, idx, score, ws, ws_bytes,
+                         stream);
 }
 
 int32_t misa_rerank(const void* q, int32_t q_dt, const float* q_scale, const float* w,
-                    const void* k, const float* k_scale, int32_t k_dt, const int32_t* q_seq,
-                    const int32_t* q_pos, const int32_t* cand, int32_t N, int32_t S, int32_t L,
-                    int32_t d, int32_t H_I, int32_t k_prime, int32_t topk, int32_t* idx,
-                    float* score, void* ws, size_t ws_bytes, void* stream) {
+                    const void* k, const float* k_scale, int32_t k_dt, const int32_t* block_table,
+                    int32_t page_size, const int32_t* q_seq, const int32_t* q_pos,
+                    const int32_t* cand, int32_t N, int32_t S, int32_t L, int32_t d, int32_t H_I,
+                    int32_t k_prime, int32_t topk, int32_t* idx, float* score, void* ws,
+                    size_t ws_bytes, void* stream) {
   if (!q || !w || !k || !q_seq || !q_pos || !cand || !idx) return MISA_ERR_NULL;
   int32_t rc = check_dtypes(q_dt, k_dt, q_scale, k_scale);
   if (rc) return rc;
   if ((rc = check_sizes(N, S, L, d, H_I))) return rc;
+  misa::KeyIndex ki;
+  if ((rc = key_index(block_table, page_size, L, ki))) return rc;
   if (topk < 1 || k_prime < topk || k_prime > kMaxTopk) return MISA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k)) return MISA_ERR_SHAPE;
   const bool f8 = q_dt == MISA_FP8_E4M3;
@@ -391,7 +442,7 @@ int32_t misa_rerank(const void* q, int32_t q_dt, const float* q_scale, const flo
   const int u_stride = topk_layout(kOneRowMinN, k_prime).u_stride;
   uint32_t* u = static_cast<uint32_t*>(ws);
   misa::ScoreArgs sa{q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, nullptr, cand,
-                     N, S, L, d, H_I, H_I, k_prime, u, u_stride, nullptr};
+                     N, S, L, d, H_I, H_I, k_prime, u, u_stride, nullptr, ki};
   hipError_t e = misa::launch_score(sa, st);
   if (e != hipSuccess) return hip_status(e);
   misa::TopkArgs ta{u, u_stride, nullptr, k_prime, N, topk, true, nullptr,
@@ -442,7 +493,7 @@ const char* misa_kernel_name(int32_t kernel_id) {
       "score_mfma_kernel", "score_f32_kernel",     "score_prefill_kernel",
       "topk_collect_kernel", "topk_final_kernel",   "topk_row_kernel",
       "score_prefill_sample", "score_prefill_full", "topk_tau_kernel", "topk_cand_kernel",
-      "route_split_kernel", "q8_prep_kernel"};
+      "route_split_kernel", "q8_prep_kernel", "pool_update_kernel"};
   if (kernel_id < 0 || kernel_id >= misa::K_COUNT_IDS) return "unknown";
   return names[kernel_id];
 }

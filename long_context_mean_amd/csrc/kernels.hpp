@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "common.hpp"
+
 namespace misa {
 
 enum KernelId : int {
@@ -25,6 +27,7 @@ enum KernelId : int {
   K_TOPK_CAND,
   K_ROUTE_SPLIT,
   K_Q8_PREP,
+  K_POOL_UPDATE,
   K_COUNT_IDS
 };
 
@@ -49,6 +52,13 @@ struct PoolArgs {
   const float* k_scale;
   int k_dt, S, L, d, B;
   float* kbar;
+  KeyIndex kidx;
+  // incremental mode (len_new != NULL): for each sequence s, only the blocks
+  // completed by tokens len_old[s] .. len_new[s]-1 are written; at most
+  // max_new tokens were appended to any sequence
+  const int32_t* len_old = nullptr;
+  const int32_t* len_new = nullptr;
+  int max_new = 0;
 };
 hipError_t launch_pool(const PoolArgs& a, hipStream_t st);
 
@@ -69,6 +79,7 @@ struct RouteArgs {
   float* partial;        // workspace [N, nchunks, H_I]
   int nchunks;           // chunks of full blocks per row
   uint16_t* kb_split;    // workspace [2, M, d] bf16: pooled keys as hi + lo (one-sequence GEMM)
+  KeyIndex kidx;         // where the keys of the partial block live
 };
 int route_blocks_per_chunk();
 bool route_uses_mfma(const RouteArgs& a);
@@ -91,6 +102,7 @@ struct ScoreArgs {
   uint32_t* u;              // [N, u_stride] order keys
   int u_stride;
   uint32_t* hist0;          // [N, kHistWords] level-0 histogram (NULL = skip)
+  KeyIndex kidx;
 };
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
 

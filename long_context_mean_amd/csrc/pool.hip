@@ -7,6 +7,14 @@
 // 16-byte pieces of a row, so a wavefront reads whole rows), accumulate in
 // fp32 registers, and reduce the row groups through LDS.  The pass is one
 // HBM read of the keys: bandwidth bound.
+//
+// Incremental mode (a decode loop appending tokens to its key cache): the
+// router only reads blocks a row sees completely and computes a row's
+// partial last block from the keys themselves, so the cached table needs
+// only the complete blocks.  Each call pools exactly the blocks that the
+// newly appended tokens complete (one workgroup per candidate block; those
+// that complete nothing exit at once): O(B d) work per B appended tokens.
+// Keys may live in a paged cache (KeyIndex).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -16,7 +24,9 @@ namespace {
 template <int KT, int D>
 __global__ __launch_bounds__(256) void pool_kernel(const uint8_t* __restrict__ k,
                                                    const float* __restrict__ k_scale, int L,
-                                                   int B, float* __restrict__ kbar) {
+                                                   int B, float* __restrict__ kbar, KeyIndex ki,
+                                                   const int32_t* __restrict__ len_old,
+                                                   const int32_t* __restrict__ len_new) {
   constexpr int EB = KeyBytes<KT>::value;
   constexpr int ROW_BYTES = D * EB;
   constexpr int CPR = ROW_BYTES / 16;          // 16-byte pieces per row
@@ -24,11 +34,18 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint8_t* __restrict__ k
   constexpr int RG = 256 / CPR;                // row groups
   __shared__ float part[RG][D + 1];
 
-  const int b = blockIdx.x, s = blockIdx.y, M = gridDim.x;
+  const int s = blockIdx.y, M = (L + B - 1) / B;
+  int b = blockIdx.x, t1;
+  if (len_new) {
+    // the (blockIdx.x)-th block at or after the one holding token len_old[s]
+    b += len_old[s] / B;
+    t1 = (b + 1) * B;
+    if (t1 > len_new[s] || (b + 1) * B <= len_old[s]) return;   // not completed by this call
+  } else {
+    t1 = (b * B + B < L) ? b * B + B : L;
+  }
   const int t0 = b * B;
-  const int t1 = (t0 + B < L) ? t0 + B : L;
   const int c = threadIdx.x % CPR, g = threadIdx.x / CPR;
-  const size_t seq_row0 = static_cast<size_t>(s) * L;
 
   float acc[EPC];
 #pragma unroll
@@ -42,9 +59,10 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint8_t* __restrict__ k
     for (int r = 0; r < U; ++r) {
       const int tt = t + r * RG;
       const int tc = tt < t1 ? tt : t;           // stay in bounds; masked below
-      x[r] = *reinterpret_cast<const uint4*>(k + (seq_row0 + tc) * ROW_BYTES + c * 16);
+      const size_t row = ki.row(s, tc);
+      x[r] = *reinterpret_cast<const uint4*>(k + row * ROW_BYTES + c * 16);
       sc[r] = 1.f;
-      if constexpr (KT == DT_E4M3) sc[r] = k_scale[seq_row0 + tc];
+      if constexpr (KT == DT_E4M3) sc[r] = k_scale[row];
     }
 #pragma unroll
     for (int r = 0; r < U; ++r) {
@@ -74,9 +92,18 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint8_t* __restrict__ k
 
 template <int KT, int D>
 hipError_t launch_pool_t(const PoolArgs& a, hipStream_t st) {
-  const int M = (a.L + a.B - 1) / a.B;
-  MISA_LAUNCH(K_POOL, (pool_kernel<KT, D>), dim3(M, a.S), dim3(256), 0, st,
-              static_cast<const uint8_t*>(a.k), a.k_scale, a.L, a.B, a.kbar);
+  if (a.len_new) {
+    // blocks that max_new appended tokens can complete: floor(max_new / B) + 1
+    const int nb = a.max_new / a.B + 1;
+    MISA_LAUNCH(K_POOL_UPDATE, (pool_kernel<KT, D>), dim3(nb, a.S), dim3(256), 0, st,
+                static_cast<const uint8_t*>(a.k), a.k_scale, a.L, a.B, a.kbar, a.kidx,
+                a.len_old, a.len_new);
+  } else {
+    const int M = (a.L + a.B - 1) / a.B;
+    MISA_LAUNCH(K_POOL, (pool_kernel<KT, D>), dim3(M, a.S), dim3(256), 0, st,
+                static_cast<const uint8_t*>(a.k), a.k_scale, a.L, a.B, a.kbar, a.kidx,
+                nullptr, nullptr);
+  }
   return hipGetLastError();
 }
 

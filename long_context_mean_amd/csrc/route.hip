@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     const float* __restrict__ k_scale, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int L, int B, int H_I, int h, int nchunks,
     const float* __restrict__ partial, int32_t* __restrict__ heads,
-    float* __restrict__ head_score) {
+    float* __restrict__ head_score, KeyIndex ki) {
   constexpr int EB = KeyBytes<KT>::value;
   constexpr int PIECES = D * EB / 16;          // 16-byte pieces per key row
   constexpr int EPP = 16 / EB;                 // elements per piece
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     for (int e = 0; e < EPP; ++e) acc[e] = 0.f;
     const uint8_t* kb = static_cast<const uint8_t*>(k);
     for (int t = Mf * B + rg; t < Ln; t += RG) {
-      const size_t row = static_cast<size_t>(s) * L + t;
+      const size_t row = ki.row(s, t);
       const uint4 x = *reinterpret_cast<const uint4*>(kb + row * (D * EB) + piece * 16);
       float v[EPP];
       unpack16<KT>(x, v);
@@ -470,7 +470,7 @@ hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
   }
   MISA_LAUNCH(K_ROUTE_SELECT, (route_select_kernel<QT, KT, D>), dim3(a.N), dim3(256), 0, st,
               a.q, a.w, a.k, a.k_scale, a.q_seq, a.q_pos, a.L, a.B, a.H_I, a.h, nchunks,
-              a.partial, a.heads, a.head_score);
+              a.partial, a.heads, a.head_score, a.kidx);
   return hipGetLastError();
 }
 

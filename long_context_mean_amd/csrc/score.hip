@@ -22,6 +22,11 @@
 //
 // score_f32_kernel (fp32 keys): one thread per key, plain FMAs (fp32 inputs
 // have no exact low-precision MFMA form).
+//
+// Keys may live in a paged cache (KeyIndex): a tile's 16 consecutive tokens
+// always share a page (pages hold a multiple of 16 tokens), so the streaming
+// kernel looks the page up once per tile through the scalar cache; candidate
+// gathers look each token's page up per lane.
 #include <cstdlib>
 
 #include "common.hpp"
@@ -46,6 +51,7 @@ struct ScoreParams {
   int u_stride;
   uint32_t* hist0;
   int tiles_per_wave;
+  KeyIndex ki;
 };
 
 template <int KT, int D>
@@ -104,34 +110,50 @@ using RawGroup = u32x4_t[U][KeyLayout<KT, D>::NLOAD];
 
 // Issues the key loads of U tiles (16 elements each) starting at element e0.
 // Without a candidate list the key address depends only on the element
-// index, so no load waits on another load; bit t of the result is set when
-// tile t's element is a valid token.
+// index (and, for paged keys, on one scalar page lookup per tile), so no load
+// waits on another vector load; bit t of the result is set when tile t's
+// element is a valid token.  Elements past the row end read a valid row of
+// the sequence and are masked.
 template <int KT, int D, int U, bool CAND>
 __device__ __forceinline__ uint32_t issue_group(RawGroup<KT, D, U>& raw, float* sc, int tile0,
                                                 int tstride, int lane, int c, int len,
-                                                const int32_t* crow, const uint8_t* kseq,
-                                                const float* sseq) {
+                                                const int32_t* crow, const uint8_t* kbase,
+                                                const float* sbase, const KeyIndex& ki, int s) {
   using LY = KeyLayout<KT, D>;
   const int rsub = lane / LY::LANES_PER_ROW, q = lane % LY::LANES_PER_ROW;
   uint32_t valid = 0;
 #pragma unroll
   for (int t = 0; t < U; ++t) {
     const int te = (tile0 + t * tstride) * 16;
+    size_t rb = 0;                                     // row of the tile's first token
+    if constexpr (!CAND) rb = ki.row_uniform(s, te < len ? te : len - 1);
     // flat: load i of lane l reads 16 bytes of row i*ROWS_PER_LOAD + l/LANES_PER_ROW
 #pragma unroll
     for (int i = 0; i < LY::NLOAD; ++i) {
       const int e = te + i * LY::ROWS_PER_LOAD + rsub;
-      int tok = -1;
-      if (e < len) tok = CAND ? crow[e] : e;
-      const int tt = tok >= 0 ? tok : 0;
-      raw[t][i] = *reinterpret_cast<const u32x4_t*>(kseq + static_cast<size_t>(tt) * LY::ROW +
-                                                     16 * q);
+      size_t row;
+      if constexpr (CAND) {
+        const int tok = e < len ? crow[e] : -1;
+        row = ki.row(s, tok >= 0 ? tok : 0);
+      } else {
+        row = e < len ? rb + (e - te) : rb;
+      }
+      raw[t][i] = *reinterpret_cast<const u32x4_t*>(kbase + row * LY::ROW + 16 * q);
     }
     const int e = te + c;
     int tok = -1;
     if (e < len) tok = CAND ? crow[e] : e;
     valid |= tok >= 0 ? (1u << t) : 0u;
-    sc[t] = (KT == DT_E4M3) ? sseq[tok >= 0 ? tok : 0] : 1.f;
+    if constexpr (KT == DT_E4M3) {
+      size_t srow;
+      if constexpr (CAND)
+        srow = ki.row(s, tok >= 0 ? tok : 0);
+      else
+        srow = e < len ? rb + c : rb;
+      sc[t] = sbase[srow];
+    } else {
+      sc[t] = 1.f;
+    }
   }
   return valid;
 }
@@ -202,14 +224,15 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
   const int ntiles = (len + 15) / 16;
   const int tstride = gridDim.x * 4;                 // wavefronts per row
   if (static_cast<int>(blockIdx.x) * 4 >= ntiles) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int g = lane >> 4, c = lane & 15;
   const bool do_hist = p.hist0 != nullptr;
 
   const int s = p.q_seq[n];
-  const uint8_t* kseq = p.k + static_cast<size_t>(s) * p.L * LY::ROW;
+  const uint8_t* kseq = p.k;                           // rows addressed through p.ki
   uint8_t* tile = tiles[wave];
-  const float* sseq = (KT == DT_E4M3) ? p.k_scale + static_cast<size_t>(s) * p.L : nullptr;
+  const float* sseq = p.k_scale;
   const int32_t* crow = CAND ? p.cand + static_cast<size_t>(n) * p.ncols : nullptr;
   uint32_t* urow = p.u + static_cast<size_t>(n) * p.u_stride;
   const int wtile = blockIdx.x * 4 + wave;            // this wavefront's first tile
@@ -220,7 +243,8 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
   float sa[U], sb[U];
   uint32_t va = 0, vb = 0;
   if (wtiles > 0)
-    va = issue_group<KT, D, U, CAND>(ra, sa, wtile, tstride, lane, c, len, crow, kseq, sseq);
+    va = issue_group<KT, D, U, CAND>(ra, sa, wtile, tstride, lane, c, len, crow, kseq, sseq,
+                                     p.ki, s);
 
   if (do_hist) {
     for (int b = threadIdx.x; b < kBins0; b += 256) lh[b] = 0u;
@@ -264,11 +288,11 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
     int left = (wtiles + U - 1) / U;                   // groups left, current included
     while (left >= 3) {
       vb = issue_group<KT, D, U, CAND>(rb, sb, t0 + gstep, tstride, lane, c, len, crow, kseq,
-                                       sseq);
+                                       sseq, p.ki, s);
       score_group<KT, NT, D, U>(ra, sa, va, t0, tstride, tile, lane, a, wv, g, c, len, urow,
                                 lh, do_hist);
       va = issue_group<KT, D, U, CAND>(ra, sa, t0 + 2 * gstep, tstride, lane, c, len, crow,
-                                       kseq, sseq);
+                                       kseq, sseq, p.ki, s);
       score_group<KT, NT, D, U>(rb, sb, vb, t0 + gstep, tstride, tile, lane, a, wv, g, c, len,
                                 urow, lh, do_hist);
       t0 += 2 * gstep;
@@ -276,7 +300,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
     }
     if (left == 2) {
       vb = issue_group<KT, D, U, CAND>(rb, sb, t0 + gstep, tstride, lane, c, len, crow, kseq,
-                                       sseq);
+                                       sseq, p.ki, s);
       score_group<KT, NT, D, U>(ra, sa, va, t0, tstride, tile, lane, a, wv, g, c, len, urow,
                                 lh, do_hist);
       score_group<KT, NT, D, U>(rb, sb, vb, t0 + gstep, tstride, tile, lane, a, wv, g, c, len,
@@ -301,7 +325,8 @@ __global__ __launch_bounds__(256) void score_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ w, const float* __restrict__ k,
     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ heads, const int32_t* __restrict__ cand, int L, int H_I,
-    int nrows, int ncols, uint32_t* __restrict__ u, int u_stride, uint32_t* __restrict__ hist0) {
+    int nrows, int ncols, uint32_t* __restrict__ u, int u_stride, uint32_t* __restrict__ hist0,
+    KeyIndex ki) {
   __shared__ float q_lds[64][D];
   __shared__ float w_lds[64];
   __shared__ uint32_t lh[kBins0];
@@ -327,8 +352,7 @@ __global__ __launch_bounds__(256) void score_f32_kernel(
     uint32_t key = 0u;
     if (tok >= 0) {
       float kr[D];
-      const float4* kp =
-          reinterpret_cast<const float4*>(k + (static_cast<size_t>(q_seq[n]) * L + tok) * D);
+      const float4* kp = reinterpret_cast<const float4*>(k + ki.row(q_seq[n], tok) * D);
 #pragma unroll
       for (int i = 0; i < D / 4; ++i) {
         const float4 x = kp[i];
@@ -379,6 +403,7 @@ hipError_t launch_mfma(const ScoreArgs& a, hipStream_t st, int tiles_per_wave) {
   p.u_stride = a.u_stride;
   p.hist0 = a.hist0;
   p.tiles_per_wave = tiles_per_wave;
+  p.ki = a.kidx;
   const int maxlen = a.cand ? a.ncols : a.L;
   const int per_wg = 4 * tiles_per_wave * 16;
   const int nchunks = (maxlen + per_wg - 1) / per_wg;
@@ -416,12 +441,12 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
       MISA_LAUNCH(K_SCORE_F32, score_f32_kernel<64>, grid, dim3(256), 0, st,
                   static_cast<const float*>(a.q), a.w, static_cast<const float*>(a.k), a.q_seq,
                   a.q_pos, a.heads, a.cand, a.L, a.H_I, nrows, a.ncols, a.u, a.u_stride,
-                  a.hist0);
+                  a.hist0, a.kidx);
     else
       MISA_LAUNCH(K_SCORE_F32, score_f32_kernel<128>, grid, dim3(256), 0, st,
                   static_cast<const float*>(a.q), a.w, static_cast<const float*>(a.k), a.q_seq,
                   a.q_pos, a.heads, a.cand, a.L, a.H_I, nrows, a.ncols, a.u, a.u_stride,
-                  a.hist0);
+                  a.hist0, a.kidx);
     return hipGetLastError();
   }
   // tiles (of 16 keys) per wavefront; short candidate lists use smaller

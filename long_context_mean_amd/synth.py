@@ -95,6 +95,34 @@ def e4m3_codes_to_f32(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
     return (v * np.asarray(scale, np.float32)[..., None]).astype(np.float32)
 
 
+def to_pages(k: np.ndarray, k_scale: Optional[np.ndarray], page_size: int, seed: int,
+             spare: int = 3):
+    """Paged storage of keys [S, L, d] (and fp8 scales [S, L]): a pool of
+    pages [P, page_size, d] holding the sequences' logical pages in a seeded
+    random order, `spare` unused pages, and the block table
+    [S, ceil(L / page_size)] of physical page numbers."""
+    S, L = k.shape[:2]
+    mp = -(-L // page_size)
+    P = S * mp + spare
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(P)[:S * mp].reshape(S, mp).astype(np.int32)
+    # unused rows hold NaN patterns (e4m3 0x7F, bf16 0x7FC0, fp32 NaN): a read
+    # of the wrong page shows up in every result
+    poison = {np.dtype(np.uint8): 0x7F, np.dtype(np.uint16): 0x7FC0}.get(k.dtype, np.nan)
+    pages = np.empty((P, page_size) + k.shape[2:], dtype=k.dtype)
+    pages[...] = np.array(poison).astype(k.dtype)
+    spages = None
+    if k_scale is not None:
+        spages = np.full((P, page_size), np.float32(1.0), dtype=np.float32)
+    for s in range(S):
+        for j in range(mp):
+            t0, t1 = j * page_size, min(L, (j + 1) * page_size)
+            pages[perm[s, j], :t1 - t0] = k[s, t0:t1]
+            if spages is not None:
+                spages[perm[s, j], :t1 - t0] = k_scale[s, t0:t1]
+    return pages, spages, perm
+
+
 # --------------------------------------------------------------------------
 # problem container
 # --------------------------------------------------------------------------

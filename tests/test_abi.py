@@ -66,11 +66,12 @@ FAKE = ctypes.c_void_p(0x100000)        # aligned, never dereferenced: validatio
 
 
 def _score(**over):
-    a = dict(q=FAKE, q_dt=1, qsc=None, w=FAKE, k=FAKE, ks=None, k_dt=1, qs=FAKE, qp=FAKE,
-             heads=FAKE, N=4, S=4, L=1000, d=128, H_I=64, h=8, topk=100, idx=FAKE, score=None,
-             ws=FAKE, ws_bytes=1 << 30)
+    a = dict(q=FAKE, q_dt=1, qsc=None, w=FAKE, k=FAKE, ks=None, k_dt=1, bt=None, ps=0, qs=FAKE,
+             qp=FAKE, heads=FAKE, N=4, S=4, L=1000, d=128, H_I=64, h=8, topk=100, idx=FAKE,
+             score=None, ws=FAKE, ws_bytes=1 << 30)
     a.update(over)
     return b.lib().misa_score_topk(a["q"], a["q_dt"], a["qsc"], a["w"], a["k"], a["ks"], a["k_dt"],
+                                   a["bt"], a["ps"],
                                    a["qs"], a["qp"], a["heads"], a["N"], a["S"], a["L"], a["d"],
                                    a["H_I"], a["h"], a["topk"], a["idx"], a["score"], a["ws"],
                                    a["ws_bytes"], None)
@@ -87,6 +88,9 @@ def _score(**over):
     (dict(N=0), 2), (dict(L=0), 2), (dict(S=0), 2), (dict(N=70000), 2),
     (dict(q=ctypes.c_void_p(0x100004)), 2),              # misaligned
     (dict(ws_bytes=16), 4),
+    (dict(ps=64), 1),                                    # paged keys without a block table
+    (dict(bt=FAKE), 2),                                  # block table with page_size 0
+    (dict(bt=FAKE, ps=48), 2), (dict(bt=FAKE, ps=8), 2), (dict(bt=FAKE, ps=1 << 17), 2),
 ])
 def test_score_topk_rejects(over, status):
     assert _score(**over) == status
@@ -95,28 +99,44 @@ def test_score_topk_rejects(over, status):
 def test_rerank_and_route_and_pool_reject():
     lib = b.lib()
     # k_prime < topk
-    assert lib.misa_rerank(FAKE, 1, None, FAKE, FAKE, None, 1, FAKE, FAKE, FAKE, 4, 4, 1000, 128,
+    KV = (FAKE, None, 1, None, 0)            # contiguous bf16 keys
+    assert lib.misa_rerank(FAKE, 1, None, FAKE, *KV, FAKE, FAKE, FAKE, 4, 4, 1000, 128,
                            64, 100, 200, FAKE, None, FAKE, 1 << 30, None) == 2
     # fp8 queries without their scale
-    assert lib.misa_rerank(FAKE, 2, None, FAKE, FAKE, FAKE, 2, FAKE, FAKE, FAKE, 4, 4, 1000, 128,
+    KV8 = (FAKE, FAKE, 2, None, 0)
+    assert lib.misa_rerank(FAKE, 2, None, FAKE, *KV8, FAKE, FAKE, FAKE, 4, 4, 1000, 128,
                            64, 200, 100, FAKE, None, FAKE, 1 << 30, None) == 1
     # fp8 queries: the bf16 copies need room past the rerank's own workspace
     own = lib.misa_workspace_bytes(b.MISA_OP_RERANK, 1, 4, 1000, 128, 64, 1, 100, 200)
-    assert lib.misa_rerank(FAKE, 2, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, FAKE, 4, 4, 1000, 128,
+    assert lib.misa_rerank(FAKE, 2, FAKE, FAKE, *KV8, FAKE, FAKE, FAKE, 4, 4, 1000, 128,
                            64, 200, 100, FAKE, None, FAKE, own, None) == 4
+    # paged keys: page size not a power of two
+    assert lib.misa_rerank(FAKE, 1, None, FAKE, FAKE, None, 1, FAKE, 100, FAKE, FAKE, FAKE, 4, 4,
+                           1000, 128, 64, 200, 100, FAKE, None, FAKE, 1 << 30, None) == 2
     # B out of range
-    assert lib.misa_route_heads(FAKE, 1, None, FAKE, FAKE, FAKE, None, 1, FAKE, FAKE, 4, 4, 1000,
+    assert lib.misa_route_heads(FAKE, 1, None, FAKE, FAKE, *KV, FAKE, FAKE, 4, 4, 1000,
                                 128, 2048, 64, 8, FAKE, None, FAKE, 1 << 30, None) == 2
     # workspace too small
-    assert lib.misa_route_heads(FAKE, 1, None, FAKE, FAKE, FAKE, None, 1, FAKE, FAKE, 4, 4,
+    assert lib.misa_route_heads(FAKE, 1, None, FAKE, FAKE, *KV, FAKE, FAKE, 4, 4,
                                 100000, 128, 128, 64, 8, FAKE, None, FAKE, 8, None) == 4
     own = lib.misa_workspace_bytes(b.MISA_OP_ROUTE, 1, 4, 100000, 128, 64, 128, 1, 0)
-    assert lib.misa_route_heads(FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, 4, 4,
+    assert lib.misa_route_heads(FAKE, 2, FAKE, FAKE, FAKE, *KV8, FAKE, FAKE, 4, 4,
                                 100000, 128, 128, 64, 8, FAKE, None, FAKE, own, None) == 4
-    assert lib.misa_pool_keys(None, None, 1, 1, 100, 128, 16, FAKE, None) == 1
-    assert lib.misa_pool_keys(FAKE, None, 2, 1, 100, 128, 16, FAKE, None) == 1
-    assert lib.misa_pool_keys(FAKE, None, 5, 1, 100, 128, 16, FAKE, None) == 3
-    assert lib.misa_pool_keys(FAKE, None, 1, 1, 100, 128, 0, FAKE, None) == 2
+    # paged route without a block table
+    assert lib.misa_route_heads(FAKE, 1, None, FAKE, FAKE, FAKE, None, 1, None, 64, FAKE, FAKE, 4,
+                                4, 1000, 128, 128, 64, 8, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert lib.misa_pool_keys(None, None, 1, None, 0, 1, 100, 128, 16, FAKE, None) == 1
+    assert lib.misa_pool_keys(FAKE, None, 2, None, 0, 1, 100, 128, 16, FAKE, None) == 1
+    assert lib.misa_pool_keys(FAKE, None, 5, None, 0, 1, 100, 128, 16, FAKE, None) == 3
+    assert lib.misa_pool_keys(FAKE, None, 1, None, 0, 1, 100, 128, 0, FAKE, None) == 2
+    assert lib.misa_pool_keys(FAKE, None, 1, FAKE, 24, 1, 100, 128, 16, FAKE, None) == 2
+    # incremental pooling: length arrays required, 0 <= max_new <= L
+    upd = lib.misa_pool_update
+    assert upd(FAKE, None, 1, None, 0, 2, 100, 128, 16, None, FAKE, 1, FAKE, None) == 1
+    assert upd(FAKE, None, 1, None, 0, 2, 100, 128, 16, FAKE, FAKE, -1, FAKE, None) == 2
+    assert upd(FAKE, None, 1, None, 0, 2, 100, 128, 16, FAKE, FAKE, 101, FAKE, None) == 2
+    assert upd(FAKE, None, 1, FAKE, 0, 2, 100, 128, 16, FAKE, FAKE, 1, FAKE, None) == 2
+    assert upd(FAKE, None, 1, None, 0, 2, 100, 128, 16, FAKE, FAKE, 0, FAKE, None) == 0  # no-op
 
 
 def _param_counts():

@@ -59,13 +59,13 @@ def fp8_gemm(p):
     return p.q_dt == synth.FP8 and p.S == 1 and p.N >= 128 and p.d == 128
 
 
-def check_misa(p, h=None, topk=None, rows=None):
+def check_misa(p, h=None, topk=None, rows=None, page_size=0):
     """Full MISA on GPU (pool -> route -> score+top-k) vs the oracle."""
     h = p.h if h is None else h
     topk = p.topk if topk is None else topk
     log(f"[misa] {p.name} N={p.N} L={p.L} d={p.d} H_I={p.H_I} h={h} k={topk} "
-        f"q_dt={synth.DTYPE_NAMES[p.q_dt]} k_dt={synth.DTYPE_NAMES[p.k_dt]}")
-    dp = DeviceProblem(p)
+        f"q_dt={synth.DTYPE_NAMES[p.q_dt]} k_dt={synth.DTYPE_NAMES[p.k_dt]} page={page_size}")
+    dp = DeviceProblem(p, page_size=page_size, page_seed=7)
     kbar, heads, r, idx, sc = misa_gpu(dp, h, topk)
     ref_kbar = oracle.pool_keys(p)
     assert np.all(np.abs(kbar - ref_kbar) <= tol(ref_kbar)), "pooled keys"
@@ -75,7 +75,7 @@ def check_misa(p, h=None, topk=None, rows=None):
     assert np.all(np.abs(r[rows] - ref_r) <= tol(ref_r)), "router scores"
     differing = check_heads(heads[rows], ref_r, h)
     ref_sc = oracle.scores(ps, heads[rows])            # replay the GPU's heads
-    extra = fp8_mfma_error_bound(ps, heads[rows]) if fp8_gemm(p) else None
+    extra = fp8_mfma_error_bound(ps, heads[rows]) if fp8_gemm(p) and not page_size else None
     swapped = check_topk(idx[rows], sc[rows], ref_sc, topk, ps.visible(), extra=extra)
     log(f"[misa] {p.name}: head rows differing at near-ties {differing}, token swaps {swapped}")
     return dp, heads, idx
@@ -522,6 +522,112 @@ def test_fp8_prefill_dense_and_dagger_parity():
 def test_c3f8_prefill_chunk_sampled_rows():
     p = synth.make("c3f8")
     check_misa(p, rows=np.r_[0:3, 127:130, 2047:2049, 4093:4096])
+
+
+# ---------------------------------------------------------------- paged keys and incremental pooling
+# A paged key cache holds the same rows in pages listed by a block table; the
+# kernels do the same arithmetic in the same order, so every output must be
+# byte-identical to the contiguous call (spare pages hold NaN patterns, so a
+# wrong page would show).  Incremental pooling writes exactly the blocks that
+# appended tokens complete, byte-identical to the full pooling pass.
+def _all_outputs(dp, k_prime):
+    kbar = dp.pool()
+    heads, r = dp.route(kbar)
+    idx, sc = dp.score_topk(heads)
+    didx, dsc = dp.dsa()
+    cand, _ = dp.score_topk(heads, k_prime)
+    gidx, gsc = dp.rerank(cand)
+    return [np_(x) for x in (kbar, heads, r, idx, sc, didx, dsc, cand, gidx, gsc)]
+
+
+@pytest.mark.parametrize("page_size", [16, 64, 256])
+@pytest.mark.parametrize("k_dt", [synth.BF16, synth.FP8])
+def test_paged_keys_byte_identical(page_size, k_dt):
+    p = synth.small("paged", 91, N=3, S=3, L=5000, d=128, H_I=64, h=8, B=128, topk=300,
+                    k_prime=1200, k_dt=k_dt, q_pos=np.array([4999, 2047, 130], np.int32))
+    log(f"[paged] page={page_size} k_dt={synth.DTYPE_NAMES[k_dt]}")
+    ref = _all_outputs(DeviceProblem(p), p.k_prime)
+    got = _all_outputs(DeviceProblem(p, page_size=page_size, page_seed=page_size), p.k_prime)
+    names = ["kbar", "heads", "r", "idx", "score", "dense idx", "dense score", "cand",
+             "rerank idx", "rerank score"]
+    for n, a, b in zip(names, ref, got):
+        assert np.array_equal(a, b, equal_nan=True), n
+
+
+def test_paged_keys_parity_with_oracle():
+    """Many rows over one paged sequence (the per-row kernels, not the GEMM)
+    and fp8 queries with paged fp8 keys, against the oracle."""
+    L, N = 6000, 200
+    pos = np.random.default_rng(92).choice(L, N, replace=False).astype(np.int32)
+    pos[:3] = [0, 127, L - 1]
+    p = synth.small("pagedrows", 92, N=N, S=1, L=L, d=128, H_I=64, h=8, B=128, topk=500,
+                    q_pos=pos, q_seq=np.zeros(N, np.int32))
+    check_misa(p, rows=np.r_[0:6, 100:103, N - 3:N], page_size=64)
+    p = synth.small("paged8", 93, N=3, S=2, L=3000, d=128, H_I=64, h=8, B=128, topk=300,
+                    q_dt=synth.FP8, k_dt=synth.FP8)
+    check_misa(p, page_size=32)
+
+
+@pytest.mark.parametrize("page_size", [0, 64])
+def test_pool_update_matches_full_pooling(page_size):
+    """Appends of ragged sizes: after each update the complete blocks equal the
+    full pooling pass bit for bit and every other table row is untouched."""
+    L, B, S = 3000, 128, 3
+    p = synth.small("upd", 94, N=S, S=S, L=L, d=128, H_I=8, h=2, B=B, topk=10, k_dt=synth.FP8)
+    dp = DeviceProblem(p, page_size=page_size, page_seed=3)
+    full = np_(dp.pool())
+    M = full.shape[1]
+    kbar = torch.full((S, M, p.d), float("nan"), dtype=torch.float32, device="cuda")
+    lens = np.zeros(S, np.int64)
+    rng = np.random.default_rng(94)
+    for step in range(12):
+        add = rng.integers(0, 400, size=S)
+        add[step % S] = 1 if step % 2 else 128
+        new = np.minimum(lens + add, L)
+        mx = int((new - lens).max())
+        dp.pool_update(torch.from_numpy(lens.astype(np.int32)).cuda(),
+                       torch.from_numpy(new.astype(np.int32)).cuda(), mx, kbar)
+        lens = new
+        got = np_(kbar)
+        for s in range(S):
+            done = int(lens[s]) // B
+            assert np.array_equal(got[s, :done], full[s, :done]), (step, s)
+            assert np.all(np.isnan(got[s, done:])), (step, s)
+
+
+def test_decode_loop_with_incremental_pool_and_pages():
+    """A decode loop: every step appends one token per sequence, updates the
+    pooled table, routes and scores the new query row over its prefix; the
+    results equal those from a full pooling pass byte for byte, and the oracle
+    at the first and last steps."""
+    S, L, B, steps, start = 3, 2304, 128, 200, 2000
+    p = synth.small("loop", 95, N=S, S=S, L=L, d=128, H_I=64, h=8, B=B, topk=256)
+    dp = DeviceProblem(p, page_size=64, page_seed=5)
+    M = -(-L // B)
+    kbar = torch.zeros((S, M, p.d), dtype=torch.float32, device="cuda")
+    zero = torch.zeros(S, dtype=torch.int32, device="cuda")
+    lens = torch.full((S,), start - 1, dtype=torch.int32, device="cuda")
+    dp.pool_update(zero, lens, start - 1, kbar)
+    for step in range(steps):
+        new = lens + 1
+        dp.pool_update(lens, new, 1, kbar)
+        lens = new
+        dp.q_pos = (lens - 1).contiguous()
+        heads, r = dp.route(kbar)
+        idx, sc = dp.score_topk(heads)
+        if step in (0, steps // 2, steps - 1):
+            full = dp.pool()
+            h2, r2 = dp.route(full)
+            i2, s2 = dp.score_topk(h2)
+            for a, b in ((heads, h2), (r, r2), (idx, i2), (sc, s2)):
+                assert np.array_equal(np_(a), np_(b)), step
+        if step in (0, steps - 1):
+            pos = np_(dp.q_pos).astype(np.int32)
+            ps = synth.Problem(p.name, p.q, p.q_dt, p.w, p.k, p.k_dt, p.k_scale, p.q_seq, pos,
+                               p.B, p.h, p.topk)
+            _, ref_r = oracle.route_heads(ps)
+            check_heads(np_(heads), ref_r, p.h)
+            check_topk(np_(idx), np_(sc), oracle.scores(ps, np_(heads)), p.topk, ps.visible())
 
 
 # ---------------------------------------------------------------- edge cases and fallback paths

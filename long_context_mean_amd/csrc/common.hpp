@@ -47,22 +47,9 @@ struct KeyIndex {
   int page_shift;
   int max_pages;
 
-  // Any lane, any token.
   __device__ __forceinline__ size_t row(int s, int t) const {
     if (table == nullptr) return static_cast<size_t>(s) * L + t;
     const int pg = table[static_cast<size_t>(s) * max_pages + (t >> page_shift)];
-    return (static_cast<size_t>(pg) << page_shift) + (t & ((1 << page_shift) - 1));
-  }
-  // s and t equal on every lane of the wavefront: the table entry is read
-  // through the scalar cache (the table is read-only while a kernel runs), so
-  // the lookup does not wait behind the wavefront's vector loads in flight.
-  __device__ __forceinline__ size_t row_uniform(int s, int t) const {
-    s = __builtin_amdgcn_readfirstlane(s);
-    t = __builtin_amdgcn_readfirstlane(t);
-    if (table == nullptr) return static_cast<size_t>(s) * L + t;
-    typedef const __attribute__((address_space(4))) int32_t cint32_t;
-    const cint32_t* tb = reinterpret_cast<const cint32_t*>(reinterpret_cast<uintptr_t>(table));
-    const int pg = tb[static_cast<size_t>(s) * max_pages + (t >> page_shift)];
     return (static_cast<size_t>(pg) << page_shift) + (t & ((1 << page_shift) - 1));
   }
 };

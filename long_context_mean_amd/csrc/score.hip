@@ -24,8 +24,10 @@
 // have no exact low-precision MFMA form).
 //
 // Keys may live in a paged cache (KeyIndex): a tile's 16 consecutive tokens
-// always share a page (pages hold a multiple of 16 tokens), so the streaming
-// kernel looks the page up once per tile through the scalar cache; candidate
+// always share a page (pages hold a multiple of 16 tokens).  The streaming
+// kernel reads the page numbers of all of a wavefront's tiles with one vector
+// load at the start (lane j: the j-th tile) and takes each tile's page from
+// that register with readlane, so the loop itself does no lookups; candidate
 // gathers look each token's page up per lane.
 #include <cstdlib>
 
@@ -109,16 +111,17 @@ template <int KT, int D, int U>
 using RawGroup = u32x4_t[U][KeyLayout<KT, D>::NLOAD];
 
 // Issues the key loads of U tiles (16 elements each) starting at element e0.
-// Without a candidate list the key address depends only on the element
-// index (and, for paged keys, on one scalar page lookup per tile), so no load
-// waits on another vector load; bit t of the result is set when tile t's
+// Without a candidate list the key address depends only on the element index
+// (and, for paged keys, on the page number held in lane ord0 + t of page_v),
+// so no load waits on another load; bit t of the result is set when tile t's
 // element is a valid token.  Elements past the row end read a valid row of
 // the sequence and are masked.
 template <int KT, int D, int U, bool CAND>
 __device__ __forceinline__ uint32_t issue_group(RawGroup<KT, D, U>& raw, float* sc, int tile0,
                                                 int tstride, int lane, int c, int len,
                                                 const int32_t* crow, const uint8_t* kbase,
-                                                const float* sbase, const KeyIndex& ki, int s) {
+                                                const float* sbase, const KeyIndex& ki, int s,
+                                                int ord0, int page_v) {
   using LY = KeyLayout<KT, D>;
   const int rsub = lane / LY::LANES_PER_ROW, q = lane % LY::LANES_PER_ROW;
   uint32_t valid = 0;
@@ -126,7 +129,15 @@ __device__ __forceinline__ uint32_t issue_group(RawGroup<KT, D, U>& raw, float* 
   for (int t = 0; t < U; ++t) {
     const int te = (tile0 + t * tstride) * 16;
     size_t rb = 0;                                     // row of the tile's first token
-    if constexpr (!CAND) rb = ki.row_uniform(s, te < len ? te : len - 1);
+    if constexpr (!CAND) {
+      const int tc = te < len ? te : len - 1;
+      if (ki.table) {
+        const int pg = __builtin_amdgcn_readlane(page_v, ord0 + t);
+        rb = (static_cast<size_t>(pg) << ki.page_shift) + (tc & ((1 << ki.page_shift) - 1));
+      } else {
+        rb = static_cast<size_t>(s) * ki.L + tc;
+      }
+    }
     // flat: load i of lane l reads 16 bytes of row i*ROWS_PER_LOAD + l/LANES_PER_ROW
 #pragma unroll
     for (int i = 0; i < LY::NLOAD; ++i) {
@@ -237,6 +248,16 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
   uint32_t* urow = p.u + static_cast<size_t>(n) * p.u_stride;
   const int wtile = blockIdx.x * 4 + wave;            // this wavefront's first tile
   const int wtiles = wtile < ntiles ? (ntiles - wtile + tstride - 1) / tstride : 0;
+  // paged keys: lane j holds the page of this wavefront's j-th tile (at most
+  // 64 tiles per wavefront; tiles past the row end use the row's last token)
+  int page_v = 0;
+  if constexpr (!CAND) {
+    if (p.ki.table) {
+      const int te = (wtile + lane * tstride) * 16;
+      const int tc = te < len ? te : len - 1;
+      page_v = p.ki.table[static_cast<size_t>(s) * p.ki.max_pages + (tc >> p.ki.page_shift)];
+    }
+  }
 
   // first key group in flight before anything else
   u32x4_t ra[U][LY::NLOAD], rb[U][LY::NLOAD];
@@ -244,7 +265,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
   uint32_t va = 0, vb = 0;
   if (wtiles > 0)
     va = issue_group<KT, D, U, CAND>(ra, sa, wtile, tstride, lane, c, len, crow, kseq, sseq,
-                                     p.ki, s);
+                                     p.ki, s, 0, page_v);
 
   if (do_hist) {
     for (int b = threadIdx.x; b < kBins0; b += 256) lh[b] = 0u;
@@ -286,21 +307,23 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
     int t0 = wtile;                                    // first tile of the current group
     const int gstep = U * tstride;                     // tiles between consecutive groups
     int left = (wtiles + U - 1) / U;                   // groups left, current included
+    int o0 = 0;                                        // ordinal of the current group's first tile
     while (left >= 3) {
       vb = issue_group<KT, D, U, CAND>(rb, sb, t0 + gstep, tstride, lane, c, len, crow, kseq,
-                                       sseq, p.ki, s);
+                                       sseq, p.ki, s, o0 + U, page_v);
       score_group<KT, NT, D, U>(ra, sa, va, t0, tstride, tile, lane, a, wv, g, c, len, urow,
                                 lh, do_hist);
       va = issue_group<KT, D, U, CAND>(ra, sa, t0 + 2 * gstep, tstride, lane, c, len, crow,
-                                       kseq, sseq, p.ki, s);
+                                       kseq, sseq, p.ki, s, o0 + 2 * U, page_v);
       score_group<KT, NT, D, U>(rb, sb, vb, t0 + gstep, tstride, tile, lane, a, wv, g, c, len,
                                 urow, lh, do_hist);
       t0 += 2 * gstep;
+      o0 += 2 * U;
       left -= 2;
     }
     if (left == 2) {
       vb = issue_group<KT, D, U, CAND>(rb, sb, t0 + gstep, tstride, lane, c, len, crow, kseq,
-                                       sseq, p.ki, s);
+                                       sseq, p.ki, s, o0 + U, page_v);
       score_group<KT, NT, D, U>(ra, sa, va, t0, tstride, tile, lane, a, wv, g, c, len, urow,
                                 lh, do_hist);
       score_group<KT, NT, D, U>(rb, sb, vb, t0 + gstep, tstride, tile, lane, a, wv, g, c, len,
@@ -453,7 +476,8 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
   // chunks so more workgroups share the gather.  MISA_SCORE_TPW overrides
   // (launch-shape tuning only).
   static const int tpw_env = env_int("MISA_SCORE_TPW", 0);
-  const int tpw = tpw_env > 0 ? tpw_env : (a.cand ? 4 : 16);
+  // (at most 64 tiles per wavefront: the paged path keeps one page number per lane)
+  const int tpw = tpw_env > 0 ? (tpw_env < 64 ? tpw_env : 64) : (a.cand ? 4 : 16);
   if (a.k_dt == DT_BF16)
     return a.d == 64 ? launch_mfma_rows<DT_BF16, 64>(a, st, tpw)
                      : launch_mfma_rows<DT_BF16, 128>(a, st, tpw);

@@ -305,3 +305,54 @@ def integer_problem(name: str, seed: int, *, N=2, S=2, L=300, d=64, H_I=8, h=3, 
     return Problem(name, q, q_dt, w, k, k_dt, k_scale,
                    np.ascontiguousarray(q_seq, np.int32), np.ascontiguousarray(q_pos, np.int32),
                    B, h, topk, k_prime, q_scale=q_scale)
+
+
+# --------------------------------------------------------------------------
+# sparse attention over the selected tokens (the consumer of the top-k)
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class AttentionProblem:
+    """q [N, H, d_qk] and the latent key/value cache kv [S, L, d_qk] as bf16
+    bits; value rows are kv[..., :d_v].  idx [N, topk] holds each row's
+    selected tokens (distinct, ascending, -1 padding at the end)."""
+    name: str
+    q: np.ndarray
+    kv: np.ndarray
+    q_seq: np.ndarray
+    idx: np.ndarray
+    d_v: int
+    scale: float
+
+    @property
+    def N(self): return self.q.shape[0]
+    @property
+    def H(self): return self.q.shape[1]
+    @property
+    def d_qk(self): return self.q.shape[2]
+    @property
+    def S(self): return self.kv.shape[0]
+    @property
+    def L(self): return self.kv.shape[1]
+    @property
+    def topk(self): return self.idx.shape[1]
+
+
+def attention_problem(name, seed, *, N, S, L, H, d_qk, d_v, topk, n_valid=None, q_seq=None,
+                      scale=None, q_sigma=1.0):
+    """Cache rows ~ N(0, 1), queries ~ N(0, q_sigma^2), each row selecting
+    n_valid[n] (default min(topk, L)) distinct tokens uniformly at random,
+    listed ascending then padded with -1.  scale defaults to 1/sqrt(d_qk)."""
+    rng = np.random.default_rng(seed)
+    kv32 = rng.standard_normal((S, L, d_qk)).astype(np.float32)
+    q32 = (q_sigma * rng.standard_normal((N, H, d_qk))).astype(np.float32)
+    if q_seq is None:
+        q_seq = np.arange(N, dtype=np.int32) % S
+    if n_valid is None:
+        n_valid = np.full(N, min(topk, L), dtype=np.int64)
+    idx = np.full((N, topk), -1, dtype=np.int32)
+    for n in range(N):
+        sel = np.sort(rng.choice(L, size=int(n_valid[n]), replace=False))
+        idx[n, :len(sel)] = sel
+    scale = float(1.0 / np.sqrt(d_qk)) if scale is None else float(scale)
+    return AttentionProblem(name, f32_to_bf16_bits(q32), f32_to_bf16_bits(kv32),
+                            np.ascontiguousarray(q_seq, dtype=np.int32), idx, d_v, scale)

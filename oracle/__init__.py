@@ -46,10 +46,12 @@ def _load():
     lib.misa_ref_score_topk.argtypes = common + [P] + [I] * 7 + [P, P, P, P]
     lib.dsa_ref_score_topk.argtypes = common + [I] * 6 + [P, P, P, P]
     lib.misa_ref_rerank.argtypes = common + [P] + [I] * 7 + [P, P, P, P]
+    lib.misa_ref_sparse_attention.argtypes = [P, I, P, I, P, P] + [I] * 7 + [ctypes.c_double,
+                                                                              P, P]
     lib.misa_ref_max_threads.argtypes = []
     for f in ("misa_ref_decode", "misa_ref_pool_keys", "misa_ref_route_heads",
               "misa_ref_scores", "misa_ref_score_topk", "dsa_ref_score_topk",
-              "misa_ref_rerank", "misa_ref_max_threads"):
+              "misa_ref_rerank", "misa_ref_sparse_attention", "misa_ref_max_threads"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -193,3 +195,20 @@ def misa_dagger(p, h=None, k_prime=None, topk=None, mac=None):
     cand, _, _ = score_topk(p, heads, k_prime, mac)
     idx, sc, kth = rerank(p, cand, topk, mac)
     return heads, cand, idx, sc, kth
+
+
+def sparse_attention(q, q_dt, kv, kv_dt, q_seq, idx, scale, d_v):
+    """Softmax attention of every head of every row over the row's selected
+    tokens (see misa_ref.h).  Returns (out [N, H, d_v], lse [N, H]) in float64."""
+    q = np.ascontiguousarray(q)
+    kv = np.ascontiguousarray(kv)
+    N, H, d_qk = q.shape
+    S, L = kv.shape[:2]
+    sq = _c(q_seq, np.int32)
+    ix = _c(idx, np.int32)
+    out = np.empty((N, H, d_v), dtype=np.float64)
+    lse = np.empty((N, H), dtype=np.float64)
+    _check(lib().misa_ref_sparse_attention(_p(q), q_dt, _p(kv), kv_dt, _p(sq), _p(ix), N, S, L, H,
+                                           d_qk, d_v, ix.shape[1], float(scale), _p(out),
+                                           _p(lse)), "sparse_attention")
+    return out, lse

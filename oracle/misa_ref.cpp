@@ -345,4 +345,59 @@ int misa_ref_rerank(const void* q, int q_dt, const float* q_scale, const float* 
   return 0;
 }
 
+int misa_ref_sparse_attention(const void* q, int q_dt, const void* kv, int kv_dt,
+                              const int32_t* q_seq, const int32_t* idx, int N, int S, int L,
+                              int H, int d_qk, int d_v, int topk, double scale, double* out,
+                              double* lse) {
+  if (!q || !kv || !q_seq || !idx || !out || !lse) return 1;
+  if ((q_dt != DT_F32 && q_dt != DT_BF16) || (kv_dt != DT_F32 && kv_dt != DT_BF16)) return 3;
+  if (N < 0 || S < 1 || L < 1 || H < 1 || d_qk < 1 || d_v < 1 || d_v > d_qk || topk < 1) return 2;
+  for (int n = 0; n < N; ++n) {
+    if (q_seq[n] < 0 || q_seq[n] >= S) return 2;
+    std::vector<int32_t> tok;
+    for (int i = 0; i < topk; ++i) {
+      const int32_t t = idx[static_cast<int64_t>(n) * topk + i];
+      if (t < 0) continue;
+      if (t >= L) return 2;
+      tok.push_back(t);
+    }
+    std::vector<int32_t> sorted_tok(tok);
+    std::sort(sorted_tok.begin(), sorted_tok.end());
+    if (std::adjacent_find(sorted_tok.begin(), sorted_tok.end()) != sorted_tok.end()) return 2;
+    // selected cache rows, decoded once
+    std::vector<double> rows(tok.size() * static_cast<size_t>(d_qk));
+    const int64_t seq0 = static_cast<int64_t>(q_seq[n]) * L;
+    for (size_t c = 0; c < tok.size(); ++c)
+      for (int i = 0; i < d_qk; ++i)
+        rows[c * d_qk + i] = stored_value(kv, kv_dt, (seq0 + tok[c]) * d_qk + i);
+#pragma omp parallel for schedule(static)
+    for (int h = 0; h < H; ++h) {
+      const int64_t qrow = (static_cast<int64_t>(n) * H + h) * d_qk;
+      std::vector<double> qh(d_qk);
+      for (int i = 0; i < d_qk; ++i) qh[i] = stored_value(q, q_dt, qrow + i);
+      double* o = out + (static_cast<int64_t>(n) * H + h) * d_v;
+      for (int i = 0; i < d_v; ++i) o[i] = 0.0;
+      if (tok.empty()) {
+        lse[static_cast<int64_t>(n) * H + h] = NEG_INF;
+        continue;
+      }
+      std::vector<double> sc(tok.size());
+      double m = NEG_INF;
+      for (size_t c = 0; c < tok.size(); ++c) {
+        sc[c] = scale * dot(qh.data(), &rows[c * d_qk], d_qk);
+        m = std::max(m, sc[c]);
+      }
+      double z = 0.0;
+      for (size_t c = 0; c < tok.size(); ++c) {
+        const double pc = std::exp(sc[c] - m);
+        z += pc;
+        for (int i = 0; i < d_v; ++i) o[i] += pc * rows[c * d_qk + i];
+      }
+      for (int i = 0; i < d_v; ++i) o[i] /= z;
+      lse[static_cast<int64_t>(n) * H + h] = m + std::log(z);
+    }
+  }
+  return 0;
+}
+
 }  // extern "C"

@@ -98,6 +98,24 @@ int misa_ref_rerank(const void* q, int q_dt, const float* q_scale, const float* 
                     const int32_t* cand, int N, int S, int L, int d, int H_I, int k_prime,
                     int topk, int32_t* idx, double* score, double* kth, uint64_t* mac);
 
+/* Sparse attention over the selected tokens (the consumer of the top-k: the
+ * indexer picks the tokens the main attention reads [MISA abstract, HF Daily
+ * Papers digest; technical summary, "Problem statement"]; the attention
+ * itself is ordinary softmax attention, not specified by the pages).
+ * For row n, head h and the valid tokens T_n = {idx[n,i] >= 0} (distinct,
+ * < L) of sequence q_seq[n]:
+ *   s_t = scale * q[n,h,:] . kv[q_seq[n], t, 0:d_qk]
+ *   out[n,h,:] = sum_t exp(s_t - m) kv[q_seq[n], t, 0:d_v] / sum_t exp(s_t - m),
+ *   m = max_t s_t,   lse[n,h] = m + log(sum_t exp(s_t - m))
+ * Value rows are the first d_v elements of the same cache rows (latent
+ * attention's shared key/value rows).  q [N,H,d_qk], kv [S,L,d_qk] (dt 0 =
+ * f32, 1 = bf16 bits); out [N,H,d_v], lse [N,H] doubles.  A row without a
+ * valid token gets out = 0, lse = -inf. */
+int misa_ref_sparse_attention(const void* q, int q_dt, const void* kv, int kv_dt,
+                              const int32_t* q_seq, const int32_t* idx, int N, int S, int L,
+                              int H, int d_qk, int d_v, int topk, double scale, double* out,
+                              double* lse);
+
 /* Threads the OpenMP runtime will use. */
 int misa_ref_max_threads(void);
 

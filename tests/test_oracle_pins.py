@@ -405,3 +405,79 @@ def test_rerank_rejects_invalid_candidates():
         oracle.rerank(p, np.array([[1, 2, 100, 3, 4, 5]], np.int32))        # past L_n
     idx, val, _ = oracle.rerank(p, np.array([[-1, 7, -1, 3, -1, -1]], np.int32))
     assert sorted(idx[0][:2].tolist()) == [3, 7] and list(idx[0][2:]) == [-1, -1, -1]
+
+
+# ---------------------------------------------------------------- sparse attention (consumer)
+def _torch_attention(p):
+    """float64 softmax attention by torch over the valid selected tokens."""
+    q = torch.from_numpy(synth.bf16_bits_to_f32(p.q).astype(np.float64))
+    kv = torch.from_numpy(synth.bf16_bits_to_f32(p.kv).astype(np.float64))
+    out = np.zeros((p.N, p.H, p.d_v))
+    lse = np.full((p.N, p.H), -np.inf)
+    for n in range(p.N):
+        sel = p.idx[n][p.idx[n] >= 0]
+        if len(sel) == 0:
+            continue
+        rows = kv[p.q_seq[n], torch.from_numpy(sel.astype(np.int64))]
+        s = p.scale * q[n] @ rows.T                                   # [H, k]
+        out[n] = (torch.softmax(s, dim=1) @ rows[:, :p.d_v]).numpy()
+        lse[n] = torch.logsumexp(s, dim=1).numpy()
+    return out, lse
+
+
+def _attn(p):
+    return oracle.sparse_attention(p.q, synth.BF16, p.kv, synth.BF16, p.q_seq, p.idx, p.scale,
+                                   p.d_v)
+
+
+def test_attention_matches_torch_softmax():
+    """Ragged selections (padding, one row with a single token, one empty row)
+    against torch.softmax / logsumexp in float64 (P-attn-1).  Catches a missing
+    scale, a softmax over the wrong axis, values taken past d_v, and padding
+    read as token -1."""
+    p = synth.attention_problem("att", 51, N=5, S=2, L=300, H=8, d_qk=96, d_v=64, topk=50,
+                                n_valid=np.array([50, 17, 1, 0, 33]))
+    out, lse = _attn(p)
+    ref_o, ref_l = _torch_attention(p)
+    np.testing.assert_allclose(out, ref_o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse[:3], ref_l[:3], rtol=1e-12)
+    np.testing.assert_allclose(lse[4], ref_l[4], rtol=1e-12)
+    assert np.all(np.isneginf(lse[3])) and not out[3].any()
+
+
+def test_attention_closed_forms():
+    """One selected token: out is that value row and lse its score; q = 0:
+    out is the mean of the selected value rows and lse = log(count)."""
+    p = synth.attention_problem("att1", 52, N=2, S=1, L=200, H=4, d_qk=64, d_v=32, topk=5,
+                                n_valid=np.array([1, 5]))
+    out, lse = _attn(p)
+    kv = synth.bf16_bits_to_f32(p.kv).astype(np.float64)
+    q = synth.bf16_bits_to_f32(p.q).astype(np.float64)
+    t = p.idx[0, 0]
+    assert np.array_equal(out[0], np.tile(kv[0, t, :32], (4, 1)))
+    np.testing.assert_allclose(lse[0], p.scale * q[0] @ kv[0, t], rtol=1e-14)
+    pz = synth.AttentionProblem("attz", np.zeros_like(p.q), p.kv, p.q_seq, p.idx, p.d_v, p.scale)
+    out, lse = _attn(pz)
+    np.testing.assert_allclose(out[1], np.tile(kv[0, p.idx[1], :32].mean(0), (4, 1)), rtol=1e-13)
+    np.testing.assert_allclose(lse[1], np.log(5.0), rtol=1e-14)
+
+
+def test_attention_is_order_invariant_and_checks_indices():
+    """Shuffling a row's selected tokens changes nothing beyond rounding;
+    duplicate or out-of-range tokens are rejected."""
+    p = synth.attention_problem("att2", 53, N=2, S=2, L=400, H=4, d_qk=64, d_v=64, topk=40)
+    out, lse = _attn(p)
+    rng = np.random.default_rng(0)
+    idx2 = np.stack([rng.permutation(r) for r in p.idx])
+    p2 = synth.AttentionProblem("att2b", p.q, p.kv, p.q_seq, idx2, p.d_v, p.scale)
+    out2, lse2 = _attn(p2)
+    np.testing.assert_allclose(out2, out, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-13)
+    bad = p.idx.copy()
+    bad[0, 1] = bad[0, 0]
+    with pytest.raises(oracle.OracleError):
+        _attn(synth.AttentionProblem("d", p.q, p.kv, p.q_seq, bad, p.d_v, p.scale))
+    bad = p.idx.copy()
+    bad[1, 0] = 400
+    with pytest.raises(oracle.OracleError):
+        _attn(synth.AttentionProblem("r", p.q, p.kv, p.q_seq, bad, p.d_v, p.scale))

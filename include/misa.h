@@ -92,7 +92,8 @@ typedef enum {
 typedef enum {
   MISA_OP_ROUTE = 0,        /* misa_route_heads */
   MISA_OP_SCORE_TOPK = 1,   /* misa_score_topk (also dsa_score_topk) */
-  MISA_OP_RERANK = 2        /* misa_rerank */
+  MISA_OP_RERANK = 2,       /* misa_rerank */
+  MISA_OP_ATTENTION = 3     /* misa_sparse_attention (d = d_v, H_I = heads) */
 } misa_op;
 
 /*
@@ -192,6 +193,37 @@ int32_t misa_rerank(const void* q, int32_t q_dt, const float* q_scale, const flo
                     const int32_t* cand, int32_t N, int32_t S, int32_t L, int32_t d, int32_t H_I,
                     int32_t k_prime, int32_t topk, int32_t* idx, float* score, void* ws,
                     size_t ws_bytes, void* stream);
+
+/*
+ * Sparse attention over the selected tokens: the consumer of the top-k (the
+ * indexer picks the tokens the main attention reads, MISA abstract and
+ * "Problem statement"; the attention itself is ordinary softmax attention,
+ * which the pages do not specify).  For row n, head h and the valid entries
+ * t of idx[n, :] (-1 = empty; distinct tokens of sequence q_seq[n]):
+ *   s_t = scale * q[n,h,:] . kv_t[0:d_qk],  m = max_t s_t,
+ *   out[n,h,:] = sum_t exp(s_t - m) kv_t[0:d_v] / sum_t exp(s_t - m),
+ *   lse[n,h] = m + log(sum_t exp(s_t - m))   (natural log)
+ * Values are the first d_v elements of the same cache rows (multi-head latent
+ * attention's shared key/value cache).  A row without a valid entry gets
+ * out = 0 and lse = -inf.
+ *   q   [N, H, d_qk] bf16 (q_dt = MISA_BF16); kv: cache rows of d_qk bf16
+ *       (kv_dt = MISA_BF16), contiguous [S, L, d_qk] or paged through
+ *       block_table/page_size exactly like keys (see the conventions)
+ *   idx [N, topk] int32 (e.g. the idx output of misa_score_topk)
+ *   out [N, H, d_v] float32, lse [N, H] float32; scale > 0
+ *   d_qk in {64, 128, 256, 576}; d_v a multiple of 32, 32 <= d_v <= min(512, d_qk);
+ *   1 <= H <= 1024.  Entries of idx are device-resident: not checked.
+ * Accuracy: fp32 dot products of exact bf16 products; the probabilities are
+ * carried as bf16 hi + lo pairs into the value products (~2^-17 relative).
+ * Workspace: misa_workspace_bytes(MISA_OP_ATTENTION, q_dt, N, L, d_v, H, 0,
+ * topk, 0).
+ */
+int32_t misa_sparse_attention(const void* q, int32_t q_dt, const void* kv, int32_t kv_dt,
+                              const int32_t* block_table, int32_t page_size,
+                              const int32_t* q_seq, const int32_t* idx, int32_t N, int32_t S,
+                              int32_t L, int32_t H, int32_t d_qk, int32_t d_v, int32_t topk,
+                              float scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                              void* stream);
 
 /*
  * Workspace bytes for `op` at these sizes with queries of dtype q_dt (0 for

@@ -22,11 +22,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmisa.so")
 
 MISA_F32, MISA_BF16, MISA_FP8_E4M3 = 0, 1, 2
-MISA_OP_ROUTE, MISA_OP_SCORE_TOPK, MISA_OP_RERANK = 0, 1, 2
+MISA_OP_ROUTE, MISA_OP_SCORE_TOPK, MISA_OP_RERANK, MISA_OP_ATTENTION = 0, 1, 2, 3
 MISA_OK = 0
 
 EXPORTED = ("misa_pool_keys", "misa_pool_update", "misa_route_heads", "misa_score_topk", "dsa_score_topk",
-            "misa_rerank", "misa_workspace_bytes", "misa_status_string",
+            "misa_rerank", "misa_sparse_attention", "misa_workspace_bytes", "misa_status_string",
             "misa_last_hip_error", "misa_profile_begin", "misa_profile_end", "misa_kernel_name")
 
 
@@ -65,6 +65,8 @@ def lib():
     L.misa_score_topk.argtypes = [P, I32, P, P] + KEYS + [P, P, P] + [I32] * 7 + [P, P, P, SZ, P]
     L.dsa_score_topk.argtypes = [P, I32, P, P] + KEYS + [P, P] + [I32] * 6 + [P, P, P, SZ, P]
     L.misa_rerank.argtypes = [P, I32, P, P] + KEYS + [P, P, P] + [I32] * 7 + [P, P, P, SZ, P]
+    L.misa_sparse_attention.argtypes = [P, I32, P, I32, P, I32, P, P] + [I32] * 7 + \
+        [ctypes.c_float, P, P, P, SZ, P]
     L.misa_workspace_bytes.argtypes = [I32] * 9
     L.misa_workspace_bytes.restype = ctypes.c_size_t
     L.misa_status_string.argtypes = [I32]
@@ -74,7 +76,7 @@ def lib():
     L.misa_profile_end.argtypes = [P, P, I32]
     L.misa_kernel_name.argtypes = [I32]
     L.misa_kernel_name.restype = ctypes.c_char_p
-    for f in ("misa_pool_keys", "misa_pool_update", "misa_route_heads", "misa_score_topk", "dsa_score_topk",
+    for f in ("misa_sparse_attention", "misa_pool_keys", "misa_pool_update", "misa_route_heads", "misa_score_topk", "dsa_score_topk",
               "misa_rerank", "misa_last_hip_error", "misa_profile_begin", "misa_profile_end"):
         getattr(L, f).restype = ctypes.c_int32
     _lib = L
@@ -268,6 +270,56 @@ def misa_rerank(q, w, k, q_seq, q_pos, cand, topk: int, k_scale=None, idx=None, 
         _ptr(score, "score", _F32, (N, topk)), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
         _stream(q)))
     return idx, score
+
+
+def misa_sparse_attention(q, kv, q_seq, idx, scale: float, d_v: int, out=None, lse=None, ws=None,
+                          block_table=None, page_size=0, L=None):
+    """Softmax attention of every head over each row's selected tokens
+    (idx [N, topk], -1 = empty); values are kv[..., :d_v].  Returns (out, lse)."""
+    N, H, d_qk = q.shape
+    S, L, _, kargs = _keys(kv, None, block_table, page_size, L, d_q=d_qk)
+    topk = idx.shape[1]
+    if out is None:
+        out = torch.empty((N, H, d_v), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((N, H), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(MISA_OP_ATTENTION, N, L, d_v, H, topk=topk, device=q.device)
+    _check("misa_sparse_attention", lib().misa_sparse_attention(
+        _ptr(q, "q", _KEYS), _dtype_code(q), kargs[0], kargs[2], kargs[3], kargs[4],
+        _ptr(q_seq, "q_seq", _I32, (N,)), _ptr(idx, "idx", _I32, (N, topk)), N, S, L, H, d_qk,
+        d_v, topk, float(scale), _ptr(out, "out", _F32, (N, H, d_v)),
+        _ptr(lse, "lse", _F32, (N, H)), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+        _stream(q)))
+    return out, lse
+
+
+class DeviceAttention:
+    """A synth.AttentionProblem on the device (bf16 tensors); page_size > 0
+    stores the cache rows as a paged cache (synth.to_pages)."""
+
+    def __init__(self, p, device="cuda", page_size: int = 0, page_seed: int = 0):
+        self.p = p
+
+        def up(a, dtype=None):
+            t = torch.from_numpy(np.ascontiguousarray(a))
+            return (t.view(dtype) if dtype is not None else t).to(device)
+
+        self.q = up(p.q.view(np.int16), torch.bfloat16)
+        kv = p.kv
+        self.kw = dict(L=None)
+        if page_size:
+            pages, _, table = synth.to_pages(kv, None, page_size, page_seed)
+            kv = pages
+            self.kw = dict(block_table=up(table), page_size=page_size, L=p.L)
+        self.kv = up(kv.view(np.int16), torch.bfloat16)
+        self.q_seq = up(p.q_seq)
+        self.idx = up(p.idx)
+
+    def run(self, idx=None, **kw):
+        return misa_sparse_attention(self.q, self.kv, self.q_seq,
+                                     self.idx if idx is None else idx, self.p.scale, self.p.d_v,
+                                     **self.kw, **kw)
 
 
 def misa_profile_begin(capacity: int):

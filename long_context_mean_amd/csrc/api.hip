@@ -24,6 +24,7 @@ constexpr int kCandMinL = 32768;      // shorter sequences keep the full path
 constexpr int kCandMaxTopk = 2048;    // about 2 topk candidates must fit the LDS select
 constexpr int kCandRegion = 16384;    // candidate slots per row, shared evenly by the splits
 constexpr int kMaxSplits = 256;
+constexpr int kMaxAttnHeads = 1024;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -135,6 +136,12 @@ size_t score_topk_bytes(int N, int L, int topk) {
   const TopkLayout t = topk_layout(N, L);
   if (!cand_eligible(N, L, topk)) return t.bytes;
   return cand_layout(t.bytes, N, L).bytes;
+}
+
+// sparse attention: per-split partial outputs, then (max, sum) pairs
+size_t attention_bytes(int N, int H, int d_v, int topk) {
+  const size_t parts = static_cast<size_t>(N) * H * misa::attn_splits(topk);
+  return align_up(parts * d_v * 4, 256) + align_up(parts * 8, 256);
 }
 
 size_t rerank_bytes(int N, int k_prime) {
@@ -317,6 +324,11 @@ int32_t misa_last_hip_error(void) { return g_last_hip; }
 
 size_t misa_workspace_bytes(int32_t op, int32_t q_dt, int32_t N, int32_t L, int32_t d,
                             int32_t H_I, int32_t B, int32_t topk, int32_t k_prime) {
+  if (op == MISA_OP_ATTENTION) {     // d = d_v, H_I = attention heads
+    if (N < 1 || N > kMaxN || L < 1 || L > kMaxL || H_I < 1 || H_I > kMaxAttnHeads) return 0;
+    if (d < 32 || d > 512 || d % 32 || topk < 1 || topk > kMaxTopk) return 0;
+    return attention_bytes(N, H_I, d, topk);
+  }
   if (N < 1 || N > kMaxN || L < 1 || L > kMaxL || H_I < 1 || H_I > 64) return 0;
   if (d != 64 && d != 128) return 0;
   if (q_dt != MISA_F32 && q_dt != MISA_BF16 && q_dt != MISA_FP8_E4M3) return 0;
@@ -450,6 +462,33 @@ int32_t misa_rerank(const void* q, int32_t q_dt, const float* q_scale, const flo
   return hip_status(misa::launch_topk(ta, st));
 }
 
+int32_t misa_sparse_attention(const void* q, int32_t q_dt, const void* kv, int32_t kv_dt,
+                              const int32_t* block_table, int32_t page_size,
+                              const int32_t* q_seq, const int32_t* idx, int32_t N, int32_t S,
+                              int32_t L, int32_t H, int32_t d_qk, int32_t d_v, int32_t topk,
+                              float scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (!q || !kv || !q_seq || !idx || !out || !lse) return MISA_ERR_NULL;
+  if (q_dt != MISA_BF16 || kv_dt != MISA_BF16) return MISA_ERR_UNSUPPORTED;
+  if (d_qk != 64 && d_qk != 128 && d_qk != 256 && d_qk != 576) return MISA_ERR_UNSUPPORTED;
+  if (d_v < 32 || d_v > 512 || d_v % 32 || d_v > d_qk) return MISA_ERR_SHAPE;
+  if (N < 1 || N > kMaxN || S < 1 || S > kMaxN || L < 1 || L > kMaxL) return MISA_ERR_SHAPE;
+  if (H < 1 || H > kMaxAttnHeads || topk < 1 || topk > kMaxTopk) return MISA_ERR_SHAPE;
+  if (!(scale > 0.f) || scale > 1e30f) return MISA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return MISA_ERR_SHAPE;
+  misa::KeyIndex ki;
+  int32_t rc = key_index(block_table, page_size, L, ki);
+  if (rc) return rc;
+  const size_t need = attention_bytes(N, H, d_v, topk);
+  if (!ws) return MISA_ERR_NULL;
+  if (ws_bytes < need) return MISA_ERR_WORKSPACE;
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  const size_t parts = static_cast<size_t>(N) * H * misa::attn_splits(topk);
+  misa::AttnArgs a{q, kv, ki, q_seq, idx, N, H, d_qk, d_v, topk, scale,
+                   reinterpret_cast<float*>(wsb), wsb + align_up(parts * d_v * 4, 256), out, lse};
+  return hip_status(misa::launch_attention(a, static_cast<hipStream_t>(stream)));
+}
+
 int32_t misa_profile_begin(int32_t capacity) {
   if (capacity < 1) return MISA_ERR_SHAPE;
   if (g_prof.on) (void)misa_profile_end(nullptr, nullptr, 0);
@@ -493,7 +532,8 @@ const char* misa_kernel_name(int32_t kernel_id) {
       "score_mfma_kernel", "score_f32_kernel",     "score_prefill_kernel",
       "topk_collect_kernel", "topk_final_kernel",   "topk_row_kernel",
       "score_prefill_sample", "score_prefill_full", "topk_tau_kernel", "topk_cand_kernel",
-      "route_split_kernel", "q8_prep_kernel", "pool_update_kernel"};
+      "route_split_kernel", "q8_prep_kernel", "pool_update_kernel", "attn_split_kernel",
+      "attn_combine_kernel"};
   if (kernel_id < 0 || kernel_id >= misa::K_COUNT_IDS) return "unknown";
   return names[kernel_id];
 }

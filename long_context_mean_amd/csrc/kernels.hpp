@@ -28,6 +28,8 @@ enum KernelId : int {
   K_ROUTE_SPLIT,
   K_Q8_PREP,
   K_POOL_UPDATE,
+  K_ATTN_SPLIT,
+  K_ATTN_COMBINE,
   K_COUNT_IDS
 };
 
@@ -212,5 +214,27 @@ struct CandTopkArgs {
 };
 int cand_topk_capacity();
 hipError_t launch_cand_topk(const CandTopkArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- sparse attention
+// Softmax attention of every head of each row over its selected tokens
+// (idx [N, topk], -1 = empty); cache rows [.., d_qk] bf16 addressed through
+// kidx, values = the first d_v elements of each row.  Splits of 64 selected
+// tokens write partials (o_part [N, H, splits, d_v], ml_part [N, H, splits]
+// float2) that a second kernel merges into out [N, H, d_v] and lse [N, H].
+struct AttnArgs {
+  const void* q;
+  const void* kv;
+  KeyIndex kidx;
+  const int32_t* q_seq;
+  const int32_t* idx;
+  int N, H, d_qk, d_v, topk;
+  float scale;
+  float* o_part;
+  void* ml_part;
+  float* out;
+  float* lse;
+};
+int attn_splits(int topk);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 
 }  // namespace misa

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from long_context_mean_amd import synth
-from long_context_mean_amd.binding import DeviceProblem
+from long_context_mean_amd.binding import DeviceAttention, DeviceProblem
 
 from parity import check_heads, check_topk, fp8_mfma_error_bound, recall, tol
 
@@ -686,3 +686,68 @@ def test_topk_at_the_limit():
     """k = 65536 (the largest the ABI takes) over 70000-token rows."""
     p = synth.small("kmax", 66, N=2, S=2, L=70000, d=64, H_I=16, h=4, B=256, topk=65536)
     check_misa(p)
+
+
+# ---------------------------------------------------------------- sparse attention (consumer)
+# Softmax attention over each row's selected tokens against the oracle:
+# outputs within 1e-3 relative / 1e-4 absolute, log-sum-exp likewise.
+def _check_attention(p, out, lse, ref=None):
+    ref_o, ref_l = oracle.sparse_attention(p.q, synth.BF16, p.kv, synth.BF16, p.q_seq, p.idx,
+                                           p.scale, p.d_v) if ref is None else ref
+    out, lse = np_(out).astype(np.float64), np_(lse).astype(np.float64)
+    empty = np.isneginf(ref_l)
+    assert np.array_equal(np.isneginf(lse), empty)
+    assert not out[empty].any()
+    err = np.abs(out - ref_o)
+    assert np.all(err <= tol(ref_o)), f"out err {err.max()} at {np.unravel_index(err.argmax(), err.shape)}"
+    e2 = np.abs(lse[~empty] - ref_l[~empty])
+    assert np.all(e2 <= tol(ref_l[~empty])), f"lse err {e2.max()}"
+    log(f"[attn] max out err {err.max():.3g}, max lse err {e2.max() if e2.size else 0:.3g}")
+
+
+@pytest.mark.parametrize("H,d_qk,d_v,topk", [(128, 576, 512, 300), (16, 128, 128, 2048),
+                                              (48, 256, 96, 130), (32, 64, 32, 64)])
+def test_sparse_attention_parity(H, d_qk, d_v, topk):
+    L = 3000
+    nv = np.array([topk, min(topk, 77), 1, 0, max(1, topk - 5)])
+    p = synth.attention_problem("attn", 101 + H, N=5, S=2, L=L, H=H, d_qk=d_qk, d_v=d_v,
+                                topk=topk, n_valid=np.minimum(nv, L))
+    log(f"[attn] H={H} d_qk={d_qk} d_v={d_v} topk={topk}")
+    out, lse = DeviceAttention(p).run()
+    _check_attention(p, out, lse)
+
+
+def test_sparse_attention_single_token_is_exact():
+    p = synth.attention_problem("attn1", 105, N=2, S=1, L=500, H=32, d_qk=576, d_v=512, topk=64,
+                                n_valid=np.array([1, 1]))
+    out, _ = DeviceAttention(p).run()
+    kv = synth.bf16_bits_to_f32(p.kv)
+    for n in range(2):
+        assert np.array_equal(np_(out)[n], np.tile(kv[0, p.idx[n, 0], :512], (32, 1)))
+
+
+@pytest.mark.parametrize("page_size", [16, 64])
+def test_sparse_attention_paged_byte_identical(page_size):
+    p = synth.attention_problem("attnp", 106, N=3, S=3, L=2000, H=64, d_qk=576, d_v=512,
+                                topk=512)
+    a = [np_(x) for x in DeviceAttention(p).run()]
+    b = [np_(x) for x in DeviceAttention(p, page_size=page_size, page_seed=9).run()]
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_indexer_selection_feeds_attention():
+    """The routed top-k of the indexer as the attention's selection: index keys
+    and a latent cache for the same 4 sequences, scored, selected, attended."""
+    L = 8000
+    pi = synth.small("ix", 107, N=4, S=4, L=L, d=128, H_I=64, h=8, B=128, topk=2048,
+                     q_pos=np.array([L - 1, 5000, 2047, 100], np.int32))
+    dp = DeviceProblem(pi)
+    heads, _ = dp.route(dp.pool())
+    idx, _ = dp.score_topk(heads)
+    sel = np_(idx)
+    p = synth.attention_problem("ixattn", 108, N=4, S=4, L=L, H=128, d_qk=576, d_v=512,
+                                topk=2048)
+    p = synth.AttentionProblem(p.name, p.q, p.kv, pi.q_seq, sel, p.d_v, p.scale)
+    out, lse = DeviceAttention(p).run()
+    assert (sel[3] >= 0).sum() == 101 and np.all(sel[3, :101] == np.arange(101))
+    _check_attention(p, out, lse)

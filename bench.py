@@ -265,6 +265,45 @@ class Serving:
         dp.score_topk(self.heads, idx=self.idx, score=None, ws=self.ws_score, want_score=False)
 
 
+def attention_extra(torch, binding, synth, idx, p, steps):
+    """Sparse attention of DeepSeek-V3.2-like decode rows (H = 128 heads,
+    576-element latent rows, values = their first 512 elements) over the
+    indexer's 2048 selected tokens per row; REPLICAS copies of the latent
+    cache rotate so the gathers are cold."""
+    import numpy as np
+
+    from long_context_mean_amd.binding import DeviceAttention
+    H, dqk, dv = 128, 576, 512
+    ap = synth.attention_problem("attn", 2001, N=p.N, S=p.S, L=p.L, H=H, d_qk=dqk, d_v=dv,
+                                 topk=p.topk, n_valid=np.zeros(p.N, np.int64))
+    da = DeviceAttention(ap)
+    kvs = [da.kv] + [da.kv.clone() for _ in range(REPLICAS - 1)]
+    sel = idx.clone()
+    out = torch.empty((p.N, H, dv), dtype=torch.float32, device="cuda")
+    lse = torch.empty((p.N, H), dtype=torch.float32, device="cuda")
+    ws = binding.workspace(binding.MISA_OP_ATTENTION, p.N, p.L, dv, H, topk=p.topk)
+
+    def step(i):
+        binding.misa_sparse_attention(da.q, kvs[i], da.q_seq, sel, ap.scale, dv, out=out,
+                                      lse=lse, ws=ws)
+    ms = timed(torch, step, steps, 5)
+    _, kt, _ = kernel_times(torch, binding, step, max(3, steps // 2), 1, 4)
+    nsel = int((sel >= 0).sum().item())
+    gathered = nsel * dqk * 2                                  # cache bytes read
+    flops = 2.0 * H * nsel * (dqk + dv)
+    sk = kt.get("attn_split_kernel")
+    del kvs, da
+    torch.cuda.empty_cache()
+    return {"sparse_attention_ms": round(ms, 4),
+            "sparse_attention_kernel_ms": {k: round(v, 5) for k, v in kt.items()},
+            "sparse_attention_shape": f"{p.N} rows x {H} heads x {nsel // p.N} selected tokens, "
+                                      f"d_qk={dqk}, d_v={dv}",
+            "sparse_attention_split_kernel_gbs": round(gathered / (sk * 1e-3) / 1e9, 1)
+            if sk else None,
+            "sparse_attention_split_kernel_tflops": round(flops / (sk * 1e-3) / 1e12, 1)
+            if sk else None}
+
+
 def timed(torch, fn, steps, warmup):
     for s in range(warmup):
         fn(s % REPLICAS)
@@ -557,6 +596,8 @@ def main():
             [np.isin(p.needles[n, :, 0], dense_idx[n]).mean() for n in range(p.N)])), 4)
         del rep
         torch.cuda.empty_cache()
+        log("[bench] sparse attention over the selected tokens (128 heads, 576/512 latent rows)")
+        extra.update(attention_extra(torch, binding, synth, srv.idx, p, args.steps))
         log("[bench] the serving step on a paged key cache (pages of 64 tokens)")
         del srv
         pg = Serving(p, torch, binding, h, page_size=64)

@@ -8,10 +8,12 @@
 //   s_t = scale * q_h . kv_t,   out_h = sum_t softmax(s)_t kv_t[0:d_v],
 //   lse_h = log sum_t exp(s_t)
 //
-// attn_split_kernel: one workgroup per (64-token split of the selection,
-// block of 32 heads, row).  The split's rows are gathered once into LDS
-// (padded rows: conflict-free for both read patterns below).  Wavefront w
-// owns heads 16*(w/2) .. +15 of the block and half of d_v.
+// attn_split_kernel: one workgroup per (split of the selection, block of 32
+// heads, row).  A split is a few chunks of 64 selected tokens, handled in
+// turn with an online softmax (running max, rescaled sum and output); each
+// chunk's rows are gathered into LDS (padded rows: conflict-free for both
+// read patterns below).  Wavefront w owns heads 16*(w/2) .. +15 of the block
+// and half of d_v, whose output stays in registers across the chunks.
 //  - S^T = K Q^T on v_mfma_f32_16x16x32_bf16: A = 16 cached rows from LDS,
 //    B = the wavefront's query heads (registers).  Output lane (g, c) holds
 //    tokens 4g..4g+3 of head c, so each head's max and sum over the split
@@ -24,6 +26,8 @@
 //    hi + lo parts (two MFMAs), so the products carry ~2^-17 relative error.
 // The split's partial (sum_t p_t v_t, max, sum_t p_t) goes to the workspace;
 // attn_combine_kernel merges the splits of each (row, head).
+#include <cstdlib>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -33,7 +37,7 @@ namespace {
 typedef short bf16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kSplitTok = 64;          // selected tokens per workgroup
+constexpr int kChunkTok = 64;          // selected tokens per chunk (one LDS fill)
 constexpr int kHeadBlock = 32;         // heads per workgroup (16 per wavefront pair)
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -43,7 +47,7 @@ struct AttnParams {
   KeyIndex ki;
   const int32_t* q_seq;
   const int32_t* idx;       // [N, topk]
-  int N, H, dv, topk, splits;
+  int N, H, dv, topk, splits, chunks;   // chunks of kChunkTok tokens per split
   float scale2;             // softmax scale * log2(e)
   float* o_part;            // [N, H, splits, dv]: sum_t p_t v_t over the split
   float2* ml_part;          // [N, H, splits]: (max in log2 units, sum_t p_t)
@@ -59,44 +63,15 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
   constexpr int DQK = KK * 32;
   constexpr int ROWP = DQK * 2 + 16;                    // padded LDS row (bytes)
   constexpr int PIECES = DQK * 2 / 16;                  // 16-byte pieces per row
-  __shared__ __align__(16) uint8_t kvt[kSplitTok * ROWP];
-  __shared__ int tok_lds[kSplitTok];
+  constexpr int MAXDVT = 16;                            // value tiles per wavefront (d_v <= 512)
+  __shared__ __align__(16) uint8_t kvt[kChunkTok * ROWP];
+  __shared__ int tok_lds[kChunkTok];
 
   const int sp = blockIdx.x, hb = blockIdx.y, n = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(tid >> 6));
   const int g = lane >> 4, c = lane & 15;
   const int s = p.q_seq[n];
-  if (tid < kSplitTok) {
-    const int e = sp * kSplitTok + tid;
-    tok_lds[tid] = e < p.topk ? p.idx[static_cast<size_t>(n) * p.topk + e] : -1;
-  }
-  __syncthreads();
-
-  // gather the split's cache rows (unselected slots read token 0, masked below)
-  constexpr int TOTAL = kSplitTok * PIECES;
-  constexpr int BATCH = 6;
-  for (int base = 0; base < TOTAL; base += 256 * BATCH) {
-    u32x4_t x[BATCH];
-#pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      const int f = base + b * 256 + tid;
-      if (f < TOTAL) {
-        const int r = f / PIECES, pc = f % PIECES;
-        const int t = tok_lds[r];
-        const size_t row = p.ki.row(s, t >= 0 ? t : 0);
-        x[b] = *reinterpret_cast<const u32x4_t*>(p.kv + row * (DQK * 2) + 16 * pc);
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      const int f = base + b * 256 + tid;
-      if (f < TOTAL) {
-        const int r = f / PIECES, pc = f % PIECES;
-        *reinterpret_cast<u32x4_t*>(kvt + r * ROWP + 16 * pc) = x[b];
-      }
-    }
-  }
 
   // this wavefront's query heads as the B operand: lane (g, c) = head c,
   // d elements 32kk + 8g .. +7
@@ -112,78 +87,129 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
       qf[kk] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
-  __syncthreads();
-
-  // S^T for the split's 4 tiles of 16 tokens, in log2 units; unselected -inf
-  float sv[4][4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    const uint8_t* arow = kvt + (16 * t + c) * ROWP + 16 * g;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t,
-                                            *reinterpret_cast<const u32x4_t*>(arow + 64 * kk));
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], acc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sv[t][i] = tok_lds[16 * t + 4 * g + i] >= 0 ? acc[i] * p.scale2 : -__builtin_inff();
-  }
-  float m = -__builtin_inff();
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) m = fmaxf(m, sv[t][i]);
-  m = fmaxf(m, __shfl_xor(m, 16, 64));
-  m = fmaxf(m, __shfl_xor(m, 32, 64));
-  // P^T as bf16 hi + lo (B operand of the 16x16x16 MFMA: k = tokens 4g..4g+3)
-  float l = 0.f;
-  bf16x4_t phi[4], plo[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    uint32_t h[4], lo[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pv = m == -__builtin_inff() ? 0.f : exp2f(sv[t][i] - m);
-      l += pv;
-      h[i] = bf16_rne(pv);
-      lo[i] = bf16_rne(pv - __uint_as_float(h[i] << 16));
-    }
-    phi[t] = bf16x4_t{static_cast<short>(h[0]), static_cast<short>(h[1]),
-                      static_cast<short>(h[2]), static_cast<short>(h[3])};
-    plo[t] = bf16x4_t{static_cast<short>(lo[0]), static_cast<short>(lo[1]),
-                      static_cast<short>(lo[2]), static_cast<short>(lo[3])};
-  }
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-
-  // O^T over this wavefront's half of d_v, 16 value columns per tile
   const int half = p.dv / 2;
+  const int dvt = half / 16;                            // value tiles of this wavefront
   const int dv0 = (wave & 1) * half;
-  const int r4 = lane & 15;                               // 4m + q within the lane group
-  typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
-  for (int j0 = 0; j0 < half; j0 += 16) {
-    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+  const int r4 = lane & 15;                             // 4m + q within the lane group
+  f32x4_t o[MAXDVT];
+#pragma unroll
+  for (int j = 0; j < MAXDVT; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_inff(), l_run = 0.f;         // per head c, in log2 units
+
+  for (int ch = 0; ch < p.chunks; ++ch) {
+    const int e0 = (sp * p.chunks + ch) * kChunkTok;
+    if (e0 >= p.topk) break;                            // uniform over the workgroup
+    __syncthreads();                                    // the previous chunk's reads are done
+    if (tid < kChunkTok) {
+      const int e = e0 + tid;
+      tok_lds[tid] = e < p.topk ? p.idx[static_cast<size_t>(n) * p.topk + e] : -1;
+    }
+    __syncthreads();
+    // gather the chunk's cache rows (unselected slots read token 0, masked below)
+    constexpr int TOTAL = kChunkTok * PIECES;
+    constexpr int BATCH = 6;
+    for (int base = 0; base < TOTAL; base += 256 * BATCH) {
+      u32x4_t x[BATCH];
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        const int f = base + b * 256 + tid;
+        if (f < TOTAL) {
+          const int r = f / PIECES, pc = f % PIECES;
+          const int t = tok_lds[r];
+          const size_t row = p.ki.row(s, t >= 0 ? t : 0);
+          x[b] = *reinterpret_cast<const u32x4_t*>(p.kv + row * (DQK * 2) + 16 * pc);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        const int f = base + b * 256 + tid;
+        if (f < TOTAL) {
+          const int r = f / PIECES, pc = f % PIECES;
+          *reinterpret_cast<u32x4_t*>(kvt + r * ROWP + 16 * pc) = x[b];
+        }
+      }
+    }
+    __syncthreads();
+
+    // S^T for the chunk's 4 tiles of 16 tokens, in log2 units; unselected -inf
+    float sv[4][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int row = 16 * t + 4 * g + (r4 >> 2);
-      const int col = dv0 + j0 + 4 * (r4 & 3);
-      // generic -> LDS address space (a C-style cast is the address-space cast)
-      lds_bf16x4_t* ap = (lds_bf16x4_t*)((__attribute__((address_space(3))) uint8_t*)kvt +
-                                         row * ROWP + col * 2);
-      const bf16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(ap);
-      o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi[t], o, 0, 0, 0);
-      o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo[t], o, 0, 0, 0);
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      const uint8_t* arow = kvt + (16 * t + c) * ROWP + 16 * g;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const bf16x8_t a = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(arow + 64 * kk));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sv[t][i] = tok_lds[16 * t + 4 * g + i] >= 0 ? acc[i] * p.scale2 : -__builtin_inff();
     }
-    if (hv) {
-      float* op = p.o_part + ((static_cast<size_t>(n) * p.H + head) * p.splits + sp) * p.dv +
-                  dv0 + j0 + 4 * g;
-      *reinterpret_cast<f32x4_t*>(op) = o;
+    float m_c = -__builtin_inff();
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m_c = fmaxf(m_c, sv[t][i]);
+    m_c = fmaxf(m_c, __shfl_xor(m_c, 16, 64));
+    m_c = fmaxf(m_c, __shfl_xor(m_c, 32, 64));
+    const float m_new = fmaxf(m_run, m_c);
+    if (m_new == -__builtin_inff()) continue;           // nothing selected so far (uniform per head)
+    const float alpha = exp2f(m_run - m_new);           // 0 when m_run is -inf
+    // P^T as bf16 hi + lo (B operand of the 16x16x16 MFMA: k = tokens 4g..4g+3)
+    float lc = 0.f;
+    bf16x4_t phi[4], plo[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint32_t h[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = exp2f(sv[t][i] - m_new);
+        lc += pv;
+        h[i] = bf16_rne(pv);
+        lo[i] = bf16_rne(pv - __uint_as_float(h[i] << 16));
+      }
+      phi[t] = bf16x4_t{static_cast<short>(h[0]), static_cast<short>(h[1]),
+                        static_cast<short>(h[2]), static_cast<short>(h[3])};
+      plo[t] = bf16x4_t{static_cast<short>(lo[0]), static_cast<short>(lo[1]),
+                        static_cast<short>(lo[2]), static_cast<short>(lo[3])};
+    }
+    lc += __shfl_xor(lc, 16, 64);
+    lc += __shfl_xor(lc, 32, 64);
+    l_run = l_run * alpha + lc;
+    m_run = m_new;
+
+    // O^T (this wavefront's half of d_v, 16 value columns per tile) += V^T P^T
+    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+#pragma unroll
+    for (int j = 0; j < MAXDVT; ++j) {
+      if (j < dvt) {
+        f32x4_t acc = o[j] * alpha;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int row = 16 * t + 4 * g + (r4 >> 2);
+          const int col = dv0 + 16 * j + 4 * (r4 & 3);
+          // generic -> LDS address space (a C-style cast is the address-space cast)
+          lds_bf16x4_t* ap = (lds_bf16x4_t*)((__attribute__((address_space(3))) uint8_t*)kvt +
+                                             row * ROWP + col * 2);
+          const bf16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(ap);
+          acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi[t], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo[t], acc, 0, 0, 0);
+        }
+        o[j] = acc;
+      }
     }
   }
-  if (hv && g == 0 && (wave & 1) == 0)
-    p.ml_part[(static_cast<size_t>(n) * p.H + head) * p.splits + sp] = make_float2(m, l);
+  if (hv) {
+    float* op = p.o_part + ((static_cast<size_t>(n) * p.H + head) * p.splits + sp) * p.dv +
+                dv0 + 4 * g;
+#pragma unroll
+    for (int j = 0; j < MAXDVT; ++j)
+      if (j < dvt) *reinterpret_cast<f32x4_t*>(op + 16 * j) = o[j];
+    if (g == 0 && (wave & 1) == 0)
+      p.ml_part[(static_cast<size_t>(n) * p.H + head) * p.splits + sp] = make_float2(m_run, l_run);
+  }
 }
 
 // One workgroup per (row, head): out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
@@ -215,11 +241,25 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   Ls = red[0] + red[1] + red[2] + red[3];
   const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
   const float* op = o_part + nh * splits * dv;
+  // splits in groups of 8 independent loads (a split with no selected token
+  // holds zeros, so its weight may be anything finite)
   for (int d = threadIdx.x; d < dv; d += 256) {
     float acc = 0.f;
-    for (int i = 0; i < splits; ++i) {
+    int i = 0;
+    for (; i + 8 <= splits; i += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = op[static_cast<size_t>(i + u) * dv + d];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = i + u;
+        const float wgt = k < 1024 ? wsh[k] : (M == -__builtin_inff() ? 0.f : exp2f(ml[k].x - M));
+        acc += wgt * v[u];
+      }
+    }
+    for (; i < splits; ++i) {
       const float wgt = i < 1024 ? wsh[i] : (M == -__builtin_inff() ? 0.f : exp2f(ml[i].x - M));
-      if (wgt != 0.f) acc += wgt * op[static_cast<size_t>(i) * dv + d];
+      acc += wgt * op[static_cast<size_t>(i) * dv + d];
     }
     out[nh * dv + d] = acc * inv;
   }
@@ -240,6 +280,7 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
   p.dv = a.d_v;
   p.topk = a.topk;
   p.splits = attn_splits(a.topk);
+  p.chunks = attn_chunks_per_split(a.topk);
   p.scale2 = a.scale * kLog2e;
   p.o_part = a.o_part;
   p.ml_part = reinterpret_cast<float2*>(a.ml_part);
@@ -255,7 +296,23 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int attn_splits(int topk) { return (topk + kSplitTok - 1) / kSplitTok; }
+// Chunks of 64 selected tokens per workgroup (MISA_ATTN_CHUNKS overrides;
+// launch-shape tuning only).
+int attn_chunks_per_split(int topk) {
+  static const int env = [] {
+    const char* v = getenv("MISA_ATTN_CHUNKS");
+    return v ? atoi(v) : 0;
+  }();
+  const int chunks = (topk + kChunkTok - 1) / kChunkTok;
+  const int per = env > 0 ? env : 2;
+  return per < chunks ? per : chunks;
+}
+
+int attn_splits(int topk) {
+  const int chunks = (topk + kChunkTok - 1) / kChunkTok;
+  const int per = attn_chunks_per_split(topk);
+  return (chunks + per - 1) / per;
+}
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   switch (a.d_qk) {

@@ -235,6 +235,7 @@ struct AttnArgs {
   float* lse;
 };
 int attn_splits(int topk);
+int attn_chunks_per_split(int topk);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 
 }  // namespace misa

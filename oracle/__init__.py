@@ -46,12 +46,14 @@ def _load():
     lib.misa_ref_score_topk.argtypes = common + [P] + [I] * 7 + [P, P, P, P]
     lib.dsa_ref_score_topk.argtypes = common + [I] * 6 + [P, P, P, P]
     lib.misa_ref_rerank.argtypes = common + [P] + [I] * 7 + [P, P, P, P]
+    lib.misa_ref_score_topk_blocks.argtypes = common + [P] + [I] * 9 + [P, P, P]
     lib.misa_ref_sparse_attention.argtypes = [P, I, P, I, P, P] + [I] * 7 + [ctypes.c_double,
                                                                               P, P]
     lib.misa_ref_max_threads.argtypes = []
     for f in ("misa_ref_decode", "misa_ref_pool_keys", "misa_ref_route_heads",
               "misa_ref_scores", "misa_ref_score_topk", "dsa_ref_score_topk",
-              "misa_ref_rerank", "misa_ref_sparse_attention", "misa_ref_max_threads"):
+              "misa_ref_rerank", "misa_ref_sparse_attention", "misa_ref_score_topk_blocks",
+              "misa_ref_max_threads"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -179,6 +181,24 @@ def rerank(p, cand, topk=None, mac=None):
                                  _p(cd), N, p.k.shape[0], p.k.shape[1], d, H_I, cd.shape[1], topk,
                                  _p(idx), _p(sc), _p(kth), _p(mac)), "rerank")
     return idx, sc, kth
+
+
+def score_topk_blocks(p, heads, m_blocks, topk=None):
+    """Routed scoring over the m_blocks best blocks (see misa_ref.h).  Returns
+    (blocks [N, m_blocks] ascending, idx [N, topk] in (score desc, index asc)
+    order, score [N, topk])."""
+    topk = p.topk if topk is None else topk
+    q, qsc, w, k, ks, sq, qp = _args(p)
+    N, H_I, d = q.shape
+    hd = _c(heads, np.int32)
+    blocks = np.empty((N, m_blocks), dtype=np.int32)
+    idx = np.empty((N, topk), dtype=np.int32)
+    sc = np.empty((N, topk), dtype=np.float64)
+    _check(lib().misa_ref_score_topk_blocks(_p(q), p.q_dt, _p(qsc), _p(w), _p(k), _p(ks), p.k_dt,
+                                            _p(sq), _p(qp), _p(hd), N, p.k.shape[0], p.k.shape[1],
+                                            d, p.B, H_I, hd.shape[1], m_blocks, topk,
+                                            _p(blocks), _p(idx), _p(sc)), "score_topk_blocks")
+    return blocks, idx, sc
 
 
 def misa(p, h=None, topk=None, mac=None):

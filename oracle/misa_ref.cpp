@@ -345,6 +345,72 @@ int misa_ref_rerank(const void* q, int q_dt, const float* q_scale, const float* 
   return 0;
 }
 
+int misa_ref_score_topk_blocks(const void* q, int q_dt, const float* q_scale, const float* w,
+                               const void* k, const float* k_scale, int k_dt,
+                               const int32_t* q_seq, const int32_t* q_pos, const int32_t* heads,
+                               int N, int S, int L, int d, int B, int H_I, int h, int m_blocks,
+                               int topk, int32_t* blocks, int32_t* idx, double* score) {
+  int rc = check_common(q, q_dt, q_scale, w, k, k_scale, k_dt, q_seq, q_pos, N, S, L, d, H_I);
+  if (rc) return rc;
+  if (!heads || !blocks || !idx) return 1;
+  if (B < 1 || h < 1 || h > H_I || m_blocks < 1 || topk < 1) return 2;
+  for (int n = 0; n < N; ++n) {
+    const int Ln = q_pos[n] + 1, s = q_seq[n];
+    const int Mn = (Ln + B - 1) / B;
+    const std::vector<int> hs = heads_of(heads, n, h, H_I);
+    const std::vector<double> qh = query_heads(q, q_dt, q_scale, n, H_I, d);
+    // block keys: means of the row's visible keys of each block
+    std::vector<double> bsc(Mn);
+    std::vector<int32_t> bid(Mn);
+    std::vector<double> mean(d), kr(d);
+    for (int b = 0; b < Mn; ++b) {
+      const int t0 = b * B, t1 = std::min((b + 1) * B, Ln);
+      std::fill(mean.begin(), mean.end(), 0.0);
+      for (int t = t0; t < t1; ++t) {
+        key_row(k, k_scale, k_dt, L, d, s, t, kr.data());
+        for (int i = 0; i < d; ++i) mean[i] += kr[i];
+      }
+      for (int i = 0; i < d; ++i) mean[i] /= (t1 - t0);
+      double acc = 0.0;
+      for (int j : hs)
+        acc += static_cast<double>(w[static_cast<int64_t>(n) * H_I + j]) *
+               relu(dot(&qh[static_cast<size_t>(j) * d], mean.data(), d));
+      bsc[b] = acc;
+      bid[b] = b;
+    }
+    // the m highest block scores (ties: lower block), listed ascending
+    std::vector<int32_t> kept(m_blocks);
+    select_topk(bsc, bid, m_blocks, kept.data(), nullptr, nullptr);
+    std::vector<int32_t> kb;
+    for (int32_t b : kept)
+      if (b >= 0) kb.push_back(b);
+    std::sort(kb.begin(), kb.end());
+    for (int i = 0; i < m_blocks; ++i)
+      blocks[static_cast<int64_t>(n) * m_blocks + i] = i < static_cast<int>(kb.size()) ? kb[i] : -1;
+    // token scores over the kept blocks' visible tokens, then the top-k
+    std::vector<int32_t> tok;
+    for (int32_t b : kb)
+      for (int t = b * B; t < std::min((b + 1) * B, Ln); ++t) tok.push_back(t);
+    std::vector<double> sc(tok.size());
+#pragma omp parallel
+    {
+      std::vector<double> kt(d);
+#pragma omp for schedule(static)
+      for (int64_t c = 0; c < static_cast<int64_t>(tok.size()); ++c) {
+        key_row(k, k_scale, k_dt, L, d, s, tok[c], kt.data());
+        double acc = 0.0;
+        for (int j : hs)
+          acc += static_cast<double>(w[static_cast<int64_t>(n) * H_I + j]) *
+                 relu(dot(&qh[static_cast<size_t>(j) * d], kt.data(), d));
+        sc[c] = acc;
+      }
+    }
+    select_topk(sc, tok, topk, idx + static_cast<int64_t>(n) * topk,
+                score ? score + static_cast<int64_t>(n) * topk : nullptr, nullptr);
+  }
+  return 0;
+}
+
 int misa_ref_sparse_attention(const void* q, int q_dt, const void* kv, int kv_dt,
                               const int32_t* q_seq, const int32_t* idx, int N, int S, int L,
                               int H, int d_qk, int d_v, int topk, double scale, double* out,

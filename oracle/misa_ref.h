@@ -98,6 +98,25 @@ int misa_ref_rerank(const void* q, int q_dt, const float* q_scale, const float* 
                     const int32_t* cand, int N, int S, int L, int d, int H_I, int k_prime,
                     int topk, int32_t* idx, double* score, double* kth, uint64_t* mac);
 
+/* Routed scoring with a block prefilter: head routing composed with a
+ * token-axis hierarchy (the MISA pages call head-axis routing complementary
+ * to token-axis hierarchies, technical summary "Key contributions"; HISA,
+ * gonzo_ML TL;DR: a coarse block-level filter, then token-level refinement
+ * that keeps the exact top-k output).  For row n with routed heads
+ * heads[n,:]:
+ *   block b (b < M_n = ceil(L_n / B)) has the key mean of the row's visible
+ *   keys b*B .. min((b+1)*B, L_n) - 1 and the score
+ *   I_blk(b) = sum_{j routed} w_j ReLU(q_j . mean_b);
+ *   the m_blocks blocks first under (I_blk desc, block asc) are kept and
+ *   listed ascending in blocks [N, m_blocks] (-1 padding);
+ *   the top-k (score desc, index asc) of the routed token scores over the
+ *   kept blocks' visible tokens goes to idx/score [N, topk] (-1 / -inf pad). */
+int misa_ref_score_topk_blocks(const void* q, int q_dt, const float* q_scale, const float* w,
+                               const void* k, const float* k_scale, int k_dt,
+                               const int32_t* q_seq, const int32_t* q_pos, const int32_t* heads,
+                               int N, int S, int L, int d, int B, int H_I, int h, int m_blocks,
+                               int topk, int32_t* blocks, int32_t* idx, double* score);
+
 /* Sparse attention over the selected tokens (the consumer of the top-k: the
  * indexer picks the tokens the main attention reads [MISA abstract, HF Daily
  * Papers digest; technical summary, "Problem statement"]; the attention

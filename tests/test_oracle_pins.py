@@ -481,3 +481,57 @@ def test_attention_is_order_invariant_and_checks_indices():
     bad[1, 0] = 400
     with pytest.raises(oracle.OracleError):
         _attn(synth.AttentionProblem("r", p.q, p.kv, p.q_seq, bad, p.d_v, p.scale))
+
+
+# ---------------------------------------------------------------- block prefilter (routing x token hierarchy)
+def test_blocks_all_kept_equals_misa():
+    """m_blocks >= M_n keeps every block, so the result is MISA's routed top-k."""
+    p = synth.small("bk1", 61, N=3, S=2, L=1000, d=64, H_I=12, h=4, B=64, topk=90,
+                    q_pos=np.array([999, 300, 64], np.int32))
+    heads, _ = oracle.route_heads(p)
+    blocks, idx, sc = oracle.score_topk_blocks(p, heads, m_blocks=16)
+    ref_idx, ref_sc, _ = oracle.score_topk(p, heads)
+    assert np.array_equal(idx, ref_idx) and np.array_equal(sc, ref_sc)
+    for n in range(p.N):
+        Mn = -(-(p.q_pos[n] + 1) // p.B)
+        assert np.array_equal(blocks[n, :Mn], np.arange(Mn)) and np.all(blocks[n, Mn:] == -1)
+
+
+def test_blocks_of_one_token_equal_misa():
+    """B = 1: a block is a token and its score is the token's score, so with
+    m_blocks >= k the k best tokens survive the filter."""
+    p = synth.small("bk2", 62, N=2, S=2, L=400, d=64, H_I=8, h=3, B=1, topk=30,
+                    q_pos=np.array([399, 120], np.int32))
+    heads, _ = oracle.route_heads(p)
+    _, idx, sc = oracle.score_topk_blocks(p, heads, m_blocks=45)
+    ref_idx, ref_sc, _ = oracle.score_topk(p, heads)
+    assert np.array_equal(idx, ref_idx)
+    np.testing.assert_allclose(sc, ref_sc, rtol=1e-12)
+
+
+def test_blocks_closed_form():
+    """Kept blocks == the m best by a float64 BLAS block score of the block
+    means (partial last block: mean of the visible keys), ties to the lower
+    block; every selected token lies in a kept block and the selection is
+    the top-k of the routed token scores restricted to those blocks."""
+    p = synth.small("bk3", 63, N=3, S=2, L=900, d=64, H_I=10, h=3, B=64, topk=70,
+                    q_pos=np.array([899, 500, 40], np.int32))
+    heads, _ = oracle.route_heads(p)
+    m = 4
+    blocks, idx, sc = oracle.score_topk_blocks(p, heads, m_blocks=m)
+    q = synth.bf16_bits_to_f32(p.q).astype(np.float64)
+    k = synth.bf16_bits_to_f32(p.k).astype(np.float64)
+    full = oracle.scores(p, heads)
+    for n in range(p.N):
+        Ln = p.q_pos[n] + 1
+        Mn = -(-Ln // p.B)
+        means = np.stack([k[p.q_seq[n], b * p.B:min((b + 1) * p.B, Ln)].mean(0) for b in range(Mn)])
+        dots = q[n, heads[n]] @ means.T
+        bs = (p.w[n, heads[n]].astype(np.float64)[:, None] * np.maximum(dots, 0)).sum(0)
+        order = np.lexsort((np.arange(Mn), -bs))[:m]
+        kept = np.sort(order)
+        assert np.array_equal(blocks[n, :len(kept)], kept)
+        toks = np.concatenate([np.arange(b * p.B, min((b + 1) * p.B, Ln)) for b in kept])
+        ref = toks[np.lexsort((toks, -full[n, toks]))][:p.topk]
+        got = idx[n][idx[n] >= 0]
+        assert np.array_equal(got, ref)

@@ -535,3 +535,23 @@ def test_blocks_closed_form():
         ref = toks[np.lexsort((toks, -full[n, toks]))][:p.topk]
         got = idx[n][idx[n] >= 0]
         assert np.array_equal(got, ref)
+
+
+def test_blocks_partial_block_uses_its_visible_mean():
+    """A partial last block of 2 visible keys aligned with the routed heads:
+    its visible-key mean makes it the best block (kept alone with m = 1);
+    averaging over B (or over future keys) would bury it."""
+    p = synth.small("bk4", 64, N=1, S=1, L=260, d=64, H_I=4, h=4, B=64, topk=5,
+                    q_pos=np.array([193], np.int32), q_dt=synth.F32, k_dt=synth.F32)
+    k = p.k.copy()
+    w = np.abs(p.w).astype(np.float32)
+    q = p.q.astype(np.float32)
+    k[0, 192] = 4 * q[0].sum(0)
+    k[0, 193] = 4 * q[0].sum(0)
+    k[0, 194:] = -k[0, 192]                      # future keys: never visible to the row
+    p = synth.Problem("bk4", q, synth.F32, w, k, synth.F32, None, p.q_seq, p.q_pos, p.B, p.h,
+                      p.topk)
+    heads = np.arange(4, dtype=np.int32)[None, :]
+    blocks, idx, _ = oracle.score_topk_blocks(p, heads, m_blocks=1)
+    assert blocks[0, 0] == 3
+    assert sorted(idx[0][idx[0] >= 0].tolist()) == [192, 193]

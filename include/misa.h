@@ -93,7 +93,8 @@ typedef enum {
   MISA_OP_ROUTE = 0,        /* misa_route_heads */
   MISA_OP_SCORE_TOPK = 1,   /* misa_score_topk (also dsa_score_topk) */
   MISA_OP_RERANK = 2,       /* misa_rerank */
-  MISA_OP_ATTENTION = 3     /* misa_sparse_attention (d = d_v, H_I = heads) */
+  MISA_OP_ATTENTION = 3,    /* misa_sparse_attention (d = d_v, H_I = heads) */
+  MISA_OP_BLOCKS = 4        /* misa_score_topk_blocks (k_prime = m_blocks) */
 } misa_op;
 
 /*
@@ -193,6 +194,35 @@ int32_t misa_rerank(const void* q, int32_t q_dt, const float* q_scale, const flo
                     const int32_t* cand, int32_t N, int32_t S, int32_t L, int32_t d, int32_t H_I,
                     int32_t k_prime, int32_t topk, int32_t* idx, float* score, void* ws,
                     size_t ws_bytes, void* stream);
+
+/*
+ * Routed scoring behind a block prefilter: head routing composed with a
+ * token-axis hierarchy (the MISA pages call head-axis routing complementary
+ * to token-axis hierarchies, technical summary "Key contributions"; HISA,
+ * gonzo_ML TL;DR: a coarse block-level filter, then token-level refinement
+ * that keeps the exact top-k output).  For row n with routed heads heads[n,:]:
+ *   block b < M_n = ceil(L_n / B) has key kbar (complete blocks: the pooled
+ *   table from misa_pool_keys / misa_pool_update; a partial last block: the
+ *   mean of the row's visible keys of that block, read from k) and score
+ *   I_blk(b) = sum_{j routed} w[n,j] * ReLU(q[n,j,:] . kbar_b);
+ *   the m_blocks blocks first under (I_blk desc, block asc) are kept; blocks
+ *   [N, m_blocks] (may be NULL) receives them ascending, -1 padded;
+ *   idx/score [N, topk] receive the routed top-k (as misa_score_topk) over the
+ *   kept blocks' visible tokens.
+ * m_blocks >= M_n gives exactly misa_score_topk's result.  Requires
+ * m_blocks * B <= 65536 and 1 <= topk <= m_blocks * B.  Cost per row:
+ * O(h M d) for the block scores plus O(h m_blocks B d) token scoring, instead
+ * of O(h L d).  Workspace: misa_workspace_bytes(MISA_OP_BLOCKS, q_dt, N, L, d,
+ * H_I, B, topk, m_blocks).
+ */
+int32_t misa_score_topk_blocks(const void* q, int32_t q_dt, const float* q_scale, const float* w,
+                               const float* kbar, const void* k, const float* k_scale,
+                               int32_t k_dt, const int32_t* block_table, int32_t page_size,
+                               const int32_t* q_seq, const int32_t* q_pos, const int32_t* heads,
+                               int32_t N, int32_t S, int32_t L, int32_t d, int32_t B,
+                               int32_t H_I, int32_t h, int32_t m_blocks, int32_t topk,
+                               int32_t* blocks, int32_t* idx, float* score, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /*
  * Sparse attention over the selected tokens: the consumer of the top-k (the

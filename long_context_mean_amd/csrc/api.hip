@@ -144,6 +144,30 @@ size_t attention_bytes(int N, int H, int d_v, int topk) {
   return align_up(parts * d_v * 4, 256) + align_up(parts * 8, 256);
 }
 
+// block prefilter: block keys, row lengths, kept blocks, candidate tokens,
+// candidate order keys
+struct BlocksLayout {
+  int ub_stride = 0, u_stride = 0;
+  size_t off_last = 0, off_blocks = 0, off_cand = 0, off_u = 0, bytes = 0;
+};
+
+BlocksLayout blocks_layout(int N, int L, int B, int m) {
+  BlocksLayout b;
+  const int mmax = (L + B - 1) / B;
+  b.ub_stride = topk_layout(kOneRowMinN, mmax).u_stride;
+  b.u_stride = topk_layout(kOneRowMinN, m * B).u_stride;
+  size_t off = align_up(static_cast<size_t>(N) * b.ub_stride * 4, 256);
+  b.off_last = off;
+  off = align_up(off + static_cast<size_t>(N) * 4, 256);
+  b.off_blocks = off;
+  off = align_up(off + static_cast<size_t>(N) * m * 4, 256);
+  b.off_cand = off;
+  off = align_up(off + static_cast<size_t>(N) * m * B * 4, 256);
+  b.off_u = off;
+  b.bytes = align_up(off + static_cast<size_t>(N) * b.u_stride * 4, 256);
+  return b;
+}
+
 size_t rerank_bytes(int N, int k_prime) {
   const TopkLayout t = topk_layout(kOneRowMinN, k_prime);   // always one row per workgroup
   return align_up(static_cast<size_t>(N) * t.u_stride * 4, 256);
@@ -343,6 +367,11 @@ size_t misa_workspace_bytes(int32_t op, int32_t q_dt, int32_t N, int32_t L, int3
     case MISA_OP_RERANK:
       if (k_prime < 1 || k_prime > kMaxTopk) return 0;
       return rerank_bytes(N, k_prime) + extra;
+    case MISA_OP_BLOCKS:            // k_prime = m_blocks
+      if (B < 1 || B > 1024 || k_prime < 1 || static_cast<int64_t>(k_prime) * B > kMaxTopk)
+        return 0;
+      if (topk < 1 || topk > k_prime * B) return 0;
+      return blocks_layout(N, L, B, k_prime).bytes + extra;
     default:
       return 0;
   }
@@ -462,6 +491,57 @@ int32_t misa_rerank(const void* q, int32_t q_dt, const float* q_scale, const flo
   return hip_status(misa::launch_topk(ta, st));
 }
 
+int32_t misa_score_topk_blocks(const void* q, int32_t q_dt, const float* q_scale, const float* w,
+                               const float* kbar, const void* k, const float* k_scale,
+                               int32_t k_dt, const int32_t* block_table, int32_t page_size,
+                               const int32_t* q_seq, const int32_t* q_pos, const int32_t* heads,
+                               int32_t N, int32_t S, int32_t L, int32_t d, int32_t B,
+                               int32_t H_I, int32_t h, int32_t m_blocks, int32_t topk,
+                               int32_t* blocks, int32_t* idx, float* score, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (!q || !w || !kbar || !k || !q_seq || !q_pos || !heads || !idx) return MISA_ERR_NULL;
+  int32_t rc = check_dtypes(q_dt, k_dt, q_scale, k_scale);
+  if (rc) return rc;
+  if ((rc = check_sizes(N, S, L, d, H_I))) return rc;
+  misa::KeyIndex ki;
+  if ((rc = key_index(block_table, page_size, L, ki))) return rc;
+  if (B < 1 || B > 1024 || h < 1 || h > H_I || m_blocks < 1) return MISA_ERR_SHAPE;
+  if (static_cast<int64_t>(m_blocks) * B > kMaxTopk || topk < 1 || topk > m_blocks * B)
+    return MISA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k)) return MISA_ERR_SHAPE;
+  const bool f8 = q_dt == MISA_FP8_E4M3;
+  const BlocksLayout bl = blocks_layout(N, L, B, m_blocks);
+  if (!ws) return MISA_ERR_NULL;
+  if (ws_bytes < bl.bytes + (f8 ? q8_bytes(N, H_I, d) : 0)) return MISA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  hipError_t e = hipSuccess;
+  if (f8) {
+    e = prep_fp8_queries(q, q_dt, w, q_scale, N, H_I, d, wsb + bl.bytes, st);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  uint32_t* ub = reinterpret_cast<uint32_t*>(wsb);
+  int32_t* last = reinterpret_cast<int32_t*>(wsb + bl.off_last);
+  int32_t* kept = blocks ? blocks : reinterpret_cast<int32_t*>(wsb + bl.off_blocks);
+  int32_t* cand = reinterpret_cast<int32_t*>(wsb + bl.off_cand);
+  uint32_t* u = reinterpret_cast<uint32_t*>(wsb + bl.off_u);
+  misa::BlockScoreArgs ba{q, q_dt, w, kbar, k, k_scale, k_dt, ki, q_seq, q_pos, heads,
+                          N, L, d, B, H_I, h, ub, bl.ub_stride, last};
+  if ((e = misa::launch_block_scores(ba, st)) != hipSuccess) return hip_status(e);
+  misa::TopkArgs tb{ub, bl.ub_stride, last, 0, N, m_blocks, true, nullptr, nullptr, 0, kept,
+                    nullptr};
+  if ((e = misa::launch_topk(tb, st)) != hipSuccess) return hip_status(e);
+  if ((e = misa::launch_expand_blocks(kept, q_pos, N, m_blocks, B, cand, st)) != hipSuccess)
+    return hip_status(e);
+  const int ncols = m_blocks * B;
+  misa::ScoreArgs sa{q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, heads, cand,
+                     N, S, L, d, H_I, h, ncols, u, bl.u_stride, nullptr, ki};
+  if ((e = misa::launch_score(sa, st)) != hipSuccess) return hip_status(e);
+  misa::TopkArgs ta{u, bl.u_stride, nullptr, ncols, N, topk, true, nullptr, cand, ncols, idx,
+                    score};
+  return hip_status(misa::launch_topk(ta, st));
+}
+
 int32_t misa_sparse_attention(const void* q, int32_t q_dt, const void* kv, int32_t kv_dt,
                               const int32_t* block_table, int32_t page_size,
                               const int32_t* q_seq, const int32_t* idx, int32_t N, int32_t S,
@@ -533,7 +613,7 @@ const char* misa_kernel_name(int32_t kernel_id) {
       "topk_collect_kernel", "topk_final_kernel",   "topk_row_kernel",
       "score_prefill_sample", "score_prefill_full", "topk_tau_kernel", "topk_cand_kernel",
       "route_split_kernel", "q8_prep_kernel", "pool_update_kernel", "attn_split_kernel",
-      "attn_combine_kernel"};
+      "attn_combine_kernel", "block_score_kernel", "expand_blocks_kernel"};
   if (kernel_id < 0 || kernel_id >= misa::K_COUNT_IDS) return "unknown";
   return names[kernel_id];
 }

@@ -30,6 +30,8 @@ enum KernelId : int {
   K_POOL_UPDATE,
   K_ATTN_SPLIT,
   K_ATTN_COMBINE,
+  K_BLOCK_SCORE,
+  K_EXPAND_BLOCKS,
   K_COUNT_IDS
 };
 
@@ -214,6 +216,32 @@ struct CandTopkArgs {
 };
 int cand_topk_capacity();
 hipError_t launch_cand_topk(const CandTopkArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- block prefilter
+// Block scores of each row under its routed heads (complete blocks from the
+// pooled table, a partial last block averaged from the keys) as order keys
+// ub [N, ub_stride], and last_block[n] = ceil(L_n / B) - 1.
+struct BlockScoreArgs {
+  const void* q;
+  int q_dt;
+  const float* w;
+  const float* kbar;
+  const void* k;
+  const float* k_scale;
+  int k_dt;
+  KeyIndex kidx;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  const int32_t* heads;
+  int N, L, d, B, H_I, h;
+  uint32_t* ub;
+  int ub_stride;
+  int32_t* last_block;
+};
+hipError_t launch_block_scores(const BlockScoreArgs& a, hipStream_t st);
+// cand[n, i*B + t] = blocks[n, i] * B + t when that token is visible, else -1
+hipError_t launch_expand_blocks(const int32_t* blocks, const int32_t* q_pos, int N, int m, int B,
+                                int32_t* cand, hipStream_t st);
 
 // ---------------------------------------------------------------- sparse attention
 // Softmax attention of every head of each row over its selected tokens

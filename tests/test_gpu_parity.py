@@ -751,3 +751,75 @@ def test_indexer_selection_feeds_attention():
     out, lse = DeviceAttention(p).run()
     assert (sel[3] >= 0).sum() == 101 and np.all(sel[3, :101] == np.arange(101))
     _check_attention(p, out, lse)
+
+
+# ---------------------------------------------------------------- block prefilter (routing x token hierarchy)
+def _block_scores_f64(p, heads):
+    """float64 block scores of every row under its heads (test-side closed form)."""
+    kd = oracle.decode(p.k, p.k_dt, p.k_scale) if p.k_dt != synth.F32 else p.k.astype(np.float64)
+    qd = oracle.decode(p.q, p.q_dt, None if p.q_scale is None else p.q_scale.reshape(-1)) \
+        if p.q_dt != synth.F32 else p.q.astype(np.float64)
+    qd = qd.reshape(p.q.shape)
+    out = []
+    for n in range(p.N):
+        Ln = p.q_pos[n] + 1
+        Mn = -(-Ln // p.B)
+        means = np.stack([kd[p.q_seq[n], b * p.B:min((b + 1) * p.B, Ln)].mean(0) for b in range(Mn)])
+        dots = qd[n, heads[n]] @ means.T
+        out.append((p.w[n, heads[n]].astype(np.float64)[:, None] * np.maximum(dots, 0)).sum(0))
+    return out
+
+
+def check_blocks(p, heads, blocks, idx, sc, m):
+    bs = _block_scores_f64(p, heads)
+    full = oracle.scores(p, heads)
+    masked = np.full_like(full, -np.inf)
+    swaps = 0
+    for n in range(p.N):
+        g = blocks[n][blocks[n] >= 0]
+        Mn = len(bs[n])
+        assert len(g) == min(m, Mn) and np.all(np.diff(g) > 0)
+        order = np.lexsort((np.arange(Mn), -bs[n]))
+        ref = set(order[:m].tolist())
+        if set(g.tolist()) != ref:
+            boundary = bs[n][order[min(m, Mn) - 1]]
+            for b in set(g.tolist()) ^ ref:
+                assert abs(bs[n][b] - boundary) <= tol(boundary), (n, b)
+            swaps += 1
+        Ln = p.q_pos[n] + 1
+        for b in g:
+            t = np.arange(b * p.B, min((b + 1) * p.B, Ln))
+            masked[n, t] = full[n, t]
+    lengths = (~np.isneginf(masked)).sum(1)
+    check_topk(idx, sc, masked, p.topk, lengths)
+    log(f"[blocks] rows with near-tie block swaps: {swaps}")
+
+
+@pytest.mark.parametrize("k_dt", [synth.BF16, synth.FP8])
+def test_blocks_all_kept_equals_score_topk(k_dt):
+    """m_blocks >= M_n: the same per-token arithmetic and selection as
+    misa_score_topk, byte for byte."""
+    p = synth.small("bkall", 111, N=3, S=3, L=5000, d=128, H_I=64, h=8, B=128, topk=300,
+                    k_dt=k_dt, q_pos=np.array([4999, 2047, 130], np.int32))
+    dp = DeviceProblem(p)
+    kbar = dp.pool()
+    heads, _ = dp.route(kbar)
+    idx, sc = dp.score_topk(heads)
+    blocks, bidx, bsc = dp.score_topk_blocks(kbar, heads, m_blocks=40)
+    assert np.array_equal(np_(idx), np_(bidx)) and np.array_equal(np_(sc), np_(bsc))
+    b = np_(blocks)
+    assert np.array_equal(b[1, :16], np.arange(16)) and np.all(b[1, 16:] == -1)
+
+
+@pytest.mark.parametrize("k_dt,page_size,m", [(synth.BF16, 0, 8), (synth.FP8, 0, 5),
+                                              (synth.BF16, 64, 12)])
+def test_blocks_parity(k_dt, page_size, m):
+    L = 9000
+    pos = np.array([L - 1, 8999 - 61, 4000, 129, 700], np.int32)      # partial last blocks
+    p = synth.small("bkp", 112, N=5, S=3, L=L, d=128, H_I=64, h=8, B=128, topk=400,
+                    k_dt=k_dt, q_pos=pos)
+    dp = DeviceProblem(p, page_size=page_size, page_seed=4)
+    kbar = dp.pool()
+    heads, _ = dp.route(kbar)
+    blocks, idx, sc = dp.score_topk_blocks(kbar, heads, m_blocks=m)
+    check_blocks(p, np_(heads), np_(blocks), np_(idx), np_(sc), m)

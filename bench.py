@@ -264,6 +264,22 @@ class Serving:
         dp.route(self.kbar[i], self.h, heads=self.heads, head_score=self.r, ws=self.ws_route)
         dp.score_topk(self.heads, idx=self.idx, score=None, ws=self.ws_score, want_score=False)
 
+    def use_blocks(self, m_blocks):
+        """Switch the step's scoring to the block prefilter (m_blocks blocks)."""
+        p = self.p
+        self.m = m_blocks
+        self.blocks = self.b.workspace(self.b.MISA_OP_BLOCKS, p.N, p.L, p.d, p.H_I, p.B,
+                                       topk=p.topk, k_prime=m_blocks,
+                                       device=self.heads.device)
+        self.kept = self.heads.new_empty((p.N, m_blocks))
+
+    def step_blocks(self, i):
+        dp = self.dps[i]
+        dp.pool_update(self.len_old, self.len_new, 1, self.kbar[i])
+        dp.route(self.kbar[i], self.h, heads=self.heads, head_score=self.r, ws=self.ws_route)
+        dp.score_topk_blocks(self.kbar[i], self.heads, self.m, blocks=self.kept, idx=self.idx,
+                             score=None, ws=self.blocks, want_score=False)
+
 
 def attention_extra(torch, binding, synth, idx, p, steps):
     """Sparse attention of DeepSeek-V3.2-like decode rows (H = 128 heads,
@@ -596,6 +612,19 @@ def main():
             [np.isin(p.needles[n, :, 0], dense_idx[n]).mean() for n in range(p.N)])), 4)
         del rep
         torch.cuda.empty_cache()
+        log("[bench] serving step with a block prefilter (routing x token hierarchy)")
+        for m_blocks in (64, 16):
+            srv.use_blocks(m_blocks)
+            ms_b = timed(torch, srv.step_blocks, args.steps, args.warmup)
+            srv.step_blocks(0)
+            torch.cuda.synchronize()
+            bidx = srv.idx.cpu().numpy()
+            extra[f"blocks{m_blocks}_step_ms"] = round(ms_b, 4)
+            extra[f"blocks{m_blocks}_tokens_per_s"] = tokens / (ms_b * 1e-3)
+            extra[f"blocks{m_blocks}_recall_vs_misa"] = round(rec(bidx, misa_idx), 4)
+            extra[f"blocks{m_blocks}_recall_vs_dense"] = round(rec(bidx, dense_idx), 4)
+        srv.step(0)
+        torch.cuda.synchronize()
         log("[bench] sparse attention over the selected tokens (128 heads, 576/512 latent rows)")
         extra.update(attention_extra(torch, binding, synth, srv.idx, p, args.steps))
         log("[bench] the serving step on a paged key cache (pages of 64 tokens)")

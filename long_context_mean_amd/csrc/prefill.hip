@@ -69,8 +69,11 @@ struct PLayout {
   static constexpr int ROW_LOADS = kKeyTile * CH / 256;  // 16-byte key loads per thread per tile
   static constexpr int PER_THREAD = ROW_LOADS + (F8 ? 1 : 0);  // + the key-scale load
   // Chunk q of row r sits at chunk position q ^ swz(r): the 16 rows read by
-  // one MFMA B fragment then hit 16 different bank groups.
-  __device__ static int swz(int r) { return CH == 16 ? (r & 15) : ((r >> 1) & 7); }
+  // one MFMA B fragment then hit 16 different 16-byte bank groups.  With
+  // 128-byte rows, rows r and r + 1 already differ in the upper half of a
+  // 256-byte bank window, so r & 7 spreads 8 consecutive rows and the
+  // r >> 3 term separates rows r and r + 8.
+  __device__ static int swz(int r) { return CH == 16 ? (r & 15) : ((r ^ (r >> 3)) & 7); }
   // A / B fragment: 8 bf16 (16 bytes) or 32 e4m3 codes (32 bytes) per lane
   using Frag = std::conditional_t<F8, i32x8_t, bf16x8_t>;
 };

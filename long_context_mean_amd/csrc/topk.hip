@@ -625,6 +625,7 @@ __global__ __launch_bounds__(256) void topk_tau_kernel(const uint32_t* __restric
 // candidates in registers.  Dynamic LDS: the row's winner bitmap (nwords_max
 // words) and a 16-bit per-word prefix of marked bits.
 constexpr int kCandThreads = 512;
+constexpr int kCandMaxK = kBins0 / 2;    // selected per row (outputs staged in hA)
 constexpr int kCandPer = kCandRow / kCandThreads;
 
 __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
@@ -637,6 +638,7 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
   __shared__ __align__(16) uint32_t hB[kBins2];
   __shared__ uint32_t spre[257];
   __shared__ uint32_t tpre[kCandThreads];
+  __shared__ uint16_t bsplit[kCandRow / 32];
   __shared__ uint32_t sm[kCandThreads / 64];
   __shared__ uint32_t res[4];
   __shared__ uint32_t bad;
@@ -668,20 +670,32 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
     }
     return;
   }
-  // candidates into registers: element j = tid + NT * i lives in split s with
-  // spre[s] <= j < spre[s + 1]; key 0 marks an empty register slot
+  // register slots holding candidates (a uniform bound: slots past it are
+  // skipped by the whole workgroup)
+  const int nsl = __builtin_amdgcn_readfirstlane(static_cast<int>((total + NT - 1) / NT));
+  // split of every 32nd element (element j lives in split s with
+  // spre[s] <= j < spre[s + 1]; empty splits have spre[s] == spre[s + 1])
+  if (tid < kCandRow / 32 && 32 * tid < static_cast<int>(total)) {
+    const uint32_t j = 32u * tid;
+    int lo = 0, hi = splits - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (spre[mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    bsplit[tid] = static_cast<uint16_t>(lo);
+  }
+  __syncthreads();
+  // candidates into registers: element j = tid + NT * i, its split found from
+  // the one of element 32 * (j / 32) forward; key 0 marks an empty slot
   uint32_t ck[kCandPer], cx[kCandPer];
 #pragma unroll
-  for (int i = 0; i < kCandPer; ++i) {
+  for (int i = 0; i < kCandPer && i < nsl; ++i) {
     const int j = tid + NT * i;
     ck[i] = 0u;
     cx[i] = 0u;
     if (j < static_cast<int>(total)) {
-      int lo = 0, hi = splits - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (spre[mid] <= static_cast<uint32_t>(j)) lo = mid; else hi = mid - 1;
-      }
+      int lo = bsplit[j >> 5];
+      while (spre[lo + 1] <= static_cast<uint32_t>(j)) ++lo;
       const uint2 e = cand[(static_cast<size_t>(n) * splits + lo) * cap + (j - spre[lo])];
       ck[i] = order_key(__uint_as_float(e.x));
       cx[i] = e.y;
@@ -692,7 +706,7 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
   __syncthreads();
   // exact threshold: three radix levels over the candidates
 #pragma unroll
-  for (int i = 0; i < kCandPer; ++i)
+  for (int i = 0; i < kCandPer && i < nsl; ++i)
     if (ck[i] != 0u) atomicAdd(&hA[ck[i] >> kShift0], 1u);
   __syncthreads();
   find_digit<NT, kBins0>(hA, K, false, sm, res);
@@ -700,14 +714,14 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
   for (int b = tid; b < kBins1; b += NT) hA[b] = 0u;
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kCandPer; ++i)
+  for (int i = 0; i < kCandPer && i < nsl; ++i)
     if (ck[i] != 0u && (ck[i] >> kShift0) == d0) atomicAdd(&hA[(ck[i] >> kShift1) & (kBins1 - 1)], 1u);
   __syncthreads();
   find_digit<NT, kBins1>(hA, r0, false, sm, res);
   const uint32_t d1 = res[0], r1 = res[1];
   const uint32_t pre = (d0 << kDigit1Bits) | d1;
 #pragma unroll
-  for (int i = 0; i < kCandPer; ++i)
+  for (int i = 0; i < kCandPer && i < nsl; ++i)
     if (ck[i] != 0u && (ck[i] >> kShift1) == pre) atomicAdd(&hB[ck[i] & (kBins2 - 1)], 1u);
   __syncthreads();
   find_digit<NT, kBins2>(hB, r1, false, sm, res);
@@ -723,13 +737,13 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
     if (tid < 64) hB[tid] = 0u;
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kCandPer; ++i)
+    for (int i = 0; i < kCandPer && i < nsl; ++i)
       if (ck[i] == T) atomicAdd(&hA[cx[i] >> 6], 1u);
     __syncthreads();
     find_digit<NT, kBins0>(hA, n_eq - K2 + 1u, false, sm, res);
     const uint32_t dA = res[0], rA = res[1];
 #pragma unroll
-    for (int i = 0; i < kCandPer; ++i)
+    for (int i = 0; i < kCandPer && i < nsl; ++i)
       if (ck[i] == T && (cx[i] >> 6) == dA) atomicAdd(&hB[cx[i] & 63u], 1u);
     __syncthreads();
     find_digit<NT, 64>(hB, rA, false, sm, res);
@@ -739,7 +753,7 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
   for (int w = tid; w < nwords; w += NT) bm[w] = 0u;
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kCandPer; ++i)
+  for (int i = 0; i < kCandPer && i < nsl; ++i)
     if (ck[i] > T || (ck[i] == T && ck[i] != 0u && cx[i] <= cut))
       atomicOr(&bm[cx[i] >> 5], 1u << (cx[i] & 31));
   __syncthreads();
@@ -757,22 +771,28 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
   uint32_t tot;
   tpre[tid] = block_excl_scan<NT>(mine, sm, tot);
   __syncthreads();
-  int32_t* idx_row = idx + static_cast<size_t>(n) * topk;
-  float* score_row = score ? score + static_cast<size_t>(n) * topk : nullptr;
+  // winners to their output slots in LDS (hA: indices, then keys), then out
+  // in order with contiguous stores
+  uint32_t* oidx = hA;
+  uint32_t* okey = hA + kCandMaxK;
 #pragma unroll
-  for (int i = 0; i < kCandPer; ++i) {
+  for (int i = 0; i < kCandPer && i < nsl; ++i) {
     const uint32_t e = cx[i];
     if (ck[i] == 0u) continue;
     const int w = static_cast<int>(e >> 5);
     const uint32_t word = bm[w];
     if (!((word >> (e & 31)) & 1u)) continue;
     const uint32_t pos = tpre[w / wpt] + wpre[w] + __popc(word & ((1u << (e & 31)) - 1u));
-    idx_row[pos] = static_cast<int32_t>(e);
-    if (score_row) score_row[pos] = key_score(ck[i]);
+    oidx[pos] = e;
+    okey[pos] = ck[i];
   }
-  for (int i = static_cast<int>(K) + tid; i < topk; i += NT) {
-    idx_row[i] = -1;
-    if (score_row) score_row[i] = -__builtin_inff();
+  __syncthreads();
+  int32_t* idx_row = idx + static_cast<size_t>(n) * topk;
+  float* score_row = score ? score + static_cast<size_t>(n) * topk : nullptr;
+  for (int i = tid; i < topk; i += NT) {
+    const bool sel = i < static_cast<int>(K);
+    idx_row[i] = sel ? static_cast<int32_t>(oidx[i]) : -1;
+    if (score_row) score_row[i] = sel ? key_score(okey[i]) : -__builtin_inff();
   }
 }
 
@@ -824,7 +844,7 @@ hipError_t launch_tau(const TauArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_cand_topk(const CandTopkArgs& a, hipStream_t st) {
-  if (a.splits < 1 || a.splits > 256) return hipErrorInvalidValue;
+  if (a.splits < 1 || a.splits > 256 || a.topk > kCandMaxK) return hipErrorInvalidValue;
   // bitmap + 16-bit word prefix for the longest row (longer rows are flagged)
   const int nwords_max = min((a.L + 31) / 32, kBitmapWords);
   const size_t lds = static_cast<size_t>(nwords_max) * 4 + (static_cast<size_t>(nwords_max) * 2 + 15) / 16 * 16;

@@ -17,6 +17,7 @@
 // -1 past the row's visible prefix or for unused block slots).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "partial_block.hpp"
 
 namespace misa {
 namespace {
@@ -63,18 +64,7 @@ __global__ __launch_bounds__(256) void block_score_kernel(BlockScoreArgs a) {
   if (cp > 0 && Mf >= b0 && Mf < b0 + nb) {
     const int piece = tid % PIECES, rg = tid / PIECES;
     float acc[EPP];
-#pragma unroll
-    for (int e = 0; e < EPP; ++e) acc[e] = 0.f;
-    const uint8_t* kp = static_cast<const uint8_t*>(a.k);
-    for (int t = Mf * a.B + rg; t < Ln; t += RG) {
-      const size_t row = a.kidx.row(s, t);
-      const uint4 x = *reinterpret_cast<const uint4*>(kp + row * (D * EB) + piece * 16);
-      float v[EPP];
-      unpack16<KT>(x, v);
-      const float sc = (KT == DT_E4M3) ? a.k_scale[row] : 1.f;
-#pragma unroll
-      for (int e = 0; e < EPP; ++e) acc[e] += (KT == DT_E4M3) ? v[e] * sc : v[e];
-    }
+    piece_sum<KT, D>(a.k, a.k_scale, a.kidx, s, Mf * a.B, Ln, tid, acc);
 #pragma unroll
     for (int e = 0; e < EPP; ++e) psum[rg][piece * EPP + e] = acc[e];
     __syncthreads();

@@ -1,0 +1,59 @@
+// Partial-block key sums for the router and the block prefilter, gfx950.
+//
+// A query row whose visible prefix ends inside a block pools that block from
+// its visible keys only (the mean of keys [t0, t1) of sequence s).  The 256
+// threads of a workgroup split each key row into 16-byte pieces: thread
+// (rg, piece) sums rows t0 + rg, t0 + rg + RG, ... of its piece.  All loads of
+// a batch are issued before any is used, so a block costs one or two memory
+// round trips instead of one per pass.
+#pragma once
+
+#include "common.hpp"
+
+namespace misa {
+
+template <int KT, int D>
+struct PieceMap {
+  static constexpr int EB = KeyBytes<KT>::value;
+  static constexpr int PIECES = D * EB / 16;   // 16-byte pieces per key row
+  static constexpr int EPP = 16 / EB;          // elements per piece
+  static constexpr int RG = 256 / PIECES;      // key rows per pass
+};
+
+// acc[e] = sum over this thread's rows t of element (piece * EPP + e) of key t
+// (e4m3 keys times their per-token scale).
+template <int KT, int D>
+__device__ __forceinline__ void piece_sum(const void* k, const float* k_scale, const KeyIndex& ki,
+                                          int s, int t0, int t1, int tid,
+                                          float (&acc)[PieceMap<KT, D>::EPP]) {
+  using PM = PieceMap<KT, D>;
+  constexpr int BATCH = 8;
+  const int piece = tid % PM::PIECES, rg = tid / PM::PIECES;
+  const uint8_t* kb = static_cast<const uint8_t*>(k);
+#pragma unroll
+  for (int e = 0; e < PM::EPP; ++e) acc[e] = 0.f;
+  for (int tb = t0 + rg; tb < t1; tb += PM::RG * BATCH) {
+    uint4 x[BATCH];
+    float sc[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int t = tb + u * PM::RG;
+      x[u] = make_uint4(0u, 0u, 0u, 0u);
+      sc[u] = 0.f;
+      if (t < t1) {
+        const size_t row = ki.row(s, t);
+        x[u] = *reinterpret_cast<const uint4*>(kb + row * (D * PM::EB) + piece * 16);
+        sc[u] = (KT == DT_E4M3) ? k_scale[row] : 1.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      float v[PM::EPP];
+      unpack16<KT>(x[u], v);
+#pragma unroll
+      for (int e = 0; e < PM::EPP; ++e) acc[e] += (KT == DT_E4M3) ? v[e] * sc[u] : v[e];
+    }
+  }
+}
+
+}  // namespace misa

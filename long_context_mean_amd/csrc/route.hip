@@ -20,6 +20,7 @@
 //    ascending order.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "partial_block.hpp"
 
 namespace misa {
 namespace {
@@ -373,18 +374,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(
   if (cp > 0) {
     const int piece = threadIdx.x % PIECES, rg = threadIdx.x / PIECES;
     float acc[EPP];
-#pragma unroll
-    for (int e = 0; e < EPP; ++e) acc[e] = 0.f;
-    const uint8_t* kb = static_cast<const uint8_t*>(k);
-    for (int t = Mf * B + rg; t < Ln; t += RG) {
-      const size_t row = ki.row(s, t);
-      const uint4 x = *reinterpret_cast<const uint4*>(kb + row * (D * EB) + piece * 16);
-      float v[EPP];
-      unpack16<KT>(x, v);
-      const float sc = (KT == DT_E4M3) ? k_scale[row] : 1.f;
-#pragma unroll
-      for (int e = 0; e < EPP; ++e) acc[e] += (KT == DT_E4M3) ? v[e] * sc : v[e];
-    }
+    piece_sum<KT, D>(k, k_scale, ki, s, Mf * B, Ln, threadIdx.x, acc);
 #pragma unroll
     for (int e = 0; e < EPP; ++e) psum[rg][piece * EPP + e] = acc[e];
   }

@@ -422,14 +422,18 @@ int32_t misa_route_heads(const void* q, int32_t q_dt, const float* q_scale, cons
   if (!ws) return MISA_ERR_NULL;
   if (ws_bytes < own + (f8 ? q8_bytes(N, H_I, d) : 0)) return MISA_ERR_WORKSPACE;
   uint8_t* wsb = static_cast<uint8_t*>(ws);
-  if (f8) {
-    const hipError_t e = prep_fp8_queries(q, q_dt, w, q_scale, N, H_I, d, wsb + own,
+  misa::RouteArgs a{q, q_dt, f8 ? q_scale : nullptr, w, kbar, k, k_scale, k_dt, q_seq, q_pos, N,
+                    S, L, d, B, H_I, h, heads, head_score, reinterpret_cast<float*>(wsb),
+                    route_chunks(L, B),
+                    reinterpret_cast<uint16_t*>(wsb + route_partial_bytes(N, L, B, H_I)), ki};
+  // the GEMM router widens e4m3 queries itself; the per-row kernels take
+  // them converted to bf16 (scale folded into the weight)
+  if (f8 && !misa::route_uses_mfma(a)) {
+    const hipError_t e = prep_fp8_queries(a.q, a.q_dt, a.w, q_scale, N, H_I, d, wsb + own,
                                           static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_status(e);
+    a.q_scale = nullptr;
   }
-  misa::RouteArgs a{q, q_dt, w, kbar, k, k_scale, k_dt, q_seq, q_pos, N, S, L, d, B, H_I, h,
-                    heads, head_score, reinterpret_cast<float*>(wsb), route_chunks(L, B),
-                    reinterpret_cast<uint16_t*>(wsb + route_partial_bytes(N, L, B, H_I)), ki};
   return hip_status(misa::launch_route(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -70,6 +70,7 @@ hipError_t launch_pool(const PoolArgs& a, hipStream_t st);
 struct RouteArgs {
   const void* q;
   int q_dt;
+  const float* q_scale;  // e4m3 q: per-head scale [N, H_I] (folded into |w|), else NULL
   const float* w;
   const float* kbar;
   const void* k;

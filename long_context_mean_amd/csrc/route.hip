@@ -40,10 +40,14 @@ __device__ __forceinline__ void load_q_row(const void* q, size_t row, float (&ou
       out[4 * i + 2] = x.z;
       out[4 * i + 3] = x.w;
     }
-  } else {
+  } else if constexpr (QT == DT_BF16) {
     const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + row * D);
 #pragma unroll
     for (int i = 0; i < D / 8; ++i) unpack16<DT_BF16>(p[i], &out[8 * i]);
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(q) + row * D);
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) unpack16<DT_E4M3>(p[i], &out[16 * i]);
   }
 }
 
@@ -228,8 +232,8 @@ __global__ __launch_bounds__(256) void route_split_kernel(const float* __restric
   }
 }
 
-template <int HPI>
-__global__ __launch_bounds__(256) void route_mfma_kernel(const uint16_t* __restrict__ q,
+template <int HPI, bool QF8>
+__global__ __launch_bounds__(256) void route_mfma_kernel(const void* __restrict__ q,
                                                          const uint16_t* __restrict__ kb_hi,
                                                          const uint16_t* __restrict__ kb_lo,
                                                          const int32_t* __restrict__ q_pos,
@@ -262,10 +266,23 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const uint16_t* __restr
     const int r = wave * 64 + rt * 16 + c;
     const int t = q0 + r / HPI, j = r % HPI;
     const bool rv = t < N && j < H_I;
-    const uint16_t* qr = q + (static_cast<size_t>(rv ? t : 0) * H_I + (rv ? j : 0)) * D;
+    const size_t qrow = static_cast<size_t>(rv ? t : 0) * H_I + (rv ? j : 0);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      u32x4_t x = *reinterpret_cast<const u32x4_t*>(qr + 32 * kk + 8 * g);
+      u32x4_t x;
+      if constexpr (QF8) {
+        // 8 e4m3 codes widened to bf16 (exact); the head scale is folded
+        // into the router weight
+        const uint2 c8 = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(q) +
+                                                         qrow * D + 32 * kk + 8 * g);
+        uint32_t b0, b1, b2, b3;
+        e4m3x4_to_bf16x4(c8.x, b0, b1);
+        e4m3x4_to_bf16x4(c8.y, b2, b3);
+        x = u32x4_t{b0, b1, b2, b3};
+      } else {
+        x = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(q) + qrow * D +
+                                              32 * kk + 8 * g);
+      }
       if (!rv) x = u32x4_t{0u, 0u, 0u, 0u};
       a[rt][kk] = __builtin_bit_cast(bf16x8_t, x);
     }
@@ -334,7 +351,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     const float* __restrict__ k_scale, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int L, int B, int H_I, int h, int nchunks,
     const float* __restrict__ partial, int32_t* __restrict__ heads,
-    float* __restrict__ head_score, KeyIndex ki) {
+    float* __restrict__ head_score, KeyIndex ki, const float* __restrict__ q_scale) {
   constexpr int EB = KeyBytes<KT>::value;
   constexpr int PIECES = D * EB / 16;          // 16-byte pieces per key row
   constexpr int EPP = 16 / EB;                 // elements per piece
@@ -399,7 +416,9 @@ __global__ __launch_bounds__(256) void route_select_kernel(
         for (int i = 0; i < D; ++i) dt += qr[i] * mean[i];
         a += fmaxf(dt, 0.f);
       }
-      r = fabsf(w[static_cast<size_t>(n) * H_I + j]) * a;
+      float wj = w[static_cast<size_t>(n) * H_I + j];
+      if (QT == DT_E4M3) wj *= q_scale[static_cast<size_t>(n) * H_I + j];
+      r = fabsf(wj) * a;
       if (head_score) head_score[static_cast<size_t>(n) * H_I + j] = r;
     }
     // top-h: a head is routed when fewer than h heads beat it under
@@ -438,16 +457,18 @@ hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
                 lo);
     const int hpi = a.H_I <= 16 ? 16 : (a.H_I <= 32 ? 32 : 64);
     const dim3 grid((a.N + 256 / hpi - 1) / (256 / hpi));
-    const uint16_t* q = static_cast<const uint16_t*>(a.q);
+    constexpr bool QF8 = QT == DT_E4M3;
     if (hpi == 16)
-      MISA_LAUNCH(K_ROUTE_PARTIAL, route_mfma_kernel<16>, grid, dim3(256), 0, st, q, hi, lo,
-                  a.q_pos, a.N, a.L, a.B, a.H_I, a.partial);
+      MISA_LAUNCH(K_ROUTE_PARTIAL, (route_mfma_kernel<16, QF8>), grid, dim3(256), 0, st, a.q,
+                  hi, lo, a.q_pos, a.N, a.L, a.B, a.H_I, a.partial);
     else if (hpi == 32)
-      MISA_LAUNCH(K_ROUTE_PARTIAL, route_mfma_kernel<32>, grid, dim3(256), 0, st, q, hi, lo,
-                  a.q_pos, a.N, a.L, a.B, a.H_I, a.partial);
+      MISA_LAUNCH(K_ROUTE_PARTIAL, (route_mfma_kernel<32, QF8>), grid, dim3(256), 0, st, a.q,
+                  hi, lo, a.q_pos, a.N, a.L, a.B, a.H_I, a.partial);
     else
-      MISA_LAUNCH(K_ROUTE_PARTIAL, route_mfma_kernel<64>, grid, dim3(256), 0, st, q, hi, lo,
-                  a.q_pos, a.N, a.L, a.B, a.H_I, a.partial);
+      MISA_LAUNCH(K_ROUTE_PARTIAL, (route_mfma_kernel<64, QF8>), grid, dim3(256), 0, st, a.q,
+                  hi, lo, a.q_pos, a.N, a.L, a.B, a.H_I, a.partial);
+  } else if constexpr (QT == DT_E4M3) {
+    return hipErrorInvalidValue;   // e4m3 queries reach the router only on the GEMM path
   } else {
     if constexpr (QT == DT_BF16)
       MISA_LAUNCH(K_ROUTE_PARTIAL, route_partial_mfma_kernel<D>, dim3(a.nchunks, a.N), dim3(256),
@@ -460,13 +481,17 @@ hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
   }
   MISA_LAUNCH(K_ROUTE_SELECT, (route_select_kernel<QT, KT, D>), dim3(a.N), dim3(256), 0, st,
               a.q, a.w, a.k, a.k_scale, a.q_seq, a.q_pos, a.L, a.B, a.H_I, a.h, nchunks,
-              a.partial, a.heads, a.head_score, a.kidx);
+              a.partial, a.heads, a.head_score, a.kidx, a.q_scale);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_route_d(const RouteArgs& a, hipStream_t st) {
   if (a.q_dt == DT_F32) return launch_route_t<DT_F32, DT_F32, D>(a, st);
+  if (a.q_dt == DT_E4M3) {
+    if constexpr (D == 128) return launch_route_t<DT_E4M3, DT_E4M3, D>(a, st);
+    return hipErrorInvalidValue;
+  }
   if (a.k_dt == DT_BF16) return launch_route_t<DT_BF16, DT_BF16, D>(a, st);
   return launch_route_t<DT_BF16, DT_E4M3, D>(a, st);
 }
@@ -476,7 +501,7 @@ hipError_t launch_route_d(const RouteArgs& a, hipStream_t st) {
 int route_blocks_per_chunk() { return kRouteBlocks; }
 
 bool route_uses_mfma(const RouteArgs& a) {
-  return a.S == 1 && a.N >= 128 && a.q_dt == DT_BF16 && a.d == 128;
+  return a.S == 1 && a.N >= 128 && (a.q_dt == DT_BF16 || a.q_dt == DT_E4M3) && a.d == 128;
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {

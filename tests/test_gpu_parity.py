@@ -682,6 +682,16 @@ def test_single_key_and_one_head():
     _exact_misa(p)
 
 
+@pytest.mark.parametrize("k_dt", [synth.BF16, synth.FP8])
+def test_largest_block_size(k_dt):
+    """B = 1024 (the largest the ABI takes): partial blocks of 904 and 453
+    visible keys and one row ending on a block boundary, pooled, routed and
+    scored bit for bit."""
+    p = synth.integer_problem("bmax", 67, N=3, S=3, L=5000, d=128, H_I=16, h=4, B=1024,
+                              topk=300, k_dt=k_dt, q_pos=np.array([4999, 1023, 2500], np.int32))
+    _exact_misa(p)
+
+
 def test_topk_at_the_limit():
     """k = 65536 (the largest the ABI takes) over 70000-token rows."""
     p = synth.small("kmax", 66, N=2, S=2, L=70000, d=64, H_I=16, h=4, B=256, topk=65536)

@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256) void route_split_kernel(const float* __restric
 }
 
 template <int HPI, bool QF8>
-__global__ __launch_bounds__(256) void route_mfma_kernel(const void* __restrict__ q,
+__global__ __launch_bounds__(256, 4) void route_mfma_kernel(const void* __restrict__ q,
                                                          const uint16_t* __restrict__ kb_hi,
                                                          const uint16_t* __restrict__ kb_lo,
                                                          const int32_t* __restrict__ q_pos,
@@ -309,24 +309,29 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const void* __restrict_
 #pragma unroll
     for (int ct = 0; ct < kRouteTile / 16; ++ct) {
       const int blk = b0 + ct * 16 + c;                // this lane's output column
-      bf16x8_t bh[KK], bl[KK];
+      // one K step of B (hi and lo) at a time against all 4 row tiles keeps
+      // the live B fragments to two (the register budget allows 4 waves/SIMD)
+      f32x4_t acc[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const int off = (ct * 16 + c) * STRIDE + 64 * kk + 16 * g;
-        bh[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(hi_t + off));
-        bl[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(lo_t + off));
+        const bf16x8_t bh =
+            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(hi_t + off));
+        const bf16x8_t bl =
+            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(lo_t + off));
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][kk], bh, acc[rt], 0, 0, 0);
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][kk], bl, acc[rt], 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][kk], bh[kk], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][kk], bl[kk], acc, 0, 0, 0);
-        }
         const bool vis = blk < mf_row[rt];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc_rows[rt][i] += vis ? relu(acc[i]) : 0.f;
+        for (int i = 0; i < 4; ++i) acc_rows[rt][i] += vis ? relu(acc[rt][i]) : 0.f;
       }
     }
   }

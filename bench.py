@@ -604,8 +604,14 @@ def main():
         def rec(a, b):
             return float(np.mean([len(set(x[x >= 0]) & set(y[y >= 0])) / max(1, (y >= 0).sum())
                                   for x, y in zip(a, b)]))
+        def iou(a, b):
+            return float(np.mean([len(set(x[x >= 0]) & set(y[y >= 0])) /
+                                  max(1, len(set(x[x >= 0]) | set(y[y >= 0])))
+                                  for x, y in zip(a, b)]))
         extra["recall_vs_dense"] = round(rec(misa_idx, dense_idx), 4)
+        extra["iou_vs_dense"] = round(iou(misa_idx, dense_idx), 4)
         extra["misa_dagger_recall_vs_dense"] = round(rec(dag_idx, dense_idx), 4)
+        extra["misa_dagger_iou_vs_dense"] = round(iou(dag_idx, dense_idx), 4)
         extra["needle_recall"] = round(float(np.mean(
             [np.isin(p.needles[n, :, 0], misa_idx[n]).mean() for n in range(p.N)])), 4)
         extra["needle_recall_dense"] = round(float(np.mean(
@@ -640,6 +646,20 @@ def main():
         extra["paged_recall_vs_dense"] = round(rec(pg.idx.cpu().numpy(), dense_idx), 4)
         del pg
         torch.cuda.empty_cache()
+        log("[bench] the serving step at h = 4 and 16")
+        for hh in (4, 16):
+            sv = Serving(p, torch, binding, hh)
+            ms_h = timed(torch, sv.step, args.steps, args.warmup)
+            sv.step(0)
+            torch.cuda.synchronize()
+            hidx = sv.idx.cpu().numpy()
+            extra[f"serving_step_ms_h{hh}"] = round(ms_h, 4)
+            extra[f"serving_tokens_per_s_h{hh}"] = tokens / (ms_h * 1e-3)
+            extra[f"recall_vs_dense_h{hh}"] = round(rec(hidx, dense_idx), 4)
+            extra[f"needle_recall_h{hh}"] = round(float(np.mean(
+                [np.isin(p.needles[n, :, 0], hidx[n]).mean() for n in range(p.N)])), 4)
+            del sv
+            torch.cuda.empty_cache()
         log("[bench] fp8-key MISA-dagger (c5 shape)")
         p5 = synth.make("c5")
         r5 = Replicas(p5, torch, binding, p5.h, k_prime=p5.k_prime)

@@ -236,8 +236,10 @@ class Serving:
     """The decode serving step on a key cache (contiguous, or paged with
     page_size tokens per page): the newest token of every sequence completes
     its last block, so the step pools that one block into the cached table
-    (misa_pool_update), then routes and scores.  REPLICAS copies of the keys
-    rotate like Replicas."""
+    (misa_pool_update), then routes and scores in one call
+    (misa_route_score_topk: the head selection runs in the scoring kernel);
+    step_two_calls does the same with misa_route_heads + misa_score_topk.
+    REPLICAS copies of the keys rotate like Replicas."""
 
     def __init__(self, p, torch, binding, h, page_size=0):
         from long_context_mean_amd.binding import DeviceProblem
@@ -257,8 +259,16 @@ class Serving:
                                           device=dev)
         self.ws_score = binding.workspace(binding.MISA_OP_SCORE_TOPK, p.N, p.L, p.d, p.H_I,
                                           topk=p.topk, device=dev)
+        self.ws_fused = binding.workspace(binding.MISA_OP_ROUTE_SCORE_TOPK, p.N, p.L, p.d,
+                                          p.H_I, p.B, topk=p.topk, device=dev)
 
     def step(self, i):
+        dp = self.dps[i]
+        dp.pool_update(self.len_old, self.len_new, 1, self.kbar[i])
+        dp.route_score_topk(self.kbar[i], self.h, heads=self.heads, head_score=self.r,
+                            idx=self.idx, score=None, ws=self.ws_fused, want_score=False)
+
+    def step_two_calls(self, i):
         dp = self.dps[i]
         dp.pool_update(self.len_old, self.len_new, 1, self.kbar[i])
         dp.route(self.kbar[i], self.h, heads=self.heads, head_score=self.r, ws=self.ws_route)
@@ -547,7 +557,7 @@ def main():
     key_bytes = p.N * p.L * p.d * 2
 
     srv = Serving(p, torch, binding, h)
-    log("[bench] timing the serving step (incremental pool + route + score/top-k)")
+    log("[bench] timing the serving step (incremental pool + route + score/top-k in one call)")
     ms = timed(torch, srv.step, args.steps, args.warmup)
     value = tokens / (ms * 1e-3)
     pct = step_percentiles(torch, srv.step, reps=max(100, args.steps), warmup=5)
@@ -578,6 +588,11 @@ def main():
         extra["pool_kernel_hbm_gbs"] = round(key_bytes / (pl_ms * 1e-3) / 1e9, 1)
 
     if not args.no_extras:
+        ms_2 = timed(torch, srv.step_two_calls, args.steps, args.warmup)
+        _, kt2, _ = kernel_times(torch, binding, srv.step_two_calls, max(3, args.steps // 2), 1,
+                                 16)
+        extra["serving_step_two_calls_ms"] = round(ms_2, 4)
+        extra["serving_step_two_calls_kernel_ms"] = {k: round(v, 5) for k, v in kt2.items()}
         ms_f = timed(torch, rep.step_misa, args.steps, args.warmup)
         _, ktf, _ = kernel_times(torch, binding, rep.step_misa, max(3, args.steps // 2), 1, 16)
         ms_d = timed(torch, rep.step_dense, args.steps, args.warmup)
@@ -685,7 +700,8 @@ def main():
                    "N": p.N, "L": p.L, "H_I": p.H_I, "h": h, "d": p.d, "B": p.B,
                    "topk": p.topk,
                    "step": "incremental block pooling (the appended token completes each "
-                           "sequence's last block) + route + routed score/top-k",
+                           "sequence's last block) + route + routed score/top-k "
+                           "(misa_route_score_topk)",
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,

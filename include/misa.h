@@ -94,7 +94,8 @@ typedef enum {
   MISA_OP_SCORE_TOPK = 1,   /* misa_score_topk (also dsa_score_topk) */
   MISA_OP_RERANK = 2,       /* misa_rerank */
   MISA_OP_ATTENTION = 3,    /* misa_sparse_attention (d = d_v, H_I = heads) */
-  MISA_OP_BLOCKS = 4        /* misa_score_topk_blocks (k_prime = m_blocks) */
+  MISA_OP_BLOCKS = 4,       /* misa_score_topk_blocks (k_prime = m_blocks) */
+  MISA_OP_ROUTE_SCORE_TOPK = 5  /* misa_route_score_topk */
 } misa_op;
 
 /*
@@ -163,6 +164,27 @@ int32_t misa_score_topk(const void* q, int32_t q_dt, const float* q_scale, const
                         const int32_t* q_pos, const int32_t* heads, int32_t N, int32_t S,
                         int32_t L, int32_t d, int32_t H_I, int32_t h, int32_t topk,
                         int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Head router + routed token scoring + top-k in one call (the two steps of
+ * the same page's "Methodology", items 1 and 2): the same results as
+ * misa_route_heads followed by misa_score_topk, bit for bit.  heads [N, h]
+ * (required) and head_score [N, H_I] (may be NULL) receive the router's
+ * outputs; idx/score the top-k.  For decode rows with bf16 queries and bf16 or
+ * e4m3 keys (not one sequence with N >= 128) the selection of the heads runs
+ * at the start of the scoring kernel, so the step launches two kernels fewer;
+ * otherwise the two calls run in turn.  All other arguments, layouts and
+ * errors are those of the two calls.
+ * Workspace: misa_workspace_bytes(MISA_OP_ROUTE_SCORE_TOPK, q_dt, N, L, d, H_I,
+ * B, topk, 0).
+ */
+int32_t misa_route_score_topk(const void* q, int32_t q_dt, const float* q_scale, const float* w,
+                              const float* kbar, const void* k, const float* k_scale,
+                              int32_t k_dt, const int32_t* block_table, int32_t page_size,
+                              const int32_t* q_seq, const int32_t* q_pos, int32_t N, int32_t S,
+                              int32_t L, int32_t d, int32_t B, int32_t H_I, int32_t h,
+                              int32_t topk, int32_t* heads, float* head_score, int32_t* idx,
+                              float* score, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Dense DSA indexer (the baseline MISA replaces: every one of the H_I heads

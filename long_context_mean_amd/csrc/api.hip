@@ -197,6 +197,13 @@ size_t q8_bytes(int N, int H_I, int d) {
   return align_up(rows * d * 2, 256) + align_up(rows * 4, 256);
 }
 
+// routed decode step: router region (partials with one more slot per row for
+// the partial-block term), then the scoring workspace
+size_t route_score_route_bytes(int q_dt, int N, int L, int d, int B, int H_I) {
+  return route_bytes(N, L, B, H_I) + align_up(static_cast<size_t>(N) * H_I * 4, 256) +
+         (q_dt == MISA_FP8_E4M3 ? q8_bytes(N, H_I, d) : 0);
+}
+
 // Converts fp8 queries into `region` and points (q, q_dt, w) at the bf16
 // problem with the same scores (see launch_q8_prep).
 hipError_t prep_fp8_queries(const void*& q, int32_t& q_dt, const float*& w, const float* q_scale,
@@ -222,12 +229,23 @@ struct Profiler {
 };
 Profiler g_prof;
 
+// The routed decode step's scoring launch picks the heads itself from the
+// router partials (see misa_route_score_topk); its histogram was cleared by
+// the router partials kernel.
+struct FusedRoute {
+  const float* partial;
+  int nchunks, B;
+  int32_t* heads_out;
+  float* head_score_out;
+};
+
 int32_t score_topk_impl(const void* q, int32_t q_dt, const float* q_scale, const float* w,
                         const void* k, const float* k_scale, int32_t k_dt,
                         const int32_t* block_table, int32_t page_size, const int32_t* q_seq,
                         const int32_t* q_pos, const int32_t* heads, int32_t N, int32_t S,
                         int32_t L, int32_t d, int32_t H_I, int32_t h, int32_t topk,
-                        int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream) {
+                        int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream,
+                        const FusedRoute* fr = nullptr) {
   if (!q || !w || !k || !q_seq || !q_pos || !idx) return MISA_ERR_NULL;
   int32_t rc = check_dtypes(q_dt, k_dt, q_scale, k_scale);
   if (rc) return rc;
@@ -246,7 +264,7 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* q_scale, const
   uint32_t* u = reinterpret_cast<uint32_t*>(base);
   uint32_t* hist = lay.one_row ? nullptr : reinterpret_cast<uint32_t*>(base + lay.off_hist);
   hipError_t e = hipSuccess;
-  if (hist) e = misa::launch_clear(hist, static_cast<size_t>(N) * misa::kHistWords, st);
+  if (hist && !fr) e = misa::launch_clear(hist, static_cast<size_t>(N) * misa::kHistWords, st);
   if (e != hipSuccess) return hip_status(e);
   // many rows over one contiguous sequence: GEMM over the gathered head rows
   // (bf16, or e4m3 straight from the codes)
@@ -307,6 +325,13 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* q_scale, const
   } else {
     misa::ScoreArgs sa{q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, heads, nullptr,
                        N, S, L, d, H_I, h, 0, u, lay.u_stride, hist, ki};
+    if (fr) {
+      sa.route_partial = fr->partial;
+      sa.route_nchunks = fr->nchunks;
+      sa.B = fr->B;
+      sa.heads_out = fr->heads_out;
+      sa.head_score_out = fr->head_score_out;
+    }
     e = misa::launch_score(sa, st);
   }
   if (e != hipSuccess) return hip_status(e);
@@ -367,6 +392,10 @@ size_t misa_workspace_bytes(int32_t op, int32_t q_dt, int32_t N, int32_t L, int3
     case MISA_OP_RERANK:
       if (k_prime < 1 || k_prime > kMaxTopk) return 0;
       return rerank_bytes(N, k_prime) + extra;
+    case MISA_OP_ROUTE_SCORE_TOPK:
+      if (B < 1 || B > 1024 || topk < 1 || topk > kMaxTopk) return 0;
+      return route_score_route_bytes(q_dt, N, L, d, B, H_I) + score_topk_bytes(N, L, topk) +
+             extra;
     case MISA_OP_BLOCKS:            // k_prime = m_blocks
       if (B < 1 || B > 1024 || k_prime < 1 || static_cast<int64_t>(k_prime) * B > kMaxTopk)
         return 0;
@@ -458,6 +487,56 @@ int32_t dsa_score_topk(const void* q, int32_t q_dt, const float* q_scale, const 
   return score_topk_impl(q, q_dt, q_scale, w, k, k_scale, k_dt, block_table, page_size, q_seq,
                          q_pos, nullptr, N, S, L, d, H_I, H_I, topk, idx, score, ws, ws_bytes,
                          stream);
+}
+
+int32_t misa_route_score_topk(const void* q, int32_t q_dt, const float* q_scale, const float* w,
+                              const float* kbar, const void* k, const float* k_scale,
+                              int32_t k_dt, const int32_t* block_table, int32_t page_size,
+                              const int32_t* q_seq, const int32_t* q_pos, int32_t N, int32_t S,
+                              int32_t L, int32_t d, int32_t B, int32_t H_I, int32_t h,
+                              int32_t topk, int32_t* heads, float* head_score, int32_t* idx,
+                              float* score, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !w || !kbar || !k || !q_seq || !q_pos || !heads || !idx) return MISA_ERR_NULL;
+  int32_t rc = check_dtypes(q_dt, k_dt, q_scale, k_scale);
+  if (rc) return rc;
+  if ((rc = check_sizes(N, S, L, d, H_I))) return rc;
+  misa::KeyIndex ki;
+  if ((rc = key_index(block_table, page_size, L, ki))) return rc;
+  if (B < 1 || B > 1024 || h < 1 || h > H_I || topk < 1 || topk > kMaxTopk) return MISA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k)) return MISA_ERR_SHAPE;
+  const size_t rb = route_score_route_bytes(q_dt, N, L, d, B, H_I);
+  const size_t sb = score_topk_bytes(N, L, topk) +
+                    (q_dt == MISA_FP8_E4M3 ? q8_bytes(N, H_I, d) : 0);
+  if (!ws) return MISA_ERR_NULL;
+  if (ws_bytes < rb + sb) return MISA_ERR_WORKSPACE;
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  // the fused form: decode rows (not the one-sequence GEMM shapes), bf16
+  // queries, bf16 or e4m3 keys; otherwise the two calls in turn
+  const bool fused = q_dt == MISA_BF16 && k_dt != MISA_F32 && !(S == 1 && N >= kOneRowMinN);
+  if (!fused) {
+    rc = misa_route_heads(q, q_dt, q_scale, w, kbar, k, k_scale, k_dt, block_table, page_size,
+                          q_seq, q_pos, N, S, L, d, B, H_I, h, heads, head_score, wsb, rb,
+                          stream);
+    if (rc) return rc;
+    return misa_score_topk(q, q_dt, q_scale, w, k, k_scale, k_dt, block_table, page_size, q_seq,
+                           q_pos, heads, N, S, L, d, H_I, h, topk, idx, score, wsb + rb, sb,
+                           stream);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const TopkLayout lay = topk_layout(N, L);
+  uint32_t* hist = lay.one_row ? nullptr : reinterpret_cast<uint32_t*>(wsb + rb + lay.off_hist);
+  const int nchunks = route_chunks(L, B);
+  float* partial = reinterpret_cast<float*>(wsb);
+  misa::RouteArgs a{q, q_dt, nullptr, w, kbar, k, k_scale, k_dt, q_seq, q_pos, N, S, L, d, B,
+                    H_I, h, heads, head_score, partial, nchunks, nullptr, ki};
+  a.partials_only = true;
+  a.hist0 = hist;
+  const hipError_t e = misa::launch_route(a, st);
+  if (e != hipSuccess) return hip_status(e);
+  const FusedRoute fr{partial, nchunks, B, heads, head_score};
+  return score_topk_impl(q, q_dt, q_scale, w, k, k_scale, k_dt, block_table, page_size, q_seq,
+                         q_pos, nullptr, N, S, L, d, H_I, h, topk, idx, score, wsb + rb, sb,
+                         stream, &fr);
 }
 
 int32_t misa_rerank(const void* q, int32_t q_dt, const float* q_scale, const float* w,

@@ -85,6 +85,12 @@ struct RouteArgs {
   int nchunks;           // chunks of full blocks per row
   uint16_t* kb_split;    // workspace [2, M, d] bf16: pooled keys as hi + lo (one-sequence GEMM)
   KeyIndex kidx;         // where the keys of the partial block live
+  // routed decode step (heads picked by the scoring kernel): only partials
+  // [N, nchunks + 1, H_I] with the partial-block term in slot nchunks, no
+  // selection kernel; hist0 (if not NULL), the scoring kernel's level-0
+  // histogram [N, kHistWords], is cleared on the way.
+  bool partials_only = false;
+  uint32_t* hist0 = nullptr;
 };
 int route_blocks_per_chunk();
 bool route_uses_mfma(const RouteArgs& a);
@@ -108,6 +114,15 @@ struct ScoreArgs {
   int u_stride;
   uint32_t* hist0;          // [N, kHistWords] level-0 histogram (NULL = skip)
   KeyIndex kidx;
+  // routed decode step: the kernel picks each row's h heads itself from the
+  // router's partials [N, route_nchunks + 1, H_I] (slot route_nchunks = the
+  // partial-block term) before scoring, and workgroup 0 of each row writes
+  // them to heads_out [N, h] (and r to head_score_out [N, H_I] if not NULL).
+  // heads must be NULL then.  NULL route_partial: heads come from `heads`.
+  const float* route_partial = nullptr;
+  int route_nchunks = 0, B = 0;
+  int32_t* heads_out = nullptr;
+  float* head_score_out = nullptr;
 };
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
 

@@ -20,36 +20,12 @@
 //    ascending order.
 #include "common.hpp"
 #include "kernels.hpp"
-#include "partial_block.hpp"
+#include "route_select.hpp"
 
 namespace misa {
 namespace {
 
 constexpr int kRouteBlocks = 16;     // pooled blocks per route_partial workgroup
-
-// Head row (D values) of q into registers as fp32.
-template <int QT, int D>
-__device__ __forceinline__ void load_q_row(const void* q, size_t row, float (&out)[D]) {
-  if constexpr (QT == DT_F32) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q) + row * D);
-#pragma unroll
-    for (int i = 0; i < D / 4; ++i) {
-      const float4 x = p[i];
-      out[4 * i] = x.x;
-      out[4 * i + 1] = x.y;
-      out[4 * i + 2] = x.z;
-      out[4 * i + 3] = x.w;
-    }
-  } else if constexpr (QT == DT_BF16) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + row * D);
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) unpack16<DT_BF16>(p[i], &out[8 * i]);
-  } else {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(q) + row * D);
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) unpack16<DT_E4M3>(p[i], &out[16 * i]);
-  }
-}
 
 template <int QT, int D>
 __global__ __launch_bounds__(256) void route_partial_kernel(
@@ -120,11 +96,26 @@ __global__ __launch_bounds__(256) void route_partial_kernel(
 // the B operand, one column per block.  Lane (g, c) gets heads 4g..4g+3
 // against block c; ReLU, the visibility mask and the sum over the 16 blocks
 // (across lanes) give the chunk's partial for every head.
-template <int D>
+//
+// For the routed decode step that selects heads inside the scoring kernel
+// (RoutePartialExtra), the grid has one more workgroup per row: it writes the
+// row's partial-block term ReLU(q_j . mean of the visible keys of the last,
+// incomplete block) to chunk slot nchunks (0 when the row ends on a block
+// boundary), and chunk 0 of each row clears that row's level-0 histogram for
+// the scoring kernel.
+struct RoutePartialExtra {
+  const void* k;
+  const float* k_scale;
+  KeyIndex ki;
+  uint32_t* hist0;         // [N, kHistWords] cleared by chunk 0 (NULL: no extra work)
+};
+
+template <int KT, int D>
 __global__ __launch_bounds__(256) void route_partial_mfma_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ kbar,
     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int L, int B, int H_I,
-    int nchunks, float* __restrict__ partial) {
+    int nchunks, int pstride, float* __restrict__ partial, RoutePartialExtra x) {
+  using PM = PieceMap<KT, D>;
   constexpr int KK = D / 32;
   constexpr int STRIDE = D * 2 + 16;                   // padded bf16 row (bytes)
   __shared__ __align__(16) uint8_t hi_t[kRouteBlocks * STRIDE];
@@ -132,11 +123,30 @@ __global__ __launch_bounds__(256) void route_partial_mfma_kernel(
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
   const int n = blockIdx.y, chunk = blockIdx.x;
+  if (x.hist0 && chunk == 0) {
+    uint32_t* h = x.hist0 + static_cast<size_t>(n) * kHistWords;
+    for (int i = threadIdx.x; i < kHistWords; i += 256) h[i] = 0u;
+  }
+  float* out = partial + (static_cast<size_t>(n) * pstride + chunk) * H_I;
+  if (chunk == nchunks) {
+    // the partial block's term, exactly as the router's selection step forms it
+    __shared__ float psum[PM::RG][D + 1];
+    __shared__ float mean[D];
+    const int Ln = q_pos[n] + 1;
+    const int Mf = Ln / B;
+    const int cp = Ln - Mf * B;
+    if (cp > 0) partial_block_mean<KT, D>(x.k, x.k_scale, x.ki, q_seq[n], Mf * B, Ln, psum, mean);
+    if (threadIdx.x < H_I)
+      out[threadIdx.x] =
+          cp > 0 ? partial_block_term<DT_BF16, D>(q, static_cast<size_t>(n) * H_I + threadIdx.x,
+                                                  mean)
+                 : 0.f;
+    return;
+  }
   const int Mf = (q_pos[n] + 1) / B;                   // blocks fully visible to row n
   const int M = (L + B - 1) / B;
   const int b0 = chunk * kRouteBlocks;
   const int nb = min(kRouteBlocks, Mf - b0);
-  float* out = partial + (static_cast<size_t>(n) * nchunks + chunk) * H_I;
   if (nb <= 0) {
     for (int j = threadIdx.x; j < H_I; j += 256) out[j] = 0.f;
     return;
@@ -357,14 +367,10 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     const int32_t* __restrict__ q_pos, int L, int B, int H_I, int h, int nchunks,
     const float* __restrict__ partial, int32_t* __restrict__ heads,
     float* __restrict__ head_score, KeyIndex ki, const float* __restrict__ q_scale) {
-  constexpr int EB = KeyBytes<KT>::value;
-  constexpr int PIECES = D * EB / 16;          // 16-byte pieces per key row
-  constexpr int EPP = 16 / EB;                 // elements per piece
-  constexpr int RG = 256 / PIECES;             // key rows per pass
-  __shared__ float psum[RG][D + 1];
+  using PM = PieceMap<KT, D>;
+  __shared__ float psum[PM::RG][D + 1];
   __shared__ float mean[D];
   __shared__ float red[4][64];
-  __shared__ float rs[64];
 
   const int n = blockIdx.x;
   const int Ln = q_pos[n] + 1;
@@ -372,84 +378,30 @@ __global__ __launch_bounds__(256) void route_select_kernel(
   const int cp = Ln - Mf * B;                 // visible keys of the partial block
   const int s = q_seq[n];
 
-  // chunk partial sums: 4 groups of 64 threads, 8 loads in flight per pass,
-  // fixed summation order
-  {
-    const int j = threadIdx.x & 63, g = threadIdx.x >> 6;
-    float a = 0.f;
-    if (j < H_I) {
-      const float* pp = partial + static_cast<size_t>(n) * nchunks * H_I + j;
-      for (int c0 = g; c0 < nchunks; c0 += 32) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int c = c0 + 4 * u;
-          v[u] = c < nchunks ? pp[static_cast<size_t>(c) * H_I] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) a += v[u];
-      }
-    }
-    red[g][j] = a;
-  }
-  // partial-block mean over the row's visible keys of that block
-  if (cp > 0) {
-    const int piece = threadIdx.x % PIECES, rg = threadIdx.x / PIECES;
-    float acc[EPP];
-    piece_sum<KT, D>(k, k_scale, ki, s, Mf * B, Ln, threadIdx.x, acc);
-#pragma unroll
-    for (int e = 0; e < EPP; ++e) psum[rg][piece * EPP + e] = acc[e];
-  }
-  __syncthreads();
-  if (cp > 0 && threadIdx.x < D) {
-    float m = 0.f;
-    for (int r = 0; r < RG; ++r) m += psum[r][threadIdx.x];
-    mean[threadIdx.x] = m / static_cast<float>(cp);
-  }
-  __syncthreads();
-
+  sum_chunk_partials(partial + static_cast<size_t>(n) * nchunks * H_I, nchunks, H_I, red);
+  if (cp > 0)
+    partial_block_mean<KT, D>(k, k_scale, ki, s, Mf * B, Ln, psum, mean);
+  else
+    __syncthreads();
   if (threadIdx.x < 64) {
     const int j = threadIdx.x;
     float r = -1.f;
     if (j < H_I) {
-      float a = (red[0][j] + red[1][j]) + (red[2][j] + red[3][j]);
-      if (cp > 0) {
-        float qr[D];
-        load_q_row<QT, D>(q, static_cast<size_t>(n) * H_I + j, qr);
-        float dt = 0.f;
-#pragma unroll
-        for (int i = 0; i < D; ++i) dt += qr[i] * mean[i];
-        a += fmaxf(dt, 0.f);
-      }
+      float a = combine_partials(red, j);
+      if (cp > 0) a += partial_block_term<QT, D>(q, static_cast<size_t>(n) * H_I + j, mean);
       float wj = w[static_cast<size_t>(n) * H_I + j];
       if (QT == DT_E4M3) wj *= q_scale[static_cast<size_t>(n) * H_I + j];
       r = fabsf(wj) * a;
       if (head_score) head_score[static_cast<size_t>(n) * H_I + j] = r;
     }
-    // top-h: a head is routed when fewer than h heads beat it under
-    // (r desc, head index asc); the 64 scores sit in LDS for the ranking
-    rs[j] = r;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    int rank = 0;
-    if (j < H_I) {
-      for (int o = 0; o < H_I; ++o) {
-        const float ro = rs[o];
-        rank += (ro > r || (ro == r && o < j)) ? 1 : 0;
-      }
-    }
-    const bool chosen = j < H_I && rank < h;
-    const uint64_t mask = __ballot(chosen);
-    if (chosen) {
-      const int pos = __popcll(mask & ((1ull << j) - 1ull));
-      heads[static_cast<size_t>(n) * h + pos] = j;
-    }
+    rank_heads(r, H_I, h, heads + static_cast<size_t>(n) * h);
   }
 }
 
 template <int QT, int KT, int D>
 hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
   int nchunks = a.nchunks;
+  if (a.partials_only && route_uses_mfma(a)) return hipErrorInvalidValue;
   if (route_uses_mfma(a)) {
     nchunks = 1;
     const int M = (a.L + a.B - 1) / a.B;
@@ -475,11 +427,19 @@ hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
   } else if constexpr (QT == DT_E4M3) {
     return hipErrorInvalidValue;   // e4m3 queries reach the router only on the GEMM path
   } else {
-    if constexpr (QT == DT_BF16)
-      MISA_LAUNCH(K_ROUTE_PARTIAL, route_partial_mfma_kernel<D>, dim3(a.nchunks, a.N), dim3(256),
-                  0, st, static_cast<const uint16_t*>(a.q), a.kbar, a.q_seq, a.q_pos, a.L, a.B,
-                  a.H_I, a.nchunks, a.partial);
-    else
+    if constexpr (QT == DT_BF16) {
+      // the routed decode step: partials plus the partial-block slot, heads
+      // picked by the scoring kernel
+      const bool fused = a.partials_only;
+      const RoutePartialExtra x{a.k, a.k_scale, a.kidx, a.hist0};
+      MISA_LAUNCH(K_ROUTE_PARTIAL, (route_partial_mfma_kernel<KT, D>),
+                  dim3(a.nchunks + (fused ? 1 : 0), a.N), dim3(256), 0, st,
+                  static_cast<const uint16_t*>(a.q), a.kbar, a.q_seq, a.q_pos, a.L, a.B, a.H_I,
+                  a.nchunks, a.nchunks + (fused ? 1 : 0), a.partial, x);
+      if (fused) return hipGetLastError();
+    } else if (a.partials_only) {
+      return hipErrorInvalidValue;     // the fused decode step takes bf16 queries only
+    } else
       MISA_LAUNCH(K_ROUTE_PARTIAL, (route_partial_kernel<QT, D>), dim3(a.nchunks, a.N),
                   dim3(256), 0, st, a.q, a.kbar, a.q_seq, a.q_pos, a.L, a.B, a.H_I, a.nchunks,
                   a.partial);

@@ -33,6 +33,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "route_select.hpp"
 
 namespace misa {
 namespace {
@@ -54,6 +55,10 @@ struct ScoreParams {
   uint32_t* hist0;
   int tiles_per_wave;
   KeyIndex ki;
+  const float* route_partial;   // routed decode step: router partials (see ScoreArgs)
+  int route_nchunks, B;
+  int32_t* heads_out;
+  float* head_score_out;
 };
 
 template <int KT, int D>
@@ -221,12 +226,16 @@ __device__ __forceinline__ void score_group(const RawGroup<KT, D, U>& raw, const
   }
 }
 
-template <int KT, int NT, int D, int U, bool CAND>
+template <int KT, int NT, int D, int U, bool CAND, bool ROUTE>
 __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
   using LY = KeyLayout<KT, D>;
   constexpr int KK = LY::KK;
   __shared__ uint32_t lh[kBins0];
   __shared__ __align__(16) uint8_t tiles[4][LY::TILE_LDS];
+  __shared__ int32_t heads_lds[ROUTE ? 64 : 1];
+  __shared__ __align__(16) uint16_t qlds[ROUTE ? 64 * D : 8];   // the row's query heads
+  __shared__ float wlds[ROUTE ? 64 : 1];                          // and their weights
+  __shared__ float red_lds[ROUTE ? 4 : 1][64];                    // router partial sums
 
   const int n = blockIdx.y;
   const int len = CAND ? p.ncols : p.q_pos[n] + 1;
@@ -259,16 +268,71 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
     }
   }
 
-  // first key group in flight before anything else
+  // routed step: the selection's inputs are loaded first (the row's query
+  // heads, their weights, the router partials), so that waiting for them
+  // leaves the first key group, issued right behind, in flight
+  constexpr int QV = ROUTE ? 64 * D / 8 / 256 : 1;     // 16-byte query pieces per thread
+  u32x4_t qv[QV];
+  float pv[ROUTE ? 16 : 1];
+  float wj = 0.f, tail = 0.f;
+  const size_t prow = static_cast<size_t>(n) * (p.route_nchunks + 1) * p.H_I;
+  const bool partial_block = ROUTE && len % p.B != 0;
+  if constexpr (ROUTE) {
+    // (unconditional loads, clamped to valid elements: an exact wait count)
+    const int nqv = p.H_I * D / 8;
+    const u32x4_t* qsrc =
+        reinterpret_cast<const u32x4_t*>(p.q + static_cast<size_t>(n) * p.H_I * D);
+#pragma unroll
+    for (int i = 0; i < QV; ++i) {
+      const int f = threadIdx.x + 256 * i;
+      qv[i] = qsrc[f < nqv ? f : nqv - 1];
+    }
+    const int jc = static_cast<int>(threadIdx.x & 63) < p.H_I ? (threadIdx.x & 63) : p.H_I - 1;
+    wj = p.w[static_cast<size_t>(n) * p.H_I + jc];
+    tail = p.route_partial[prow + static_cast<size_t>(p.route_nchunks) * p.H_I + jc];
+    load_chunk_partials(p.route_partial + prow, p.route_nchunks, p.H_I, pv);
+  }
+
+  // first key group in flight before anything else (unconditional: a
+  // wavefront without tiles reads a valid row and scores nothing)
   u32x4_t ra[U][LY::NLOAD], rb[U][LY::NLOAD];
   float sa[U], sb[U];
   uint32_t va = 0, vb = 0;
-  if (wtiles > 0)
-    va = issue_group<KT, D, U, CAND>(ra, sa, wtile, tstride, lane, c, len, crow, kseq, sseq,
-                                     p.ki, s, 0, page_v);
+  va = issue_group<KT, D, U, CAND>(ra, sa, wtile, tstride, lane, c, len, crow, kseq, sseq,
+                                   p.ki, s, 0, page_v);
 
   if (do_hist) {
     for (int b = threadIdx.x; b < kBins0; b += 256) lh[b] = 0u;
+  }
+  if constexpr (ROUTE) {
+    // the router's selection step for this row, as the selection kernel
+    // forms it (same partial order, same ranking), while the first keys load
+    finish_chunk_partials(p.route_partial + prow, p.route_nchunks, p.H_I, pv, red_lds);
+    const int nqv = p.H_I * D / 8;
+#pragma unroll
+    for (int i = 0; i < QV; ++i) {
+      const int f = threadIdx.x + 256 * i;
+      if (f < nqv) reinterpret_cast<u32x4_t*>(qlds)[f] = qv[i];
+    }
+    if (threadIdx.x < 64) wlds[threadIdx.x] = static_cast<int>(threadIdx.x) < p.H_I ? wj : 0.f;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const int j = threadIdx.x;
+      float r = -1.f;
+      if (j < p.H_I) {
+        float a = combine_partials(red_lds, j);
+        if (partial_block) a += tail;
+        r = fabsf(wj) * a;
+        if (blockIdx.x == 0 && p.head_score_out)
+          p.head_score_out[static_cast<size_t>(n) * p.H_I + j] = r;
+      }
+      rank_heads(r, p.H_I, p.nrows, heads_lds);
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      if (blockIdx.x == 0 && j < p.nrows)
+        p.heads_out[static_cast<size_t>(n) * p.nrows + j] = heads_lds[j];
+    }
+    __syncthreads();
   }
   // A operand: head rows of this query row; W: weights of this lane's D rows.
   bf16x8_t a[NT][KK];
@@ -278,8 +342,8 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
     const int r = nt * 16 + c;
     int j = 0;
     const bool rv = r < p.nrows;
-    if (rv) j = p.heads ? p.heads[static_cast<size_t>(n) * p.nrows + r] : r;
-    const uint16_t* qrow = p.q + (static_cast<size_t>(n) * p.H_I + j) * D;
+    if (rv) j = ROUTE ? heads_lds[r] : p.heads ? p.heads[static_cast<size_t>(n) * p.nrows + r] : r;
+    const uint16_t* qrow = ROUTE ? qlds + j * D : p.q + (static_cast<size_t>(n) * p.H_I + j) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + elem_off<KT>(g, kk));
@@ -291,8 +355,9 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
       const int rr = nt * 16 + 4 * g + i;
       float wf = 0.f;
       if (rr < p.nrows) {
-        const int jj = p.heads ? p.heads[static_cast<size_t>(n) * p.nrows + rr] : rr;
-        wf = p.w[static_cast<size_t>(n) * p.H_I + jj];
+        const int jj = ROUTE ? heads_lds[rr]
+                             : p.heads ? p.heads[static_cast<size_t>(n) * p.nrows + rr] : rr;
+        wf = ROUTE ? wlds[jj] : p.w[static_cast<size_t>(n) * p.H_I + jj];
       }
       wv[nt][i] = wf;
     }
@@ -427,21 +492,30 @@ hipError_t launch_mfma(const ScoreArgs& a, hipStream_t st, int tiles_per_wave) {
   p.hist0 = a.hist0;
   p.tiles_per_wave = tiles_per_wave;
   p.ki = a.kidx;
+  p.route_partial = a.route_partial;
+  p.route_nchunks = a.route_nchunks;
+  p.B = a.B;
+  p.heads_out = a.heads_out;
+  p.head_score_out = a.head_score_out;
+  if (a.route_partial) p.nrows = a.h;
   const int maxlen = a.cand ? a.ncols : a.L;
   const int per_wg = 4 * tiles_per_wave * 16;
   const int nchunks = (maxlen + per_wg - 1) / per_wg;
   if (a.cand)
-    MISA_LAUNCH(K_SCORE_MFMA, (score_mfma_kernel<KT, NT, D, U, true>), dim3(nchunks, a.N),
+    MISA_LAUNCH(K_SCORE_MFMA, (score_mfma_kernel<KT, NT, D, U, true, false>), dim3(nchunks, a.N),
+                dim3(256), 0, st, p);
+  else if (a.route_partial)
+    MISA_LAUNCH(K_SCORE_MFMA, (score_mfma_kernel<KT, NT, D, U, false, true>), dim3(nchunks, a.N),
                 dim3(256), 0, st, p);
   else
-    MISA_LAUNCH(K_SCORE_MFMA, (score_mfma_kernel<KT, NT, D, U, false>), dim3(nchunks, a.N),
-                dim3(256), 0, st, p);
+    MISA_LAUNCH(K_SCORE_MFMA, (score_mfma_kernel<KT, NT, D, U, false, false>),
+                dim3(nchunks, a.N), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
 template <int KT, int D>
 hipError_t launch_mfma_rows(const ScoreArgs& a, hipStream_t st, int tpw) {
-  const int nrows = a.heads ? a.h : a.H_I;
+  const int nrows = (a.heads || a.route_partial) ? a.h : a.H_I;
   if (nrows <= 16) return launch_mfma<KT, 1, D>(a, st, tpw);
   if (nrows <= 32) return launch_mfma<KT, 2, D>(a, st, tpw);
   if (nrows <= 48) return launch_mfma<KT, 3, D>(a, st, tpw);

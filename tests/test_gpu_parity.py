@@ -833,3 +833,59 @@ def test_blocks_parity(k_dt, page_size, m):
     heads, _ = dp.route(kbar)
     blocks, idx, sc = dp.score_topk_blocks(kbar, heads, m_blocks=m)
     check_blocks(p, np_(heads), np_(blocks), np_(idx), np_(sc), m)
+
+
+# ---------------------------------------------------------------- routing inside the scoring pass
+# misa_route_score_topk: the same bits as misa_route_heads + misa_score_topk,
+# whether the head selection runs at the start of the scoring kernel (decode
+# rows, bf16 queries) or the two calls run in turn (every other shape).
+@pytest.mark.parametrize("case", [
+    dict(N=4, S=4, L=9000, d=128, H_I=64, h=8, B=128, topk=2048,
+         q_pos=np.array([8999, 8191, 127, 5000], np.int32)),               # partial blocks, ragged
+    dict(N=3, S=2, L=5000, d=64, H_I=32, h=8, B=64, topk=300,
+         q_seq=np.array([0, 1, 1], np.int32)),
+    dict(N=2, S=2, L=4097, d=128, H_I=16, h=1, B=32, topk=50),
+    dict(N=5, S=1, L=3000, d=128, H_I=64, h=16, B=128, topk=3100),         # k > L_n
+    dict(N=1, S=1, L=1, d=128, H_I=16, h=16, B=128, topk=5),              # one key
+    dict(N=130, S=1, L=2000, d=128, H_I=16, h=4, B=64, topk=100),          # GEMM shapes: two calls
+])
+@pytest.mark.parametrize("k_dt,q_dt,page_size", [(synth.BF16, synth.BF16, 0),
+                                                 (synth.FP8, synth.BF16, 0),
+                                                 (synth.BF16, synth.BF16, 64),
+                                                 (synth.FP8, synth.FP8, 0)])
+def test_route_score_topk_equals_two_calls(case, k_dt, q_dt, page_size):
+    p = synth.small("fused", 71, k_dt=k_dt, q_dt=q_dt, **case)
+    log(f"[fused] N={p.N} S={p.S} L={p.L} d={p.d} H_I={p.H_I} h={p.h} k={p.topk} "
+        f"q_dt={synth.DTYPE_NAMES[q_dt]} k_dt={synth.DTYPE_NAMES[k_dt]} page={page_size}")
+    dp = DeviceProblem(p, page_size=page_size, page_seed=3)
+    kbar = dp.pool()
+    heads, r = dp.route(kbar)
+    idx, sc = dp.score_topk(heads)
+    h2, r2, idx2, sc2 = dp.route_score_topk(kbar)
+    assert np.array_equal(np_(heads), np_(h2))
+    assert np.array_equal(np_(r).view(np.uint32), np_(r2).view(np.uint32))
+    assert np.array_equal(np_(idx), np_(idx2))
+    assert np.array_equal(np_(sc).view(np.uint32), np_(sc2).view(np.uint32))
+
+
+def test_route_score_topk_against_the_oracle():
+    """The fused call at a decode shape vs the oracle (heads within the
+    router tolerance, top-k on the GPU's heads)."""
+    p = synth.small("fused_ref", 72, N=4, S=4, L=20000, d=128, H_I=64, h=8, B=128, topk=2048,
+                    q_pos=np.array([19999, 12000, 640, 19000], np.int32))
+    dp = DeviceProblem(p)
+    heads, r, idx, sc = (np_(t) for t in dp.route_score_topk(dp.pool()))
+    _, ref_r = oracle.route_heads(p)
+    assert np.all(np.abs(r - ref_r) <= tol(ref_r)), "router scores"
+    check_heads(heads, ref_r, p.h)
+    check_topk(idx, sc, oracle.scores(p, heads), p.topk, p.visible())
+
+
+def test_route_score_topk_integer_inputs_bit_exact():
+    p = synth.integer_problem("fused_int", 73, N=3, S=3, L=3000, d=128, H_I=32, h=6, B=64,
+                              topk=400, q_pos=np.array([2999, 1000, 63], np.int32))
+    dp = DeviceProblem(p)
+    heads, r, idx, sc = (np_(t) for t in dp.route_score_topk(dp.pool()))
+    ref_heads, _ = oracle.route_heads(p)
+    assert np.array_equal(heads, ref_heads)
+    check_topk(idx, sc, oracle.scores(p, ref_heads), p.topk, p.visible(), exact=True)

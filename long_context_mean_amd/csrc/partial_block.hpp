@@ -3,9 +3,9 @@
 // A query row whose visible prefix ends inside a block pools that block from
 // its visible keys only (the mean of keys [t0, t1) of sequence s).  The 256
 // threads of a workgroup split each key row into 16-byte pieces: thread
-// (rg, piece) sums rows t0 + rg, t0 + rg + RG, ... of its piece.  All loads of
-// a batch are issued before any is used, so a block costs one or two memory
-// round trips instead of one per pass.
+// (rg, piece) sums rows t0 + rg, t0 + rg + RG, ... of its piece, in that order.
+// All loads of a batch are issued before any is used, so a 64-key block costs
+// one memory round trip instead of one per pass.
 #pragma once
 
 #include "common.hpp"
@@ -27,7 +27,9 @@ __device__ __forceinline__ void piece_sum(const void* k, const float* k_scale, c
                                           int s, int t0, int t1, int tid,
                                           float (&acc)[PieceMap<KT, D>::EPP]) {
   using PM = PieceMap<KT, D>;
-  constexpr int BATCH = 8;
+  // enough loads in flight to cover a 64-key block in one round trip (more
+  // would only hold registers; a longer range takes further passes)
+  constexpr int BATCH = PM::RG >= 64 ? 1 : (64 / PM::RG > 8 ? 8 : 64 / PM::RG);
   const int piece = tid % PM::PIECES, rg = tid / PM::PIECES;
   const uint8_t* kb = static_cast<const uint8_t*>(k);
 #pragma unroll

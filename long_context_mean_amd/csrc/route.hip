@@ -132,15 +132,18 @@ __global__ __launch_bounds__(256) void route_partial_mfma_kernel(
     // the partial block's term, exactly as the router's selection step forms it
     __shared__ float psum[PM::RG][D + 1];
     __shared__ float mean[D];
+    __shared__ float part[4][64];
+    QQuarter<DT_BF16, D> qq;
+    load_q_quarter<DT_BF16, D>(q, static_cast<size_t>(n) * H_I, H_I, qq);
     const int Ln = q_pos[n] + 1;
     const int Mf = Ln / B;
     const int cp = Ln - Mf * B;
-    if (cp > 0) partial_block_mean<KT, D>(x.k, x.k_scale, x.ki, q_seq[n], Mf * B, Ln, psum, mean);
+    if (cp > 0) {
+      partial_block_mean<KT, D>(x.k, x.k_scale, x.ki, q_seq[n], Mf * B, Ln, psum, mean);
+      partial_block_terms<DT_BF16, D>(qq, H_I, mean, part);
+    }
     if (threadIdx.x < H_I)
-      out[threadIdx.x] =
-          cp > 0 ? partial_block_term<DT_BF16, D>(q, static_cast<size_t>(n) * H_I + threadIdx.x,
-                                                  mean)
-                 : 0.f;
+      out[threadIdx.x] = cp > 0 ? partial_block_term_sum(part, threadIdx.x) : 0.f;
     return;
   }
   const int Mf = (q_pos[n] + 1) / B;                   // blocks fully visible to row n
@@ -360,7 +363,9 @@ __global__ __launch_bounds__(256, 4) void route_mfma_kernel(const void* __restri
   }
 }
 
-template <int QT, int KT, int D>
+// NP: the chunk partials each thread loads up front (1 when the partials
+// come from the MFMA router, which leaves one chunk per row).
+template <int QT, int KT, int D, int NP>
 __global__ __launch_bounds__(256) void route_select_kernel(
     const void* __restrict__ q, const float* __restrict__ w, const void* __restrict__ k,
     const float* __restrict__ k_scale, const int32_t* __restrict__ q_seq,
@@ -371,6 +376,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(
   __shared__ float psum[PM::RG][D + 1];
   __shared__ float mean[D];
   __shared__ float red[4][64];
+  __shared__ float part[4][64];
 
   const int n = blockIdx.x;
   const int Ln = q_pos[n] + 1;
@@ -378,19 +384,29 @@ __global__ __launch_bounds__(256) void route_select_kernel(
   const int cp = Ln - Mf * B;                 // visible keys of the partial block
   const int s = q_seq[n];
 
-  sum_chunk_partials(partial + static_cast<size_t>(n) * nchunks * H_I, nchunks, H_I, red);
-  if (cp > 0)
+  // the loads that need nothing else (partials, this thread's quarter of a
+  // query head, the head's weight) go out together, ahead of the key reads
+  const float* prow = partial + static_cast<size_t>(n) * nchunks * H_I;
+  float pv[NP];
+  load_chunk_partials<NP>(prow, nchunks, H_I, pv);
+  QQuarter<QT, D> qq;
+  load_q_quarter<QT, D>(q, static_cast<size_t>(n) * H_I, H_I, qq);
+  const int jc = (threadIdx.x & 63) < H_I ? (threadIdx.x & 63) : H_I - 1;
+  float wj = w[static_cast<size_t>(n) * H_I + jc];
+  if (QT == DT_E4M3) wj *= q_scale[static_cast<size_t>(n) * H_I + jc];
+  finish_chunk_partials<NP>(prow, nchunks, H_I, pv, red);
+  if (cp > 0) {
     partial_block_mean<KT, D>(k, k_scale, ki, s, Mf * B, Ln, psum, mean);
-  else
+    partial_block_terms<QT, D>(qq, H_I, mean, part);
+  } else {
     __syncthreads();
+  }
   if (threadIdx.x < 64) {
     const int j = threadIdx.x;
     float r = -1.f;
     if (j < H_I) {
       float a = combine_partials(red, j);
-      if (cp > 0) a += partial_block_term<QT, D>(q, static_cast<size_t>(n) * H_I + j, mean);
-      float wj = w[static_cast<size_t>(n) * H_I + j];
-      if (QT == DT_E4M3) wj *= q_scale[static_cast<size_t>(n) * H_I + j];
+      if (cp > 0) a += partial_block_term_sum(part, j);
       r = fabsf(wj) * a;
       if (head_score) head_score[static_cast<size_t>(n) * H_I + j] = r;
     }
@@ -444,7 +460,15 @@ hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
                   dim3(256), 0, st, a.q, a.kbar, a.q_seq, a.q_pos, a.L, a.B, a.H_I, a.nchunks,
                   a.partial);
   }
-  MISA_LAUNCH(K_ROUTE_SELECT, (route_select_kernel<QT, KT, D>), dim3(a.N), dim3(256), 0, st,
+  if constexpr (D == 128 && QT != DT_F32) {
+    if (nchunks == 1) {
+      MISA_LAUNCH(K_ROUTE_SELECT, (route_select_kernel<QT, KT, D, 1>), dim3(a.N), dim3(256), 0,
+                  st, a.q, a.w, a.k, a.k_scale, a.q_seq, a.q_pos, a.L, a.B, a.H_I, a.h, nchunks,
+                  a.partial, a.heads, a.head_score, a.kidx, a.q_scale);
+      return hipGetLastError();
+    }
+  }
+  MISA_LAUNCH(K_ROUTE_SELECT, (route_select_kernel<QT, KT, D, 16>), dim3(a.N), dim3(256), 0, st,
               a.q, a.w, a.k, a.k_scale, a.q_seq, a.q_pos, a.L, a.B, a.H_I, a.h, nchunks,
               a.partial, a.heads, a.head_score, a.kidx, a.q_scale);
   return hipGetLastError();

@@ -37,53 +37,50 @@ __device__ __forceinline__ void load_q_row(const void* q, size_t row, float (&ou
 }
 
 // Chunk partial sums of one row: thread (g, j) = (tid / 64, tid % 64) sums
-// chunks g, g + 4, g + 8, ... of head j in that order (16 loads in flight per
-// pass) into red[g][j].  load_chunk_partials issues the first pass's loads
-// (so a caller can put other loads behind them), finish_chunk_partials adds
-// them and runs the remaining passes; the caller synchronises before reading
-// red.
+// chunks g, g + 4, g + 8, ... of head j in that order into red[g][j].
+// load_chunk_partials issues the first pass's NP loads (so a caller can put
+// other loads behind them), finish_chunk_partials adds them and runs the
+// remaining passes (16 loads in flight each, 4 when NP < 16); the caller synchronises before
+// reading red.  The sum does not depend on NP: the masked slots add +0 to a
+// sum of non-negative terms.
+template <int NP = 16>
 __device__ __forceinline__ void load_chunk_partials(const float* __restrict__ partial_row,
-                                                    int nchunks, int H_I, float (&v)[16]) {
+                                                    int nchunks, int H_I, float (&v)[NP]) {
   const int j = threadIdx.x & 63, g = threadIdx.x >> 6;
   // every load is issued (clamped to an element of the row; the sum masks
   // them), so the wait for them is an exact count that leaves later loads in
   // flight
   const int jc = j < H_I ? j : H_I - 1;
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
+  for (int u = 0; u < NP; ++u) {
     const int c = g + 4 * u;
     v[u] = partial_row[static_cast<size_t>(c < nchunks ? c : nchunks - 1) * H_I + jc];
   }
 }
 
+template <int NP = 16>
 __device__ __forceinline__ void finish_chunk_partials(const float* __restrict__ partial_row,
-                                                      int nchunks, int H_I, const float (&v)[16],
+                                                      int nchunks, int H_I, const float (&v)[NP],
                                                       float (&red)[4][64]) {
   const int j = threadIdx.x & 63, g = threadIdx.x >> 6;
   float a = 0.f;
 #pragma unroll
-  for (int u = 0; u < 16; ++u) a += (j < H_I && g + 4 * u < nchunks) ? v[u] : 0.f;
+  for (int u = 0; u < NP; ++u) a += (j < H_I && g + 4 * u < nchunks) ? v[u] : 0.f;
   if (j < H_I) {
+    constexpr int RP = NP < 16 ? 4 : 16;   // loads in flight per remaining pass
     const float* pp = partial_row + j;
-    for (int c0 = g + 64; c0 < nchunks; c0 += 64) {
-      float w[16];
+    for (int c0 = g + 4 * NP; c0 < nchunks; c0 += 4 * RP) {
+      float w[RP];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
+      for (int u = 0; u < RP; ++u) {
         const int c = c0 + 4 * u;
         w[u] = c < nchunks ? pp[static_cast<size_t>(c) * H_I] : 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < 16; ++u) a += w[u];
+      for (int u = 0; u < RP; ++u) a += w[u];
     }
   }
   red[g][j] = a;
-}
-
-__device__ __forceinline__ void sum_chunk_partials(const float* __restrict__ partial_row,
-                                                   int nchunks, int H_I, float (&red)[4][64]) {
-  float v[16];
-  load_chunk_partials(partial_row, nchunks, H_I, v);
-  finish_chunk_partials(partial_row, nchunks, H_I, v, red);
 }
 
 __device__ __forceinline__ float combine_partials(const float (&red)[4][64], int j) {
@@ -112,16 +109,58 @@ __device__ __forceinline__ void partial_block_mean(const void* k, const float* k
   __syncthreads();
 }
 
-// ReLU(q[row] . mean), the partial block's term of one head.
+// A quarter of a head row of q as raw 16-byte pieces: thread (w, j) =
+// (tid / 64, tid % 64) holds elements [w * D / 4, (w + 1) * D / 4) of head j
+// (clamped to head H_I - 1, so every load is issued and the caller can wait
+// for it with an exact count behind later loads).
 template <int QT, int D>
-__device__ __forceinline__ float partial_block_term(const void* q, size_t row,
-                                                    const float (&mean)[D]) {
-  float qr[D];
-  load_q_row<QT, D>(q, row, qr);
-  float dt = 0.f;
+struct QQuarter {
+  static constexpr int DW = D / 4;
+  static constexpr int NV = DW * KeyBytes<QT>::value / 16;
+  static_assert(NV * 16 == DW * KeyBytes<QT>::value, "a quarter of d must be whole 16-byte loads");
+  uint4 x[NV];
+};
+
+template <int QT, int D>
+__device__ __forceinline__ void load_q_quarter(const void* q, size_t row0, int H_I,
+                                               QQuarter<QT, D>& qq) {
+  using QQ = QQuarter<QT, D>;
+  const int j = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int jc = j < H_I ? j : H_I - 1;
+  const uint4* p = reinterpret_cast<const uint4*>(
+      static_cast<const uint8_t*>(q) +
+      ((row0 + jc) * D + static_cast<size_t>(w) * QQ::DW) * KeyBytes<QT>::value);
 #pragma unroll
-  for (int i = 0; i < D; ++i) dt = fmaf(qr[i], mean[i], dt);
-  return fmaxf(dt, 0.f);
+  for (int i = 0; i < QQ::NV; ++i) qq.x[i] = p[i];
+}
+
+// The partial block's terms ReLU(q[row0 + j] . mean) of heads j < H_I: the 4
+// wavefronts each take their quarter of d for every head (ascending fmaf), the
+// quarters are added in a fixed order by lane j after the barrier
+// (partial_block_term_sum).  Every thread calls it.
+template <int QT, int D>
+__device__ __forceinline__ void partial_block_terms(const QQuarter<QT, D>& qq, int H_I,
+                                                    const float (&mean)[D],
+                                                    float (&part)[4][64]) {
+  using QQ = QQuarter<QT, D>;
+  constexpr int EPV = 16 / KeyBytes<QT>::value;
+  const int j = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float acc = 0.f;
+  if (j < H_I) {
+#pragma unroll
+    for (int i = 0; i < QQ::NV; ++i) {
+      float qv[EPV];
+      unpack16<QT>(qq.x[i], qv);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc = fmaf(qv[e], mean[w * QQ::DW + i * EPV + e], acc);
+    }
+  }
+  part[w][j] = acc;
+  __syncthreads();
+}
+
+__device__ __forceinline__ float partial_block_term_sum(const float (&part)[4][64], int j) {
+  return fmaxf((part[0][j] + part[1][j]) + (part[2][j] + part[3][j]), 0.f);
 }
 
 // Wavefront 0 only (lane j = head j, r = its importance >= 0, any value for

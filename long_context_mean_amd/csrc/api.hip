@@ -269,7 +269,8 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* q_scale, const
   // many rows over one contiguous sequence: GEMM over the gathered head rows
   // (bf16, or e4m3 straight from the codes)
   const bool gemm = S == 1 && !block_table && lay.one_row && N >= kOneRowMinN &&
-                    ((q_dt == MISA_BF16 && k_dt == MISA_BF16) || (f8 && d == 128));
+                    ((q_dt == MISA_BF16 && k_dt == MISA_BF16) || (f8 && d == 128)) &&
+                    static_cast<size_t>(L) * d * (f8 ? 1 : 2) < (size_t{1} << 32);
   if (f8 && !gemm) {
     e = prep_fp8_queries(q, q_dt, w, q_scale, N, H_I, d, base + q8_off, st);
     if (e != hipSuccess) return hip_status(e);

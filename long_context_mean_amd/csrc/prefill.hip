@@ -35,6 +35,7 @@ namespace misa {
 namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kRowsPerWG = 256;       // gathered head rows per workgroup
@@ -58,6 +59,7 @@ struct PrefillParams {
   uint32_t* cnt_out;
   uint2* cand_out;
   int cap, splits;
+  uint32_t k_bytes;          // bytes of the key sequence (below 4 GiB)
 };
 
 template <int D, bool F8>
@@ -84,16 +86,74 @@ constexpr int kStages = 3;                             // LDS key tiles in fligh
 // (global_load_lds_dwordx4: each wavefront instruction fills 1 KB of the
 // tile, lane l the l-th 16 bytes).  s >= L (in the same units) reads row 0
 // instead (masked later).  Completion is tracked by vmcnt.
+//
+// A lane's source offsets from the tile's first key row are the same for
+// every tile, so they are formed once (DmaLane); a tile whose 64 keys are all
+// below L is read with buffer loads whose per-tile part is one scalar offset,
+// so it costs no per-lane address work.  The key sequence is below 4 GiB (the
+// launcher checks), so every offset fits the 32-bit buffer offsets.
+template <int D, bool F8>
+struct DmaLane {
+  // With 16 chunks per row, load j's rows are 16 j rows past load 0's and the
+  // swizzle (row & 15) is the same, so one lane offset serves every load and
+  // load j adds a scalar 16 j rows; otherwise each load keeps its own.
+  static constexpr bool ONE = PLayout<D, F8>::CH == 16;
+  static constexpr int NOFF = ONE ? 1 : PLayout<D, F8>::ROW_LOADS;
+  uint32_t off[NOFF];                        // byte offset of the lane's chunk
+  uint32_t soff;                             // fp8: byte offset of the lane's key scale
+  uint32_t k_bytes;                          // bytes of the key sequence
+  __device__ void init(uint32_t key_bytes, int key_step, int wave, int lane) {
+    using LY = PLayout<D, F8>;
+#pragma unroll
+    for (int j = 0; j < NOFF; ++j) {
+      const int f = (j * 4 + wave) * 64 + lane;
+      const int r = f / LY::CH;
+      off[j] = static_cast<uint32_t>(r * key_step * LY::ROW + 16 * ((f % LY::CH) ^ LY::swz(r)));
+    }
+    soff = static_cast<uint32_t>(lane * key_step * 4);
+    k_bytes = key_bytes;
+  }
+};
+
+// buffer_load_dword{,x4} ... lds: `bytes` per lane from rsrc at voff + soff
+// into LDS at lds + 4 or 16 * lane
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
+                                                uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)(lds), 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buffer_to_lds4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
+                                               uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)(lds), 4, voff, soff, 0, 0);
+}
+
 template <int D, bool F8>
 __device__ __forceinline__ void dma_key_tile(const uint8_t* k, const float* k_scale, int key0,
                                              int L, int key_step, uint8_t* tile, float* scales,
-                                             int wave, int lane) {
+                                             const DmaLane<D, F8>& dl, int wave, int lane) {
   using LY = PLayout<D, F8>;
+  // buffer resources over the keys and their scales (uniform; formed in
+  // scalar registers)
+  const __amdgpu_buffer_rsrc_t keys = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(k), 0,
+                                                      static_cast<int>(dl.k_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t kscl = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(k_scale), 0, static_cast<int>(dl.k_bytes / LY::ROW * 4u), 0x00020000);
+  if (key0 + kKeyTile <= L) {
+    const uint32_t row0 = static_cast<uint32_t>(key0) * static_cast<uint32_t>(key_step);
+    if constexpr (F8)
+      buffer_to_lds4(kscl, scales, dl.soff, row0 * 4u);
+#pragma unroll
+    for (int j = 0; j < LY::ROW_LOADS; ++j) {
+      using DL = DmaLane<D, F8>;
+      const uint32_t so = (row0 + (DL::ONE ? 16u * j * key_step : 0u)) * LY::ROW;
+      buffer_to_lds16(keys, tile + (j * 4 + wave) * 1024, dl.off[DL::ONE ? 0 : j], so);
+    }
+    return;
+  }
   if constexpr (F8) {
     // this wavefront's copy of the tile's 64 key scales (lane l -> key key0 + l)
     const int key = key0 + lane < L ? key0 + lane : 0;
-    __builtin_amdgcn_global_load_lds(k_scale + static_cast<size_t>(key) * key_step, scales, 4, 0,
-                                     0);
+    buffer_to_lds4(kscl, scales, static_cast<uint32_t>(key * key_step) * 4u, 0u);
   }
 #pragma unroll
   for (int j = 0; j < LY::ROW_LOADS; ++j) {
@@ -102,9 +162,9 @@ __device__ __forceinline__ void dma_key_tile(const uint8_t* k, const float* k_sc
     const int r = f / LY::CH;
     int key = key0 + r;
     key = key < L ? key : 0;
-    const uint8_t* src = k + static_cast<size_t>(key) * key_step * LY::ROW +
-                         16 * ((f % LY::CH) ^ LY::swz(r));
-    __builtin_amdgcn_global_load_lds(src, tile + blk * 1024, 16, 0, 0);
+    const uint32_t off = static_cast<uint32_t>(key * key_step) * LY::ROW +
+                         16u * ((f % LY::CH) ^ LY::swz(r));
+    buffer_to_lds16(keys, tile + blk * 1024, off, 0u);
   }
 }
 
@@ -156,11 +216,18 @@ struct OutState {
   static constexpr int NG = RowMap<HP>::NG;
   int pos[NG];             // key s is visible iff s <= pos (-1: no row)
   uint32_t* urow;          // plain mode: order-key row of group 0 (group q: + q * step)
-  uint2* crow;             // candidate mode: (key, token) list of group 0's row and split
-  size_t step;             // elements from one group's row to the next
+  size_t step;             // plain mode: elements from one group's row to the next
+  // candidate mode: the workgroup's (score, token) lists of this split as a
+  // buffer resource; a store at an offset past its end is dropped by the
+  // hardware, which is how lanes without a candidate skip theirs
+  __amdgpu_buffer_rsrc_t lists;
+  uint32_t lbase[NG];      // byte offset of group q's list in `lists`
+  uint32_t lt;             // lanes of the lane group below this one
   float tau[NG];           // candidate mode: threshold score
   uint32_t cnt[NG];        // candidate mode: scores >= tau so far (uniform over the lane group)
 };
+
+constexpr uint32_t kDropOffset = 0x80000000u;   // past every candidate resource's end
 
 // One LDS key tile (64 keys) against the wavefront's 4 row tiles.  MASK: some
 // (row, key) of the tile may be outside the causal prefix or the row block.
@@ -207,14 +274,19 @@ __device__ __forceinline__ void score_tile(const uint8_t* tile, const float* sca
     float v[RM::NG];
 #pragma unroll
     for (int q = 0; q < RM::NG; ++q) v[q] = 0.f;
+    // the 4 row tiles' chains interleaved (consecutive MFMAs independent)
+    f32x4_t acc[4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) acc = mfma_step<F8>(a[rt][kk], b[kk], acc);
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[rt / RM::TQ] = fmaf(wv[rt][i], relu(acc[i]), v[rt / RM::TQ]);
-    }
+      for (int rt = 0; rt < 4; ++rt) acc[rt] = mfma_step<F8>(a[rt][kk], b[kk], acc[rt]);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        v[rt / RM::TQ] = fmaf(wv[rt][i], relu(acc[rt][i]), v[rt / RM::TQ]);
     const int key = key0 + ct * 16 + c;
     float ks = 1.f;
     if constexpr (F8) ks = scales[ct * 16 + c];
@@ -237,9 +309,11 @@ __device__ __forceinline__ void score_tile(const uint8_t* tile, const float* sca
         const uint64_t m = __ballot(pass);
         // slots in key order within the lane group (16 keys of one query row)
         const uint32_t grp = static_cast<uint32_t>(m >> (16 * g)) & 0xFFFFu;
-        const uint32_t slot = o.cnt[q] + __popc(grp & ((1u << c) - 1u));
-        if (pass && slot < static_cast<uint32_t>(cap))
-          o.crow[q * o.step + slot] = make_uint2(__float_as_uint(x), static_cast<uint32_t>(key));
+        const uint32_t slot = o.cnt[q] + __popc(grp & o.lt);
+        const uint32_t off =
+            pass && slot < static_cast<uint32_t>(cap) ? o.lbase[q] + slot * 8u : kDropOffset;
+        const u32x2_t e = {__float_as_uint(x), static_cast<uint32_t>(key)};
+        __builtin_amdgcn_raw_buffer_store_b64(e, o.lists, off, 0, 0);
         o.cnt[q] += __popc(grp);
       }
     }
@@ -257,7 +331,8 @@ __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(Pre
   __shared__ int pos_lds[QB];
 
   if (p.block_flag && p.block_flag[blockIdx.y] == 0u) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int qrow0 = blockIdx.y * QB;
   for (int i = tid; i < QB; i += 256) {
@@ -319,11 +394,20 @@ __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(Pre
   OutState<HP, CAND> o;
   // group q's row is group 0's row + q * rstep (rows past N are never written)
   constexpr int rstep = RM::IN_LANE ? 4 : 1;
-  const size_t t0 = static_cast<size_t>(qrow0 + RM::out_row(wave, 0, g));
   if constexpr (CAND) {
-    o.crow = p.cand_out + (t0 * p.splits + blockIdx.x) * p.cap;
-    o.step = static_cast<size_t>(rstep) * p.splits * p.cap;
+    // lists of rows qrow0 .. qrow0 + nrow - 1 for this split: row r's list
+    // starts r * splits * cap entries after row 0's
+    const int nrow = min(QB, p.N - qrow0);
+    const uint32_t row_bytes = static_cast<uint32_t>(p.splits) * p.cap * 8u;
+    o.lists = __builtin_amdgcn_make_buffer_rsrc(
+        p.cand_out + (static_cast<size_t>(qrow0) * p.splits + blockIdx.x) * p.cap, 0,
+        static_cast<int>((nrow - 1) * row_bytes + static_cast<uint32_t>(p.cap) * 8u), 0x00020000);
+#pragma unroll
+    for (int q = 0; q < RM::NG; ++q)
+      o.lbase[q] = static_cast<uint32_t>(RM::out_row(wave, q, g)) * row_bytes;
+    o.lt = (1u << c) - 1u;
   } else {
+    const size_t t0 = static_cast<size_t>(qrow0 + RM::out_row(wave, 0, g));
     o.urow = p.u + t0 * p.u_stride;
     o.step = static_cast<size_t>(rstep) * p.u_stride;
   }
@@ -347,11 +431,13 @@ __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(Pre
   constexpr int S = kStages;
   constexpr int AHEAD = (S - 2) * LY::PER_THREAD;      // loads still in flight after a wait
   const int ntiles = (ks1 - ks0 + kKeyTile - 1) / kKeyTile;
+  DmaLane<D, F8> dl;
+  dl.init(p.k_bytes, p.key_step, wave, lane);
 #pragma unroll
   for (int j = 0; j < S - 1; ++j)
     if (j < ntiles)
       dma_key_tile<D, F8>(p.k, p.k_scale, ks0 + j * kKeyTile, p.L, p.key_step, tiles[j],
-                          kscales[j][F8 ? wave : 0], wave, lane);
+                          kscales[j][F8 ? wave : 0], dl, wave, lane);
   if (ntiles >= S - 1)
     wait_vm_barrier<AHEAD>();
   else
@@ -369,7 +455,7 @@ __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(Pre
     const int nb = buf == 0 ? S - 1 : buf - 1;          // the buffer tile i-1 was read from
     if (i + S - 1 < ntiles) {
       dma_key_tile<D, F8>(p.k, p.k_scale, key0 + (S - 1) * kKeyTile, p.L, p.key_step, tiles[nb],
-                          kscales[nb][F8 ? wave : 0], wave, lane);
+                          kscales[nb][F8 ? wave : 0], dl, wave, lane);
       wait_vm_barrier<AHEAD>();                         // tile i+1 has landed
     } else {
       wait_vm_barrier<0>();
@@ -458,6 +544,9 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   p.cnt_out = a.cnt_out;
   p.cand_out = a.cand_out;
   p.cap = a.cap;
+  const size_t k_bytes = static_cast<size_t>(a.L) * PLayout<D, F8>::ROW;
+  if (k_bytes >= (size_t{1} << 32)) return hipErrorInvalidValue;
+  p.k_bytes = static_cast<uint32_t>(k_bytes);
   constexpr int QB = kRowsPerWG / HP;
   const int qblocks = (a.N + QB - 1) / QB;
   const int splits = a.cand_out ? splits_t<HP, D, F8, true>(a.N, p.L)

@@ -112,8 +112,8 @@ def _counter_per_dispatch(db, counter, name_part):
 
 # source files whose text defines each measured kernel
 KERNEL_SOURCES = {
-    "score_mfma_kernel": ["score.hip"],
-    "pool_kernel": ["pool.hip"],
+    "score_mfma_kernel": ["score.hip", "route_select.hpp", "partial_block.hpp"],
+    "pool_kernel": ["pool.hip", "pool_block.hpp"],
     "score_prefill_kernel": ["prefill.hip"],
 }
 
@@ -235,10 +235,12 @@ class Replicas:
 class Serving:
     """The decode serving step on a key cache (contiguous, or paged with
     page_size tokens per page): the newest token of every sequence completes
-    its last block, so the step pools that one block into the cached table
-    (misa_pool_update), then routes and scores in one call
-    (misa_route_score_topk: the head selection runs in the scoring kernel);
-    step_two_calls does the same with misa_route_heads + misa_score_topk.
+    its last block, so the step pools that one block into the cached table,
+    routes and scores in one call (misa_pool_route_score_topk: the pooling
+    runs in the router's launch, the head selection in the scoring kernel);
+    step_pool_then_fused makes the pooling a call of its own
+    (misa_pool_update + misa_route_score_topk), step_two_calls also splits
+    the routing from the scoring (misa_route_heads + misa_score_topk).
     REPLICAS copies of the keys rotate like Replicas."""
 
     def __init__(self, p, torch, binding, h, page_size=0):
@@ -263,6 +265,12 @@ class Serving:
                                           p.H_I, p.B, topk=p.topk, device=dev)
 
     def step(self, i):
+        dp = self.dps[i]
+        dp.pool_route_score_topk(self.kbar[i], self.len_old, self.len_new, 1, self.h,
+                                 heads=self.heads, head_score=self.r, idx=self.idx, score=None,
+                                 ws=self.ws_fused, want_score=False)
+
+    def step_pool_then_fused(self, i):
         dp = self.dps[i]
         dp.pool_update(self.len_old, self.len_new, 1, self.kbar[i])
         dp.route_score_topk(self.kbar[i], self.h, heads=self.heads, head_score=self.r,
@@ -593,6 +601,8 @@ def main():
                                  16)
         extra["serving_step_two_calls_ms"] = round(ms_2, 4)
         extra["serving_step_two_calls_kernel_ms"] = {k: round(v, 5) for k, v in kt2.items()}
+        extra["serving_step_pool_then_fused_ms"] = round(
+            timed(torch, srv.step_pool_then_fused, args.steps, args.warmup), 4)
         ms_f = timed(torch, rep.step_misa, args.steps, args.warmup)
         _, ktf, _ = kernel_times(torch, binding, rep.step_misa, max(3, args.steps // 2), 1, 16)
         ms_d = timed(torch, rep.step_dense, args.steps, args.warmup)
@@ -700,8 +710,8 @@ def main():
                    "N": p.N, "L": p.L, "H_I": p.H_I, "h": h, "d": p.d, "B": p.B,
                    "topk": p.topk,
                    "step": "incremental block pooling (the appended token completes each "
-                           "sequence's last block) + route + routed score/top-k "
-                           "(misa_route_score_topk)",
+                           "sequence's last block) + route + routed score/top-k in one "
+                           "call (misa_pool_route_score_topk)",
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -187,6 +187,31 @@ int32_t misa_route_score_topk(const void* q, int32_t q_dt, const float* q_scale,
                               float* score, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * One decode serving step (the same page, "Methodology" items 1 and 2): the
+ * incremental pooling of misa_pool_update (kbar [S, ceil(L/B), d], read and
+ * written: the blocks completed by tokens len_old[s] .. len_new[s] - 1),
+ * then misa_route_score_topk on the updated table, with the same results bit
+ * for bit, the written kbar entries included.  For the decode rows that
+ * misa_route_score_topk fuses (bf16 queries, bf16 or e4m3 keys, not one
+ * sequence with N >= 128) the pooling runs inside the router's launch: the
+ * router's workgroups that need a block completed by this call pool it
+ * themselves with the pooling kernel's arithmetic, and further workgroups of
+ * the same launch write the table, so the step has no separate pooling
+ * launch; otherwise the calls run in turn.  Arguments, layouts, errors and
+ * the workspace (misa_workspace_bytes(MISA_OP_ROUTE_SCORE_TOPK, ...)) are
+ * those of the two calls; nothing runs if any check of either fails.
+ */
+int32_t misa_pool_route_score_topk(const void* q, int32_t q_dt, const float* q_scale,
+                                   const float* w, float* kbar, const void* k,
+                                   const float* k_scale, int32_t k_dt, const int32_t* block_table,
+                                   int32_t page_size, const int32_t* q_seq, const int32_t* q_pos,
+                                   const int32_t* len_old, const int32_t* len_new, int32_t max_new,
+                                   int32_t N, int32_t S, int32_t L, int32_t d, int32_t B,
+                                   int32_t H_I, int32_t h, int32_t topk, int32_t* heads,
+                                   float* head_score, int32_t* idx, float* score, void* ws,
+                                   size_t ws_bytes, void* stream);
+
+/*
  * Dense DSA indexer (the baseline MISA replaces: every one of the H_I heads
  * scores every prefix token, MISA abstract and "Problem statement"):
  * misa_score_topk with all H_I heads.

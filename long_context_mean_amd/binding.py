@@ -27,7 +27,7 @@ MISA_OP_ROUTE_SCORE_TOPK = 5
 MISA_OK = 0
 
 EXPORTED = ("misa_pool_keys", "misa_pool_update", "misa_route_heads", "misa_score_topk",
-            "misa_route_score_topk", "dsa_score_topk",
+            "misa_route_score_topk", "misa_pool_route_score_topk", "dsa_score_topk",
             "misa_rerank", "misa_score_topk_blocks", "misa_sparse_attention",
             "misa_workspace_bytes", "misa_status_string",
             "misa_last_hip_error", "misa_profile_begin", "misa_profile_end", "misa_kernel_name")
@@ -68,6 +68,9 @@ def lib():
     L.misa_score_topk.argtypes = [P, I32, P, P] + KEYS + [P, P, P] + [I32] * 7 + [P, P, P, SZ, P]
     L.misa_route_score_topk.argtypes = ([P, I32, P, P, P] + KEYS + [P, P] + [I32] * 8 +
                                         [P, P, P, P, P, SZ, P])
+    # ... kbar <keys> q_seq q_pos len_old len_new max_new N S L d B H_I h topk ...
+    L.misa_pool_route_score_topk.argtypes = ([P, I32, P, P, P] + KEYS + [P, P, P, P] +
+                                             [I32] * 9 + [P, P, P, P, P, SZ, P])
     L.dsa_score_topk.argtypes = [P, I32, P, P] + KEYS + [P, P] + [I32] * 6 + [P, P, P, SZ, P]
     L.misa_rerank.argtypes = [P, I32, P, P] + KEYS + [P, P, P] + [I32] * 7 + [P, P, P, SZ, P]
     L.misa_score_topk_blocks.argtypes = [P, I32, P, P, P] + KEYS + [P, P, P] + [I32] * 9 + \
@@ -83,7 +86,7 @@ def lib():
     L.misa_profile_end.argtypes = [P, P, I32]
     L.misa_kernel_name.argtypes = [I32]
     L.misa_kernel_name.restype = ctypes.c_char_p
-    for f in ("misa_score_topk_blocks", "misa_sparse_attention", "misa_pool_keys", "misa_pool_update", "misa_route_heads", "misa_score_topk", "misa_route_score_topk", "dsa_score_topk",
+    for f in ("misa_score_topk_blocks", "misa_sparse_attention", "misa_pool_keys", "misa_pool_update", "misa_route_heads", "misa_score_topk", "misa_route_score_topk", "misa_pool_route_score_topk", "dsa_score_topk",
               "misa_rerank", "misa_last_hip_error", "misa_profile_begin", "misa_profile_end"):
         getattr(L, f).restype = ctypes.c_int32
     _lib = L
@@ -260,6 +263,36 @@ def misa_route_score_topk(q, w, kbar, k, q_seq, q_pos, B: int, h: int, topk: int
         _ptr(idx, "idx", _I32, (N, topk)), _ptr(score, "score", _F32, (N, topk)),
         _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(q)))
     return heads, head_score, idx, score
+
+
+def misa_pool_route_score_topk(q, w, kbar, k, q_seq, q_pos, len_old, len_new, max_new: int,
+                               B: int, h: int, topk: int, k_scale=None, heads=None,
+                               head_score=None, idx=None, score=None, ws=None, want_scores=True,
+                               want_score=True, q_scale=None, block_table=None, page_size=0,
+                               L=None):
+    N, H_I, d = q.shape
+    S, L, _, kargs = _keys(k, k_scale, block_table, page_size, L, d_q=d)
+    if heads is None:
+        heads = torch.empty((N, h), dtype=torch.int32, device=q.device)
+    if head_score is None and want_scores:
+        head_score = torch.empty((N, H_I), dtype=torch.float32, device=q.device)
+    if idx is None:
+        idx = torch.empty((N, topk), dtype=torch.int32, device=q.device)
+    if score is None and want_score:
+        score = torch.empty((N, topk), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(MISA_OP_ROUTE_SCORE_TOPK, N, L, d, H_I, B, topk=topk,
+                       q_dt=_dtype_code(q), device=q.device)
+    _check("misa_pool_route_score_topk", lib().misa_pool_route_score_topk(
+        _ptr(q, "q", _KEYS), _dtype_code(q), _ptr(q_scale, "q_scale", _F32, (N, H_I)),
+        _ptr(w, "w", _F32, (N, H_I)), _ptr(kbar, "kbar", _F32, (S, -(-L // B), d)), *kargs,
+        _ptr(q_seq, "q_seq", _I32, (N,)), _ptr(q_pos, "q_pos", _I32, (N,)),
+        _ptr(len_old, "len_old", _I32, (S,)), _ptr(len_new, "len_new", _I32, (S,)), max_new,
+        N, S, L, d, B, H_I, h, topk, _ptr(heads, "heads", _I32, (N, h)),
+        _ptr(head_score, "head_score", _F32, (N, H_I)), _ptr(idx, "idx", _I32, (N, topk)),
+        _ptr(score, "score", _F32, (N, topk)), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+        _stream(q)))
+    return kbar, heads, head_score, idx, score
 
 
 def dsa_score_topk(q, w, k, q_seq, q_pos, topk: int, k_scale=None, idx=None, score=None,
@@ -455,6 +488,13 @@ class DeviceProblem:
                                      self.p.B, self.p.h if h is None else h,
                                      self.p.topk if topk is None else topk,
                                      q_scale=self.q_scale, **self.kv, **kw)
+
+    def pool_route_score_topk(self, kbar, len_old, len_new, max_new, h=None, topk=None, **kw):
+        return misa_pool_route_score_topk(self.q, self.w, kbar, self.k, self.q_seq, self.q_pos,
+                                          len_old, len_new, max_new, self.p.B,
+                                          self.p.h if h is None else h,
+                                          self.p.topk if topk is None else topk,
+                                          q_scale=self.q_scale, **self.kv, **kw)
 
     def score_topk_blocks(self, kbar, heads, m_blocks, topk=None, **kw):
         return misa_score_topk_blocks(self.q, self.w, kbar, self.k, self.q_seq, self.q_pos, heads,

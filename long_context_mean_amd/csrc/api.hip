@@ -540,6 +540,63 @@ int32_t misa_route_score_topk(const void* q, int32_t q_dt, const float* q_scale,
                          stream, &fr);
 }
 
+int32_t misa_pool_route_score_topk(const void* q, int32_t q_dt, const float* q_scale,
+                                   const float* w, float* kbar, const void* k,
+                                   const float* k_scale, int32_t k_dt, const int32_t* block_table,
+                                   int32_t page_size, const int32_t* q_seq, const int32_t* q_pos,
+                                   const int32_t* len_old, const int32_t* len_new, int32_t max_new,
+                                   int32_t N, int32_t S, int32_t L, int32_t d, int32_t B,
+                                   int32_t H_I, int32_t h, int32_t topk, int32_t* heads,
+                                   float* head_score, int32_t* idx, float* score, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  // the checks of both calls, before anything runs
+  int32_t rc = check_pool(k, k_scale, k_dt, S, L, d, B, kbar);
+  if (rc) return rc;
+  if (!len_old || !len_new) return MISA_ERR_NULL;
+  if (max_new < 0 || max_new > L) return MISA_ERR_SHAPE;
+  if (!q || !w || !q_seq || !q_pos || !heads || !idx) return MISA_ERR_NULL;
+  if ((rc = check_dtypes(q_dt, k_dt, q_scale, k_scale))) return rc;
+  if ((rc = check_sizes(N, S, L, d, H_I))) return rc;
+  misa::KeyIndex ki;
+  if ((rc = key_index(block_table, page_size, L, ki))) return rc;
+  if (h < 1 || h > H_I || topk < 1 || topk > kMaxTopk) return MISA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k)) return MISA_ERR_SHAPE;
+  const size_t rb = route_score_route_bytes(q_dt, N, L, d, B, H_I);
+  const size_t sb = score_topk_bytes(N, L, topk) +
+                    (q_dt == MISA_FP8_E4M3 ? q8_bytes(N, H_I, d) : 0);
+  if (!ws) return MISA_ERR_NULL;
+  if (ws_bytes < rb + sb) return MISA_ERR_WORKSPACE;
+  const bool fused = q_dt == MISA_BF16 && k_dt != MISA_F32 && !(S == 1 && N >= kOneRowMinN);
+  if (!fused || max_new == 0) {
+    rc = misa_pool_update(k, k_scale, k_dt, block_table, page_size, S, L, d, B, len_old, len_new,
+                          max_new, kbar, stream);
+    if (rc) return rc;
+    return misa_route_score_topk(q, q_dt, q_scale, w, kbar, k, k_scale, k_dt, block_table,
+                                 page_size, q_seq, q_pos, N, S, L, d, B, H_I, h, topk, heads,
+                                 head_score, idx, score, ws, ws_bytes, stream);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  const TopkLayout lay = topk_layout(N, L);
+  uint32_t* hist = lay.one_row ? nullptr : reinterpret_cast<uint32_t*>(wsb + rb + lay.off_hist);
+  const int nchunks = route_chunks(L, B);
+  float* partial = reinterpret_cast<float*>(wsb);
+  misa::RouteArgs a{q, q_dt, nullptr, w, kbar, k, k_scale, k_dt, q_seq, q_pos, N, S, L, d, B,
+                    H_I, h, heads, head_score, partial, nchunks, nullptr, ki};
+  a.partials_only = true;
+  a.hist0 = hist;
+  a.len_old = len_old;
+  a.len_new = len_new;
+  a.max_new = max_new;
+  a.kbar_out = kbar;
+  const hipError_t e = misa::launch_route(a, st);
+  if (e != hipSuccess) return hip_status(e);
+  const FusedRoute fr{partial, nchunks, B, heads, head_score};
+  return score_topk_impl(q, q_dt, q_scale, w, k, k_scale, k_dt, block_table, page_size, q_seq,
+                         q_pos, nullptr, N, S, L, d, H_I, h, topk, idx, score, wsb + rb, sb,
+                         stream, &fr);
+}
+
 int32_t misa_rerank(const void* q, int32_t q_dt, const float* q_scale, const float* w,
                     const void* k, const float* k_scale, int32_t k_dt, const int32_t* block_table,
                     int32_t page_size, const int32_t* q_seq, const int32_t* q_pos,

@@ -91,6 +91,13 @@ struct RouteArgs {
   // histogram [N, kHistWords], is cleared on the way.
   bool partials_only = false;
   uint32_t* hist0 = nullptr;
+  // with partials_only: also pool the blocks completed by tokens
+  // len_old[s] .. len_new[s] - 1 into kbar_out (= kbar), max_new bounding
+  // len_new - len_old; the chunks pool such blocks for themselves
+  const int32_t* len_old = nullptr;
+  const int32_t* len_new = nullptr;
+  int max_new = 0;
+  float* kbar_out = nullptr;
 };
 int route_blocks_per_chunk();
 bool route_uses_mfma(const RouteArgs& a);

@@ -17,6 +17,7 @@
 // Keys may live in a paged cache (KeyIndex).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "pool_block.hpp"
 
 namespace misa {
 namespace {
@@ -27,12 +28,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint8_t* __restrict__ k
                                                    int B, float* __restrict__ kbar, KeyIndex ki,
                                                    const int32_t* __restrict__ len_old,
                                                    const int32_t* __restrict__ len_new) {
-  constexpr int EB = KeyBytes<KT>::value;
-  constexpr int ROW_BYTES = D * EB;
-  constexpr int CPR = ROW_BYTES / 16;          // 16-byte pieces per row
-  constexpr int EPC = 16 / EB;                 // elements per piece
-  constexpr int RG = 256 / CPR;                // row groups
-  __shared__ float part[RG][D + 1];
+  __shared__ float part[PoolMap<KT, D>::RG][D + 1];
 
   const int s = blockIdx.y, M = (L + B - 1) / B;
   int b = blockIdx.x, t1;
@@ -44,50 +40,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint8_t* __restrict__ k
   } else {
     t1 = (b * B + B < L) ? b * B + B : L;
   }
-  const int t0 = b * B;
-  const int c = threadIdx.x % CPR, g = threadIdx.x / CPR;
-
-  float acc[EPC];
-#pragma unroll
-  for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
-
-  constexpr int U = 8;
-  for (int t = t0 + g; t < t1; t += U * RG) {
-    uint4 x[U];
-    float sc[U];
-#pragma unroll
-    for (int r = 0; r < U; ++r) {
-      const int tt = t + r * RG;
-      const int tc = tt < t1 ? tt : t;           // stay in bounds; masked below
-      const size_t row = ki.row(s, tc);
-      x[r] = *reinterpret_cast<const uint4*>(k + row * ROW_BYTES + c * 16);
-      sc[r] = 1.f;
-      if constexpr (KT == DT_E4M3) sc[r] = k_scale[row];
-    }
-#pragma unroll
-    for (int r = 0; r < U; ++r) {
-      if (t + r * RG < t1) {
-        float v[EPC];
-        unpack16<KT>(x[r], v);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          if constexpr (KT == DT_E4M3)
-            acc[e] += v[e] * sc[r];
-          else
-            acc[e] += v[e];
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < EPC; ++e) part[g][c * EPC + e] = acc[e];
-  __syncthreads();
-  if (threadIdx.x < D) {
-    float sum = 0.f;
-#pragma unroll 8
-    for (int r = 0; r < RG; ++r) sum += part[r][threadIdx.x];
-    kbar[(static_cast<size_t>(s) * M + b) * D + threadIdx.x] = sum / static_cast<float>(t1 - t0);
-  }
+  const float m = pool_block_mean<KT, D>(k, k_scale, ki, s, b * B, t1, part);
+  if (threadIdx.x < D) kbar[(static_cast<size_t>(s) * M + b) * D + threadIdx.x] = m;
 }
 
 template <int KT, int D>

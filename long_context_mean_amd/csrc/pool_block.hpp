@@ -1,0 +1,80 @@
+// The mean of one block of index keys, shared by the pooling kernel and by
+// the decode router, which pools the blocks a call completes itself so it
+// needs no separate pooling launch before it (MISA technical summary,
+// gist.science, "Methodology" item 1: blocks summarised by mean-pooled index
+// keys).  Both use this one function, so the table entries they produce are
+// the same bits.
+#pragma once
+
+#include "common.hpp"
+
+namespace misa {
+
+template <int KT, int D>
+struct PoolMap {
+  static constexpr int EB = KeyBytes<KT>::value;
+  static constexpr int ROW_BYTES = D * EB;
+  static constexpr int CPR = ROW_BYTES / 16;   // 16-byte pieces per row
+  static constexpr int EPC = 16 / EB;          // elements per piece
+  static constexpr int RG = 256 / CPR;         // row groups
+};
+
+// Mean of key rows [t0, t1) of sequence s with 256 threads: thread
+// (g, c) = (tid / CPR, tid % CPR) sums rows t0 + g, t0 + g + RG, ... of its
+// 16-byte piece c (e4m3 codes times the row's scale), the row groups are
+// added in order through `part`, and thread i < D returns the mean of
+// element i (other threads return 0).  Every thread calls it; it ends with
+// the threads < D still reading `part`, so a caller reusing `part`
+// synchronises first.
+template <int KT, int D>
+__device__ __forceinline__ float pool_block_mean(const uint8_t* __restrict__ k,
+                                                 const float* __restrict__ k_scale,
+                                                 const KeyIndex& ki, int s, int t0, int t1,
+                                                 float (&part)[PoolMap<KT, D>::RG][D + 1]) {
+  using PM = PoolMap<KT, D>;
+  const int c = threadIdx.x % PM::CPR, g = threadIdx.x / PM::CPR;
+  float acc[PM::EPC];
+#pragma unroll
+  for (int e = 0; e < PM::EPC; ++e) acc[e] = 0.f;
+
+  constexpr int U = 8;
+  for (int t = t0 + g; t < t1; t += U * PM::RG) {
+    uint4 x[U];
+    float sc[U];
+#pragma unroll
+    for (int r = 0; r < U; ++r) {
+      const int tt = t + r * PM::RG;
+      const int tc = tt < t1 ? tt : t;           // stay in bounds; masked below
+      const size_t row = ki.row(s, tc);
+      x[r] = *reinterpret_cast<const uint4*>(k + row * PM::ROW_BYTES + c * 16);
+      sc[r] = 1.f;
+      if constexpr (KT == DT_E4M3) sc[r] = k_scale[row];
+    }
+#pragma unroll
+    for (int r = 0; r < U; ++r) {
+      if (t + r * PM::RG < t1) {
+        float v[PM::EPC];
+        unpack16<KT>(x[r], v);
+#pragma unroll
+        for (int e = 0; e < PM::EPC; ++e) {
+          if constexpr (KT == DT_E4M3)
+            acc[e] += v[e] * sc[r];
+          else
+            acc[e] += v[e];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < PM::EPC; ++e) part[g][c * PM::EPC + e] = acc[e];
+  __syncthreads();
+  float sum = 0.f;
+  if (threadIdx.x < D) {
+#pragma unroll 8
+    for (int r = 0; r < PM::RG; ++r) sum += part[r][threadIdx.x];
+    sum /= static_cast<float>(t1 - t0);
+  }
+  return sum;
+}
+
+}  // namespace misa

@@ -20,6 +20,7 @@
 //    ascending order.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "pool_block.hpp"
 #include "route_select.hpp"
 
 namespace misa {
@@ -103,11 +104,22 @@ __global__ __launch_bounds__(256) void route_partial_kernel(
 // incomplete block) to chunk slot nchunks (0 when the row ends on a block
 // boundary), and chunk 0 of each row clears that row's level-0 histogram for
 // the scoring kernel.
+//
+// With the incremental pooling folded in (pool_new, the blocks completed by
+// the tokens len_old[s] .. len_new[s] - 1), workgroups nchunks + 1 .. of row 0
+// pool those blocks into the table, as the pooling kernel does, and a chunk
+// holding such a block pools it for itself from the keys with the same
+// function instead of reading the table: no workgroup reads an entry this
+// launch writes, and the routes equal those after a separate pooling call.
 struct RoutePartialExtra {
   const void* k;
   const float* k_scale;
   KeyIndex ki;
   uint32_t* hist0;         // [N, kHistWords] cleared by chunk 0 (NULL: no extra work)
+  const int32_t* len_old = nullptr;   // [S] (NULL: no pooling)
+  const int32_t* len_new = nullptr;   // [S]
+  float* kbar_out = nullptr;          // the table (the kbar the chunks read)
+  int npool = 0;                      // pooling workgroups per sequence
 };
 
 template <int KT, int D>
@@ -122,7 +134,26 @@ __global__ __launch_bounds__(256) void route_partial_mfma_kernel(
   __shared__ __align__(16) uint8_t lo_t[kRouteBlocks * STRIDE];
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+  // key-row sums of the pooling paths (one array for all of them)
+  static_assert(PoolMap<KT, D>::RG == PM::RG, "pooling and partial-block maps agree");
+  __shared__ float kpart[PM::RG][D + 1];
+
   const int n = blockIdx.y, chunk = blockIdx.x;
+  const int M = (L + B - 1) / B;
+  if (chunk > nchunks) {
+    // pooling workgroup: block (pb % npool)-th at or after the one holding
+    // token len_old[s] of sequence s = pb / npool, if this call completes it
+    if (n != 0) return;
+    const int pb = chunk - (nchunks + 1);
+    const int s = pb / x.npool;
+    const int b = pb % x.npool + x.len_old[s] / B;
+    const int t1 = (b + 1) * B;
+    if (t1 > x.len_new[s] || t1 <= x.len_old[s]) return;
+    const float m = pool_block_mean<KT, D>(static_cast<const uint8_t*>(x.k), x.k_scale, x.ki, s,
+                                           b * B, t1, kpart);
+    if (threadIdx.x < D) x.kbar_out[(static_cast<size_t>(s) * M + b) * D + threadIdx.x] = m;
+    return;
+  }
   if (x.hist0 && chunk == 0) {
     uint32_t* h = x.hist0 + static_cast<size_t>(n) * kHistWords;
     for (int i = threadIdx.x; i < kHistWords; i += 256) h[i] = 0u;
@@ -130,7 +161,6 @@ __global__ __launch_bounds__(256) void route_partial_mfma_kernel(
   float* out = partial + (static_cast<size_t>(n) * pstride + chunk) * H_I;
   if (chunk == nchunks) {
     // the partial block's term, exactly as the router's selection step forms it
-    __shared__ float psum[PM::RG][D + 1];
     __shared__ float mean[D];
     __shared__ float part[4][64];
     QQuarter<DT_BF16, D> qq;
@@ -139,7 +169,7 @@ __global__ __launch_bounds__(256) void route_partial_mfma_kernel(
     const int Mf = Ln / B;
     const int cp = Ln - Mf * B;
     if (cp > 0) {
-      partial_block_mean<KT, D>(x.k, x.k_scale, x.ki, q_seq[n], Mf * B, Ln, psum, mean);
+      partial_block_mean<KT, D>(x.k, x.k_scale, x.ki, q_seq[n], Mf * B, Ln, kpart, mean);
       partial_block_terms<DT_BF16, D>(qq, H_I, mean, part);
     }
     if (threadIdx.x < H_I)
@@ -147,7 +177,6 @@ __global__ __launch_bounds__(256) void route_partial_mfma_kernel(
     return;
   }
   const int Mf = (q_pos[n] + 1) / B;                   // blocks fully visible to row n
-  const int M = (L + B - 1) / B;
   const int b0 = chunk * kRouteBlocks;
   const int nb = min(kRouteBlocks, Mf - b0);
   if (nb <= 0) {
@@ -168,13 +197,42 @@ __global__ __launch_bounds__(256) void route_partial_mfma_kernel(
       a[kk] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
-  // the chunk's pooled keys, split into hi / lo bf16 rows
+  // blocks [nlo, nhi) of this chunk are completed by this call: pooled here
+  // (after the loads of the query and of the table's blocks are issued, so
+  // their round trips overlap the key reads)
+  int nlo = 0, nhi = 0;
+  if (x.len_new) {
+    const int s = q_seq[n];
+    nlo = max(b0, x.len_old[s] / B);
+    nhi = min(b0 + nb, x.len_new[s] / B);
+  }
+  constexpr int PER = kRouteBlocks * D / 4 / 256;      // table float4s per thread
   const float* src = kbar + (static_cast<size_t>(q_seq[n]) * M + b0) * D;
-  for (int f = tid; f < kRouteBlocks * D / 4; f += 256) {
+  float4 kx[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int f = tid + 256 * i;
     const int blk = f / (D / 4), col = (f % (D / 4)) * 4;
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (blk < nb) x = *reinterpret_cast<const float4*>(src + static_cast<size_t>(blk) * D + col);
-    const float xs[4] = {x.x, x.y, x.z, x.w};
+    kx[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (blk < nb && !(b0 + blk >= nlo && b0 + blk < nhi))
+      kx[i] = *reinterpret_cast<const float4*>(src + static_cast<size_t>(blk) * D + col);
+  }
+  __shared__ __align__(16) float fresh[kRouteBlocks][D];
+  for (int b = nlo; b < nhi; ++b) {
+    const float m = pool_block_mean<KT, D>(static_cast<const uint8_t*>(x.k), x.k_scale, x.ki,
+                                           q_seq[n], b * B, (b + 1) * B, kpart);
+    if (tid < D) fresh[b - b0][tid] = m;
+    __syncthreads();
+  }
+  // the chunk's pooled keys, split into hi / lo bf16 rows
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int f = tid + 256 * i;
+    const int blk = f / (D / 4), col = (f % (D / 4)) * 4;
+    const float4 xv = (b0 + blk >= nlo && b0 + blk < nhi)
+                          ? *reinterpret_cast<const float4*>(&fresh[blk][col])
+                          : kx[i];
+    const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
     uint32_t hb[4], lb[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -447,9 +505,17 @@ hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
       // the routed decode step: partials plus the partial-block slot, heads
       // picked by the scoring kernel
       const bool fused = a.partials_only;
-      const RoutePartialExtra x{a.k, a.k_scale, a.kidx, a.hist0};
-      MISA_LAUNCH(K_ROUTE_PARTIAL, (route_partial_mfma_kernel<KT, D>),
-                  dim3(a.nchunks + (fused ? 1 : 0), a.N), dim3(256), 0, st,
+      RoutePartialExtra x{a.k, a.k_scale, a.kidx, a.hist0};
+      int gx = a.nchunks + (fused ? 1 : 0);
+      if (fused && a.len_new && a.max_new > 0) {
+        x.len_old = a.len_old;
+        x.len_new = a.len_new;
+        x.kbar_out = a.kbar_out;
+        x.npool = a.max_new / a.B + 1;     // blocks max_new tokens can complete
+        gx += x.npool * a.S;
+      }
+      MISA_LAUNCH(K_ROUTE_PARTIAL, (route_partial_mfma_kernel<KT, D>), dim3(gx, a.N), dim3(256),
+                  0, st,
                   static_cast<const uint16_t*>(a.q), a.kbar, a.q_seq, a.q_pos, a.L, a.B, a.H_I,
                   a.nchunks, a.nchunks + (fused ? 1 : 0), a.partial, x);
       if (fused) return hipGetLastError();

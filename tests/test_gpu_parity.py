@@ -868,6 +868,55 @@ def test_route_score_topk_equals_two_calls(case, k_dt, q_dt, page_size):
     assert np.array_equal(np_(sc).view(np.uint32), np_(sc2).view(np.uint32))
 
 
+# misa_pool_route_score_topk: the same bits as misa_pool_update followed by
+# misa_route_score_topk, the pooled table included.  The table's entries for
+# the blocks the call completes start stale (a constant), so a router
+# workgroup that read one instead of pooling it would change the routes.
+@pytest.mark.parametrize("case", [
+    dict(N=4, S=4, L=9000, d=128, H_I=64, h=8, B=128, topk=2048,
+         len_new=[8960, 8192, 128, 5001], new=[1, 1, 1, 1], max_new=1),    # one block each, one partial
+    dict(N=3, S=3, L=5000, d=64, H_I=32, h=8, B=64, topk=300, q_seq=[0, 0, 1],
+         len_new=[1300, 2000, 900], new=[300, 0, 600], max_new=600,          # several blocks; a row
+         q_pos=[1299, 1100, 1999]),                                        # behind; a sequence with no row
+    dict(N=2, S=2, L=4097, d=128, H_I=16, h=1, B=32, topk=50,
+         len_new=[4097, 4096], new=[97, 64], max_new=100),
+    dict(N=130, S=1, L=2000, d=128, H_I=16, h=4, B=64, topk=100,           # GEMM shape: calls in turn
+         len_new=[2000], new=[200], max_new=200),
+])
+@pytest.mark.parametrize("k_dt,page_size", [(synth.BF16, 0), (synth.FP8, 0), (synth.BF16, 64)])
+def test_pool_route_score_topk_equals_separate_calls(case, k_dt, page_size):
+    case = dict(case)
+    len_new = np.array(case.pop("len_new"), np.int32)
+    len_old = len_new - np.array(case.pop("new"), np.int32)
+    max_new = case.pop("max_new")
+    S = case["S"]
+    q_seq = np.array(case.pop("q_seq", None) or
+                     [min(i * S // case["N"], S - 1) for i in range(case["N"])], np.int32)
+    q_pos = case.pop("q_pos", None)
+    q_pos = np.array(q_pos, np.int32) if q_pos is not None else len_new[q_seq] - 1
+    p = synth.small("pool_fused", 74, k_dt=k_dt, q_seq=q_seq, q_pos=q_pos, **case)
+    log(f"[pool+fused] N={p.N} S={p.S} L={p.L} d={p.d} B={p.B} k_dt={synth.DTYPE_NAMES[k_dt]} "
+        f"page={page_size} len_old={len_old.tolist()} len_new={len_new.tolist()}")
+    dp = DeviceProblem(p, page_size=page_size, page_seed=5)
+    full = dp.pool()
+    stale = full.clone()
+    for s in range(S):
+        b0, b1 = len_old[s] // p.B, len_new[s] // p.B
+        stale[s, b0:b1] = 7.5
+    lo = torch.from_numpy(len_old).to(full.device)
+    hi = torch.from_numpy(len_new).to(full.device)
+    ka, kb = stale.clone(), stale.clone()
+    dp.pool_update(lo, hi, max_new, ka)
+    heads, r, idx, sc = (np_(t) for t in dp.route_score_topk(ka))
+    _, h2, r2, idx2, sc2 = dp.pool_route_score_topk(kb, lo, hi, max_new)
+    assert np.array_equal(np_(ka).view(np.uint32), np_(kb).view(np.uint32)), "pooled table"
+    assert np.array_equal(np_(ka).view(np.uint32), np_(full).view(np.uint32)), "table vs full pool"
+    assert np.array_equal(heads, np_(h2))
+    assert np.array_equal(r.view(np.uint32), np_(r2).view(np.uint32))
+    assert np.array_equal(idx, np_(idx2))
+    assert np.array_equal(sc.view(np.uint32), np_(sc2).view(np.uint32))
+
+
 def test_route_score_topk_against_the_oracle():
     """The fused call at a decode shape vs the oracle (heads within the
     router tolerance, top-k on the GPU's heads)."""

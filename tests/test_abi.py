@@ -178,6 +178,40 @@ def test_route_score_topk_workspace_covers_both_steps():
                                 topk=min(2048, L), ws_bytes=both - 1) == 4
 
 
+def _pool_route_score(**over):
+    a = dict(q=FAKE, q_dt=1, qsc=None, w=FAKE, kbar=FAKE, k=FAKE, ks=None, k_dt=1, bt=None, ps=0,
+             qs=FAKE, qp=FAKE, lo=FAKE, hi=FAKE, max_new=1, N=4, S=4, L=1000, d=128, B=128,
+             H_I=64, h=8, topk=100, heads=FAKE, hs=None, idx=FAKE, score=None, ws=FAKE,
+             ws_bytes=1 << 30)
+    a.update(over)
+    return b.lib().misa_pool_route_score_topk(
+        a["q"], a["q_dt"], a["qsc"], a["w"], a["kbar"], a["k"], a["ks"], a["k_dt"], a["bt"],
+        a["ps"], a["qs"], a["qp"], a["lo"], a["hi"], a["max_new"], a["N"], a["S"], a["L"], a["d"],
+        a["B"], a["H_I"], a["h"], a["topk"], a["heads"], a["hs"], a["idx"], a["score"], a["ws"],
+        a["ws_bytes"], None)
+
+
+# every check of both calls runs before anything is enqueued (a failing
+# route/score check must not leave the table half updated)
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1), (dict(kbar=None), 1), (dict(k=None), 1), (dict(lo=None), 1),
+    (dict(hi=None), 1), (dict(heads=None), 1), (dict(idx=None), 1), (dict(ws=None), 1),
+    (dict(k_dt=2), 1), (dict(q_dt=0), 3), (dict(d=96), 3), (dict(B=0), 2), (dict(B=2048), 2),
+    (dict(max_new=-1), 2), (dict(max_new=1001), 2), (dict(h=0), 2), (dict(h=65), 2),
+    (dict(topk=0), 2), (dict(N=0), 2), (dict(q=ctypes.c_void_p(0x100004)), 2),
+    (dict(ps=64), 1), (dict(ws_bytes=16), 4),
+])
+def test_pool_route_score_topk_rejects(over, status):
+    assert _pool_route_score(**over) == status
+
+
+def test_pool_route_score_topk_workspace_is_the_fused_calls():
+    lib = b.lib()
+    both = lib.misa_workspace_bytes(b.MISA_OP_ROUTE_SCORE_TOPK, 1, 4, 131072, 128, 64, 128, 2048,
+                                    0)
+    assert _pool_route_score(L=131072, topk=2048, ws_bytes=both - 1) == 4
+
+
 def _param_counts():
     text = open(os.path.join(ROOT, "include", "misa.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)

@@ -272,13 +272,15 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(
   const int base = blockIdx.x * kChunk;
   if (base >= len) return;
   uint32_t* h0 = hist + static_cast<size_t>(n) * kHistWords;
-  find_digit<256, kBins0>(h0, static_cast<uint32_t>(topk), true, sm, res);
-  const uint32_t K = res[2], d0 = res[0];
-  if (K == 0) return;
+  // the chunk's keys do not depend on the threshold digit: their loads go
+  // out first, so they and the histogram's share one round trip
   const uint32_t* row = u + static_cast<size_t>(n) * u_stride;
   const int i0 = base + threadIdx.x * kPerThread;
   uint32_t v[16];
   load16(row, i0, len, v);
+  find_digit<256, kBins0>(h0, static_cast<uint32_t>(topk), true, sm, res);
+  const uint32_t K = res[2], d0 = res[0];
+  if (K == 0) return;
   uint32_t sure = 0, n_cand = 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -340,6 +342,11 @@ __global__ __launch_bounds__(1024) void topk_final_kernel(
     }
   }
   const uint32_t c = h0g[kCandCountOffset];
+  // the first candidate of every thread, read before the count is known (the
+  // list holds kCandCap >= 1024 entries, so the read stays inside it)
+  const uint2* cl = clist + static_cast<size_t>(n) * kCandCap;
+  static_assert(kCandCap >= 1024, "one speculative candidate per thread");
+  const uint2 e_first = cl[threadIdx.x];
   find_digit<1024, kBins0>(h0g, static_cast<uint32_t>(topk), true, sm, res);
   const uint32_t K = res[2], d0 = res[0], r0 = res[1];
   __syncthreads();
@@ -350,9 +357,8 @@ __global__ __launch_bounds__(1024) void topk_final_kernel(
 #pragma unroll
     for (int q = 0; q < kBitmapWords / 4096; ++q)
       *reinterpret_cast<uint4*>(&bm[4 * (threadIdx.x + q * 1024)]) = bw[q];
-    const uint2* cl = clist + static_cast<size_t>(n) * kCandCap;
     for (int i = threadIdx.x; i < static_cast<int>(c); i += 1024) {
-      const uint2 e = cl[i];
+      const uint2 e = i < 1024 ? e_first : cl[i];
       cu[i] = e.x;
       ci[i] = e.y;
     }

@@ -105,12 +105,13 @@ __global__ __launch_bounds__(256) void route_partial_kernel(
 // boundary), and chunk 0 of each row clears that row's level-0 histogram for
 // the scoring kernel.
 //
-// With the incremental pooling folded in (pool_new, the blocks completed by
-// the tokens len_old[s] .. len_new[s] - 1), workgroups nchunks + 1 .. of row 0
-// pool those blocks into the table, as the pooling kernel does, and a chunk
+// With the incremental pooling folded in (the blocks completed by the tokens
+// len_old[s] .. len_new[s] - 1), workgroups nchunks + 1 .. of row 0 pool
+// those blocks into the table, as the pooling kernel does, and a chunk
 // holding such a block pools it for itself from the keys with the same
-// function instead of reading the table: no workgroup reads an entry this
-// launch writes, and the routes equal those after a separate pooling call.
+// function instead of using the table's entry (which it may read while it is
+// rewritten, and discards): the routes equal those after a separate pooling
+// call.
 struct RoutePartialExtra {
   const void* k;
   const float* k_scale;
@@ -197,15 +198,9 @@ __global__ __launch_bounds__(256) void route_partial_mfma_kernel(
       a[kk] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
-  // blocks [nlo, nhi) of this chunk are completed by this call: pooled here
-  // (after the loads of the query and of the table's blocks are issued, so
-  // their round trips overlap the key reads)
-  int nlo = 0, nhi = 0;
-  if (x.len_new) {
-    const int s = q_seq[n];
-    nlo = max(b0, x.len_old[s] / B);
-    nhi = min(b0 + nb, x.len_new[s] / B);
-  }
+  // the chunk's table entries; those of blocks completed by this call
+  // ([nlo, nhi), known only once len_old / len_new arrive) are read too but
+  // replaced below, so these loads wait for nothing but q_seq
   constexpr int PER = kRouteBlocks * D / 4 / 256;      // table float4s per thread
   const float* src = kbar + (static_cast<size_t>(q_seq[n]) * M + b0) * D;
   float4 kx[PER];
@@ -214,8 +209,16 @@ __global__ __launch_bounds__(256) void route_partial_mfma_kernel(
     const int f = tid + 256 * i;
     const int blk = f / (D / 4), col = (f % (D / 4)) * 4;
     kx[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (blk < nb && !(b0 + blk >= nlo && b0 + blk < nhi))
-      kx[i] = *reinterpret_cast<const float4*>(src + static_cast<size_t>(blk) * D + col);
+    if (blk < nb) kx[i] = *reinterpret_cast<const float4*>(src + static_cast<size_t>(blk) * D + col);
+  }
+  // blocks [nlo, nhi) of this chunk are completed by this call: pooled here
+  // (the loads of the query and of the table go out first, so their round
+  // trips overlap the key reads)
+  int nlo = 0, nhi = 0;
+  if (x.len_new) {
+    const int s = q_seq[n];
+    nlo = max(b0, x.len_old[s] / B);
+    nhi = min(b0 + nb, x.len_new[s] / B);
   }
   __shared__ __align__(16) float fresh[kRouteBlocks][D];
   for (int b = nlo; b < nhi; ++b) {

@@ -599,9 +599,11 @@ __global__ __launch_bounds__(256) void topk_tau_kernel(const uint32_t* __restric
   const int len = pos + 1;
   const int m = (pos >> shift) + 1;                    // visible samples
   const int K = min(topk, len);
-  // sample rank whose key about 2K of the row's keys reach; at least
-  // min(K, 32), since the sampled keys are row keys themselves
-  long long r = (2LL * K * m + len - 1) / len;
+  // sample rank whose key about 1.75 K of the row's keys reach (the k-th
+  // score lies below it unless the sample overstates the top keys by ~6
+  // standard deviations at L = 64K, k = 2048); at least min(K, 32), since the
+  // sampled keys are row keys themselves
+  long long r = (7LL * K * m + 4LL * len - 1) / (4LL * len);
   r = max(r, static_cast<long long>(min(K, 32)));
   r = min(r, static_cast<long long>(m));
   const uint32_t* row = us + static_cast<size_t>(n) * us_stride;

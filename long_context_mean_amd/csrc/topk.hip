@@ -607,18 +607,34 @@ __global__ __launch_bounds__(256) void topk_tau_kernel(const uint32_t* __restric
   r = max(r, static_cast<long long>(min(K, 32)));
   r = min(r, static_cast<long long>(m));
   const uint32_t* row = us + static_cast<size_t>(n) * us_stride;
+  // the sample keys in batches of 16 per thread, all loads of a batch issued
+  // before the first histogram update (one round trip per batch, not one per
+  // key); out-of-range slots reread key 0 and are skipped
+  constexpr int PB = 16;
+  auto sweep = [&](auto&& use) {
+    for (int i0 = 0; i0 < m; i0 += 256 * PB) {
+      uint32_t v[PB];
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        const int i = i0 + static_cast<int>(threadIdx.x) + 256 * u;
+        v[u] = row[i < m ? i : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < PB; ++u)
+        if (i0 + static_cast<int>(threadIdx.x) + 256 * u < m) use(v[u]);
+    }
+  };
   for (int b = threadIdx.x; b < kBins0; b += 256) hA[b] = 0u;
   __syncthreads();
-  for (int i = threadIdx.x; i < m; i += 256) atomicAdd(&hA[row[i] >> kShift0], 1u);
+  sweep([&](uint32_t v) { atomicAdd(&hA[v >> kShift0], 1u); });
   __syncthreads();
   find_digit<256, kBins0>(hA, static_cast<uint32_t>(r), true, sm, res);
   const uint32_t d0 = res[0], r0 = res[1];
   for (int b = threadIdx.x; b < kBins1; b += 256) hA[b] = 0u;
   __syncthreads();
-  for (int i = threadIdx.x; i < m; i += 256) {
-    const uint32_t v = row[i];
+  sweep([&](uint32_t v) {
     if ((v >> kShift0) == d0) atomicAdd(&hA[(v >> kShift1) & (kBins1 - 1)], 1u);
-  }
+  });
   __syncthreads();
   find_digit<256, kBins1>(hA, r0, false, sm, res);
   if (threadIdx.x == 0) {

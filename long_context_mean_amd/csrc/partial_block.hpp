@@ -53,7 +53,8 @@ __device__ __forceinline__ void piece_sum(const void* k, const float* k_scale, c
       float v[PM::EPP];
       unpack16<KT>(x[u], v);
 #pragma unroll
-      for (int e = 0; e < PM::EPP; ++e) acc[e] += (KT == DT_E4M3) ? v[e] * sc[u] : v[e];
+      for (int e = 0; e < PM::EPP; ++e)   // explicit fma: the same at every call site
+        acc[e] = (KT == DT_E4M3) ? fmaf(v[e], sc[u], acc[e]) : acc[e] + v[e];
     }
   }
 }

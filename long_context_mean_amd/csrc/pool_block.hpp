@@ -19,52 +19,63 @@ struct PoolMap {
   static constexpr int RG = 256 / CPR;         // row groups
 };
 
-// Mean of key rows [t0, t1) of sequence s with 256 threads: thread
-// (g, c) = (tid / CPR, tid % CPR) sums rows t0 + g, t0 + g + RG, ... of its
-// 16-byte piece c (e4m3 codes times the row's scale), the row groups are
-// added in order through `part`, and thread i < D returns the mean of
-// element i (other threads return 0).  Every thread calls it; it ends with
-// the threads < D still reading `part`, so a caller reusing `part`
-// synchronises first.
+// One batch of a thread's rows: rows t, t + RG, ..., t + (U - 1) RG of its
+// piece (rows at or past t1 reread row t; the sum skips them).
 template <int KT, int D>
-__device__ __forceinline__ float pool_block_mean(const uint8_t* __restrict__ k,
-                                                 const float* __restrict__ k_scale,
-                                                 const KeyIndex& ki, int s, int t0, int t1,
-                                                 float (&part)[PoolMap<KT, D>::RG][D + 1]) {
-  using PM = PoolMap<KT, D>;
-  const int c = threadIdx.x % PM::CPR, g = threadIdx.x / PM::CPR;
-  float acc[PM::EPC];
-#pragma unroll
-  for (int e = 0; e < PM::EPC; ++e) acc[e] = 0.f;
+struct PoolBatch {
+  static constexpr int U = 8;
+  uint4 x[U];
+  float sc[U];
+};
 
-  constexpr int U = 8;
-  for (int t = t0 + g; t < t1; t += U * PM::RG) {
-    uint4 x[U];
-    float sc[U];
+template <int KT, int D>
+__device__ __forceinline__ void pool_batch_load(const uint8_t* __restrict__ k,
+                                                const float* __restrict__ k_scale,
+                                                const KeyIndex& ki, int s, int t, int t1,
+                                                PoolBatch<KT, D>& pb) {
+  using PM = PoolMap<KT, D>;
+  const int c = threadIdx.x % PM::CPR;
 #pragma unroll
-    for (int r = 0; r < U; ++r) {
-      const int tt = t + r * PM::RG;
-      const int tc = tt < t1 ? tt : t;           // stay in bounds; masked below
-      const size_t row = ki.row(s, tc);
-      x[r] = *reinterpret_cast<const uint4*>(k + row * PM::ROW_BYTES + c * 16);
-      sc[r] = 1.f;
-      if constexpr (KT == DT_E4M3) sc[r] = k_scale[row];
-    }
+  for (int r = 0; r < PoolBatch<KT, D>::U; ++r) {
+    const int tt = t + r * PM::RG;
+    const int tc = tt < t1 ? tt : t;             // stay in bounds; masked below
+    const size_t row = ki.row(s, tc);
+    pb.x[r] = *reinterpret_cast<const uint4*>(k + row * PM::ROW_BYTES + c * 16);
+    pb.sc[r] = 1.f;
+    if constexpr (KT == DT_E4M3) pb.sc[r] = k_scale[row];
+  }
+}
+
+template <int KT, int D>
+__device__ __forceinline__ void pool_batch_add(const PoolBatch<KT, D>& pb, int t, int t1,
+                                               float (&acc)[PoolMap<KT, D>::EPC]) {
+  using PM = PoolMap<KT, D>;
 #pragma unroll
-    for (int r = 0; r < U; ++r) {
-      if (t + r * PM::RG < t1) {
-        float v[PM::EPC];
-        unpack16<KT>(x[r], v);
+  for (int r = 0; r < PoolBatch<KT, D>::U; ++r) {
+    if (t + r * PM::RG < t1) {
+      float v[PM::EPC];
+      unpack16<KT>(pb.x[r], v);
 #pragma unroll
-        for (int e = 0; e < PM::EPC; ++e) {
-          if constexpr (KT == DT_E4M3)
-            acc[e] += v[e] * sc[r];
-          else
-            acc[e] += v[e];
-        }
+      for (int e = 0; e < PM::EPC; ++e) {
+        // an explicit fma: the compiler may not contract a separate multiply
+        // and add differently at different call sites
+        if constexpr (KT == DT_E4M3)
+          acc[e] = fmaf(v[e], pb.sc[r], acc[e]);
+        else
+          acc[e] += v[e];
       }
     }
   }
+}
+
+// The row groups' sums added in order through `part`; thread i < D returns
+// the mean of element i (other threads 0).  Ends with the threads < D still
+// reading `part`, so a caller reusing `part` synchronises first.
+template <int KT, int D>
+__device__ __forceinline__ float pool_reduce(const float (&acc)[PoolMap<KT, D>::EPC], int t0,
+                                             int t1, float (&part)[PoolMap<KT, D>::RG][D + 1]) {
+  using PM = PoolMap<KT, D>;
+  const int c = threadIdx.x % PM::CPR, g = threadIdx.x / PM::CPR;
 #pragma unroll
   for (int e = 0; e < PM::EPC; ++e) part[g][c * PM::EPC + e] = acc[e];
   __syncthreads();
@@ -75,6 +86,28 @@ __device__ __forceinline__ float pool_block_mean(const uint8_t* __restrict__ k,
     sum /= static_cast<float>(t1 - t0);
   }
   return sum;
+}
+
+// Mean of key rows [t0, t1) of sequence s with 256 threads: thread
+// (g, c) = (tid / CPR, tid % CPR) sums rows t0 + g, t0 + g + RG, ... of its
+// 16-byte piece c (e4m3 codes times the row's scale) in batches of U rows,
+// then pool_reduce.  Every thread calls it.
+template <int KT, int D>
+__device__ __forceinline__ float pool_block_mean(const uint8_t* __restrict__ k,
+                                                 const float* __restrict__ k_scale,
+                                                 const KeyIndex& ki, int s, int t0, int t1,
+                                                 float (&part)[PoolMap<KT, D>::RG][D + 1]) {
+  using PM = PoolMap<KT, D>;
+  const int g = threadIdx.x / PM::CPR;
+  float acc[PM::EPC];
+#pragma unroll
+  for (int e = 0; e < PM::EPC; ++e) acc[e] = 0.f;
+  for (int t = t0 + g; t < t1; t += PoolBatch<KT, D>::U * PM::RG) {
+    PoolBatch<KT, D> pb;
+    pool_batch_load<KT, D>(k, k_scale, ki, s, t, t1, pb);
+    pool_batch_add<KT, D>(pb, t, t1, acc);
+  }
+  return pool_reduce<KT, D>(acc, t0, t1, part);
 }
 
 }  // namespace misa

@@ -882,6 +882,8 @@ def test_route_score_topk_equals_two_calls(case, k_dt, q_dt, page_size):
          len_new=[4097, 4096], new=[97, 64], max_new=100),
     dict(N=130, S=1, L=2000, d=128, H_I=16, h=4, B=64, topk=100,           # GEMM shape: calls in turn
          len_new=[2000], new=[200], max_new=200),
+    dict(N=2, S=2, L=3000, d=128, H_I=16, h=4, B=64, topk=100,             # nothing appended
+         len_new=[3000, 2999], new=[0, 0], max_new=0),
 ])
 @pytest.mark.parametrize("k_dt,page_size", [(synth.BF16, 0), (synth.FP8, 0), (synth.BF16, 64)])
 def test_pool_route_score_topk_equals_separate_calls(case, k_dt, page_size):

@@ -652,7 +652,7 @@ constexpr int kCandThreads = 512;
 constexpr int kCandMaxK = kBins0 / 2;    // selected per row (outputs staged in hA)
 constexpr int kCandPer = kCandRow / kCandThreads;
 
-__global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
+__global__ __launch_bounds__(kCandThreads, 8) void topk_cand_kernel(
     const uint32_t* __restrict__ cnt, const uint2* __restrict__ cand, int splits, int cap,
     const int32_t* __restrict__ q_pos, int topk, int rows_per_block, int nwords_max,
     uint32_t* __restrict__ row_flag, uint32_t* __restrict__ block_flag,

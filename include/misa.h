@@ -65,8 +65,22 @@
  *  - Errors: host-checkable arguments are validated before anything is
  *    enqueued; a failed check returns its status and launches nothing.  A HIP
  *    launch failure returns MISA_ERR_HIP (see misa_last_hip_error).
- *    Device-resident values (q_seq, q_pos, heads, cand) are NOT read on the
- *    host: out-of-range values there are undefined behaviour.
+ *    Device-resident values (q_seq, q_pos, heads, cand, idx of the attention,
+ *    len_old / len_new) are preconditions and are NOT read on the host in
+ *    normal use: out-of-range values there are undefined behaviour.
+ *  - Debug validation: with the environment variable MISA_DEBUG_SYNC set to
+ *    "1" (read at every call), each entry point first synchronises `stream`,
+ *    copies those device-resident arguments to the host and checks them:
+ *    0 <= q_seq[n] < S, 0 <= q_pos[n] < L; heads distinct in [0, H_I);
+ *    cand entries -1 or in [0, L_n) with the valid ones strictly ascending;
+ *    attention idx entries -1 or distinct in [0, L); 0 <= len_old[s] <=
+ *    len_new[s] <= L with len_new - len_old <= max_new.  A violation returns
+ *    MISA_ERR_SHAPE before anything is launched (outputs untouched).
+ *    Block-table entries are never checked (the pool size is not an
+ *    argument).  The synchronisation makes this a debugging aid only.
+ *  - The library keeps no state between calls except the kernel-timing
+ *    records of misa_profile_begin/end, which belong to the calling host
+ *    thread; calls from several threads on different streams are safe.
  */
 #ifndef MISA_H
 #define MISA_H
@@ -316,6 +330,17 @@ int32_t misa_sparse_attention(const void* q, int32_t q_dt, const void* kv, int32
 size_t misa_workspace_bytes(int32_t op, int32_t q_dt, int32_t N, int32_t L, int32_t d,
                             int32_t H_I, int32_t B, int32_t topk, int32_t k_prime);
 
+/*
+ * Diagnostic of the prefill candidate path (rows sharing one contiguous key
+ * sequence with N >= 128, L >= 32768, topk <= 2048, see
+ * misa_workspace_bytes): a misa_score_topk or dsa_score_topk call that takes
+ * it leaves one uint32 flag per row in its workspace, at this byte offset:
+ * 1 when the row's sampled threshold could not prove its top-k and the row
+ * was re-scored in full, else 0.  Returns -1 when calls at these sizes do not
+ * take that path.
+ */
+int64_t misa_candidate_flags_offset(int32_t N, int32_t L, int32_t topk);
+
 /* Static description of a status code. */
 const char* misa_status_string(int32_t status);
 
@@ -332,7 +357,8 @@ int32_t misa_last_hip_error(void);
  * synchronises the recorded events and writes up to `max` records:
  * kernel_id[i] (see misa_kernel_name) and ms[i], the elapsed time between the
  * pair.  It returns the number of records written (negative on error) and
- * frees the events.  Profiling is process-global and not thread-safe.
+ * frees the events.  The profiling state belongs to the calling host
+ * thread: only launches made by that thread are timed.
  */
 int32_t misa_profile_begin(int32_t capacity);
 int32_t misa_profile_end(int32_t* kernel_id, float* ms, int32_t max);

@@ -29,7 +29,7 @@ MISA_OK = 0
 EXPORTED = ("misa_pool_keys", "misa_pool_update", "misa_route_heads", "misa_score_topk",
             "misa_route_score_topk", "misa_pool_route_score_topk", "dsa_score_topk",
             "misa_rerank", "misa_score_topk_blocks", "misa_sparse_attention",
-            "misa_workspace_bytes", "misa_status_string",
+            "misa_workspace_bytes", "misa_candidate_flags_offset", "misa_status_string",
             "misa_last_hip_error", "misa_profile_begin", "misa_profile_end", "misa_kernel_name")
 
 
@@ -79,6 +79,8 @@ def lib():
         [ctypes.c_float, P, P, P, SZ, P]
     L.misa_workspace_bytes.argtypes = [I32] * 9
     L.misa_workspace_bytes.restype = ctypes.c_size_t
+    L.misa_candidate_flags_offset.argtypes = [I32] * 3
+    L.misa_candidate_flags_offset.restype = ctypes.c_int64
     L.misa_status_string.argtypes = [I32]
     L.misa_status_string.restype = ctypes.c_char_p
     L.misa_last_hip_error.argtypes = []
@@ -170,6 +172,12 @@ def workspace(op: int, N: int, L: int, d: int, H_I: int, B: int = 1, topk: int =
 # ---------------------------------------------------------------- the C entry points
 def misa_workspace_bytes(op, q_dt, N, L, d, H_I, B=1, topk=1, k_prime=0) -> int:
     return int(lib().misa_workspace_bytes(op, q_dt, N, L, d, H_I, B, topk, k_prime))
+
+
+def misa_candidate_flags_offset(N, L, topk) -> int:
+    """Byte offset of the candidate path's per-row fallback flags in a score
+    workspace, or -1 when calls at these sizes do not take that path."""
+    return int(lib().misa_candidate_flags_offset(N, L, topk))
 
 
 def misa_pool_keys(k: torch.Tensor, B: int, k_scale: Optional[torch.Tensor] = None,

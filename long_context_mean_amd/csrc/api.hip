@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
+#include <utility>
 #include <vector>
 
 #include "common.hpp"
@@ -221,13 +223,114 @@ hipError_t prep_fp8_queries(const void*& q, int32_t& q_dt, const float*& w, cons
 }
 
 // ---------------------------------------------------------------- kernel timing
+// Per host thread: a thread's misa_profile_begin times the launches that
+// thread makes, so threads calling the library never share this state.
 struct Profiler {
   bool on = false;
   int cap = 0, used = 0;
   std::vector<hipEvent_t> ev0, ev1;
   std::vector<int> ids;
 };
-Profiler g_prof;
+thread_local Profiler g_prof;
+
+void profiler_release(Profiler& pr) {
+  for (size_t i = 0; i < pr.ev0.size(); ++i) {
+    if (pr.ev0[i]) (void)hipEventDestroy(pr.ev0[i]);
+    if (pr.ev1[i]) (void)hipEventDestroy(pr.ev1[i]);
+  }
+  pr = Profiler();
+}
+
+// ---------------------------------------------------------------- debug validation
+// With MISA_DEBUG_SYNC=1 in the environment (read at every call) each entry
+// point synchronises the caller's stream, copies the device-resident index
+// arguments to the host and checks them before it launches anything; an
+// out-of-range value returns MISA_ERR_SHAPE.  Release use leaves it unset.
+bool debug_sync() {
+  const char* v = getenv("MISA_DEBUG_SYNC");
+  return v && v[0] == '1' && v[1] == '\0';
+}
+
+// Copies n int32 values from the device after the stream's earlier work.
+int32_t fetch_i32(const int32_t* dev, size_t n, hipStream_t st, std::vector<int32_t>& out) {
+  out.assign(n, 0);
+  if (n == 0) return MISA_OK;
+  hipError_t e = hipStreamSynchronize(st);
+  if (e == hipSuccess) e = hipMemcpy(out.data(), dev, n * sizeof(int32_t), hipMemcpyDeviceToHost);
+  return hip_status(e);
+}
+
+// Rows: 0 <= q_seq[n] < S, 0 <= q_pos[n] < L.
+int32_t debug_rows(const int32_t* q_seq, const int32_t* q_pos, int N, int S, int L,
+                   hipStream_t st, std::vector<int32_t>* pos_out = nullptr) {
+  std::vector<int32_t> seq, pos;
+  int32_t rc = fetch_i32(q_seq, N, st, seq);
+  if (!rc && q_pos) rc = fetch_i32(q_pos, N, st, pos);
+  if (rc) return rc;
+  for (int n = 0; n < N; ++n) {
+    if (seq[n] < 0 || seq[n] >= S) return MISA_ERR_SHAPE;
+    if (q_pos && (pos[n] < 0 || pos[n] >= L)) return MISA_ERR_SHAPE;
+  }
+  if (pos_out) *pos_out = std::move(pos);
+  return MISA_OK;
+}
+
+// Heads: every row lists h distinct heads in [0, H_I).
+int32_t debug_heads(const int32_t* heads, int N, int h, int H_I, hipStream_t st) {
+  std::vector<int32_t> hd;
+  int32_t rc = fetch_i32(heads, static_cast<size_t>(N) * h, st, hd);
+  if (rc) return rc;
+  for (int n = 0; n < N; ++n) {
+    uint64_t seen = 0;
+    for (int i = 0; i < h; ++i) {
+      const int32_t j = hd[static_cast<size_t>(n) * h + i];
+      if (j < 0 || j >= H_I || ((seen >> j) & 1u)) return MISA_ERR_SHAPE;
+      seen |= uint64_t{1} << j;
+    }
+  }
+  return MISA_OK;
+}
+
+// Token lists (MISA-dagger candidates, attention selections): entries are -1
+// or tokens below the row's bound; valid ones strictly ascending when
+// `ascending`, else distinct.
+int32_t debug_tokens(const int32_t* tok, int N, int stride, const std::vector<int32_t>& bound,
+                     int L, bool ascending, hipStream_t st) {
+  std::vector<int32_t> t;
+  int32_t rc = fetch_i32(tok, static_cast<size_t>(N) * stride, st, t);
+  if (rc) return rc;
+  std::vector<uint8_t> seen;
+  for (int n = 0; n < N; ++n) {
+    const int32_t lim = bound.empty() ? L : bound[n] + 1;
+    int32_t last = -1;
+    if (!ascending) seen.assign(static_cast<size_t>(L), 0);
+    for (int i = 0; i < stride; ++i) {
+      const int32_t x = t[static_cast<size_t>(n) * stride + i];
+      if (x == -1) continue;
+      if (x < 0 || x >= lim) return MISA_ERR_SHAPE;
+      if (ascending) {
+        if (x <= last) return MISA_ERR_SHAPE;
+        last = x;
+      } else {
+        if (seen[x]) return MISA_ERR_SHAPE;
+        seen[x] = 1;
+      }
+    }
+  }
+  return MISA_OK;
+}
+
+// Appended lengths: 0 <= len_old[s] <= len_new[s] <= L, len_new - len_old <= max_new.
+int32_t debug_lens(const int32_t* len_old, const int32_t* len_new, int S, int L, int max_new,
+                   hipStream_t st) {
+  std::vector<int32_t> a, b;
+  int32_t rc = fetch_i32(len_old, S, st, a);
+  if (!rc) rc = fetch_i32(len_new, S, st, b);
+  if (rc) return rc;
+  for (int s = 0; s < S; ++s)
+    if (a[s] < 0 || a[s] > b[s] || b[s] > L || b[s] - a[s] > max_new) return MISA_ERR_SHAPE;
+  return MISA_OK;
+}
 
 // The routed decode step's scoring launch picks the heads itself from the
 // router partials (see misa_route_score_topk); its histogram was cleared by
@@ -260,6 +363,10 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* q_scale, const
   if (!ws) return MISA_ERR_NULL;
   if (ws_bytes < (f8 ? q8_off + q8_bytes(N, H_I, d) : lay.bytes)) return MISA_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!fr && debug_sync()) {
+    if ((rc = debug_rows(q_seq, q_pos, N, S, L, st))) return rc;
+    if (heads && (rc = debug_heads(heads, N, h, H_I, st))) return rc;
+  }
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint32_t* u = reinterpret_cast<uint32_t*>(base);
   uint32_t* hist = lay.one_row ? nullptr : reinterpret_cast<uint32_t*>(base + lay.off_hist);
@@ -407,6 +514,13 @@ size_t misa_workspace_bytes(int32_t op, int32_t q_dt, int32_t N, int32_t L, int3
   }
 }
 
+int64_t misa_candidate_flags_offset(int32_t N, int32_t L, int32_t topk) {
+  if (N < 1 || N > kMaxN || L < 1 || L > kMaxL || topk < 1 || topk > kMaxTopk) return -1;
+  if (!cand_eligible(N, L, topk)) return -1;
+  const TopkLayout t = topk_layout(N, L);
+  return static_cast<int64_t>(cand_layout(t.bytes, N, L).off_rflag);
+}
+
 int32_t misa_pool_keys(const void* k, const float* k_scale, int32_t k_dt,
                        const int32_t* block_table, int32_t page_size, int32_t S, int32_t L,
                        int32_t d, int32_t B, float* kbar, void* stream) {
@@ -428,6 +542,9 @@ int32_t misa_pool_update(const void* k, const float* k_scale, int32_t k_dt,
   if (max_new < 0 || max_new > L) return MISA_ERR_SHAPE;
   misa::KeyIndex ki;
   if ((rc = key_index(block_table, page_size, L, ki))) return rc;
+  if (debug_sync() && (rc = debug_lens(len_old, len_new, S, L, max_new,
+                                        static_cast<hipStream_t>(stream))))
+    return rc;
   if (max_new == 0) return MISA_OK;
   misa::PoolArgs a{k, k_scale, k_dt, S, L, d, B, kbar, ki, len_old, len_new, max_new};
   return hip_status(misa::launch_pool(a, static_cast<hipStream_t>(stream)));
@@ -451,6 +568,9 @@ int32_t misa_route_heads(const void* q, int32_t q_dt, const float* q_scale, cons
   const size_t own = route_bytes(N, L, B, H_I);
   if (!ws) return MISA_ERR_NULL;
   if (ws_bytes < own + (f8 ? q8_bytes(N, H_I, d) : 0)) return MISA_ERR_WORKSPACE;
+  if (debug_sync() &&
+      (rc = debug_rows(q_seq, q_pos, N, S, L, static_cast<hipStream_t>(stream))))
+    return rc;
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   misa::RouteArgs a{q, q_dt, f8 ? q_scale : nullptr, w, kbar, k, k_scale, k_dt, q_seq, q_pos, N,
                     S, L, d, B, H_I, h, heads, head_score, reinterpret_cast<float*>(wsb),
@@ -510,6 +630,9 @@ int32_t misa_route_score_topk(const void* q, int32_t q_dt, const float* q_scale,
                     (q_dt == MISA_FP8_E4M3 ? q8_bytes(N, H_I, d) : 0);
   if (!ws) return MISA_ERR_NULL;
   if (ws_bytes < rb + sb) return MISA_ERR_WORKSPACE;
+  if (debug_sync() &&
+      (rc = debug_rows(q_seq, q_pos, N, S, L, static_cast<hipStream_t>(stream))))
+    return rc;
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   // the fused form: decode rows (not the one-sequence GEMM shapes), bf16
   // queries, bf16 or e4m3 keys; otherwise the two calls in turn
@@ -566,6 +689,11 @@ int32_t misa_pool_route_score_topk(const void* q, int32_t q_dt, const float* q_s
                     (q_dt == MISA_FP8_E4M3 ? q8_bytes(N, H_I, d) : 0);
   if (!ws) return MISA_ERR_NULL;
   if (ws_bytes < rb + sb) return MISA_ERR_WORKSPACE;
+  if (debug_sync()) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = debug_lens(len_old, len_new, S, L, max_new, st))) return rc;
+    if ((rc = debug_rows(q_seq, q_pos, N, S, L, st))) return rc;
+  }
   const bool fused = q_dt == MISA_BF16 && k_dt != MISA_F32 && !(S == 1 && N >= kOneRowMinN);
   if (!fused || max_new == 0) {
     rc = misa_pool_update(k, k_scale, k_dt, block_table, page_size, S, L, d, B, len_old, len_new,
@@ -616,6 +744,11 @@ int32_t misa_rerank(const void* q, int32_t q_dt, const float* q_scale, const flo
   if (!ws) return MISA_ERR_NULL;
   if (ws_bytes < own + (f8 ? q8_bytes(N, H_I, d) : 0)) return MISA_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_sync()) {
+    std::vector<int32_t> pos;
+    if ((rc = debug_rows(q_seq, q_pos, N, S, L, st, &pos))) return rc;
+    if ((rc = debug_tokens(cand, N, k_prime, pos, L, true, st))) return rc;
+  }
   if (f8) {
     const hipError_t e =
         prep_fp8_queries(q, q_dt, w, q_scale, N, H_I, d, static_cast<uint8_t*>(ws) + own, st);
@@ -655,6 +788,10 @@ int32_t misa_score_topk_blocks(const void* q, int32_t q_dt, const float* q_scale
   if (!ws) return MISA_ERR_NULL;
   if (ws_bytes < bl.bytes + (f8 ? q8_bytes(N, H_I, d) : 0)) return MISA_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_sync()) {
+    if ((rc = debug_rows(q_seq, q_pos, N, S, L, st))) return rc;
+    if ((rc = debug_heads(heads, N, h, H_I, st))) return rc;
+  }
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   hipError_t e = hipSuccess;
   if (f8) {
@@ -703,6 +840,11 @@ int32_t misa_sparse_attention(const void* q, int32_t q_dt, const void* kv, int32
   const size_t need = attention_bytes(N, H, d_v, topk);
   if (!ws) return MISA_ERR_NULL;
   if (ws_bytes < need) return MISA_ERR_WORKSPACE;
+  if (debug_sync()) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = debug_rows(q_seq, nullptr, N, S, L, st))) return rc;
+    if ((rc = debug_tokens(idx, N, topk, {}, L, false, st))) return rc;
+  }
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   const size_t parts = static_cast<size_t>(N) * H * misa::attn_splits(topk);
   misa::AttnArgs a{q, kv, ki, q_seq, idx, N, H, d_qk, d_v, topk, scale,
@@ -712,14 +854,17 @@ int32_t misa_sparse_attention(const void* q, int32_t q_dt, const void* kv, int32
 
 int32_t misa_profile_begin(int32_t capacity) {
   if (capacity < 1) return MISA_ERR_SHAPE;
-  if (g_prof.on) (void)misa_profile_end(nullptr, nullptr, 0);
+  profiler_release(g_prof);
   g_prof.ev0.assign(capacity, nullptr);
   g_prof.ev1.assign(capacity, nullptr);
   g_prof.ids.assign(capacity, -1);
   for (int i = 0; i < capacity; ++i) {
     hipError_t e = hipEventCreate(&g_prof.ev0[i]);
     if (e == hipSuccess) e = hipEventCreate(&g_prof.ev1[i]);
-    if (e != hipSuccess) return hip_status(e);
+    if (e != hipSuccess) {
+      profiler_release(g_prof);           // the events created so far
+      return hip_status(e);
+    }
   }
   g_prof.cap = capacity;
   g_prof.used = 0;
@@ -739,11 +884,7 @@ int32_t misa_profile_end(int32_t* kernel_id, float* ms, int32_t max) {
       ++written;
     }
   }
-  for (size_t i = 0; i < g_prof.ev0.size(); ++i) {
-    if (g_prof.ev0[i]) (void)hipEventDestroy(g_prof.ev0[i]);
-    if (g_prof.ev1[i]) (void)hipEventDestroy(g_prof.ev1[i]);
-  }
-  g_prof = Profiler();
+  profiler_release(g_prof);
   return written;
 }
 

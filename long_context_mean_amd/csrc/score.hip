@@ -29,8 +29,6 @@
 // load at the start (lane j: the j-th tile) and takes each tile's page from
 // that register with readlane, so the loop itself does no lookups; candidate
 // gathers look each token's page up per lane.
-#include <cstdlib>
-
 #include "common.hpp"
 #include "kernels.hpp"
 #include "route_select.hpp"
@@ -522,11 +520,6 @@ hipError_t launch_mfma_rows(const ScoreArgs& a, hipStream_t st, int tpw) {
   return launch_mfma<KT, 4, D>(a, st, tpw);
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return v ? atoi(v) : dflt;
-}
-
 }  // namespace
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
@@ -547,11 +540,9 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   // tiles (of 16 keys) per wavefront; short candidate lists use smaller
-  // chunks so more workgroups share the gather.  MISA_SCORE_TPW overrides
-  // (launch-shape tuning only).
-  static const int tpw_env = env_int("MISA_SCORE_TPW", 0);
-  // (at most 64 tiles per wavefront: the paged path keeps one page number per lane)
-  const int tpw = tpw_env > 0 ? (tpw_env < 64 ? tpw_env : 64) : (a.cand ? 4 : 16);
+  // chunks so more workgroups share the gather (at most 64 tiles per
+  // wavefront: the paged path keeps one page number per lane)
+  const int tpw = a.cand ? 4 : 16;
   if (a.k_dt == DT_BF16)
     return a.d == 64 ? launch_mfma_rows<DT_BF16, 64>(a, st, tpw)
                      : launch_mfma_rows<DT_BF16, 128>(a, st, tpw);

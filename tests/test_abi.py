@@ -255,3 +255,17 @@ def test_binding_pointer_checks():
     with pytest.raises(ValueError, match="GPU tensor"):
         b._ptr(object(), "t")
     assert b._ptr(None, "t") is None
+
+
+def test_candidate_flags_offset():
+    """The prefill candidate path's row flags lie inside the score workspace
+    at the sizes that take the path; other sizes report -1."""
+    BF = b.MISA_BF16
+    for N, L in ((4096, 65536), (4096, 131072), (128, 32768)):
+        off = b.misa_candidate_flags_offset(N, L, 2048)
+        ws = b.misa_workspace_bytes(b.MISA_OP_SCORE_TOPK, BF, N, L, 128, 64, 128, 2048, 0)
+        assert 0 <= off and off + 4 * N <= ws and off % 256 == 0
+    assert b.misa_candidate_flags_offset(4, 131072, 2048) == -1      # decode rows
+    assert b.misa_candidate_flags_offset(4096, 20000, 2048) == -1    # short prefix
+    assert b.misa_candidate_flags_offset(4096, 65536, 4096) == -1    # large k
+    assert b.misa_candidate_flags_offset(0, 65536, 2048) == -1

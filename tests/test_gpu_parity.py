@@ -59,14 +59,18 @@ def fp8_gemm(p):
     return p.q_dt == synth.FP8 and p.S == 1 and p.N >= 128 and p.d == 128
 
 
-def check_misa(p, h=None, topk=None, rows=None, page_size=0):
-    """Full MISA on GPU (pool -> route -> score+top-k) vs the oracle."""
+def check_misa(p, h=None, topk=None, rows=None, page_size=0, ws=None):
+    """Full MISA on GPU (pool -> route -> score+top-k) vs the oracle.  `ws`:
+    the score call's workspace (None: the binding allocates one)."""
     h = p.h if h is None else h
     topk = p.topk if topk is None else topk
     log(f"[misa] {p.name} N={p.N} L={p.L} d={p.d} H_I={p.H_I} h={h} k={topk} "
         f"q_dt={synth.DTYPE_NAMES[p.q_dt]} k_dt={synth.DTYPE_NAMES[p.k_dt]} page={page_size}")
     dp = DeviceProblem(p, page_size=page_size, page_seed=7)
-    kbar, heads, r, idx, sc = misa_gpu(dp, h, topk)
+    kbar = dp.pool()
+    heads, r = dp.route(kbar, h)
+    idx, sc = dp.score_topk(heads, topk, ws=ws)
+    kbar, heads, r, idx, sc = (np_(t) for t in (kbar, heads, r, idx, sc))
     ref_kbar = oracle.pool_keys(p)
     assert np.all(np.abs(kbar - ref_kbar) <= tol(ref_kbar)), "pooled keys"
     rows = np.arange(p.N) if rows is None else np.asarray(rows)
@@ -228,10 +232,36 @@ def test_c2_decode_batch():
     log(f"[c2] recall of dense top-k by MISA h=8: {recall(idx, np_(didx)):.4f}")
 
 
+def check_single_call(dp, h, len_old, len_new, max_new):
+    """misa_pool_route_score_topk against misa_pool_keys + misa_route_heads +
+    misa_score_topk on the same device problem, bit for bit: the table starts
+    with the entries of the blocks the call completes zeroed, so a router
+    workgroup that read one instead of pooling it would change the routes."""
+    p = dp.p
+    kbar = dp.pool()
+    heads, r = dp.route(kbar, h)
+    idx, sc = dp.score_topk(heads)
+    table = kbar.clone()
+    for s in range(p.S):
+        table[s, len_old[s] // p.B:len_new[s] // p.B] = 0.0
+    lo = torch.from_numpy(np.asarray(len_old, np.int32)).cuda()
+    hi = torch.from_numpy(np.asarray(len_new, np.int32)).cuda()
+    table, h2, r2, idx2, sc2 = dp.pool_route_score_topk(table, lo, hi, max_new, h)
+    assert torch.equal(table.view(torch.int32), kbar.view(torch.int32)), "pooled table"
+    assert np.array_equal(np_(heads), np_(h2)), "heads"
+    assert np.array_equal(np_(r).view(np.uint32), np_(r2).view(np.uint32)), "router scores"
+    assert np.array_equal(np_(idx), np_(idx2)), "top-k"
+    assert np.array_equal(np_(sc).view(np.uint32), np_(sc2).view(np.uint32)), "scores"
+
+
 @pytest.mark.parametrize("h", [4, 8, 16])
 def test_c4_long_decode_needles(h):
     p = synth.make("c4")
     dp, heads, idx = check_misa(p, h=h)
+    # the benchmark's single call (the newest token completes each sequence's
+    # last block): 64 router chunks per row plus the partial-block slot
+    log(f"[c4] single serving-step call, h={h}")
+    check_single_call(dp, h, np.full(p.S, p.L - 1), np.full(p.S, p.L), 1)
     if h == 8:
         didx, dsc = dp.dsa()
         didx = np_(didx)
@@ -264,10 +294,87 @@ def test_c5_misa_dagger_fp8():
     log(f"[c5] MISA-dagger recall of dense top-k {recall(np_(idx), np_(didx)):.4f}")
 
 
+@pytest.mark.parametrize("L,B,pos", [
+    (20000, 16, [19999, 19922, 16383]),      # 1250 / 1245 / exactly 1024 full blocks
+    (200000, 128, [199935, 199922]),         # 1562 full blocks, the second row a partial one
+])
+def test_decode_more_than_64_router_chunks(L, B, pos):
+    """Rows with more than 1024 full blocks (over 64 router chunks of 16):
+    the chunk partials take the remaining passes of their sum, in the
+    router's selection kernel and in the single call's scoring prologue
+    alike.  Heads against the oracle, the single call against the separate
+    calls bit for bit (each row's newest token appended by the call)."""
+    N = len(pos)
+    p = synth.small("chunks", 75, N=N, S=N, L=L, d=128, H_I=64, h=8, B=B, topk=2048,
+                    q_pos=np.array(pos, np.int32), n_clusters=64)
+    log(f"[chunks] N={N} L={L} B={B}: {(L // B + 15) // 16} router chunks per full row")
+    dp, heads, idx = check_misa(p)
+    check_single_call(dp, p.h, p.q_pos[p.q_seq], p.q_pos[p.q_seq] + 1, 1)
+
+
+def prefill_sample_rows(p, idx_gpu, sc_gpu, n_tie=8):
+    """Rows of a prefill chunk to check against the oracle: the first and last
+    16, every row at a block boundary of its visible prefix (positions
+    b*B - 1 and b*B), two near the middle, and up to n_tie rows whose GPU top-k
+    holds ties at the k-th score."""
+    N = p.N
+    pos = p.q_pos.astype(np.int64)
+    edge = np.nonzero((pos % p.B == 0) | (pos % p.B == p.B - 1))[0]
+    ties = []
+    for n in range(N):
+        v = sc_gpu[n][idx_gpu[n] >= 0]
+        if v.size and np.count_nonzero(v == v.min()) > 1:
+            ties.append(n)
+    rows = np.unique(np.r_[0:16, N - 16:N, edge, N // 2, N // 2 + 1, ties[:n_tie]])
+    return rows, len(ties)
+
+
+def candidate_fallback_rows(ws, N, L, topk):
+    """Rows the prefill candidate path sent to the full path (its flags in the
+    score workspace)."""
+    from long_context_mean_amd import binding
+    off = binding.misa_candidate_flags_offset(N, L, topk)
+    assert off >= 0, "these sizes do not take the candidate path"
+    flags = np_(ws[off:off + 4 * N]).view(np.uint32)
+    return int(flags.sum())
+
+
+def check_prefill_chunk(p, dense_rows=24):
+    """A prefill chunk at full size: routed MISA on sampled rows against the
+    oracle (which rows: prefill_sample_rows), how many rows the candidate path
+    sent to the full path, and the dense 64-head path on a subset."""
+    from long_context_mean_amd import binding
+    ws = binding.workspace(binding.MISA_OP_SCORE_TOPK, p.N, p.L, p.d, p.H_I, topk=p.topk,
+                           q_dt=p.q_dt)
+    dp = DeviceProblem(p)
+    heads, _ = dp.route(dp.pool())
+    idx, sc = (np_(t) for t in dp.score_topk(heads, ws=ws))
+    rows, n_ties = prefill_sample_rows(p, idx, sc)
+    fb = candidate_fallback_rows(ws, p.N, p.L, p.topk)
+    log(f"[{p.name}] {len(rows)} sampled rows ({n_ties} rows with k-th score ties); "
+        f"candidate path: {p.N - fb} rows proven, {fb} re-scored in full")
+    assert fb < p.N // 8, "the sampled threshold should prove most rows"
+    check_misa(p, rows=rows, ws=ws)
+    assert candidate_fallback_rows(ws, p.N, p.L, p.topk) == fb
+    didx, dsc = dp.dsa(ws=ws)
+    drows = rows[np.linspace(0, len(rows) - 1, dense_rows).astype(int)]
+    ps = sub_problem(p, drows)
+    extra = fp8_mfma_error_bound(ps, None) if fp8_gemm(p) else None
+    check_topk(np_(didx)[drows], np_(dsc)[drows], oracle.scores(ps, None), p.topk,
+               ps.visible(), extra=extra)
+
+
 def test_c3_prefill_chunk_sampled_rows():
     p = synth.make("c3")
-    rows = np.r_[0:3, 127:130, 2047:2049, 3976, 4093:4096]   # row 3976: 852 zero-score ties at the k-th score
-    check_misa(p, rows=rows)
+    check_prefill_chunk(p)
+    # row 3976: 852 zero-score ties at the k-th score
+    check_misa(p, rows=np.r_[3976])
+
+
+def test_c3x_prefill_chunk_sampled_rows():
+    """The L = 128K prefill chunk (its candidate select keeps a bitmap twice
+    c3's in LDS)."""
+    check_prefill_chunk(synth.make("c3x"))
 
 
 # ---------------------------------------------------------------- prefill (rows sharing one prefix)
@@ -520,8 +627,7 @@ def test_fp8_prefill_dense_and_dagger_parity():
 
 
 def test_c3f8_prefill_chunk_sampled_rows():
-    p = synth.make("c3f8")
-    check_misa(p, rows=np.r_[0:3, 127:130, 2047:2049, 4093:4096])
+    check_prefill_chunk(synth.make("c3f8"))
 
 
 # ---------------------------------------------------------------- paged keys and incremental pooling
@@ -940,3 +1046,69 @@ def test_route_score_topk_integer_inputs_bit_exact():
     ref_heads, _ = oracle.route_heads(p)
     assert np.array_equal(heads, ref_heads)
     check_topk(idx, sc, oracle.scores(p, ref_heads), p.topk, p.visible(), exact=True)
+
+
+# ---------------------------------------------------------------- debug validation (MISA_DEBUG_SYNC=1)
+def _sentinel(shape, dtype=torch.int32):
+    return torch.full(shape, 12345, dtype=dtype, device="cuda")
+
+
+def test_debug_sync_rejects_bad_device_indices(monkeypatch):
+    """With MISA_DEBUG_SYNC=1 the device-resident index arguments are checked
+    on the host before anything is launched: an out-of-range q_pos / q_seq,
+    a repeated head, a candidate list out of order and an appended length
+    past L each return MISA_ERR_SHAPE, launch no kernel and leave the
+    outputs untouched."""
+    from long_context_mean_amd import binding
+    p = synth.small("dbg", 120, N=3, S=2, L=3000, d=128, H_I=16, h=4, B=128, topk=100,
+                    k_prime=400)
+    dp = DeviceProblem(p)
+    kbar = dp.pool()
+    heads, _ = dp.route(kbar)
+    cand, _ = dp.score_topk(heads, p.k_prime)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("MISA_DEBUG_SYNC", "1")
+    good_pos = dp.q_pos
+
+    def expect_shape_error(fn, outs):
+        binding.misa_profile_begin(64)
+        with pytest.raises(binding.MisaError) as e:
+            fn()
+        torch.cuda.synchronize()
+        recs = binding.misa_profile_end(64)
+        assert e.value.status == 2, e.value
+        assert recs == [], f"kernels launched: {recs}"
+        for t in outs:
+            assert torch.all(t == 12345), "output written"
+
+    dp.q_pos = torch.tensor([2999, 3000, 5], dtype=torch.int32, device="cuda")   # 3000 >= L
+    idx = _sentinel((p.N, p.topk))
+    expect_shape_error(lambda: dp.score_topk(heads, idx=idx, want_score=False), [idx])
+    hd = _sentinel((p.N, p.h))
+    expect_shape_error(lambda: dp.route(kbar, heads=hd, want_scores=False), [hd])
+    expect_shape_error(lambda: dp.route_score_topk(kbar, heads=hd, idx=idx, want_scores=False,
+                                                   want_score=False), [hd, idx])
+    dp.q_pos = good_pos
+    dp.q_seq = torch.tensor([0, 2, 1], dtype=torch.int32, device="cuda")        # 2 >= S
+    expect_shape_error(lambda: dp.dsa(idx=idx, want_score=False), [idx])
+    dp.q_seq = torch.from_numpy(p.q_seq).cuda()
+    dup = heads.clone()
+    dup[1, 1] = dup[1, 0]
+    expect_shape_error(lambda: dp.score_topk(dup, idx=idx, want_score=False), [idx])
+    bad = cand.clone()
+    bad[2, 5], bad[2, 6] = bad[2, 6].item(), bad[2, 5].item()                    # out of order
+    expect_shape_error(lambda: dp.rerank(bad, idx=idx, want_score=False), [idx])
+    lo = torch.full((p.S,), p.L - 1, dtype=torch.int32, device="cuda")
+    hi = torch.tensor([p.L, p.L + 1], dtype=torch.int32, device="cuda")        # past L
+    table = torch.full_like(kbar, 12345.0)
+    expect_shape_error(lambda: dp.pool_update(lo, hi, 2, table), [table])
+    expect_shape_error(lambda: dp.pool_route_score_topk(table, lo, hi, 2, heads=hd, idx=idx,
+                                                        want_scores=False, want_score=False),
+                       [table, hd, idx])
+    # valid arguments with the check on: the same results as without it
+    i1, s1 = dp.score_topk(heads)
+    g1, _ = dp.rerank(cand)
+    monkeypatch.delenv("MISA_DEBUG_SYNC")
+    i2, s2 = dp.score_topk(heads)
+    g2, _ = dp.rerank(cand)
+    assert torch.equal(i1, i2) and torch.equal(s1, s2) and torch.equal(g1, g2)

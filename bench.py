@@ -441,8 +441,10 @@ def measured_mfma_tflops(torch, fp8=False):
 
 def cpu_baseline(p, h, min_seconds=10.0, max_passes=200):
     """The oracle on the host cores over the whole workload, repeated until
-    about min_seconds of CPU work have run (one pass is well under a second)."""
+    about min_seconds of CPU work have run (one pass is well under a second);
+    beside it, one-thread oracle times of the two small decode workloads."""
     import oracle
+    from long_context_mean_amd import synth
     passes, t0 = 0, time.perf_counter()
     while True:
         oracle.misa(p, h=h)
@@ -450,26 +452,41 @@ def cpu_baseline(p, h, min_seconds=10.0, max_passes=200):
         dt = time.perf_counter() - t0
         if dt >= min_seconds or passes >= max_passes:
             break
+    threads = oracle.max_threads()
+    one = {}
+    oracle.set_threads(1)
+    try:
+        for name in ("c1", "c2"):
+            pc = synth.make(name)
+            t1 = time.perf_counter()
+            oracle.misa(pc)
+            one[f"{name}_ms"] = round((time.perf_counter() - t1) * 1e3, 1)
+            one[f"{name}_tokens_per_s"] = round(pc.tokens_indexed() /
+                                                (time.perf_counter() - t1), 1)
+    finally:
+        oracle.set_threads(threads)
     return {"value": passes * p.tokens_indexed() / dt, "unit": "tokens/s",
-            "cores": oracle.max_threads(), "kind": "oracle",
+            "cores": threads, "kind": "oracle",
             "sample": f"the full workload ({p.N} queries x {p.L} keys, pooling+routing+scoring+"
-                      f"top-k in double precision), {passes} passes in {dt:.1f} s"}
+                      f"top-k in double precision), {passes} passes in {dt:.1f} s",
+            "cores_available": len(os.sched_getaffinity(0)),
+            "one_thread": one}
 
 
-def prefill_main(args):
-    """Prefill chunk: 4096 consecutive query rows over one causal prefix."""
-    import torch
-
+def prefill_measure(torch, workload, h, steps, warmup):
+    """Prefill chunk `workload` (4096 consecutive query rows over one causal
+    prefix): the routed step (pool -> route -> score + top-k), the dense
+    64-head step, kernel times and the scoring GEMM against the MFMA peak."""
     from long_context_mean_amd import binding, synth
     from long_context_mean_amd.binding import DeviceProblem
-    p = synth.make(args.workload, h=args.h)
+    p = synth.make(workload, h=h)
     dp = DeviceProblem(p)
     N, L, d, H_I, B = p.N, p.L, p.d, p.H_I, p.B
     fp8 = p.q_dt == synth.FP8
     M = -(-L // B)
     dev = dp.q.device
     kbar = torch.empty((1, M, d), dtype=torch.float32, device=dev)
-    heads = torch.empty((N, args.h), dtype=torch.int32, device=dev)
+    heads = torch.empty((N, h), dtype=torch.int32, device=dev)
     r = torch.empty((N, H_I), dtype=torch.float32, device=dev)
     idx = torch.empty((N, p.topk), dtype=torch.int32, device=dev)
     ws_r = binding.workspace(binding.MISA_OP_ROUTE, N, L, d, H_I, B, q_dt=p.q_dt, device=dev)
@@ -479,7 +496,7 @@ def prefill_main(args):
 
     def step(_):
         binding.misa_pool_keys(dp.k, B, ks, kbar=kbar)
-        binding.misa_route_heads(dp.q, dp.w, kbar, dp.k, dp.q_seq, dp.q_pos, B, args.h,
+        binding.misa_route_heads(dp.q, dp.w, kbar, dp.k, dp.q_seq, dp.q_pos, B, h,
                                  k_scale=ks, q_scale=qs, heads=heads, head_score=r, ws=ws_r)
         binding.misa_score_topk(dp.q, dp.w, dp.k, dp.q_seq, dp.q_pos, heads, p.topk, k_scale=ks,
                                 q_scale=qs, idx=idx, ws=ws_s, want_score=False)
@@ -488,13 +505,13 @@ def prefill_main(args):
         binding.dsa_score_topk(dp.q, dp.w, dp.k, dp.q_seq, dp.q_pos, p.topk, k_scale=ks,
                                q_scale=qs, idx=idx, ws=ws_s, want_score=False)
 
-    ms = timed(torch, step, args.steps, args.warmup)
-    pct = step_percentiles(torch, step, reps=max(20, args.steps), warmup=2)
-    ms_e, kt, per = kernel_times(torch, binding, step, max(3, args.steps // 4), 1, 16)
-    ms_d = timed(torch, dense, max(3, args.steps // 4), 1)
+    ms = timed(torch, step, steps, warmup)
+    pct = step_percentiles(torch, step, reps=max(20, steps), warmup=2)
+    ms_e, kt, per = kernel_times(torch, binding, step, max(3, steps // 4), 1, 16)
+    ms_d = timed(torch, dense, max(3, steps // 4), 1)
     _, ktd, _ = kernel_times(torch, binding, dense, 3, 1, 8)
     pairs = p.tokens_indexed()
-    flops = 2.0 * args.h * d * pairs
+    flops = 2.0 * h * d * pairs
     sc_ms = kt.get("score_prefill_kernel")
     tflops = flops / (sc_ms * 1e-3) / 1e12 if sc_ms else None
     dflops = 2.0 * H_I * d * pairs
@@ -502,11 +519,11 @@ def prefill_main(args):
     peak = 5000.0 if fp8 else 2500.0              # dense MFMA: e4m3 5.0, bf16 2.5 PFLOP/s
     line = {
         "metric": "prefix tokens indexed/sec (prefill chunk)", "value": pairs / (ms * 1e-3),
-        "unit": "(query, prefix token) pairs/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "unit": "(query, prefix token) pairs/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "dtype": "e4m3" if fp8 else "bf16", "data": "synthetic",
         "config": {"workload": f"prefill chunk: {N} rows at positions {int(p.q_pos[0])}.."
-                               f"{int(p.q_pos[-1])} over L={L}, H_I={H_I}, d={d}, h={args.h}, "
+                               f"{int(p.q_pos[-1])} over L={L}, H_I={H_I}, d={d}, h={h}, "
                                f"B={B}, top-k={p.topk}" +
                                (", e4m3 q (per-head scale) and k (per-token scale)" if fp8
                                 else "")},
@@ -523,7 +540,16 @@ def prefill_main(args):
                   "dense_score_tflops": round(dflops / (dsc * 1e-3) / 1e12, 1) if dsc else None,
                   "routed_score_vs_dense_score": round(dsc / sc_ms, 3) if dsc and sc_ms else None},
     }
-    mtf = measured_mfma_tflops(torch, fp8)
+    del dp, ws_s, ws_r
+    torch.cuda.empty_cache()
+    return line
+
+
+def prefill_main(args):
+    import torch
+    line = prefill_measure(torch, args.workload, args.h, args.steps, args.warmup)
+    mtf = measured_mfma_tflops(torch, line["dtype"] == "e4m3")
+    tflops = line["roofline"]["achieved"]
     line["roofline"]["measured_peak"] = mtf
     line["roofline"]["frac_vs_measured_peak"] = round(tflops / mtf, 4) if tflops and mtf else None
     print(json.dumps(line), flush=True)
@@ -581,7 +607,14 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(dominant, "c4"),
                 "kernel": dominant, "kernel_ms": round(kt[dominant], 5),
-                "algorithmic_bytes_per_launch": alg}
+                "algorithmic_bytes_per_launch": alg,
+                "frac_is": f"{dominant} alone: its algorithmic bytes over its own duration"}
+    # the whole step against the same roofline: the step's algorithmic bytes
+    # (every key once, plus the pooled table the router reads) over ms_per_step
+    step_bytes = key_bytes + p.S * (p.L // p.B) * p.d * 4
+    roofline["step_algorithmic_bytes"] = step_bytes
+    roofline["step_achieved"] = round(step_bytes / (ms * 1e-3) / 1e9, 1)
+    roofline["step_frac"] = round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
 
     extra = {"kernel_ms": {k: round(v, 5) for k, v in kt.items()},
              "step_ms_with_kernel_events": round(ms_ev, 4), "step_us_percentiles": pct}
@@ -694,6 +727,18 @@ def main():
         extra["fp8_misa_dagger_tokens_per_s"] = p5.tokens_indexed() / (ms5 * 1e-3)
         extra["fp8_dense_dsa_ms"] = round(ms5d, 4)
         del r5
+        torch.cuda.empty_cache()
+        log("[bench] prefill chunk at L=128K (4096 rows): routed and dense 64-head steps")
+        pl = prefill_measure(torch, "c3x", h, 10, 2)
+        extra["prefill_c3x"] = {
+            "workload": pl["config"]["workload"], "ms_per_step": pl["ms_per_step"],
+            "pairs_per_s": pl["value"], "dense_ms": pl["extra"]["dense_ms"],
+            "speedup_vs_dense": pl["extra"]["speedup_vs_dense"],
+            "kernel_ms": pl["extra"]["kernel_ms"],
+            "score_prefill_kernel_tflops": pl["roofline"]["achieved"],
+            "score_prefill_kernel_mfma_frac": pl["roofline"]["frac"],
+            "mfma_peak_tflops": pl["roofline"]["peak"],
+            "dense_score_tflops": pl["extra"]["dense_score_tflops"]}
 
     cpu = None
     if not args.no_cpu_baseline:

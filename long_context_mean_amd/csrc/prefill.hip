@@ -11,9 +11,12 @@
 // times the key matrix [d, L].  One workgroup (4 wavefronts) owns 256 such
 // head rows (256 / HP query rows) and one slice of the key range; each
 // wavefront keeps its 4 row tiles of v_mfma_f32_16x16x32_bf16 A operands in
-// registers for the whole slice.  Key tiles of 64 keys are read with flat
-// 16-byte loads into a double-buffered padded LDS tile (one barrier per tile)
-// and each B fragment read from LDS feeds 4 MFMAs.  The epilogue applies
+// registers for the whole slice.  Key tiles of 64 keys stream into a
+// three-stage LDS ring by direct-to-LDS buffer loads (buffer_load ... lds,
+// 16 bytes per lane, no VGPR round trip); each lane's source offset is
+// XOR-swizzled so the B-fragment reads of a tile are free of bank conflicts,
+// an explicit vmcnt wait and one barrier hand a stage to the MFMAs, and each
+// B fragment read from LDS feeds 4 MFMAs.  The epilogue applies
 // ReLU, multiplies by the head weight, sums the HP rows of each query row
 // (in-lane, then across lane groups) and writes the order key of every
 // causally visible (row, key) pair; tiles away from the causal diagonal store

@@ -50,6 +50,8 @@ def _load():
     lib.misa_ref_sparse_attention.argtypes = [P, I, P, I, P, P] + [I] * 7 + [ctypes.c_double,
                                                                               P, P]
     lib.misa_ref_max_threads.argtypes = []
+    lib.misa_ref_set_threads.argtypes = [I]
+    lib.misa_ref_set_threads.restype = None
     for f in ("misa_ref_decode", "misa_ref_pool_keys", "misa_ref_route_heads",
               "misa_ref_scores", "misa_ref_score_topk", "dsa_ref_score_topk",
               "misa_ref_rerank", "misa_ref_sparse_attention", "misa_ref_score_topk_blocks",
@@ -95,6 +97,11 @@ def _args(p):
 
 def max_threads() -> int:
     return lib().misa_ref_max_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads of the caller's later oracle calls (OpenMP)."""
+    lib().misa_ref_set_threads(int(n))
 
 
 def decode(src: np.ndarray, dt: int, scale=None) -> np.ndarray:

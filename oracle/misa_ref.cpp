@@ -157,6 +157,10 @@ extern "C" {
 
 int misa_ref_max_threads(void) { return omp_get_max_threads(); }
 
+void misa_ref_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+}
+
 int misa_ref_decode(const void* src, const float* scale, int dt, int64_t rows, int d,
                     double* out) {
   if (!src || !out || (dt == DT_E4M3 && !scale)) return 1;

@@ -138,6 +138,10 @@ int misa_ref_sparse_attention(const void* q, int q_dt, const void* kv, int kv_dt
 /* Threads the OpenMP runtime will use. */
 int misa_ref_max_threads(void);
 
+/* Threads for the calling thread's later calls (n > 0; timing of the
+ * one-thread baseline). */
+void misa_ref_set_threads(int n);
+
 #ifdef __cplusplus
 }
 #endif

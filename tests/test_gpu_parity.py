@@ -82,6 +82,18 @@ def check_misa(p, h=None, topk=None, rows=None, page_size=0, ws=None):
     extra = fp8_mfma_error_bound(ps, heads[rows]) if fp8_gemm(p) and not page_size else None
     swapped = check_topk(idx[rows], sc[rows], ref_sc, topk, ps.visible(), extra=extra)
     log(f"[misa] {p.name}: head rows differing at near-ties {differing}, token swaps {swapped}")
+    if extra is not None:
+        # how much of the e4m3 matrix-core bound the scores actually use
+        errs, used = [], []
+        for i, n in enumerate(rows):
+            sel = idx[n][idx[n] >= 0]
+            e = np.abs(sc[n][:len(sel)].astype(np.float64) - ref_sc[i, sel])
+            b = extra[i, sel]
+            errs.append(np.max(e / (tol(ref_sc[i, sel]) + b)))
+            if (b > 0).any():
+                used.append(np.max(e[b > 0] / b[b > 0]))
+        log(f"[misa] {p.name}: max |gpu - oracle| / (tol + fp8 bound) {max(errs):.3g}; "
+            f"max |gpu - oracle| / fp8 bound {max(used) if used else 0:.3g}")
     return dp, heads, idx
 
 

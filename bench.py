@@ -530,7 +530,7 @@ def prefill_measure(torch, workload, h, steps, warmup):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1) if tflops else None,
                      "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4) if tflops else None,
-                     "traffic": measured_traffic("score_prefill_kernel", args.workload),
+                     "traffic": measured_traffic("score_prefill_kernel", workload),
                      "kernel": "score_prefill_kernel", "kernel_ms": sc_ms,
                      "algorithmic_flop_per_launch": flops},
         "extra": {"kernel_ms": {k: round(v, 4) for k, v in kt.items()},

@@ -777,6 +777,33 @@ def test_rows_longer_than_lds_bitmap():
     _exact_misa(p, rows=np.r_[0:3, 125:128])
 
 
+@pytest.mark.parametrize("k_dt,start", [(synth.BF16, 0), (synth.FP8, 20000), (synth.BF16, 37000)])
+def test_decode_topk_concentrated_in_one_stretch(k_dt, start):
+    """Every positive score lies in one stretch of 1800 tokens (keys elsewhere
+    give every head a negative dot, score 0): the scoring workgroups holding
+    the stretch have more winners than their candidate cut keeps, so the
+    decode selection must notice it and take the full radix path; the rest
+    of the top-k are zero-score ties won by the lowest indices.  Bit-exact."""
+    L, N = 40000, 2
+    p = synth.integer_problem("stretch", 68, N=N, S=N, L=L, d=128, H_I=8, h=4, B=128,
+                              topk=2048, k_dt=k_dt)
+    rng = np.random.default_rng(68)
+    k32 = -np.ones((N, L, 128), np.float64)
+    k32[:, start:start + 1800] = rng.integers(0, 4, size=(N, 1800, 128))
+    k = synth.f64_to_e4m3_codes(k32) if k_dt == synth.FP8 else synth.f32_to_bf16_bits(
+        k32.astype(np.float32))
+    q = synth.f32_to_bf16_bits(rng.integers(1, 3, size=(N, 8, 128)).astype(np.float32))
+    w = rng.integers(1, 4, size=(N, 8)).astype(np.float32)
+    p = synth.Problem(p.name, q, synth.BF16, w, k, k_dt, p.k_scale, p.q_seq, p.q_pos, p.B, p.h,
+                      p.topk, p.k_prime)
+    dp = _exact_misa(p)
+    h2, _, idx2, sc2 = (np_(t) for t in dp.route_score_topk(dp.pool()))
+    heads, _ = dp.route(dp.pool())
+    idx, sc = dp.score_topk(heads)
+    assert np.array_equal(np_(idx), idx2) and np.array_equal(np_(sc).view(np.uint32),
+                                                             sc2.view(np.uint32))
+
+
 @pytest.mark.parametrize("N", [3, 130])
 def test_all_scores_tied(N):
     """Zero keys: every score is 0, the threshold bin holds every token (more

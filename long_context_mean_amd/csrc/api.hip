@@ -85,7 +85,7 @@ int32_t check_pool(const void* k, const float* k_scale, int32_t k_dt, int32_t S,
 struct TopkLayout {
   bool one_row = false;
   int u_stride = 0;
-  size_t off_hist = 0, off_wg_head = 0, off_wg_cand = 0, bytes = 0;
+  size_t off_hist = 0, bytes = 0;
 };
 
 TopkLayout topk_layout(int N, int len_max) {
@@ -97,23 +97,9 @@ TopkLayout topk_layout(int N, int len_max) {
   if (!t.one_row) {
     t.off_hist = off;
     off = align_up(off + misa::topk_few_rows_bytes(N, t.u_stride), 256);
-    // the scoring workgroups' candidates: headers [N, kWgMax], slots [N, kWgSlots]
-    t.off_wg_head = off;
-    off = align_up(off + static_cast<size_t>(N) * misa::kWgMax * 8, 256);
-    t.off_wg_cand = off;
-    off = align_up(off + static_cast<size_t>(N) * misa::kWgSlots * 8, 256);
   }
   t.bytes = off;
   return t;
-}
-
-// Few long rows select from the streaming scoring kernel's per-workgroup
-// candidates (one selection launch, no row-wide histogram) when keys are
-// bf16 or e4m3, k <= 2048 and rows have at most 2^18 tokens (the winner
-// bitmap lives in LDS); otherwise collect + final over the histogram.
-bool wg_topk(const TopkLayout& lay, int L, int topk, int k_dt) {
-  return !lay.one_row && k_dt != MISA_F32 && topk <= 2048 && L <= (1 << 18) &&
-         misa::score_workgroups_per_row(L, false) <= misa::kWgMax;
 }
 
 // Candidate path region, placed after the full-path layout.
@@ -383,10 +369,7 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* q_scale, const
   }
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint32_t* u = reinterpret_cast<uint32_t*>(base);
-  const bool wg = wg_topk(lay, L, topk, k_dt);
-  uint32_t* hist = lay.one_row || wg ? nullptr : reinterpret_cast<uint32_t*>(base + lay.off_hist);
-  uint2* wg_head = wg ? reinterpret_cast<uint2*>(base + lay.off_wg_head) : nullptr;
-  uint2* wg_cand = wg ? reinterpret_cast<uint2*>(base + lay.off_wg_cand) : nullptr;
+  uint32_t* hist = lay.one_row ? nullptr : reinterpret_cast<uint32_t*>(base + lay.off_hist);
   hipError_t e = hipSuccess;
   if (hist && !fr) e = misa::launch_clear(hist, static_cast<size_t>(N) * misa::kHistWords, st);
   if (e != hipSuccess) return hip_status(e);
@@ -450,9 +433,6 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* q_scale, const
   } else {
     misa::ScoreArgs sa{q, q_dt, w, k, k_scale, k_dt, q_seq, q_pos, heads, nullptr,
                        N, S, L, d, H_I, h, 0, u, lay.u_stride, hist, ki};
-    sa.wg_head = wg_head;
-    sa.wg_cand = wg_cand;
-    sa.wg_topk = topk;
     if (fr) {
       sa.route_partial = fr->partial;
       sa.route_nchunks = fr->nchunks;
@@ -465,9 +445,6 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* q_scale, const
   if (e != hipSuccess) return hip_status(e);
   misa::TopkArgs ta{u, lay.u_stride, q_pos, 0, N, topk, lay.one_row, hist,
                     nullptr, 0, idx, score};
-  ta.wg_head = wg_head;
-  ta.wg_cand = wg_cand;
-  ta.wg_nwg = misa::score_workgroups_per_row(L, false);
   return hip_status(misa::launch_topk(ta, st));
 }
 
@@ -671,9 +648,7 @@ int32_t misa_route_score_topk(const void* q, int32_t q_dt, const float* q_scale,
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   const TopkLayout lay = topk_layout(N, L);
-  uint32_t* hist = lay.one_row || wg_topk(lay, L, topk, k_dt)
-                       ? nullptr
-                       : reinterpret_cast<uint32_t*>(wsb + rb + lay.off_hist);
+  uint32_t* hist = lay.one_row ? nullptr : reinterpret_cast<uint32_t*>(wsb + rb + lay.off_hist);
   const int nchunks = route_chunks(L, B);
   float* partial = reinterpret_cast<float*>(wsb);
   misa::RouteArgs a{q, q_dt, nullptr, w, kbar, k, k_scale, k_dt, q_seq, q_pos, N, S, L, d, B,
@@ -731,9 +706,7 @@ int32_t misa_pool_route_score_topk(const void* q, int32_t q_dt, const float* q_s
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   const TopkLayout lay = topk_layout(N, L);
-  uint32_t* hist = lay.one_row || wg_topk(lay, L, topk, k_dt)
-                       ? nullptr
-                       : reinterpret_cast<uint32_t*>(wsb + rb + lay.off_hist);
+  uint32_t* hist = lay.one_row ? nullptr : reinterpret_cast<uint32_t*>(wsb + rb + lay.off_hist);
   const int nchunks = route_chunks(L, B);
   float* partial = reinterpret_cast<float*>(wsb);
   misa::RouteArgs a{q, q_dt, nullptr, w, kbar, k, k_scale, k_dt, q_seq, q_pos, N, S, L, d, B,

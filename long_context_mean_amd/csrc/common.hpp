@@ -18,31 +18,6 @@ constexpr int kShift1 = kShift0 - kDigit1Bits;            // 8
 constexpr int kHistWords = kBins0 + 64;
 constexpr int kCandCountOffset = kBins0;
 
-// Decode top-k from per-workgroup candidates: every scoring workgroup of a
-// row writes the keys of its top bins (at least wg_tmin of its keys when it
-// has that many, at most wg_cap) into its own slots, and one selection
-// workgroup per row takes the exact top-k from them.  A row has nwr scoring
-// workgroups (kWgMax at most) sharing kWgSlots slots.
-constexpr int kWgMax = 1024;
-constexpr int kWgSlots = 16384;
-
-// Slots per workgroup (a power of two, at most 1024 = the keys one
-// workgroup scores) and the count of its top keys it must write: three times
-// its share of the k wanted, at least 48 (a workgroup of 1024 uniformly
-// placed keys holds 16 of a 2048-of-131072 selection on average, with a
-// standard deviation of 4).
-__host__ __device__ __forceinline__ int wg_cap(int nwr) {
-  int c = 1024;
-  while (c > 16 && c * nwr > kWgSlots) c >>= 1;
-  return c;
-}
-__host__ __device__ __forceinline__ int wg_tmin(int nwr, int topk) {
-  const int cap = wg_cap(nwr);
-  int t = (3 * topk + nwr - 1) / nwr;
-  t = t < 48 ? 48 : t;
-  return t < cap ? t : cap;
-}
-
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;

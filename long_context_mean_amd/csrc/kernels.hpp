@@ -130,16 +130,7 @@ struct ScoreArgs {
   int route_nchunks = 0, B = 0;
   int32_t* heads_out = nullptr;
   float* head_score_out = nullptr;
-  // decode candidate mode (few long rows, no cand, bf16 or e4m3 keys; hist0
-  // NULL): each workgroup writes its top keys to wg_cand [N, kWgSlots] and
-  // (count, cutoff key) to wg_head [N, kWgMax] for the top-wg_topk selection
-  uint2* wg_head = nullptr;
-  uint2* wg_cand = nullptr;
-  int wg_topk = 0;
 };
-// Workgroups per row of the streaming scoring launch (decode candidate mode
-// needs at most kWgMax of them).
-int score_workgroups_per_row(int len_max, bool cand);
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------- fp8 queries
@@ -210,12 +201,6 @@ struct TopkArgs {
   int32_t* idx;
   float* score;
   const uint32_t* row_flag = nullptr;   // one-row mode: rows whose flag is 0 are skipped
-  // few-rows mode from the scoring kernel's per-workgroup candidates (see
-  // ScoreArgs::wg_cand): one selection workgroup per row, the full radix
-  // path over u when the candidates cannot prove the result
-  const uint2* wg_head = nullptr;
-  const uint2* wg_cand = nullptr;
-  int wg_nwg = 0;           // scoring workgroups per row of that launch
 };
 int topk_chunk();
 size_t topk_few_rows_bytes(int N, int u_stride);

@@ -32,7 +32,6 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "route_select.hpp"
-#include "select.hpp"
 
 namespace misa {
 namespace {
@@ -58,9 +57,6 @@ struct ScoreParams {
   int route_nchunks, B;
   int32_t* heads_out;
   float* head_score_out;
-  uint2* wg_head;               // decode candidate mode (see ScoreArgs)
-  uint2* wg_cand;
-  int wg_topk;
 };
 
 template <int KT, int D>
@@ -182,8 +178,7 @@ __device__ __forceinline__ void score_group(const RawGroup<KT, D, U>& raw, const
                                             int lane,
                                             const bf16x8_t (&a)[NT][KeyLayout<KT, D>::KK],
                                             const float (&wv)[NT][4], int g, int c, int len,
-                                            uint32_t* urow, uint32_t* lh, bool do_hist,
-                                            uint32_t* ukw, int ord0) {
+                                            uint32_t* urow, uint32_t* lh, bool do_hist) {
   using LY = KeyLayout<KT, D>;
   constexpr int KK = LY::KK;
   const int rsub = lane / LY::LANES_PER_ROW, q = lane % LY::LANES_PER_ROW;
@@ -217,88 +212,32 @@ __device__ __forceinline__ void score_group(const RawGroup<KT, D, U>& raw, const
         part += wv[nt][i] * fmaxf(v, 0.f);
       }
     }
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
+    // the four lane groups' partial head sums: lanes 16 apart, then 32 apart
+    // (gfx950 lane swaps; a + b is the same in either lane of a pair)
+    {
+      const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part),
+                                                        __float_as_uint(part), false, false);
+      part = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
+                                                        __float_as_uint(part), false, false);
+      part = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+    }
     const int e = (tile0 + t * tstride) * 16 + c;
-    if (g == 0) {
-      const bool ok = ((valid >> t) & 1u) && e < len;
+    if (g == 0 && e < len) {
+      const bool ok = (valid >> t) & 1u;
       const uint32_t key = ok ? order_key(part) : 0u;
-      if (e < len) urow[e] = key;
+      urow[e] = key;
       if (do_hist && ok) atomicAdd(&lh[key >> kShift0], 1u);
-      if (ukw) ukw[(ord0 + t) * 16 + c] = key;       // the workgroup's own keys
     }
   }
-}
-
-// Decode candidate mode, after a workgroup has scored all its tiles: from its
-// local histogram (lh, complete) the bin holding its wg_tmin-th largest key;
-// its keys of that bin and above (below wg_cap of them, else only those above
-// the bin; all of them when they fit) go to its candidate slots, with a header
-// (count, cutoff key): every key of the workgroup at or above the cutoff is a
-// candidate (cutoff 0: all of them).  ukeys holds each wavefront's keys in
-// tile order (0 = empty); wtile / wtiles: the wavefront's first tile and
-// tile count.  Every thread calls it.
-__device__ __forceinline__ void wg_candidates(const uint32_t* lh, const uint32_t* ukeys,
-                                              int ntiles, int topk, int wtile, int wtiles,
-                                              int tstride, uint2* head, uint2* slots,
-                                              uint32_t* sm, uint32_t* res, uint32_t* wcnt) {
-  const int nwr = min(static_cast<int>(gridDim.x), (ntiles + 3) >> 2);
-  const int cap = wg_cap(nwr);
-  find_digit<256, kBins0>(lh, static_cast<uint32_t>(wg_tmin(nwr, topk)), true, sm, res);
-  const uint32_t d = res[0], rank = res[1], K = res[2], total = res[3];
-  uint32_t cut = 1u, hcut = 0u;                     // every valid key, no constraint
-  if (total > static_cast<uint32_t>(cap)) {
-    const uint32_t ge = (K - rank) + lh[d];          // keys in bins >= d
-    cut = ge <= static_cast<uint32_t>(cap) ? (d << kShift0)
-          : d + 1 < static_cast<uint32_t>(kBins0) ? ((d + 1) << kShift0) : 0xFFFFFFFFu;
-    hcut = cut;
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t* kw = ukeys + wave * 256;
-  const int nk = wtiles * 16;
-  uint32_t mine = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int sidx = lane + 64 * i;
-    mine += (sidx < nk && kw[sidx] >= cut) ? 1u : 0u;
-  }
-  const uint32_t incl = wave_incl_scan(mine);
-  if (lane == 63) wcnt[wave] = incl;
-  __syncthreads();
-  uint32_t pos = incl - mine;
-  uint32_t tot = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    pos += w < wave ? wcnt[w] : 0u;
-    tot += wcnt[w];
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int sidx = lane + 64 * i;
-    if (sidx < nk) {
-      const uint32_t key = kw[sidx];
-      if (key >= cut) {
-        const int tok = (wtile + (sidx >> 4) * tstride) * 16 + (sidx & 15);
-        // (pos < cap always holds for finite scores; the bound keeps NaN
-        // inputs, whose keys can reach the cutoff sentinel, in the slots)
-        if (pos < static_cast<uint32_t>(cap))
-          slots[blockIdx.x * cap + pos] = make_uint2(key, static_cast<uint32_t>(tok));
-        ++pos;
-      }
-    }
-  }
-  if (threadIdx.x == 0) head[blockIdx.x] = make_uint2(tot, hcut);
 }
 
 template <int KT, int NT, int D, int U, bool CAND, bool ROUTE>
 __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
   using LY = KeyLayout<KT, D>;
   constexpr int KK = LY::KK;
-  __shared__ __align__(16) uint32_t lh[kBins0];
+  __shared__ uint32_t lh[kBins0];
   __shared__ __align__(16) uint8_t tiles[4][LY::TILE_LDS];
-  // decode candidate mode: each wavefront's keys in tile order (at most 16 tiles)
-  __shared__ uint32_t ukeys[CAND ? 1 : 4 * 256];
-  __shared__ uint32_t wsm[4], wres[4], wcnt[4];
   __shared__ int32_t heads_lds[ROUTE ? 64 : 1];
   __shared__ __align__(16) uint16_t qlds[ROUTE ? 64 * D : 8];   // the row's query heads
   __shared__ float wlds[ROUTE ? 64 : 1];                          // and their weights
@@ -314,9 +253,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int g = lane >> 4, c = lane & 15;
-  const bool wgc = !CAND && p.wg_cand != nullptr;
-  const bool do_hist = p.hist0 != nullptr || wgc;
-  uint32_t* ukw = wgc ? ukeys + (threadIdx.x >> 6) * 256 : nullptr;
+  const bool do_hist = p.hist0 != nullptr;
 
   const int s = p.q_seq[n];
   const uint8_t* kseq = p.k;                           // rows addressed through p.ki
@@ -446,11 +383,11 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
       vb = issue_group<KT, D, U, CAND>(rb, sb, t0 + gstep, tstride, lane, c, len, crow, kseq,
                                        sseq, p.ki, s, o0 + U, page_v);
       score_group<KT, NT, D, U>(ra, sa, va, t0, tstride, tile, lane, a, wv, g, c, len, urow,
-                                lh, do_hist, ukw, o0);
+                                lh, do_hist);
       va = issue_group<KT, D, U, CAND>(ra, sa, t0 + 2 * gstep, tstride, lane, c, len, crow,
                                        kseq, sseq, p.ki, s, o0 + 2 * U, page_v);
       score_group<KT, NT, D, U>(rb, sb, vb, t0 + gstep, tstride, tile, lane, a, wv, g, c, len,
-                                urow, lh, do_hist, ukw, o0 + U);
+                                urow, lh, do_hist);
       t0 += 2 * gstep;
       o0 += 2 * U;
       left -= 2;
@@ -459,20 +396,15 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
       vb = issue_group<KT, D, U, CAND>(rb, sb, t0 + gstep, tstride, lane, c, len, crow, kseq,
                                        sseq, p.ki, s, o0 + U, page_v);
       score_group<KT, NT, D, U>(ra, sa, va, t0, tstride, tile, lane, a, wv, g, c, len, urow,
-                                lh, do_hist, ukw, o0);
+                                lh, do_hist);
       score_group<KT, NT, D, U>(rb, sb, vb, t0 + gstep, tstride, tile, lane, a, wv, g, c, len,
-                                urow, lh, do_hist, ukw, o0 + U);
+                                urow, lh, do_hist);
     } else {
       score_group<KT, NT, D, U>(ra, sa, va, t0, tstride, tile, lane, a, wv, g, c, len, urow,
-                                lh, do_hist, ukw, o0);
+                                lh, do_hist);
     }
   }
-  if (wgc) {
-    __syncthreads();
-    wg_candidates(lh, ukeys, ntiles, p.wg_topk, wtile, wtiles, tstride,
-                  p.wg_head + static_cast<size_t>(n) * kWgMax,
-                  p.wg_cand + static_cast<size_t>(n) * kWgSlots, wsm, wres, wcnt);
-  } else if (do_hist) {
+  if (do_hist) {
     __syncthreads();
     uint32_t* hg = p.hist0 + static_cast<size_t>(n) * kHistWords;
     for (int b = threadIdx.x; b < kBins0; b += 256) {
@@ -571,9 +503,6 @@ hipError_t launch_mfma(const ScoreArgs& a, hipStream_t st, int tiles_per_wave) {
   p.B = a.B;
   p.heads_out = a.heads_out;
   p.head_score_out = a.head_score_out;
-  p.wg_head = a.wg_head;
-  p.wg_cand = a.wg_cand;
-  p.wg_topk = a.wg_topk;
   if (a.route_partial) p.nrows = a.h;
   const int maxlen = a.cand ? a.ncols : a.L;
   const int per_wg = 4 * tiles_per_wave * 16;
@@ -599,18 +528,7 @@ hipError_t launch_mfma_rows(const ScoreArgs& a, hipStream_t st, int tpw) {
   return launch_mfma<KT, 4, D>(a, st, tpw);
 }
 
-// Tiles (of 16 keys) per wavefront; short candidate lists use smaller chunks
-// so more workgroups share the gather (at most 64 tiles per wavefront: the
-// paged path keeps one page number per lane; at most 16 in the decode
-// candidate mode, whose key slots hold 16 tiles per wavefront).
-int tiles_per_wave(bool cand) { return cand ? 4 : 16; }
-
 }  // namespace
-
-int score_workgroups_per_row(int len_max, bool cand) {
-  const int per_wg = 4 * tiles_per_wave(cand) * 16;
-  return (len_max + per_wg - 1) / per_wg;
-}
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
   if (a.k_dt == DT_F32) {
@@ -629,10 +547,10 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
                   a.hist0, a.kidx);
     return hipGetLastError();
   }
-  const int tpw = tiles_per_wave(a.cand != nullptr);
-  if (a.wg_cand && (a.cand || a.hist0 || tpw > 16 ||
-                    score_workgroups_per_row(a.L, false) > kWgMax))
-    return hipErrorInvalidValue;
+  // tiles (of 16 keys) per wavefront; short candidate lists use smaller
+  // chunks so more workgroups share the gather (at most 64 tiles per
+  // wavefront: the paged path keeps one page number per lane)
+  const int tpw = a.cand ? 4 : 16;
   if (a.k_dt == DT_BF16)
     return a.d == 64 ? launch_mfma_rows<DT_BF16, 64>(a, st, tpw)
                      : launch_mfma_rows<DT_BF16, 128>(a, st, tpw);

@@ -24,7 +24,6 @@
 //    workgroup per row with every histogram in LDS.
 #include "common.hpp"
 #include "kernels.hpp"
-#include "select.hpp"
 
 namespace misa {
 namespace {
@@ -33,6 +32,64 @@ constexpr int kChunk = 4096;          // elements per collect workgroup
 constexpr int kPerThread = 16;        // contiguous elements per thread per tile
 constexpr int kCandCap = 8192;        // candidates resolved in LDS
 constexpr int kBitmapWords = 8192;    // rows up to 262144 elements use the LDS bitmap
+
+// Finds the bin of a histogram (NBINS bins, bin NBINS-1 = largest keys) that
+// holds the K-th largest element.  With clamp_total, K = min(K, total) first.
+// All NT threads call it; results in `res`: [0] digit, [1] rank inside the
+// digit's bin (1-based), [2] K, [3] total.  K == 0 leaves digit/rank 0.
+template <int NT, int NBINS>
+__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t K, bool clamp_total, uint32_t* sm,
+                           uint32_t* res) {
+  constexpr int PER = NBINS >= NT ? NBINS / NT : 1;
+  const int t = static_cast<int>(threadIdx.x);
+  const bool owner = NBINS >= NT || t < NBINS;
+  const int lo = NBINS - (t + 1) * PER;                 // this thread's lowest bin
+  uint32_t v[PER];
+  if (owner) {
+    if constexpr (PER % 4 == 0) {
+      const uint4* p4 = reinterpret_cast<const uint4*>(hist + lo);
+#pragma unroll
+      for (int q = 0; q < PER / 4; ++q) {
+        const uint4 x = p4[q];
+        v[4 * q] = x.x;
+        v[4 * q + 1] = x.y;
+        v[4 * q + 2] = x.z;
+        v[4 * q + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < PER; ++q) v[q] = hist[lo + q];
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) v[q] = 0u;
+  }
+  uint32_t c = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) c += v[q];
+  uint32_t total;
+  const uint32_t above = block_excl_scan<NT>(c, sm, total);
+  if (clamp_total && K > total) K = total;
+  if (t == 0) {
+    res[0] = 0;
+    res[1] = 0;
+    res[2] = K;
+    res[3] = total;
+  }
+  __syncthreads();
+  if (K > 0 && above < K && K <= above + c) {
+    uint32_t acc = above;
+#pragma unroll
+    for (int q = PER - 1; q >= 0; --q) {
+      if (acc < K && acc + v[q] >= K) {
+        res[0] = static_cast<uint32_t>(lo + q);
+        res[1] = K - acc;
+      }
+      acc += v[q];
+    }
+  }
+  __syncthreads();
+}
 
 // Ties at the threshold: among the n_eq candidates whose key equals T, the K2
 // lowest token indices win (K2 <= n_eq).  Returns the largest winning index.
@@ -373,181 +430,6 @@ __global__ __launch_bounds__(1024) void topk_final_kernel(
       }
     }
     base_pos += tot;
-  }
-}
-
-// ---------------------------------------------------------------- few long rows, workgroup candidates
-// One 1024-thread workgroup per row selects from the candidates the scoring
-// workgroups wrote (each: its keys at or above its cutoff, see the scoring
-// kernel).  With T the exact K-th largest candidate: every key of the row at
-// or above T is a candidate whenever T is at least every workgroup's cutoff,
-// so the candidates' top-K is the row's, ties at T included (lowest token
-// indices win).  Otherwise (or with fewer than K candidates) the workgroup
-// runs the full radix select over the row's order keys u.  Rows of at most
-// 2^18 tokens and K <= 2048 (the winner bitmap and the staged outputs live in
-// LDS).
-constexpr int kWgPer = kWgSlots / 1024;       // candidate slots per thread
-
-__global__ __launch_bounds__(1024) void topk_wgcand_kernel(
-    const uint32_t* __restrict__ u, int u_stride, const int32_t* __restrict__ q_pos,
-    int fixed_len, const uint2* __restrict__ head, const uint2* __restrict__ cand, int nwg,
-    int topk, int32_t* __restrict__ idx, float* __restrict__ score) {
-  __shared__ __align__(16) uint32_t bm[kBitmapWords];     // winners; fallback: level-1 histogram
-  __shared__ __align__(16) uint16_t wpre[kBitmapWords];   // marked bits before each word (per thread)
-  __shared__ __align__(16) uint32_t hA[kBins0];           // histograms, then the staged outputs
-  __shared__ __align__(16) uint32_t hB[kBins2];
-  __shared__ uint32_t hcnt[kWgMax];
-  __shared__ uint32_t tpre[1024];
-  __shared__ uint32_t ci[kWgSlots];                       // candidate token of slot tid + NT * i
-  __shared__ uint32_t sm[16];
-  __shared__ uint32_t res[4];
-  __shared__ uint32_t cmax;
-  constexpr int NT = 1024;
-  const int n = blockIdx.x, tid = threadIdx.x;
-  const int len = row_len(q_pos, fixed_len, n);
-  const int nwr = min(nwg, ((len + 15) / 16 + 3) >> 2);  // scoring workgroups of this row
-  const int cap = wg_cap(nwr);
-  int lcap = 0;
-  while ((1 << lcap) < cap) ++lcap;
-  const uint32_t K = static_cast<uint32_t>(min(topk, len));
-  const uint32_t* row = u + static_cast<size_t>(n) * u_stride;
-  int32_t* idx_row = idx + static_cast<size_t>(n) * topk;
-  float* score_row = score ? score + static_cast<size_t>(n) * topk : nullptr;
-
-  // the headers and every slot of the row's workgroups in one round trip
-  // (slots past a workgroup's count hold stale data and are masked below)
-  uint2 hd = make_uint2(0u, 0u);
-  if (tid < nwr) hd = head[static_cast<size_t>(n) * kWgMax + tid];
-  const uint2* crow = cand + static_cast<size_t>(n) * kWgSlots;
-  const int nslots = nwr * cap;
-  uint32_t ck[kWgPer];
-  uint2 ce[kWgPer];
-#pragma unroll
-  for (int i = 0; i < kWgPer; ++i) {
-    const int s = tid + NT * i;
-    ce[i] = crow[s < nslots ? s : 0];
-  }
-#pragma unroll
-  for (int i = 0; i < kWgPer; ++i) {
-    ck[i] = ce[i].x;
-    ci[tid + NT * i] = ce[i].y;
-  }
-  if (tid == 0) cmax = 0u;
-  if (tid < nwr) hcnt[tid] = hd.x;
-  for (int b = tid; b < kBins0; b += NT) hA[b] = 0u;
-  if (tid < kBins2) hB[tid] = 0u;
-  __syncthreads();
-  if (tid < nwr && hd.y) atomicMax(&cmax, hd.y);
-#pragma unroll
-  for (int i = 0; i < kWgPer; ++i) {
-    const int s = tid + NT * i;
-    if (s >= nslots || static_cast<uint32_t>(s & (cap - 1)) >= hcnt[s >> lcap]) ck[i] = 0u;
-  }
-  const uint32_t total = block_sum<NT>(tid < nwr ? hd.x : 0u, sm);
-  bool ok = total >= K;
-  uint32_t T = 0, K2 = 0, n_eq = 0;
-  if (ok && K > 0) {
-    // exact threshold among the candidates: three radix levels
-#pragma unroll
-    for (int i = 0; i < kWgPer; ++i)
-      if (ck[i] != 0u) atomicAdd(&hA[ck[i] >> kShift0], 1u);
-    __syncthreads();
-    find_digit<NT, kBins0>(hA, K, false, sm, res);
-    const uint32_t d0 = res[0], r0 = res[1];
-    for (int b = tid; b < kBins1; b += NT) hA[b] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kWgPer; ++i)
-      if (ck[i] != 0u && (ck[i] >> kShift0) == d0)
-        atomicAdd(&hA[(ck[i] >> kShift1) & (kBins1 - 1)], 1u);
-    __syncthreads();
-    find_digit<NT, kBins1>(hA, r0, false, sm, res);
-    const uint32_t d1 = res[0], r1 = res[1];
-    const uint32_t pre = (d0 << kDigit1Bits) | d1;
-#pragma unroll
-    for (int i = 0; i < kWgPer; ++i)
-      if (ck[i] != 0u && (ck[i] >> kShift1) == pre) atomicAdd(&hB[ck[i] & (kBins2 - 1)], 1u);
-    __syncthreads();
-    find_digit<NT, kBins2>(hB, r1, false, sm, res);
-    T = (d0 << kShift0) | (d1 << kShift1) | res[0];
-    K2 = res[1];
-    n_eq = hB[res[0]];
-    ok = T >= cmax;                   // every key >= T is a candidate
-    __syncthreads();
-  }
-  if (!ok) {
-    row_select<NT>(row, len, topk, nullptr, idx_row, score_row, hA, bm, hB, false, sm, res);
-    return;
-  }
-  if (K == 0) {
-    for (int i = tid; i < topk; i += NT) {
-      idx_row[i] = -1;
-      if (score_row) score_row[i] = -__builtin_inff();
-    }
-    return;
-  }
-  // ties at T: the K2 lowest token indices win (radix select on the indices,
-  // below 2^18: bits 6..17, then 0..5)
-  uint32_t cut = 0xFFFFFFFFu;
-  if (n_eq != K2) {
-    for (int b = tid; b < kBins0; b += NT) hA[b] = 0u;
-    if (tid < 64) hB[tid] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kWgPer; ++i)
-      if (ck[i] == T) atomicAdd(&hA[ci[tid + NT * i] >> 6], 1u);
-    __syncthreads();
-    find_digit<NT, kBins0>(hA, n_eq - K2 + 1u, false, sm, res);
-    const uint32_t dA = res[0], rA = res[1];
-#pragma unroll
-    for (int i = 0; i < kWgPer; ++i)
-      if (ck[i] == T && (ci[tid + NT * i] >> 6) == dA) atomicAdd(&hB[ci[tid + NT * i] & 63u], 1u);
-    __syncthreads();
-    find_digit<NT, 64>(hB, rA, false, sm, res);
-    cut = (dA << 6) | res[0];
-  }
-  const int nwords = (len + 31) / 32;
-  for (int w = tid; w < nwords; w += NT) bm[w] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kWgPer; ++i)
-    if (ck[i] > T || (ck[i] == T && ck[i] != 0u && ci[tid + NT * i] <= cut))
-      atomicOr(&bm[ci[tid + NT * i] >> 5], 1u << (ci[tid + NT * i] & 31));
-  __syncthreads();
-  // output position of a winner = marked bits before it: thread prefix over
-  // wpt consecutive words, plus a prefix inside the thread's words
-  const int wpt = (nwords + NT - 1) / NT;
-  uint32_t mine = 0;
-  for (int q = 0; q < wpt; ++q) {
-    const int w = tid * wpt + q;
-    if (w < nwords) {
-      wpre[w] = static_cast<uint16_t>(mine);
-      mine += __popc(bm[w]);
-    }
-  }
-  uint32_t tot;
-  tpre[tid] = block_excl_scan<NT>(mine, sm, tot);
-  __syncthreads();
-  // winners to their output slots in LDS (hA: indices, then keys), then out
-  // in order with contiguous stores
-  uint32_t* oidx = hA;
-  uint32_t* okey = hA + kBins0 / 2;
-#pragma unroll
-  for (int i = 0; i < kWgPer; ++i) {
-    const uint32_t e = ci[tid + NT * i];
-    if (ck[i] == 0u || ck[i] < T) continue;
-    const int w = static_cast<int>(e >> 5);
-    const uint32_t word = bm[w];
-    if (!((word >> (e & 31)) & 1u)) continue;
-    const uint32_t pos = tpre[w / wpt] + wpre[w] + __popc(word & ((1u << (e & 31)) - 1u));
-    oidx[pos] = e;
-    okey[pos] = ck[i];
-  }
-  __syncthreads();
-  for (int i = tid; i < topk; i += NT) {
-    const bool sel = i < static_cast<int>(K);
-    idx_row[i] = sel ? static_cast<int32_t>(oidx[i]) : -1;
-    if (score_row) score_row[i] = sel ? key_score(okey[i]) : -__builtin_inff();
   }
 }
 
@@ -951,15 +833,6 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.one_row_per_block) {
     MISA_LAUNCH(K_TOPK_ROW, topk_row_kernel, dim3(a.N), dim3(1024), 0, st, a.u, a.u_stride,
                 a.q_pos, a.fixed_len, a.topk, a.cand, a.cand_stride, a.idx, a.score, a.row_flag);
-    return hipGetLastError();
-  }
-  if (a.wg_cand) {
-    if (a.topk > kBins0 / 2 || a.u_stride / 32 > kBitmapWords || a.wg_nwg < 1 ||
-        a.wg_nwg > kWgMax)
-      return hipErrorInvalidValue;
-    MISA_LAUNCH(K_TOPK_FINAL, topk_wgcand_kernel, dim3(a.N), dim3(1024), 0, st, a.u,
-                a.u_stride, a.q_pos, a.fixed_len, a.wg_head, a.wg_cand, a.wg_nwg, a.topk, a.idx,
-                a.score);
     return hipGetLastError();
   }
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };

@@ -226,6 +226,27 @@ int32_t misa_pool_route_score_topk(const void* q, int32_t q_dt, const float* q_s
                                    size_t ws_bytes, void* stream);
 
 /*
+ * misa_pool_route_score_topk for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments, results and errors, without ws/ws_bytes.
+ * Its scratch is a 32 MiB array the library holds on every GPU it runs on
+ * (until the process ends); a call whose workspace
+ * (misa_workspace_bytes(MISA_OP_ROUTE_SCORE_TOPK, ...)) exceeds 32 MiB
+ * returns MISA_ERR_WORKSPACE and launches nothing.  It calls no allocation
+ * routine (MISA_DEBUG_SYNC=1 copies its checks' inputs to host memory).
+ * Every call on one GPU uses that GPU's array: calls that overlap on one GPU
+ * (concurrent streams, several host threads) race and must be serialised by
+ * the caller.
+ */
+int32_t misa_pool_route_score_topk_scratch(
+    const void* q, int32_t q_dt, const float* q_scale, const float* w, float* kbar, const void* k,
+    const float* k_scale, int32_t k_dt, const int32_t* block_table, int32_t page_size,
+    const int32_t* q_seq, const int32_t* q_pos, const int32_t* len_old, const int32_t* len_new,
+    int32_t max_new, int32_t N, int32_t S, int32_t L, int32_t d, int32_t B, int32_t H_I,
+    int32_t h, int32_t topk, int32_t* heads, float* head_score, int32_t* idx, float* score,
+    void* stream);
+
+/*
  * Dense DSA indexer (the baseline MISA replaces: every one of the H_I heads
  * scores every prefix token, MISA abstract and "Problem statement"):
  * misa_score_topk with all H_I heads.

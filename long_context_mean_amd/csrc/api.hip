@@ -5,6 +5,7 @@
 
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 #include <utility>
 #include <vector>
 
@@ -448,6 +449,36 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* q_scale, const
   return hip_status(misa::launch_topk(ta, st));
 }
 
+// ---------------------------------------------------------------- static scratch
+// Device scratch of misa_pool_route_score_topk_scratch, for callers that
+// cannot allocate: one array per GPU the library runs on, held until the
+// process ends.  Host code never uses the array's name as an address: each
+// device's address comes from hipGetSymbolAddress, taken once per device with
+// that device current.
+constexpr size_t kScratchBytes = size_t{32} << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int32_t scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return MISA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return MISA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MISA_OK;
+}
+
 }  // namespace
 
 namespace misa {
@@ -723,6 +754,31 @@ int32_t misa_pool_route_score_topk(const void* q, int32_t q_dt, const float* q_s
   return score_topk_impl(q, q_dt, q_scale, w, k, k_scale, k_dt, block_table, page_size, q_seq,
                          q_pos, nullptr, N, S, L, d, H_I, h, topk, idx, score, wsb + rb, sb,
                          stream, &fr);
+}
+
+int32_t misa_pool_route_score_topk_scratch(
+    const void* q, int32_t q_dt, const float* q_scale, const float* w, float* kbar, const void* k,
+    const float* k_scale, int32_t k_dt, const int32_t* block_table, int32_t page_size,
+    const int32_t* q_seq, const int32_t* q_pos, const int32_t* len_old, const int32_t* len_new,
+    int32_t max_new, int32_t N, int32_t S, int32_t L, int32_t d, int32_t B, int32_t H_I,
+    int32_t h, int32_t topk, int32_t* heads, float* head_score, int32_t* idx, float* score,
+    void* stream) {
+  // the call's own checks first: with a zero-byte workspace (never touched)
+  // only its workspace check fails, after every other check, and nothing runs
+  int32_t rc = misa_pool_route_score_topk(
+      q, q_dt, q_scale, w, kbar, k, k_scale, k_dt, block_table, page_size, q_seq, q_pos, len_old,
+      len_new, max_new, N, S, L, d, B, H_I, h, topk, heads, head_score, idx, score,
+      reinterpret_cast<void*>(uintptr_t{256}), 0, stream);
+  if (rc != MISA_ERR_WORKSPACE) return rc;
+  const size_t need =
+      misa_workspace_bytes(MISA_OP_ROUTE_SCORE_TOPK, q_dt, N, L, d, H_I, B, topk, 0);
+  if (need > kScratchBytes) return MISA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((rc = scratch_of_current_device(&ws))) return rc;
+  return misa_pool_route_score_topk(q, q_dt, q_scale, w, kbar, k, k_scale, k_dt, block_table,
+                                    page_size, q_seq, q_pos, len_old, len_new, max_new, N, S, L,
+                                    d, B, H_I, h, topk, heads, head_score, idx, score, ws,
+                                    kScratchBytes, stream);
 }
 
 int32_t misa_rerank(const void* q, int32_t q_dt, const float* q_scale, const float* w,

@@ -269,3 +269,33 @@ def test_candidate_flags_offset():
     assert b.misa_candidate_flags_offset(4096, 20000, 2048) == -1    # short prefix
     assert b.misa_candidate_flags_offset(4096, 65536, 4096) == -1    # large k
     assert b.misa_candidate_flags_offset(0, 65536, 2048) == -1
+
+
+def _scratch_step(**over):
+    a = dict(q=FAKE, q_dt=1, qsc=None, w=FAKE, kbar=FAKE, k=FAKE, ks=None, k_dt=1, bt=None, ps=0,
+             qs=FAKE, qp=FAKE, lo=FAKE, hi=FAKE, max_new=1, N=4, S=4, L=1000, d=128, B=128,
+             H_I=64, h=8, topk=100, heads=FAKE, hs=None, idx=FAKE, score=None)
+    a.update(over)
+    return b.lib().misa_pool_route_score_topk_scratch(
+        a["q"], a["q_dt"], a["qsc"], a["w"], a["kbar"], a["k"], a["ks"], a["k_dt"], a["bt"],
+        a["ps"], a["qs"], a["qp"], a["lo"], a["hi"], a["max_new"], a["N"], a["S"], a["L"], a["d"],
+        a["B"], a["H_I"], a["h"], a["topk"], a["heads"], a["hs"], a["idx"], a["score"], None)
+
+
+# the static-scratch serving step: the same checks, before the GPU is touched
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1), (dict(kbar=None), 1), (dict(k=None), 1), (dict(lo=None), 1),
+    (dict(hi=None), 1), (dict(heads=None), 1), (dict(idx=None), 1), (dict(k_dt=2), 1),
+    (dict(q_dt=0), 3), (dict(d=96), 3), (dict(B=0), 2), (dict(max_new=-1), 2), (dict(h=65), 2),
+    (dict(topk=0), 2), (dict(N=0), 2), (dict(q=ctypes.c_void_p(0x100004)), 2), (dict(ps=64), 1),
+])
+def test_scratch_serving_step_rejects(over, status):
+    assert _scratch_step(**over) == status
+
+
+def test_scratch_serving_step_size_limit():
+    """Workspaces above the 32 MiB scratch are refused (4 rows of 2^21 keys
+    need 32 MiB of order keys alone)."""
+    need = b.misa_workspace_bytes(b.MISA_OP_ROUTE_SCORE_TOPK, 1, 4, 1 << 21, 128, 64, 128, 2048)
+    assert need > 32 << 20
+    assert _scratch_step(L=1 << 21, topk=2048, max_new=1) == 4

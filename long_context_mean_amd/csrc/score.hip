@@ -38,6 +38,8 @@ namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+constexpr int kMaxTpw = 16;    // tiles per wavefront at most (LDS key slots)
+
 struct ScoreParams {
   const uint16_t* q;
   const float* w;
@@ -178,7 +180,8 @@ __device__ __forceinline__ void score_group(const RawGroup<KT, D, U>& raw, const
                                             int lane,
                                             const bf16x8_t (&a)[NT][KeyLayout<KT, D>::KK],
                                             const float (&wv)[NT][4], int g, int c, int len,
-                                            uint32_t* urow, uint32_t* lh, bool do_hist) {
+                                            uint32_t* ukw, int ord0, uint32_t* lh,
+                                            bool do_hist) {
   using LY = KeyLayout<KT, D>;
   constexpr int KK = LY::KK;
   const int rsub = lane / LY::LANES_PER_ROW, q = lane % LY::LANES_PER_ROW;
@@ -222,11 +225,14 @@ __device__ __forceinline__ void score_group(const RawGroup<KT, D, U>& raw, const
                                                         __float_as_uint(part), false, false);
       part = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
     }
+    // the order key goes to the wavefront's LDS key slots (written to u in
+    // one burst after the loop: a global store here would sit in the same
+    // in-order memory counter as the key loads in flight)
     const int e = (tile0 + t * tstride) * 16 + c;
-    if (g == 0 && e < len) {
-      const bool ok = (valid >> t) & 1u;
+    if (g == 0) {
+      const bool ok = ((valid >> t) & 1u) && e < len;
       const uint32_t key = ok ? order_key(part) : 0u;
-      urow[e] = key;
+      ukw[(ord0 + t) * 16 + c] = key;
       if (do_hist && ok) atomicAdd(&lh[key >> kShift0], 1u);
     }
   }
@@ -238,6 +244,8 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
   constexpr int KK = LY::KK;
   __shared__ uint32_t lh[kBins0];
   __shared__ __align__(16) uint8_t tiles[4][LY::TILE_LDS];
+  // each wavefront's order keys in tile order (at most kMaxTpw tiles of 16)
+  __shared__ __align__(16) uint32_t ukeys[4][kMaxTpw * 16];
   __shared__ int32_t heads_lds[ROUTE ? 64 : 1];
   __shared__ __align__(16) uint16_t qlds[ROUTE ? 64 * D : 8];   // the row's query heads
   __shared__ float wlds[ROUTE ? 64 : 1];                          // and their weights
@@ -261,6 +269,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
   const float* sseq = p.k_scale;
   const int32_t* crow = CAND ? p.cand + static_cast<size_t>(n) * p.ncols : nullptr;
   uint32_t* urow = p.u + static_cast<size_t>(n) * p.u_stride;
+  uint32_t* ukw = ukeys[threadIdx.x >> 6];
   const int wtile = blockIdx.x * 4 + wave;            // this wavefront's first tile
   const int wtiles = wtile < ntiles ? (ntiles - wtile + tstride - 1) / tstride : 0;
   // paged keys: lane j holds the page of this wavefront's j-th tile (at most
@@ -299,13 +308,16 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
     load_chunk_partials(p.route_partial + prow, p.route_nchunks, p.H_I, pv);
   }
 
-  // first key group in flight before anything else (unconditional: a
-  // wavefront without tiles reads a valid row and scores nothing)
-  u32x4_t ra[U][LY::NLOAD], rb[U][LY::NLOAD];
-  float sa[U], sb[U];
-  uint32_t va = 0, vb = 0;
+  // the first two key groups in flight before anything else (unconditional:
+  // a wavefront without tiles reads valid rows and scores nothing)
+  const int gstep = U * tstride;                       // tiles between consecutive groups
+  u32x4_t ra[U][LY::NLOAD], rb[U][LY::NLOAD], rc[U][LY::NLOAD];
+  float sa[U], sb[U], sc[U];
+  uint32_t va = 0, vb = 0, vc = 0;
   va = issue_group<KT, D, U, CAND>(ra, sa, wtile, tstride, lane, c, len, crow, kseq, sseq,
                                    p.ki, s, 0, page_v);
+  vb = issue_group<KT, D, U, CAND>(rb, sb, wtile + gstep, tstride, lane, c, len, crow, kseq,
+                                   sseq, p.ki, s, U, page_v);
 
   if (do_hist) {
     for (int b = threadIdx.x; b < kBins0; b += 256) lh[b] = 0u;
@@ -370,38 +382,49 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
   }
   if (do_hist) __syncthreads();
 
-  // ping-pong over two register buffers: the next group's loads are in
-  // flight while the current group is scored.  Loads in the steady-state
-  // loop are unconditional (elements past the row end read token 0 and are
-  // masked), so the compiler's wait counts never drain the prefetch.
+  // three register buffers in rotation: while group i is scored, groups i+1
+  // and i+2 are in flight (group i+2 is issued just before group i is
+  // scored).  Every load is unconditional (groups past the wavefront's last
+  // tile read valid rows and are never scored), so the compiler's wait counts
+  // are exact and never drain the prefetch.
   if (wtiles > 0) {
-    int t0 = wtile;                                    // first tile of the current group
-    const int gstep = U * tstride;                     // tiles between consecutive groups
-    int left = (wtiles + U - 1) / U;                   // groups left, current included
-    int o0 = 0;                                        // ordinal of the current group's first tile
-    while (left >= 3) {
-      vb = issue_group<KT, D, U, CAND>(rb, sb, t0 + gstep, tstride, lane, c, len, crow, kseq,
-                                       sseq, p.ki, s, o0 + U, page_v);
-      score_group<KT, NT, D, U>(ra, sa, va, t0, tstride, tile, lane, a, wv, g, c, len, urow,
-                                lh, do_hist);
-      va = issue_group<KT, D, U, CAND>(ra, sa, t0 + 2 * gstep, tstride, lane, c, len, crow,
-                                       kseq, sseq, p.ki, s, o0 + 2 * U, page_v);
+    const int ng = (wtiles + U - 1) / U;               // groups of this wavefront
+    int t0 = wtile;                                    // first tile of group i
+    int o0 = 0;                                        // ordinal of group i's first tile
+    int i = 0;
+    for (; i + 3 <= ng; i += 3) {
+      vc = issue_group<KT, D, U, CAND>(rc, sc, t0 + 2 * gstep, tstride, lane, c, len, crow, kseq,
+                                       sseq, p.ki, s, o0 + 2 * U, page_v);
+      score_group<KT, NT, D, U>(ra, sa, va, t0, tstride, tile, lane, a, wv, g, c, len, ukw,
+                                o0, lh, do_hist);
+      va = issue_group<KT, D, U, CAND>(ra, sa, t0 + 3 * gstep, tstride, lane, c, len, crow, kseq,
+                                       sseq, p.ki, s, o0 + 3 * U, page_v);
       score_group<KT, NT, D, U>(rb, sb, vb, t0 + gstep, tstride, tile, lane, a, wv, g, c, len,
-                                urow, lh, do_hist);
-      t0 += 2 * gstep;
-      o0 += 2 * U;
-      left -= 2;
+                                ukw, o0 + U, lh, do_hist);
+      vb = issue_group<KT, D, U, CAND>(rb, sb, t0 + 4 * gstep, tstride, lane, c, len, crow, kseq,
+                                       sseq, p.ki, s, o0 + 4 * U, page_v);
+      score_group<KT, NT, D, U>(rc, sc, vc, t0 + 2 * gstep, tstride, tile, lane, a, wv, g, c,
+                                len, ukw, o0 + 2 * U, lh, do_hist);
+      t0 += 3 * gstep;
+      o0 += 3 * U;
     }
-    if (left == 2) {
-      vb = issue_group<KT, D, U, CAND>(rb, sb, t0 + gstep, tstride, lane, c, len, crow, kseq,
-                                       sseq, p.ki, s, o0 + U, page_v);
-      score_group<KT, NT, D, U>(ra, sa, va, t0, tstride, tile, lane, a, wv, g, c, len, urow,
-                                lh, do_hist);
+    // groups i (in ra) and i+1 (in rb) are in flight; at most two remain
+    if (i < ng)
+      score_group<KT, NT, D, U>(ra, sa, va, t0, tstride, tile, lane, a, wv, g, c, len, ukw,
+                                o0, lh, do_hist);
+    if (i + 1 < ng)
       score_group<KT, NT, D, U>(rb, sb, vb, t0 + gstep, tstride, tile, lane, a, wv, g, c, len,
-                                urow, lh, do_hist);
-    } else {
-      score_group<KT, NT, D, U>(ra, sa, va, t0, tstride, tile, lane, a, wv, g, c, len, urow,
-                                lh, do_hist);
+                                ukw, o0 + U, lh, do_hist);
+    // the wavefront's order keys to u: tile j's 16 keys are 64 contiguous
+    // bytes, written by 4 lanes with 16-byte stores (keys past the row end
+    // are 0, inside the row's padded stride)
+    __builtin_amdgcn_wave_barrier();
+    for (int j0 = 0; j0 < wtiles; j0 += 16) {
+      const int j = j0 + (lane >> 2), qd = lane & 3;
+      if (j < wtiles) {
+        const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(ukw + j * 16 + 4 * qd);
+        *reinterpret_cast<u32x4_t*>(urow + (wtile + j * tstride) * 16 + 4 * qd) = kv;
+      }
     }
   }
   if (do_hist) {
@@ -550,7 +573,7 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
   // tiles (of 16 keys) per wavefront; short candidate lists use smaller
   // chunks so more workgroups share the gather (at most 64 tiles per
   // wavefront: the paged path keeps one page number per lane)
-  const int tpw = a.cand ? 4 : 16;
+  const int tpw = a.cand ? 4 : kMaxTpw;
   if (a.k_dt == DT_BF16)
     return a.d == 64 ? launch_mfma_rows<DT_BF16, 64>(a, st, tpw)
                      : launch_mfma_rows<DT_BF16, 128>(a, st, tpw);

@@ -60,6 +60,13 @@ def parse():
                                                    "COPY_WRITE_DB"),
                     help="print the per-launch HBM traffic record of --kernel from rocprofv3 "
                          "--pmc FETCH_SIZE / WRITE_SIZE databases, scaled by the copy probe's")
+    ap.add_argument("--counters", metavar="DB",
+                    help="print the per-launch matrix-core counter summary of --match dispatches "
+                         "from a rocprofv3 --pmc database (SQ_INSTS_MFMA, "
+                         "SQ_VALU_MFMA_BUSY_CYCLES, SQ_VALU_MFMA_COEXEC_CYCLES, SQ_INSTS_VALU, "
+                         "SQ_BUSY_CYCLES, SQ_WAVE_CYCLES, GRBM_GUI_ACTIVE)")
+    ap.add_argument("--flop", type=float, default=None,
+                    help="algorithmic flop per launch (for --counters)")
     ap.add_argument("--kernel", default="score_mfma_kernel")
     ap.add_argument("--match", default=None,
                     help="kernel-name substring selecting the dispatches (default: --kernel)")
@@ -142,6 +149,48 @@ def traffic_record(fetch_db, write_db, copy_fetch_db, copy_write_db, kernel, mat
             "copy_fetch_kib": cf, "copy_write_kib": cw, "scale_fetch": sf, "scale_write": sw,
             "fetch_bytes_per_launch": kf * 1024.0 * sf, "write_bytes_per_launch": kw * 1024.0 * sw,
             "traffic_bytes_per_launch": (kf * 1024.0 * sf + kw * 1024.0 * sw), "command": cmd}
+
+
+def counter_record(db, match, flop, cmd, mfma_flop=16384, simds=1024, xcds=8):
+    """Matrix-core counters per launch of the dispatches whose kernel name
+    contains `match`: the rocprofv3 values are sums over the chip (per-SE or
+    per-SIMD counters added up; GRBM_GUI_ACTIVE once per XCD), averaged over
+    the dispatches."""
+    import sqlite3
+    c = sqlite3.connect(db)
+    rows = c.execute("select dispatch_id, kernel_name, counter_name, value, duration "
+                     "from counters_collection").fetchall()
+    per, dur, name = {}, {}, None
+    for did, kn, cn, v, d in rows:
+        if match in kn:
+            per.setdefault(did, {})
+            per[did][cn] = per[did].get(cn, 0.0) + v
+            dur[did] = d
+            name = kn
+    if not per:
+        return None
+    keys = sorted({k for v in per.values() for k in v})
+    mean = {k: sum(v.get(k, 0.0) for v in per.values()) / len(per) for k in keys}
+    rec = {"kernel": name.replace("misa::(anonymous namespace)::", "").split("(")[0],
+           "dispatches": len(per), "command": cmd,
+           "counters_per_launch": {k: round(v) for k, v in mean.items()},
+           "profiled_duration_us": round(sum(dur.values()) / len(dur) / 1e3, 2)}
+    gui = mean.get("GRBM_GUI_ACTIVE", 0.0) / xcds          # cycles the chip was busy
+    mf = mean.get("SQ_INSTS_MFMA", 0.0)
+    busy = mean.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+    if gui and busy:
+        rec["mfma_busy_frac_of_simd_cycles"] = round(busy / (gui * simds), 4)
+        rec["clock_ghz_under_load"] = round(gui / (rec["profiled_duration_us"] * 1e3), 3)
+    if busy and "SQ_VALU_MFMA_COEXEC_CYCLES" in mean:
+        rec["coexec_frac_of_mfma_busy"] = round(mean["SQ_VALU_MFMA_COEXEC_CYCLES"] / busy, 4)
+    if mf:
+        rec["mfma_busy_cycles_per_mfma"] = round(busy / mf, 2)
+        rec["non_mfma_valu_per_mfma"] = round((mean.get("SQ_INSTS_VALU", 0.0) - mf) / mf, 3)
+        rec["flop_from_counters"] = mf * mfma_flop
+        if flop:
+            rec["algorithmic_flop"] = flop
+            rec["counter_flop_over_algorithmic"] = round(mf * mfma_flop / flop, 4)
+    return rec
 
 
 def measured_traffic(kernel, workload):
@@ -562,6 +611,10 @@ def main():
         return
     if args.traffic:
         print(json.dumps(traffic_record(*args.traffic, args.kernel, args.match or args.kernel,
+                                        args.cmd), indent=1))
+        return
+    if args.counters:
+        print(json.dumps(counter_record(args.counters, args.match or args.kernel, args.flop,
                                         args.cmd), indent=1))
         return
     if args.gpus != 1:

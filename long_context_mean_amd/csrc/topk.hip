@@ -32,6 +32,7 @@ constexpr int kChunk = 4096;          // elements per collect workgroup
 constexpr int kPerThread = 16;        // contiguous elements per thread per tile
 constexpr int kCandCap = 8192;        // candidates resolved in LDS
 constexpr int kBitmapWords = 8192;    // rows up to 262144 elements use the LDS bitmap
+constexpr int kFinalThreads = 1024;   // threads of the few-rows final selection
 
 // Finds the bin of a histogram (NBINS bins, bin NBINS-1 = largest keys) that
 // holds the K-th largest element.  With clamp_total, K = min(K, total) first.
@@ -307,7 +308,8 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(
   }
 }
 
-__global__ __launch_bounds__(1024) void topk_final_kernel(
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_final_kernel(
     const uint32_t* __restrict__ u, int u_stride, const int32_t* __restrict__ q_pos,
     int fixed_len, const uint32_t* hist, const uint32_t* __restrict__ bitmap,
     const uint2* __restrict__ clist, int topk, int32_t* __restrict__ idx,
@@ -330,10 +332,10 @@ __global__ __launch_bounds__(1024) void topk_final_kernel(
   // the bitmap words (certain winners) and the candidate count are read in
   // the same round trip as the level-0 histogram
   const uint32_t* bmg = bitmap + static_cast<size_t>(n) * (u_stride / 32);
-  uint4 bw[kBitmapWords / 4096];
+  uint4 bw[kBitmapWords / (4 * NT)];
 #pragma unroll
-  for (int q = 0; q < kBitmapWords / 4096; ++q) {
-    const int w = 4 * (threadIdx.x + q * 1024);
+  for (int q = 0; q < kBitmapWords / (4 * NT); ++q) {
+    const int w = 4 * (threadIdx.x + q * NT);
     bw[q] = w + 3 < nwords ? *reinterpret_cast<const uint4*>(bmg + w) : make_uint4(0u, 0u, 0u, 0u);
     if (w < nwords && w + 3 >= nwords) {          // ragged last words
       bw[q].x = bmg[w];
@@ -343,11 +345,11 @@ __global__ __launch_bounds__(1024) void topk_final_kernel(
   }
   const uint32_t c = h0g[kCandCountOffset];
   // the first candidate of every thread, read before the count is known (the
-  // list holds kCandCap >= 1024 entries, so the read stays inside it)
+  // list holds kCandCap >= NT entries, so the read stays inside it)
   const uint2* cl = clist + static_cast<size_t>(n) * kCandCap;
-  static_assert(kCandCap >= 1024, "one speculative candidate per thread");
+  static_assert(kCandCap >= NT, "one speculative candidate per thread");
   const uint2 e_first = cl[threadIdx.x];
-  find_digit<1024, kBins0>(h0g, static_cast<uint32_t>(topk), true, sm, res);
+  find_digit<NT, kBins0>(h0g, static_cast<uint32_t>(topk), true, sm, res);
   const uint32_t K = res[2], d0 = res[0], r0 = res[1];
   __syncthreads();
   bool fallback = c > static_cast<uint32_t>(kCandCap) || nwords > kBitmapWords;
@@ -355,40 +357,40 @@ __global__ __launch_bounds__(1024) void topk_final_kernel(
   if (!fallback && K > 0) {
     // certain winners (bitmap) and the candidates of bin d0 into LDS
 #pragma unroll
-    for (int q = 0; q < kBitmapWords / 4096; ++q)
-      *reinterpret_cast<uint4*>(&bm[4 * (threadIdx.x + q * 1024)]) = bw[q];
-    for (int i = threadIdx.x; i < static_cast<int>(c); i += 1024) {
-      const uint2 e = i < 1024 ? e_first : cl[i];
+    for (int q = 0; q < kBitmapWords / (4 * NT); ++q)
+      *reinterpret_cast<uint4*>(&bm[4 * (threadIdx.x + q * NT)]) = bw[q];
+    for (int i = threadIdx.x; i < static_cast<int>(c); i += NT) {
+      const uint2 e = i < NT ? e_first : cl[i];
       cu[i] = e.x;
       ci[i] = e.y;
     }
-    for (int b = threadIdx.x; b < kBins1; b += 1024) hA[b] = 0u;
+    for (int b = threadIdx.x; b < kBins1; b += NT) hA[b] = 0u;
     if (threadIdx.x < kBins2) hB[threadIdx.x] = 0u;
     __syncthreads();
     // exact threshold among the candidates: digits 1 and 2 (rank r0)
-    for (int i = threadIdx.x; i < static_cast<int>(c); i += 1024)
+    for (int i = threadIdx.x; i < static_cast<int>(c); i += NT)
       atomicAdd(&hA[(cu[i] >> kShift1) & (kBins1 - 1)], 1u);
     __syncthreads();
-    find_digit<1024, kBins1>(hA, r0, false, sm, res);
+    find_digit<NT, kBins1>(hA, r0, false, sm, res);
     const uint32_t d1 = res[0], r1 = res[1];
     __syncthreads();
     const uint32_t pre = (d0 << kDigit1Bits) | d1;
-    for (int i = threadIdx.x; i < static_cast<int>(c); i += 1024)
+    for (int i = threadIdx.x; i < static_cast<int>(c); i += NT)
       if ((cu[i] >> kShift1) == pre) atomicAdd(&hB[cu[i] & (kBins2 - 1)], 1u);
     __syncthreads();
-    find_digit<1024, kBins2>(hB, r1, false, sm, res);
+    find_digit<NT, kBins2>(hB, r1, false, sm, res);
     T = (d0 << kShift0) | (d1 << kShift1) | res[0];
     K2 = res[1];
     n_eq = hB[res[0]];                    // candidates whose key equals T
     __syncthreads();
   }
   if (fallback) {
-    for (int b = threadIdx.x; b < kBins0; b += 1024) hA[b] = h0g[b];
+    for (int b = threadIdx.x; b < kBins0; b += NT) hA[b] = h0g[b];
     __syncthreads();
-    row_select<1024>(row, len, topk, nullptr, idx_row, score_row, hA, cu, hB, true, sm, res);
+    row_select<NT>(row, len, topk, nullptr, idx_row, score_row, hA, cu, hB, true, sm, res);
     return;
   }
-  for (int i = static_cast<int>(K) + threadIdx.x; i < topk; i += 1024) {
+  for (int i = static_cast<int>(K) + threadIdx.x; i < topk; i += NT) {
     idx_row[i] = -1;
     if (score_row) score_row[i] = -__builtin_inff();
   }
@@ -397,26 +399,30 @@ __global__ __launch_bounds__(1024) void topk_final_kernel(
   // mark the candidate winners: key > T, or key == T among the K2 lowest
   // indices (all ties win when n_eq == K2, the usual case)
   const uint32_t cut = n_eq == K2 ? 0xFFFFFFFFu
-                                  : tie_cut<1024>(cu, ci, static_cast<int>(c), T, K2, n_eq, hA,
+                                  : tie_cut<NT>(cu, ci, static_cast<int>(c), T, K2, n_eq, hA,
                                                   hB, sm, res);
-  for (int i = threadIdx.x; i < static_cast<int>(c); i += 1024) {
+  for (int i = threadIdx.x; i < static_cast<int>(c); i += NT) {
     const uint32_t kv = cu[i], e = ci[i];
     if (kv > T || (kv == T && e <= cut)) atomicOr(&bm[e >> 5], 1u << (e & 31));
   }
   __syncthreads();
 
-  // ordered emit of every marked element
+  // ordered emit of every marked element (WPT consecutive words per thread)
+  constexpr int WPT = 4096 / NT;
   uint32_t base_pos = 0;
-  for (int w0 = 0; w0 < nwords; w0 += 4 * 1024) {
-    const int w = w0 + 4 * threadIdx.x;
-    uint32_t wd[4];
+  for (int w0 = 0; w0 < nwords; w0 += WPT * NT) {
+    const int w = w0 + WPT * threadIdx.x;
+    uint32_t wd[WPT];
+    uint32_t cnt = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) wd[q] = (w + q < nwords) ? bm[w + q] : 0u;
-    const uint32_t cnt = __popc(wd[0]) + __popc(wd[1]) + __popc(wd[2]) + __popc(wd[3]);
+    for (int q = 0; q < WPT; ++q) {
+      wd[q] = (w + q < nwords) ? bm[w + q] : 0u;
+      cnt += __popc(wd[q]);
+    }
     uint32_t tot;
-    uint32_t pos = base_pos + block_excl_scan<1024>(cnt, sm, tot);
+    uint32_t pos = base_pos + block_excl_scan<NT>(cnt, sm, tot);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < WPT; ++q) {
       uint32_t bits = wd[q];
       while (bits) {
         const int b = __ffs(bits) - 1;
@@ -843,7 +849,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   const int nchunks = a.u_stride / kChunk;
   MISA_LAUNCH(K_TOPK_COLLECT, topk_collect_kernel, dim3(nchunks, a.N), dim3(256), 0, st, a.u,
               a.u_stride, a.q_pos, a.fixed_len, a.hist, bitmap, clist, a.topk);
-  MISA_LAUNCH(K_TOPK_FINAL, topk_final_kernel, dim3(a.N), dim3(1024), 0, st, a.u, a.u_stride,
+  MISA_LAUNCH(K_TOPK_FINAL, topk_final_kernel<kFinalThreads>, dim3(a.N), dim3(kFinalThreads), 0,
+              st, a.u, a.u_stride,
               a.q_pos, a.fixed_len, a.hist, bitmap, clist, a.topk, a.idx, a.score);
   return hipGetLastError();
 }

@@ -93,7 +93,8 @@ TopkLayout topk_layout(int N, int len_max) {
   TopkLayout t;
   const int chunk = misa::topk_chunk();
   t.u_stride = static_cast<int>(align_up(static_cast<size_t>(len_max), chunk));
-  t.one_row = N >= kOneRowMinN || t.u_stride <= chunk;
+  // many rows, or rows short enough for one workgroup's registers
+  t.one_row = N >= kOneRowMinN || t.u_stride <= misa::topk_small_row();
   size_t off = align_up(static_cast<size_t>(N) * t.u_stride * 4, 256);
   if (!t.one_row) {
     t.off_hist = off;

@@ -203,6 +203,9 @@ struct TopkArgs {
   const uint32_t* row_flag = nullptr;   // one-row mode: rows whose flag is 0 are skipped
 };
 int topk_chunk();
+// Rows of at most this many elements are selected by one workgroup holding
+// the whole row in registers.
+int topk_small_row();
 size_t topk_few_rows_bytes(int N, int u_stride);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 hipError_t launch_clear(uint32_t* p, size_t n_words, hipStream_t st);

@@ -439,6 +439,141 @@ __global__ __launch_bounds__(NT) void topk_final_kernel(
   }
 }
 
+// ---------------------------------------------------------------- short rows in registers
+// Rows of at most kSmallRow elements (MISA-dagger's rerank, the block
+// prefilter's selects, short decode rows): one 1024-thread workgroup per row;
+// thread t holds elements 16t .. 16t+15 in registers for every pass.  The
+// keys of such a row are often close together (re-scored candidates, block
+// scores), so the radix digits are taken on key - min over the row's key
+// range (digits [sA, 32), [sB, sA), [0, sB) with (max - min) >> sA < 4096),
+// which spreads the histogram's LDS atomics.  Ties at the threshold T go to
+// the lowest indices: a thread's elements are contiguous, so a block prefix
+// of the per-thread tie counts ranks them.  Outputs in index order from a
+// block prefix of the per-thread winner counts.
+constexpr int kSmallRow = 1024 * kPerThread;
+
+__global__ __launch_bounds__(1024) void topk_small_kernel(
+    const uint32_t* __restrict__ u, int u_stride, const int32_t* __restrict__ q_pos,
+    int fixed_len, int topk, const int32_t* __restrict__ cand, int cand_stride,
+    int32_t* __restrict__ idx, float* __restrict__ score) {
+  constexpr int NT = 1024;
+  __shared__ __align__(16) uint32_t hA[kBins0];
+  __shared__ __align__(16) uint32_t hB[kBins2];
+  __shared__ uint32_t sm[16];
+  __shared__ uint32_t res[4];
+  __shared__ uint32_t kmin, kmax;
+  const int n = blockIdx.x, tid = threadIdx.x;
+  const int len = row_len(q_pos, fixed_len, n);
+  const uint32_t* row = u + static_cast<size_t>(n) * u_stride;
+  const int32_t* cand_row = cand ? cand + static_cast<size_t>(n) * cand_stride : nullptr;
+  int32_t* idx_row = idx + static_cast<size_t>(n) * topk;
+  float* score_row = score ? score + static_cast<size_t>(n) * topk : nullptr;
+  const int i0 = tid * kPerThread;
+  uint32_t v[kPerThread];
+  if (i0 < len) {
+    load16(row, i0, len, v);                  // in bounds: rows are padded to whole chunks
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) v[j] = 0u;
+  }
+  if (tid == 0) {
+    kmin = 0xFFFFFFFFu;
+    kmax = 0u;
+  }
+  for (int b = tid; b < kBins0; b += NT) hA[b] = 0u;
+  if (tid < kBins2) hB[tid] = 0u;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u, nv = 0;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    if (v[j] != 0u) {
+      lo = min(lo, v[j]);
+      hi = max(hi, v[j]);
+      ++nv;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), o, 64)));
+    hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), o, 64)));
+  }
+  __syncthreads();
+  if ((tid & 63) == 0) {
+    atomicMin(&kmin, lo);
+    atomicMax(&kmax, hi);
+  }
+  const uint32_t K = min(static_cast<uint32_t>(topk), block_sum<NT>(nv, sm));
+  const uint32_t base = kmin, range = kmax - kmin;   // (synchronised by block_sum)
+  uint32_t T = 0, K2 = 0;
+  if (K > 0) {
+    int sA = 0;
+    while ((range >> sA) >= static_cast<uint32_t>(kBins0)) ++sA;
+    const int sB = sA > 12 ? sA - 12 : 0;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j)
+      if (v[j] != 0u) atomicAdd(&hA[(v[j] - base) >> sA], 1u);
+    __syncthreads();
+    find_digit<NT, kBins0>(hA, K, false, sm, res);
+    const uint32_t dA = res[0];
+    uint32_t r = res[1], dB = 0, dC = 0;
+    if (sA > 0) {
+      for (int b = tid; b < kBins0; b += NT) hA[b] = 0u;
+      __syncthreads();
+      const uint32_t mB = (1u << (sA - sB)) - 1u;
+#pragma unroll
+      for (int j = 0; j < kPerThread; ++j)
+        if (v[j] != 0u && ((v[j] - base) >> sA) == dA)
+          atomicAdd(&hA[((v[j] - base) >> sB) & mB], 1u);
+      __syncthreads();
+      find_digit<NT, kBins0>(hA, r, false, sm, res);
+      dB = res[0];
+      r = res[1];
+      if (sB > 0) {                           // sB <= 8: the last digit fits hB
+        const uint32_t preB = (dA << (sA - sB)) | dB;
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j)
+          if (v[j] != 0u && ((v[j] - base) >> sB) == preB)
+            atomicAdd(&hB[(v[j] - base) & ((1u << sB) - 1u)], 1u);
+        __syncthreads();
+        find_digit<NT, kBins2>(hB, r, false, sm, res);
+        dC = res[0];
+        r = res[1];
+      }
+    }
+    T = base + ((dA << sA) | (dB << sB) | dC);
+    K2 = r;                                   // ties at T that win: the K2 lowest indices
+  }
+  // this thread's winners: keys above T, and ties ranked by index
+  uint32_t ties = 0;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) ties += (K > 0 && v[j] == T) ? 1u : 0u;
+  uint32_t tie_tot;
+  uint32_t tie_rank = block_excl_scan<NT>(ties, sm, tie_tot);
+  uint32_t sel = 0, nsel = 0;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const bool eq = K > 0 && v[j] == T;
+    const bool win = (K > 0 && v[j] > T) || (eq && tie_rank < K2);
+    tie_rank += eq ? 1u : 0u;
+    sel |= win ? (1u << j) : 0u;
+    nsel += win ? 1u : 0u;
+  }
+  uint32_t tot;
+  uint32_t pos = block_excl_scan<NT>(nsel, sm, tot);
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    if ((sel >> j) & 1u) {
+      const int e = i0 + j;
+      idx_row[pos] = cand_row ? cand_row[e] : e;
+      if (score_row) score_row[pos] = key_score(v[j]);
+      ++pos;
+    }
+  }
+  for (int i = static_cast<int>(K) + tid; i < topk; i += NT) {
+    idx_row[i] = -1;
+    if (score_row) score_row[i] = -__builtin_inff();
+  }
+}
+
 __global__ void topk_clear_kernel(uint32_t* __restrict__ p, size_t n_words) {
   for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n_words;
        i += static_cast<size_t>(gridDim.x) * blockDim.x)
@@ -836,6 +971,11 @@ size_t topk_few_rows_bytes(int N, int u_stride) {
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
+  if (a.one_row_per_block && !a.row_flag && a.u_stride <= kSmallRow) {
+    MISA_LAUNCH(K_TOPK_ROW, topk_small_kernel, dim3(a.N), dim3(1024), 0, st, a.u, a.u_stride,
+                a.q_pos, a.fixed_len, a.topk, a.cand, a.cand_stride, a.idx, a.score);
+    return hipGetLastError();
+  }
   if (a.one_row_per_block) {
     MISA_LAUNCH(K_TOPK_ROW, topk_row_kernel, dim3(a.N), dim3(1024), 0, st, a.u, a.u_stride,
                 a.q_pos, a.fixed_len, a.topk, a.cand, a.cand_stride, a.idx, a.score, a.row_flag);
@@ -865,6 +1005,8 @@ hipError_t launch_clear(uint32_t* p, size_t n_words, hipStream_t st) {
 }
 
 int topk_chunk() { return kChunk; }
+
+int topk_small_row() { return kSmallRow; }
 
 int cand_topk_capacity() { return kCandRow; }
 

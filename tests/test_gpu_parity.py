@@ -804,11 +804,11 @@ def test_decode_topk_concentrated_in_one_stretch(k_dt, start):
                                                              sc2.view(np.uint32))
 
 
-@pytest.mark.parametrize("N", [3, 130])
-def test_all_scores_tied(N):
+@pytest.mark.parametrize("N,L", [(3, 20000), (130, 20000), (3, 12000)])
+def test_all_scores_tied(N, L):
     """Zero keys: every score is 0, the threshold bin holds every token (more
-    than the LDS candidate list), and the lowest indices must win."""
-    L = 20000
+    than the LDS candidate list), and the lowest indices must win (rows of
+    12000 tokens take the register-resident short-row select)."""
     p = synth.integer_problem("tied", 64, N=N, S=1, L=L, d=128, H_I=16, h=4, B=128,
                               topk=1500, q_pos=(L - 1 - np.arange(N)).astype(np.int32),
                               q_seq=np.zeros(N, np.int32))

@@ -446,11 +446,64 @@ __global__ __launch_bounds__(NT) void topk_final_kernel(
 // keys of such a row are often close together (re-scored candidates, block
 // scores), so the radix digits are taken on key - min over the row's key
 // range (digits [sA, 32), [sB, sA), [0, sB) with (max - min) >> sA < 4096),
-// which spreads the histogram's LDS atomics.  Ties at the threshold T go to
-// the lowest indices: a thread's elements are contiguous, so a block prefix
-// of the per-thread tie counts ranks them.  Outputs in index order from a
-// block prefix of the per-thread winner counts.
+// which spreads the histogram's LDS atomics; a row whose range fits 12 bits
+// needs one level.  Ties at the threshold T go to the lowest indices: a
+// thread's elements are contiguous, so a block prefix of the per-thread tie
+// counts ranks them (skipped when every tie wins).  Outputs in index order
+// from a block prefix of the per-thread winner counts.
 constexpr int kSmallRow = 1024 * kPerThread;
+
+// Block prefix with one barrier: exclusive prefix of v over the threads in
+// index order and the total.  `sm` (NT/64 words) must not be in use by a
+// previous call that some thread may still be reading.
+template <int NT>
+__device__ __forceinline__ uint32_t block_prefix1(uint32_t v, uint32_t* sm, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane == 63) sm[wid] = incl;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    const uint32_t s = sm[i];
+    before += (i < wid) ? s : 0u;
+    tot += s;
+  }
+  total = tot;
+  return before + incl - v;
+}
+
+// The bin of a 4096-bin histogram (bin 4095 = largest keys) holding the K-th
+// largest element, 1 <= K <= its total, with two barriers (the histogram's
+// updates must be complete, i.e. a barrier between them and this call).
+// res[0] = bin, res[1] = rank of the element inside the bin (1-based).
+template <int NT>
+__device__ __forceinline__ void locate_bin(const uint32_t* hist, uint32_t K, uint32_t* sm,
+                                           uint32_t* res) {
+  constexpr int PER = kBins0 / NT;
+  const int lo = kBins0 - (static_cast<int>(threadIdx.x) + 1) * PER;
+  uint32_t vb[PER];
+  uint32_t c = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    vb[q] = hist[lo + q];
+    c += vb[q];
+  }
+  uint32_t total;
+  const uint32_t above = block_prefix1<NT>(c, sm, total);
+  if (above < K && K <= above + c) {
+    uint32_t acc = above;
+#pragma unroll
+    for (int q = PER - 1; q >= 0; --q) {
+      if (acc < K && acc + vb[q] >= K) {
+        res[0] = static_cast<uint32_t>(lo + q);
+        res[1] = K - acc;
+      }
+      acc += vb[q];
+    }
+  }
+  __syncthreads();
+}
 
 __global__ __launch_bounds__(1024) void topk_small_kernel(
     const uint32_t* __restrict__ u, int u_stride, const int32_t* __restrict__ q_pos,
@@ -458,10 +511,11 @@ __global__ __launch_bounds__(1024) void topk_small_kernel(
     int32_t* __restrict__ idx, float* __restrict__ score) {
   constexpr int NT = 1024;
   __shared__ __align__(16) uint32_t hA[kBins0];
-  __shared__ __align__(16) uint32_t hB[kBins2];
-  __shared__ uint32_t sm[16];
-  __shared__ uint32_t res[4];
-  __shared__ uint32_t kmin, kmax;
+  __shared__ __align__(16) uint32_t hA2[kBins0];
+  __shared__ __align__(16) uint32_t hB[kBins0];
+  __shared__ uint32_t sm[4][16];
+  __shared__ uint32_t res[3][4];
+  __shared__ uint32_t wmin[16], wmax[16];
   const int n = blockIdx.x, tid = threadIdx.x;
   const int len = row_len(q_pos, fixed_len, n);
   const uint32_t* row = u + static_cast<size_t>(n) * u_stride;
@@ -470,18 +524,21 @@ __global__ __launch_bounds__(1024) void topk_small_kernel(
   float* score_row = score ? score + static_cast<size_t>(n) * topk : nullptr;
   const int i0 = tid * kPerThread;
   uint32_t v[kPerThread];
+  int32_t ct[kPerThread];                     // the elements' output indices
   if (i0 < len) {
     load16(row, i0, len, v);                  // in bounds: rows are padded to whole chunks
   } else {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) v[j] = 0u;
   }
-  if (tid == 0) {
-    kmin = 0xFFFFFFFFu;
-    kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j)
+    ct[j] = cand_row ? (i0 + j < len ? cand_row[i0 + j] : -1) : i0 + j;
+  for (int b = tid; b < kBins0; b += NT) {
+    hA[b] = 0u;
+    hA2[b] = 0u;
+    hB[b] = 0u;
   }
-  for (int b = tid; b < kBins0; b += NT) hA[b] = 0u;
-  if (tid < kBins2) hB[tid] = 0u;
   uint32_t lo = 0xFFFFFFFFu, hi = 0u, nv = 0;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
@@ -496,15 +553,22 @@ __global__ __launch_bounds__(1024) void topk_small_kernel(
     lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), o, 64)));
     hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), o, 64)));
   }
-  __syncthreads();
   if ((tid & 63) == 0) {
-    atomicMin(&kmin, lo);
-    atomicMax(&kmax, hi);
+    wmin[tid >> 6] = lo;
+    wmax[tid >> 6] = hi;
   }
-  const uint32_t K = min(static_cast<uint32_t>(topk), block_sum<NT>(nv, sm));
-  const uint32_t base = kmin, range = kmax - kmin;   // (synchronised by block_sum)
-  uint32_t T = 0, K2 = 0;
+  uint32_t nv_tot;
+  (void)block_prefix1<NT>(nv, sm[0], nv_tot);   // (its barrier also publishes wmin / wmax)
+  const uint32_t K = min(static_cast<uint32_t>(topk), nv_tot);
+  uint32_t T = 0, K2 = 0, n_eq = 0;
   if (K > 0) {
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+      kmin = min(kmin, wmin[w]);
+      kmax = max(kmax, wmax[w]);
+    }
+    const uint32_t base = kmin, range = kmax - kmin;
     int sA = 0;
     while ((range >> sA) >= static_cast<uint32_t>(kBins0)) ++sA;
     const int sB = sA > 12 ? sA - 12 : 0;
@@ -512,42 +576,48 @@ __global__ __launch_bounds__(1024) void topk_small_kernel(
     for (int j = 0; j < kPerThread; ++j)
       if (v[j] != 0u) atomicAdd(&hA[(v[j] - base) >> sA], 1u);
     __syncthreads();
-    find_digit<NT, kBins0>(hA, K, false, sm, res);
-    const uint32_t dA = res[0];
-    uint32_t r = res[1], dB = 0, dC = 0;
+    locate_bin<NT>(hA, K, sm[1], res[0]);
+    const uint32_t dA = res[0][0];
+    uint32_t r = res[0][1], dB = 0, dC = 0;
+    n_eq = hA[dA];
     if (sA > 0) {
-      for (int b = tid; b < kBins0; b += NT) hA[b] = 0u;
-      __syncthreads();
       const uint32_t mB = (1u << (sA - sB)) - 1u;
 #pragma unroll
       for (int j = 0; j < kPerThread; ++j)
         if (v[j] != 0u && ((v[j] - base) >> sA) == dA)
-          atomicAdd(&hA[((v[j] - base) >> sB) & mB], 1u);
+          atomicAdd(&hA2[((v[j] - base) >> sB) & mB], 1u);
       __syncthreads();
-      find_digit<NT, kBins0>(hA, r, false, sm, res);
-      dB = res[0];
-      r = res[1];
-      if (sB > 0) {                           // sB <= 8: the last digit fits hB
+      locate_bin<NT>(hA2, r, sm[2], res[1]);
+      dB = res[1][0];
+      r = res[1][1];
+      n_eq = hA2[dB];
+      if (sB > 0) {                           // sB <= 8
         const uint32_t preB = (dA << (sA - sB)) | dB;
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j)
           if (v[j] != 0u && ((v[j] - base) >> sB) == preB)
             atomicAdd(&hB[(v[j] - base) & ((1u << sB) - 1u)], 1u);
         __syncthreads();
-        find_digit<NT, kBins2>(hB, r, false, sm, res);
-        dC = res[0];
-        r = res[1];
+        locate_bin<NT>(hB, r, sm[3], res[2]);
+        dC = res[2][0];
+        r = res[2][1];
+        n_eq = hB[dC];
       }
     }
     T = base + ((dA << sA) | (dB << sB) | dC);
     K2 = r;                                   // ties at T that win: the K2 lowest indices
   }
-  // this thread's winners: keys above T, and ties ranked by index
-  uint32_t ties = 0;
+  // this thread's winners: keys above T, and ties ranked by index (every tie
+  // wins when K2 == n_eq, the usual case: no ranking needed)
+  uint32_t tie_rank = 0;
+  if (K2 != n_eq) {
+    uint32_t ties = 0;
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) ties += (K > 0 && v[j] == T) ? 1u : 0u;
-  uint32_t tie_tot;
-  uint32_t tie_rank = block_excl_scan<NT>(ties, sm, tie_tot);
+    for (int j = 0; j < kPerThread; ++j) ties += (v[j] == T) ? 1u : 0u;
+    uint32_t tie_tot;
+    __syncthreads();                          // sm[0] is free again
+    tie_rank = block_prefix1<NT>(ties, sm[0], tie_tot);
+  }
   uint32_t sel = 0, nsel = 0;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
@@ -558,12 +628,12 @@ __global__ __launch_bounds__(1024) void topk_small_kernel(
     nsel += win ? 1u : 0u;
   }
   uint32_t tot;
-  uint32_t pos = block_excl_scan<NT>(nsel, sm, tot);
+  // (sm[1]'s readers in the first level's locate_bin passed its closing barrier)
+  uint32_t pos = block_prefix1<NT>(nsel, sm[1], tot);
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
     if ((sel >> j) & 1u) {
-      const int e = i0 + j;
-      idx_row[pos] = cand_row ? cand_row[e] : e;
+      idx_row[pos] = ct[j];
       if (score_row) score_row[pos] = key_score(v[j]);
       ++pos;
     }

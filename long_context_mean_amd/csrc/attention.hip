@@ -37,6 +37,9 @@ typedef short bf16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kChunkTok = 64;          // selected tokens per chunk (one LDS fill)
+// chunks per split: 2 measured best against 1 and 4 at 128 heads x 2048
+// selected tokens
+constexpr int kChunksPerSplit = 2;
 constexpr int kHeadBlock = 32;         // heads per workgroup (16 per wavefront pair)
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -57,7 +60,11 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int KK>
+// DVF: value tiles per wavefront (d_v / 32) fixed at compile time, or 0 to
+// take them from d_v at run time.  With DVF fixed the value products run as
+// DVF independent accumulation chains side by side; the run-time form
+// handles one tile's chain at a time.
+template <int KK, int DVF>
 __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
   constexpr int DQK = KK * 32;
   constexpr int ROWP = DQK * 2 + 16;                    // padded LDS row (bytes)
@@ -87,7 +94,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
     }
   }
   const int half = p.dv / 2;
-  const int dvt = half / 16;                            // value tiles of this wavefront
+  const int dvt = DVF > 0 ? DVF : half / 16;            // value tiles of this wavefront
   const int dv0 = (wave & 1) * half;
   const int r4 = lane & 15;                             // 4m + q within the lane group
   f32x4_t o[MAXDVT];
@@ -130,21 +137,28 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
     }
     __syncthreads();
 
-    // S^T for the chunk's 4 tiles of 16 tokens, in log2 units; unselected -inf
+    // S^T for the chunk's 4 tiles of 16 tokens, in log2 units; unselected
+    // -inf.  The 4 tiles' accumulation chains (over d, in order) run side by
+    // side.
     float sv[4][4];
+    {
+      f32x4_t acc[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      const uint8_t* arow = kvt + (16 * t + c) * ROWP + 16 * g;
+      for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8_t a = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const u32x4_t*>(arow + 64 * kk));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], acc, 0, 0, 0);
-      }
+      for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sv[t][i] = tok_lds[16 * t + 4 * g + i] >= 0 ? acc[i] * p.scale2 : -__builtin_inff();
+        for (int t = 0; t < 4; ++t) {
+          const bf16x8_t a = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const u32x4_t*>(kvt + (16 * t + c) * ROWP + 16 * g +
+                                                          64 * kk));
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], acc[t], 0, 0, 0);
+        }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sv[t][i] = tok_lds[16 * t + 4 * g + i] >= 0 ? acc[t][i] * p.scale2 : -__builtin_inff();
     }
     float m_c = -__builtin_inff();
 #pragma unroll
@@ -179,24 +193,47 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
     l_run = l_run * alpha + lc;
     m_run = m_new;
 
-    // O^T (this wavefront's half of d_v, 16 value columns per tile) += V^T P^T
+    // O^T (this wavefront's half of d_v, 16 value columns per tile) += V^T P^T;
+    // per tile j: rescale, then the 4 token tiles' hi and lo products in order
     typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+    if constexpr (DVF > 0) {
 #pragma unroll
-    for (int j = 0; j < MAXDVT; ++j) {
-      if (j < dvt) {
-        f32x4_t acc = o[j] * alpha;
+      for (int j = 0; j < DVF; ++j) o[j] = o[j] * alpha;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int row = 16 * t + 4 * g + (r4 >> 2);
+      for (int t = 0; t < 4; ++t) {
+        const int row = 16 * t + 4 * g + (r4 >> 2);
+        bf16x4_t av[DVF];
+#pragma unroll
+        for (int j = 0; j < DVF; ++j) {
           const int col = dv0 + 16 * j + 4 * (r4 & 3);
-          // generic -> LDS address space (a C-style cast is the address-space cast)
           lds_bf16x4_t* ap = (lds_bf16x4_t*)((__attribute__((address_space(3))) uint8_t*)kvt +
                                              row * ROWP + col * 2);
-          const bf16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(ap);
-          acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi[t], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo[t], acc, 0, 0, 0);
+          av[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(ap);
         }
-        o[j] = acc;
+#pragma unroll
+        for (int j = 0; j < DVF; ++j) {
+          o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[j], phi[t], o[j], 0, 0, 0);
+          o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[j], plo[t], o[j], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < MAXDVT; ++j) {
+        if (j < dvt) {
+          f32x4_t acc = o[j] * alpha;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int row = 16 * t + 4 * g + (r4 >> 2);
+            const int col = dv0 + 16 * j + 4 * (r4 & 3);
+            // generic -> LDS address space (a C-style cast is the address-space cast)
+            lds_bf16x4_t* ap = (lds_bf16x4_t*)((__attribute__((address_space(3))) uint8_t*)kvt +
+                                               row * ROWP + col * 2);
+            const bf16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(ap);
+            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi[t], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo[t], acc, 0, 0, 0);
+          }
+          o[j] = acc;
+        }
       }
     }
   }
@@ -204,7 +241,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
     float* op = p.o_part + ((static_cast<size_t>(n) * p.H + head) * p.splits + sp) * p.dv +
                 dv0 + 4 * g;
 #pragma unroll
-    for (int j = 0; j < MAXDVT; ++j)
+    for (int j = 0; j < (DVF > 0 ? DVF : MAXDVT); ++j)
       if (j < dvt) *reinterpret_cast<f32x4_t*>(op + 16 * j) = o[j];
     if (g == 0 && (wave & 1) == 0)
       p.ml_part[(static_cast<size_t>(n) * p.H + head) * p.splits + sp] = make_float2(m_run, l_run);
@@ -266,7 +303,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
     lse[nh] = Ls > 0.f ? (M + log2f(Ls)) * 0.6931471805599453f : -__builtin_inff();
 }
 
-template <int KK>
+template <int KK, int DVF>
 hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
   AttnParams p;
   p.q = static_cast<const uint16_t*>(a.q);
@@ -284,7 +321,7 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
   p.o_part = a.o_part;
   p.ml_part = reinterpret_cast<float2*>(a.ml_part);
   const dim3 grid(p.splits, (a.H + kHeadBlock - 1) / kHeadBlock, a.N);
-  MISA_LAUNCH(K_ATTN_SPLIT, attn_split_kernel<KK>, grid, dim3(256), 0, st, p);
+  MISA_LAUNCH(K_ATTN_SPLIT, (attn_split_kernel<KK, DVF>), grid, dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   MISA_LAUNCH(K_ATTN_COMBINE, attn_combine_kernel, dim3(a.N * a.H), dim3(256), 0, st,
@@ -295,12 +332,9 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
 
 }  // namespace
 
-// Chunks of 64 selected tokens per workgroup (2: measured best against 1 and
-// 4 at 128 heads x 2048 selected tokens).
 int attn_chunks_per_split(int topk) {
   const int chunks = (topk + kChunkTok - 1) / kChunkTok;
-  constexpr int per = 2;
-  return per < chunks ? per : chunks;
+  return kChunksPerSplit < chunks ? kChunksPerSplit : chunks;
 }
 
 int attn_splits(int topk) {
@@ -309,12 +343,27 @@ int attn_splits(int topk) {
   return (chunks + per - 1) / per;
 }
 
+// d_v of 64, 128, 256 or 512 (value tiles per wavefront 2, 4, 8 or 16) take
+// the fixed forms; other d_v the run-time one.
+template <int KK>
+hipError_t launch_attn_kk(const AttnArgs& a, hipStream_t st) {
+  const int dvt = a.d_v / 32;
+  if (dvt == 2) return launch_attn_t<KK, 2>(a, st);
+  if constexpr (KK >= 4)
+    if (dvt == 4) return launch_attn_t<KK, 4>(a, st);
+  if constexpr (KK >= 8)
+    if (dvt == 8) return launch_attn_t<KK, 8>(a, st);
+  if constexpr (KK >= 16)
+    if (dvt == 16) return launch_attn_t<KK, 16>(a, st);
+  return launch_attn_t<KK, 0>(a, st);
+}
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   switch (a.d_qk) {
-    case 64: return launch_attn_t<2>(a, st);
-    case 128: return launch_attn_t<4>(a, st);
-    case 256: return launch_attn_t<8>(a, st);
-    default: return launch_attn_t<18>(a, st);
+    case 64: return launch_attn_kk<2>(a, st);
+    case 128: return launch_attn_kk<4>(a, st);
+    case 256: return launch_attn_kk<8>(a, st);
+    default: return launch_attn_kk<18>(a, st);
   }
 }
 

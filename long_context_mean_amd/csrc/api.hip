@@ -450,6 +450,33 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* q_scale, const
   return hip_status(misa::launch_topk(ta, st));
 }
 
+// Host checks of misa_pool_route_score_topk (every argument but the
+// workspace): the key index and the route / score workspace parts on success.
+int32_t check_pool_route_score_topk(const void* q, int32_t q_dt, const float* q_scale,
+                                    const float* w, const float* kbar, const void* k,
+                                    const float* k_scale, int32_t k_dt,
+                                    const int32_t* block_table, int32_t page_size,
+                                    const int32_t* q_seq, const int32_t* q_pos,
+                                    const int32_t* len_old, const int32_t* len_new,
+                                    int32_t max_new, int32_t N, int32_t S, int32_t L, int32_t d,
+                                    int32_t B, int32_t H_I, int32_t h, int32_t topk,
+                                    const int32_t* heads, const int32_t* idx,
+                                    misa::KeyIndex* ki, size_t* rb, size_t* sb) {
+  int32_t rc = check_pool(k, k_scale, k_dt, S, L, d, B, kbar);
+  if (rc) return rc;
+  if (!len_old || !len_new) return MISA_ERR_NULL;
+  if (max_new < 0 || max_new > L) return MISA_ERR_SHAPE;
+  if (!q || !w || !q_seq || !q_pos || !heads || !idx) return MISA_ERR_NULL;
+  if ((rc = check_dtypes(q_dt, k_dt, q_scale, k_scale))) return rc;
+  if ((rc = check_sizes(N, S, L, d, H_I))) return rc;
+  if ((rc = key_index(block_table, page_size, L, *ki))) return rc;
+  if (h < 1 || h > H_I || topk < 1 || topk > kMaxTopk) return MISA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k)) return MISA_ERR_SHAPE;
+  *rb = route_score_route_bytes(q_dt, N, L, d, B, H_I);
+  *sb = score_topk_bytes(N, L, topk) + (q_dt == MISA_FP8_E4M3 ? q8_bytes(N, H_I, d) : 0);
+  return MISA_OK;
+}
+
 // ---------------------------------------------------------------- static scratch
 // Device scratch of misa_pool_route_score_topk_scratch, for callers that
 // cannot allocate: one array per GPU the library runs on, held until the
@@ -705,20 +732,13 @@ int32_t misa_pool_route_score_topk(const void* q, int32_t q_dt, const float* q_s
                                    float* head_score, int32_t* idx, float* score, void* ws,
                                    size_t ws_bytes, void* stream) {
   // the checks of both calls, before anything runs
-  int32_t rc = check_pool(k, k_scale, k_dt, S, L, d, B, kbar);
-  if (rc) return rc;
-  if (!len_old || !len_new) return MISA_ERR_NULL;
-  if (max_new < 0 || max_new > L) return MISA_ERR_SHAPE;
-  if (!q || !w || !q_seq || !q_pos || !heads || !idx) return MISA_ERR_NULL;
-  if ((rc = check_dtypes(q_dt, k_dt, q_scale, k_scale))) return rc;
-  if ((rc = check_sizes(N, S, L, d, H_I))) return rc;
   misa::KeyIndex ki;
-  if ((rc = key_index(block_table, page_size, L, ki))) return rc;
-  if (h < 1 || h > H_I || topk < 1 || topk > kMaxTopk) return MISA_ERR_SHAPE;
-  if (!aligned16(q) || !aligned16(k)) return MISA_ERR_SHAPE;
-  const size_t rb = route_score_route_bytes(q_dt, N, L, d, B, H_I);
-  const size_t sb = score_topk_bytes(N, L, topk) +
-                    (q_dt == MISA_FP8_E4M3 ? q8_bytes(N, H_I, d) : 0);
+  size_t rb = 0, sb = 0;
+  int32_t rc = check_pool_route_score_topk(q, q_dt, q_scale, w, kbar, k, k_scale, k_dt,
+                                           block_table, page_size, q_seq, q_pos, len_old,
+                                           len_new, max_new, N, S, L, d, B, H_I, h, topk, heads,
+                                           idx, &ki, &rb, &sb);
+  if (rc) return rc;
   if (!ws) return MISA_ERR_NULL;
   if (ws_bytes < rb + sb) return MISA_ERR_WORKSPACE;
   if (debug_sync()) {
@@ -764,16 +784,16 @@ int32_t misa_pool_route_score_topk_scratch(
     int32_t max_new, int32_t N, int32_t S, int32_t L, int32_t d, int32_t B, int32_t H_I,
     int32_t h, int32_t topk, int32_t* heads, float* head_score, int32_t* idx, float* score,
     void* stream) {
-  // the call's own checks first: with a zero-byte workspace (never touched)
-  // only its workspace check fails, after every other check, and nothing runs
-  int32_t rc = misa_pool_route_score_topk(
-      q, q_dt, q_scale, w, kbar, k, k_scale, k_dt, block_table, page_size, q_seq, q_pos, len_old,
-      len_new, max_new, N, S, L, d, B, H_I, h, topk, heads, head_score, idx, score,
-      reinterpret_cast<void*>(uintptr_t{256}), 0, stream);
-  if (rc != MISA_ERR_WORKSPACE) return rc;
-  const size_t need =
-      misa_workspace_bytes(MISA_OP_ROUTE_SCORE_TOPK, q_dt, N, L, d, H_I, B, topk, 0);
-  if (need > kScratchBytes) return MISA_ERR_WORKSPACE;
+  // the workspace call's own checks, then its workspace size against the
+  // scratch array's
+  misa::KeyIndex ki;
+  size_t rb = 0, sb = 0;
+  int32_t rc = check_pool_route_score_topk(q, q_dt, q_scale, w, kbar, k, k_scale, k_dt,
+                                           block_table, page_size, q_seq, q_pos, len_old,
+                                           len_new, max_new, N, S, L, d, B, H_I, h, topk, heads,
+                                           idx, &ki, &rb, &sb);
+  if (rc) return rc;
+  if (rb + sb > kScratchBytes) return MISA_ERR_WORKSPACE;
   void* ws = nullptr;
   if ((rc = scratch_of_current_device(&ws))) return rc;
   return misa_pool_route_score_topk(q, q_dt, q_scale, w, kbar, k, k_scale, k_dt, block_table,

@@ -238,11 +238,13 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
     }
   }
   if (hv) {
+    // the partials are read once, by the combine kernel: non-temporal stores
+    // keep them from displacing cached data
     float* op = p.o_part + ((static_cast<size_t>(n) * p.H + head) * p.splits + sp) * p.dv +
                 dv0 + 4 * g;
 #pragma unroll
     for (int j = 0; j < (DVF > 0 ? DVF : MAXDVT); ++j)
-      if (j < dvt) *reinterpret_cast<f32x4_t*>(op + 16 * j) = o[j];
+      if (j < dvt) __builtin_nontemporal_store(o[j], reinterpret_cast<f32x4_t*>(op + 16 * j));
     if (g == 0 && (wave & 1) == 0)
       p.ml_part[(static_cast<size_t>(n) * p.H + head) * p.splits + sp] = make_float2(m_run, l_run);
   }
@@ -278,14 +280,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
   const float* op = o_part + nh * splits * dv;
   // splits in groups of 8 independent loads (a split with no selected token
-  // holds zeros, so its weight may be anything finite)
+  // holds zeros, so its weight may be anything finite); the partials are
+  // read once, non-temporally
   for (int d = threadIdx.x; d < dv; d += 256) {
     float acc = 0.f;
     int i = 0;
     for (; i + 8 <= splits; i += 8) {
       float v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = op[static_cast<size_t>(i + u) * dv + d];
+      for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(&op[static_cast<size_t>(i + u) * dv + d]);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int k = i + u;
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
     }
     for (; i < splits; ++i) {
       const float wgt = i < 1024 ? wsh[i] : (M == -__builtin_inff() ? 0.f : exp2f(ml[i].x - M));
-      acc += wgt * op[static_cast<size_t>(i) * dv + d];
+      acc += wgt * __builtin_nontemporal_load(&op[static_cast<size_t>(i) * dv + d]);
     }
     out[nh * dv + d] = acc * inv;
   }

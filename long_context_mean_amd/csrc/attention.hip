@@ -260,6 +260,20 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   __shared__ float red[4];
   const size_t nh = blockIdx.x;
   const float2* ml = ml_part + nh * splits;
+  const float* op = o_part + nh * splits * dv;
+  // the first PS splits of this thread's (at most two: d_v <= 512) output
+  // columns, loaded before the weights are known: unconditional loads of
+  // clamped (valid) addresses, so they are all in flight together; the
+  // partials are read once, non-temporally
+  constexpr int PS = 16;
+  float pv[2][PS];
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+    const int d = min(static_cast<int>(threadIdx.x) + 256 * c2, dv - 1);
+#pragma unroll
+    for (int u = 0; u < PS; ++u)
+      pv[c2][u] = __builtin_nontemporal_load(&op[static_cast<size_t>(min(u, splits - 1)) * dv + d]);
+  }
   float M = -__builtin_inff();
   for (int i = threadIdx.x; i < splits; i += 256) M = fmaxf(M, ml[i].x);
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
@@ -278,28 +292,31 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   __syncthreads();
   Ls = red[0] + red[1] + red[2] + red[3];
   const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-  const float* op = o_part + nh * splits * dv;
-  // splits in groups of 8 independent loads (a split with no selected token
-  // holds zeros, so its weight may be anything finite); the partials are
-  // read once, non-temporally
-  for (int d = threadIdx.x; d < dv; d += 256) {
+  auto weight = [&](int k) {
+    return k < 1024 ? wsh[k] : (M == -__builtin_inff() ? 0.f : exp2f(ml[k].x - M));
+  };
+  // splits in order (a split with no selected token holds zeros, so its
+  // weight may be anything finite); past the prefetched ones in groups of 8
+  // independent loads
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+    const int d = static_cast<int>(threadIdx.x) + 256 * c2;
+    if (d >= dv) break;
     float acc = 0.f;
-    int i = 0;
+#pragma unroll
+    for (int u = 0; u < PS; ++u)
+      if (u < splits) acc += weight(u) * pv[c2][u];
+    int i = PS;
     for (; i + 8 <= splits; i += 8) {
       float v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(&op[static_cast<size_t>(i + u) * dv + d]);
+      for (int u = 0; u < 8; ++u)
+        v[u] = __builtin_nontemporal_load(&op[static_cast<size_t>(i + u) * dv + d]);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = i + u;
-        const float wgt = k < 1024 ? wsh[k] : (M == -__builtin_inff() ? 0.f : exp2f(ml[k].x - M));
-        acc += wgt * v[u];
-      }
+      for (int u = 0; u < 8; ++u) acc += weight(i + u) * v[u];
     }
-    for (; i < splits; ++i) {
-      const float wgt = i < 1024 ? wsh[i] : (M == -__builtin_inff() ? 0.f : exp2f(ml[i].x - M));
-      acc += wgt * __builtin_nontemporal_load(&op[static_cast<size_t>(i) * dv + d]);
-    }
+    for (; i < splits; ++i)
+      acc += weight(i) * __builtin_nontemporal_load(&op[static_cast<size_t>(i) * dv + d]);
     out[nh * dv + d] = acc * inv;
   }
   if (threadIdx.x == 0)

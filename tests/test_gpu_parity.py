@@ -862,9 +862,12 @@ def _check_attention(p, out, lse, ref=None):
 
 @pytest.mark.parametrize("H,d_qk,d_v,topk", [(128, 576, 512, 300), (16, 128, 128, 2048),
                                               (48, 256, 96, 130), (32, 64, 32, 64),
-                                              (32, 576, 256, 200), (16, 64, 64, 100)])
+                                              (32, 576, 256, 200), (16, 64, 64, 100),
+                                              (16, 128, 128, 2600), (32, 576, 512, 3000)])
 def test_sparse_attention_parity(H, d_qk, d_v, topk):
-    """Value widths 64/128/256/512 (compile-time value tiles) and 32/96 (run-time)."""
+    """Value widths 64/128/256/512 (compile-time value tiles) and 32/96 (run-time);
+    up to 24 splits of 128 selected tokens (the combine's loads past its first 16
+    splits: a group of 8, and a ragged tail)."""
     L = 3000
     nv = np.array([topk, min(topk, 77), 1, 0, max(1, topk - 5)])
     p = synth.attention_problem("attn", 101 + H, N=5, S=2, L=L, H=H, d_qk=d_qk, d_v=d_v,

@@ -419,8 +419,7 @@ int32_t score_topk_impl(const void* q, int32_t q_dt, const float* q_scale, const
     mp.cand_out = cand;
     mp.cap = cap;
     if ((e = misa::launch_prefill(mp, st)) != hipSuccess) return hip_status(e);
-    misa::CandTopkArgs ca{cnt, cand, splits, cap, q_pos, N, L, topk, qb, rflag, bflag, idx,
-                          score};
+    misa::CandTopkArgs ca{cnt, cand, splits, cap, q_pos, N, topk, qb, rflag, bflag, idx, score};
     if ((e = misa::launch_cand_topk(ca, st)) != hipSuccess) return hip_status(e);
     misa::PrefillArgs fp = prefill_args(u, lay.u_stride);
     fp.block_flag = bflag;

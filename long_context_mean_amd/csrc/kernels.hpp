@@ -226,15 +226,15 @@ hipError_t launch_tau(const TauArgs& a, hipStream_t st);
 
 // Exact top-k of each row from its candidate list (the scores >= tau[n]).  A row
 // whose candidates cannot prove the result (a split list overflowed, fewer
-// than min(topk, L_n) candidates, too many candidates or ties for the LDS
-// path) is flagged in row_flag[n] and block_flag[n / rows_per_block] and left
-// to the full path; other rows get idx/score written and row_flag[n] = 0.
+// than min(topk, L_n) candidates, or more than the per-row capacity) is
+// flagged in row_flag[n] and block_flag[n / rows_per_block] and left to the
+// full path; other rows get idx/score written and row_flag[n] = 0.
 struct CandTopkArgs {
   const uint32_t* cnt;
   const uint2* cand;
   int splits, cap;
   const int32_t* q_pos;
-  int N, L, topk, rows_per_block;     // L: longest row length
+  int N, topk, rows_per_block;
   uint32_t* row_flag;
   uint32_t* block_flag;
   int32_t* idx;

@@ -473,25 +473,27 @@ __device__ __forceinline__ uint32_t block_prefix1(uint32_t v, uint32_t* sm, uint
   return before + incl - v;
 }
 
-// The bin of a 4096-bin histogram (bin 4095 = largest keys) holding the K-th
-// largest element, 1 <= K <= its total, with two barriers (the histogram's
-// updates must be complete, i.e. a barrier between them and this call).
-// res[0] = bin, res[1] = rank of the element inside the bin (1-based).
-template <int NT>
+// The bin of an NBINS-bin histogram (bin NBINS-1 = largest keys) holding the
+// K-th largest element, 1 <= K <= its total, with two barriers (the
+// histogram's updates must be complete, i.e. a barrier between them and this
+// call).  res[0] = bin, res[1] = rank of the element inside the bin (1-based).
+template <int NT, int NBINS>
 __device__ __forceinline__ void locate_bin(const uint32_t* hist, uint32_t K, uint32_t* sm,
                                            uint32_t* res) {
-  constexpr int PER = kBins0 / NT;
-  const int lo = kBins0 - (static_cast<int>(threadIdx.x) + 1) * PER;
+  constexpr int PER = NBINS >= NT ? NBINS / NT : 1;
+  const int t = static_cast<int>(threadIdx.x);
+  const bool owner = NBINS >= NT || t < NBINS;
+  const int lo = NBINS - (t + 1) * PER;
   uint32_t vb[PER];
   uint32_t c = 0;
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
-    vb[q] = hist[lo + q];
+    vb[q] = owner ? hist[lo + q] : 0u;
     c += vb[q];
   }
   uint32_t total;
   const uint32_t above = block_prefix1<NT>(c, sm, total);
-  if (above < K && K <= above + c) {
+  if (owner && above < K && K <= above + c) {
     uint32_t acc = above;
 #pragma unroll
     for (int q = PER - 1; q >= 0; --q) {
@@ -505,43 +507,28 @@ __device__ __forceinline__ void locate_bin(const uint32_t* hist, uint32_t K, uin
   __syncthreads();
 }
 
-__global__ __launch_bounds__(1024) void topk_small_kernel(
-    const uint32_t* __restrict__ u, int u_stride, const int32_t* __restrict__ q_pos,
-    int fixed_len, int topk, const int32_t* __restrict__ cand, int cand_stride,
-    int32_t* __restrict__ idx, float* __restrict__ score) {
-  constexpr int NT = 1024;
-  __shared__ __align__(16) uint32_t hA[kBins0];
-  __shared__ __align__(16) uint32_t hA2[kBins0];
-  __shared__ __align__(16) uint32_t hB[kBins0];
-  __shared__ uint32_t sm[4][16];
-  __shared__ uint32_t res[3][4];
-  __shared__ uint32_t wmin[16], wmax[16];
-  const int n = blockIdx.x, tid = threadIdx.x;
-  const int len = row_len(q_pos, fixed_len, n);
-  const uint32_t* row = u + static_cast<size_t>(n) * u_stride;
-  const int32_t* cand_row = cand ? cand + static_cast<size_t>(n) * cand_stride : nullptr;
-  int32_t* idx_row = idx + static_cast<size_t>(n) * topk;
-  float* score_row = score ? score + static_cast<size_t>(n) * topk : nullptr;
-  const int i0 = tid * kPerThread;
-  uint32_t v[kPerThread];
-  int32_t ct[kPerThread];                     // the elements' output indices
-  if (i0 < len) {
-    load16(row, i0, len, v);                  // in bounds: rows are padded to whole chunks
-  } else {
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) v[j] = 0u;
-  }
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j)
-    ct[j] = cand_row ? (i0 + j < len ? cand_row[i0 + j] : -1) : i0 + j;
+// The selection of one row whose elements sit in registers: thread t holds
+// elements PT*t .. PT*t+PT-1 (in index order, PT <= 32) as order keys v (0 = empty) and
+// their output indices ct; the min(topk, valid) first under (key desc, index
+// asc) are written in index order to idx_row / score_row, then the padding.
+// NT threads; LDS: two 4096-word histograms and a 256-word one, sm
+// [4][NT/64], res [3][4], wmin / wmax [NT/64].
+template <int NT, int PT>
+__device__ __forceinline__ void select_in_registers(const uint32_t (&v)[PT],
+                                                    const int32_t (&ct)[PT], int topk,
+                                                    int32_t* idx_row, float* score_row,
+                                                    uint32_t* hA, uint32_t* hA2, uint32_t* hB,
+                                                    uint32_t (*sm)[NT / 64], uint32_t (*res)[4],
+                                                    uint32_t* wmin, uint32_t* wmax) {
+  const int tid = static_cast<int>(threadIdx.x);
   for (int b = tid; b < kBins0; b += NT) {
     hA[b] = 0u;
     hA2[b] = 0u;
-    hB[b] = 0u;
   }
+  if (tid < kBins2) hB[tid] = 0u;
   uint32_t lo = 0xFFFFFFFFu, hi = 0u, nv = 0;
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
+  for (int j = 0; j < PT; ++j) {
     if (v[j] != 0u) {
       lo = min(lo, v[j]);
       hi = max(hi, v[j]);
@@ -573,32 +560,32 @@ __global__ __launch_bounds__(1024) void topk_small_kernel(
     while ((range >> sA) >= static_cast<uint32_t>(kBins0)) ++sA;
     const int sB = sA > 12 ? sA - 12 : 0;
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j)
+    for (int j = 0; j < PT; ++j)
       if (v[j] != 0u) atomicAdd(&hA[(v[j] - base) >> sA], 1u);
     __syncthreads();
-    locate_bin<NT>(hA, K, sm[1], res[0]);
+    locate_bin<NT, kBins0>(hA, K, sm[1], res[0]);
     const uint32_t dA = res[0][0];
     uint32_t r = res[0][1], dB = 0, dC = 0;
     n_eq = hA[dA];
     if (sA > 0) {
       const uint32_t mB = (1u << (sA - sB)) - 1u;
 #pragma unroll
-      for (int j = 0; j < kPerThread; ++j)
+      for (int j = 0; j < PT; ++j)
         if (v[j] != 0u && ((v[j] - base) >> sA) == dA)
           atomicAdd(&hA2[((v[j] - base) >> sB) & mB], 1u);
       __syncthreads();
-      locate_bin<NT>(hA2, r, sm[2], res[1]);
+      locate_bin<NT, kBins0>(hA2, r, sm[2], res[1]);
       dB = res[1][0];
       r = res[1][1];
       n_eq = hA2[dB];
       if (sB > 0) {                           // sB <= 8
         const uint32_t preB = (dA << (sA - sB)) | dB;
 #pragma unroll
-        for (int j = 0; j < kPerThread; ++j)
+        for (int j = 0; j < PT; ++j)
           if (v[j] != 0u && ((v[j] - base) >> sB) == preB)
             atomicAdd(&hB[(v[j] - base) & ((1u << sB) - 1u)], 1u);
         __syncthreads();
-        locate_bin<NT>(hB, r, sm[3], res[2]);
+        locate_bin<NT, kBins2>(hB, r, sm[3], res[2]);
         dC = res[2][0];
         r = res[2][1];
         n_eq = hB[dC];
@@ -613,14 +600,14 @@ __global__ __launch_bounds__(1024) void topk_small_kernel(
   if (K2 != n_eq) {
     uint32_t ties = 0;
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) ties += (v[j] == T) ? 1u : 0u;
+    for (int j = 0; j < PT; ++j) ties += (v[j] == T) ? 1u : 0u;
     uint32_t tie_tot;
     __syncthreads();                          // sm[0] is free again
     tie_rank = block_prefix1<NT>(ties, sm[0], tie_tot);
   }
   uint32_t sel = 0, nsel = 0;
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
+  for (int j = 0; j < PT; ++j) {
     const bool eq = K > 0 && v[j] == T;
     const bool win = (K > 0 && v[j] > T) || (eq && tie_rank < K2);
     tie_rank += eq ? 1u : 0u;
@@ -631,7 +618,7 @@ __global__ __launch_bounds__(1024) void topk_small_kernel(
   // (sm[1]'s readers in the first level's locate_bin passed its closing barrier)
   uint32_t pos = block_prefix1<NT>(nsel, sm[1], tot);
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
+  for (int j = 0; j < PT; ++j) {
     if ((sel >> j) & 1u) {
       idx_row[pos] = ct[j];
       if (score_row) score_row[pos] = key_score(v[j]);
@@ -642,6 +629,40 @@ __global__ __launch_bounds__(1024) void topk_small_kernel(
     idx_row[i] = -1;
     if (score_row) score_row[i] = -__builtin_inff();
   }
+}
+
+
+__global__ __launch_bounds__(1024) void topk_small_kernel(
+    const uint32_t* __restrict__ u, int u_stride, const int32_t* __restrict__ q_pos,
+    int fixed_len, int topk, const int32_t* __restrict__ cand, int cand_stride,
+    int32_t* __restrict__ idx, float* __restrict__ score) {
+  constexpr int NT = 1024;
+  __shared__ __align__(16) uint32_t hA[kBins0];
+  __shared__ __align__(16) uint32_t hA2[kBins0];
+  __shared__ __align__(16) uint32_t hB[kBins2];
+  __shared__ uint32_t sm[4][NT / 64];
+  __shared__ uint32_t res[3][4];
+  __shared__ uint32_t wmin[NT / 64], wmax[NT / 64];
+  const int n = blockIdx.x, tid = threadIdx.x;
+  const int len = row_len(q_pos, fixed_len, n);
+  const uint32_t* row = u + static_cast<size_t>(n) * u_stride;
+  const int32_t* cand_row = cand ? cand + static_cast<size_t>(n) * cand_stride : nullptr;
+  int32_t* idx_row = idx + static_cast<size_t>(n) * topk;
+  float* score_row = score ? score + static_cast<size_t>(n) * topk : nullptr;
+  const int i0 = tid * kPerThread;
+  uint32_t v[kPerThread];
+  int32_t ct[kPerThread];                     // the elements' output indices
+  if (i0 < len) {
+    load16(row, i0, len, v);                  // in bounds: rows are padded to whole chunks
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) v[j] = 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j)
+    ct[j] = cand_row ? (i0 + j < len ? cand_row[i0 + j] : -1) : i0 + j;
+  select_in_registers<NT, kPerThread>(v, ct, topk, idx_row, score_row, hA, hA2, hB, sm, res,
+                                      wmin, wmax);
 }
 
 __global__ void topk_clear_kernel(uint32_t* __restrict__ p, size_t n_words) {
@@ -856,35 +877,37 @@ __global__ __launch_bounds__(256) void topk_tau_kernel(const uint32_t* __restric
   }
 }
 
-// One 512-thread workgroup per row; each thread keeps up to kCandPer
-// candidates in registers.  Dynamic LDS: the row's winner bitmap (nwords_max
-// words) and a 16-bit per-word prefix of marked bits.
+// One 512-thread workgroup per row.  The row's candidate lists, concatenated
+// split after split, are in ascending token order (each list in key order,
+// the splits in key-range order), so thread t takes the concatenated
+// candidates 16t .. 16t+15 into registers and the row is selected like a
+// short row (select_in_registers): a row of up to kCandRow candidates, its
+// outputs already in token order.  (Measured: 3 of these workgroups per CU
+// beat 2 of 1024 threads with 8 candidates each, and 4 capped at 64 VGPRs,
+// which spill.)
 constexpr int kCandThreads = 512;
-constexpr int kCandMaxK = kBins0 / 2;    // selected per row (outputs staged in hA)
-constexpr int kCandPer = kCandRow / kCandThreads;
+constexpr int kCandPer = kPerThread;     // candidates per thread
+constexpr int kCandMaxK = kBins0 / 2;    // selected per row at most
+static_assert(kCandThreads * kCandPer >= kCandRow, "a row's candidates fit the registers");
 
-__global__ __launch_bounds__(kCandThreads, 8) void topk_cand_kernel(
+__global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
     const uint32_t* __restrict__ cnt, const uint2* __restrict__ cand, int splits, int cap,
-    const int32_t* __restrict__ q_pos, int topk, int rows_per_block, int nwords_max,
+    const int32_t* __restrict__ q_pos, int topk, int rows_per_block,
     uint32_t* __restrict__ row_flag, uint32_t* __restrict__ block_flag,
     int32_t* __restrict__ idx, float* __restrict__ score) {
-  extern __shared__ __align__(16) uint32_t dyn[];
+  constexpr int NT = kCandThreads;
   __shared__ __align__(16) uint32_t hA[kBins0];
+  __shared__ __align__(16) uint32_t hA2[kBins0];
   __shared__ __align__(16) uint32_t hB[kBins2];
   __shared__ uint32_t spre[257];
-  __shared__ uint32_t tpre[kCandThreads];
-  __shared__ uint16_t bsplit[kCandRow / 32];
-  __shared__ uint32_t sm[kCandThreads / 64];
-  __shared__ uint32_t res[4];
+  __shared__ uint32_t sm[4][NT / 64];
+  __shared__ uint32_t res[3][4];
+  __shared__ uint32_t wmin[NT / 64], wmax[NT / 64];
   __shared__ uint32_t bad;
-  constexpr int NT = kCandThreads;
-  uint32_t* bm = dyn;
-  uint16_t* wpre = reinterpret_cast<uint16_t*>(dyn + nwords_max);
   const int n = blockIdx.x;
   const int tid = threadIdx.x;
   const int len = q_pos[n] + 1;
   const uint32_t K = static_cast<uint32_t>(min(topk, len));
-  const int nwords = (len + 31) / 32;
   // split counts -> offsets; overflow check
   uint32_t cs = 0;
   if (tid < splits) cs = cnt[static_cast<size_t>(n) * splits + tid];
@@ -892,12 +915,11 @@ __global__ __launch_bounds__(kCandThreads, 8) void topk_cand_kernel(
   __syncthreads();
   if (cs > static_cast<uint32_t>(cap)) bad = 1u;
   uint32_t total;
-  const uint32_t before = block_excl_scan<NT>(cs, sm, total);
+  const uint32_t before = block_excl_scan<NT>(cs, sm[0], total);
   if (tid < splits) spre[tid] = before;
   if (tid == 0) spre[splits] = total;
   __syncthreads();
-  const bool flag = bad != 0u || total < K || total > static_cast<uint32_t>(kCandRow) ||
-                    nwords > nwords_max;
+  const bool flag = bad != 0u || total < K || total > static_cast<uint32_t>(kCandRow);
   if (flag) {
     if (tid == 0) {
       row_flag[n] = 1u;
@@ -905,130 +927,49 @@ __global__ __launch_bounds__(kCandThreads, 8) void topk_cand_kernel(
     }
     return;
   }
-  // register slots holding candidates (a uniform bound: slots past it are
-  // skipped by the whole workgroup)
-  const int nsl = __builtin_amdgcn_readfirstlane(static_cast<int>((total + NT - 1) / NT));
-  // split of every 32nd element (element j lives in split s with
-  // spre[s] <= j < spre[s + 1]; empty splits have spre[s] == spre[s + 1])
-  if (tid < kCandRow / 32 && 32 * tid < static_cast<int>(total)) {
-    const uint32_t j = 32u * tid;
+  // this thread's candidates p0 .. p0+15 (positions past the total read the
+  // last candidate and are marked empty): the list holding each position is
+  // the last split s with spre[s] <= p, found by bisection for the first and
+  // by stepping for the rest; then the 16 loads, all in flight together
+  const int p0 = tid * kCandPer;
+  const int last = static_cast<int>(total) - 1;
+  int sp;
+  {
+    const uint32_t p = static_cast<uint32_t>(min(p0, last));
     int lo = 0, hi = splits - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (spre[mid] <= j) lo = mid; else hi = mid - 1;
+      if (spre[mid] <= p) lo = mid; else hi = mid - 1;
     }
-    bsplit[tid] = static_cast<uint16_t>(lo);
+    sp = lo;
   }
-  __syncthreads();
-  // candidates into registers: element j = tid + NT * i, its split found from
-  // the one of element 32 * (j / 32) forward; key 0 marks an empty slot
-  uint32_t ck[kCandPer], cx[kCandPer];
+  uint32_t off[kCandPer];
 #pragma unroll
-  for (int i = 0; i < kCandPer && i < nsl; ++i) {
-    const int j = tid + NT * i;
-    ck[i] = 0u;
-    cx[i] = 0u;
-    if (j < static_cast<int>(total)) {
-      int lo = bsplit[j >> 5];
-      while (spre[lo + 1] <= static_cast<uint32_t>(j)) ++lo;
-      const uint2 e = cand[(static_cast<size_t>(n) * splits + lo) * cap + (j - spre[lo])];
-      ck[i] = order_key(__uint_as_float(e.x));
-      cx[i] = e.y;
-    }
+  for (int j = 0; j < kCandPer; ++j) {
+    const uint32_t p = static_cast<uint32_t>(min(p0 + j, last));
+    while (spre[sp + 1] <= p) ++sp;
+    off[j] = static_cast<uint32_t>(sp) * static_cast<uint32_t>(cap) + (p - spre[sp]);
   }
-  for (int b = tid; b < kBins0; b += NT) hA[b] = 0u;
-  if (tid < kBins2) hB[tid] = 0u;
-  __syncthreads();
-  // exact threshold: three radix levels over the candidates
+  const uint2* crow = cand + static_cast<size_t>(n) * splits * cap;
+  uint32_t v[kCandPer];
+  int32_t ct[kCandPer];
 #pragma unroll
-  for (int i = 0; i < kCandPer && i < nsl; ++i)
-    if (ck[i] != 0u) atomicAdd(&hA[ck[i] >> kShift0], 1u);
-  __syncthreads();
-  find_digit<NT, kBins0>(hA, K, false, sm, res);
-  const uint32_t d0 = res[0], r0 = res[1];
-  for (int b = tid; b < kBins1; b += NT) hA[b] = 0u;
-  __syncthreads();
+  for (int j = 0; j < kCandPer; ++j) {
+    const uint2 e = crow[off[j]];
+    v[j] = e.x;
+    ct[j] = static_cast<int32_t>(e.y);
+  }
 #pragma unroll
-  for (int i = 0; i < kCandPer && i < nsl; ++i)
-    if (ck[i] != 0u && (ck[i] >> kShift0) == d0) atomicAdd(&hA[(ck[i] >> kShift1) & (kBins1 - 1)], 1u);
-  __syncthreads();
-  find_digit<NT, kBins1>(hA, r0, false, sm, res);
-  const uint32_t d1 = res[0], r1 = res[1];
-  const uint32_t pre = (d0 << kDigit1Bits) | d1;
-#pragma unroll
-  for (int i = 0; i < kCandPer && i < nsl; ++i)
-    if (ck[i] != 0u && (ck[i] >> kShift1) == pre) atomicAdd(&hB[ck[i] & (kBins2 - 1)], 1u);
-  __syncthreads();
-  find_digit<NT, kBins2>(hB, r1, false, sm, res);
-  const uint32_t T = (d0 << kShift0) | (d1 << kShift1) | res[0];
-  const uint32_t K2 = res[1];
-  const uint32_t n_eq = hB[res[0]];
-  __syncthreads();
-  // ties at T: the K2 lowest token indices win (radix select on the indices,
-  // which are < 2^18 here: bits 6..17, then 0..5)
-  uint32_t cut = 0xFFFFFFFFu;
-  if (n_eq != K2) {
-    for (int b = tid; b < kBins0; b += NT) hA[b] = 0u;
-    if (tid < 64) hB[tid] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kCandPer && i < nsl; ++i)
-      if (ck[i] == T) atomicAdd(&hA[cx[i] >> 6], 1u);
-    __syncthreads();
-    find_digit<NT, kBins0>(hA, n_eq - K2 + 1u, false, sm, res);
-    const uint32_t dA = res[0], rA = res[1];
-#pragma unroll
-    for (int i = 0; i < kCandPer && i < nsl; ++i)
-      if (ck[i] == T && (cx[i] >> 6) == dA) atomicAdd(&hB[cx[i] & 63u], 1u);
-    __syncthreads();
-    find_digit<NT, 64>(hB, rA, false, sm, res);
-    cut = (dA << 6) | res[0];
+  for (int j = 0; j < kCandPer; ++j) {
+    const bool ok = p0 + j <= last;
+    v[j] = ok ? order_key(__uint_as_float(v[j])) : 0u;
+    ct[j] = ok ? ct[j] : -1;
   }
   if (tid == 0) row_flag[n] = 0u;
-  for (int w = tid; w < nwords; w += NT) bm[w] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kCandPer && i < nsl; ++i)
-    if (ck[i] > T || (ck[i] == T && ck[i] != 0u && cx[i] <= cut))
-      atomicOr(&bm[cx[i] >> 5], 1u << (cx[i] & 31));
-  __syncthreads();
-  // output position of a winner = marked bits before it: thread prefix over
-  // wpt consecutive words, plus a 16-bit prefix inside the thread's words
-  const int wpt = (nwords + NT - 1) / NT;
-  uint32_t mine = 0;
-  for (int q = 0; q < wpt; ++q) {
-    const int w = tid * wpt + q;
-    if (w < nwords) {
-      wpre[w] = static_cast<uint16_t>(mine);
-      mine += __popc(bm[w]);
-    }
-  }
-  uint32_t tot;
-  tpre[tid] = block_excl_scan<NT>(mine, sm, tot);
-  __syncthreads();
-  // winners to their output slots in LDS (hA: indices, then keys), then out
-  // in order with contiguous stores
-  uint32_t* oidx = hA;
-  uint32_t* okey = hA + kCandMaxK;
-#pragma unroll
-  for (int i = 0; i < kCandPer && i < nsl; ++i) {
-    const uint32_t e = cx[i];
-    if (ck[i] == 0u) continue;
-    const int w = static_cast<int>(e >> 5);
-    const uint32_t word = bm[w];
-    if (!((word >> (e & 31)) & 1u)) continue;
-    const uint32_t pos = tpre[w / wpt] + wpre[w] + __popc(word & ((1u << (e & 31)) - 1u));
-    oidx[pos] = e;
-    okey[pos] = ck[i];
-  }
-  __syncthreads();
   int32_t* idx_row = idx + static_cast<size_t>(n) * topk;
   float* score_row = score ? score + static_cast<size_t>(n) * topk : nullptr;
-  for (int i = tid; i < topk; i += NT) {
-    const bool sel = i < static_cast<int>(K);
-    idx_row[i] = sel ? static_cast<int32_t>(oidx[i]) : -1;
-    if (score_row) score_row[i] = sel ? key_score(okey[i]) : -__builtin_inff();
-  }
+  select_in_registers<NT, kCandPer>(v, ct, topk, idx_row, score_row, hA, hA2, hB, sm, res, wmin,
+                                    wmax);
 }
 
 }  // namespace
@@ -1088,12 +1029,9 @@ hipError_t launch_tau(const TauArgs& a, hipStream_t st) {
 
 hipError_t launch_cand_topk(const CandTopkArgs& a, hipStream_t st) {
   if (a.splits < 1 || a.splits > 256 || a.topk > kCandMaxK) return hipErrorInvalidValue;
-  // bitmap + 16-bit word prefix for the longest row (longer rows are flagged)
-  const int nwords_max = min((a.L + 31) / 32, kBitmapWords);
-  const size_t lds = static_cast<size_t>(nwords_max) * 4 + (static_cast<size_t>(nwords_max) * 2 + 15) / 16 * 16;
-  MISA_LAUNCH(K_TOPK_CAND, topk_cand_kernel, dim3(a.N), dim3(kCandThreads), lds, st, a.cnt,
-              a.cand, a.splits, a.cap, a.q_pos, a.topk, a.rows_per_block, nwords_max, a.row_flag,
-              a.block_flag, a.idx, a.score);
+  MISA_LAUNCH(K_TOPK_CAND, topk_cand_kernel, dim3(a.N), dim3(kCandThreads), 0, st, a.cnt, a.cand,
+              a.splits, a.cap, a.q_pos, a.topk, a.rows_per_block, a.row_flag, a.block_flag, a.idx,
+              a.score);
   return hipGetLastError();
 }
 

@@ -782,9 +782,10 @@ def main():
         del r5
         torch.cuda.empty_cache()
         log("[bench] prefill chunk at L=128K (4096 rows): routed and dense 64-head steps")
-        pl = prefill_measure(torch, "c3x", h, 10, 2)
+        pl = prefill_measure(torch, "c3x", h, 30, 3)
         extra["prefill_c3x"] = {
             "workload": pl["config"]["workload"], "ms_per_step": pl["ms_per_step"],
+            "step_us_percentiles": pl["extra"]["step_us_percentiles"],
             "pairs_per_s": pl["value"], "dense_ms": pl["extra"]["dense_ms"],
             "speedup_vs_dense": pl["extra"]["speedup_vs_dense"],
             "kernel_ms": pl["extra"]["kernel_ms"],

@@ -14,9 +14,11 @@ constexpr int kBins0 = 1 << kDigit0Bits, kBins1 = 1 << kDigit1Bits, kBins2 = 1 <
 constexpr int kShift0 = 32 - kDigit0Bits;                 // 20
 constexpr int kShift1 = kShift0 - kDigit1Bits;            // 8
 // Per-row words of the level-0 histogram region in the workspace: 4096 bins,
-// then the candidate count, padded to keep rows 256-byte aligned.
+// then the candidate count and the selection's level-0 digit, its rank and K
+// (written by the collect step), padded to keep rows 256-byte aligned.
 constexpr int kHistWords = kBins0 + 64;
 constexpr int kCandCountOffset = kBins0;
+constexpr int kMetaOffset = kCandCountOffset + 1;
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;

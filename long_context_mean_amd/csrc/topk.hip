@@ -14,12 +14,14 @@
 //    the k-th key; elements above it are certain winners and are recorded in
 //    a bitmap (each chunk writes its own words, no atomics); elements in bin
 //    d0 are appended to a short candidate list.
-//  topk_final (one 1024-thread workgroup per row) loads the bitmap and the
-//    candidates into LDS, resolves the exact threshold among the candidates
-//    with two more radix levels, marks the candidate winners in the bitmap
-//    and emits every marked element in index order.  When the candidates do
-//    not fit in LDS (heavily tied scores) or the row is very long, the same
-//    workgroup falls back to a full radix select over the row.
+//  topk_final (grid: 32768-element slices x rows, 1024 threads) loads the
+//    candidates into LDS and resolves the exact threshold among them with two
+//    more radix levels (every workgroup of a row finds the same one), counts
+//    the winners before its slice (bitmap words and candidates), marks the
+//    candidate winners inside it and emits the slice's winners in index
+//    order, a bitmap word per thread.  When the candidates do not fit in LDS
+//    (heavily tied scores) or the row is very long, the row's first workgroup
+//    falls back to a full radix select over the row.
 // Many rows or short rows (prefill, rerank): topk_row, one 1024-thread
 //    workgroup per row with every histogram in LDS.
 #include "common.hpp"
@@ -281,6 +283,13 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(
   load16(row, i0, len, v);
   find_digit<256, kBins0>(h0, static_cast<uint32_t>(topk), true, sm, res);
   const uint32_t K = res[2], d0 = res[0];
+  // the final workgroups read the digit, its rank and K instead of scanning
+  // the histogram again
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    h0[kMetaOffset] = d0;
+    h0[kMetaOffset + 1] = res[1];
+    h0[kMetaOffset + 2] = K;
+  }
   if (K == 0) return;
   uint32_t sure = 0, n_cand = 0;
 #pragma unroll
@@ -314,128 +323,135 @@ __global__ __launch_bounds__(NT) void topk_final_kernel(
     int fixed_len, const uint32_t* hist, const uint32_t* __restrict__ bitmap,
     const uint2* __restrict__ clist, int topk, int32_t* __restrict__ idx,
     float* __restrict__ score) {
-  __shared__ __align__(16) uint32_t bm[kBitmapWords];   // winners, one bit per element
+  constexpr int kSlice = 32 * NT;                       // elements per workgroup, a word per thread
+  static_assert(kBitmapWords == 8 * NT, "two 16-byte bitmap loads per thread cover the row");
+  __shared__ __align__(16) uint32_t bm[NT];             // the slice's winners, one bit per element
   __shared__ __align__(16) uint32_t cu[kCandCap];       // candidate order key
   __shared__ __align__(16) uint32_t ci[kCandCap];       // candidate element index
   __shared__ __align__(16) uint32_t hA[kBins0];
   __shared__ __align__(16) uint32_t hB[kBins2];
   __shared__ uint32_t sm[16];
   __shared__ uint32_t res[4];
-  const int n = blockIdx.x;
+  __shared__ uint32_t wcnt[NT / 64];                    // winners before the slice, per wavefront
+  const int n = blockIdx.y, slice = blockIdx.x;
   const int len = row_len(q_pos, fixed_len, n);
+  const int s0 = slice * kSlice;
+  if (slice > 0 && s0 >= len) return;
   const uint32_t* row = u + static_cast<size_t>(n) * u_stride;
   const uint32_t* h0g = hist + static_cast<size_t>(n) * kHistWords;
   int32_t* idx_row = idx + static_cast<size_t>(n) * topk;
   float* score_row = score ? score + static_cast<size_t>(n) * topk : nullptr;
   const int nwords = (len + 31) / 32;
+  const int w0 = s0 / 32;                               // the slice's first bitmap word
+  const int t = static_cast<int>(threadIdx.x);
 
-  // the bitmap words (certain winners) and the candidate count are read in
-  // the same round trip as the level-0 histogram
+  // one round trip: the candidate count with the collect's digit, rank and K;
+  // the certain-winner words before the slice (counted) and the slice's own
+  // word; every thread's first candidate (the list holds kCandCap >= NT
+  // entries, so the read stays inside it)
   const uint32_t* bmg = bitmap + static_cast<size_t>(n) * (u_stride / 32);
-  uint4 bw[kBitmapWords / (4 * NT)];
+  const uint4 meta = len > 0 ? *reinterpret_cast<const uint4*>(h0g + kCandCountOffset)
+                             : make_uint4(0u, 0u, 0u, 0u);
+  uint4 pw[2];
 #pragma unroll
-  for (int q = 0; q < kBitmapWords / (4 * NT); ++q) {
-    const int w = 4 * (threadIdx.x + q * NT);
-    bw[q] = w + 3 < nwords ? *reinterpret_cast<const uint4*>(bmg + w) : make_uint4(0u, 0u, 0u, 0u);
-    if (w < nwords && w + 3 >= nwords) {          // ragged last words
-      bw[q].x = bmg[w];
-      if (w + 1 < nwords) bw[q].y = bmg[w + 1];
-      if (w + 2 < nwords) bw[q].z = bmg[w + 2];
-    }
+  for (int q = 0; q < 2; ++q) {
+    const int w = 4 * (t + q * NT);
+    pw[q] = w < w0 ? *reinterpret_cast<const uint4*>(bmg + w) : make_uint4(0u, 0u, 0u, 0u);
   }
-  const uint32_t c = h0g[kCandCountOffset];
-  // the first candidate of every thread, read before the count is known (the
-  // list holds kCandCap >= NT entries, so the read stays inside it)
+  const uint32_t wd = w0 + t < nwords ? bmg[w0 + t] : 0u;
   const uint2* cl = clist + static_cast<size_t>(n) * kCandCap;
   static_assert(kCandCap >= NT, "one speculative candidate per thread");
-  const uint2 e_first = cl[threadIdx.x];
-  find_digit<NT, kBins0>(h0g, static_cast<uint32_t>(topk), true, sm, res);
-  const uint32_t K = res[2], d0 = res[0], r0 = res[1];
-  __syncthreads();
-  bool fallback = c > static_cast<uint32_t>(kCandCap) || nwords > kBitmapWords;
-  uint32_t T = 0, K2 = 0, n_eq = 0;
-  if (!fallback && K > 0) {
-    // certain winners (bitmap) and the candidates of bin d0 into LDS
-#pragma unroll
-    for (int q = 0; q < kBitmapWords / (4 * NT); ++q)
-      *reinterpret_cast<uint4*>(&bm[4 * (threadIdx.x + q * NT)]) = bw[q];
-    for (int i = threadIdx.x; i < static_cast<int>(c); i += NT) {
-      const uint2 e = i < NT ? e_first : cl[i];
-      cu[i] = e.x;
-      ci[i] = e.y;
-    }
-    for (int b = threadIdx.x; b < kBins1; b += NT) hA[b] = 0u;
-    if (threadIdx.x < kBins2) hB[threadIdx.x] = 0u;
-    __syncthreads();
-    // exact threshold among the candidates: digits 1 and 2 (rank r0)
-    for (int i = threadIdx.x; i < static_cast<int>(c); i += NT)
-      atomicAdd(&hA[(cu[i] >> kShift1) & (kBins1 - 1)], 1u);
-    __syncthreads();
-    find_digit<NT, kBins1>(hA, r0, false, sm, res);
-    const uint32_t d1 = res[0], r1 = res[1];
-    __syncthreads();
-    const uint32_t pre = (d0 << kDigit1Bits) | d1;
-    for (int i = threadIdx.x; i < static_cast<int>(c); i += NT)
-      if ((cu[i] >> kShift1) == pre) atomicAdd(&hB[cu[i] & (kBins2 - 1)], 1u);
-    __syncthreads();
-    find_digit<NT, kBins2>(hB, r1, false, sm, res);
-    T = (d0 << kShift0) | (d1 << kShift1) | res[0];
-    K2 = res[1];
-    n_eq = hB[res[0]];                    // candidates whose key equals T
-    __syncthreads();
-  }
+  const uint2 e_first = cl[t];
+  const uint32_t c = meta.x, d0 = meta.y, r0 = meta.z, K = meta.w;
+  const bool fallback = c > static_cast<uint32_t>(kCandCap) || nwords > kBitmapWords;
   if (fallback) {
-    for (int b = threadIdx.x; b < kBins0; b += NT) hA[b] = h0g[b];
+    if (slice > 0) return;
+    for (int b = t; b < kBins0; b += NT) hA[b] = h0g[b];
     __syncthreads();
     row_select<NT>(row, len, topk, nullptr, idx_row, score_row, hA, cu, hB, true, sm, res);
     return;
   }
-  for (int i = static_cast<int>(K) + threadIdx.x; i < topk; i += NT) {
-    idx_row[i] = -1;
-    if (score_row) score_row[i] = -__builtin_inff();
+  if (slice == 0) {
+    for (int i = static_cast<int>(K) + t; i < topk; i += NT) {
+      idx_row[i] = -1;
+      if (score_row) score_row[i] = -__builtin_inff();
+    }
   }
   if (K == 0) return;
 
-  // mark the candidate winners: key > T, or key == T among the K2 lowest
-  // indices (all ties win when n_eq == K2, the usual case)
+  // the slice's certain winners and the candidates of bin d0 into LDS
+  bm[t] = wd;
+  {
+    uint32_t pre = 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      pre += __popc(pw[q].x) + __popc(pw[q].y) + __popc(pw[q].z) + __popc(pw[q].w);
+    pre = wave_sum(pre);
+    if ((t & 63) == 0) wcnt[t >> 6] = pre;
+  }
+  for (int i = t; i < static_cast<int>(c); i += NT) {
+    const uint2 e = i < NT ? e_first : cl[i];
+    cu[i] = e.x;
+    ci[i] = e.y;
+  }
+  for (int b = t; b < kBins1; b += NT) hA[b] = 0u;
+  if (t < kBins2) hB[t] = 0u;
+  __syncthreads();
+  // exact threshold among the candidates: digits 1 and 2 (rank r0); every
+  // workgroup of the row finds the same one
+  for (int i = t; i < static_cast<int>(c); i += NT)
+    atomicAdd(&hA[(cu[i] >> kShift1) & (kBins1 - 1)], 1u);
+  __syncthreads();
+  find_digit<NT, kBins1>(hA, r0, false, sm, res);
+  const uint32_t d1 = res[0], r1 = res[1];
+  __syncthreads();
+  const uint32_t pre = (d0 << kDigit1Bits) | d1;
+  for (int i = t; i < static_cast<int>(c); i += NT)
+    if ((cu[i] >> kShift1) == pre) atomicAdd(&hB[cu[i] & (kBins2 - 1)], 1u);
+  __syncthreads();
+  find_digit<NT, kBins2>(hB, r1, false, sm, res);
+  const uint32_t T = (d0 << kShift0) | (d1 << kShift1) | res[0];
+  const uint32_t K2 = res[1];
+  const uint32_t n_eq = hB[res[0]];                    // candidates whose key equals T
+  __syncthreads();
+
+  // candidate winners (key > T, or key == T among the K2 lowest indices; all
+  // ties win when n_eq == K2, the usual case): marked when in the slice,
+  // counted when before it
   const uint32_t cut = n_eq == K2 ? 0xFFFFFFFFu
                                   : tie_cut<NT>(cu, ci, static_cast<int>(c), T, K2, n_eq, hA,
                                                   hB, sm, res);
-  for (int i = threadIdx.x; i < static_cast<int>(c); i += NT) {
+  uint32_t cb = 0;
+  for (int i = t; i < static_cast<int>(c); i += NT) {
     const uint32_t kv = cu[i], e = ci[i];
-    if (kv > T || (kv == T && e <= cut)) atomicOr(&bm[e >> 5], 1u << (e & 31));
+    if (kv > T || (kv == T && e <= cut)) {
+      const int r = static_cast<int>(e) - s0;
+      if (r >= 0 && r < kSlice)
+        atomicOr(&bm[r >> 5], 1u << (r & 31));
+      else if (r < 0)
+        ++cb;
+    }
   }
+  cb = wave_sum(cb);
+  if ((t & 63) == 0) wcnt[t >> 6] += cb;
   __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) before += wcnt[i];
 
-  // ordered emit of every marked element (WPT consecutive words per thread)
-  constexpr int WPT = 4096 / NT;
-  uint32_t base_pos = 0;
-  for (int w0 = 0; w0 < nwords; w0 += WPT * NT) {
-    const int w = w0 + WPT * threadIdx.x;
-    uint32_t wd[WPT];
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int q = 0; q < WPT; ++q) {
-      wd[q] = (w + q < nwords) ? bm[w + q] : 0u;
-      cnt += __popc(wd[q]);
+  // ordered emit of the slice: word t holds elements s0 + 32t .. s0 + 32t + 31
+  uint32_t bits = bm[t];
+  uint32_t tot;
+  uint32_t pos = before + block_excl_scan<NT>(__popc(bits), sm, tot);
+  while (bits) {
+    const int b = __ffs(bits) - 1;
+    bits &= bits - 1u;
+    const int e = s0 + 32 * t + b;
+    if (pos < K) {
+      idx_row[pos] = e;
+      if (score_row) score_row[pos] = key_score(row[e]);
     }
-    uint32_t tot;
-    uint32_t pos = base_pos + block_excl_scan<NT>(cnt, sm, tot);
-#pragma unroll
-    for (int q = 0; q < WPT; ++q) {
-      uint32_t bits = wd[q];
-      while (bits) {
-        const int b = __ffs(bits) - 1;
-        bits &= bits - 1u;
-        const uint32_t e = static_cast<uint32_t>(32 * (w + q) + b);
-        if (pos < K) {
-          idx_row[pos] = static_cast<int32_t>(e);
-          if (score_row) score_row[pos] = key_score(row[e]);
-        }
-        ++pos;
-      }
-    }
-    base_pos += tot;
+    ++pos;
   }
 }
 
@@ -1000,8 +1016,9 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   const int nchunks = a.u_stride / kChunk;
   MISA_LAUNCH(K_TOPK_COLLECT, topk_collect_kernel, dim3(nchunks, a.N), dim3(256), 0, st, a.u,
               a.u_stride, a.q_pos, a.fixed_len, a.hist, bitmap, clist, a.topk);
-  MISA_LAUNCH(K_TOPK_FINAL, topk_final_kernel<kFinalThreads>, dim3(a.N), dim3(kFinalThreads), 0,
-              st, a.u, a.u_stride,
+  const int nslices = (a.u_stride + 32 * kFinalThreads - 1) / (32 * kFinalThreads);
+  MISA_LAUNCH(K_TOPK_FINAL, topk_final_kernel<kFinalThreads>, dim3(nslices, a.N),
+              dim3(kFinalThreads), 0, st, a.u, a.u_stride,
               a.q_pos, a.fixed_len, a.hist, bitmap, clist, a.topk, a.idx, a.score);
   return hipGetLastError();
 }

@@ -123,6 +123,13 @@ struct RoutePartialExtra {
   int npool = 0;                      // pooling workgroups per sequence
 };
 
+// Zeroes row n's level-0 histogram region (the scoring kernel's atomics add
+// into it).
+__device__ __forceinline__ void clear_hist_row(uint32_t* hist0, int n) {
+  uint32_t* h = hist0 + static_cast<size_t>(n) * kHistWords;
+  for (int i = threadIdx.x; i < kHistWords; i += 256) h[i] = 0u;
+}
+
 template <int KT, int D>
 __global__ __launch_bounds__(256) void route_partial_mfma_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ kbar,
@@ -155,10 +162,6 @@ __global__ __launch_bounds__(256) void route_partial_mfma_kernel(
     if (threadIdx.x < D) x.kbar_out[(static_cast<size_t>(s) * M + b) * D + threadIdx.x] = m;
     return;
   }
-  if (x.hist0 && chunk == 0) {
-    uint32_t* h = x.hist0 + static_cast<size_t>(n) * kHistWords;
-    for (int i = threadIdx.x; i < kHistWords; i += 256) h[i] = 0u;
-  }
   float* out = partial + (static_cast<size_t>(n) * pstride + chunk) * H_I;
   if (chunk == nchunks) {
     // the partial block's term, exactly as the router's selection step forms it
@@ -166,24 +169,22 @@ __global__ __launch_bounds__(256) void route_partial_mfma_kernel(
     __shared__ float part[4][64];
     QQuarter<DT_BF16, D> qq;
     load_q_quarter<DT_BF16, D>(q, static_cast<size_t>(n) * H_I, H_I, qq);
+    const int s = q_seq[n];
     const int Ln = q_pos[n] + 1;
     const int Mf = Ln / B;
     const int cp = Ln - Mf * B;
     if (cp > 0) {
-      partial_block_mean<KT, D>(x.k, x.k_scale, x.ki, q_seq[n], Mf * B, Ln, kpart, mean);
+      partial_block_mean<KT, D>(x.k, x.k_scale, x.ki, s, Mf * B, Ln, kpart, mean);
       partial_block_terms<DT_BF16, D>(qq, H_I, mean, part);
     }
+    if (x.hist0 && chunk == 0) clear_hist_row(x.hist0, n);
     if (threadIdx.x < H_I)
       out[threadIdx.x] = cp > 0 ? partial_block_term_sum(part, threadIdx.x) : 0.f;
     return;
   }
-  const int Mf = (q_pos[n] + 1) / B;                   // blocks fully visible to row n
-  const int b0 = chunk * kRouteBlocks;
-  const int nb = min(kRouteBlocks, Mf - b0);
-  if (nb <= 0) {
-    for (int j = threadIdx.x; j < H_I; j += 256) out[j] = 0.f;
-    return;
-  }
+  // loads in the order of their dependences, none behind a store of this
+  // workgroup: the query heads (the row alone), the chunk's table entries
+  // (the row's sequence), then the row's length and the sequence's lengths
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   // A operand: head 16 * wave + c, elements 32 kk + 8 g .. + 8
@@ -198,32 +199,51 @@ __global__ __launch_bounds__(256) void route_partial_mfma_kernel(
       a[kk] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
-  // the chunk's table entries; those of blocks completed by this call
-  // ([nlo, nhi), known only once len_old / len_new arrive) are read too but
-  // replaced below, so these loads wait for nothing but q_seq
+  // the chunk's table entries, every load issued (entries past the table's
+  // end read its last one; entries past the row's visible blocks are zeroed
+  // below); those of blocks completed by this call ([nlo, nhi)) are replaced
+  // below
+  const int s = q_seq[n];
+  const int b0 = chunk * kRouteBlocks;
   constexpr int PER = kRouteBlocks * D / 4 / 256;      // table float4s per thread
-  const float* src = kbar + (static_cast<size_t>(q_seq[n]) * M + b0) * D;
+  const float* tab = kbar + static_cast<size_t>(s) * M * D;
   float4 kx[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int f = tid + 256 * i;
     const int blk = f / (D / 4), col = (f % (D / 4)) * 4;
-    kx[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (blk < nb) kx[i] = *reinterpret_cast<const float4*>(src + static_cast<size_t>(blk) * D + col);
+    const int e = min(b0 + blk, M - 1);
+    kx[i] = *reinterpret_cast<const float4*>(tab + static_cast<size_t>(e) * D + col);
+  }
+  const int Mf = (q_pos[n] + 1) / B;                   // blocks fully visible to row n
+  const int nb = min(kRouteBlocks, Mf - b0);
+  int len_old = 0, len_new = 0;
+  if (x.len_new) {
+    len_old = x.len_old[s];
+    len_new = x.len_new[s];
+  }
+  if (x.hist0 && chunk == 0) clear_hist_row(x.hist0, n);
+  if (nb <= 0) {
+    for (int jj = threadIdx.x; jj < H_I; jj += 256) out[jj] = 0.f;
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int blk = (tid + 256 * i) / (D / 4);
+    if (blk >= nb) kx[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   // blocks [nlo, nhi) of this chunk are completed by this call: pooled here
   // (the loads of the query and of the table go out first, so their round
   // trips overlap the key reads)
   int nlo = 0, nhi = 0;
   if (x.len_new) {
-    const int s = q_seq[n];
-    nlo = max(b0, x.len_old[s] / B);
-    nhi = min(b0 + nb, x.len_new[s] / B);
+    nlo = max(b0, len_old / B);
+    nhi = min(b0 + nb, len_new / B);
   }
   __shared__ __align__(16) float fresh[kRouteBlocks][D];
   for (int b = nlo; b < nhi; ++b) {
     const float m = pool_block_mean<KT, D>(static_cast<const uint8_t*>(x.k), x.k_scale, x.ki,
-                                           q_seq[n], b * B, (b + 1) * B, kpart);
+                                           s, b * B, (b + 1) * B, kpart);
     if (tid < D) fresh[b - b0][tid] = m;
     __syncthreads();
   }

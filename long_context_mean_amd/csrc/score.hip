@@ -252,7 +252,15 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
   __shared__ float red_lds[ROUTE ? 4 : 1][64];                    // router partial sums
 
   const int n = blockIdx.y;
-  const int len = CAND ? p.ncols : p.q_pos[n] + 1;
+  // the row's length and its sequence travel together (one scalar round trip)
+  // the row's length and sequence, and the arguments the first loads
+  // address with, are all read before the exit test (two scalar round trips
+  // in all: the arguments, then the row's two words)
+  const int qp = CAND ? 0 : p.q_pos[n];
+  const int s = p.q_seq[n];
+  asm volatile("" ::"s"(qp), "s"(s), "s"(p.q), "s"(p.k), "s"(p.ki.table), "s"(p.ki.L),
+               "s"(p.H_I), "s"(p.route_partial), "s"(p.route_nchunks), "s"(gridDim.x));
+  const int len = CAND ? p.ncols : qp + 1;
   // tiles of 16 elements are dealt round-robin to the row's wavefronts, so at
   // any moment the whole grid streams one compact stretch of the keys
   const int ntiles = (len + 15) / 16;
@@ -263,7 +271,6 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
   const int g = lane >> 4, c = lane & 15;
   const bool do_hist = p.hist0 != nullptr;
 
-  const int s = p.q_seq[n];
   const uint8_t* kseq = p.k;                           // rows addressed through p.ki
   uint8_t* tile = tiles[wave];
   const float* sseq = p.k_scale;

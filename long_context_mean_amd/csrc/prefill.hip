@@ -277,14 +277,18 @@ __device__ __forceinline__ void score_tile(const uint8_t* tile, const float* sca
     float v[RM::NG];
 #pragma unroll
     for (int q = 0; q < RM::NG; ++q) v[q] = 0.f;
-    // the 4 row tiles' chains interleaved (consecutive MFMAs independent)
+    // the 4 row tiles' chains interleaved (consecutive MFMAs independent),
+    // issued at raised wave priority: a wavefront with MFMAs ready goes ahead
+    // of the others' epilogues, which fill the vector pipe meanwhile
     f32x4_t acc[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) acc[rt] = mfma_step<F8>(a[rt][kk], b[kk], acc[rt]);
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll

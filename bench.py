@@ -190,6 +190,18 @@ def counter_record(db, match, flop, cmd, mfma_flop=16384, simds=1024, xcds=8):
         if flop:
             rec["algorithmic_flop"] = flop
             rec["counter_flop_over_algorithmic"] = round(mf * mfma_flop / flop, 4)
+    wave = mean.get("SQ_WAVE_CYCLES", 0.0)
+    if wave and "SQ_WAIT_INST_ANY" in mean:
+        # wave-time shares: SQ_WAVE_CYCLES, SQ_WAIT_INST_* and SQ_ACTIVE_INST_*
+        # are quad-cycles summed over the wavefronts
+        rec["wave_time_waiting_on_dependencies"] = round(mean["SQ_WAIT_INST_ANY"] / wave, 4)
+        if "SQ_WAIT_INST_LDS" in mean:
+            rec["wave_time_waiting_on_lds"] = round(mean["SQ_WAIT_INST_LDS"] / wave, 4)
+        if "SQ_ACTIVE_INST_VALU" in mean:
+            rec["wave_time_issuing_vector_or_matrix"] = round(mean["SQ_ACTIVE_INST_VALU"] / wave, 4)
+        if mean.get("SQ_INSTS_LDS"):
+            rec["lds_bank_conflict_cycles_per_lds_instruction"] = round(
+                mean.get("SQ_LDS_BANK_CONFLICT", 0.0) / mean["SQ_INSTS_LDS"], 4)
     return rec
 
 

@@ -804,6 +804,23 @@ def test_decode_topk_concentrated_in_one_stretch(k_dt, start):
                                                              sc2.view(np.uint32))
 
 
+def test_decode_rows_across_final_slices():
+    """The few-rows selection emits each row in 32768-element slices, one
+    workgroup per slice: a batch with a row shorter than k (all of it
+    selected), a row of exactly one slice (its second workgroup has no
+    elements), a row one element into its second slice, and a row over
+    three slices.  Against the oracle, and bit-identical to the call that
+    also routes."""
+    L = 70000
+    pos = np.array([100, 32767, 32768, L - 1], np.int32)
+    p = synth.small("slices", 71, N=4, S=4, L=L, d=128, H_I=16, h=4, B=64, topk=2048,
+                    q_pos=pos, q_seq=np.arange(4, dtype=np.int32))
+    dp, heads, idx = check_misa(p)
+    assert np.all(idx[0, :101] >= 0) and np.all(idx[0, 101:] == -1), "short row: all selected"
+    h2, _, idx2, _ = (np_(t) for t in dp.route_score_topk(dp.pool()))
+    assert np.array_equal(h2, heads) and np.array_equal(idx2, idx)
+
+
 @pytest.mark.parametrize("N,L", [(3, 20000), (130, 20000), (3, 12000)])
 def test_all_scores_tied(N, L):
     """Zero keys: every score is 0, the threshold bin holds every token (more

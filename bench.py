@@ -16,7 +16,8 @@ it with the same protocol: the step with a full pooling pass instead of the
 incremental update (its scoring then reads keys the pooling pass has just
 brought into the Infinity Cache), the same serving step on a paged key cache,
 the dense 64-head DSA indexer, and MISA-dagger (coarse top-8192 + all-head
-rerank) on bf16 and fp8 keys.
+rerank) on bf16 and fp8 keys, both with a full pooling pass and in serving
+form (the single call at top-8192, then the rerank call).
 
 Prints ONE JSON line.  `value` = prefix tokens indexed per second (sum of
 the visible prefix lengths per step / time per step).
@@ -342,6 +343,27 @@ class Serving:
         dp.pool_update(self.len_old, self.len_new, 1, self.kbar[i])
         dp.route(self.kbar[i], self.h, heads=self.heads, head_score=self.r, ws=self.ws_route)
         dp.score_topk(self.heads, idx=self.idx, score=None, ws=self.ws_score, want_score=False)
+
+    def use_dagger(self, k_prime):
+        """MISA-dagger in serving form: the single call selects the top k_prime
+        tokens under the routed heads, then misa_rerank re-scores them with
+        every head and keeps the top k."""
+        p, b = self.p, self.b
+        dev = self.heads.device
+        self.k_prime = k_prime
+        self.cand = self.heads.new_empty((p.N, k_prime))
+        self.sc = self.r.new_empty((p.N, p.topk))
+        self.ws_dag = b.workspace(b.MISA_OP_ROUTE_SCORE_TOPK, p.N, p.L, p.d, p.H_I, p.B,
+                                  topk=k_prime, device=dev)
+        self.ws_rerank = b.workspace(b.MISA_OP_RERANK, p.N, p.L, p.d, p.H_I, topk=p.topk,
+                                     k_prime=k_prime, q_dt=p.q_dt, device=dev)
+
+    def step_dagger(self, i):
+        dp = self.dps[i]
+        dp.pool_route_score_topk(self.kbar[i], self.len_old, self.len_new, 1, self.h,
+                                 topk=self.k_prime, heads=self.heads, head_score=self.r,
+                                 idx=self.cand, score=None, ws=self.ws_dag, want_score=False)
+        dp.rerank(self.cand, idx=self.idx, score=self.sc, ws=self.ws_rerank)
 
     def use_blocks(self, m_blocks):
         """Switch the step's scoring to the block prefilter (m_blocks blocks)."""
@@ -705,6 +727,9 @@ def main():
         _, ktf, _ = kernel_times(torch, binding, rep.step_misa, max(3, args.steps // 2), 1, 16)
         ms_d = timed(torch, rep.step_dense, args.steps, args.warmup)
         ms_g = timed(torch, rep.step_dagger, args.steps, args.warmup)
+        srv.use_dagger(8192)
+        ms_gs = timed(torch, srv.step_dagger, args.steps, args.warmup)
+        _, ktg, _ = kernel_times(torch, binding, srv.step_dagger, max(3, args.steps // 2), 1, 16)
         extra.update({
             "full_pool_step_ms": round(ms_f, 4),
             "full_pool_step_tokens_per_s": tokens / (ms_f * 1e-3),
@@ -712,6 +737,8 @@ def main():
             "dense_dsa_ms": round(ms_d, 4),
             "speedup_vs_dense": round(ms_d / ms, 3),
             "misa_dagger_ms": round(ms_g, 4),
+            "misa_dagger_serving_ms": round(ms_gs, 4),
+            "misa_dagger_serving_kernel_ms": {k: round(v, 5) for k, v in ktg.items()},
         })
         # recall of the dense top-k set (outside timing)
         srv.step(0)
@@ -787,9 +814,20 @@ def main():
         p5 = synth.make("c5")
         r5 = Replicas(p5, torch, binding, p5.h, k_prime=p5.k_prime)
         ms5 = timed(torch, r5.step_dagger, args.steps, args.warmup)
+        s5 = Serving(p5, torch, binding, p5.h)
+        s5.use_dagger(p5.k_prime)
+        ms5s = timed(torch, s5.step_dagger, args.steps, args.warmup)
+        s5.step_dagger(0)
+        r5.step_dagger(0)
+        torch.cuda.synchronize()
+        same5 = bool(torch.equal(s5.idx, r5.idx))
+        del s5
         ms5d = timed(torch, r5.step_dense, args.steps, args.warmup)
         extra["fp8_misa_dagger_ms"] = round(ms5, 4)
+        extra["fp8_misa_dagger_serving_ms"] = round(ms5s, 4)
+        extra["fp8_misa_dagger_serving_same_idx"] = same5
         extra["fp8_misa_dagger_tokens_per_s"] = p5.tokens_indexed() / (ms5 * 1e-3)
+        extra["fp8_misa_dagger_serving_tokens_per_s"] = p5.tokens_indexed() / (ms5s * 1e-3)
         extra["fp8_dense_dsa_ms"] = round(ms5d, 4)
         del r5
         torch.cuda.empty_cache()

@@ -457,8 +457,9 @@ __global__ __launch_bounds__(NT) void topk_final_kernel(
 
 // ---------------------------------------------------------------- short rows in registers
 // Rows of at most kSmallRow elements (MISA-dagger's rerank, the block
-// prefilter's selects, short decode rows): one 1024-thread workgroup per row;
-// thread t holds elements 16t .. 16t+15 in registers for every pass.  The
+// prefilter's selects, short decode rows): one workgroup per row, of 256, 512
+// or 1024 threads (as few as hold the row); thread t holds elements
+// 16t .. 16t+15 in registers for every pass.  The
 // keys of such a row are often close together (re-scored candidates, block
 // scores), so the radix digits are taken on key - min over the row's key
 // range (digits [sA, 32), [sB, sA), [0, sB) with (max - min) >> sA < 4096),
@@ -536,6 +537,7 @@ __device__ __forceinline__ void select_in_registers(const uint32_t (&v)[PT],
                                                     uint32_t* hA, uint32_t* hA2, uint32_t* hB,
                                                     uint32_t (*sm)[NT / 64], uint32_t (*res)[4],
                                                     uint32_t* wmin, uint32_t* wmax) {
+  static_assert(NT >= kBins2, "one thread per level-2 bin clears the histogram");
   const int tid = static_cast<int>(threadIdx.x);
   for (int b = tid; b < kBins0; b += NT) {
     hA[b] = 0u;
@@ -648,11 +650,11 @@ __device__ __forceinline__ void select_in_registers(const uint32_t (&v)[PT],
 }
 
 
-__global__ __launch_bounds__(1024) void topk_small_kernel(
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_small_kernel(
     const uint32_t* __restrict__ u, int u_stride, const int32_t* __restrict__ q_pos,
     int fixed_len, int topk, const int32_t* __restrict__ cand, int cand_stride,
     int32_t* __restrict__ idx, float* __restrict__ score) {
-  constexpr int NT = 1024;
   __shared__ __align__(16) uint32_t hA[kBins0];
   __shared__ __align__(16) uint32_t hA2[kBins0];
   __shared__ __align__(16) uint32_t hB[kBins2];
@@ -999,8 +1001,17 @@ size_t topk_few_rows_bytes(int N, int u_stride) {
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.one_row_per_block && !a.row_flag && a.u_stride <= kSmallRow) {
-    MISA_LAUNCH(K_TOPK_ROW, topk_small_kernel, dim3(a.N), dim3(1024), 0, st, a.u, a.u_stride,
-                a.q_pos, a.fixed_len, a.topk, a.cand, a.cand_stride, a.idx, a.score);
+    // as few threads as hold the row (16 elements each): fewer wavefronts
+    // in every barrier of the select
+    if (a.u_stride <= 256 * kPerThread)
+      MISA_LAUNCH(K_TOPK_ROW, topk_small_kernel<256>, dim3(a.N), dim3(256), 0, st, a.u,
+                  a.u_stride, a.q_pos, a.fixed_len, a.topk, a.cand, a.cand_stride, a.idx, a.score);
+    else if (a.u_stride <= 512 * kPerThread)
+      MISA_LAUNCH(K_TOPK_ROW, topk_small_kernel<512>, dim3(a.N), dim3(512), 0, st, a.u,
+                  a.u_stride, a.q_pos, a.fixed_len, a.topk, a.cand, a.cand_stride, a.idx, a.score);
+    else
+      MISA_LAUNCH(K_TOPK_ROW, topk_small_kernel<1024>, dim3(a.N), dim3(1024), 0, st, a.u,
+                  a.u_stride, a.q_pos, a.fixed_len, a.topk, a.cand, a.cand_stride, a.idx, a.score);
     return hipGetLastError();
   }
   if (a.one_row_per_block) {

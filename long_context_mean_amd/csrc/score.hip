@@ -580,7 +580,7 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
   // tiles (of 16 keys) per wavefront; short candidate lists use smaller
   // chunks so more workgroups share the gather (at most 64 tiles per
   // wavefront: the paged path keeps one page number per lane)
-  const int tpw = a.cand ? 4 : kMaxTpw;
+  const int tpw = a.cand ? 2 : kMaxTpw;
   if (a.k_dt == DT_BF16)
     return a.d == 64 ? launch_mfma_rows<DT_BF16, 64>(a, st, tpw)
                      : launch_mfma_rows<DT_BF16, 128>(a, st, tpw);

@@ -585,7 +585,11 @@ __device__ __forceinline__ void select_in_registers(const uint32_t (&v)[PT],
     const uint32_t dA = res[0][0];
     uint32_t r = res[0][1], dB = 0, dC = 0;
     n_eq = hA[dA];
-    if (sA > 0) {
+    // a threshold bin taken whole (rank inside it == its count) ends the
+    // search: every key at or above its lower edge wins and no tie straddles
+    // the cut (the same for every thread: the counts are in LDS)
+    bool whole = r == n_eq;
+    if (sA > 0 && !whole) {
       const uint32_t mB = (1u << (sA - sB)) - 1u;
 #pragma unroll
       for (int j = 0; j < PT; ++j)
@@ -596,7 +600,8 @@ __device__ __forceinline__ void select_in_registers(const uint32_t (&v)[PT],
       dB = res[1][0];
       r = res[1][1];
       n_eq = hA2[dB];
-      if (sB > 0) {                           // sB <= 8
+      whole = r == n_eq;
+      if (sB > 0 && !whole) {                 // sB <= 8
         const uint32_t preB = (dA << (sA - sB)) | dB;
 #pragma unroll
         for (int j = 0; j < PT; ++j)
@@ -609,8 +614,16 @@ __device__ __forceinline__ void select_in_registers(const uint32_t (&v)[PT],
         n_eq = hB[dC];
       }
     }
-    T = base + ((dA << sA) | (dB << sB) | dC);
-    K2 = r;                                   // ties at T that win: the K2 lowest indices
+    if (whole) {
+      // winners: keys >= the bin's lower edge (>= base >= 1, so T >= 0 and
+      // empty slots, key 0, never win)
+      T = base + ((dA << sA) | (dB << sB)) - 1u;
+      K2 = 0;
+      n_eq = 0;
+    } else {
+      T = base + ((dA << sA) | (dB << sB) | dC);
+      K2 = r;                                 // ties at T that win: the K2 lowest indices
+    }
   }
   // this thread's winners: keys above T, and ties ranked by index (every tie
   // wins when K2 == n_eq, the usual case: no ranking needed)

@@ -404,16 +404,23 @@ __global__ __launch_bounds__(NT) void topk_final_kernel(
   __syncthreads();
   find_digit<NT, kBins1>(hA, r0, false, sm, res);
   const uint32_t d1 = res[0], r1 = res[1];
+  // a digit-1 bin taken whole (rank inside it == its count): every candidate
+  // at or above its lower edge wins, so that edge is T with every tie winning
+  // and the last level is skipped (the same for every thread: LDS counts)
+  const bool whole = r1 == hA[d1];
   __syncthreads();
-  const uint32_t pre = (d0 << kDigit1Bits) | d1;
-  for (int i = t; i < static_cast<int>(c); i += NT)
-    if ((cu[i] >> kShift1) == pre) atomicAdd(&hB[cu[i] & (kBins2 - 1)], 1u);
-  __syncthreads();
-  find_digit<NT, kBins2>(hB, r1, false, sm, res);
-  const uint32_t T = (d0 << kShift0) | (d1 << kShift1) | res[0];
-  const uint32_t K2 = res[1];
-  const uint32_t n_eq = hB[res[0]];                    // candidates whose key equals T
-  __syncthreads();
+  uint32_t T = (d0 << kShift0) | (d1 << kShift1), K2 = 0, n_eq = 0;
+  if (!whole) {
+    const uint32_t pre = (d0 << kDigit1Bits) | d1;
+    for (int i = t; i < static_cast<int>(c); i += NT)
+      if ((cu[i] >> kShift1) == pre) atomicAdd(&hB[cu[i] & (kBins2 - 1)], 1u);
+    __syncthreads();
+    find_digit<NT, kBins2>(hB, r1, false, sm, res);
+    T |= res[0];
+    K2 = res[1];
+    n_eq = hB[res[0]];                                 // candidates whose key equals T
+    __syncthreads();
+  }
 
   // candidate winners (key > T, or key == T among the K2 lowest indices; all
   // ties win when n_eq == K2, the usual case): marked when in the slice,
@@ -787,16 +794,22 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(
   __syncthreads();
   find_digit<1024, kBins1>(hA, r0, false, sm, res);
   const uint32_t d1 = res[0], r1 = res[1];
+  // a digit-1 bin taken whole: its lower edge is T, every tie wins, and the
+  // last level is skipped
+  const bool whole = r1 == hA[d1];
   __syncthreads();
-  const uint32_t pre = (d0 << kDigit1Bits) | d1;
-  for (int i = threadIdx.x; i < static_cast<int>(c); i += 1024)
-    if ((cu[i] >> kShift1) == pre) atomicAdd(&hB[cu[i] & (kBins2 - 1)], 1u);
-  __syncthreads();
-  find_digit<1024, kBins2>(hB, r1, false, sm, res);
-  const uint32_t T = (d0 << kShift0) | (d1 << kShift1) | res[0];
-  const uint32_t K2 = res[1];
-  const uint32_t n_eq = hB[res[0]];
-  __syncthreads();
+  uint32_t T = (d0 << kShift0) | (d1 << kShift1), K2 = 0, n_eq = 0;
+  if (!whole) {
+    const uint32_t pre = (d0 << kDigit1Bits) | d1;
+    for (int i = threadIdx.x; i < static_cast<int>(c); i += 1024)
+      if ((cu[i] >> kShift1) == pre) atomicAdd(&hB[cu[i] & (kBins2 - 1)], 1u);
+    __syncthreads();
+    find_digit<1024, kBins2>(hB, r1, false, sm, res);
+    T |= res[0];
+    K2 = res[1];
+    n_eq = hB[res[0]];
+    __syncthreads();
+  }
   // mark the candidate winners: key > T, or key == T among the K2 lowest
   // indices (all ties win when n_eq == K2, the usual case)
   const uint32_t cut = n_eq == K2 ? 0xFFFFFFFFu

@@ -246,19 +246,31 @@ __device__ __forceinline__ void row_select(const uint32_t* row, int len, int top
     if (score_row) score_row[i] = -__builtin_inff();
   }
   if (K == 0) return;
-  hist_range<NT, 1>(row, span, len, d0, h1);
-  __syncthreads();
-  find_digit<NT, kBins1>(h1, r0, false, sm, res);
-  const uint32_t d1 = res[0], r1 = res[1];
-  __syncthreads();
-  hist_range<NT, 2>(row, span, len, (d0 << kDigit1Bits) | d1, h2);
-  __syncthreads();
-  find_digit<NT, kBins2>(h2, r1, false, sm, res);
+  // a bin taken whole (rank inside it == its count) ends the search: its
+  // lower edge is the threshold and every key equal to it wins, so the
+  // remaining sweeps over the row are skipped
   Threshold th;
   th.K = K;
-  th.T = (d0 << kShift0) | (d1 << kShift1) | res[0];
-  th.K2 = res[1];
-  __syncthreads();
+  th.K2 = 0xFFFFFFFFu;
+  if (r0 == h0[d0]) {
+    th.T = d0 << kShift0;
+  } else {
+    hist_range<NT, 1>(row, span, len, d0, h1);
+    __syncthreads();
+    find_digit<NT, kBins1>(h1, r0, false, sm, res);
+    const uint32_t d1 = res[0], r1 = res[1];
+    const bool whole = r1 == h1[d1];
+    __syncthreads();
+    th.T = (d0 << kShift0) | (d1 << kShift1);
+    if (!whole) {
+      hist_range<NT, 2>(row, span, len, (d0 << kDigit1Bits) | d1, h2);
+      __syncthreads();
+      find_digit<NT, kBins2>(h2, r1, false, sm, res);
+      th.T |= res[0];
+      th.K2 = res[1];
+      __syncthreads();
+    }
+  }
   compact_row<NT>(row, span, len, th, cand_row, idx_row, score_row, sm);
 }
 

@@ -20,8 +20,9 @@
 //    the winners before its slice (bitmap words and candidates), marks the
 //    candidate winners inside it and emits the slice's winners in index
 //    order, a bitmap word per thread.  When the candidates do not fit in LDS
-//    (heavily tied scores) or the row is very long, the row's first workgroup
-//    falls back to a full radix select over the row.
+//    (heavily tied scores, or rows of millions of tokens) or the row is longer
+//    than 2^24 tokens, the row's first workgroup falls back to a full radix
+//    select over the row.
 // Many rows or short rows (prefill, rerank): topk_row, one 1024-thread
 //    workgroup per row with every histogram in LDS.
 #include "common.hpp"
@@ -96,26 +97,39 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t K, boo
 
 // Ties at the threshold: among the n_eq candidates whose key equals T, the K2
 // lowest token indices win (K2 <= n_eq).  Returns the largest winning index.
-// Radix select on the indices (< 2^18: bits 6..17, then 0..5) in hA (4096
-// words) and hB (64 words); every thread calls it.
+// Radix select on the indices in hA (4096 words) and hB (64 words): indices
+// below 2^18 take bits 6..17, then 0..5; with `big` (indices below 2^24)
+// bits 12..23, then 6..11, then 0..5.  Every thread calls it.
 template <int NT>
 __device__ __forceinline__ uint32_t tie_cut(const uint32_t* cu, const uint32_t* ci, int total,
-                                            uint32_t T, uint32_t K2, uint32_t n_eq, uint32_t* hA,
-                                            uint32_t* hB, uint32_t* sm, uint32_t* res) {
+                                            uint32_t T, uint32_t K2, uint32_t n_eq, bool big,
+                                            uint32_t* hA, uint32_t* hB, uint32_t* sm,
+                                            uint32_t* res) {
+  const int sA = big ? 12 : 6;
   for (int b = threadIdx.x; b < 4096; b += NT) hA[b] = 0u;
   if (threadIdx.x < 64) hB[threadIdx.x] = 0u;
   __syncthreads();
   for (int i = threadIdx.x; i < total; i += NT)
-    if (cu[i] == T) atomicAdd(&hA[ci[i] >> 6], 1u);
+    if (cu[i] == T) atomicAdd(&hA[ci[i] >> sA], 1u);
   __syncthreads();
   // the K2-th smallest index is the (n_eq - K2 + 1)-th largest
   find_digit<NT, 4096>(hA, n_eq - K2 + 1u, false, sm, res);
-  const uint32_t dA = res[0], rA = res[1];
+  uint32_t pre = res[0], r = res[1];                 // index bits [sA, ..) decided
+  if (big) {
+    for (int i = threadIdx.x; i < total; i += NT)
+      if (cu[i] == T && (ci[i] >> 12) == pre) atomicAdd(&hB[(ci[i] >> 6) & 63u], 1u);
+    __syncthreads();
+    find_digit<NT, 64>(hB, r, false, sm, res);
+    pre = (pre << 6) | res[0];                       // bits [6, ..) decided
+    r = res[1];
+    if (threadIdx.x < 64) hB[threadIdx.x] = 0u;
+    __syncthreads();
+  }
   for (int i = threadIdx.x; i < total; i += NT)
-    if (cu[i] == T && (ci[i] >> 6) == dA) atomicAdd(&hB[ci[i] & 63u], 1u);
+    if (cu[i] == T && (ci[i] >> 6) == pre) atomicAdd(&hB[ci[i] & 63u], 1u);
   __syncthreads();
-  find_digit<NT, 64>(hB, rA, false, sm, res);
-  const uint32_t cut = (dA << 6) | res[0];
+  find_digit<NT, 64>(hB, r, false, sm, res);
+  const uint32_t cut = (pre << 6) | res[0];
   __syncthreads();
   return cut;
 }
@@ -336,7 +350,7 @@ __global__ __launch_bounds__(NT) void topk_final_kernel(
     const uint2* __restrict__ clist, int topk, int32_t* __restrict__ idx,
     float* __restrict__ score) {
   constexpr int kSlice = 32 * NT;                       // elements per workgroup, a word per thread
-  static_assert(kBitmapWords == 8 * NT, "two 16-byte bitmap loads per thread cover the row");
+  static_assert(kBitmapWords == 8 * NT, "two 16-byte bitmap loads per thread cover 2^18 tokens");
   __shared__ __align__(16) uint32_t bm[NT];             // the slice's winners, one bit per element
   __shared__ __align__(16) uint32_t cu[kCandCap];       // candidate order key
   __shared__ __align__(16) uint32_t ci[kCandCap];       // candidate element index
@@ -375,7 +389,8 @@ __global__ __launch_bounds__(NT) void topk_final_kernel(
   static_assert(kCandCap >= NT, "one speculative candidate per thread");
   const uint2 e_first = cl[t];
   const uint32_t c = meta.x, d0 = meta.y, r0 = meta.z, K = meta.w;
-  const bool fallback = c > static_cast<uint32_t>(kCandCap) || nwords > kBitmapWords;
+  // (rows past 2^24 tokens would need a fourth index level in the tie cut)
+  const bool fallback = c > static_cast<uint32_t>(kCandCap) || len > (1 << 24);
   if (fallback) {
     if (slice > 0) return;
     for (int b = t; b < kBins0; b += NT) hA[b] = h0g[b];
@@ -398,6 +413,12 @@ __global__ __launch_bounds__(NT) void topk_final_kernel(
 #pragma unroll
     for (int q = 0; q < 2; ++q)
       pre += __popc(pw[q].x) + __popc(pw[q].y) + __popc(pw[q].z) + __popc(pw[q].w);
+    // rows past 2^18 tokens: the words before the slice beyond the first
+    // kBitmapWords (w0 is a multiple of 4, so no load reaches the slice)
+    for (int w = 4 * (t + 2 * NT); w < w0; w += 4 * NT) {
+      const uint4 x = *reinterpret_cast<const uint4*>(bmg + w);
+      pre += __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
+    }
     pre = wave_sum(pre);
     if ((t & 63) == 0) wcnt[t >> 6] = pre;
   }
@@ -438,8 +459,8 @@ __global__ __launch_bounds__(NT) void topk_final_kernel(
   // ties win when n_eq == K2, the usual case): marked when in the slice,
   // counted when before it
   const uint32_t cut = n_eq == K2 ? 0xFFFFFFFFu
-                                  : tie_cut<NT>(cu, ci, static_cast<int>(c), T, K2, n_eq, hA,
-                                                  hB, sm, res);
+                                  : tie_cut<NT>(cu, ci, static_cast<int>(c), T, K2, n_eq,
+                                                len > (1 << 18), hA, hB, sm, res);
   uint32_t cb = 0;
   for (int i = t; i < static_cast<int>(c); i += NT) {
     const uint32_t kv = cu[i], e = ci[i];
@@ -825,8 +846,8 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(
   // mark the candidate winners: key > T, or key == T among the K2 lowest
   // indices (all ties win when n_eq == K2, the usual case)
   const uint32_t cut = n_eq == K2 ? 0xFFFFFFFFu
-                                  : tie_cut<1024>(cu, ci, static_cast<int>(c), T, K2, n_eq, hA,
-                                                  hB, sm, res);
+                                  : tie_cut<1024>(cu, ci, static_cast<int>(c), T, K2, n_eq, false,
+                                                  hA, hB, sm, res);
   for (int i = threadIdx.x; i < static_cast<int>(c); i += 1024) {
     const uint32_t kv = cu[i], e = ci[i];
     if (kv > T || (kv == T && e <= cut)) atomicOr(&bm[e >> 5], 1u << (e & 31));

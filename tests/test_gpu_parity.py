@@ -763,9 +763,9 @@ def _exact_misa(p, rows=None):
 
 
 def test_rows_longer_than_lds_bitmap():
-    """Rows past 2^18 tokens: the few-rows select and the one-row select both
-    fall back to the full radix path (and the prefill candidate path flags
-    every row)."""
+    """Rows past 2^18 tokens with integer scores: the few-rows select takes
+    the full radix path when its candidate list overflows, the one-row select
+    always does (and the prefill candidate path flags every row)."""
     L = 300000
     p = synth.integer_problem("long2", 61, N=2, S=2, L=L, d=64, H_I=8, h=2, B=512, topk=3000,
                               q_pos=np.array([L - 1, 270000], np.int32))
@@ -775,6 +775,53 @@ def test_rows_longer_than_lds_bitmap():
                               topk=100, q_pos=pos.astype(np.int32),
                               q_seq=np.zeros(128, np.int32))
     _exact_misa(p, rows=np.r_[0:3, 125:128])
+
+
+def _order_keys(x):
+    b = np.asarray(x, np.float32).view(np.uint32)
+    return np.where(b & 0x80000000, ~b, b | 0x80000000).astype(np.uint32)
+
+
+def test_long_rows_sliced_final():
+    """Decode rows past 2^18 tokens with random scores: the sliced final
+    select (its counts of the winners before a slice read past the first
+    8192 bitmap words) against the oracle; the rows' candidate lists fit, so
+    the full radix path is not what runs."""
+    L = 300000
+    p = synth.small("long3", 73, N=3, S=3, L=L, d=128, H_I=16, h=4, B=128, topk=2048,
+                    q_pos=np.array([L - 1, 280000, 262200], np.int32),
+                    q_seq=np.arange(3, dtype=np.int32))
+    dp, heads, idx = check_misa(p)
+    ref = oracle.scores(p, heads)
+    for n in range(p.N):
+        key = _order_keys(ref[n, :p.q_pos[n] + 1])
+        d0 = np.sort(key)[::-1][p.topk - 1] >> 20
+        assert np.sum((key >> 20) == d0) < 7000, "candidates overflow: fallback path"
+
+
+def test_long_row_ties_past_2_18():
+    """Exact ties at the k-th score among tokens on both sides of 2^18: 200
+    keys score 2x, 3000 identical keys at 250000, 250010, .. score x, the
+    rest 0.  The 1848 lowest-index ties win, so the tie cut (three index
+    levels in rows past 2^18 tokens) lands at token 268470.  Bit-exact."""
+    L, N = 300000, 2
+    p = synth.integer_problem("ties18", 74, N=N, S=N, L=L, d=128, H_I=8, h=4, B=128,
+                              topk=2048)
+    rng = np.random.default_rng(74)
+    k32 = -np.ones((N, L, 128), np.float32)
+    k32[:, 250000:280000:10] = 1.0
+    k32[:, 1003:280000:1400] = 2.0
+    k = synth.f32_to_bf16_bits(k32)
+    del k32
+    q = synth.f32_to_bf16_bits(rng.integers(1, 3, size=(N, 8, 128)).astype(np.float32))
+    w = rng.integers(1, 4, size=(N, 8)).astype(np.float32)
+    p = synth.Problem(p.name, q, synth.BF16, w, k, synth.BF16, p.k_scale, p.q_seq, p.q_pos, p.B,
+                      p.h, p.topk, p.k_prime)
+    dp = _exact_misa(p)
+    idx = np_(dp.score_topk(dp.route(dp.pool())[0])[0])
+    for n in range(N):
+        sel = idx[n][idx[n] >= 0]
+        assert 268470 in sel and 268480 not in sel
 
 
 @pytest.mark.parametrize("k_dt,start", [(synth.BF16, 0), (synth.FP8, 20000), (synth.BF16, 37000)])

@@ -34,7 +34,7 @@ namespace {
 constexpr int kChunk = 4096;          // elements per collect workgroup
 constexpr int kPerThread = 16;        // contiguous elements per thread per tile
 constexpr int kCandCap = 8192;        // candidates resolved in LDS
-constexpr int kBitmapWords = 8192;    // rows up to 262144 elements use the LDS bitmap
+constexpr int kBitmapWords = 8192;    // 262144 elements: the one-row select's LDS bitmap of a row
 constexpr int kFinalThreads = 1024;   // threads of the few-rows final selection
 
 // Finds the bin of a histogram (NBINS bins, bin NBINS-1 = largest keys) that

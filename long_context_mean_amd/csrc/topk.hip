@@ -920,17 +920,25 @@ __global__ __launch_bounds__(256) void topk_tau_kernel(const uint32_t* __restric
   // before the first histogram update (one round trip per batch, not one per
   // key); out-of-range slots reread key 0 and are skipped
   constexpr int PB = 16;
+  // a row of at most one batch (4096 samples: L <= 128K at a stride of 32)
+  // keeps its batch in registers for the second level instead of reading
+  // it again
+  const bool one = m <= 256 * PB;
+  bool held = false;                                   // vb holds the row's one batch
+  uint32_t vb[PB];
   auto sweep = [&](auto&& use) {
     for (int i0 = 0; i0 < m; i0 += 256 * PB) {
-      uint32_t v[PB];
+      if (!held) {
 #pragma unroll
-      for (int u = 0; u < PB; ++u) {
-        const int i = i0 + static_cast<int>(threadIdx.x) + 256 * u;
-        v[u] = row[i < m ? i : 0];
+        for (int u = 0; u < PB; ++u) {
+          const int i = i0 + static_cast<int>(threadIdx.x) + 256 * u;
+          vb[u] = row[i < m ? i : 0];
+        }
+        held = one;
       }
 #pragma unroll
       for (int u = 0; u < PB; ++u)
-        if (i0 + static_cast<int>(threadIdx.x) + 256 * u < m) use(v[u]);
+        if (i0 + static_cast<int>(threadIdx.x) + 256 * u < m) use(vb[u]);
     }
   };
   for (int b = threadIdx.x; b < kBins0; b += 256) hA[b] = 0u;

@@ -16,7 +16,7 @@ import oracle
 from long_context_mean_amd import synth
 from long_context_mean_amd.binding import DeviceAttention, DeviceProblem
 
-from parity import check_heads, check_topk, fp8_mfma_error_bound, recall, tol
+from parity import check_heads, check_topk, fp8_mfma_error_bound, recall, tol, top_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -79,7 +79,10 @@ def check_misa(p, h=None, topk=None, rows=None, page_size=0, ws=None):
     assert np.all(np.abs(r[rows] - ref_r) <= tol(ref_r)), "router scores"
     differing = check_heads(heads[rows], ref_r, h)
     ref_sc = oracle.scores(ps, heads[rows])            # replay the GPU's heads
-    extra = fp8_mfma_error_bound(ps, heads[rows]) if fp8_gemm(p) and not page_size else None
+    extra = None
+    if fp8_gemm(p) and not page_size:
+        toks = top_tokens(ref_sc, idx[rows], topk, ps.visible())
+        extra = fp8_mfma_error_bound(ps, heads[rows], toks)
     swapped = check_topk(idx[rows], sc[rows], ref_sc, topk, ps.visible(), extra=extra)
     log(f"[misa] {p.name}: head rows differing at near-ties {differing}, token swaps {swapped}")
     if extra is not None:
@@ -371,9 +374,12 @@ def check_prefill_chunk(p, dense_rows=24):
     didx, dsc = dp.dsa(ws=ws)
     drows = rows[np.linspace(0, len(rows) - 1, dense_rows).astype(int)]
     ps = sub_problem(p, drows)
-    extra = fp8_mfma_error_bound(ps, None) if fp8_gemm(p) else None
-    check_topk(np_(didx)[drows], np_(dsc)[drows], oracle.scores(ps, None), p.topk,
-               ps.visible(), extra=extra)
+    ref_sc = oracle.scores(ps, None)
+    extra = None
+    if fp8_gemm(p):
+        toks = top_tokens(ref_sc, np_(didx)[drows], p.topk, ps.visible())
+        extra = fp8_mfma_error_bound(ps, None, toks)
+    check_topk(np_(didx)[drows], np_(dsc)[drows], ref_sc, p.topk, ps.visible(), extra=extra)
 
 
 def test_c3_prefill_chunk_sampled_rows():

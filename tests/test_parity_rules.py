@@ -4,7 +4,7 @@ instruction v_mfma_f32_16x16x128_f8f6f4 returned for the same products."""
 import numpy as np
 
 from long_context_mean_amd import synth
-from parity import fp8_mfma_error_bound
+from parity import fp8_mfma_error_bound, top_tokens
 
 
 def _one_dot(qv, kv, w=1.0, qs=1.0, ks=1.0, d=16):
@@ -117,3 +117,31 @@ def test_bound_covers_the_emulated_instruction():
                 ratios.append(err / bound[s])
         if not clustered:
             assert max(ratios) > 0.02, max(ratios)
+
+
+def test_bound_on_a_token_subset():
+    """Bounding only some tokens gives the same values there as bounding all of
+    them, and NaN at every other visible token (so a comparison that consults
+    one fails); tokens past the row's length stay 0."""
+    rng = np.random.default_rng(77)
+    p = _random_fp8_problem(rng, L=200, d=128, H_I=4, clustered=True)
+    p.q_pos[:] = 150
+    full = fp8_mfma_error_bound(p)
+    toks = [np.array([3, 150, 7, 7, 199, -1, 0])]
+    sub = fp8_mfma_error_bound(p, None, toks)
+    keep = np.array([0, 3, 7, 150])
+    assert np.array_equal(sub[0, keep], full[0, keep])
+    rest = np.setdiff1d(np.arange(151), keep)
+    assert np.isnan(sub[0, rest]).all()
+    assert not sub[0, 151:].any()
+    heads = np.array([[1, 3]])
+    assert np.array_equal(fp8_mfma_error_bound(p, heads, toks)[0, keep],
+                          fp8_mfma_error_bound(p, heads)[0, keep])
+
+
+def test_top_tokens_union():
+    """top_tokens: the oracle's top-k (lower index first among equal scores)
+    joined with the GPU's selection, padding ignored."""
+    ref = np.array([[1.0, 5.0, 5.0, -np.inf, 2.0, 0.5]])
+    got = top_tokens(ref, np.array([[4, 1, -1]]), 2, [5])
+    assert got[0].tolist() == [1, 2, 4]

@@ -51,7 +51,14 @@ struct KeyIndex {
 
   __device__ __forceinline__ size_t row(int s, int t) const {
     if (table == nullptr) return static_cast<size_t>(s) * L + t;
-    const int pg = table[static_cast<size_t>(s) * max_pages + (t >> page_shift)];
+    return row_in_page(page(s, t), t);
+  }
+  // paged: the page holding token t of sequence s, and the row of token t in
+  // page pg (split so that a caller can have many page reads in flight)
+  __device__ __forceinline__ int page(int s, int t) const {
+    return table[static_cast<size_t>(s) * max_pages + (t >> page_shift)];
+  }
+  __device__ __forceinline__ size_t row_in_page(int pg, int t) const {
     return (static_cast<size_t>(pg) << page_shift) + (t & ((1 << page_shift) - 1));
   }
 };

@@ -35,17 +35,40 @@ __device__ __forceinline__ void piece_sum(const void* k, const float* k_scale, c
 #pragma unroll
   for (int e = 0; e < PM::EPP; ++e) acc[e] = 0.f;
   for (int tb = t0 + rg; tb < t1; tb += PM::RG * BATCH) {
+    // every load issued (rows past t1 read row t0 and add 0), page numbers
+    // first for paged keys, so the batch is one round trip (two paged)
     uint4 x[BATCH];
     float sc[BATCH];
+    size_t row[BATCH];
+    if (ki.table) {
+      int pg[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int t = tb + u * PM::RG;
+        pg[u] = ki.page(s, t < t1 ? t : t0);
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int t = tb + u * PM::RG;
+        row[u] = ki.row_in_page(pg[u], t < t1 ? t : t0);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int t = tb + u * PM::RG;
+        row[u] = static_cast<size_t>(s) * ki.L + (t < t1 ? t : t0);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      const int t = tb + u * PM::RG;
-      x[u] = make_uint4(0u, 0u, 0u, 0u);
-      sc[u] = 0.f;
-      if (t < t1) {
-        const size_t row = ki.row(s, t);
-        x[u] = *reinterpret_cast<const uint4*>(kb + row * (D * PM::EB) + piece * 16);
-        sc[u] = (KT == DT_E4M3) ? k_scale[row] : 1.f;
+      x[u] = *reinterpret_cast<const uint4*>(kb + row[u] * (D * PM::EB) + piece * 16);
+      sc[u] = (KT == DT_E4M3) ? k_scale[row[u]] : 1.f;
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      if (tb + u * PM::RG >= t1) {
+        x[u] = make_uint4(0u, 0u, 0u, 0u);
+        sc[u] = 0.f;
       }
     }
 #pragma unroll

@@ -34,15 +34,31 @@ __device__ __forceinline__ void pool_batch_load(const uint8_t* __restrict__ k,
                                                 const KeyIndex& ki, int s, int t, int t1,
                                                 PoolBatch<KT, D>& pb) {
   using PM = PoolMap<KT, D>;
+  constexpr int U = PoolBatch<KT, D>::U;
   const int c = threadIdx.x % PM::CPR;
+  int tc[U];
 #pragma unroll
-  for (int r = 0; r < PoolBatch<KT, D>::U; ++r) {
+  for (int r = 0; r < U; ++r) {
     const int tt = t + r * PM::RG;
-    const int tc = tt < t1 ? tt : t;             // stay in bounds; masked below
-    const size_t row = ki.row(s, tc);
-    pb.x[r] = *reinterpret_cast<const uint4*>(k + row * PM::ROW_BYTES + c * 16);
+    tc[r] = tt < t1 ? tt : t;                    // stay in bounds; masked below
+  }
+  size_t row[U];
+  if (ki.table) {
+    // paged keys: every row's page number in flight together, then the rows
+    int pg[U];
+#pragma unroll
+    for (int r = 0; r < U; ++r) pg[r] = ki.page(s, tc[r]);
+#pragma unroll
+    for (int r = 0; r < U; ++r) row[r] = ki.row_in_page(pg[r], tc[r]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < U; ++r) row[r] = static_cast<size_t>(s) * ki.L + tc[r];
+  }
+#pragma unroll
+  for (int r = 0; r < U; ++r) {
+    pb.x[r] = *reinterpret_cast<const uint4*>(k + row[r] * PM::ROW_BYTES + c * 16);
     pb.sc[r] = 1.f;
-    if constexpr (KT == DT_E4M3) pb.sc[r] = k_scale[row];
+    if constexpr (KT == DT_E4M3) pb.sc[r] = k_scale[row[r]];
   }
 }
 

@@ -130,11 +130,51 @@ __device__ __forceinline__ uint32_t issue_group(RawGroup<KT, D, U>& raw, float* 
   using LY = KeyLayout<KT, D>;
   const int rsub = lane / LY::LANES_PER_ROW, q = lane % LY::LANES_PER_ROW;
   uint32_t valid = 0;
+  if constexpr (CAND) {
+    // candidate lists: lane c of each group of 16 reads element c of each
+    // tile (unconditionally, clamped to the list; masked below) and, for
+    // paged keys, that token's page; a lane loading a key row takes the row's
+    // token and page from the lane of that element by a cross-lane read, so
+    // a group costs two round trips (three paged) however many rows it holds
+    int tokc[U], pgc[U];
+#pragma unroll
+    for (int t = 0; t < U; ++t) {
+      const int e = (tile0 + t * tstride) * 16 + c;
+      tokc[t] = crow[e < len ? e : len - 1];
+      pgc[t] = 0;
+    }
+    if (ki.table) {
+#pragma unroll
+      for (int t = 0; t < U; ++t) pgc[t] = ki.page(s, tokc[t] >= 0 ? tokc[t] : 0);
+    }
+#pragma unroll
+    for (int t = 0; t < U; ++t) {
+#pragma unroll
+      for (int i = 0; i < LY::NLOAD; ++i) {
+        // load i of lane l reads 16 bytes of the tile's row i*ROWS_PER_LOAD + l/LANES_PER_ROW
+        const int src = i * LY::ROWS_PER_LOAD + rsub;
+        const int tk = __shfl(tokc[t], src, 64);
+        const int tok = tk >= 0 ? tk : 0;
+        const size_t row = ki.table ? ki.row_in_page(__shfl(pgc[t], src, 64), tok)
+                                    : static_cast<size_t>(s) * ki.L + tok;
+        raw[t][i] = *reinterpret_cast<const u32x4_t*>(kbase + row * LY::ROW + 16 * q);
+      }
+      const int e = (tile0 + t * tstride) * 16 + c;
+      valid |= e < len && tokc[t] >= 0 ? (1u << t) : 0u;
+      if constexpr (KT == DT_E4M3) {
+        const int tok = tokc[t] >= 0 ? tokc[t] : 0;
+        sc[t] = sbase[ki.table ? ki.row_in_page(pgc[t], tok) : static_cast<size_t>(s) * ki.L + tok];
+      } else {
+        sc[t] = 1.f;
+      }
+    }
+    return valid;
+  }
 #pragma unroll
   for (int t = 0; t < U; ++t) {
     const int te = (tile0 + t * tstride) * 16;
     size_t rb = 0;                                     // row of the tile's first token
-    if constexpr (!CAND) {
+    {
       const int tc = te < len ? te : len - 1;
       if (ki.table) {
         const int pg = __builtin_amdgcn_readlane(page_v, ord0 + t);
@@ -147,29 +187,15 @@ __device__ __forceinline__ uint32_t issue_group(RawGroup<KT, D, U>& raw, float* 
 #pragma unroll
     for (int i = 0; i < LY::NLOAD; ++i) {
       const int e = te + i * LY::ROWS_PER_LOAD + rsub;
-      size_t row;
-      if constexpr (CAND) {
-        const int tok = e < len ? crow[e] : -1;
-        row = ki.row(s, tok >= 0 ? tok : 0);
-      } else {
-        row = e < len ? rb + (e - te) : rb;
-      }
+      const size_t row = e < len ? rb + (e - te) : rb;
       raw[t][i] = *reinterpret_cast<const u32x4_t*>(kbase + row * LY::ROW + 16 * q);
     }
     const int e = te + c;
-    int tok = -1;
-    if (e < len) tok = CAND ? crow[e] : e;
-    valid |= tok >= 0 ? (1u << t) : 0u;
-    if constexpr (KT == DT_E4M3) {
-      size_t srow;
-      if constexpr (CAND)
-        srow = ki.row(s, tok >= 0 ? tok : 0);
-      else
-        srow = e < len ? rb + c : rb;
-      sc[t] = sbase[srow];
-    } else {
+    valid |= e < len ? (1u << t) : 0u;
+    if constexpr (KT == DT_E4M3)
+      sc[t] = sbase[e < len ? rb + c : rb];
+    else
       sc[t] = 1.f;
-    }
   }
   return valid;
 }
@@ -323,8 +349,12 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
   uint32_t va = 0, vb = 0, vc = 0;
   va = issue_group<KT, D, U, CAND>(ra, sa, wtile, tstride, lane, c, len, crow, kseq, sseq,
                                    p.ki, s, 0, page_v);
-  vb = issue_group<KT, D, U, CAND>(rb, sb, wtile + gstep, tstride, lane, c, len, crow, kseq,
-                                   sseq, p.ki, s, U, page_v);
+  // (a candidate-list wavefront has its tiles in one group as a rule: its
+  // second group, whose index reads would wait behind the first's keys, is
+  // read only when it is scored)
+  if (!CAND || wtiles > U)
+    vb = issue_group<KT, D, U, CAND>(rb, sb, wtile + gstep, tstride, lane, c, len, crow, kseq,
+                                     sseq, p.ki, s, U, page_v);
 
   if (do_hist) {
     for (int b = threadIdx.x; b < kBins0; b += 256) lh[b] = 0u;

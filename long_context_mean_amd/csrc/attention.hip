@@ -115,16 +115,33 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
     constexpr int TOTAL = kChunkTok * PIECES;
     constexpr int BATCH = 6;
     for (int base = 0; base < TOTAL; base += 256 * BATCH) {
+      // every read issued (pieces past the chunk re-read its last one and
+      // are not stored), page numbers first for a paged cache, so a batch is
+      // one round trip (two paged) rather than one per guarded read
       u32x4_t x[BATCH];
+      int tk[BATCH];
+      size_t row[BATCH];
 #pragma unroll
       for (int b = 0; b < BATCH; ++b) {
         const int f = base + b * 256 + tid;
-        if (f < TOTAL) {
-          const int r = f / PIECES, pc = f % PIECES;
-          const int t = tok_lds[r];
-          const size_t row = p.ki.row(s, t >= 0 ? t : 0);
-          x[b] = *reinterpret_cast<const u32x4_t*>(p.kv + row * (DQK * 2) + 16 * pc);
-        }
+        const int t = tok_lds[(f < TOTAL ? f : TOTAL - 1) / PIECES];
+        tk[b] = t >= 0 ? t : 0;
+      }
+      if (p.ki.table) {
+        int pg[BATCH];
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) pg[b] = p.ki.page(s, tk[b]);
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) row[b] = p.ki.row_in_page(pg[b], tk[b]);
+      } else {
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) row[b] = static_cast<size_t>(s) * p.ki.L + tk[b];
+      }
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        const int f = base + b * 256 + tid;
+        const int pc = (f < TOTAL ? f : TOTAL - 1) % PIECES;
+        x[b] = *reinterpret_cast<const u32x4_t*>(p.kv + row[b] * (DQK * 2) + 16 * pc);
       }
 #pragma unroll
       for (int b = 0; b < BATCH; ++b) {

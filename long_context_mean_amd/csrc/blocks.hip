@@ -45,19 +45,59 @@ __global__ __launch_bounds__(256) void block_score_kernel(BlockScoreArgs a) {
   const int s = a.q_seq[n];
   const int M = (a.L + a.B - 1) / a.B;
 
-  // routed query heads (fp32) and their weights
-  for (int f = tid; f < a.h * D; f += 256) {
-    const int j = f / D, i = f % D;
-    const int head = a.heads[static_cast<size_t>(n) * a.h + j];
-    const size_t e = (static_cast<size_t>(n) * a.H_I + head) * D + i;
-    qh[j][i] = QT == DT_F32 ? static_cast<const float*>(a.q)[e]
-                            : bf16_lo(static_cast<const uint16_t*>(a.q)[e]);
-    if (i == 0) wh[j] = a.w[static_cast<size_t>(n) * a.H_I + head];
+  // routed query heads (fp32) and their weights, in batches of 8 elements
+  // per thread whose reads are all issued (elements past h * D re-read head
+  // h - 1 and are not stored), the head indices first
+  constexpr int QB = 8;
+  for (int f0 = tid; f0 < a.h * D; f0 += 256 * QB) {
+    int head[QB];
+#pragma unroll
+    for (int k = 0; k < QB; ++k) {
+      const int j = (f0 + 256 * k) / D;
+      head[k] = a.heads[static_cast<size_t>(n) * a.h + (j < a.h ? j : a.h - 1)];
+    }
+    float qv[QB], wv[QB];
+#pragma unroll
+    for (int k = 0; k < QB; ++k) {
+      const size_t e = (static_cast<size_t>(n) * a.H_I + head[k]) * D + (f0 + 256 * k) % D;
+      qv[k] = QT == DT_F32 ? static_cast<const float*>(a.q)[e]
+                           : bf16_lo(static_cast<const uint16_t*>(a.q)[e]);
+      wv[k] = a.w[static_cast<size_t>(n) * a.H_I + head[k]];
+    }
+#pragma unroll
+    for (int k = 0; k < QB; ++k) {
+      const int f = f0 + 256 * k;
+      if (f < a.h * D) {
+        qh[f / D][f % D] = qv[k];
+        if (f % D == 0) wh[f / D] = wv[k];
+      }
+    }
   }
-  // complete blocks from the pooled table
-  for (int f = tid; f < nb * D; f += 256) {
-    const int i = f / D, c = f % D;
-    if (b0 + i < Mf) kb[i][c] = a.kbar[(static_cast<size_t>(s) * M + b0 + i) * D + c];
+  // complete blocks from the pooled table: 16-byte reads, all in flight
+  // (blocks past the table's end re-read its last one; only the row's
+  // complete blocks are stored)
+  {
+    constexpr int V4 = kBlocksPerWG * D / 4 / 256;      // float4 reads per thread
+    float4 tv[V4];
+#pragma unroll
+    for (int k = 0; k < V4; ++k) {
+      const int f = tid + 256 * k;
+      const int i = f / (D / 4), c4 = f % (D / 4);
+      const int bb = b0 + i < M ? b0 + i : M - 1;
+      tv[k] = *reinterpret_cast<const float4*>(a.kbar + (static_cast<size_t>(s) * M + bb) * D +
+                                               4 * c4);
+    }
+#pragma unroll
+    for (int k = 0; k < V4; ++k) {
+      const int f = tid + 256 * k;
+      const int i = f / (D / 4), c4 = f % (D / 4);
+      if (i < nb && b0 + i < Mf) {
+        kb[i][4 * c4] = tv[k].x;
+        kb[i][4 * c4 + 1] = tv[k].y;
+        kb[i][4 * c4 + 2] = tv[k].z;
+        kb[i][4 * c4 + 3] = tv[k].w;
+      }
+    }
   }
   // a partial last block: the mean of the row's visible keys of that block
   const int cp = Ln - Mf * a.B;

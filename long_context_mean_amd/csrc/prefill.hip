@@ -360,42 +360,56 @@ __global__ __launch_bounds__(256, HP == 4 ? 2 : 3) void score_prefill_kernel(Pre
     return;
   }
 
-  // A operand (4 row tiles of this wavefront) and the weights of the lane's rows
+  // A operand (4 row tiles of this wavefront) and the weights of the lane's
+  // rows.  Every read is issued unconditionally (rows past N or past h read
+  // row N - 1 / head slot h - 1 and are zeroed), the head indices first, so
+  // the setup is two round trips rather than one per guarded read.
   typename LY::Frag a[4][KK];
   float wv[4][4];
+  int ja[4], jw[4][4];
+  bool va[4], vw[4][4];
+  size_t ta[4], tw[4][4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     int qr, hs;
     RM::row(wave, rt, c, qr, hs);                       // row c of the tile: this lane's A data
     const int t = qrow0 + qr;
-    const bool rv = t < p.N && hs < p.h;
-    int j = 0;
-    if (rv) j = p.heads ? p.heads[static_cast<size_t>(t) * p.h + hs] : hs;
-    const uint8_t* qrp = p.q + (static_cast<size_t>(rv ? t : 0) * p.H_I + j) * LY::ROW;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if constexpr (F8) {
-        i32x8_t x = *reinterpret_cast<const i32x8_t*>(qrp + 32 * g);
-        if (!rv) x = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        a[rt][kk] = x;
-      } else {
-        u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrp + 64 * kk + 16 * g);
-        if (!rv) x = u32x4_t{0u, 0u, 0u, 0u};
-        a[rt][kk] = __builtin_bit_cast(bf16x8_t, x);
-      }
-    }
+    va[rt] = t < p.N && hs < p.h;
+    ta[rt] = static_cast<size_t>(t < p.N ? t : p.N - 1);
+    const int hc = hs < p.h ? hs : p.h - 1;
+    ja[rt] = p.heads ? p.heads[ta[rt] * p.h + hc] : hc;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int qo, ho;
       RM::row(wave, rt, 4 * g + i, qo, ho);             // output rows of this lane's results
       const int tt = qrow0 + qo;
-      float wf = 0.f;
-      if (tt < p.N && ho < p.h) {
-        const int jj = p.heads ? p.heads[static_cast<size_t>(tt) * p.h + ho] : ho;
-        wf = p.w[static_cast<size_t>(tt) * p.H_I + jj];
-        if constexpr (F8) wf *= p.q_scale[static_cast<size_t>(tt) * p.H_I + jj];
+      vw[rt][i] = tt < p.N && ho < p.h;
+      tw[rt][i] = static_cast<size_t>(tt < p.N ? tt : p.N - 1);
+      const int hoc = ho < p.h ? ho : p.h - 1;
+      jw[rt][i] = p.heads ? p.heads[tw[rt][i] * p.h + hoc] : hoc;
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const uint8_t* qrp = p.q + (ta[rt] * p.H_I + ja[rt]) * LY::ROW;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if constexpr (F8) {
+        i32x8_t x = *reinterpret_cast<const i32x8_t*>(qrp + 32 * g);
+        if (!va[rt]) x = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        a[rt][kk] = x;
+      } else {
+        u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrp + 64 * kk + 16 * g);
+        if (!va[rt]) x = u32x4_t{0u, 0u, 0u, 0u};
+        a[rt][kk] = __builtin_bit_cast(bf16x8_t, x);
       }
-      wv[rt][i] = wf;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t wi = tw[rt][i] * p.H_I + jw[rt][i];
+      float wf = p.w[wi];
+      if constexpr (F8) wf *= p.q_scale[wi];
+      wv[rt][i] = vw[rt][i] ? wf : 0.f;
     }
   }
   OutState<HP, CAND> o;

@@ -390,15 +390,29 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
     __syncthreads();
   }
   // A operand: head rows of this query row; W: weights of this lane's D rows.
+  // (every read unconditional: rows past nrows read row nrows - 1 and are
+  // zeroed; the head indices first, so the setup is two round trips)
   bf16x8_t a[NT][KK];
   float wv[NT][4];
+  int ja[NT], jw[NT][4];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = nt * 16 + c;
-    int j = 0;
-    const bool rv = r < p.nrows;
-    if (rv) j = ROUTE ? heads_lds[r] : p.heads ? p.heads[static_cast<size_t>(n) * p.nrows + r] : r;
-    const uint16_t* qrow = ROUTE ? qlds + j * D : p.q + (static_cast<size_t>(n) * p.H_I + j) * D;
+    const int rc = r < p.nrows ? r : p.nrows - 1;
+    ja[nt] = ROUTE ? heads_lds[rc] : p.heads ? p.heads[static_cast<size_t>(n) * p.nrows + rc] : rc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = nt * 16 + 4 * g + i;
+      const int rrc = rr < p.nrows ? rr : p.nrows - 1;
+      jw[nt][i] = ROUTE ? heads_lds[rrc]
+                        : p.heads ? p.heads[static_cast<size_t>(n) * p.nrows + rrc] : rrc;
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const bool rv = nt * 16 + c < p.nrows;
+    const uint16_t* qrow =
+        ROUTE ? qlds + ja[nt] * D : p.q + (static_cast<size_t>(n) * p.H_I + ja[nt]) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + elem_off<KT>(g, kk));
@@ -407,14 +421,8 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rr = nt * 16 + 4 * g + i;
-      float wf = 0.f;
-      if (rr < p.nrows) {
-        const int jj = ROUTE ? heads_lds[rr]
-                             : p.heads ? p.heads[static_cast<size_t>(n) * p.nrows + rr] : rr;
-        wf = ROUTE ? wlds[jj] : p.w[static_cast<size_t>(n) * p.H_I + jj];
-      }
-      wv[nt][i] = wf;
+      const float wf = ROUTE ? wlds[jw[nt][i]] : p.w[static_cast<size_t>(n) * p.H_I + jw[nt][i]];
+      wv[nt][i] = nt * 16 + 4 * g + i < p.nrows ? wf : 0.f;
     }
   }
   if (do_hist) __syncthreads();

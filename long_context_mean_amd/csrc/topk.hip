@@ -375,19 +375,26 @@ __global__ __launch_bounds__(NT) void topk_final_kernel(
   // the certain-winner words before the slice (counted) and the slice's own
   // word; every thread's first candidate (the list holds kCandCap >= NT
   // entries, so the read stays inside it)
+  // (every read unconditional, at an address inside the row's regions, and
+  // the value dropped where it does not apply: a guarded read would wait
+  // on its own)
   const uint32_t* bmg = bitmap + static_cast<size_t>(n) * (u_stride / 32);
-  const uint4 meta = len > 0 ? *reinterpret_cast<const uint4*>(h0g + kCandCountOffset)
-                             : make_uint4(0u, 0u, 0u, 0u);
+  const uint4 meta_r = *reinterpret_cast<const uint4*>(h0g + kCandCountOffset);
   uint4 pw[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int w = 4 * (t + q * NT);
-    pw[q] = w < w0 ? *reinterpret_cast<const uint4*>(bmg + w) : make_uint4(0u, 0u, 0u, 0u);
+    pw[q] = *reinterpret_cast<const uint4*>(bmg + (w < w0 ? w : 0));
   }
-  const uint32_t wd = w0 + t < nwords ? bmg[w0 + t] : 0u;
+  const uint32_t wd_r = bmg[w0 + t < nwords ? w0 + t : 0];
   const uint2* cl = clist + static_cast<size_t>(n) * kCandCap;
   static_assert(kCandCap >= NT, "one speculative candidate per thread");
   const uint2 e_first = cl[t];
+  const uint4 meta = len > 0 ? meta_r : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    if (4 * (t + q * NT) >= w0) pw[q] = make_uint4(0u, 0u, 0u, 0u);
+  const uint32_t wd = w0 + t < nwords ? wd_r : 0u;
   const uint32_t c = meta.x, d0 = meta.y, r0 = meta.z, K = meta.w;
   // (rows past 2^24 tokens would need a fourth index level in the tie cut)
   const bool fallback = c > static_cast<uint32_t>(kCandCap) || len > (1 << 24);

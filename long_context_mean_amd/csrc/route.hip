@@ -121,6 +121,7 @@ struct RoutePartialExtra {
   const int32_t* len_new = nullptr;   // [S]
   float* kbar_out = nullptr;          // the table (the kbar the chunks read)
   int npool = 0;                      // pooling workgroups per sequence
+  int S = 0;                          // sequences (len_old / len_new entries)
 };
 
 // Zeroes row n's level-0 histogram region (the scoring kernel's atomics add
@@ -154,9 +155,10 @@ __global__ __launch_bounds__(256) void route_partial_mfma_kernel(
     if (n != 0) return;
     const int pb = chunk - (nchunks + 1);
     const int s = pb / x.npool;
-    const int b = pb % x.npool + x.len_old[s] / B;
+    const int lo = x.len_old[s], hi = x.len_new[s];    // one round trip for both
+    const int b = pb % x.npool + lo / B;
     const int t1 = (b + 1) * B;
-    if (t1 > x.len_new[s] || t1 <= x.len_old[s]) return;
+    if (t1 > hi || t1 <= lo) return;
     const float m = pool_block_mean<KT, D>(static_cast<const uint8_t*>(x.k), x.k_scale, x.ki, s,
                                            b * B, t1, kpart);
     if (threadIdx.x < D) x.kbar_out[(static_cast<size_t>(s) * M + b) * D + threadIdx.x] = m;
@@ -203,6 +205,15 @@ __global__ __launch_bounds__(256) void route_partial_mfma_kernel(
   // end read its last one; entries past the row's visible blocks are zeroed
   // below); those of blocks completed by this call ([nlo, nhi)) are replaced
   // below
+  // with few sequences each lane reads one sequence's lengths alongside the
+  // row's sequence, so the lengths of a block this call completes do not
+  // wait for it (one round trip fewer before that block's keys are read)
+  int lo_v = 0, hi_v = 0;
+  if (x.len_new && x.S <= 64) {
+    const int l = lane < x.S ? lane : 0;
+    lo_v = x.len_old[l];
+    hi_v = x.len_new[l];
+  }
   const int s = q_seq[n];
   const int b0 = chunk * kRouteBlocks;
   constexpr int PER = kRouteBlocks * D / 4 / 256;      // table float4s per thread
@@ -219,8 +230,13 @@ __global__ __launch_bounds__(256) void route_partial_mfma_kernel(
   const int nb = min(kRouteBlocks, Mf - b0);
   int len_old = 0, len_new = 0;
   if (x.len_new) {
-    len_old = x.len_old[s];
-    len_new = x.len_new[s];
+    if (x.S <= 64) {
+      len_old = __builtin_amdgcn_readlane(lo_v, s);
+      len_new = __builtin_amdgcn_readlane(hi_v, s);
+    } else {
+      len_old = x.len_old[s];
+      len_new = x.len_new[s];
+    }
   }
   if (x.hist0 && chunk == 0) clear_hist_row(x.hist0, n);
   if (nb <= 0) {
@@ -535,6 +551,7 @@ hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
         x.len_new = a.len_new;
         x.kbar_out = a.kbar_out;
         x.npool = a.max_new / a.B + 1;     // blocks max_new tokens can complete
+        x.S = a.S;
         gx += x.npool * a.S;
       }
       MISA_LAUNCH(K_ROUTE_PARTIAL, (route_partial_mfma_kernel<KT, D>), dim3(gx, a.N), dim3(256),

@@ -163,7 +163,8 @@ __device__ __forceinline__ uint32_t issue_group(RawGroup<KT, D, U>& raw, float* 
       valid |= e < len && tokc[t] >= 0 ? (1u << t) : 0u;
       if constexpr (KT == DT_E4M3) {
         const int tok = tokc[t] >= 0 ? tokc[t] : 0;
-        sc[t] = sbase[ki.table ? ki.row_in_page(pgc[t], tok) : static_cast<size_t>(s) * ki.L + tok];
+        sc[t] = sbase[ki.table ? ki.row_in_page(pgc[t], tok)
+                               : static_cast<size_t>(s) * ki.L + tok];
       } else {
         sc[t] = 1.f;
       }
@@ -173,15 +174,13 @@ __device__ __forceinline__ uint32_t issue_group(RawGroup<KT, D, U>& raw, float* 
 #pragma unroll
   for (int t = 0; t < U; ++t) {
     const int te = (tile0 + t * tstride) * 16;
-    size_t rb = 0;                                     // row of the tile's first token
-    {
-      const int tc = te < len ? te : len - 1;
-      if (ki.table) {
-        const int pg = __builtin_amdgcn_readlane(page_v, ord0 + t);
-        rb = (static_cast<size_t>(pg) << ki.page_shift) + (tc & ((1 << ki.page_shift) - 1));
-      } else {
-        rb = static_cast<size_t>(s) * ki.L + tc;
-      }
+    size_t rb;                                         // row of the tile's first token
+    const int tc = te < len ? te : len - 1;
+    if (ki.table) {
+      const int pg = __builtin_amdgcn_readlane(page_v, ord0 + t);
+      rb = (static_cast<size_t>(pg) << ki.page_shift) + (tc & ((1 << ki.page_shift) - 1));
+    } else {
+      rb = static_cast<size_t>(s) * ki.L + tc;
     }
     // flat: load i of lane l reads 16 bytes of row i*ROWS_PER_LOAD + l/LANES_PER_ROW
 #pragma unroll

@@ -1104,6 +1104,9 @@ def test_route_score_topk_equals_two_calls(case, k_dt, q_dt, page_size):
          len_new=[2000], new=[200], max_new=200),
     dict(N=2, S=2, L=3000, d=128, H_I=16, h=4, B=64, topk=100,             # nothing appended
          len_new=[3000, 2999], new=[0, 0], max_new=0),
+    dict(N=70, S=70, L=1500, d=128, H_I=16, h=4, B=64, topk=100,           # more than 64 sequences
+         len_new=[64 * (1 + s % 23) + (5 if s % 2 else 0) for s in range(70)],
+         new=[1] * 70, max_new=1),
 ])
 @pytest.mark.parametrize("k_dt,page_size", [(synth.BF16, 0), (synth.FP8, 0), (synth.BF16, 64)])
 def test_pool_route_score_topk_equals_separate_calls(case, k_dt, page_size):

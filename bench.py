@@ -810,6 +810,25 @@ def main():
                 [np.isin(p.needles[n, :, 0], hidx[n]).mean() for n in range(p.N)])), 4)
             del sv
             torch.cuda.empty_cache()
+        log("[bench] the serving step at 32 queries, each over its own 131072 keys")
+        p32 = synth.small("c4x32", 1104, N=32, S=32, L=p.L, d=p.d, H_I=p.H_I, h=h, B=p.B,
+                          topk=p.topk, n_clusters=64, sigma=0.5)
+        s32 = Serving(p32, torch, binding, h)
+        ms32 = timed(torch, s32.step, args.steps, args.warmup)
+        _, kt32, _ = kernel_times(torch, binding, s32.step, max(3, args.steps // 2), 1, 8)
+        keys32 = p32.S * p32.L * p32.d * 2
+        bytes32 = keys32 + p32.S * (p32.L // p32.B) * p32.d * 4
+        extra["serving_step_n32"] = {
+            "workload": "32 queries x L=131072 bf16 keys (32 sequences), H_I=64, d=128, h=8, "
+                        "B=128, top-k=2048, the c4 mixture recipe without needles",
+            "ms_per_step": round(ms32, 4),
+            "tokens_per_s": p32.tokens_indexed() / (ms32 * 1e-3),
+            "kernel_ms": {k: round(v, 5) for k, v in kt32.items()},
+            "score_kernel_hbm_gbs": round(keys32 / (kt32["score_mfma_kernel"] * 1e-3) / 1e9, 1)
+            if kt32.get("score_mfma_kernel") else None,
+            "step_frac": round(bytes32 / (ms32 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del s32, p32
+        torch.cuda.empty_cache()
         log("[bench] fp8-key MISA-dagger (c5 shape)")
         p5 = synth.make("c5")
         r5 = Replicas(p5, torch, binding, p5.h, k_prime=p5.k_prime)

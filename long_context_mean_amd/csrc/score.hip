@@ -73,6 +73,20 @@ struct KeyLayout {
   static constexpr int TILE_LDS = 16 * LDS_STRIDE;
 };
 
+// Adds a 256-thread workgroup's LDS level-0 histogram to the row's global
+// one.  Each thread's 16 bin counts are read together, then added (a loop that
+// waited for each count before its atomic took 16 LDS round trips at the end of
+// every workgroup); the caller has synchronised the workgroup.
+__device__ __forceinline__ void flush_hist(const uint32_t* lh, uint32_t* hg) {
+  constexpr int kPerT = kBins0 / 256;
+  uint32_t cnt[kPerT];
+#pragma unroll
+  for (int i = 0; i < kPerT; ++i) cnt[i] = lh[threadIdx.x + 256 * i];
+#pragma unroll
+  for (int i = 0; i < kPerT; ++i)
+    if (cnt[i]) atomicAdd(&hg[threadIdx.x + 256 * i], cnt[i]);
+}
+
 // d-elements that lane group g (= lane / 16) feeds to MFMA kk, as the first
 // of 8 consecutive elements.  Load p of a lane reads bytes [64p + 16g, +16)
 // of its key row, so one load instruction covers 64 contiguous bytes of each
@@ -473,11 +487,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
   }
   if (do_hist) {
     __syncthreads();
-    uint32_t* hg = p.hist0 + static_cast<size_t>(n) * kHistWords;
-    for (int b = threadIdx.x; b < kBins0; b += 256) {
-      const uint32_t cnt = lh[b];
-      if (cnt) atomicAdd(&hg[b], cnt);
-    }
+    flush_hist(lh, p.hist0 + static_cast<size_t>(n) * kHistWords);
   }
 }
 
@@ -536,11 +546,7 @@ __global__ __launch_bounds__(256) void score_f32_kernel(
   }
   if (hist0) {
     __syncthreads();
-    uint32_t* hg = hist0 + static_cast<size_t>(n) * kHistWords;
-    for (int b = threadIdx.x; b < kBins0; b += 256) {
-      const uint32_t cnt = lh[b];
-      if (cnt) atomicAdd(&hg[b], cnt);
-    }
+    flush_hist(lh, hist0 + static_cast<size_t>(n) * kHistWords);
   }
 }
 
